@@ -1,0 +1,241 @@
+"""CPU oracle for the Qwen3-MoE sparse FFN block -- TEST INFRASTRUCTURE ONLY.
+
+Thin ctypes wrapper over ``q3moe_oracle.c`` (plain scalar C, double
+accumulation).  Only the tests, the package's smoke check and the benchmark's
+CPU-baseline leg may import this package; the HIP library never does.
+
+Every function takes and returns NumPy arrays on the host.
+
+Parity status per function (how each is pinned is listed in the tests):
+  dequant_block / dequant_matrix  pinned: hand-built blocks with closed-form
+                                  values, orientation probe, page byte counts
+  qgemv                           pinned: dense NumPy product of the pinned
+                                  dequantisation, row-constant probe
+  route                           pinned: brute-force full sort, softmax
+                                  closed forms, ties, shift invariance
+  expert_ffn                      pinned: dense-over-all-experts brute force,
+                                  single-expert dense MLP, zero cases
+  rmsnorm / attn_prologue /       pinned: RMS closed form, rotation invariants,
+  rope_neox                       NEOX-vs-interleaved discriminator
+Agreement with real GGUF files is not pinned (no files; the bit layout is
+the GGUF k-quant reading).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from pathlib import Path
+
+import numpy as np
+
+HERE = Path(__file__).resolve().parent
+SRC = HERE / "q3moe_oracle.c"
+LIB = HERE / "libq3moe_oracle.so"
+
+Q4_K, Q6_K = 1, 2
+BLOCK_BYTES = {Q4_K: 144, Q6_K: 210}
+
+
+def build(src: Path = SRC, out: Path = LIB, extra_flags=()) -> Path:
+    """Compile the oracle with gcc (no fast-math: IEEE double throughout)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", *extra_flags,
+           "-o", str(out), str(src), "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+def _stale() -> bool:
+    return not LIB.exists() or LIB.stat().st_mtime < SRC.stat().st_mtime
+
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+
+
+def _declare(lib):
+    sig = {
+        "orc_half_to_double": (ctypes.c_double, [ctypes.c_uint16]),
+        "orc_block_bytes": (ctypes.c_int, [ctypes.c_int]),
+        "orc_dequant_block": (ctypes.c_int, [ctypes.c_int, _P, _P]),
+        "orc_dequant_row": (ctypes.c_int, [ctypes.c_int, _P, _I64, _I64, _P]),
+        "orc_dequant_matrix": (ctypes.c_int, [ctypes.c_int, _P, _I64, _I64, _P]),
+        "orc_qgemv": (ctypes.c_int, [ctypes.c_int, _P, _I64, _I64, _P, _P]),
+        "orc_router_logits": (None, [_P, _I64, _I64, _P, _I32, _P]),
+        "orc_topk_softmax": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _P]),
+        "orc_route": (ctypes.c_int, [_P, _I64, _I64, _P, _I32, _I32, _P, _P, _P]),
+        "orc_expert_ffn_f64": (ctypes.c_int, [_P, _I64, _I64, _I64, _I32, _I32, _P, _P,
+                                              _P, ctypes.c_int, _I64,
+                                              _P, ctypes.c_int, _I64,
+                                              _P, ctypes.c_int, _I64, _P]),
+        "orc_expert_ffn": (ctypes.c_int, [_P, _I64, _I64, _I64, _I32, _I32, _P, _P,
+                                          _P, ctypes.c_int, _I64,
+                                          _P, ctypes.c_int, _I64,
+                                          _P, ctypes.c_int, _I64, _P, ctypes.c_int]),
+        "orc_rmsnorm": (ctypes.c_int, [_P, _I64, _I64, _P, ctypes.c_float, _P]),
+        "orc_rope_neox": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, ctypes.c_double]),
+        "orc_attn_prologue": (ctypes.c_int, [_P, _P, _I64, _I32, _I32, _I32, _P, _P, _P,
+                                             ctypes.c_float, ctypes.c_float]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = None
+
+
+def load(path: Path | None = None):
+    """Load the oracle library (building it first if the source is newer)."""
+    global _lib
+    if path is not None:
+        return _declare(ctypes.CDLL(str(path)))
+    if _lib is None:
+        if _stale():
+            build()
+        _lib = _declare(ctypes.CDLL(str(LIB)))
+    return _lib
+
+
+def _c(a: np.ndarray, dtype) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+class Oracle:
+    """Callable view of one oracle build (the real one, or a test variant)."""
+
+    def __init__(self, lib=None):
+        self.lib = lib if lib is not None else load()
+
+    def half_to_double(self, bits: int) -> float:
+        return self.lib.orc_half_to_double(bits)
+
+    def dequant_block(self, qtype: int, blk: np.ndarray) -> np.ndarray:
+        blk = _c(blk, np.uint8)
+        assert blk.size == BLOCK_BYTES[qtype]
+        out = np.empty(256, np.float64)
+        assert self.lib.orc_dequant_block(qtype, _p(blk), _p(out)) == 0
+        return out
+
+    def dequant_matrix(self, qtype: int, mat: np.ndarray, rows: int, cols: int) -> np.ndarray:
+        mat = _c(mat, np.uint8)
+        assert mat.size >= rows * (cols // 256) * BLOCK_BYTES[qtype]
+        out = np.empty((rows, cols), np.float64)
+        assert self.lib.orc_dequant_matrix(qtype, _p(mat), rows, cols, _p(out)) == 0
+        return out
+
+    def qgemv(self, qtype: int, mat: np.ndarray, rows: int, cols: int, x: np.ndarray) -> np.ndarray:
+        mat = _c(mat, np.uint8)
+        x = _c(x, np.float64)
+        y = np.empty(rows, np.float64)
+        assert self.lib.orc_qgemv(qtype, _p(mat), rows, cols, _p(x), _p(y)) == 0
+        return y
+
+    def router_logits(self, x: np.ndarray, router: np.ndarray) -> np.ndarray:
+        x = _c(x, np.float32)
+        router = _c(router, np.float32)
+        T, H = x.shape
+        E = router.shape[0]
+        out = np.empty((T, E), np.float64)
+        self.lib.orc_router_logits(_p(x), T, H, _p(router), E, _p(out))
+        return out
+
+    def topk_softmax(self, logits: np.ndarray, k: int):
+        logits = _c(logits, np.float64)
+        T, E = logits.shape
+        idx = np.empty((T, k), np.int32)
+        w = np.empty((T, k), np.float64)
+        assert self.lib.orc_topk_softmax(_p(logits), T, E, k, _p(idx), _p(w)) == 0
+        return idx, w
+
+    def route(self, x: np.ndarray, router: np.ndarray, k: int):
+        """-> (idx int32 [T,k], w f32 [T,k], logits f64 [T,E])."""
+        x = _c(x, np.float32)
+        router = _c(router, np.float32)
+        T, H = x.shape
+        E = router.shape[0]
+        idx = np.empty((T, k), np.int32)
+        w = np.empty((T, k), np.float32)
+        logits = np.empty((T, E), np.float64)
+        assert self.lib.orc_route(_p(x), T, H, _p(router), E, k, _p(idx), _p(w), _p(logits)) == 0
+        return idx, w, logits
+
+    def _ffn_args(self, x, idx, w, gate, up, down, F, E):
+        x = _c(x, np.float32)
+        idx = _c(idx, np.int32)
+        w = _c(w, np.float32)
+        T, H = x.shape
+        k = idx.shape[1]
+        tens = []
+        for (buf, qt) in (gate, up, down):
+            buf = _c(buf, np.uint8)
+            E_ = buf.shape[0] if buf.ndim == 2 else E
+            stride = buf.shape[1] if buf.ndim == 2 else buf.size // E_
+            tens.append((buf, qt, stride))
+        return x, idx, w, T, H, k, tens
+
+    def expert_ffn(self, x, idx, w, gate, up, down, F: int, E: int,
+                   out: np.ndarray | None = None, accumulate: bool = False) -> np.ndarray:
+        """gate/up/down are (uint8 [E, stride], qtype) pairs.  -> f32 [T, H]."""
+        x, idx, w, T, H, k, tens = self._ffn_args(x, idx, w, gate, up, down, F, E)
+        res = np.zeros((T, H), np.float32) if out is None else _c(out, np.float32).copy()
+        (g, gq, gs), (u, uq, us), (d, dq, ds) = tens
+        rc = self.lib.orc_expert_ffn(_p(x), T, H, F, E, k, _p(idx), _p(w),
+                                     _p(g), gq, gs, _p(u), uq, us, _p(d), dq, ds,
+                                     _p(res), 1 if accumulate else 0)
+        assert rc == 0, rc
+        return res
+
+    def expert_ffn_f64(self, x, idx, w, gate, up, down, F: int, E: int) -> np.ndarray:
+        x, idx, w, T, H, k, tens = self._ffn_args(x, idx, w, gate, up, down, F, E)
+        res = np.empty((T, H), np.float64)
+        (g, gq, gs), (u, uq, us), (d, dq, ds) = tens
+        rc = self.lib.orc_expert_ffn_f64(_p(x), T, H, F, E, k, _p(idx), _p(w),
+                                         _p(g), gq, gs, _p(u), uq, us, _p(d), dq, ds, _p(res))
+        assert rc == 0, rc
+        return res
+
+    def rmsnorm(self, x: np.ndarray, gain: np.ndarray, eps: float) -> np.ndarray:
+        x = _c(x, np.float32)
+        gain = _c(gain, np.float32)
+        T, n = x.shape
+        out = np.empty_like(x)
+        self.lib.orc_rmsnorm(_p(x), T, n, _p(gain), eps, _p(out))
+        return out
+
+    def rope_neox(self, x: np.ndarray, pos: np.ndarray, base: float) -> np.ndarray:
+        """x f32 [T, n_heads, D] -> rotated copy."""
+        x = _c(x, np.float32).copy()
+        pos = _c(pos, np.int32)
+        T, nh, D = x.shape
+        assert self.lib.orc_rope_neox(_p(x), T, nh, D, _p(pos), base) == 0
+        return x
+
+    def attn_prologue(self, q, k, q_norm, k_norm, pos, eps: float, rope_base: float):
+        """q f32 [T, n_q, D], k f32 [T, n_kv, D] -> normalised and rotated copies."""
+        q = _c(q, np.float32).copy()
+        k = _c(k, np.float32).copy()
+        T, nq, D = q.shape
+        nkv = k.shape[1]
+        rc = self.lib.orc_attn_prologue(_p(q), _p(k), T, nq, nkv, D,
+                                        _p(_c(q_norm, np.float32)), _p(_c(k_norm, np.float32)),
+                                        _p(_c(pos, np.int32)), eps, rope_base)
+        assert rc == 0
+        return q, k
+
+
+_default = None
+
+
+def oracle() -> Oracle:
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default
