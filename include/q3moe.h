@@ -1,0 +1,172 @@
+/*
+ * q3moe -- the Qwen3-MoE sparse FFN block for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Unless a comment says otherwise every tensor pointer is a DEVICE
+ * pointer (HBM) owned by the caller, and every `stream` argument is a
+ * hipStream_t handle passed as void* (NULL selects the null stream).
+ *
+ * Common contract of every entry point:
+ *  - Arguments are validated on the host before anything is enqueued.  A
+ *    failed check returns a status code and enqueues nothing.
+ *  - On success the call only enqueues kernels on `stream` and returns; it
+ *    never synchronises with the host and never allocates memory.  Buffers
+ *    must stay alive until the stream has passed the work.
+ *  - The library keeps no pointer after a call returns and holds no mutable
+ *    global state; concurrent calls on different streams with disjoint
+ *    buffers are safe.
+ *  - T = 0 (no tokens) is valid and enqueues nothing.
+ *  - Q3MOE_E_HIP reports a failed kernel launch (hipGetLastError).
+ *
+ * The block (aprender issue #3714 "qwen3moe has NO working CUDA path",
+ * "File facts" and gap G3): an f32 router GEMV over E experts, softmax,
+ * top-k with renormalised weights, per selected expert the gate and up
+ * GEMVs, SwiGLU and the down GEMV on k-quant weights read in place at
+ * base + e*stride, and the routing-weighted sum of the expert outputs.
+ * The optional attention prologue applies per-head Q/K RMSNorm (aprender
+ * PR #1228, "The fix") and NEOX RoPE (SharpInference issue #6, closing
+ * comment) with an explicit head_dim (aprender issue #479, "Fix Applied").
+ */
+#ifndef Q3MOE_H
+#define Q3MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t q3moe_status;
+enum {
+    Q3MOE_OK = 0,
+    Q3MOE_E_NULL = 1,       /* a required pointer is NULL                       */
+    Q3MOE_E_SHAPE = 2,      /* a size is out of range or inconsistent           */
+    Q3MOE_E_QTYPE = 3,      /* unknown or unsupported quantisation type         */
+    Q3MOE_E_ALIGN = 4,      /* a pointer or stride is not 16-byte aligned       */
+    Q3MOE_E_WORKSPACE = 5,  /* workspace NULL or smaller than the size query    */
+    Q3MOE_E_HIP = 6,        /* the HIP runtime rejected a launch                */
+    Q3MOE_E_ALIAS = 7       /* an output overlaps an input it must not overlap  */
+};
+
+/* k-quant super-block formats (256 weights each).  The GGUF k-quant layout:
+ *  Q3MOE_Q4_K, 144 bytes: fp16 d, fp16 dmin, 12 bytes of packed 6-bit
+ *    scales and mins for 8 sub-blocks of 32, 128 bytes of 4-bit quants;
+ *    weight = d*scale*q - dmin*min.
+ *  Q3MOE_Q6_K, 210 bytes: 128 bytes of low nibbles, 64 bytes of 2-bit high
+ *    parts, 16 int8 scales (one per 16 weights), fp16 d;
+ *    weight = d*scale*(q - 32). */
+enum { Q3MOE_Q4_K = 1, Q3MOE_Q6_K = 2 };
+
+/* One 3-D expert tensor: E matrices of `rows` x `cols` weights.  Matrix e
+ * starts at (const char*)base + e*expert_stride_bytes; inside it, row r is
+ * cols/256 consecutive super-blocks (the super-blocks run along the
+ * reduction dimension).  base must be 16-byte aligned; the stride must be a
+ * multiple of 16 and at least rows*(cols/256)*block_bytes.  The tensor is
+ * read in place (no repacking), as the per-expert pointer base + e*stride
+ * in "File facts" of issue #3714 allows. */
+typedef struct q3moe_experts {
+    const void *base;
+    int32_t qtype;
+    int32_t reserved;               /* must be 0 */
+    int64_t expert_stride_bytes;
+} q3moe_experts;
+
+/* Human-readable name of a status code (static storage). */
+const char *q3moe_status_string(q3moe_status s);
+
+/* Bytes per 256-weight super-block: 144 (Q4_K), 210 (Q6_K), 0 otherwise. */
+int32_t q3moe_qtype_block_bytes(int32_t qtype);
+
+/* rows*(cols/256)*block_bytes, or -1 when cols % 256 != 0 or qtype unknown.
+ * For the Qwen3-30B-A3B layer this is 884,736 (Q4_K 768x2048) and
+ * 1,290,240 (Q6_K 2048x768), the per-expert sizes of "File facts". */
+int64_t q3moe_expert_matrix_bytes(int32_t qtype, int64_t rows, int64_t cols);
+
+/* ---------------------------------------------------------------- route --
+ * Router GEMV, softmax, top-k and renormalisation (issue #3714, gap G3; the
+ * on-device form planned as kernel K1 under G8).
+ *   hidden   [T x H] f32, row-major, 16-byte aligned, H % 4 == 0
+ *   router   [E x H] f32, row-major (the ffn_gate_inp matrix), 16-byte aligned
+ *   topk_idx [T x k] int32 out: the k experts with the largest logits, in
+ *            descending logit order, equal logits broken by the lower index
+ *   topk_w   [T x k] f32 out: softmax over the k selected logits (equal to
+ *            the full softmax renormalised over the selected set); sums to 1
+ * Logits are accumulated in double, which keeps the top-k choice stable
+ * against summation order (the near-tie risk named in "Risk to track").
+ * Limits: 1 <= k <= 32, k <= E <= 1024, 1 <= H.
+ * workspace: device memory of at least q3moe_route_workspace_bytes(T, E)
+ * bytes, 16-byte aligned; contents need no initialisation.
+ * Errors: E_NULL, E_SHAPE, E_ALIGN, E_WORKSPACE, E_HIP. */
+size_t q3moe_route_workspace_bytes(int64_t T, int32_t E);
+q3moe_status q3moe_route(const float *hidden, int64_t T, int64_t H,
+                         const float *router, int32_t E, int32_t top_k,
+                         int32_t *topk_idx, float *topk_w,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/* ----------------------------------------------------------- expert FFN --
+ * For each token t and slot s with e = topk_idx[t*k+s] (issue #3714, gap G3;
+ * the device-side expert-pointer gather and weighted accumulate planned as
+ * K3 and K2 under G8):
+ *   g = Wg[e] x_t, u = Wu[e] x_t         (F values each; gate/up are F x H)
+ *   h = silu(g) * u, silu(z) = z / (1 + exp(-z))
+ *   y = Wd[e] h                          (H values; down is H x F)
+ *   out[t] = [out[t] +] sum over s in slot order of topk_w[t*k+s] * y
+ *   hidden   [T x H] f32, 16-byte aligned (the FFN input)
+ *   topk_idx [T x k] int32, each in [0, E); an index outside that range
+ *            makes that slot contribute zero (caller error, not reported)
+ *   topk_w   [T x k] f32
+ *   gate, up Q4_K expert tensors of F x H matrices
+ *   down     Q4_K or Q6_K expert tensor of H x F matrices (the qtype may
+ *            differ per layer, as ffn_down_exps does in the 30B-A3B files)
+ *   out      [T x H] f32, 16-byte aligned, must not overlap hidden.
+ *            accumulate = 0: out = block output; 1: out += block output
+ *            (the residual add fused).
+ * Limits: H % 256 == 0, F % 256 == 0, 256 <= H <= 4096, 256 <= F <= 1536,
+ * 1 <= k <= 32, k <= E.
+ * workspace: at least q3moe_expert_ffn_workspace_bytes(T, H, F, E, k)
+ * bytes, 16-byte aligned, contents need no initialisation.
+ * Errors: E_NULL, E_SHAPE, E_QTYPE, E_ALIGN, E_WORKSPACE, E_ALIAS, E_HIP. */
+size_t q3moe_expert_ffn_workspace_bytes(int64_t T, int64_t H, int64_t F,
+                                        int32_t E, int32_t top_k);
+q3moe_status q3moe_expert_ffn(const float *hidden, int64_t T, int64_t H, int64_t F,
+                              int32_t E, int32_t top_k,
+                              const int32_t *topk_idx, const float *topk_w,
+                              q3moe_experts gate, q3moe_experts up, q3moe_experts down,
+                              float *out, int32_t accumulate,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------ attention prologue --
+ * In place on q [T x n_q_heads x head_dim] and k [T x n_kv_heads x head_dim]
+ * (f32, row-major): for every head slice, RMSNorm with the gain vector shared
+ * by all heads of that projection (q_norm or k_norm, head_dim values),
+ *   y = gain * x / sqrt(mean(x^2) + eps),
+ * applied after the projection and its bias and before RoPE (aprender
+ * PR #1228, "The fix"); then NEOX RoPE at positions[t]: element i pairs with
+ * element i + head_dim/2 (SharpInference issue #6) and rotates by
+ * positions[t] * rope_base^(-2i/head_dim), all head_dim elements rotated.
+ * head_dim is explicit and need not equal hidden/heads (aprender issue #479:
+ * 128 for Qwen3 where hidden/heads is 64 or 80).  Angles are formed in
+ * double precision.
+ * Limits: head_dim even, 2 <= head_dim <= 512; n_q_heads >= 1,
+ * n_kv_heads >= 1, n_q_heads % n_kv_heads == 0; eps >= 0; rope_base > 0.
+ * Errors: E_NULL, E_SHAPE, E_ALIAS (q and k overlap), E_HIP. */
+q3moe_status q3moe_attn_prologue(float *q, float *k, int64_t T, int32_t n_q_heads,
+                                 int32_t n_kv_heads, int32_t head_dim,
+                                 const float *q_norm, const float *k_norm,
+                                 const int32_t *positions, float eps, float rope_base,
+                                 void *stream);
+
+/* --------------------------------------------------------------- RMSNorm --
+ * out[t] = gain * x[t] / sqrt(mean(x[t]^2) + eps) for x [T x n] f32; the
+ * per-layer input / post-attention norm of the decoder layer.  out may equal
+ * x (in place) but must not partially overlap it.
+ * Limits: 1 <= n <= 65536, eps >= 0.
+ * Errors: E_NULL, E_SHAPE, E_ALIAS, E_HIP. */
+q3moe_status q3moe_rmsnorm(const float *x, int64_t T, int64_t n, const float *gain,
+                           float eps, float *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q3MOE_H */

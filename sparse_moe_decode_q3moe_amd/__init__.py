@@ -1,0 +1,11 @@
+"""Qwen3-MoE sparse FFN block on AMD Instinct MI355X (gfx950).
+
+The compute path is libq3moe.so (hand-written HIP kernels behind a C ABI,
+include/q3moe.h); this package is its Python binding plus the seeded input
+generator.  Functions carry the C entry points' names.
+"""
+from ._lib import (  # noqa: F401
+    EXPORTS, Experts, Q3MoeError, Q4_K, Q6_K, library,
+    q3moe_attn_prologue, q3moe_expert_ffn, q3moe_expert_ffn_workspace_bytes,
+    q3moe_rmsnorm, q3moe_route, q3moe_route_workspace_bytes,
+)

@@ -1,0 +1,144 @@
+// C-ABI entry points: host-side validation, then kernel launches on the
+// caller's stream.  The contract is documented in include/q3moe.h.
+#include <hip/hip_runtime.h>
+
+#include "../../include/q3moe.h"
+#include "device_common.h"
+#include "internal.h"
+
+using q3moe::ExpertTensor;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+q3moe_status from_hip(hipError_t e) { return e == hipSuccess ? Q3MOE_OK : Q3MOE_E_HIP; }
+
+q3moe_status check_experts(const q3moe_experts& x, int64_t rows, int64_t cols, bool allow_q6,
+                           ExpertTensor& out) {
+    if (!x.base) return Q3MOE_E_NULL;
+    if (x.reserved != 0) return Q3MOE_E_SHAPE;
+    if (x.qtype != Q3MOE_Q4_K && !(allow_q6 && x.qtype == Q3MOE_Q6_K)) return Q3MOE_E_QTYPE;
+    if (!aligned16(x.base) || (x.expert_stride_bytes & 15) != 0) return Q3MOE_E_ALIGN;
+    if (x.expert_stride_bytes < q3moe_expert_matrix_bytes(x.qtype, rows, cols)) return Q3MOE_E_SHAPE;
+    out.base = static_cast<const uint8_t*>(x.base);
+    out.qtype = x.qtype;
+    out.stride = x.expert_stride_bytes;
+    return Q3MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* q3moe_status_string(q3moe_status s) {
+    switch (s) {
+        case Q3MOE_OK: return "ok";
+        case Q3MOE_E_NULL: return "a required pointer is NULL";
+        case Q3MOE_E_SHAPE: return "a size is out of range or inconsistent";
+        case Q3MOE_E_QTYPE: return "unknown or unsupported quantisation type";
+        case Q3MOE_E_ALIGN: return "a pointer or stride is not 16-byte aligned";
+        case Q3MOE_E_WORKSPACE: return "workspace missing or smaller than the size query";
+        case Q3MOE_E_HIP: return "the HIP runtime rejected a launch";
+        case Q3MOE_E_ALIAS: return "an output overlaps an input it must not overlap";
+        default: return "unknown status";
+    }
+}
+
+int32_t q3moe_qtype_block_bytes(int32_t qtype) {
+    return qtype == Q3MOE_Q4_K ? q3moe::kQ4KBytes : qtype == Q3MOE_Q6_K ? q3moe::kQ6KBytes : 0;
+}
+
+int64_t q3moe_expert_matrix_bytes(int32_t qtype, int64_t rows, int64_t cols) {
+    const int32_t bb = q3moe_qtype_block_bytes(qtype);
+    if (!bb || rows < 0 || cols < 0 || cols % 256) return -1;
+    return rows * (cols / 256) * bb;
+}
+
+size_t q3moe_route_workspace_bytes(int64_t T, int32_t E) {
+    return q3moe::route_workspace_bytes(T, E);
+}
+
+q3moe_status q3moe_route(const float* hidden, int64_t T, int64_t H, const float* router,
+                         int32_t E, int32_t top_k, int32_t* topk_idx, float* topk_w,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+    if (T < 0 || H < 1 || E < 1 || E > q3moe::kMaxExperts || top_k < 1 ||
+        top_k > q3moe::kMaxTopK || top_k > E || (H & 3) != 0 || T > 0x7fffffff)
+        return Q3MOE_E_SHAPE;
+    if (T == 0) return Q3MOE_OK;
+    if (!hidden || !router || !topk_idx || !topk_w) return Q3MOE_E_NULL;
+    if (!aligned16(hidden) || !aligned16(router)) return Q3MOE_E_ALIGN;
+    if (!workspace || workspace_bytes < q3moe_route_workspace_bytes(T, E))
+        return Q3MOE_E_WORKSPACE;
+    if (!aligned16(workspace)) return Q3MOE_E_ALIGN;
+    return from_hip(q3moe::launch_route(hidden, T, H, router, E, top_k, topk_idx, topk_w,
+                                        workspace, as_stream(stream)));
+}
+
+size_t q3moe_expert_ffn_workspace_bytes(int64_t T, int64_t H, int64_t F, int32_t E,
+                                        int32_t top_k) {
+    return q3moe::expert_ffn_workspace_bytes(T, H, F, E, top_k);
+}
+
+q3moe_status q3moe_expert_ffn(const float* hidden, int64_t T, int64_t H, int64_t F, int32_t E,
+                              int32_t top_k, const int32_t* topk_idx, const float* topk_w,
+                              q3moe_experts gate, q3moe_experts up, q3moe_experts down,
+                              float* out, int32_t accumulate, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    if (T < 0 || H % 256 || F % 256 || H < 256 || H > 4096 || F < 256 || F > 1536 || E < 1 ||
+        top_k < 1 || top_k > q3moe::kMaxTopK || top_k > E || (accumulate != 0 && accumulate != 1) ||
+        T * top_k > 0x7fffffff)
+        return Q3MOE_E_SHAPE;
+    if (T == 0) return Q3MOE_OK;
+    if (!hidden || !topk_idx || !topk_w || !out) return Q3MOE_E_NULL;
+    ExpertTensor g, u, d;
+    q3moe_status st;
+    if ((st = check_experts(gate, F, H, false, g)) != Q3MOE_OK) return st;
+    if ((st = check_experts(up, F, H, false, u)) != Q3MOE_OK) return st;
+    if ((st = check_experts(down, H, F, true, d)) != Q3MOE_OK) return st;
+    if (!aligned16(hidden) || !aligned16(out)) return Q3MOE_E_ALIGN;
+    const size_t act = (size_t)T * (size_t)H * sizeof(float);
+    if (overlaps(hidden, act, out, act)) return Q3MOE_E_ALIAS;
+    if (!workspace || workspace_bytes < q3moe_expert_ffn_workspace_bytes(T, H, F, E, top_k))
+        return Q3MOE_E_WORKSPACE;
+    if (!aligned16(workspace)) return Q3MOE_E_ALIGN;
+    return from_hip(q3moe::launch_expert_ffn(hidden, T, H, F, E, top_k, topk_idx, topk_w, g, u,
+                                             d, out, accumulate, workspace, as_stream(stream)));
+}
+
+q3moe_status q3moe_attn_prologue(float* q, float* k, int64_t T, int32_t n_q_heads,
+                                 int32_t n_kv_heads, int32_t head_dim, const float* q_norm,
+                                 const float* k_norm, const int32_t* positions, float eps,
+                                 float rope_base, void* stream) {
+    if (T < 0 || T > 0x7fffffff || n_q_heads < 1 || n_kv_heads < 1 ||
+        n_q_heads % n_kv_heads != 0 || head_dim < 2 || head_dim > 512 || (head_dim & 1) ||
+        !(eps >= 0.0f) || !(rope_base > 0.0f) || n_q_heads + n_kv_heads > 65535)
+        return Q3MOE_E_SHAPE;
+    if (T == 0) return Q3MOE_OK;
+    if (!q || !k || !q_norm || !k_norm || !positions) return Q3MOE_E_NULL;
+    if (overlaps(q, (size_t)T * n_q_heads * head_dim * sizeof(float), k,
+                 (size_t)T * n_kv_heads * head_dim * sizeof(float)))
+        return Q3MOE_E_ALIAS;
+    return from_hip(q3moe::launch_attn_prologue(q, k, T, n_q_heads, n_kv_heads, head_dim, q_norm,
+                                                k_norm, positions, eps, rope_base,
+                                                as_stream(stream)));
+}
+
+q3moe_status q3moe_rmsnorm(const float* x, int64_t T, int64_t n, const float* gain, float eps,
+                           float* out, void* stream) {
+    if (T < 0 || T > 0x7fffffff || n < 1 || n > 65536 || !(eps >= 0.0f)) return Q3MOE_E_SHAPE;
+    if (T == 0) return Q3MOE_OK;
+    if (!x || !gain || !out) return Q3MOE_E_NULL;
+    const size_t nb = (size_t)T * (size_t)n * sizeof(float);
+    if (x != out && overlaps(x, nb, out, nb)) return Q3MOE_E_ALIAS;
+    return from_hip(q3moe::launch_rmsnorm(x, T, n, gain, eps, out, as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,41 @@
+// Internal launchers shared between the C-ABI layer and the kernel files.
+// Every launcher assumes its arguments were validated by api.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace q3moe {
+
+struct ExpertTensor {
+    const uint8_t* base;
+    int32_t qtype;
+    int64_t stride;
+};
+
+constexpr int kMaxTopK = 32;
+constexpr int kMaxExperts = 1024;
+
+// route.hip
+size_t route_workspace_bytes(int64_t T, int32_t E);
+hipError_t launch_route(const float* hidden, int64_t T, int64_t H, const float* router,
+                        int32_t E, int32_t k, int32_t* idx, float* w, void* ws,
+                        hipStream_t stream);
+
+// ffn.hip
+size_t expert_ffn_workspace_bytes(int64_t T, int64_t H, int64_t F, int32_t E, int32_t k);
+hipError_t launch_expert_ffn(const float* hidden, int64_t T, int64_t H, int64_t F, int32_t E,
+                             int32_t k, const int32_t* idx, const float* w,
+                             const ExpertTensor& gate, const ExpertTensor& up,
+                             const ExpertTensor& down, float* out, int accumulate, void* ws,
+                             hipStream_t stream);
+
+// norm.hip
+hipError_t launch_rmsnorm(const float* x, int64_t T, int64_t n, const float* gain, float eps,
+                          float* out, hipStream_t stream);
+hipError_t launch_attn_prologue(float* q, float* k, int64_t T, int32_t nq, int32_t nkv,
+                                int32_t D, const float* qn, const float* kn,
+                                const int32_t* pos, float eps, float base, hipStream_t stream);
+
+}  // namespace q3moe

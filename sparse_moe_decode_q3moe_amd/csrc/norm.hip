@@ -1,0 +1,97 @@
+// RMSNorm and the fused attention prologue (per-head Q/K RMSNorm, then NEOX
+// RoPE).  Sources: aprender PR #1228 "The fix" (per-head norm with one gain
+// vector per projection, after the bias and before RoPE); SharpInference
+// issue #6 closing comment (NEOX pairing i <-> i + head_dim/2); aprender
+// issue #479 "Fix Applied" (head_dim explicit, not hidden/heads).
+#include "device_common.h"
+#include "internal.h"
+
+namespace q3moe {
+
+namespace {
+
+constexpr int kNormThreads = 256;
+
+// One workgroup per row: out = gain * x / sqrt(mean(x^2) + eps).
+__global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(const float* __restrict__ x,
+                                                               int64_t n,
+                                                               const float* __restrict__ gain,
+                                                               float eps, float* out) {
+    const int64_t t = blockIdx.x;
+    const int tid = threadIdx.x;
+    const float* xr = x + t * n;
+    __shared__ float part[kNormThreads / kWave];
+    float ss = 0.f;
+    for (int64_t i = tid; i < n; i += kNormThreads) ss = fmaf(xr[i], xr[i], ss);
+    ss = wave_sum(ss);
+    if ((tid & 63) == 0) part[tid >> 6] = ss;
+    __syncthreads();
+    const float tot = (part[0] + part[1]) + (part[2] + part[3]);
+    const float inv = 1.0f / sqrtf(tot / (float)n + eps);
+    for (int64_t i = tid; i < n; i += kNormThreads) out[t * n + i] = gain[i] * (xr[i] * inv);
+}
+
+// One wave per (token, head): lane i owns the NEOX pair (i, i + D/2) for
+// i = lane, lane + 64, ... < D/2.  RMSNorm over the whole head, then the
+// rotation by pos * base^(-2i/D), with the angle and its sine/cosine in
+// double precision (at position 4095 an f32 angle would carry ~2e-4 rad of
+// rounding error).
+constexpr int kMaxPairsPerLane = 4;   // head_dim <= 512
+
+__global__ __launch_bounds__(kWave) void attn_prologue_kernel(
+    float* q, float* k, int32_t nq, int32_t nkv, int32_t D, const float* __restrict__ qn,
+    const float* __restrict__ kn, const int32_t* __restrict__ pos, float eps, float base) {
+    const int h = blockIdx.y;
+    const int64_t t = blockIdx.x;
+    const int lane = threadIdx.x;
+    const bool isq = h < nq;
+    float* p = isq ? q + (t * nq + h) * (int64_t)D : k + (t * nkv + (h - nq)) * (int64_t)D;
+    const float* g = isq ? qn : kn;
+    const int half = D / 2;
+    float a[kMaxPairsPerLane], b[kMaxPairsPerLane];
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMaxPairsPerLane; ++j) {
+        const int i = lane + kWave * j;
+        a[j] = (i < half) ? p[i] : 0.f;
+        b[j] = (i < half) ? p[i + half] : 0.f;
+        ss = fmaf(a[j], a[j], fmaf(b[j], b[j], ss));
+    }
+    ss = wave_sum(ss);
+    const float inv = 1.0f / sqrtf(ss / (float)D + eps);
+    const double pd = (double)pos[t];
+    const double lb = log((double)base);
+#pragma unroll
+    for (int j = 0; j < kMaxPairsPerLane; ++j) {
+        const int i = lane + kWave * j;
+        if (i < half) {
+            const float ya = g[i] * (a[j] * inv);
+            const float yb = g[i + half] * (b[j] * inv);
+            const double theta = pd * exp(-2.0 * (double)i / (double)D * lb);
+            double sd, cd;
+            sincos(theta, &sd, &cd);
+            const float c = (float)cd, s = (float)sd;
+            p[i] = ya * c - yb * s;
+            p[i + half] = ya * s + yb * c;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_rmsnorm(const float* x, int64_t T, int64_t n, const float* gain, float eps,
+                          float* out, hipStream_t stream) {
+    hipLaunchKernelGGL(rmsnorm_kernel, dim3((unsigned)T), dim3(kNormThreads), 0, stream, x, n,
+                       gain, eps, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_prologue(float* q, float* k, int64_t T, int32_t nq, int32_t nkv,
+                                int32_t D, const float* qn, const float* kn, const int32_t* pos,
+                                float eps, float base, hipStream_t stream) {
+    hipLaunchKernelGGL(attn_prologue_kernel, dim3((unsigned)T, (unsigned)(nq + nkv)), dim3(kWave),
+                       0, stream, q, k, nq, nkv, D, qn, kn, pos, eps, base);
+    return hipGetLastError();
+}
+
+}  // namespace q3moe

@@ -1,0 +1,146 @@
+"""The C-ABI library on the host: it loads, exports every function that
+include/q3moe.h declares, reports the page-printed byte counts, and rejects
+bad arguments with a status code before any HIP call is made (so these
+tests need no GPU)."""
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+import sparse_moe_decode_q3moe_amd as q3
+from sparse_moe_decode_q3moe_amd import _lib
+
+ROOT = Path(__file__).resolve().parent.parent
+HEADER = ROOT / "include" / "q3moe.h"
+
+OK, E_NULL, E_SHAPE, E_QTYPE, E_ALIGN, E_WORKSPACE, E_HIP, E_ALIAS = range(8)
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
+    return sorted(set(re.findall(r"\b(q3moe_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return q3.library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) == 9, names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(_lib.EXPORTS) == names
+
+
+def test_byte_counts(lib):
+    assert lib.q3moe_qtype_block_bytes(q3.Q4_K) == 144
+    assert lib.q3moe_qtype_block_bytes(q3.Q6_K) == 210
+    assert lib.q3moe_qtype_block_bytes(7) == 0
+    assert lib.q3moe_expert_matrix_bytes(q3.Q4_K, 768, 2048) == 884736
+    assert lib.q3moe_expert_matrix_bytes(q3.Q6_K, 2048, 768) == 1290240
+    assert lib.q3moe_expert_matrix_bytes(q3.Q4_K, 2048, 768) == 884736
+    assert lib.q3moe_expert_matrix_bytes(q3.Q4_K, 2, 100) == -1
+    assert lib.q3moe_route_workspace_bytes(3, 128) == 3 * 128 * 8
+    ws = lib.q3moe_expert_ffn_workspace_bytes(5, 2048, 768, 128, 8)
+    assert ws >= 5 * 8 * 768 * 4 and ws % 256 == 0
+    for s in range(8):
+        assert lib.q3moe_status_string(s)
+
+
+FAKE = ctypes.c_void_p(0x10000)          # aligned, never dereferenced: validation fails first
+FAKE_MIS = ctypes.c_void_p(0x10004)
+
+
+def _experts(base=FAKE, qtype=q3.Q4_K, stride=884736, reserved=0):
+    return _lib._Experts(base.value if base else None, qtype, reserved, stride)
+
+
+def _ffn(lib, T=1, H=2048, F=768, E=128, k=8, hidden=FAKE, idx=FAKE, w=FAKE,
+         gate=None, up=None, down=None, out=ctypes.c_void_p(0x40000), acc=0, ws=FAKE,
+         ws_bytes=1 << 30):
+    gate = gate or _experts()
+    up = up or _experts()
+    down = down or _experts(qtype=q3.Q6_K, stride=1290240)
+    return lib.q3moe_expert_ffn(hidden, T, H, F, E, k, idx, w, gate, up, down, out, acc, ws,
+                                ws_bytes, None)
+
+
+def test_expert_ffn_validation(lib):
+    assert _ffn(lib, T=0) == OK                            # nothing to do, nothing enqueued
+    assert _ffn(lib, H=2000) == E_SHAPE
+    assert _ffn(lib, F=700) == E_SHAPE
+    assert _ffn(lib, H=8192) == E_SHAPE
+    assert _ffn(lib, k=0) == E_SHAPE
+    assert _ffn(lib, k=33, E=64) == E_SHAPE
+    assert _ffn(lib, k=9, E=8) == E_SHAPE
+    assert _ffn(lib, acc=2) == E_SHAPE
+    assert _ffn(lib, hidden=None) == E_NULL
+    assert _ffn(lib, out=None) == E_NULL
+    assert _ffn(lib, gate=_experts(base=None)) == E_NULL
+    assert _ffn(lib, gate=_experts(qtype=q3.Q6_K, stride=1 << 21)) == E_QTYPE
+    assert _ffn(lib, down=_experts(qtype=9, stride=1 << 21)) == E_QTYPE
+    assert _ffn(lib, gate=_experts(base=FAKE_MIS)) == E_ALIGN
+    assert _ffn(lib, gate=_experts(stride=884736 + 8)) == E_ALIGN
+    assert _ffn(lib, gate=_experts(stride=884736 - 16)) == E_SHAPE
+    assert _ffn(lib, down=_experts(qtype=q3.Q6_K, stride=884736)) == E_SHAPE
+    assert _ffn(lib, gate=_experts(reserved=1)) == E_SHAPE
+    assert _ffn(lib, hidden=FAKE_MIS) == E_ALIGN
+    assert _ffn(lib, out=ctypes.c_void_p(0x10000 + 4096)) == E_ALIAS
+    assert _ffn(lib, ws=None) == E_WORKSPACE
+    assert _ffn(lib, ws_bytes=100) == E_WORKSPACE
+    assert _ffn(lib, ws=FAKE_MIS) == E_ALIGN
+
+
+def _route(lib, T=1, H=2048, E=128, k=8, hidden=FAKE, router=FAKE, idx=FAKE, w=FAKE, ws=FAKE,
+           ws_bytes=1 << 20):
+    return lib.q3moe_route(hidden, T, H, router, E, k, idx, w, ws, ws_bytes, None)
+
+
+def test_route_validation(lib):
+    assert _route(lib, T=0) == OK
+    assert _route(lib, T=-1) == E_SHAPE
+    assert _route(lib, k=0) == E_SHAPE
+    assert _route(lib, k=33, E=64) == E_SHAPE
+    assert _route(lib, E=1025, k=8) == E_SHAPE
+    assert _route(lib, k=9, E=8) == E_SHAPE
+    assert _route(lib, H=2046) == E_SHAPE
+    assert _route(lib, router=None) == E_NULL
+    assert _route(lib, idx=None) == E_NULL
+    assert _route(lib, hidden=FAKE_MIS) == E_ALIGN
+    assert _route(lib, ws=None) == E_WORKSPACE
+    assert _route(lib, T=4, ws_bytes=4 * 128 * 8 - 1) == E_WORKSPACE
+
+
+def test_prologue_and_rmsnorm_validation(lib):
+    P = lib.q3moe_attn_prologue
+    q, k = FAKE, ctypes.c_void_p(0x10000 + (1 << 20))
+    args = dict(T=1, nq=32, nkv=4, D=128)
+
+    def pro(T=1, nq=32, nkv=4, D=128, qp=q, kp=k, qn=FAKE, kn=FAKE, pos=FAKE, eps=1e-6, base=1e7):
+        return P(qp, kp, T, nq, nkv, D, qn, kn, pos, eps, base, None)
+
+    assert pro(T=0) == OK
+    assert pro(D=127) == E_SHAPE
+    assert pro(D=514) == E_SHAPE
+    assert pro(nq=30, nkv=4) == E_SHAPE
+    assert pro(eps=-1.0) == E_SHAPE
+    assert pro(base=0.0) == E_SHAPE
+    assert pro(qn=None) == E_NULL
+    assert pro(pos=None) == E_NULL
+    assert pro(kp=ctypes.c_void_p(0x10000 + 1024)) == E_ALIAS
+    R = lib.q3moe_rmsnorm
+    assert R(FAKE, 0, 2048, FAKE, 1e-6, FAKE, None) == OK
+    assert R(FAKE, 1, 0, FAKE, 1e-6, FAKE, None) == E_SHAPE
+    assert R(FAKE, 1, 2048, None, 1e-6, FAKE, None) == E_NULL
+    assert R(FAKE, 2, 2048, FAKE, 1e-6, ctypes.c_void_p(0x10000 + 64), None) == E_ALIAS
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    x = torch.zeros(1, 256)
+    r = torch.zeros(8, 256)
+    with pytest.raises(ValueError):
+        q3.q3moe_route(x, r, 2)

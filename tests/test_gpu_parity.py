@@ -1,0 +1,240 @@
+"""HIP path vs the CPU oracle, element by element on the same seeded inputs.
+
+Indices bit-exact; f32 outputs within 1e-4 relative L2 per token.  Shapes
+span the tiny layer, the Qwen3-30B-A3B decode layer at full size (all 128
+experts resident, the launch configuration the benchmark times), batched
+and ragged token counts, the Q4_K-down layers of the 48-layer stack, the
+maximum supported sizes and the degenerate cases (T = 0, k = 1, k = E,
+E = 1, an out-of-range expert index, padded expert strides).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_moe_decode_q3moe_amd as q3
+from sparse_moe_decode_q3moe_amd import inputs as gen
+from parity import (assert_indices_equal, assert_rows_close, experts_of, gpu_moe, oracle_moe,
+                    oracle_tensors, say)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device visible")
+    q3.library()
+
+
+# ------------------------------------------------------------------ route --
+
+ROUTE_CASES = [  # (T, H, E, k, seed)
+    (4, 256, 8, 2, 1),        # tiny layer
+    (1, 2048, 128, 8, 2),     # 30B-A3B decode
+    (16, 2048, 128, 8, 3),    # batch 16
+    (13, 2048, 128, 8, 4),    # ragged
+    (5, 2048, 128, 1, 5),     # k = 1
+    (3, 256, 8, 8, 6),        # k = E
+    (7, 2052, 100, 6, 7),     # E not a multiple of 64, H not a multiple of 256
+    (600, 2048, 128, 8, 8),   # more tokens than one token tile
+]
+
+
+@pytest.mark.parametrize("T,H,E,k,seed", ROUTE_CASES)
+def test_route_parity(T, H, E, k, seed):
+    say(f"route T={T} H={H} E={E} k={k} seed={seed}")
+    g = gen.make_generator(seed)
+    x = gen.normal_f32((T, H), 1.0, g)
+    R = gen.normal_f32((E, H), 0.02, g)
+    ref_idx, ref_w, logits = oracle.oracle().route(x.numpy(), R.numpy(), k)
+    idx, w = q3.q3moe_route(x.to(DEV), R.to(DEV), k)
+    torch.cuda.synchronize()
+    assert_indices_equal(idx.cpu().numpy(), ref_idx, logits, k, "route")
+    np.testing.assert_allclose(w.cpu().numpy(), ref_w, rtol=1e-6, atol=0)
+
+
+def test_route_ties_take_lower_index():
+    say("route ties")
+    g = gen.make_generator(9)
+    x = gen.normal_f32((2, 512), 1.0, g)
+    R = gen.normal_f32((32, 512), 0.02, g)
+    R[[5, 9, 30]] = 0.01 * torch.sign(x[0])
+    idx, w = q3.q3moe_route(x.to(DEV), R.to(DEV), 4)
+    ref_idx, ref_w, _ = oracle.oracle().route(x.numpy(), R.numpy(), 4)
+    assert idx.cpu().numpy()[0, :3].tolist() == [5, 9, 30]
+    assert np.array_equal(idx.cpu().numpy(), ref_idx)
+
+
+# ------------------------------------------------------------- expert FFN --
+
+FFN_CASES = {  # name: (shape, seed)
+    "tiny_T4": (gen.TINY, 11),
+    "a3b_decode_T1": (gen.QWEN3_30B_A3B, 12),
+    "a3b_batch_T16": (gen.MoeShape(T=16, H=2048, E=128, k=8, F=768, down_qtype=gen.Q6_K), 13),
+    "a3b_q4k_down_T3": (gen.MoeShape(T=3, H=2048, E=128, k=8, F=768, down_qtype=gen.Q4_K), 14),
+    "ragged_q6k_F512": (gen.MoeShape(T=5, H=256, E=6, k=3, F=512, down_qtype=gen.Q6_K), 15),
+    "max_H4096_F1536": (gen.MoeShape(T=2, H=4096, E=4, k=2, F=1536, down_qtype=gen.Q6_K), 16),
+    "k32": (gen.MoeShape(T=2, H=256, E=32, k=32, F=256, down_qtype=gen.Q6_K), 17),
+    "k_equals_E": (gen.MoeShape(T=3, H=512, E=4, k=4, F=256, down_qtype=gen.Q4_K), 18),
+    "single_expert": (gen.MoeShape(T=2, H=512, E=1, k=1, F=256, down_qtype=gen.Q6_K), 19),
+}
+
+
+@pytest.fixture(scope="module")
+def layers():
+    cache = {}
+
+    def get(name):
+        if name not in cache:
+            shape, seed = FFN_CASES[name]
+            cpu = gen.moe_layer(shape, seed)
+            x = gen.hidden_states(shape.T, shape.H, seed + 500)
+            cache[name] = (cpu, cpu.to(DEV), x)
+        return cache[name]
+    return get
+
+
+@pytest.mark.parametrize("name", list(FFN_CASES))
+def test_moe_block_parity(layers, name):
+    cpu, dev, x = layers(name)
+    s = cpu.shape
+    say(f"moe block {name}: T={s.T} H={s.H} E={s.E} k={s.k} F={s.F} down={s.down_qtype}")
+    ref_idx, ref_w, logits, ref = oracle_moe(cpu, x.numpy())
+    idx, w, out = gpu_moe(dev, x.to(DEV))
+    torch.cuda.synchronize()
+    assert_indices_equal(idx.cpu().numpy(), ref_idx, logits, s.k, name)
+    err = assert_rows_close(out.cpu().numpy(), ref, what=name)
+    say(f"  max rel L2 {err:.2e}")
+
+
+@pytest.mark.parametrize("name", ["tiny_T4", "a3b_decode_T1", "a3b_q4k_down_T3"])
+def test_accumulate_adds_to_out(layers, name):
+    cpu, dev, x = layers(name)
+    s = cpu.shape
+    say(f"accumulate {name}")
+    prev = (x * 100.0).contiguous()
+    _, _, _, ref = oracle_moe(cpu, x.numpy(), out=prev.numpy(), accumulate=True)
+    out = prev.to(DEV)
+    gpu_moe(dev, x.to(DEV), out=out, accumulate=True)
+    torch.cuda.synchronize()
+    assert_rows_close(out.cpu().numpy(), ref, what=f"{name} accumulate")
+
+
+def test_expert_ffn_given_routing(layers):
+    """Fixed routing (including repeated experts within a token) through the
+    FFN entry point alone."""
+    cpu, dev, x = layers("a3b_batch_T16")
+    s = cpu.shape
+    say("expert ffn with fixed routing")
+    g = gen.make_generator(21)
+    idx = torch.randint(0, s.E, (s.T, s.k), generator=g, dtype=torch.int32)
+    idx[0, :] = 7                                  # the same expert in every slot
+    w = torch.rand((s.T, s.k), generator=g)
+    ref = oracle.oracle().expert_ffn(x.numpy(), idx.numpy(), w.numpy(), *oracle_tensors(cpu),
+                                     F=s.F, E=s.E)
+    out = q3.q3moe_expert_ffn(x.to(DEV), idx.to(DEV), w.to(DEV), *experts_of(dev), F=s.F)
+    torch.cuda.synchronize()
+    assert_rows_close(out.cpu().numpy(), ref, what="fixed routing")
+
+
+def test_out_of_range_index_contributes_zero(layers):
+    cpu, dev, x = layers("tiny_T4")
+    s = cpu.shape
+    say("out-of-range expert index")
+    o = oracle.oracle()
+    idx, w, _ = o.route(x.numpy(), cpu.router.numpy(), s.k)
+    bad = idx.copy()
+    bad[1, 1] = s.E + 3
+    bad[2, 0] = -1
+    w0 = w.copy()
+    w0[1, 1] = 0.0
+    w0[2, 0] = 0.0
+    ref = o.expert_ffn(x.numpy(), idx, w0, *oracle_tensors(cpu), F=s.F, E=s.E)
+    out = q3.q3moe_expert_ffn(x.to(DEV), torch.from_numpy(bad).to(DEV),
+                              torch.from_numpy(w).to(DEV), *experts_of(dev), F=s.F)
+    torch.cuda.synchronize()
+    assert_rows_close(out.cpu().numpy(), ref, what="invalid index")
+
+
+def test_padded_expert_stride(layers):
+    cpu, dev, x = layers("ragged_q6k_F512")
+    s = cpu.shape
+    say("padded expert strides")
+    pad = lambda t: torch.cat([t, torch.full((t.shape[0], 272), 0xAB, dtype=torch.uint8)], 1)
+    padded = gen.MoeLayer(s, cpu.router, pad(cpu.gate), pad(cpu.up), pad(cpu.down))
+    _, _, _, ref = oracle_moe(cpu, x.numpy())
+    _, _, out = gpu_moe(padded.to(DEV), x.to(DEV))
+    torch.cuda.synchronize()
+    assert_rows_close(out.cpu().numpy(), ref, what="padded stride")
+
+
+def test_zero_tokens_is_a_no_op(layers):
+    cpu, dev, x = layers("tiny_T4")
+    s = cpu.shape
+    say("T = 0")
+    empty = torch.empty((0, s.H), device=DEV)
+    idx, w = q3.q3moe_route(empty, dev.router, s.k)
+    out = q3.q3moe_expert_ffn(empty, idx, w, *experts_of(dev), F=s.F)
+    torch.cuda.synchronize()
+    assert out.shape == (0, s.H) and idx.shape == (0, s.k)
+
+
+def test_bitwise_repeatable(layers):
+    cpu, dev, x = layers("a3b_decode_T1")
+    say("repeatability")
+    xd = x.to(DEV)
+    a = gpu_moe(dev, xd)[2].clone()
+    b = gpu_moe(dev, xd)[2].clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+# -------------------------------------------------------- norm / prologue --
+
+PROLOGUE_CASES = [  # (T, n_q, n_kv, D, max_pos)
+    (1, 32, 4, 128, 4096),     # Qwen3-30B-A3B decode, position 4095
+    (16, 32, 4, 128, 4096),    # batch 16
+    (3, 32, 8, 128, 40960),    # Qwen3-4B head layout (head_dim 128 != 2560/32)
+    (5, 8, 2, 64, 1000),
+    (2, 4, 4, 256, 100000),
+    (2, 2, 1, 512, 7),
+    (1, 1, 1, 2, 3),
+]
+
+
+@pytest.mark.parametrize("T,nq,nkv,D,max_pos", PROLOGUE_CASES)
+def test_attn_prologue_parity(T, nq, nkv, D, max_pos):
+    say(f"prologue T={T} nq={nq} nkv={nkv} D={D}")
+    g = gen.make_generator(31 + D + T)
+    q = gen.normal_f32((T, nq, D), 1.0, g)
+    k = gen.normal_f32((T, nkv, D), 3.0, g)
+    qn = gen.uniform_f32((D,), 0.5, 1.5, g)
+    kn = gen.uniform_f32((D,), 0.5, 1.5, g)
+    pos = torch.randint(0, max_pos, (T,), generator=g, dtype=torch.int32)
+    pos[0] = max_pos - 1
+    rq, rk = oracle.oracle().attn_prologue(q.numpy(), k.numpy(), qn.numpy(), kn.numpy(),
+                                           pos.numpy(), 1e-6, 1e7)
+    qd, kd = q.to(DEV), k.to(DEV)
+    q3.q3moe_attn_prologue(qd, kd, qn.to(DEV), kn.to(DEV), pos.to(DEV), 1e-6, 1e7)
+    torch.cuda.synchronize()
+    assert_rows_close(qd.cpu().numpy().reshape(T * nq, D), rq.reshape(T * nq, D), what="q")
+    assert_rows_close(kd.cpu().numpy().reshape(T * nkv, D), rk.reshape(T * nkv, D), what="k")
+
+
+@pytest.mark.parametrize("T,n", [(1, 2048), (16, 2048), (3, 2560), (4, 100)])
+def test_rmsnorm_parity(T, n):
+    say(f"rmsnorm T={T} n={n}")
+    g = gen.make_generator(41 + n)
+    x = gen.normal_f32((T, n), 50.0, g)
+    gain = gen.uniform_f32((n,), 0.5, 1.5, g)
+    ref = oracle.oracle().rmsnorm(x.numpy(), gain.numpy(), 1e-6)
+    out = q3.q3moe_rmsnorm(x.to(DEV), gain.to(DEV), 1e-6)
+    torch.cuda.synchronize()
+    assert_rows_close(out.cpu().numpy(), ref, what="rmsnorm")
+    xi = x.to(DEV)
+    q3.q3moe_rmsnorm(xi, gain.to(DEV), 1e-6, out=xi)      # in place
+    torch.cuda.synchronize()
+    assert_rows_close(xi.cpu().numpy(), ref, what="rmsnorm in place")
