@@ -81,7 +81,7 @@ def main():
     idx = torch.empty((GRAPH_STEPS, 1, k), dtype=torch.int32, device=dev)
     wts = torch.empty((GRAPH_STEPS, 1, k), dtype=torch.float32, device=dev)
     outs = torch.empty((GRAPH_STEPS, 1, H), dtype=torch.float32, device=dev)
-    ws_route = torch.empty(q3.q3moe_route_workspace_bytes(1, E), dtype=torch.uint8, device=dev)
+    ws_route = torch.zeros(q3.q3moe_route_workspace_bytes(1, E), dtype=torch.uint8, device=dev)
     ws_ffn = torch.empty(q3.q3moe_expert_ffn_workspace_bytes(1, H, F, E, k), dtype=torch.uint8,
                          device=dev)
 
@@ -182,7 +182,7 @@ def main():
         "wall_s_timed_region": round(wall, 4),
         "roofline": {
             "bound": "hbm",
-            "kernel": "expert FFN (q3moe_expert_ffn: gate/up+SwiGLU kernel, down+combine kernel)",
+            "kernel": "expert FFN (q3moe_expert_ffn: one persistent kernel, ffn_fused8_kernel)",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

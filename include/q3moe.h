@@ -95,7 +95,14 @@ int64_t q3moe_expert_matrix_bytes(int32_t qtype, int64_t rows, int64_t cols);
  * against summation order (the near-tie risk named in "Risk to track").
  * Limits: 1 <= k <= 32, k <= E <= 1024, 1 <= H.
  * workspace: device memory of at least q3moe_route_workspace_bytes(T, E)
- * bytes, 16-byte aligned; contents need no initialisation.
+ * bytes, 16-byte aligned.  Its first 4 KiB hold completion counters and
+ * must be zero before the first call that uses the workspace (e.g. one
+ * hipMemset after allocation); every call leaves them zero again, so the
+ * workspace can be reused by later calls of any size on the same stream.
+ * Calls that overlap in time (different streams) need different workspaces.
+ * For T <= 8 the whole route is one kernel: each workgroup computes one
+ * expert's logits and the last one to finish selects the top-k (nothing
+ * waits on another workgroup).
  * Errors: E_NULL, E_SHAPE, E_ALIGN, E_WORKSPACE, E_HIP. */
 size_t q3moe_route_workspace_bytes(int64_t T, int32_t E);
 q3moe_status q3moe_route(const float *hidden, int64_t T, int64_t H,
@@ -124,10 +131,23 @@ q3moe_status q3moe_route(const float *hidden, int64_t T, int64_t H,
  * Limits: H % 256 == 0, F % 256 == 0, 256 <= H <= 4096, 256 <= F <= 1536,
  * 1 <= k <= 32, k <= E.
  * workspace: at least q3moe_expert_ffn_workspace_bytes(T, H, F, E, k)
- * bytes, 16-byte aligned, contents need no initialisation.
+ * bytes, 16-byte aligned.  Its first 8 KiB hold synchronisation words
+ * and must be zero before the first call that uses the workspace (e.g. one
+ * hipMemset after allocation); every call leaves its counters at zero
+ * again, so a workspace can be reused by later calls of any size on the
+ * same stream.  Calls that overlap in time (different streams) need
+ * different workspaces.
+ * For small T the library runs the whole FFN as one persistent kernel with
+ * at most one workgroup per compute unit, whose down-projection waves wait
+ * on counters in the workspace; each wait is bounded.  The int32 at byte
+ * offset q3moe_expert_ffn_status_offset(...) of the workspace is a sticky
+ * status word: it stays 0 unless a bounded wait ran out, in which case that
+ * call's output is invalid.
  * Errors: E_NULL, E_SHAPE, E_QTYPE, E_ALIGN, E_WORKSPACE, E_ALIAS, E_HIP. */
 size_t q3moe_expert_ffn_workspace_bytes(int64_t T, int64_t H, int64_t F,
                                         int32_t E, int32_t top_k);
+size_t q3moe_expert_ffn_status_offset(int64_t T, int64_t H, int64_t F,
+                                      int32_t E, int32_t top_k);
 q3moe_status q3moe_expert_ffn(const float *hidden, int64_t T, int64_t H, int64_t F,
                               int32_t E, int32_t top_k,
                               const int32_t *topk_idx, const float *topk_w,

@@ -21,7 +21,7 @@ Q4_K, Q6_K = 1, 2
 EXPORTS = (
     "q3moe_status_string", "q3moe_qtype_block_bytes", "q3moe_expert_matrix_bytes",
     "q3moe_route_workspace_bytes", "q3moe_route",
-    "q3moe_expert_ffn_workspace_bytes", "q3moe_expert_ffn",
+    "q3moe_expert_ffn_workspace_bytes", "q3moe_expert_ffn_status_offset", "q3moe_expert_ffn",
     "q3moe_attn_prologue", "q3moe_rmsnorm",
 )
 
@@ -45,6 +45,7 @@ _SIGS = {
     "q3moe_route_workspace_bytes": (ctypes.c_size_t, [_I64, _I32]),
     "q3moe_route": (_I32, [_P, _I64, _I64, _P, _I32, _I32, _P, _P, _P, ctypes.c_size_t, _P]),
     "q3moe_expert_ffn_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64, _I32, _I32]),
+    "q3moe_expert_ffn_status_offset": (ctypes.c_size_t, [_I64, _I64, _I64, _I32, _I32]),
     "q3moe_expert_ffn": (_I32, [_P, _I64, _I64, _I64, _I32, _I32, _P, _P, _Experts, _Experts,
                                 _Experts, _P, _I32, _P, ctypes.c_size_t, _P]),
     "q3moe_attn_prologue": (_I32, [_P, _P, _I64, _I32, _I32, _I32, _P, _P, _P, _F, _F, _P]),
@@ -110,9 +111,10 @@ class Experts(NamedTuple):
 
 
 def _workspace(nbytes: int, device, given: Optional[torch.Tensor]) -> torch.Tensor:
+    """A caller-provided workspace, or a fresh zero-filled one."""
     if given is not None:
         return given
-    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+    return torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=device)
 
 
 def q3moe_route_workspace_bytes(T: int, E: int) -> int:
@@ -146,6 +148,17 @@ def q3moe_route(hidden: torch.Tensor, router: torch.Tensor, top_k: int,
 
 def q3moe_expert_ffn_workspace_bytes(T: int, H: int, F: int, E: int, top_k: int) -> int:
     return library().q3moe_expert_ffn_workspace_bytes(T, H, F, E, top_k)
+
+
+def q3moe_expert_ffn_status_offset(T: int, H: int, F: int, E: int, top_k: int) -> int:
+    return library().q3moe_expert_ffn_status_offset(T, H, F, E, top_k)
+
+
+def expert_ffn_status(workspace: torch.Tensor, T: int, H: int, F: int, E: int, top_k: int) -> int:
+    """The status word an expert-FFN call left in its workspace (0 = ok).
+    Synchronises with the device."""
+    off = q3moe_expert_ffn_status_offset(T, H, F, E, top_k)
+    return int(workspace[off:off + 4].view(torch.int32).item())
 
 
 def q3moe_expert_ffn(hidden: torch.Tensor, topk_idx: torch.Tensor, topk_w: torch.Tensor,

@@ -87,6 +87,10 @@ size_t q3moe_expert_ffn_workspace_bytes(int64_t T, int64_t H, int64_t F, int32_t
     return q3moe::expert_ffn_workspace_bytes(T, H, F, E, top_k);
 }
 
+size_t q3moe_expert_ffn_status_offset(int64_t T, int64_t H, int64_t F, int32_t E, int32_t top_k) {
+    return q3moe::expert_ffn_status_offset(T, H, F, E, top_k);
+}
+
 q3moe_status q3moe_expert_ffn(const float* hidden, int64_t T, int64_t H, int64_t F, int32_t E,
                               int32_t top_k, const int32_t* topk_idx, const float* topk_w,
                               q3moe_experts gate, q3moe_experts up, q3moe_experts down,

@@ -119,4 +119,104 @@ __device__ __forceinline__ float q6k_unit_dot(const uint8_t* lds, int boff, int 
     return d * (float)sc * (sq - 32.f * sx);
 }
 
+// ---------------------------------------------------------------------------
+// Activation pieces.  The decode kernels multiply k-quant weights, which are
+// small integers once the per-block scales are factored out, by activations
+// split into two bf16 pieces, x = hi + lo (hi = bf16(x), lo = bf16(x - hi),
+// both round-to-nearest-even; |x - hi - lo| <= 2^-18 |x|).  A weight q is
+// exact as the bf16 value 128 + q (q < 128), so v_dot2_f32_bf16 forms
+// sum (128 + q)(hi + lo) with exact products; the 128 offset is removed with
+// the per-16 group sums of hi + lo.
+//
+// Layout of a vector of K values (K a multiple of 256): slot s holds values
+// 4s..4s+3 in 16 bytes:
+//   dword 0 = hi(4s)   | hi(4s+2) << 16     dword 2 = lo(4s)   | lo(4s+2) << 16
+//   dword 1 = hi(4s+1) | hi(4s+3) << 16     dword 3 = lo(4s+1) | lo(4s+3) << 16
+// which matches the weight pairs (w & 0x000F000F) / (w >> 8 & 0x000F000F)
+// taken from a dword of four consecutive quant bytes.  In global memory the
+// slots are contiguous (K*4 bytes); in LDS every 64 slots (one 256-value
+// super-block) are followed by 16 bytes of padding so that lanes reading
+// the same slot of different blocks hit different banks.
+constexpr int kSlotBytes = 16;
+constexpr int kBlockPieceStride = 64 * kSlotBytes + 16;   // 1040 bytes per 256 values in LDS
+
+__device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
+    const uint32_t u = __float_as_uint(x);
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t b) { return __uint_as_float(b << 16); }
+
+struct Pieces4 {
+    uint4 slot;     // the 16-byte slot
+    float sum;      // (hi + lo) summed over the 4 values
+};
+
+__device__ __forceinline__ Pieces4 make_pieces4(float4 v) {
+    const float x[4] = {v.x, v.y, v.z, v.w};
+    uint32_t hb[4], lb[4];
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        hb[i] = bf16_rne_bits(x[i]);
+        const float r = x[i] - bf16_bits_to_float(hb[i]);
+        lb[i] = bf16_rne_bits(r);
+        s += bf16_bits_to_float(hb[i]) + bf16_bits_to_float(lb[i]);
+    }
+    Pieces4 p;
+    p.slot = make_uint4(hb[0] | (hb[2] << 16), hb[1] | (hb[3] << 16), lb[0] | (lb[2] << 16),
+                        lb[1] | (lb[3] << 16));
+    p.sum = s;
+    return p;
+}
+
+__device__ __forceinline__ float slot_sum(uint4 s) {
+    auto f = [](uint32_t w) { return bf16_bits_to_float(w & 0xffffu) + bf16_bits_to_float(w >> 16); };
+    return (f(s.x) + f(s.y)) + (f(s.z) + f(s.w));
+}
+
+// LDS byte offset of slot s in the padded layout.
+__device__ __forceinline__ int piece_slot_off(int s) { return (s >> 6) * kBlockPieceStride + (s & 63) * kSlotBytes; }
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// ---------------------------------------------------------------------------
+// Direct HBM -> LDS copy by one wave (gfx950 global_load_lds_dwordx4): lane i
+// of each 1 KiB step moves bytes [16i, 16i+16) of that step; nbytes must be a
+// multiple of 16 and both addresses 16-byte aligned.  The loads are only
+// issued here; the caller waits (s_waitcnt vmcnt) before reading the LDS.
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ void wave_copy_to_lds(uint8_t* lds, const uint8_t* __restrict__ g,
+                                                 int nbytes, int lane) {
+    const int n16 = nbytes >> 4;
+    for (int base = 0; base < n16; base += kWave) {
+        if (base + lane < n16)
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(g + (base + lane) * 16),
+                                             (lds_ptr_t)(lds + base * 16), 16, 0, 0);
+    }
+}
+
+// The same with device-scope coherent loads (sc1): they bypass the per-XCD
+// L2, so they see data that another XCD wrote with device-scope stores
+// without an L2 invalidate.
+constexpr int kCachePolicySc1 = 16;
+
+__device__ __forceinline__ void wave_copy_to_lds_coherent(uint8_t* lds, const uint8_t* g,
+                                                          int nbytes, int lane) {
+    const int n16 = nbytes >> 4;
+    for (int base = 0; base < n16; base += kWave) {
+        if (base + lane < n16)
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(g + (base + lane) * 16),
+                                             (lds_ptr_t)(lds + base * 16), 16, 0, kCachePolicySc1);
+    }
+}
+
+__device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0); }
+
 }  // namespace q3moe

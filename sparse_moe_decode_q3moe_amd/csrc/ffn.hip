@@ -1,6 +1,8 @@
 // Sparse expert FFN on k-quant weights read in place (aprender issue #3714,
 // gap G3 and "File facts": expert e at base + e*stride, gate/up Q4_K, down
-// Q6_K or Q4_K per layer).  Two kernels:
+// Q6_K or Q4_K per layer).  launch_expert_ffn sends hidden sizes that are a
+// power-of-two number of super-blocks (up to 16) to the decode kernels in
+// ffn_decode.hip; every other shape runs the generic pair of kernels here:
 //   gateup: per (token, slot) pair and 8-row tile, g = Wg[e] x and u = Wu[e] x
 //           for the same 8 rows, then h = silu(g) * u into the workspace;
 //   down:   per (token, 8 output rows), y_s = Wd[e_s] h_s for every slot and
@@ -145,8 +147,19 @@ size_t down_lds(int64_t F, int32_t qtype) {
 size_t expert_ffn_workspace_bytes(int64_t T, int64_t H, int64_t F, int32_t E, int32_t k) {
     (void)H;
     (void)E;
-    const size_t h = (size_t)(T > 0 ? T : 0) * (size_t)k * (size_t)F * sizeof(float);
-    return (h + 255) & ~(size_t)255;
+    const int64_t t = T > 0 ? T : 0;
+    // synchronisation words, then h (f32 or activation pieces, 4 bytes/value)
+    const size_t h = (size_t)t * (size_t)k * (size_t)F * sizeof(float);
+    return kFfnSyncBytes + ((h + 255) & ~(size_t)255);
+}
+
+size_t expert_ffn_status_offset(int64_t T, int64_t H, int64_t F, int32_t E, int32_t k) {
+    (void)T;
+    (void)H;
+    (void)F;
+    (void)E;
+    (void)k;
+    return 0;
 }
 
 hipError_t launch_expert_ffn(const float* hidden, int64_t T, int64_t H, int64_t F, int32_t E,
@@ -154,7 +167,10 @@ hipError_t launch_expert_ffn(const float* hidden, int64_t T, int64_t H, int64_t 
                              const ExpertTensor& gate, const ExpertTensor& up,
                              const ExpertTensor& down, float* out, int accumulate, void* ws,
                              hipStream_t stream) {
-    float* hbuf = static_cast<float*>(ws);
+    if (decode_ffn_supported(H, F, k))
+        return launch_decode_ffn(hidden, T, H, F, E, k, idx, w, gate, up, down, out, accumulate, ws,
+                                 stream);
+    float* hbuf = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kFfnSyncBytes);
     const size_t l1 = gateup_lds(H), l2 = down_lds(F, down.qtype);
     hipError_t err;
     if (l1 > 65536 &&

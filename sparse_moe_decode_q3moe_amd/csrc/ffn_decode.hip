@@ -1,0 +1,950 @@
+// Expert FFN for decode-sized batches (aprender issue #3714: "File facts"
+// fixes the expert layout, gap G3 the steps, G8 the device-side gather and
+// weighted accumulate).  Two kernels per call:
+//
+//   gu_decode_kernel   one wave per task = (token-slot pair, R rows of the
+//                      selected expert's gate AND up matrices): direct
+//                      HBM->LDS loads of both R-row tiles, dequantise in
+//                      registers, h = silu(g) * u written as activation
+//                      pieces for the down kernel.
+//   down_decode_kernel one workgroup per (token, 8 output rows): every wave
+//                      loads the 8-row tiles of two slots' down matrices and
+//                      those slots' h pieces, dequantises, multiplies by the
+//                      routing weight, and the workgroup sums the slots in
+//                      slot order (deterministic, no atomics).
+//
+// Weights are never repacked: tiles are read in place at base + e*stride
+// with 16-byte coalesced direct-to-LDS loads, all issued before any wait.
+// Arithmetic: weights as exact small integers (bf16 128 + q), activations as
+// bf16 hi + lo pieces, v_dot2_f32_bf16 with f32 accumulation; the per-block
+// scales, the Q4_K min term and the integer offsets are applied per 16/32
+// group in f32.
+#include <atomic>
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace q3moe {
+
+namespace {
+
+constexpr int kGuWaves = 4;
+constexpr int kDnWaves = 4;
+constexpr int kDnRows = 8;          // output rows per down workgroup
+constexpr int kDnSlotsPerWave = 2;  // lanes 0-31 one slot, lanes 32-63 the next
+constexpr uint32_t kBf16Bias = 0x43004300u;   // bf16 128.0 in both halves
+
+__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z)); }
+
+__device__ __forceinline__ void store_h_piece(uint8_t* __restrict__ hp, int64_t value_index,
+                                              float h) {
+    // value i lives in slot i/4 at half-word (i%4 == 0: 0, 1: 2, 2: 1, 3: 3) of
+    // the hi pair dwords, and the same half-word of the lo pair dwords (+8 B)
+    const uint32_t hb = bf16_rne_bits(h);
+    const uint32_t lb = bf16_rne_bits(h - bf16_bits_to_float(hb));
+    const int pos = (int)(value_index & 3);
+    const int hw = ((pos & 1) << 1) | (pos >> 1);
+    uint16_t* slot = reinterpret_cast<uint16_t*>(hp + (value_index >> 2) * kSlotBytes);
+    // device-scope stores write through the per-XCD L2, so a down wave on
+    // any XCD that later reads them with coherent loads sees them
+    __hip_atomic_store(slot + hw, (uint16_t)hb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(slot + 4 + hw, (uint16_t)lb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// A whole slot (values i..i+3, i a multiple of 4) with device-scope stores.
+__device__ __forceinline__ void store_h_slot(uint8_t* __restrict__ hp, int64_t value_index,
+                                             uint4 slot) {
+    uint32_t* d = reinterpret_cast<uint32_t*>(hp + (value_index >> 2) * kSlotBytes);
+    __hip_atomic_store(d + 0, slot.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(d + 1, slot.y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(d + 2, slot.z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(d + 3, slot.w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Q4_K scale and min of sub-block j (compile-time j) from the three dwords
+// holding the 12 packed bytes.
+template <int J>
+__device__ __forceinline__ void q4k_sm_const(uint32_t s0, uint32_t s1, uint32_t s2, int& sc, int& mn) {
+    if constexpr (J < 4) {
+        sc = (s0 >> (8 * J)) & 63;
+        mn = (s1 >> (8 * J)) & 63;
+    } else {
+        constexpr int jj = J - 4;
+        sc = ((s2 >> (8 * jj)) & 15) | (((s0 >> (8 * jj + 6)) & 3) << 4);
+        mn = ((s2 >> (8 * jj + 4)) & 15) | (((s1 >> (8 * jj + 6)) & 3) << 4);
+    }
+}
+
+// The same with a run-time sub-block index.
+__device__ __forceinline__ void q4k_sm_var(uint32_t s0, uint32_t s1, uint32_t s2, int j, int& sc, int& mn) {
+    if (j < 4) {
+        sc = (s0 >> (8 * j)) & 63;
+        mn = (s1 >> (8 * j)) & 63;
+    } else {
+        const int jj = j - 4;
+        sc = ((s2 >> (8 * jj)) & 15) | (((s0 >> (8 * jj + 6)) & 3) << 4);
+        mn = ((s2 >> (8 * jj + 4)) & 15) | (((s1 >> (8 * jj + 6)) & 3) << 4);
+    }
+}
+
+// Eight quant dwords (32 bytes, chunk c of a Q4_K block) against the pieces of
+// the matching activations: returns the two raw dot products
+// A = sum (128 + q_lo) x~ over sub-block 2c's 32 weights, B likewise for 2c+1.
+__device__ __forceinline__ void q4k_chunk_dots(const uint32_t* qw, const uint8_t* xblk, int c,
+                                               float& A, float& B) {
+    float a = 0.f, b = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const uint4 xa = *reinterpret_cast<const uint4*>(xblk + (16 * c + q) * kSlotBytes);
+        const uint4 xb = *reinterpret_cast<const uint4*>(xblk + (16 * c + 8 + q) * kSlotBytes);
+        const uint32_t w = qw[q];
+        const uint32_t p0 = (w & 0x000f000fu) | kBf16Bias;
+        const uint32_t p1 = ((w >> 8) & 0x000f000fu) | kBf16Bias;
+        const uint32_t p2 = ((w >> 4) & 0x000f000fu) | kBf16Bias;
+        const uint32_t p3 = ((w >> 12) & 0x000f000fu) | kBf16Bias;
+        a = dot2_bf16(p0, xa.x, a);
+        a = dot2_bf16(p1, xa.y, a);
+        a = dot2_bf16(p0, xa.z, a);
+        a = dot2_bf16(p1, xa.w, a);
+        b = dot2_bf16(p2, xb.x, b);
+        b = dot2_bf16(p3, xb.y, b);
+        b = dot2_bf16(p2, xb.z, b);
+        b = dot2_bf16(p3, xb.w, b);
+    }
+    A = a;
+    B = b;
+}
+
+// Whole Q4_K block (256 weights) in LDS against its 256 activations' pieces
+// (xblk) and group sums (gsum, 16 values).
+__device__ __forceinline__ float q4k_block_dot(const uint8_t* blk, const uint8_t* xblk,
+                                               const float* gsum) {
+    const uint4 hdr = *reinterpret_cast<const uint4*>(blk);
+    const float d = half_bits_to_float(hdr.x & 0xffffu);
+    const float dmin = half_bits_to_float(hdr.x >> 16);
+    float row = 0.f;
+#define Q3MOE_Q4K_CHUNK(C)                                                                  \
+    {                                                                                       \
+        const uint4 qa = *reinterpret_cast<const uint4*>(blk + 16 + 32 * (C));              \
+        const uint4 qb = *reinterpret_cast<const uint4*>(blk + 32 + 32 * (C));              \
+        const uint32_t qw[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};            \
+        float A, B;                                                                         \
+        q4k_chunk_dots(qw, xblk, (C), A, B);                                                \
+        int sc0, mn0, sc1, mn1;                                                             \
+        q4k_sm_const<2 * (C)>(hdr.y, hdr.z, hdr.w, sc0, mn0);                               \
+        q4k_sm_const<2 * (C) + 1>(hdr.y, hdr.z, hdr.w, sc1, mn1);                           \
+        const float sx0 = gsum[4 * (C)] + gsum[4 * (C) + 1];                                \
+        const float sx1 = gsum[4 * (C) + 2] + gsum[4 * (C) + 3];                            \
+        row += d * ((float)sc0 * (A - 128.f * sx0) + (float)sc1 * (B - 128.f * sx1)) -      \
+               dmin * ((float)mn0 * sx0 + (float)mn1 * sx1);                                \
+    }
+    Q3MOE_Q4K_CHUNK(0)
+    Q3MOE_Q4K_CHUNK(1)
+    Q3MOE_Q4K_CHUNK(2)
+    Q3MOE_Q4K_CHUNK(3)
+#undef Q3MOE_Q4K_CHUNK
+    return row;
+}
+
+// Convert one token's H activations (global f32) into pieces + group sums
+// in LDS, using all threads of the workgroup.  H/4 is a multiple of 64 so
+// every wave that enters the loop is full.
+__device__ __forceinline__ void activations_to_pieces(const float* __restrict__ x, int H,
+                                                      uint8_t* xp, float* gs, int tid, int nthr) {
+    for (int s = tid; s < H / 4; s += nthr) {
+        const Pieces4 pc = make_pieces4(reinterpret_cast<const float4*>(x)[s]);
+        *reinterpret_cast<uint4*>(xp + piece_slot_off(s)) = pc.slot;
+        float g = pc.sum + __shfl_xor(pc.sum, 1, kWave);
+        g += __shfl_xor(g, 2, kWave);
+        if ((s & 3) == 0) gs[s >> 2] = g;
+    }
+}
+
+// Gate/up task geometry for NB = H/256 dividing 32: R = 32/NB rows of one
+// expert's gate and up matrices, 2 x 32 super-blocks = 9,216 bytes.
+template <int NB>
+struct GuTask {
+    static constexpr int H = NB * kQK;
+    static constexpr int R = 32 / NB;
+    static constexpr int ROWB = NB * kQ4KBytes;
+    static constexpr int TASKB = R * ROWB;                  // bytes per matrix
+};
+
+template <int NB>
+__device__ __forceinline__ void gu_issue(const uint8_t* __restrict__ gbase, int64_t gstride,
+                                         const uint8_t* __restrict__ ubase, int64_t ustride, int e,
+                                         int64_t r0, uint8_t* wg, int lane) {
+    using G = GuTask<NB>;
+    wave_copy_to_lds(wg, gbase + (int64_t)e * gstride + r0 * G::ROWB, G::TASKB, lane);
+    wave_copy_to_lds(wg + G::TASKB, ubase + (int64_t)e * ustride + r0 * G::ROWB, G::TASKB, lane);
+}
+
+// Lane = m*32 + rho*NB + b: matrix m (0 gate, 1 up), row rho of the task,
+// super-block b of the row.  Writes h = silu(g)*u of the R rows as pieces.
+template <int NB>
+__device__ __forceinline__ void gu_compute(const uint8_t* wg, const uint8_t* xp, const float* gs,
+                                           bool valid, int lane, uint8_t* __restrict__ hpieces,
+                                           int64_t value_base) {
+    using G = GuTask<NB>;
+    const int m = lane >> 5, rho = (lane & 31) / NB, b = lane % NB;
+    float row = valid ? q4k_block_dot(wg + m * G::TASKB + rho * G::ROWB + b * kQ4KBytes,
+                                      xp + b * kBlockPieceStride, gs + b * 16)
+                      : 0.f;
+#pragma unroll
+    for (int o = 1; o < NB; o <<= 1) row += __shfl_xor(row, o, kWave);
+    const float up = __shfl_xor(row, 32, kWave);
+    const float h = silu_f(row) * up;                  // meaningful where m == 0 && b == 0
+    if constexpr (G::R >= 4) {
+        // gather rows 4q..4q+3 into the lane of row 4q and store the whole slot
+        const float h1 = __shfl(h, (lane + NB) & 63, kWave);
+        const float h2 = __shfl(h, (lane + 2 * NB) & 63, kWave);
+        const float h3 = __shfl(h, (lane + 3 * NB) & 63, kWave);
+        if (m == 0 && b == 0 && (rho & 3) == 0)
+            store_h_slot(hpieces, value_base + rho, make_pieces4(make_float4(h, h1, h2, h3)).slot);
+    } else {
+        if (m == 0 && b == 0) store_h_piece(hpieces, value_base + rho, h);
+    }
+}
+
+// Gate/up for H = 2048 (8 super-blocks per row, 4 rows of gate and 4 of up
+// per task) with each lane owning a column chunk: lane = b*8 + c*2 + hp owns
+// quant bytes 32c + 16hp .. +15 of super-block b, i.e. 16 weights of
+// sub-block 2c (low nibbles) and 16 of sub-block 2c+1 (high nibbles).  The
+// lane loads its 32 activations and its weights straight into registers
+// (16 quant bytes and the 16-byte block header per row), so nothing goes
+// through LDS and each row is consumed as soon as its loads land.  The 8 row
+// partials are folded across the wave with a transposed butterfly: after it,
+// lanes 8q..8q+7 hold row q (q < 4 gate row q, else up row q-4).
+struct XCols {
+    uint4 lo[4], hi[4];      // pieces of the low-nibble and high-nibble values
+    float slo, shi;          // their sums (one 16-value group each)
+};
+
+// The lane's 32 activations of one token from the token's piece blocks in
+// LDS (xp: 8 blocks of kBlockPieceStride bytes; gs: the 16-value group sums).
+__device__ __forceinline__ XCols load_xcols(const uint8_t* xp, const float* gs, int lane) {
+    const int b = lane >> 3, c = (lane >> 1) & 3, hp = lane & 1;
+    const uint8_t* xb = xp + b * kBlockPieceStride;
+    XCols x;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        x.lo[q] = *reinterpret_cast<const uint4*>(xb + (16 * c + 4 * hp + q) * kSlotBytes);
+        x.hi[q] = *reinterpret_cast<const uint4*>(xb + (16 * c + 8 + 4 * hp + q) * kSlotBytes);
+    }
+    x.slo = gs[b * 16 + 4 * c + hp];
+    x.shi = gs[b * 16 + 4 * c + 2 + hp];
+    return x;
+}
+
+// One row's contribution of this lane: hdr = the block header (d, dmin, 12
+// scale bytes), qv = the lane's 16 quant bytes.
+__device__ __forceinline__ float q4k_cols_row(uint4 hdr, uint4 qv, const XCols& x, int lane) {
+    const int c = (lane >> 1) & 3;
+    const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
+    float A = 0.f, B = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t w = qw[q];
+        const uint32_t p0 = (w & 0x000f000fu) | kBf16Bias;
+        const uint32_t p1 = ((w >> 8) & 0x000f000fu) | kBf16Bias;
+        const uint32_t p2 = ((w >> 4) & 0x000f000fu) | kBf16Bias;
+        const uint32_t p3 = ((w >> 12) & 0x000f000fu) | kBf16Bias;
+        A = dot2_bf16(p0, x.lo[q].x, A);
+        A = dot2_bf16(p1, x.lo[q].y, A);
+        A = dot2_bf16(p0, x.lo[q].z, A);
+        A = dot2_bf16(p1, x.lo[q].w, A);
+        B = dot2_bf16(p2, x.hi[q].x, B);
+        B = dot2_bf16(p3, x.hi[q].y, B);
+        B = dot2_bf16(p2, x.hi[q].z, B);
+        B = dot2_bf16(p3, x.hi[q].w, B);
+    }
+    int sc0, mn0, sc1, mn1;
+    q4k_sm_var(hdr.y, hdr.z, hdr.w, 2 * c, sc0, mn0);
+    q4k_sm_var(hdr.y, hdr.z, hdr.w, 2 * c + 1, sc1, mn1);
+    const float d = half_bits_to_float(hdr.x & 0xffffu);
+    const float dmin = half_bits_to_float(hdr.x >> 16);
+    return d * ((float)sc0 * (A - 128.f * x.slo) + (float)sc1 * (B - 128.f * x.shi)) -
+           dmin * ((float)mn0 * x.slo + (float)mn1 * x.shi);
+}
+
+// Sum v[0..7] over the 64 lanes; returns row (lane >> 3)'s total.
+__device__ __forceinline__ float fold8_rows(const float v[8], int lane) {
+    const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8;
+    float a[4], c[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float send = b5 ? v[i] : v[i + 4];
+        const float keep = b5 ? v[i + 4] : v[i];
+        a[i] = keep + __shfl_xor(send, 32, kWave);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const float send = b4 ? a[i] : a[i + 2];
+        const float keep = b4 ? a[i + 2] : a[i];
+        c[i] = keep + __shfl_xor(send, 16, kWave);
+    }
+    const float send = b3 ? c[0] : c[1];
+    float r = (b3 ? c[1] : c[0]) + __shfl_xor(send, 8, kWave);
+    r += __shfl_xor(r, 4, kWave);
+    r += __shfl_xor(r, 2, kWave);
+    r += __shfl_xor(r, 1, kWave);
+    return r;
+}
+
+// grid: T*k*(F/R)/kGuWaves workgroups of kGuWaves waves, one task per wave.
+template <int NB>
+__global__ __launch_bounds__(kGuWaves * kWave) void gu_decode_kernel(
+    const float* __restrict__ hidden, int64_t F, int32_t E, int32_t k,
+    const int32_t* __restrict__ idx, const uint8_t* __restrict__ gbase, int64_t gstride,
+    const uint8_t* __restrict__ ubase, int64_t ustride, uint8_t* __restrict__ hpieces) {
+    using G = GuTask<NB>;
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint8_t* wg = smem + wave * 2 * G::TASKB;
+    uint8_t* xp = smem + kGuWaves * 2 * G::TASKB;
+    float* gs = reinterpret_cast<float*>(xp + NB * kBlockPieceStride);
+
+    const int tiles = (int)(F / G::R);                    // tasks per pair, a multiple of kGuWaves
+    const int64_t task = (int64_t)blockIdx.x * kGuWaves + wave;
+    const int64_t p = task / tiles;                       // same for the whole workgroup
+    const int64_t t = p / k;
+    const int64_t r0 = (task % tiles) * G::R;
+    const int e = idx[p];
+    const bool valid = e >= 0 && e < E;
+    if (valid) gu_issue<NB>(gbase, gstride, ubase, ustride, e, r0, wg, lane);
+    activations_to_pieces(hidden + t * G::H, G::H, xp, gs, tid, kGuWaves * kWave);
+    wait_all_loads();
+    __syncthreads();
+    gu_compute<NB>(wg, xp, gs, valid, lane, hpieces, p * F + r0);
+}
+
+// ----------------------------------------------------------------- down --
+
+// Q6_K: lane handles (n, lh) of its row's block: l = 16lh..16lh+15 for all
+// four r, i.e. 64 weights in four 16-weight scale groups.
+__device__ __forceinline__ float q6k_lane_dot(const uint8_t* lds, int boff, int n, int lh,
+                                              const uint8_t* xblk, const float* gsum) {
+    const uint4 La = lds_read16_a2(lds, boff + 64 * n + 16 * lh);        // r = 0 (lo), 2 (hi)
+    const uint4 Lb = lds_read16_a2(lds, boff + 64 * n + 32 + 16 * lh);   // r = 1 (lo), 3 (hi)
+    const uint4 Hd = lds_read16_a2(lds, boff + 128 + 32 * n + 16 * lh);
+    const uint32_t la[4] = {La.x, La.y, La.z, La.w};
+    const uint32_t lb[4] = {Lb.x, Lb.y, Lb.z, Lb.w};
+    const uint32_t hd[4] = {Hd.x, Hd.y, Hd.z, Hd.w};
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int lq = 0; lq < 4; ++lq) {
+        uint32_t q[4];
+        q[0] = (la[lq] & 0x0f0f0f0fu) | ((hd[lq] << 4) & 0x30303030u);
+        q[1] = (lb[lq] & 0x0f0f0f0fu) | ((hd[lq] << 2) & 0x30303030u);
+        q[2] = ((la[lq] >> 4) & 0x0f0f0f0fu) | (hd[lq] & 0x30303030u);
+        q[3] = ((lb[lq] >> 4) & 0x0f0f0f0fu) | ((hd[lq] >> 2) & 0x30303030u);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const uint4 x = *reinterpret_cast<const uint4*>(
+                xblk + (32 * n + 8 * r + 4 * lh + lq) * kSlotBytes);
+            const uint32_t p0 = (q[r] & 0x00ff00ffu) | kBf16Bias;
+            const uint32_t p1 = ((q[r] >> 8) & 0x00ff00ffu) | kBf16Bias;
+            float a = acc[r];
+            a = dot2_bf16(p0, x.x, a);
+            a = dot2_bf16(p1, x.y, a);
+            a = dot2_bf16(p0, x.z, a);
+            a = dot2_bf16(p1, x.w, a);
+            acc[r] = a;
+        }
+    }
+    const float d = half_bits_to_float(lds[boff + 208] | (lds[boff + 209] << 8));
+    float sum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int g = 8 * n + 2 * r + lh;
+        const float sc = (float)(int8_t)lds[boff + 192 + g];
+        sum += sc * (acc[r] - 160.f * gsum[g]);
+    }
+    return d * sum;
+}
+
+// Q4_K down rows: lane handles chunk c (sub-blocks 2c, 2c+1, 64 weights).
+__device__ __forceinline__ float q4k_lane_dot(const uint8_t* blk, int c, const uint8_t* xblk,
+                                              const float* gsum) {
+    const uint4 hdr = *reinterpret_cast<const uint4*>(blk);
+    const uint4 qa = *reinterpret_cast<const uint4*>(blk + 16 + 32 * c);
+    const uint4 qb = *reinterpret_cast<const uint4*>(blk + 32 + 32 * c);
+    const uint32_t qw[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+    float A, B;
+    q4k_chunk_dots(qw, xblk, c, A, B);
+    int sc0, mn0, sc1, mn1;
+    q4k_sm_var(hdr.y, hdr.z, hdr.w, 2 * c, sc0, mn0);
+    q4k_sm_var(hdr.y, hdr.z, hdr.w, 2 * c + 1, sc1, mn1);
+    const float d = half_bits_to_float(hdr.x & 0xffffu);
+    const float dmin = half_bits_to_float(hdr.x >> 16);
+    const float sx0 = gsum[4 * c] + gsum[4 * c + 1];
+    const float sx1 = gsum[4 * c + 2] + gsum[4 * c + 3];
+    return d * ((float)sc0 * (A - 128.f * sx0) + (float)sc1 * (B - 128.f * sx1)) -
+           dmin * ((float)mn0 * sx0 + (float)mn1 * sx1);
+}
+
+// Geometry of a down slot region in LDS: the 8-row tile of one expert's down
+// matrix, 16 bytes of padding (the unaligned Q6_K reads look up to 4 bytes
+// ahead), that slot's h pieces (padded blocks) and their group sums.
+struct DnGeom {
+    int nb, bb, rowb, tile, tile_pad, pieces, sums, per_slot;
+    bool q6;
+    __host__ __device__ DnGeom(int64_t F, int32_t qtype) {
+        nb = (int)(F / kQK);
+        q6 = qtype == 2;
+        bb = q6 ? kQ6KBytes : kQ4KBytes;
+        rowb = nb * bb;
+        tile = kDnRows * rowb;                            // multiple of 16
+        tile_pad = tile + 16;
+        pieces = nb * kBlockPieceStride;
+        sums = nb * 16 * 4;
+        per_slot = tile_pad + pieces + sums;
+    }
+};
+
+__device__ __forceinline__ void dn_issue_weights(uint8_t* reg, const DnGeom& g,
+                                                 const uint8_t* __restrict__ dbase, int64_t dstride,
+                                                 int e, int64_t r0, int lane) {
+    wave_copy_to_lds(reg, dbase + (int64_t)e * dstride + r0 * g.rowb, g.tile, lane);
+}
+
+__device__ __forceinline__ void dn_issue_h(uint8_t* reg, const DnGeom& g, const uint8_t* hsrc,
+                                           int lane) {
+    for (int b = 0; b < g.nb; ++b)
+        wave_copy_to_lds_coherent(reg + g.tile_pad + b * kBlockPieceStride, hsrc + b * 1024, 1024,
+                                  lane);
+}
+
+// Group sums (16 values = 4 slots per group) of a slot region's h pieces.
+__device__ __forceinline__ void dn_group_sums(uint8_t* reg, const DnGeom& g, int lane) {
+    const uint8_t* xs = reg + g.tile_pad;
+    float* gs = reinterpret_cast<float*>(reg + g.tile_pad + g.pieces);
+    for (int gi = lane; gi < g.nb * 16; gi += kWave) {
+        float v = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            v += slot_sum(*reinterpret_cast<const uint4*>(xs + piece_slot_off(4 * gi + i)));
+        gs[gi] = v;
+    }
+}
+
+// This lane's share (quarter u of every super-block) of output row rho.
+__device__ __forceinline__ float dn_lane_row(const uint8_t* reg, const DnGeom& g, int rho, int u) {
+    const uint8_t* xs = reg + g.tile_pad;
+    const float* gs = reinterpret_cast<const float*>(xs + g.pieces);
+    float y = 0.f;
+    for (int b = 0; b < g.nb; ++b) {
+        const int boff = rho * g.rowb + b * g.bb;
+        y += g.q6 ? q6k_lane_dot(reg, boff, u >> 1, u & 1, xs + b * kBlockPieceStride, gs + b * 16)
+                  : q4k_lane_dot(reg + boff, u, xs + b * kBlockPieceStride, gs + b * 16);
+    }
+    return y;
+}
+
+// grid: (T, H/8).  Dynamic LDS: 4 waves x 2 slot regions + the slot-result
+// table.  Lane = sh*32 + rho*4 + u: slot sh of the wave's pair, output row
+// rho, quarter u of each super-block.
+__global__ __launch_bounds__(kDnWaves * kWave) void down_decode_kernel(
+    int64_t H, int64_t F, int32_t E, int32_t k, const int32_t* __restrict__ idx,
+    const float* __restrict__ w, const uint8_t* __restrict__ dbase, int32_t qtype,
+    int64_t dstride, const uint8_t* __restrict__ hpieces, float* __restrict__ out,
+    int accumulate) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const DnGeom g(F, qtype);
+    uint8_t* wbase = smem + wave * kDnSlotsPerWave * g.per_slot;
+    float* ys = reinterpret_cast<float*>(smem + kDnWaves * kDnSlotsPerWave * g.per_slot);
+
+    const int64_t t = blockIdx.x;
+    const int64_t r0 = (int64_t)blockIdx.y * kDnRows;
+    const int sh = lane >> 5, rho = (lane >> 2) & 7, u = lane & 3;
+    const int group = kDnWaves * kDnSlotsPerWave;
+
+    for (int s0 = 0; s0 < k; s0 += group) {
+        int ev[kDnSlotsPerWave];
+#pragma unroll
+        for (int j = 0; j < kDnSlotsPerWave; ++j) {
+            const int s = s0 + wave * kDnSlotsPerWave + j;
+            ev[j] = s < k ? idx[t * k + s] : -1;
+            if (ev[j] >= 0 && ev[j] < E) {
+                uint8_t* reg = wbase + j * g.per_slot;
+                dn_issue_weights(reg, g, dbase, dstride, ev[j], r0, lane);
+                dn_issue_h(reg, g, hpieces + (t * k + s) * F * 4, lane);
+            }
+        }
+        wait_all_loads();
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kDnSlotsPerWave; ++j) dn_group_sums(wbase + j * g.per_slot, g, lane);
+        __syncthreads();
+        const int s = s0 + wave * kDnSlotsPerWave + sh;
+        const int e = ev[sh];
+        const bool valid = s < k && e >= 0 && e < E;
+        float y = valid ? dn_lane_row(wbase + sh * g.per_slot, g, rho, u) : 0.f;
+        y += __shfl_xor(y, 1, kWave);
+        y += __shfl_xor(y, 2, kWave);
+        if (u == 0 && s < k) ys[s * kDnRows + rho] = valid ? w[t * k + s] * y : 0.f;
+        __syncthreads();
+    }
+    if (tid < kDnRows) {
+        float acc = 0.f;
+        for (int s = 0; s < k; ++s) acc += ys[s * kDnRows + tid];
+        float* o = out + t * H + r0 + tid;
+        *o = accumulate ? *o + acc : acc;
+    }
+}
+
+// The 8 rows of one gate/up task as this lane's registers: the block header
+// and the lane's 16 quant bytes of gate rows r0..r0+3, then of up rows.
+struct GuRows {
+    uint4 hdr[8], qv[8];
+    bool valid;
+};
+
+// Loads are unconditional (an out-of-range expert reads expert 0's rows and
+// its result is dropped), so they form one straight-line group that the
+// scheduler keeps ahead of the arithmetic that waits on older loads.
+__device__ __forceinline__ void gu_rows_load(GuRows& g, int e, int32_t E,
+                                             const uint8_t* __restrict__ gbase, int64_t gstride,
+                                             const uint8_t* __restrict__ ubase, int64_t ustride,
+                                             int64_t r0, int lane) {
+    using G = GuTask<8>;
+    const int b = lane >> 3, c = (lane >> 1) & 3, hp = lane & 1;
+    const int qoff = 16 + 32 * c + 16 * hp;
+    g.valid = e >= 0 && e < E;
+    const int64_t es = g.valid ? e : 0;
+    const uint8_t* g0 = gbase + es * gstride + r0 * G::ROWB + b * kQ4KBytes;
+    const uint8_t* u0 = ubase + es * ustride + r0 * G::ROWB + b * kQ4KBytes;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint8_t* row = (i < 4 ? g0 : u0) + (i & 3) * G::ROWB;
+        g.hdr[i] = *reinterpret_cast<const uint4*>(row);
+        g.qv[i] = *reinterpret_cast<const uint4*>(row + qoff);
+    }
+}
+
+// h = silu(gate) * up of the task's 4 rows, stored as one piece slot at
+// value index value_base (a multiple of 4) with device-scope stores.
+__device__ __forceinline__ void gu_rows_finish(const GuRows& g, const XCols& x, int lane,
+                                               uint8_t* __restrict__ hpieces, int64_t value_base) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = g.valid ? q4k_cols_row(g.hdr[i], g.qv[i], x, lane) : 0.f;
+    const float r = fold8_rows(v, lane);               // lanes 8q..: row q
+    const float up = __shfl_xor(r, 32, kWave);          // lane 8q (q < 4) gets up row q
+    const float h = silu_f(r) * up;
+    const float h1 = __shfl(h, 8, kWave), h2 = __shfl(h, 16, kWave), h3 = __shfl(h, 24, kWave);
+    if (lane == 0) store_h_slot(hpieces, value_base, make_pieces4(make_float4(h, h1, h2, h3)).slot);
+}
+
+// ------------------------------------------------------------ fused path --
+//
+// One persistent kernel for the whole expert FFN of a few tokens at H = 2048.
+// Each workgroup (one per CU) has 8 waves: 6 compute gate/up tasks from
+// registers, 2 request the workgroup's down tiles into LDS at once, so the
+// down weights stream while gate/up computes; all 8 then share the down
+// projection of the workgroup's output rows.
+//
+// Hand-off of h between workgroups: gate/up waves store h pieces with
+// device-scope (write-through) stores and wait for them to complete; each
+// then counts itself on an LDS counter, and the last of the workgroup adds 1
+// to one of 16 global counters, each in its own 128-byte line (workgroup g
+// uses stripe g % 16).  One down wave per workgroup polls the 16 stripes
+// with device-scope loads until every stripe has counted all of its
+// workgroups; then all waves read the slots' h pieces with device-scope
+// loads.  No L2 write-back or invalidate is needed because every access that
+// crosses CUs is coherent at device scope.  Every s_barrier is reached by all
+// waves of the workgroup.  Exit: each workgroup counts itself on its stripe
+// of a second counter set; the workgroup that completes a stripe counts on a
+// top counter, and the one that completes the top counter zeroes everything
+// for the next call.  All waits are bounded: one that runs out sets the
+// status word instead of hanging.
+constexpr int kFzGu = 6;
+constexpr int kFzDn = 2;
+constexpr int kFzWaves = kFzGu + kFzDn;
+constexpr int kFzNB = 8;                               // H = 2048
+constexpr int kSpinLimit = 1 << 22;
+constexpr int kStripes = 16;
+constexpr int kLineInts = 32;                          // 128-byte spacing of counters
+// int32 offsets inside the workspace's synchronisation header
+constexpr int kSyncStatus = 0;
+constexpr int kSyncGuDone = 64;                        // + kLineInts * stripe
+constexpr int kSyncExit = kSyncGuDone + kStripes * kLineInts;
+constexpr int kSyncExitTop = kSyncExit + kStripes * kLineInts;
+static_assert((kSyncExitTop + 1) * 4 <= (int)kFfnSyncBytes, "sync header too small");
+
+__device__ __forceinline__ int stripe_members(int stripe, int grid) {
+    return grid / kStripes + (stripe < grid % kStripes ? 1 : 0);
+}
+
+// Poll the gate/up completion stripes until all `grid` workgroups counted.
+__device__ __forceinline__ bool wait_all_gate_up(const int32_t* sync, int grid, int32_t* status,
+                                                 int lane) {
+    const bool mine = lane < kStripes;
+    const int need = mine ? stripe_members(lane, grid) : 0;
+    const int32_t* ctr = sync + kSyncGuDone + (mine ? lane : 0) * kLineInts;
+    int spins = 0;
+    while (true) {
+        const int v = mine ? __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+        if (__all(v >= need)) return true;
+        __builtin_amdgcn_s_sleep(2);
+        if (++spins > kSpinLimit) {
+            if (lane == 0) __hip_atomic_fetch_or(status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return false;
+        }
+    }
+}
+
+constexpr int kFzMaxSlots = 8;                        // the fused path serves k <= 8
+constexpr int kFzMaxTokens = 4;                        // and T <= 4 (T*k routing entries <= 32)
+static_assert(kFzWaves * kWave * 4 == kFzNB * kQK, "one float4 of activations per thread and token");
+
+struct FusedLds {
+    int xp_bytes, dn_off, hp_off, res_off, ctr_off, total;
+};
+
+__host__ __device__ inline FusedLds fused_lds(int64_t T, int64_t F, int32_t qtype) {
+    const DnGeom d(F, qtype);
+    FusedLds L;
+    L.xp_bytes = kFzNB * kBlockPieceStride + kFzNB * 16 * 4;       // pieces + group sums per token
+    L.dn_off = (int)T * L.xp_bytes;                                 // down tiles, one per slot
+    L.hp_off = L.dn_off + kFzMaxSlots * d.tile_pad;                 // h pieces + group sums per slot
+    L.res_off = L.hp_off + kFzMaxSlots * (d.pieces + d.sums);       // [slot][block][row] partials
+    L.ctr_off = L.res_off + kFzMaxSlots * d.nb * kDnRows * 4;       // gate/up waves done
+    L.total = L.ctr_off + 16;
+    return L;
+}
+
+// Value of lane `src` (wave-uniform) of v.
+__device__ __forceinline__ int lane_value(int v, int src) { return __builtin_amdgcn_readlane(v, src); }
+
+// grid: at most one workgroup per CU, kFzWaves waves each.  sync is the
+// workspace's synchronisation header: its counters are zero when the kernel
+// starts and zero again when it ends.  The routing entries (T*k <= 32) live
+// in one register per lane of every wave and are read with readlane.
+__global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
+    const float* __restrict__ hidden, int64_t T, int64_t F, int32_t E, int32_t k,
+    const int32_t* __restrict__ idx, const float* __restrict__ w,
+    const uint8_t* __restrict__ gbase, int64_t gstride, const uint8_t* __restrict__ ubase,
+    int64_t ustride, const uint8_t* __restrict__ dbase, int32_t dqtype, int64_t dstride,
+    float* __restrict__ out, int accumulate, uint8_t* __restrict__ hpieces,
+    int32_t* __restrict__ sync) {
+    using G = GuTask<kFzNB>;
+    constexpr int kThr = kFzWaves * kWave;
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int grid = (int)gridDim.x, wg = (int)blockIdx.x;
+    const FusedLds L = fused_lds(T, F, dqtype);
+    const DnGeom dg(F, dqtype);
+    int32_t* status = sync + kSyncStatus;
+    float* res = reinterpret_cast<float*>(smem + L.res_off);
+    int32_t* gu_ctr = reinterpret_cast<int32_t*>(smem + L.ctr_off);
+
+    const int64_t tiles = F / G::R;
+    const int64_t n_gu = T * k * tiles;
+    const int64_t row_units = G::H / kDnRows;
+    const int64_t n_dn = T * row_units;
+    const int64_t gu_step = (int64_t)grid * kFzGu;
+    const bool is_gu = wave < kFzGu;
+
+    // ---- (1) routing, then the activations of all T tokens as pieces in LDS
+    // (one float4 per thread and token), built once for all waves
+    const int nr = (int)(T * k);
+    const int my_idx = lane < nr ? idx[lane] : -1;
+    const float my_w = lane < nr ? w[lane] : 0.f;
+    float4 xv[kFzMaxTokens];
+#pragma unroll
+    for (int j = 0; j < kFzMaxTokens; ++j)
+        if (j < T) xv[j] = reinterpret_cast<const float4*>(hidden + j * G::H)[tid];
+    if (tid == 0) *gu_ctr = 0;
+#pragma unroll
+    for (int j = 0; j < kFzMaxTokens; ++j) {
+        if (j < T) {                                           // whole workgroup in or out
+            uint8_t* xp = smem + j * L.xp_bytes;
+            const Pieces4 pc = make_pieces4(xv[j]);
+            *reinterpret_cast<uint4*>(xp + piece_slot_off(tid)) = pc.slot;
+            float g = pc.sum + __shfl_xor(pc.sum, 1, kWave);
+            g += __shfl_xor(g, 2, kWave);
+            if ((tid & 3) == 0) reinterpret_cast<float*>(xp + kFzNB * kBlockPieceStride)[tid >> 2] = g;
+        }
+    }
+    __syncthreads();                          // no direct-to-LDS load is in flight yet
+
+    int64_t unit = wg;
+    if (is_gu) {
+        // gate/up tasks: request the weights, then read the token's pieces
+        int64_t xc = -1;                      // token whose pieces x holds
+        XCols x;
+        for (int64_t tau = (int64_t)wg * kFzGu + wave; tau < n_gu; tau += gu_step) {
+            const int64_t p = tau / tiles, t = p / k, r0 = (tau % tiles) * G::R;
+            const int e = lane_value(my_idx, (int)p);
+            GuRows rows;
+            gu_rows_load(rows, e, E, gbase, gstride, ubase, ustride, r0, lane);
+            if (t != xc) {
+                const uint8_t* xp = smem + t * L.xp_bytes;
+                x = load_xcols(xp, reinterpret_cast<const float*>(xp + kFzNB * kBlockPieceStride), lane);
+                xc = t;
+            }
+            gu_rows_finish(rows, x, lane, hpieces, p * F + r0);
+        }
+        wait_all_loads();                     // this wave's h stores have completed
+        if (lane == 0) {
+            const int before = __hip_atomic_fetch_add(gu_ctr, 1, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_WORKGROUP);
+            if (before == kFzGu - 1)          // the workgroup's last gate/up wave
+                __hip_atomic_fetch_add(sync + kSyncGuDone + (wg % kStripes) * kLineInts, 1,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    } else if (unit < n_dn) {
+        // down waves: request the first unit's tiles for all slots
+        const int dw = wave - kFzGu;
+        const int64_t t = unit / row_units, r0 = (unit % row_units) * kDnRows;
+        for (int s = dw; s < k; s += kFzDn) {
+            const int e = lane_value(my_idx, (int)(t * k + s));
+            if (e >= 0 && e < E)
+                dn_issue_weights(smem + L.dn_off + s * dg.tile_pad, dg, dbase, dstride, e, r0, lane);
+        }
+    }
+
+    // ---- (2) one down wave waits until every workgroup's h is out
+    if (wave == kFzGu && unit < n_dn) wait_all_gate_up(sync, grid, status, lane);
+    __syncthreads();
+
+    // ---- (3) down projection and combine, all waves
+    const int ih = lane >> 5, rho = (lane >> 2) & 7, u = lane & 3;
+    const int items = k * dg.nb;
+    for (int j = 0; unit < n_dn; unit += grid, ++j) {
+        const int64_t t = unit / row_units, r0 = (unit % row_units) * kDnRows;
+        if (j > 0) {
+            for (int s = wave; s < k; s += kFzWaves) {
+                const int e = lane_value(my_idx, (int)(t * k + s));
+                if (e >= 0 && e < E)
+                    dn_issue_weights(smem + L.dn_off + s * dg.tile_pad, dg, dbase, dstride, e, r0, lane);
+            }
+        }
+        for (int q = wave; q < items; q += kFzWaves) {        // one 1 KiB piece block per step
+            const int s = q / dg.nb, b = q % dg.nb;
+            const int e = lane_value(my_idx, (int)(t * k + s));
+            if (e >= 0 && e < E)
+                wave_copy_to_lds_coherent(smem + L.hp_off + s * (dg.pieces + dg.sums) + b * kBlockPieceStride,
+                                          hpieces + ((t * k + s) * F + b * kQK) * 4, 1024, lane);
+        }
+        wait_all_loads();
+        __syncthreads();
+        for (int gi = tid; gi < k * dg.nb * 16; gi += kThr) {  // group sums of the h pieces
+            const int s = gi / (dg.nb * 16), g = gi % (dg.nb * 16);
+            const uint8_t* xs = smem + L.hp_off + s * (dg.pieces + dg.sums);
+            float v = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                v += slot_sum(*reinterpret_cast<const uint4*>(xs + piece_slot_off(4 * g + i)));
+            reinterpret_cast<float*>(smem + L.hp_off + s * (dg.pieces + dg.sums) + dg.pieces)[g] = v;
+        }
+        __syncthreads();
+        for (int it = 2 * wave; it < items; it += 2 * kFzWaves) {
+            const int item = it + ih;
+            const int sa = it / dg.nb, sb = (it + 1 < items ? it + 1 : it) / dg.nb;
+            const int ea = lane_value(my_idx, (int)(t * k + sa));
+            const int eb = lane_value(my_idx, (int)(t * k + sb));
+            const int s = ih ? sb : sa, b = item % dg.nb;
+            const int e = ih ? eb : ea;
+            const bool valid = item < items && e >= 0 && e < E;
+            float y = 0.f;
+            if (valid) {
+                const uint8_t* tile = smem + L.dn_off + s * dg.tile_pad;
+                const uint8_t* xs = smem + L.hp_off + s * (dg.pieces + dg.sums);
+                const float* gs = reinterpret_cast<const float*>(xs + dg.pieces) + b * 16;
+                const int boff = rho * dg.rowb + b * dg.bb;
+                y = dg.q6 ? q6k_lane_dot(tile, boff, u >> 1, u & 1, xs + b * kBlockPieceStride, gs)
+                          : q4k_lane_dot(tile + boff, u, xs + b * kBlockPieceStride, gs);
+            }
+            y += __shfl_xor(y, 1, kWave);
+            y += __shfl_xor(y, 2, kWave);
+            if (item < items && u == 0) res[(s * dg.nb + b) * kDnRows + rho] = y;
+        }
+        __syncthreads();
+        if (wave == 0) {                      // lane = slot * 8 + row; fixed-order tree over slots
+            const int s = lane >> 3, row = lane & 7;
+            const int src = (int)(t * k) + (s < k ? s : 0);
+            const int e = __shfl(my_idx, src, kWave);
+            const float ws = __shfl(my_w, src, kWave);
+            float acc = 0.f;
+            if (s < k && e >= 0 && e < E) {
+                float ys = 0.f;
+                for (int b = 0; b < dg.nb; ++b) ys += res[(s * dg.nb + b) * kDnRows + row];
+                acc = ws * ys;
+            }
+            acc += __shfl_xor(acc, 8, kWave);
+            acc += __shfl_xor(acc, 16, kWave);
+            acc += __shfl_xor(acc, 32, kWave);
+            if (lane < kDnRows) {
+                float* o = out + t * G::H + r0 + lane;
+                *o = accumulate ? *o + acc : acc;
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---- exit: the last workgroup zeroes the counters for the next call
+    wait_all_loads();                         // this thread's counter atomics have completed
+    if (tid == 0) {
+        const int st = wg % kStripes;
+        const int32_t done = __hip_atomic_fetch_add(sync + kSyncExit + st * kLineInts, 1,
+                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (done == stripe_members(st, grid) - 1) {           // this stripe is complete
+            const int used = grid < kStripes ? grid : kStripes;
+            const int32_t top = __hip_atomic_fetch_add(sync + kSyncExitTop, 1, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT);
+            if (top == used - 1) {                            // every workgroup has finished
+                for (int i = 0; i < kStripes; ++i) {
+                    __hip_atomic_store(sync + kSyncGuDone + i * kLineInts, 0, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(sync + kSyncExit + i * kLineInts, 0, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                }
+                __hip_atomic_store(sync + kSyncExitTop, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    }
+}
+
+constexpr size_t kMaxLdsPerWorkgroup = 160 * 1024;
+constexpr int kMaxDevices = 64;
+
+// Compute-unit count of the current device, cached per device (an immutable
+// device fact; the cache only saves the query on later calls).
+int cu_count() {
+    static std::atomic<int> cache[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+    if (dev < kMaxDevices) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+        return 0;
+    if (dev < kMaxDevices) cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+// Raise a kernel's dynamic-LDS limit once per (kernel, device, size) instead
+// of on every launch, so launches inside a captured graph make no attribute
+// call.
+struct LdsLimit {
+    std::atomic<int> set[kMaxDevices];
+};
+
+hipError_t ensure_lds(const void* fn, LdsLimit& lim, int bytes) {
+    if (bytes <= 65536) return hipSuccess;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+    const bool cached = dev >= 0 && dev < kMaxDevices;
+    if (cached && bytes <= lim.set[dev].load(std::memory_order_relaxed)) return hipSuccess;
+    const hipError_t err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (err == hipSuccess && cached) lim.set[dev].store(bytes, std::memory_order_relaxed);
+    return err;
+}
+
+size_t gu_lds_bytes(int nb) {
+    const int R = 32 / nb;
+    const size_t taskb = (size_t)R * nb * kQ4KBytes;
+    return kGuWaves * 2 * taskb + (size_t)nb * kBlockPieceStride + (size_t)nb * 16 * 4;
+}
+
+size_t down_lds_bytes(int64_t F, int32_t qtype) {
+    const DnGeom g(F, qtype);
+    return (size_t)kDnWaves * kDnSlotsPerWave * g.per_slot + (size_t)kMaxTopK * kDnRows * 4;
+}
+
+template <int NB>
+hipError_t launch_gu(const float* hidden, int64_t T, int64_t F, int32_t E, int32_t k,
+                     const int32_t* idx, const ExpertTensor& gate, const ExpertTensor& up,
+                     uint8_t* hp, hipStream_t stream) {
+    constexpr int R = 32 / NB;
+    const int64_t tasks = T * k * (F / R);
+    const size_t lds = gu_lds_bytes(NB);
+    static LdsLimit lds_set;
+    hipError_t err = ensure_lds(reinterpret_cast<const void*>(gu_decode_kernel<NB>), lds_set, (int)lds);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(gu_decode_kernel<NB>, dim3((unsigned)(tasks / kGuWaves)), dim3(kGuWaves * kWave),
+                       lds, stream, hidden, F, E, k, idx, gate.base, gate.stride, up.base, up.stride, hp);
+    return hipGetLastError();
+}
+
+hipError_t launch_down(const float* w, int64_t T, int64_t H, int64_t F, int32_t E, int32_t k,
+                       const int32_t* idx, const ExpertTensor& down, const uint8_t* hp, float* out,
+                       int accumulate, hipStream_t stream) {
+    const size_t lds = down_lds_bytes(F, down.qtype);
+    static LdsLimit lds_set;
+    hipError_t err = ensure_lds(reinterpret_cast<const void*>(down_decode_kernel), lds_set, (int)lds);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(down_decode_kernel, dim3((unsigned)T, (unsigned)(H / kDnRows)),
+                       dim3(kDnWaves * kWave), lds, stream, H, F, E, k, idx, w, down.base, down.qtype,
+                       down.stride, hp, out, accumulate);
+    return hipGetLastError();
+}
+
+hipError_t launch_fused8(const float* hidden, int64_t T, int64_t F, int32_t E, int32_t k,
+                         const int32_t* idx, const float* w, const ExpertTensor& gate,
+                         const ExpertTensor& up, const ExpertTensor& down, float* out,
+                         int accumulate, uint8_t* hp, int32_t* sync, int grid, hipStream_t stream) {
+    const FusedLds L = fused_lds(T, F, down.qtype);
+    static LdsLimit lds_set;
+    hipError_t err = ensure_lds(reinterpret_cast<const void*>(ffn_fused8_kernel), lds_set, L.total);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(ffn_fused8_kernel, dim3((unsigned)grid), dim3(kFzWaves * kWave),
+                       (size_t)L.total, stream, hidden, T, F, E, k, idx, w, gate.base, gate.stride,
+                       up.base, up.stride, down.base, down.qtype, down.stride, out, accumulate, hp,
+                       sync);
+    return hipGetLastError();
+}
+
+template <int NB>
+hipError_t launch_decode_nb(const float* hidden, int64_t T, int64_t H, int64_t F, int32_t E,
+                            int32_t k, const int32_t* idx, const float* w, const ExpertTensor& gate,
+                            const ExpertTensor& up, const ExpertTensor& down, float* out,
+                            int accumulate, uint8_t* hp, int32_t* sync, hipStream_t stream) {
+    if constexpr (NB == kFzNB) {
+        const int cus = cu_count();
+        const int64_t tiles = F / GuTask<NB>::R;
+        const int64_t need = (T * k * tiles + kFzGu - 1) / kFzGu;
+        const int64_t units = T * (H / kDnRows);
+        const int64_t want = need > units ? need : units;
+        const int64_t grid = want < cus ? want : cus;
+        if (k <= kFzMaxSlots && T <= kFzMaxTokens && cus > 0 &&
+            (size_t)fused_lds(T, F, down.qtype).total <= kMaxLdsPerWorkgroup)
+            return launch_fused8(hidden, T, F, E, k, idx, w, gate, up, down, out, accumulate, hp,
+                                 sync, (int)grid, stream);
+    }
+    hipError_t err = launch_gu<NB>(hidden, T, F, E, k, idx, gate, up, hp, stream);
+    if (err != hipSuccess) return err;
+    return launch_down(w, T, H, F, E, k, idx, down, hp, out, accumulate, stream);
+}
+
+}  // namespace
+
+bool decode_ffn_supported(int64_t H, int64_t F, int32_t k) {
+    const int64_t nb = H / kQK;
+    return (nb == 1 || nb == 2 || nb == 4 || nb == 8 || nb == 16) && F % kQK == 0 && k >= 1;
+}
+
+
+hipError_t launch_decode_ffn(const float* hidden, int64_t T, int64_t H, int64_t F, int32_t E,
+                             int32_t k, const int32_t* idx, const float* w,
+                             const ExpertTensor& gate, const ExpertTensor& up,
+                             const ExpertTensor& down, float* out, int accumulate, void* ws,
+                             hipStream_t stream) {
+    int32_t* sync = static_cast<int32_t*>(ws);
+    uint8_t* hp = static_cast<uint8_t*>(ws) + kFfnSyncBytes;
+    switch (H / kQK) {
+        case 1: return launch_decode_nb<1>(hidden, T, H, F, E, k, idx, w, gate, up, down, out, accumulate, hp, sync, stream);
+        case 2: return launch_decode_nb<2>(hidden, T, H, F, E, k, idx, w, gate, up, down, out, accumulate, hp, sync, stream);
+        case 4: return launch_decode_nb<4>(hidden, T, H, F, E, k, idx, w, gate, up, down, out, accumulate, hp, sync, stream);
+        case 8: return launch_decode_nb<8>(hidden, T, H, F, E, k, idx, w, gate, up, down, out, accumulate, hp, sync, stream);
+        case 16: return launch_decode_nb<16>(hidden, T, H, F, E, k, idx, w, gate, up, down, out, accumulate, hp, sync, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace q3moe

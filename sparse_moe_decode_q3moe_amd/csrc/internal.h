@@ -17,14 +17,30 @@ struct ExpertTensor {
 constexpr int kMaxTopK = 32;
 constexpr int kMaxExperts = 1024;
 
-// route.hip
+// route.hip.  The route workspace starts with kRouteSyncBytes of completion
+// counters (zero before the first call; every call leaves them zero), then
+// holds the logits.
+constexpr size_t kRouteSyncBytes = 4096;
 size_t route_workspace_bytes(int64_t T, int32_t E);
 hipError_t launch_route(const float* hidden, int64_t T, int64_t H, const float* router,
                         int32_t E, int32_t k, int32_t* idx, float* w, void* ws,
                         hipStream_t stream);
 
-// ffn.hip
+// ffn_decode.hip: the decode-batch path (H/256 in {1, 2, 4, 8, 16})
+bool decode_ffn_supported(int64_t H, int64_t F, int32_t k);
+// The expert-FFN workspace starts with kFfnSyncBytes of synchronisation
+// words (the status word, then line-spaced completion counters of the fused
+// kernel), then holds the intermediate h from that offset on.
+constexpr size_t kFfnSyncBytes = 8192;
+hipError_t launch_decode_ffn(const float* hidden, int64_t T, int64_t H, int64_t F, int32_t E,
+                             int32_t k, const int32_t* idx, const float* w,
+                             const ExpertTensor& gate, const ExpertTensor& up,
+                             const ExpertTensor& down, float* out, int accumulate, void* ws,
+                             hipStream_t stream);
+
+// ffn.hip: dispatch, and the generic path for any H, F multiple of 256
 size_t expert_ffn_workspace_bytes(int64_t T, int64_t H, int64_t F, int32_t E, int32_t k);
+size_t expert_ffn_status_offset(int64_t T, int64_t H, int64_t F, int32_t E, int32_t k);
 hipError_t launch_expert_ffn(const float* hidden, int64_t T, int64_t H, int64_t F, int32_t E,
                              int32_t k, const int32_t* idx, const float* w,
                              const ExpertTensor& gate, const ExpertTensor& up,

@@ -4,6 +4,18 @@
 // f32 x f32 products are exact in double and summation-order noise drops
 // to ~1e-16, which keeps the top-k choice identical to any other double
 // evaluation except at genuine ties ("Risk to track" in the same issue).
+//
+// Decode-sized batches (T <= 8) run as ONE kernel: workgroup e computes
+// expert e's logits for every token, and the last workgroup to finish
+// (found with striped completion counters, no waiting) selects the top-k of
+// every token.  Larger batches run a logits kernel over (expert, 8-token
+// tile) and a top-k kernel with one wave per token.
+//
+// Selection (both paths): k rounds of a wave-wide argmax over the token's
+// logits, larger value first and equal values broken by the lower expert
+// index; weights are the softmax over the selected logits in double (the
+// first selected logit subtracted), normalised by their sum taken in rank
+// order, then rounded to f32.
 #include "device_common.h"
 #include "internal.h"
 
@@ -12,135 +24,269 @@ namespace q3moe {
 namespace {
 
 constexpr int kRouteThreads = 256;
+constexpr int kRouteWaves = kRouteThreads / kWave;
 constexpr int kRouteTokTile = 8;
+constexpr int kRouteChunk = 4;                         // float4 per thread and pass
 
-// One workgroup per (expert e, tile of up to 8 tokens).  Threads stride the
-// router row in float4 units; the row stays in registers across the token
-// tile while each token's hidden vector streams from L2.
-__global__ __launch_bounds__(kRouteThreads) void router_logits_kernel(
-    const float* __restrict__ hidden, int64_t T, int64_t H, const float* __restrict__ router,
-    int32_t E, double* __restrict__ logits) {
-    const int e = blockIdx.x;
-    const int64_t t0 = (int64_t)blockIdx.y * kRouteTokTile;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// Workspace: kRouteSyncBytes of counters (zero between calls), then the
+// logits [T x E] doubles.
+constexpr int kRtStripes = 16;
+constexpr int kRtLineInts = 32;                        // 128-byte spacing
+constexpr int kRtTop = kRtStripes * kRtLineInts;       // int offset of the top counter
+static_assert((kRtStripes + 1) * kRtLineInts * 4 <= (int)kRouteSyncBytes, "route sync header");
+
+// This thread's share of row e of the router dotted with tokens t0..t0+ntok-1
+// (ntok <= 8), accumulated in double.  Loads use clamped indices and a zero
+// mask instead of branches so they are not serialised behind one another.
+__device__ __forceinline__ void router_row_dots(const float* __restrict__ hidden, int64_t t0,
+                                                int ntok, int64_t H,
+                                                const float* __restrict__ row, int tid,
+                                                double acc[kRouteTokTile]) {
     const int64_t n4 = H / 4;
-    const float4* r4 = reinterpret_cast<const float4*>(router + (int64_t)e * H);
-    __shared__ double part[kRouteTokTile][kRouteThreads / kWave];
-
-    const int ntok = (int)((T - t0) < kRouteTokTile ? (T - t0) : kRouteTokTile);
-    double acc[kRouteTokTile];
+    const float4* r4 = reinterpret_cast<const float4*>(row);
 #pragma unroll
     for (int j = 0; j < kRouteTokTile; ++j) acc[j] = 0.0;
-    for (int64_t i = tid; i < n4; i += kRouteThreads) {
-        const float4 rv = r4[i];
+    for (int64_t base = 0; base < n4; base += kRouteChunk * kRouteThreads) {
+        float4 rv[kRouteChunk];
+        float keep[kRouteChunk];
+        int64_t ii[kRouteChunk];
 #pragma unroll
-        for (int j = 0; j < kRouteTokTile; ++j) {
-            if (j < ntok) {
-                const float4 xv = reinterpret_cast<const float4*>(hidden + (t0 + j) * H)[i];
-                double a = acc[j];
-                a = fma((double)rv.x, (double)xv.x, a);
-                a = fma((double)rv.y, (double)xv.y, a);
-                a = fma((double)rv.z, (double)xv.z, a);
-                a = fma((double)rv.w, (double)xv.w, a);
-                acc[j] = a;
-            }
+        for (int c = 0; c < kRouteChunk; ++c) {
+            const int64_t i = base + c * kRouteThreads + tid;
+            keep[c] = i < n4 ? 1.0f : 0.0f;
+            ii[c] = i < n4 ? i : n4 - 1;
+            rv[c] = r4[ii[c]];
         }
-    }
+        for (int j = 0; j < ntok; ++j) {
+            const float4* x4 = reinterpret_cast<const float4*>(hidden + (t0 + j) * H);
+            float4 xv[kRouteChunk];
 #pragma unroll
-    for (int j = 0; j < kRouteTokTile; ++j) {
-        const double s = wave_sum_f64(acc[j]);
-        if (lane == 0) part[j][wave] = s;
-    }
-    __syncthreads();
-    if (tid < ntok) {
-        double s = 0.0;
+            for (int c = 0; c < kRouteChunk; ++c) xv[c] = x4[ii[c]];
+            double a = acc[j];
 #pragma unroll
-        for (int w = 0; w < kRouteThreads / kWave; ++w) s += part[tid][w];
-        logits[(t0 + tid) * E + e] = s;
+            for (int c = 0; c < kRouteChunk; ++c) {
+                const double kc = (double)keep[c];
+                a = fma((double)rv[c].x * kc, (double)xv[c].x, a);
+                a = fma((double)rv[c].y * kc, (double)xv[c].y, a);
+                a = fma((double)rv[c].z * kc, (double)xv[c].z, a);
+                a = fma((double)rv[c].w * kc, (double)xv[c].w, a);
+            }
+            acc[j] = a;
+        }
     }
 }
 
-// One wave per token: k rounds of a wave-wide argmax over the token's E
-// logits (larger value first, lower index on equal values), then the
-// softmax over the k selected logits in double, rounded to f32.
-__global__ __launch_bounds__(kWave) void topk_softmax_kernel(const double* __restrict__ logits,
-                                                             int32_t E, int32_t k,
-                                                             int32_t* __restrict__ idx,
-                                                             float* __restrict__ w) {
-    const int64_t t = blockIdx.x;
-    const int lane = threadIdx.x;
-    constexpr int kPer = kMaxExperts / kWave;
-    double v[kPer];
-    const double* lt = logits + t * E;
+// Workgroup-wide sums of acc[0..ntok); thread j < ntok receives token j's sum.
+__device__ __forceinline__ double workgroup_token_sums(double acc[kRouteTokTile], int ntok,
+                                                       int tid) {
+    __shared__ double part[kRouteTokTile][kRouteWaves];
+    const int lane = tid & 63, wave = tid >> 6;
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        const int e = lane + kWave * j;
-        v[j] = (e < E) ? lt[e] : -INFINITY;
+    for (int j = 0; j < kRouteTokTile; ++j) {
+        if (j < ntok) {
+            const double s = wave_sum_f64(acc[j]);
+            if (lane == 0) part[j][wave] = s;
+        }
     }
-    bool taken[kPer];
+    __syncthreads();
+    double s = 0.0;
+    if (tid < ntok) {
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) taken[j] = (lane + kWave * j) >= E;
+        for (int w = 0; w < kRouteWaves; ++w) s += part[tid][w];
+    }
+    return s;
+}
 
-    double sel_val = 0.0;   // lane s < k keeps the s-th selected logit
-    int sel_idx = 0;
-    for (int s = 0; s < k; ++s) {
-        double bv = -INFINITY;
+// Lane `src` (wave-uniform) of a double.
+__device__ __forceinline__ double readlane_f64(double v, int src) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, src);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), src);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// One wave: top-k and weights of one token whose logits lane e % 64 holds in
+// v[e / 64] (experts beyond E are never chosen).  Writes idx[0..k), w[0..k).
+template <int NPER>
+__device__ __forceinline__ void topk_wave(const double v_in[NPER], int32_t E, int32_t k,
+                                          int lane, int32_t* __restrict__ idx,
+                                          float* __restrict__ w) {
+    double v[NPER];
+    bool live[NPER];
+#pragma unroll
+    for (int j = 0; j < NPER; ++j) {
+        v[j] = v_in[j];
+        live[j] = lane + kWave * j < E;
+    }
+    double my_v = 0.0, top = 0.0;
+    int my_i = 0;
+    for (int r = 0; r < k; ++r) {
+        // this lane's best live candidate: larger value, then lower index
+        // (indices grow with j, so a strict > keeps the lower one)
+        double bv = 0.0;
         int bi = 0x7fffffff;
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-            const int e = lane + kWave * j;
-            if (!taken[j] && (v[j] > bv || (v[j] == bv && e < bi))) {
+        for (int j = 0; j < NPER; ++j) {
+            if (live[j] && (bi == 0x7fffffff || v[j] > bv)) {
                 bv = v[j];
-                bi = e;
+                bi = lane + kWave * j;
             }
         }
 #pragma unroll
         for (int m = 32; m >= 1; m >>= 1) {
             const double ov = __shfl_xor(bv, m, kWave);
             const int oi = __shfl_xor(bi, m, kWave);
-            if (ov > bv || (ov == bv && oi < bi)) {
-                bv = ov;
-                bi = oi;
-            }
+            const bool take = oi != 0x7fffffff &&
+                              (bi == 0x7fffffff || ov > bv || (ov == bv && oi < bi));
+            bv = take ? ov : bv;
+            bi = take ? oi : bi;
         }
-        // bi is now the same in every lane; mark it taken in its owner lane.
-        if ((bi & (kWave - 1)) == lane) {
+        if (r == 0) top = bv;
+        if (lane == r) {
+            my_v = bv;
+            my_i = bi;
+        }
 #pragma unroll
-            for (int j = 0; j < kPer; ++j)
-                if (lane + kWave * j == bi) taken[j] = true;
-        }
-        if (lane == s) {
-            sel_val = bv;
-            sel_idx = bi;
-        }
+        for (int j = 0; j < NPER; ++j)
+            if (lane + kWave * j == bi) live[j] = false;
     }
-    const double top = __shfl(sel_val, 0, kWave);
-    const double ex = (lane < k) ? exp(sel_val - top) : 0.0;
-    const double den = wave_sum_f64(ex);
+    // lane r < k holds rank r; normaliser summed in rank order
+    const double ex = lane < k ? exp(my_v - top) : 0.0;
+    double den = 0.0;
+    for (int r = 0; r < k; ++r)
+        den += readlane_f64(ex, r);
     if (lane < k) {
-        idx[t * k + lane] = sel_idx;
-        w[t * k + lane] = (float)(ex / den);
+        idx[lane] = my_i;
+        w[lane] = (float)(ex / den);
     }
+}
+
+
+// ------------------------------------------------------------ T <= 8 --
+// grid: E workgroups; workgroup e computes logits[t][e] for every token and
+// stores them with device-scope stores; after they complete it counts itself
+// on stripe e % 16, the workgroup completing a stripe counts on the top
+// counter, and the one completing the top counter (every logit is then
+// visible at device scope) selects the top-k of all tokens, one wave per
+// token, reading the logits with device-scope loads.  It finally zeroes the
+// counters for the next call.  Nothing waits on another workgroup.
+__device__ __forceinline__ int rt_stripe_members(int stripe, int grid) {
+    return grid / kRtStripes + (stripe < grid % kRtStripes ? 1 : 0);
+}
+
+template <int NPER>
+__global__ __launch_bounds__(kRouteThreads) void route_small_kernel(
+    const float* __restrict__ hidden, int32_t T, int64_t H, const float* __restrict__ router,
+    int32_t E, int32_t k, int32_t* __restrict__ idx, float* __restrict__ w,
+    int32_t* __restrict__ sync, double* __restrict__ logits) {
+    const int e = blockIdx.x, grid = (int)gridDim.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    __shared__ int last;
+    double acc[kRouteTokTile];
+    router_row_dots(hidden, 0, T, H, router + (int64_t)e * H, tid, acc);
+    const double s = workgroup_token_sums(acc, T, tid);
+    if (tid < T)
+        __hip_atomic_store(logits + (int64_t)tid * E + e, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    wait_all_loads();                         // the logit stores have completed
+    __syncthreads();
+    if (tid == 0) {
+        int is_last = 0;
+        const int st = e % kRtStripes;
+        const int done = __hip_atomic_fetch_add(sync + st * kRtLineInts, 1, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+        if (done == rt_stripe_members(st, grid) - 1) {
+            const int used = grid < kRtStripes ? grid : kRtStripes;
+            const int top = __hip_atomic_fetch_add(sync + kRtTop, 1, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+            is_last = top == used - 1;
+        }
+        last = is_last;
+    }
+    __syncthreads();
+    if (!last) return;
+    for (int t = wave; t < T; t += kRouteWaves) {
+        double v[NPER];
+#pragma unroll
+        for (int j = 0; j < NPER; ++j) {
+            const int ee = lane + kWave * j;
+            v[j] = ee < E ? __hip_atomic_load(logits + (int64_t)t * E + ee, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT)
+                          : 0.0;
+        }
+        topk_wave<NPER>(v, E, k, lane, idx + (int64_t)t * k, w + (int64_t)t * k);
+    }
+    if (tid < kRtStripes) __hip_atomic_store(sync + tid * kRtLineInts, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) __hip_atomic_store(sync + kRtTop, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ------------------------------------------------------------- T > 8 --
+// grid: (E, ceil(T / 8)).
+__global__ __launch_bounds__(kRouteThreads) void router_logits_kernel(
+    const float* __restrict__ hidden, int64_t T, int64_t H, const float* __restrict__ router,
+    int32_t E, double* __restrict__ logits) {
+    const int e = blockIdx.x;
+    const int64_t t0 = (int64_t)blockIdx.y * kRouteTokTile;
+    const int tid = threadIdx.x;
+    const int ntok = (int)((T - t0) < kRouteTokTile ? (T - t0) : kRouteTokTile);
+    double acc[kRouteTokTile];
+    router_row_dots(hidden, t0, ntok, H, router + (int64_t)e * H, tid, acc);
+    const double s = workgroup_token_sums(acc, ntok, tid);
+    if (tid < ntok) logits[(t0 + tid) * E + e] = s;
+}
+
+// grid: ceil(T / 4) workgroups, one wave per token.
+template <int NPER>
+__global__ __launch_bounds__(kRouteThreads) void topk_kernel(const double* __restrict__ logits,
+                                                             int64_t T, int32_t E, int32_t k,
+                                                             int32_t* __restrict__ idx,
+                                                             float* __restrict__ w) {
+    const int lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * kRouteWaves + (threadIdx.x >> 6);
+    if (t >= T) return;
+    double v[NPER];
+#pragma unroll
+    for (int j = 0; j < NPER; ++j) {
+        const int ee = lane + kWave * j;
+        v[j] = ee < E ? logits[t * E + ee] : 0.0;
+    }
+    topk_wave<NPER>(v, E, k, lane, idx + t * k, w + t * k);
+}
+
+template <int NPER>
+hipError_t launch_route_nper(const float* hidden, int64_t T, int64_t H, const float* router,
+                             int32_t E, int32_t k, int32_t* idx, float* w, int32_t* sync,
+                             double* logits, hipStream_t stream) {
+    if (T <= kRouteTokTile) {
+        hipLaunchKernelGGL(route_small_kernel<NPER>, dim3((unsigned)E), dim3(kRouteThreads), 0,
+                           stream, hidden, (int32_t)T, H, router, E, k, idx, w, sync, logits);
+        return hipGetLastError();
+    }
+    dim3 g1((unsigned)E, (unsigned)((T + kRouteTokTile - 1) / kRouteTokTile));
+    hipLaunchKernelGGL(router_logits_kernel, g1, dim3(kRouteThreads), 0, stream, hidden, T, H,
+                       router, E, logits);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(topk_kernel<NPER>, dim3((unsigned)((T + kRouteWaves - 1) / kRouteWaves)),
+                       dim3(kRouteThreads), 0, stream, logits, T, E, k, idx, w);
+    return hipGetLastError();
 }
 
 }  // namespace
 
 size_t route_workspace_bytes(int64_t T, int32_t E) {
-    return (size_t)(T > 0 ? T : 0) * (size_t)E * sizeof(double);
+    return kRouteSyncBytes + (size_t)(T > 0 ? T : 0) * (size_t)E * sizeof(double);
 }
 
 hipError_t launch_route(const float* hidden, int64_t T, int64_t H, const float* router,
                         int32_t E, int32_t k, int32_t* idx, float* w, void* ws,
                         hipStream_t stream) {
-    double* logits = static_cast<double*>(ws);
-    dim3 g1(E, (unsigned)((T + kRouteTokTile - 1) / kRouteTokTile));
-    hipLaunchKernelGGL(router_logits_kernel, g1, dim3(kRouteThreads), 0, stream, hidden, T, H,
-                       router, E, logits);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(topk_softmax_kernel, dim3((unsigned)T), dim3(kWave), 0, stream, logits, E,
-                       k, idx, w);
-    return hipGetLastError();
+    int32_t* sync = static_cast<int32_t*>(ws);
+    double* logits = reinterpret_cast<double*>(static_cast<uint8_t*>(ws) + kRouteSyncBytes);
+    if (E <= 64) return launch_route_nper<1>(hidden, T, H, router, E, k, idx, w, sync, logits, stream);
+    if (E <= 128) return launch_route_nper<2>(hidden, T, H, router, E, k, idx, w, sync, logits, stream);
+    if (E <= 256) return launch_route_nper<4>(hidden, T, H, router, E, k, idx, w, sync, logits, stream);
+    if (E <= 512) return launch_route_nper<8>(hidden, T, H, router, E, k, idx, w, sync, logits, stream);
+    return launch_route_nper<16>(hidden, T, H, router, E, k, idx, w, sync, logits, stream);
 }
 
 }  // namespace q3moe

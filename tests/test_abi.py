@@ -29,7 +29,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(_lib.EXPORTS) == names
@@ -43,7 +43,7 @@ def test_byte_counts(lib):
     assert lib.q3moe_expert_matrix_bytes(q3.Q6_K, 2048, 768) == 1290240
     assert lib.q3moe_expert_matrix_bytes(q3.Q4_K, 2048, 768) == 884736
     assert lib.q3moe_expert_matrix_bytes(q3.Q4_K, 2, 100) == -1
-    assert lib.q3moe_route_workspace_bytes(3, 128) == 3 * 128 * 8
+    assert lib.q3moe_route_workspace_bytes(3, 128) == 4096 + 3 * 128 * 8
     ws = lib.q3moe_expert_ffn_workspace_bytes(5, 2048, 768, 128, 8)
     assert ws >= 5 * 8 * 768 * 4 and ws % 256 == 0
     for s in range(8):
@@ -111,7 +111,7 @@ def test_route_validation(lib):
     assert _route(lib, idx=None) == E_NULL
     assert _route(lib, hidden=FAKE_MIS) == E_ALIGN
     assert _route(lib, ws=None) == E_WORKSPACE
-    assert _route(lib, T=4, ws_bytes=4 * 128 * 8 - 1) == E_WORKSPACE
+    assert _route(lib, T=4, ws_bytes=4096 + 4 * 128 * 8 - 1) == E_WORKSPACE
 
 
 def test_prologue_and_rmsnorm_validation(lib):

@@ -40,6 +40,12 @@ ROUTE_CASES = [  # (T, H, E, k, seed)
     (3, 256, 8, 8, 6),        # k = E
     (7, 2052, 100, 6, 7),     # E not a multiple of 64, H not a multiple of 256
     (600, 2048, 128, 8, 8),   # more tokens than one token tile
+    (8, 2048, 128, 8, 20),    # the largest one-kernel batch
+    (9, 512, 128, 8, 21),     # the smallest two-kernel batch
+    (1, 512, 1024, 32, 22),   # maximum E and k, one kernel
+    (11, 512, 1024, 32, 23),  # maximum E and k, two kernels
+    (6, 512, 64, 8, 24),      # one logit per lane
+    (2, 256, 1, 1, 25),       # a single expert
 ]
 
 
@@ -54,6 +60,25 @@ def test_route_parity(T, H, E, k, seed):
     torch.cuda.synchronize()
     assert_indices_equal(idx.cpu().numpy(), ref_idx, logits, k, "route")
     np.testing.assert_allclose(w.cpu().numpy(), ref_w, rtol=1e-6, atol=0)
+
+
+def test_route_workspace_reuse_across_sizes():
+    """One workspace, zeroed once, through calls of both kernel shapes: each
+    call matches the oracle and the completion counters end at zero."""
+    E, H, k = 128, 2048, 8
+    ws = torch.zeros(q3.q3moe_route_workspace_bytes(600, E), dtype=torch.uint8, device=DEV)
+    g = gen.make_generator(26)
+    R = gen.normal_f32((E, H), 0.02, g)
+    Rd = R.to(DEV)
+    for T in (1, 8, 3, 600, 2, 9, 1, 5):
+        say(f"route reuse T={T}")
+        x = gen.normal_f32((T, H), 1.0, g)
+        idx, w = q3.q3moe_route(x.to(DEV), Rd, k, workspace=ws)
+        ref_idx, ref_w, logits = oracle.oracle().route(x.numpy(), R.numpy(), k)
+        torch.cuda.synchronize()
+        assert_indices_equal(idx.cpu().numpy(), ref_idx, logits, k, f"route reuse T={T}")
+        np.testing.assert_allclose(w.cpu().numpy(), ref_w, rtol=1e-6, atol=0)
+        assert int(ws[:4096].count_nonzero().item()) == 0
 
 
 def test_route_ties_take_lower_index():
@@ -80,6 +105,11 @@ FFN_CASES = {  # name: (shape, seed)
     "k32": (gen.MoeShape(T=2, H=256, E=32, k=32, F=256, down_qtype=gen.Q6_K), 17),
     "k_equals_E": (gen.MoeShape(T=3, H=512, E=4, k=4, F=256, down_qtype=gen.Q4_K), 18),
     "single_expert": (gen.MoeShape(T=2, H=512, E=1, k=1, F=256, down_qtype=gen.Q6_K), 19),
+    # hidden sizes that are not a power-of-two number of super-blocks run the
+    # generic kernels
+    "generic_H768": (gen.MoeShape(T=3, H=768, E=6, k=2, F=512, down_qtype=gen.Q6_K), 20),
+    "generic_H2560_q4k_down": (gen.MoeShape(T=2, H=2560, E=4, k=2, F=256, down_qtype=gen.Q4_K), 21),
+    "a3b_k1_T2": (gen.MoeShape(T=2, H=2048, E=128, k=1, F=768, down_qtype=gen.Q6_K), 22),
 }
 
 
@@ -238,3 +268,67 @@ def test_rmsnorm_parity(T, n):
     q3.q3moe_rmsnorm(xi, gain.to(DEV), 1e-6, out=xi)      # in place
     torch.cuda.synchronize()
     assert_rows_close(xi.cpu().numpy(), ref, what="rmsnorm in place")
+
+
+# ------------------------------------------- workspace reuse, graph replay --
+
+def test_workspace_reuse_across_sizes(layers):
+    """One zero-initialised workspace serves calls of different token counts
+    (the fused persistent kernel for small T, the two-kernel path for larger
+    T); every call matches the oracle and leaves the status word at 0."""
+    cpu, dev, _ = layers("a3b_decode_T1")
+    s = cpu.shape
+    say("workspace reuse across token counts")
+    Tmax = 16
+    ws = torch.zeros(q3.q3moe_expert_ffn_workspace_bytes(Tmax, s.H, s.F, s.E, s.k),
+                     dtype=torch.uint8, device=DEV)
+    o = oracle.oracle()
+    for i, T in enumerate([1, 3, 16, 2, 4, 1, 5, 1]):
+        x = gen.hidden_states(T, s.H, 900 + i)
+        idx, w, _ = o.route(x.numpy(), cpu.router.numpy(), s.k)
+        ref = o.expert_ffn(x.numpy(), idx, w, *oracle_tensors(cpu), F=s.F, E=s.E)
+        out = q3.q3moe_expert_ffn(x.to(DEV), torch.from_numpy(idx).to(DEV),
+                                  torch.from_numpy(w).to(DEV), *experts_of(dev), F=s.F,
+                                  workspace=ws)
+        torch.cuda.synchronize()
+        assert q3.expert_ffn_status(ws, T, s.H, s.F, s.E, s.k) == 0
+        assert_rows_close(out.cpu().numpy(), ref, what=f"reuse T={T}")
+
+
+def test_graph_replay_matches_eager(layers):
+    """The decode step (route + fused expert FFN) captured in a HIP graph and
+    replayed several times, with eager work in between, gives the eager
+    result bit for bit on every replay."""
+    cpu, dev, _ = layers("a3b_decode_T1")
+    s = cpu.shape
+    say("graph replay")
+    n = 4
+    xs = gen.hidden_states(n, s.H, 77).to(DEV).view(n, 1, s.H).contiguous()
+    idx = torch.empty((n, 1, s.k), dtype=torch.int32, device=DEV)
+    w = torch.empty((n, 1, s.k), dtype=torch.float32, device=DEV)
+    outs = torch.empty((n, 1, s.H), dtype=torch.float32, device=DEV)
+    ws_r = torch.zeros(q3.q3moe_route_workspace_bytes(1, s.E), dtype=torch.uint8, device=DEV)
+    ws_f = torch.zeros(q3.q3moe_expert_ffn_workspace_bytes(1, s.H, s.F, s.E, s.k),
+                       dtype=torch.uint8, device=DEV)
+    ex = experts_of(dev)
+
+    def step(i):
+        q3.q3moe_route(xs[i], dev.router, s.k, idx[i], w[i], workspace=ws_r)
+        q3.q3moe_expert_ffn(xs[i], idx[i], w[i], *ex, F=s.F, out=outs[i], workspace=ws_f)
+
+    for i in range(n):
+        step(i)
+    torch.cuda.synchronize()
+    eager = outs.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            step(i)
+    for rep in range(3):
+        outs.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(outs, eager), f"replay {rep} differs"
+        gpu_moe(dev, xs[0])                      # unrelated eager work between replays
+        torch.cuda.synchronize()
+    assert q3.expert_ffn_status(ws_f, 1, s.H, s.F, s.E, s.k) == 0
