@@ -202,6 +202,19 @@ __device__ __forceinline__ void wave_copy_to_lds(uint8_t* lds, const uint8_t* __
     }
 }
 
+// The same for data read once (expert weights): non-temporal loads, so the
+// stream does not evict reused lines (code, routing, counters) from L2.
+constexpr int kCachePolicyNt = 2;
+__device__ __forceinline__ void wave_stream_to_lds(uint8_t* lds, const uint8_t* __restrict__ g,
+                                                   int nbytes, int lane) {
+    const int n16 = nbytes >> 4;
+    for (int base = 0; base < n16; base += kWave) {
+        if (base + lane < n16)
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(g + (base + lane) * 16),
+                                             (lds_ptr_t)(lds + base * 16), 16, 0, kCachePolicyNt);
+    }
+}
+
 // The same with device-scope coherent loads (sc1): they bypass the per-XCD
 // L2, so they see data that another XCD wrote with device-scope stores
 // without an L2 invalidate.

@@ -36,6 +36,25 @@ constexpr uint32_t kBf16Bias = 0x43004300u;   // bf16 128.0 in both halves
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z)); }
 
+// 16 bytes of data read once (expert weights), loaded non-temporally so the
+// stream does not evict reused lines (code, routing, counters) from L2.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream16(const uint8_t* p) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Bytes q0..q3 of v (each < 128) as bf16 pairs (128 + q0, 128 + q2) and
+// (128 + q1, 128 + q3): the byte goes into the mantissa under exponent byte
+// 0x43, in the value order of an activation piece slot.
+constexpr uint32_t kBias8 = 0x43434343u;
+__device__ __forceinline__ uint32_t bf16_pair_even(uint32_t v) {
+    return __builtin_amdgcn_perm(kBias8, v, 0x04020400u);
+}
+__device__ __forceinline__ uint32_t bf16_pair_odd(uint32_t v) {
+    return __builtin_amdgcn_perm(kBias8, v, 0x04030401u);
+}
+
 __device__ __forceinline__ void store_h_piece(uint8_t* __restrict__ hp, int64_t value_index,
                                               float h) {
     // value i lives in slot i/4 at half-word (i%4 == 0: 0, 1: 2, 2: 1, 3: 3) of
@@ -244,11 +263,10 @@ __device__ __forceinline__ float q4k_cols_row(uint4 hdr, uint4 qv, const XCols& 
     float A = 0.f, B = 0.f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const uint32_t w = qw[q];
-        const uint32_t p0 = (w & 0x000f000fu) | kBf16Bias;
-        const uint32_t p1 = ((w >> 8) & 0x000f000fu) | kBf16Bias;
-        const uint32_t p2 = ((w >> 4) & 0x000f000fu) | kBf16Bias;
-        const uint32_t p3 = ((w >> 12) & 0x000f000fu) | kBf16Bias;
+        const uint32_t lo = qw[q] & 0x0f0f0f0fu;              // low nibbles of the 4 bytes
+        const uint32_t hi = (qw[q] >> 4) & 0x0f0f0f0fu;       // high nibbles
+        const uint32_t p0 = bf16_pair_even(lo), p1 = bf16_pair_odd(lo);
+        const uint32_t p2 = bf16_pair_even(hi), p3 = bf16_pair_odd(hi);
         A = dot2_bf16(p0, x.lo[q].x, A);
         A = dot2_bf16(p1, x.lo[q].y, A);
         A = dot2_bf16(p0, x.lo[q].z, A);
@@ -405,7 +423,7 @@ struct DnGeom {
 __device__ __forceinline__ void dn_issue_weights(uint8_t* reg, const DnGeom& g,
                                                  const uint8_t* __restrict__ dbase, int64_t dstride,
                                                  int e, int64_t r0, int lane) {
-    wave_copy_to_lds(reg, dbase + (int64_t)e * dstride + r0 * g.rowb, g.tile, lane);
+    wave_stream_to_lds(reg, dbase + (int64_t)e * dstride + r0 * g.rowb, g.tile, lane);
 }
 
 __device__ __forceinline__ void dn_issue_h(uint8_t* reg, const DnGeom& g, const uint8_t* hsrc,
@@ -518,8 +536,8 @@ __device__ __forceinline__ void gu_rows_load(GuRows& g, int e, int32_t E,
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const uint8_t* row = (i < 4 ? g0 : u0) + (i & 3) * G::ROWB;
-        g.hdr[i] = *reinterpret_cast<const uint4*>(row);
-        g.qv[i] = *reinterpret_cast<const uint4*>(row + qoff);
+        g.hdr[i] = load_stream16(row);
+        g.qv[i] = load_stream16(row + qoff);
     }
 }
 
