@@ -48,7 +48,15 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=20,
                     help="replays of the FFN-only graph used for kernel timing")
+    ap.add_argument("--pmc-pass", action="store_true",
+                    help="for hardware-counter runs: a few eager steps (no graph), then one "
+                         "device-to-device copy of PMC_COPY_BYTES that calibrates the "
+                         "FETCH_SIZE / WRITE_SIZE counters; prints one line, no timing")
     return ap.parse_args()
+
+
+PMC_COPY_BYTES = 256 << 20
+PMC_STEPS = 16
 
 
 def main():
@@ -82,7 +90,7 @@ def main():
     wts = torch.empty((GRAPH_STEPS, 1, k), dtype=torch.float32, device=dev)
     outs = torch.empty((GRAPH_STEPS, 1, H), dtype=torch.float32, device=dev)
     ws_route = torch.zeros(q3.q3moe_route_workspace_bytes(1, E), dtype=torch.uint8, device=dev)
-    ws_ffn = torch.empty(q3.q3moe_expert_ffn_workspace_bytes(1, H, F, E, k), dtype=torch.uint8,
+    ws_ffn = torch.zeros(q3.q3moe_expert_ffn_workspace_bytes(1, H, F, E, k), dtype=torch.uint8,
                          device=dev)
 
     def route(i):
@@ -101,6 +109,18 @@ def main():
     for i in range(GRAPH_STEPS):
         step(i)
     torch.cuda.synchronize()
+
+    if args.pmc_pass:
+        for i in range(PMC_STEPS):
+            step(i)
+        src = torch.ones(PMC_COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"pmc_pass": True, "ffn_dispatches": GRAPH_STEPS + PMC_STEPS,
+                          "copy_bytes": PMC_COPY_BYTES}), flush=True)
+        return
 
     def capture(fn, n):
         g = torch.cuda.CUDAGraph()

@@ -28,12 +28,51 @@ constexpr int kRouteWaves = kRouteThreads / kWave;
 constexpr int kRouteTokTile = 8;
 constexpr int kRouteChunk = 4;                         // float4 per thread and pass
 
-// Workspace: kRouteSyncBytes of counters (zero between calls), then the
-// logits [T x E] doubles.
-constexpr int kRtStripes = 16;
-constexpr int kRtLineInts = 32;                        // 128-byte spacing
-constexpr int kRtTop = kRtStripes * kRtLineInts;       // int offset of the top counter
-static_assert((kRtStripes + 1) * kRtLineInts * 4 <= (int)kRouteSyncBytes, "route sync header");
+// Workspace: kRouteSyncBytes holding the arrival counter (zero between
+// calls), then the logits [T x E] doubles.
+
+// Lane `src` (wave-uniform) of a double.
+__device__ __forceinline__ double readlane_f64(double v, int src) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, src);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), src);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// A double moved across lanes by a DPP pattern (both halves; lanes without a
+// source keep their own value).
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const int lo = (int)(uint32_t)b, hi = (int)(uint32_t)(b >> 32);
+    const uint32_t nlo = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, CTRL, 0xf, 0xf, false);
+    const uint32_t nhi = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, CTRL, 0xf, 0xf, false);
+    return __builtin_bit_cast(double, ((uint64_t)nhi << 32) | nlo);
+}
+constexpr int kDppQuadXor1 = 0xb1;        // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4e;        // quad_perm [2,3,0,1]
+constexpr int kDppRowRor4 = 0x124;
+constexpr int kDppRowRor8 = 0x128;
+
+// Wave-wide max / sum of a double, uniform in every lane: DPP inside each row
+// of 16 lanes, then the four row results combined in a fixed order.  No LDS
+// round trips on the dependent chain.
+__device__ __forceinline__ double wave_max_f64(double v) {
+    v = fmax(v, dpp_f64<kDppQuadXor1>(v));
+    v = fmax(v, dpp_f64<kDppQuadXor2>(v));
+    v = fmax(v, dpp_f64<kDppRowRor4>(v));
+    v = fmax(v, dpp_f64<kDppRowRor8>(v));
+    return fmax(fmax(readlane_f64(v, 0), readlane_f64(v, 16)),
+                fmax(readlane_f64(v, 32), readlane_f64(v, 48)));
+}
+
+__device__ __forceinline__ double wave_sum_dpp_f64(double v) {
+    v += dpp_f64<kDppQuadXor1>(v);
+    v += dpp_f64<kDppQuadXor2>(v);
+    v += dpp_f64<kDppRowRor4>(v);
+    v += dpp_f64<kDppRowRor8>(v);
+    return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
+}
 
 // This thread's share of row e of the router dotted with tokens t0..t0+ntok-1
 // (ntok <= 8), accumulated in double.  Loads use clamped indices and a zero
@@ -84,7 +123,7 @@ __device__ __forceinline__ double workgroup_token_sums(double acc[kRouteTokTile]
 #pragma unroll
     for (int j = 0; j < kRouteTokTile; ++j) {
         if (j < ntok) {
-            const double s = wave_sum_f64(acc[j]);
+            const double s = wave_sum_dpp_f64(acc[j]);
             if (lane == 0) part[j][wave] = s;
         }
     }
@@ -97,16 +136,11 @@ __device__ __forceinline__ double workgroup_token_sums(double acc[kRouteTokTile]
     return s;
 }
 
-// Lane `src` (wave-uniform) of a double.
-__device__ __forceinline__ double readlane_f64(double v, int src) {
-    const uint64_t b = __builtin_bit_cast(uint64_t, v);
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, src);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), src);
-    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
-}
-
 // One wave: top-k and weights of one token whose logits lane e % 64 holds in
-// v[e / 64] (experts beyond E are never chosen).  Writes idx[0..k), w[0..k).
+// v[e / 64] (experts beyond E are never chosen).  Each round takes the
+// wave-wide max of the live logits, then the lowest expert index holding it
+// (ballots over j = 0, 1, ...: index 64j + lane grows with j, then lane).
+// Writes idx[0..k), w[0..k).
 template <int NPER>
 __device__ __forceinline__ void topk_wave(const double v_in[NPER], int32_t E, int32_t k,
                                           int lane, int32_t* __restrict__ idx,
@@ -121,34 +155,36 @@ __device__ __forceinline__ void topk_wave(const double v_in[NPER], int32_t E, in
     double my_v = 0.0, top = 0.0;
     int my_i = 0;
     for (int r = 0; r < k; ++r) {
-        // this lane's best live candidate: larger value, then lower index
-        // (indices grow with j, so a strict > keeps the lower one)
-        double bv = 0.0;
-        int bi = 0x7fffffff;
+        double lm = -__builtin_inf();
+#pragma unroll
+        for (int j = 0; j < NPER; ++j)
+            if (live[j]) lm = fmax(lm, v[j]);
+        const double m = wave_max_f64(lm);
+        int win = -1;
 #pragma unroll
         for (int j = 0; j < NPER; ++j) {
-            if (live[j] && (bi == 0x7fffffff || v[j] > bv)) {
-                bv = v[j];
-                bi = lane + kWave * j;
+            const uint64_t hit = __ballot(live[j] && v[j] == m);
+            if (win < 0 && hit) win = kWave * j + __builtin_ctzll(hit);
+        }
+        if (win < 0) {                        // only NaN left: the lowest live index
+#pragma unroll
+            for (int j = 0; j < NPER; ++j) {
+                const uint64_t hit = __ballot(live[j]);
+                if (win < 0 && hit) win = kWave * j + __builtin_ctzll(hit);
             }
         }
+        double val = m;
 #pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) {
-            const double ov = __shfl_xor(bv, m, kWave);
-            const int oi = __shfl_xor(bi, m, kWave);
-            const bool take = oi != 0x7fffffff &&
-                              (bi == 0x7fffffff || ov > bv || (ov == bv && oi < bi));
-            bv = take ? ov : bv;
-            bi = take ? oi : bi;
-        }
-        if (r == 0) top = bv;
+        for (int j = 0; j < NPER; ++j)
+            if (win >> 6 == j) val = readlane_f64(v[j], win & 63);
+        if (r == 0) top = val;
         if (lane == r) {
-            my_v = bv;
-            my_i = bi;
+            my_v = val;
+            my_i = win;
         }
 #pragma unroll
         for (int j = 0; j < NPER; ++j)
-            if (lane + kWave * j == bi) live[j] = false;
+            if (lane + kWave * j == win) live[j] = false;
     }
     // lane r < k holds rank r; normaliser summed in rank order
     const double ex = lane < k ? exp(my_v - top) : 0.0;
@@ -161,18 +197,14 @@ __device__ __forceinline__ void topk_wave(const double v_in[NPER], int32_t E, in
     }
 }
 
-
 // ------------------------------------------------------------ T <= 8 --
 // grid: E workgroups; workgroup e computes logits[t][e] for every token and
 // stores them with device-scope stores; after they complete it counts itself
-// on stripe e % 16, the workgroup completing a stripe counts on the top
-// counter, and the one completing the top counter (every logit is then
-// visible at device scope) selects the top-k of all tokens, one wave per
-// token, reading the logits with device-scope loads.  It finally zeroes the
-// counters for the next call.  Nothing waits on another workgroup.
-__device__ __forceinline__ int rt_stripe_members(int stripe, int grid) {
-    return grid / kRtStripes + (stripe < grid % kRtStripes ? 1 : 0);
-}
+// on one device-scope counter, and the workgroup that completes the count
+// (every logit is then visible at device scope) selects the top-k of all
+// tokens, one wave per token, reading the logits with device-scope loads.
+// It finally zeroes the counter for the next call.  Nothing waits on
+// another workgroup.
 
 template <int NPER>
 __global__ __launch_bounds__(kRouteThreads) void route_small_kernel(
@@ -190,17 +222,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_small_kernel(
     wait_all_loads();                         // the logit stores have completed
     __syncthreads();
     if (tid == 0) {
-        int is_last = 0;
-        const int st = e % kRtStripes;
-        const int done = __hip_atomic_fetch_add(sync + st * kRtLineInts, 1, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-        if (done == rt_stripe_members(st, grid) - 1) {
-            const int used = grid < kRtStripes ? grid : kRtStripes;
-            const int top = __hip_atomic_fetch_add(sync + kRtTop, 1, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-            is_last = top == used - 1;
-        }
-        last = is_last;
+        const int done = __hip_atomic_fetch_add(sync, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last = done == grid - 1;
     }
     __syncthreads();
     if (!last) return;
@@ -215,8 +238,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_small_kernel(
         }
         topk_wave<NPER>(v, E, k, lane, idx + (int64_t)t * k, w + (int64_t)t * k);
     }
-    if (tid < kRtStripes) __hip_atomic_store(sync + tid * kRtLineInts, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (tid == 0) __hip_atomic_store(sync + kRtTop, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) __hip_atomic_store(sync, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------- T > 8 --
