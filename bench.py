@@ -58,6 +58,27 @@ def parse():
 PMC_COPY_BYTES = 256 << 20
 PMC_STEPS = 16
 
+# HBM bytes per expert-FFN launch measured with the FETCH_SIZE and
+# WRITE_SIZE counters (two rocprofv3 --pmc runs of `bench.py --pmc-pass`,
+# each scaled by what the counter reads for the calibration copy), summarised
+# in profiles/ffn_fused8_kernel_a3b_decode_b1_traffic.md.  The figure belongs
+# to the kernel sources it was measured on; when they change it is reported
+# as null until the counters are taken again.
+TRAFFIC_BYTES_PER_LAUNCH = 25_612_842
+TRAFFIC_SOURCES_SHA256 = "cd6f7a62a956e2e4516b974e6470497fc028956f9876feb614eb6ce1b650fef3"
+TRAFFIC_SOURCES = ("sparse_moe_decode_q3moe_amd/csrc/ffn_decode.hip",
+                   "sparse_moe_decode_q3moe_amd/csrc/device_common.h")
+
+
+def measured_traffic():
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(root, rel), "rb") as f:
+            h.update(f.read())
+    return TRAFFIC_BYTES_PER_LAUNCH if h.hexdigest() == TRAFFIC_SOURCES_SHA256 else None
+
 
 def main():
     args = parse()
@@ -207,7 +228,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(),
             "bytes_per_launch": ffn_bytes,
             "avg_launch_us": round(ffn_us, 3),
         },
