@@ -17,6 +17,8 @@ Parity status per function (how each is pinned is listed in the tests):
                                   single-expert dense MLP, zero cases
   rmsnorm / attn_prologue /       pinned: RMS closed form, rotation invariants,
   rope_neox                       NEOX-vs-interleaved discriminator
+  group_by_expert                 pinned: a library sort of (expert, pair),
+                                  a hand-worked example, count/offset invariants
 Agreement with real GGUF files is not pinned (no files; the bit layout is
 the GGUF k-quant reading).
 """
@@ -74,6 +76,7 @@ def _declare(lib):
                                           _P, ctypes.c_int, _I64,
                                           _P, ctypes.c_int, _I64, _P, ctypes.c_int]),
         "orc_rmsnorm": (ctypes.c_int, [_P, _I64, _I64, _P, ctypes.c_float, _P]),
+        "orc_group_by_expert": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _P, _P]),
         "orc_rope_neox": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, ctypes.c_double]),
         "orc_attn_prologue": (ctypes.c_int, [_P, _P, _I64, _I32, _I32, _I32, _P, _P, _P,
                                              ctypes.c_float, ctypes.c_float]),
@@ -166,6 +169,18 @@ class Oracle:
         logits = np.empty((T, E), np.float64)
         assert self.lib.orc_route(_p(x), T, H, _p(router), E, k, _p(idx), _p(w), _p(logits)) == 0
         return idx, w, logits
+
+    def group_by_expert(self, idx: np.ndarray, E: int):
+        """idx int32 [T, k] -> (counts int32 [E], offsets int32 [E+1], pairs int32 [n])
+        where n = offsets[E] (pairs with an index outside [0, E) are dropped)."""
+        idx = _c(idx, np.int32)
+        T, k = idx.shape
+        counts = np.empty(E, np.int32)
+        offsets = np.empty(E + 1, np.int32)
+        pairs = np.empty(max(1, T * k), np.int32)
+        assert self.lib.orc_group_by_expert(_p(idx), T, k, E, _p(counts), _p(offsets),
+                                            _p(pairs)) == 0
+        return counts, offsets, pairs[:offsets[E]].copy()
 
     def _ffn_args(self, x, idx, w, gate, up, down, F, E):
         x = _c(x, np.float32)

@@ -286,6 +286,26 @@ int orc_expert_ffn(const float *x, int64_t T, int64_t H, int64_t F, int32_t E, i
     return rc;
 }
 
+/* Token -> expert grouping of the routed (token, slot) pairs (survey row
+ * a3; the pages' plan groups tokens by expert for batched prefill, #3714
+ * gap list).  Pair p = t*k + slot with expert idx[p].  For every expert e in
+ * order, the pairs routed to it in increasing p: counts[e] of them starting
+ * at offsets[e]; offsets[E] is the number of grouped pairs.  A pair whose
+ * index is outside [0, E) is not grouped. */
+int orc_group_by_expert(const int32_t *idx, int64_t T, int32_t k, int32_t E,
+                        int32_t *counts, int32_t *offsets, int32_t *pairs)
+{
+    int64_t n = T * k, pos = 0;
+    for (int32_t e = 0; e < E; e++) {
+        offsets[e] = (int32_t)pos;
+        for (int64_t p = 0; p < n; p++)
+            if (idx[p] == e) pairs[pos++] = (int32_t)p;
+        counts[e] = (int32_t)(pos - offsets[e]);
+    }
+    offsets[E] = (int32_t)pos;
+    return 0;
+}
+
 /* RMSNorm of one vector: y = g * x / sqrt(mean(x^2) + eps). */
 static void rmsnorm_vec(const double *x, int64_t n, const float *g, double eps, double *y)
 {

@@ -522,4 +522,48 @@ def pin_prologue(o):
     assert not np.allclose(qb, qw, atol=1e-2)
 
 
+# ------------------------------------------------- token -> expert grouping --
+
+def pin_group_hand_example(o):
+    """A worked example: 3 tokens, k = 2, E = 4.
+    Pairs (p = t*k + slot): 0->2, 1->0, 2->2, 3->3, 4->0, 5->2.
+    Expert 0: pairs 1, 4; expert 1: none; expert 2: pairs 0, 2, 5; expert 3: pair 3."""
+    idx = np.array([[2, 0], [2, 3], [0, 2]], np.int32)
+    counts, offsets, pairs = o.group_by_expert(idx, 4)
+    assert counts.tolist() == [2, 0, 3, 1]
+    assert offsets.tolist() == [0, 2, 2, 5, 6]
+    assert pairs.tolist() == [1, 4, 0, 2, 5, 3]
+
+
+def pin_group_library_sort(o):
+    """Random routings (incl. out-of-range indices) against a library sort of
+    the valid pairs by (expert, pair), and the count / offset invariants."""
+    rng = np.random.default_rng(31)
+    for T, k, E in [(1, 8, 128), (13, 8, 128), (512, 8, 128), (40, 3, 5), (9, 32, 1024), (0, 4, 7)]:
+        idx = rng.integers(-2, E + 2, size=(T, k)).astype(np.int32)
+        counts, offsets, pairs = o.group_by_expert(idx, E)
+        flat = idx.reshape(-1)
+        valid = [p for p in range(flat.size) if 0 <= flat[p] < E]
+        expect = sorted(valid, key=lambda p: (int(flat[p]), p))
+        assert pairs.tolist() == expect
+        assert offsets[0] == 0 and offsets[E] == len(valid)
+        assert np.array_equal(np.diff(offsets), counts)
+        assert counts.tolist() == [int(np.sum(flat == e)) for e in range(E)]
+
+
+def pin_group_skewed_routing(o):
+    """Half of 64 tokens pick the same 4 experts: their pairs come first
+    within those experts' lists in token order, every pair exactly once."""
+    T, k, E = 64, 8, 128
+    rng = np.random.default_rng(5)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    idx[::2, :4] = [3, 17, 64, 101]
+    counts, offsets, pairs = o.group_by_expert(idx, E)
+    assert sorted(pairs.tolist()) == list(range(T * k))
+    for e in (3, 17, 64, 101):
+        seg = pairs[offsets[e]:offsets[e + 1]]
+        assert list(seg) == sorted(seg) and all(idx.reshape(-1)[seg] == e)
+        assert counts[e] >= T // 2
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

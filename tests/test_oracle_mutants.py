@@ -50,6 +50,10 @@ MUTANTS = [
      "rmsnorm_vec(v, D, g, (double)eps, y);\n                rope_neox_head(y, D, (double)pos[t], (double)rope_base);",
      "rope_neox_head(v, D, (double)pos[t], (double)rope_base);\n                rmsnorm_vec(v, D, g, (double)eps, y);"),
     ("prologue_k_gain_for_q", "const float *g = pass == 0 ? q_norm : k_norm;", "const float *g = k_norm;"),
+    ("group_offsets_off_by_one", "offsets[e] = (int32_t)pos;", "offsets[e] = (int32_t)(pos + 1);"),
+    ("group_keeps_last_pair_out", "for (int64_t p = 0; p < n; p++)\n            if (idx[p] == e)", "for (int64_t p = 0; p + 1 < n; p++)\n            if (idx[p] == e)"),
+    ("group_token_not_pair", "if (idx[p] == e) pairs[pos++] = (int32_t)p;", "if (idx[p] == e) pairs[pos++] = (int32_t)(p / k);"),
+    ("group_reverse_order", "for (int64_t p = 0; p < n; p++)\n            if (idx[p] == e)", "for (int64_t p = n - 1; p >= 0; p--)\n            if (idx[p] == e)"),
     ("prologue_head_dim_halved", "rmsnorm_vec(v, D, g, (double)eps, y);", "rmsnorm_vec(v, D / 2, g, (double)eps, y); rmsnorm_vec(v + D / 2, D / 2, g, (double)eps, y + D / 2);"),
 ]
 
