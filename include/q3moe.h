@@ -110,6 +110,26 @@ q3moe_status q3moe_route(const float *hidden, int64_t T, int64_t H,
                          int32_t *topk_idx, float *topk_w,
                          void *workspace, size_t workspace_bytes, void *stream);
 
+/* ------------------------------------------------ token -> expert grouping --
+ * The routed (token, slot) pairs grouped by expert, for the batched expert
+ * FFN (the pages' plan groups prefill tokens by expert: issue #3714, gap
+ * list).  Pair p = t*top_k + slot has expert topk_idx[p].
+ *   counts  [E] int32 out: pairs routed to each expert
+ *   offsets [E+1] int32 out: exclusive prefix of counts; offsets[E] is the
+ *           number of grouped pairs
+ *   pairs   [T*top_k] int32 out: pair indices ordered by (expert, pair),
+ *           i.e. stable in token and slot order; entries from offsets[E]
+ *           on are left untouched
+ * A pair whose index is outside [0, E) is not grouped.  Runs as one
+ * workgroup; unlike the other entry points it also launches for T = 0
+ * (writing zero counts and offsets).
+ * Limits: 1 <= top_k <= 32, 1 <= E <= 1024, T*top_k < 2^31.
+ * Errors: E_NULL, E_SHAPE, E_ALIAS (an output overlaps topk_idx or another
+ * output), E_HIP. */
+q3moe_status q3moe_group_by_expert(const int32_t *topk_idx, int64_t T, int32_t top_k,
+                                   int32_t E, int32_t *counts, int32_t *offsets,
+                                   int32_t *pairs, void *stream);
+
 /* ----------------------------------------------------------- expert FFN --
  * For each token t and slot s with e = topk_idx[t*k+s] (issue #3714, gap G3;
  * the device-side expert-pointer gather and weighted accumulate planned as

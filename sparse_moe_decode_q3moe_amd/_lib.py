@@ -20,7 +20,7 @@ LIB_PATH = PKG / "libq3moe.so"
 Q4_K, Q6_K = 1, 2
 EXPORTS = (
     "q3moe_status_string", "q3moe_qtype_block_bytes", "q3moe_expert_matrix_bytes",
-    "q3moe_route_workspace_bytes", "q3moe_route",
+    "q3moe_route_workspace_bytes", "q3moe_route", "q3moe_group_by_expert",
     "q3moe_expert_ffn_workspace_bytes", "q3moe_expert_ffn_status_offset", "q3moe_expert_ffn",
     "q3moe_attn_prologue", "q3moe_rmsnorm",
 )
@@ -44,6 +44,7 @@ _SIGS = {
     "q3moe_expert_matrix_bytes": (_I64, [_I32, _I64, _I64]),
     "q3moe_route_workspace_bytes": (ctypes.c_size_t, [_I64, _I32]),
     "q3moe_route": (_I32, [_P, _I64, _I64, _P, _I32, _I32, _P, _P, _P, ctypes.c_size_t, _P]),
+    "q3moe_group_by_expert": (_I32, [_P, _I64, _I32, _I32, _P, _P, _P, _P]),
     "q3moe_expert_ffn_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64, _I32, _I32]),
     "q3moe_expert_ffn_status_offset": (ctypes.c_size_t, [_I64, _I64, _I64, _I32, _I32]),
     "q3moe_expert_ffn": (_I32, [_P, _I64, _I64, _I64, _I32, _I32, _P, _P, _Experts, _Experts,
@@ -144,6 +145,29 @@ def q3moe_route(hidden: torch.Tensor, router: torch.Tensor, top_k: int,
         _ptr(hidden), T, H, _ptr(router), E, top_k, _ptr(topk_idx), _ptr(topk_w),
         _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
     return topk_idx, topk_w
+
+
+def q3moe_group_by_expert(topk_idx: torch.Tensor, E: int, counts: Optional[torch.Tensor] = None,
+                          offsets: Optional[torch.Tensor] = None,
+                          pairs: Optional[torch.Tensor] = None, stream=None):
+    """-> (counts int32 [E], offsets int32 [E+1], pairs int32 [T*k]) on the
+    device; pairs[:offsets[E]] is the grouped list."""
+    _need(topk_idx, "topk_idx", torch.int32, 2)
+    T, k = topk_idx.shape
+    dev = topk_idx.device
+    if counts is None:
+        counts = torch.empty(E, dtype=torch.int32, device=dev)
+    if offsets is None:
+        offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    if pairs is None:
+        pairs = torch.empty(max(1, T * k), dtype=torch.int32, device=dev)
+    for t, name in ((counts, "counts"), (offsets, "offsets"), (pairs, "pairs")):
+        _need(t, name, torch.int32, 1)
+    if counts.numel() < E or offsets.numel() < E + 1 or pairs.numel() < T * k:
+        raise ValueError("output tensors too small")
+    _check("q3moe_group_by_expert", library().q3moe_group_by_expert(
+        _ptr(topk_idx), T, k, E, _ptr(counts), _ptr(offsets), _ptr(pairs), _stream(stream)))
+    return counts, offsets, pairs
 
 
 def q3moe_expert_ffn_workspace_bytes(T: int, H: int, F: int, E: int, top_k: int) -> int:

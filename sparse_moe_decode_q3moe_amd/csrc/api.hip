@@ -82,6 +82,24 @@ q3moe_status q3moe_route(const float* hidden, int64_t T, int64_t H, const float*
                                         workspace, as_stream(stream)));
 }
 
+q3moe_status q3moe_group_by_expert(const int32_t* topk_idx, int64_t T, int32_t top_k,
+                                   int32_t E, int32_t* counts, int32_t* offsets,
+                                   int32_t* pairs, void* stream) {
+    if (T < 0 || top_k < 1 || top_k > q3moe::kMaxTopK || E < 1 || E > q3moe::kMaxExperts ||
+        T * (int64_t)top_k > 0x7fffffff)
+        return Q3MOE_E_SHAPE;
+    if (!counts || !offsets || (T > 0 && (!topk_idx || !pairs))) return Q3MOE_E_NULL;
+    const int64_t n = T * top_k;
+    if (n > 0 && (overlaps(pairs, n * 4, topk_idx, n * 4) || overlaps(counts, E * 4, topk_idx, n * 4) ||
+                  overlaps(offsets, (E + 1) * 4, topk_idx, n * 4)))
+        return Q3MOE_E_ALIAS;
+    if (overlaps(counts, E * 4, offsets, (E + 1) * 4) ||
+        (n > 0 && (overlaps(pairs, n * 4, counts, E * 4) || overlaps(pairs, n * 4, offsets, (E + 1) * 4))))
+        return Q3MOE_E_ALIAS;
+    return from_hip(q3moe::launch_group_by_expert(topk_idx, n, E, counts, offsets, pairs,
+                                                  as_stream(stream)));
+}
+
 size_t q3moe_expert_ffn_workspace_bytes(int64_t T, int64_t H, int64_t F, int32_t E,
                                         int32_t top_k) {
     return q3moe::expert_ffn_workspace_bytes(T, H, F, E, top_k);

@@ -827,7 +827,6 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
 }
 
 constexpr size_t kMaxLdsPerWorkgroup = 160 * 1024;
-constexpr int kMaxDevices = 64;
 
 // Compute-unit count of the current device, cached per device (an immutable
 // device fact; the cache only saves the query on later calls).
@@ -844,24 +843,6 @@ int cu_count() {
         return 0;
     if (dev < kMaxDevices) cache[dev].store(n, std::memory_order_relaxed);
     return n;
-}
-
-// Raise a kernel's dynamic-LDS limit once per (kernel, device, size) instead
-// of on every launch, so launches inside a captured graph make no attribute
-// call.
-struct LdsLimit {
-    std::atomic<int> set[kMaxDevices];
-};
-
-hipError_t ensure_lds(const void* fn, LdsLimit& lim, int bytes) {
-    if (bytes <= 65536) return hipSuccess;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) dev = -1;
-    const bool cached = dev >= 0 && dev < kMaxDevices;
-    if (cached && bytes <= lim.set[dev].load(std::memory_order_relaxed)) return hipSuccess;
-    const hipError_t err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    if (err == hipSuccess && cached) lim.set[dev].store(bytes, std::memory_order_relaxed);
-    return err;
 }
 
 size_t gu_lds_bytes(int nb) {

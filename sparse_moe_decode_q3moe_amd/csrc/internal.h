@@ -3,6 +3,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <atomic>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -16,6 +18,30 @@ struct ExpertTensor {
 
 constexpr int kMaxTopK = 32;
 constexpr int kMaxExperts = 1024;
+
+// Raise a kernel's dynamic-LDS limit once per (kernel, device, size) instead
+// of on every launch, so launches inside a captured graph make no attribute
+// call.  One LdsLimit per kernel (a function-local static at the launch site).
+constexpr int kMaxDevices = 64;
+struct LdsLimit {
+    std::atomic<int> set[kMaxDevices];
+};
+
+inline hipError_t ensure_lds(const void* fn, LdsLimit& lim, int bytes) {
+    if (bytes <= 65536) return hipSuccess;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+    const bool cached = dev >= 0 && dev < kMaxDevices;
+    if (cached && bytes <= lim.set[dev].load(std::memory_order_relaxed)) return hipSuccess;
+    const hipError_t err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (err == hipSuccess && cached) lim.set[dev].store(bytes, std::memory_order_relaxed);
+    return err;
+}
+
+// group.hip: counts [E], offsets [E+1] and the pair list ordered by (expert,
+// pair) of idx [n] (pairs outside [0, E) are not grouped).
+hipError_t launch_group_by_expert(const int32_t* idx, int64_t n, int32_t E, int32_t* counts,
+                                  int32_t* offsets, int32_t* pairs, hipStream_t stream);
 
 // route.hip.  The route workspace starts with kRouteSyncBytes of completion
 // counters (zero before the first call; every call leaves them zero), then

@@ -29,7 +29,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(_lib.EXPORTS) == names
@@ -112,6 +112,22 @@ def test_route_validation(lib):
     assert _route(lib, hidden=FAKE_MIS) == E_ALIGN
     assert _route(lib, ws=None) == E_WORKSPACE
     assert _route(lib, T=4, ws_bytes=4096 + 4 * 128 * 8 - 1) == E_WORKSPACE
+
+
+def test_group_validation(lib):
+    G = lib.q3moe_group_by_expert
+    c, o, p = ctypes.c_void_p(0x20000), ctypes.c_void_p(0x30000), ctypes.c_void_p(0x40000)
+    assert G(FAKE, -1, 8, 128, c, o, p, None) == E_SHAPE
+    assert G(FAKE, 4, 0, 128, c, o, p, None) == E_SHAPE
+    assert G(FAKE, 4, 33, 128, c, o, p, None) == E_SHAPE
+    assert G(FAKE, 4, 8, 0, c, o, p, None) == E_SHAPE
+    assert G(FAKE, 4, 8, 1025, c, o, p, None) == E_SHAPE
+    assert G(FAKE, 1 << 28, 32, 128, c, o, p, None) == E_SHAPE
+    assert G(None, 4, 8, 128, c, o, p, None) == E_NULL
+    assert G(FAKE, 4, 8, 128, None, o, p, None) == E_NULL
+    assert G(FAKE, 4, 8, 128, c, o, None, None) == E_NULL
+    assert G(FAKE, 4, 8, 128, c, o, ctypes.c_void_p(0x10000 + 64), None) == E_ALIAS
+    assert G(FAKE, 4, 8, 128, c, ctypes.c_void_p(0x20000 + 256), p, None) == E_ALIAS
 
 
 def test_prologue_and_rmsnorm_validation(lib):
