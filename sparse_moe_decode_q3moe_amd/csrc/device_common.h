@@ -170,6 +170,43 @@ __device__ __forceinline__ Pieces4 make_pieces4(float4 v) {
     return p;
 }
 
+// Three pieces of 4 values: x = hi + mid + lo, each bf16 round-to-nearest-
+// even of what the previous ones leave, so |x - hi - mid - lo| <= 2^-27 |x|.
+// The slot holds (hi, mid) in the two-piece layout above; `lo` holds the third
+// piece as dword 0 = lo(4s) | lo(4s+2) << 16, dword 1 = lo(4s+1) | lo(4s+3) << 16.
+// Used for the gate/up input, whose rounding the outputs amplify most.
+struct Pieces4x3 {
+    uint4 slot;
+    uint2 lo;
+    float sum;      // (hi + mid + lo) summed over the 4 values
+};
+
+__device__ __forceinline__ Pieces4x3 make_pieces4x3(float4 v) {
+    const float x[4] = {v.x, v.y, v.z, v.w};
+    uint32_t hb[4], mb[4], lb[4];
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        hb[i] = bf16_rne_bits(x[i]);
+        const float r1 = x[i] - bf16_bits_to_float(hb[i]);
+        mb[i] = bf16_rne_bits(r1);
+        const float r2 = r1 - bf16_bits_to_float(mb[i]);
+        lb[i] = bf16_rne_bits(r2);
+        s += (bf16_bits_to_float(hb[i]) + bf16_bits_to_float(mb[i])) + bf16_bits_to_float(lb[i]);
+    }
+    Pieces4x3 p;
+    p.slot = make_uint4(hb[0] | (hb[2] << 16), hb[1] | (hb[3] << 16), mb[0] | (mb[2] << 16),
+                        mb[1] | (mb[3] << 16));
+    p.lo = make_uint2(lb[0] | (lb[2] << 16), lb[1] | (lb[3] << 16));
+    p.sum = s;
+    return p;
+}
+
+// LDS layout of the third pieces: 8 bytes per slot, 64 slots per 256 values
+// followed by 16 bytes of padding.
+constexpr int kBlockLoStride = 64 * 8 + 16;
+__device__ __forceinline__ int piece_lo_off(int s) { return (s >> 6) * kBlockLoStride + (s & 63) * 8; }
+
 __device__ __forceinline__ float slot_sum(uint4 s) {
     auto f = [](uint32_t w) { return bf16_bits_to_float(w & 0xffffu) + bf16_bits_to_float(w >> 16); };
     return (f(s.x) + f(s.y)) + (f(s.z) + f(s.w));

@@ -145,9 +145,8 @@ size_t down_lds(int64_t F, int32_t qtype) {
 }  // namespace
 
 size_t expert_ffn_workspace_bytes(int64_t T, int64_t H, int64_t F, int32_t E, int32_t k) {
-    (void)H;
-    (void)E;
     const int64_t t = T > 0 ? T : 0;
+    if (t >= kPrefillMinTokens) return prefill_workspace_bytes(t, H, F, E, k);
     // synchronisation words, then h (f32 or activation pieces, 4 bytes/value)
     const size_t h = (size_t)t * (size_t)k * (size_t)F * sizeof(float);
     return kFfnSyncBytes + ((h + 255) & ~(size_t)255);
@@ -167,19 +166,19 @@ hipError_t launch_expert_ffn(const float* hidden, int64_t T, int64_t H, int64_t 
                              const ExpertTensor& gate, const ExpertTensor& up,
                              const ExpertTensor& down, float* out, int accumulate, void* ws,
                              hipStream_t stream) {
+    if (T >= kPrefillMinTokens)
+        return launch_prefill_ffn(hidden, T, H, F, E, k, idx, w, gate, up, down, out, accumulate, ws,
+                                  stream);
     if (decode_ffn_supported(H, F, k))
         return launch_decode_ffn(hidden, T, H, F, E, k, idx, w, gate, up, down, out, accumulate, ws,
                                  stream);
     float* hbuf = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kFfnSyncBytes);
     const size_t l1 = gateup_lds(H), l2 = down_lds(F, down.qtype);
+    static LdsLimit lim1, lim2;
     hipError_t err;
-    if (l1 > 65536 &&
-        (err = hipFuncSetAttribute(reinterpret_cast<const void*>(gateup_q4k_kernel),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)l1)) != hipSuccess)
+    if ((err = ensure_lds(reinterpret_cast<const void*>(gateup_q4k_kernel), lim1, (int)l1)) != hipSuccess)
         return err;
-    if (l2 > 65536 &&
-        (err = hipFuncSetAttribute(reinterpret_cast<const void*>(down_combine_kernel),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)l2)) != hipSuccess)
+    if ((err = ensure_lds(reinterpret_cast<const void*>(down_combine_kernel), lim2, (int)l2)) != hipSuccess)
         return err;
     hipLaunchKernelGGL(gateup_q4k_kernel, dim3((unsigned)(T * k), (unsigned)(F / kRowTile)),
                        dim3(kThreads), l1, stream, hidden, H, F, E, k, idx, gate.base, gate.stride,

@@ -15,10 +15,10 @@
 //
 // Weights are never repacked: tiles are read in place at base + e*stride
 // with 16-byte coalesced direct-to-LDS loads, all issued before any wait.
-// Arithmetic: weights as exact small integers (bf16 128 + q), activations as
-// bf16 hi + lo pieces, v_dot2_f32_bf16 with f32 accumulation; the per-block
-// scales, the Q4_K min term and the integer offsets are applied per 16/32
-// group in f32.
+// Arithmetic: weights as exact small integers (bf16 128 + q); the gate/up
+// input as three bf16 pieces (hi + mid + lo) and h as two (hi + lo);
+// v_dot2_f32_bf16 with f32 accumulation; the per-block scales, the Q4_K min
+// term and the integer offsets are applied per 16/32 group in f32.
 #include <atomic>
 
 #include "device_common.h"
@@ -108,19 +108,22 @@ __device__ __forceinline__ void q4k_sm_var(uint32_t s0, uint32_t s1, uint32_t s2
 
 // Eight quant dwords (32 bytes, chunk c of a Q4_K block) against the pieces of
 // the matching activations: returns the two raw dot products
-// A = sum (128 + q_lo) x~ over sub-block 2c's 32 weights, B likewise for 2c+1.
-__device__ __forceinline__ void q4k_chunk_dots(const uint32_t* qw, const uint8_t* xblk, int c,
-                                               float& A, float& B) {
+// A = sum (128 + 8 q_lo) x~ over sub-block 2c's 32 weights, B likewise for
+// 2c+1.  The nibble sits in the top of the bf16 mantissa (exact), so the 128
+// offset is 16x the largest weight rather than 128x: the sums stay close to
+// the useful part and lose less to f32 rounding when the offset is removed.
+// xlo (the third pieces, or nullptr for two-piece activations) in the
+// piece_lo_off layout of the same block.
+__device__ __forceinline__ void q4k_chunk_dots(const uint32_t* qw, const uint8_t* xblk,
+                                               const uint8_t* xlo, int c, float& A, float& B) {
     float a = 0.f, b = 0.f;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
         const uint4 xa = *reinterpret_cast<const uint4*>(xblk + (16 * c + q) * kSlotBytes);
         const uint4 xb = *reinterpret_cast<const uint4*>(xblk + (16 * c + 8 + q) * kSlotBytes);
-        const uint32_t w = qw[q];
-        const uint32_t p0 = (w & 0x000f000fu) | kBf16Bias;
-        const uint32_t p1 = ((w >> 8) & 0x000f000fu) | kBf16Bias;
-        const uint32_t p2 = ((w >> 4) & 0x000f000fu) | kBf16Bias;
-        const uint32_t p3 = ((w >> 12) & 0x000f000fu) | kBf16Bias;
+        const uint32_t lo = (qw[q] << 3) & 0x78787878u, hi = (qw[q] >> 1) & 0x78787878u;
+        const uint32_t p0 = bf16_pair_even(lo), p1 = bf16_pair_odd(lo);
+        const uint32_t p2 = bf16_pair_even(hi), p3 = bf16_pair_odd(hi);
         a = dot2_bf16(p0, xa.x, a);
         a = dot2_bf16(p1, xa.y, a);
         a = dot2_bf16(p0, xa.z, a);
@@ -129,6 +132,14 @@ __device__ __forceinline__ void q4k_chunk_dots(const uint32_t* qw, const uint8_t
         b = dot2_bf16(p3, xb.y, b);
         b = dot2_bf16(p2, xb.z, b);
         b = dot2_bf16(p3, xb.w, b);
+        if (xlo) {
+            const uint2 la = *reinterpret_cast<const uint2*>(xlo + (16 * c + q) * 8);
+            const uint2 lb = *reinterpret_cast<const uint2*>(xlo + (16 * c + 8 + q) * 8);
+            a = dot2_bf16(p0, la.x, a);
+            a = dot2_bf16(p1, la.y, a);
+            b = dot2_bf16(p2, lb.x, b);
+            b = dot2_bf16(p3, lb.y, b);
+        }
     }
     A = a;
     B = b;
@@ -137,9 +148,9 @@ __device__ __forceinline__ void q4k_chunk_dots(const uint32_t* qw, const uint8_t
 // Whole Q4_K block (256 weights) in LDS against its 256 activations' pieces
 // (xblk) and group sums (gsum, 16 values).
 __device__ __forceinline__ float q4k_block_dot(const uint8_t* blk, const uint8_t* xblk,
-                                               const float* gsum) {
+                                               const uint8_t* xlo, const float* gsum) {
     const uint4 hdr = *reinterpret_cast<const uint4*>(blk);
-    const float d = half_bits_to_float(hdr.x & 0xffffu);
+    const float d8 = 0.125f * half_bits_to_float(hdr.x & 0xffffu);   // weights enter as 128 + 8q
     const float dmin = half_bits_to_float(hdr.x >> 16);
     float row = 0.f;
 #define Q3MOE_Q4K_CHUNK(C)                                                                  \
@@ -148,13 +159,13 @@ __device__ __forceinline__ float q4k_block_dot(const uint8_t* blk, const uint8_t
         const uint4 qb = *reinterpret_cast<const uint4*>(blk + 32 + 32 * (C));              \
         const uint32_t qw[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};            \
         float A, B;                                                                         \
-        q4k_chunk_dots(qw, xblk, (C), A, B);                                                \
+        q4k_chunk_dots(qw, xblk, xlo, (C), A, B);                                           \
         int sc0, mn0, sc1, mn1;                                                             \
         q4k_sm_const<2 * (C)>(hdr.y, hdr.z, hdr.w, sc0, mn0);                               \
         q4k_sm_const<2 * (C) + 1>(hdr.y, hdr.z, hdr.w, sc1, mn1);                           \
         const float sx0 = gsum[4 * (C)] + gsum[4 * (C) + 1];                                \
         const float sx1 = gsum[4 * (C) + 2] + gsum[4 * (C) + 3];                            \
-        row += d * ((float)sc0 * (A - 128.f * sx0) + (float)sc1 * (B - 128.f * sx1)) -      \
+        row += d8 * ((float)sc0 * (A - 128.f * sx0) + (float)sc1 * (B - 128.f * sx1)) -     \
                dmin * ((float)mn0 * sx0 + (float)mn1 * sx1);                                \
     }
     Q3MOE_Q4K_CHUNK(0)
@@ -169,10 +180,12 @@ __device__ __forceinline__ float q4k_block_dot(const uint8_t* blk, const uint8_t
 // in LDS, using all threads of the workgroup.  H/4 is a multiple of 64 so
 // every wave that enters the loop is full.
 __device__ __forceinline__ void activations_to_pieces(const float* __restrict__ x, int H,
-                                                      uint8_t* xp, float* gs, int tid, int nthr) {
+                                                      uint8_t* xp, uint8_t* xlo, float* gs, int tid,
+                                                      int nthr) {
     for (int s = tid; s < H / 4; s += nthr) {
-        const Pieces4 pc = make_pieces4(reinterpret_cast<const float4*>(x)[s]);
+        const Pieces4x3 pc = make_pieces4x3(reinterpret_cast<const float4*>(x)[s]);
         *reinterpret_cast<uint4*>(xp + piece_slot_off(s)) = pc.slot;
+        *reinterpret_cast<uint2*>(xlo + piece_lo_off(s)) = pc.lo;
         float g = pc.sum + __shfl_xor(pc.sum, 1, kWave);
         g += __shfl_xor(g, 2, kWave);
         if ((s & 3) == 0) gs[s >> 2] = g;
@@ -201,13 +214,13 @@ __device__ __forceinline__ void gu_issue(const uint8_t* __restrict__ gbase, int6
 // Lane = m*32 + rho*NB + b: matrix m (0 gate, 1 up), row rho of the task,
 // super-block b of the row.  Writes h = silu(g)*u of the R rows as pieces.
 template <int NB>
-__device__ __forceinline__ void gu_compute(const uint8_t* wg, const uint8_t* xp, const float* gs,
-                                           bool valid, int lane, uint8_t* __restrict__ hpieces,
-                                           int64_t value_base) {
+__device__ __forceinline__ void gu_compute(const uint8_t* wg, const uint8_t* xp, const uint8_t* xlo,
+                                           const float* gs, bool valid, int lane,
+                                           uint8_t* __restrict__ hpieces, int64_t value_base) {
     using G = GuTask<NB>;
     const int m = lane >> 5, rho = (lane & 31) / NB, b = lane % NB;
     float row = valid ? q4k_block_dot(wg + m * G::TASKB + rho * G::ROWB + b * kQ4KBytes,
-                                      xp + b * kBlockPieceStride, gs + b * 16)
+                                      xp + b * kBlockPieceStride, xlo + b * kBlockLoStride, gs + b * 16)
                       : 0.f;
 #pragma unroll
     for (int o = 1; o < NB; o <<= 1) row += __shfl_xor(row, o, kWave);
@@ -235,20 +248,26 @@ __device__ __forceinline__ void gu_compute(const uint8_t* wg, const uint8_t* xp,
 // partials are folded across the wave with a transposed butterfly: after it,
 // lanes 8q..8q+7 hold row q (q < 4 gate row q, else up row q-4).
 struct XCols {
-    uint4 lo[4], hi[4];      // pieces of the low-nibble and high-nibble values
+    uint4 lo[4], hi[4];      // (hi, mid) pieces of the low-nibble and high-nibble values
+    uint2 lo3[4], hi3[4];    // their third pieces
     float slo, shi;          // their sums (one 16-value group each)
 };
 
 // The lane's 32 activations of one token from the token's piece blocks in
-// LDS (xp: 8 blocks of kBlockPieceStride bytes; gs: the 16-value group sums).
-__device__ __forceinline__ XCols load_xcols(const uint8_t* xp, const float* gs, int lane) {
+// LDS (xp: 8 blocks of kBlockPieceStride bytes; gs: the 16-value group sums;
+// xlo: the third pieces, 8 blocks of kBlockLoStride bytes).
+__device__ __forceinline__ XCols load_xcols(const uint8_t* xp, const float* gs, const uint8_t* xlo,
+                                            int lane) {
     const int b = lane >> 3, c = (lane >> 1) & 3, hp = lane & 1;
     const uint8_t* xb = xp + b * kBlockPieceStride;
+    const uint8_t* xl = xlo + b * kBlockLoStride;
     XCols x;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         x.lo[q] = *reinterpret_cast<const uint4*>(xb + (16 * c + 4 * hp + q) * kSlotBytes);
         x.hi[q] = *reinterpret_cast<const uint4*>(xb + (16 * c + 8 + 4 * hp + q) * kSlotBytes);
+        x.lo3[q] = *reinterpret_cast<const uint2*>(xl + (16 * c + 4 * hp + q) * 8);
+        x.hi3[q] = *reinterpret_cast<const uint2*>(xl + (16 * c + 8 + 4 * hp + q) * 8);
     }
     x.slo = gs[b * 16 + 4 * c + hp];
     x.shi = gs[b * 16 + 4 * c + 2 + hp];
@@ -263,8 +282,8 @@ __device__ __forceinline__ float q4k_cols_row(uint4 hdr, uint4 qv, const XCols& 
     float A = 0.f, B = 0.f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const uint32_t lo = qw[q] & 0x0f0f0f0fu;              // low nibbles of the 4 bytes
-        const uint32_t hi = (qw[q] >> 4) & 0x0f0f0f0fu;       // high nibbles
+        const uint32_t lo = (qw[q] << 3) & 0x78787878u;       // 8 * low nibbles of the 4 bytes
+        const uint32_t hi = (qw[q] >> 1) & 0x78787878u;       // 8 * high nibbles
         const uint32_t p0 = bf16_pair_even(lo), p1 = bf16_pair_odd(lo);
         const uint32_t p2 = bf16_pair_even(hi), p3 = bf16_pair_odd(hi);
         A = dot2_bf16(p0, x.lo[q].x, A);
@@ -275,13 +294,17 @@ __device__ __forceinline__ float q4k_cols_row(uint4 hdr, uint4 qv, const XCols& 
         B = dot2_bf16(p3, x.hi[q].y, B);
         B = dot2_bf16(p2, x.hi[q].z, B);
         B = dot2_bf16(p3, x.hi[q].w, B);
+        A = dot2_bf16(p0, x.lo3[q].x, A);
+        A = dot2_bf16(p1, x.lo3[q].y, A);
+        B = dot2_bf16(p2, x.hi3[q].x, B);
+        B = dot2_bf16(p3, x.hi3[q].y, B);
     }
     int sc0, mn0, sc1, mn1;
     q4k_sm_var(hdr.y, hdr.z, hdr.w, 2 * c, sc0, mn0);
     q4k_sm_var(hdr.y, hdr.z, hdr.w, 2 * c + 1, sc1, mn1);
     const float d = half_bits_to_float(hdr.x & 0xffffu);
     const float dmin = half_bits_to_float(hdr.x >> 16);
-    return d * ((float)sc0 * (A - 128.f * x.slo) + (float)sc1 * (B - 128.f * x.shi)) -
+    return 0.125f * d * ((float)sc0 * (A - 128.f * x.slo) + (float)sc1 * (B - 128.f * x.shi)) -
            dmin * ((float)mn0 * x.slo + (float)mn1 * x.shi);
 }
 
@@ -321,6 +344,7 @@ __global__ __launch_bounds__(kGuWaves * kWave) void gu_decode_kernel(
     uint8_t* wg = smem + wave * 2 * G::TASKB;
     uint8_t* xp = smem + kGuWaves * 2 * G::TASKB;
     float* gs = reinterpret_cast<float*>(xp + NB * kBlockPieceStride);
+    uint8_t* xlo = reinterpret_cast<uint8_t*>(gs + NB * 16);
 
     const int tiles = (int)(F / G::R);                    // tasks per pair, a multiple of kGuWaves
     const int64_t task = (int64_t)blockIdx.x * kGuWaves + wave;
@@ -330,10 +354,10 @@ __global__ __launch_bounds__(kGuWaves * kWave) void gu_decode_kernel(
     const int e = idx[p];
     const bool valid = e >= 0 && e < E;
     if (valid) gu_issue<NB>(gbase, gstride, ubase, ustride, e, r0, wg, lane);
-    activations_to_pieces(hidden + t * G::H, G::H, xp, gs, tid, kGuWaves * kWave);
+    activations_to_pieces(hidden + t * G::H, G::H, xp, xlo, gs, tid, kGuWaves * kWave);
     wait_all_loads();
     __syncthreads();
-    gu_compute<NB>(wg, xp, gs, valid, lane, hpieces, p * F + r0);
+    gu_compute<NB>(wg, xp, xlo, gs, valid, lane, hpieces, p * F + r0);
 }
 
 // ----------------------------------------------------------------- down --
@@ -389,7 +413,7 @@ __device__ __forceinline__ float q4k_lane_dot(const uint8_t* blk, int c, const u
     const uint4 qb = *reinterpret_cast<const uint4*>(blk + 32 + 32 * c);
     const uint32_t qw[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
     float A, B;
-    q4k_chunk_dots(qw, xblk, c, A, B);
+    q4k_chunk_dots(qw, xblk, nullptr, c, A, B);
     int sc0, mn0, sc1, mn1;
     q4k_sm_var(hdr.y, hdr.z, hdr.w, 2 * c, sc0, mn0);
     q4k_sm_var(hdr.y, hdr.z, hdr.w, 2 * c + 1, sc1, mn1);
@@ -397,7 +421,7 @@ __device__ __forceinline__ float q4k_lane_dot(const uint8_t* blk, int c, const u
     const float dmin = half_bits_to_float(hdr.x >> 16);
     const float sx0 = gsum[4 * c] + gsum[4 * c + 1];
     const float sx1 = gsum[4 * c + 2] + gsum[4 * c + 3];
-    return d * ((float)sc0 * (A - 128.f * sx0) + (float)sc1 * (B - 128.f * sx1)) -
+    return 0.125f * d * ((float)sc0 * (A - 128.f * sx0) + (float)sc1 * (B - 128.f * sx1)) -
            dmin * ((float)mn0 * sx0 + (float)mn1 * sx1);
 }
 
@@ -624,7 +648,7 @@ struct FusedLds {
 __host__ __device__ inline FusedLds fused_lds(int64_t T, int64_t F, int32_t qtype) {
     const DnGeom d(F, qtype);
     FusedLds L;
-    L.xp_bytes = kFzNB * kBlockPieceStride + kFzNB * 16 * 4;       // pieces + group sums per token
+    L.xp_bytes = kFzNB * kBlockPieceStride + kFzNB * 16 * 4 + kFzNB * kBlockLoStride;       // pieces + group sums per token
     L.dn_off = (int)T * L.xp_bytes;                                 // down tiles, one per slot
     L.hp_off = L.dn_off + kFzMaxSlots * d.tile_pad;                 // h pieces + group sums per slot
     L.res_off = L.hp_off + kFzMaxSlots * (d.pieces + d.sums);       // [slot][block][row] partials
@@ -679,8 +703,9 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
     for (int j = 0; j < kFzMaxTokens; ++j) {
         if (j < T) {                                           // whole workgroup in or out
             uint8_t* xp = smem + j * L.xp_bytes;
-            const Pieces4 pc = make_pieces4(xv[j]);
+            const Pieces4x3 pc = make_pieces4x3(xv[j]);
             *reinterpret_cast<uint4*>(xp + piece_slot_off(tid)) = pc.slot;
+            *reinterpret_cast<uint2*>(xp + kFzNB * kBlockPieceStride + kFzNB * 16 * 4 + piece_lo_off(tid)) = pc.lo;
             float g = pc.sum + __shfl_xor(pc.sum, 1, kWave);
             g += __shfl_xor(g, 2, kWave);
             if ((tid & 3) == 0) reinterpret_cast<float*>(xp + kFzNB * kBlockPieceStride)[tid >> 2] = g;
@@ -700,7 +725,8 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
             gu_rows_load(rows, e, E, gbase, gstride, ubase, ustride, r0, lane);
             if (t != xc) {
                 const uint8_t* xp = smem + t * L.xp_bytes;
-                x = load_xcols(xp, reinterpret_cast<const float*>(xp + kFzNB * kBlockPieceStride), lane);
+                x = load_xcols(xp, reinterpret_cast<const float*>(xp + kFzNB * kBlockPieceStride),
+                               xp + kFzNB * kBlockPieceStride + kFzNB * 16 * 4, lane);
                 xc = t;
             }
             gu_rows_finish(rows, x, lane, hpieces, p * F + r0);
@@ -848,7 +874,8 @@ int cu_count() {
 size_t gu_lds_bytes(int nb) {
     const int R = 32 / nb;
     const size_t taskb = (size_t)R * nb * kQ4KBytes;
-    return kGuWaves * 2 * taskb + (size_t)nb * kBlockPieceStride + (size_t)nb * 16 * 4;
+    return kGuWaves * 2 * taskb + (size_t)nb * kBlockPieceStride + (size_t)nb * 16 * 4 +
+           (size_t)nb * kBlockLoStride;
 }
 
 size_t down_lds_bytes(int64_t F, int32_t qtype) {

@@ -26,7 +26,8 @@ constexpr int kGrpIndexBits = 10;                       // E <= 1024
 
 __global__ __launch_bounds__(kGrpThreads) void group_by_expert_kernel(
     const int32_t* __restrict__ idx, int64_t n, int32_t E, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ pairs) {
+    int32_t* __restrict__ offsets, int32_t* __restrict__ pairs, int32_t* __restrict__ tile_off,
+    int32_t tile_rows) {
     extern __shared__ int32_t lds_i32[];
     int32_t* hist = lds_i32;                            // [wave][E]
     int32_t* scan = lds_i32 + kGrpWaves * E;            // [kGrpThreads]
@@ -70,6 +71,19 @@ __global__ __launch_bounds__(kGrpThreads) void group_by_expert_kernel(
     }
     if (tid == kGrpThreads - 1) offsets[E] = scan[tid];
     __syncthreads();
+    if (tile_off) {                                     // tiles of tile_rows pairs per expert
+        const int32_t tiles = (total + tile_rows - 1) / tile_rows;
+        scan[tid] = tiles;
+        __syncthreads();
+        for (int off = 1; off < kGrpThreads; off <<= 1) {
+            const int32_t v = tid >= off ? scan[tid - off] : 0;
+            __syncthreads();
+            scan[tid] += v;
+            __syncthreads();
+        }
+        if (tid < E) tile_off[tid] = scan[tid] - tiles;
+        if (tid == kGrpThreads - 1) tile_off[E] = scan[tid];
+    }
 
     const uint64_t lower = (1ull << lane) - 1ull;
     for (int64_t c0 = b0; c0 < b1; c0 += kWave) {
@@ -96,13 +110,14 @@ __global__ __launch_bounds__(kGrpThreads) void group_by_expert_kernel(
 }  // namespace
 
 hipError_t launch_group_by_expert(const int32_t* idx, int64_t n, int32_t E, int32_t* counts,
-                                  int32_t* offsets, int32_t* pairs, hipStream_t stream) {
+                                  int32_t* offsets, int32_t* pairs, hipStream_t stream,
+                                  int32_t* tile_off, int32_t tile_rows) {
     const size_t lds = ((size_t)kGrpWaves * E + kGrpThreads) * sizeof(int32_t);
     static LdsLimit lds_set;
     const hipError_t err = ensure_lds(reinterpret_cast<const void*>(group_by_expert_kernel), lds_set, (int)lds);
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(group_by_expert_kernel, dim3(1), dim3(kGrpThreads), lds, stream, idx, n, E,
-                       counts, offsets, pairs);
+                       counts, offsets, pairs, tile_off, tile_rows);
     return hipGetLastError();
 }
 

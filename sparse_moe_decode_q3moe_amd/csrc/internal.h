@@ -39,9 +39,21 @@ inline hipError_t ensure_lds(const void* fn, LdsLimit& lim, int bytes) {
 }
 
 // group.hip: counts [E], offsets [E+1] and the pair list ordered by (expert,
-// pair) of idx [n] (pairs outside [0, E) are not grouped).
+// pair) of idx [n] (pairs outside [0, E) are not grouped); optionally also
+// tile_off [E+1], the exclusive prefix of ceil(counts / tile_rows).
 hipError_t launch_group_by_expert(const int32_t* idx, int64_t n, int32_t E, int32_t* counts,
-                                  int32_t* offsets, int32_t* pairs, hipStream_t stream);
+                                  int32_t* offsets, int32_t* pairs, hipStream_t stream,
+                                  int32_t* tile_off = nullptr, int32_t tile_rows = 1);
+
+// prefill.hip: the batched expert FFN for larger T (tokens grouped by
+// expert, matrix-core tiles).  Workspace layout in prefill_workspace_bytes.
+constexpr int64_t kPrefillMinTokens = 32;
+size_t prefill_workspace_bytes(int64_t T, int64_t H, int64_t F, int32_t E, int32_t k);
+hipError_t launch_prefill_ffn(const float* hidden, int64_t T, int64_t H, int64_t F, int32_t E,
+                              int32_t k, const int32_t* idx, const float* w,
+                              const ExpertTensor& gate, const ExpertTensor& up,
+                              const ExpertTensor& down, float* out, int accumulate, void* ws,
+                              hipStream_t stream);
 
 // route.hip.  The route workspace starts with kRouteSyncBytes of completion
 // counters (zero before the first call; every call leaves them zero), then

@@ -110,6 +110,13 @@ FFN_CASES = {  # name: (shape, seed)
     "generic_H768": (gen.MoeShape(T=3, H=768, E=6, k=2, F=512, down_qtype=gen.Q6_K), 20),
     "generic_H2560_q4k_down": (gen.MoeShape(T=2, H=2560, E=4, k=2, F=256, down_qtype=gen.Q4_K), 21),
     "a3b_k1_T2": (gen.MoeShape(T=2, H=2048, E=128, k=1, F=768, down_qtype=gen.Q6_K), 22),
+    # T >= 32: the batched path (grouping + matrix-core tiles)
+    "a3b_prefill_T512": (gen.MoeShape(T=512, H=2048, E=128, k=8, F=768, down_qtype=gen.Q6_K), 23),
+    "a3b_prefill_q4k_down_T64": (gen.MoeShape(T=64, H=2048, E=128, k=8, F=768, down_qtype=gen.Q4_K), 24),
+    "prefill_tiny_T40": (gen.MoeShape(T=40, H=256, E=8, k=2, F=256, down_qtype=gen.Q4_K), 25),
+    "prefill_ragged_T37_F512": (gen.MoeShape(T=37, H=512, E=6, k=3, F=512, down_qtype=gen.Q6_K), 26),
+    "prefill_k32_T33": (gen.MoeShape(T=33, H=256, E=32, k=32, F=256, down_qtype=gen.Q6_K), 27),
+    "prefill_H4096_F1536": (gen.MoeShape(T=32, H=4096, E=4, k=2, F=1536, down_qtype=gen.Q6_K), 28),
 }
 
 
@@ -140,7 +147,25 @@ def test_moe_block_parity(layers, name):
     say(f"  max rel L2 {err:.2e}")
 
 
-@pytest.mark.parametrize("name", ["tiny_T4", "a3b_decode_T1", "a3b_q4k_down_T3"])
+def test_prefill_skewed_routing(layers):
+    """The 512-token prefill with half the tokens sent to the same 4 hot
+    experts (tiles of ~280 pairs for those experts)."""
+    cpu, dev, x = layers("a3b_prefill_T512")
+    s = cpu.shape
+    say("prefill skewed routing, T=512")
+    xs, rs = gen.skewed_hidden_and_router(cpu, x, seed=31)
+    skew = gen.MoeLayer(s, rs, cpu.gate, cpu.up, cpu.down)
+    ref_idx, ref_w, logits, ref = oracle_moe(skew, xs.numpy())
+    counts = np.bincount(ref_idx.reshape(-1), minlength=s.E)
+    assert np.sort(counts)[-4:].min() >= 200
+    idx, w, out = gpu_moe(gen.MoeLayer(s, rs.to(DEV), dev.gate, dev.up, dev.down), xs.to(DEV))
+    torch.cuda.synchronize()
+    assert_indices_equal(idx.cpu().numpy(), ref_idx, logits, s.k, "skewed prefill")
+    err = assert_rows_close(out.cpu().numpy(), ref, what="skewed prefill")
+    say(f"  max rel L2 {err:.2e}")
+
+
+@pytest.mark.parametrize("name", ["tiny_T4", "a3b_decode_T1", "a3b_q4k_down_T3", "prefill_tiny_T40"])
 def test_accumulate_adds_to_out(layers, name):
     cpu, dev, x = layers(name)
     s = cpu.shape
@@ -170,8 +195,9 @@ def test_expert_ffn_given_routing(layers):
     assert_rows_close(out.cpu().numpy(), ref, what="fixed routing")
 
 
-def test_out_of_range_index_contributes_zero(layers):
-    cpu, dev, x = layers("tiny_T4")
+@pytest.mark.parametrize("name", ["tiny_T4", "prefill_tiny_T40"])
+def test_out_of_range_index_contributes_zero(layers, name):
+    cpu, dev, x = layers(name)
     s = cpu.shape
     say("out-of-range expert index")
     o = oracle.oracle()
