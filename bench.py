@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=20,
                     help="replays of the FFN-only graph used for kernel timing")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the 512-token prefill measurement")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="for hardware-counter runs: a few eager steps (no graph), then one "
                          "device-to-device copy of PMC_COPY_BYTES that calibrates the "
@@ -234,12 +236,102 @@ def main():
         },
     }
 
+    if not args.no_prefill:
+        result["prefill_512"] = prefill_bench(torch, q3, gen, layers, experts, shape, dev)
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, torch, gen, layers, xs, outs, shape)
 
     print(json.dumps(result), flush=True)
     if result.get("cpu_baseline", {}).get("guard_ok") is False:
         sys.exit(1)
+
+
+PREFILL_T = 512
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def prefill_bench(torch, q3, gen, layers, experts, shape, dev):
+    """The same layer at T = 512 tokens per step (the batched path: grouping
+    by expert and matrix-core tiles), uniform and skewed routing.  Steps
+    rotate through the 16 layer copies; each step touches (almost) every
+    expert, ~392 MB of weights.  Reported beside the batch-1 decode figure."""
+    import math as _m
+    T, H, E, k, F = PREFILL_T, shape.H, shape.E, shape.k, shape.F
+    x_uni = gen.hidden_states(T, H, 8, device=dev)
+    variants = {"uniform": [(x_uni, L.router) for L in layers]}
+    skewed = []
+    for i, L in enumerate(layers):
+        xs_, rs_ = gen.skewed_hidden_and_router(L, x_uni, seed=40 + i)
+        skewed.append((xs_, rs_))
+    variants["skewed"] = skewed
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    wts = torch.empty((T, k), dtype=torch.float32, device=dev)
+    out = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ws_r = torch.zeros(q3.q3moe_route_workspace_bytes(T, E), dtype=torch.uint8, device=dev)
+    ws_f = torch.zeros(q3.q3moe_expert_ffn_workspace_bytes(T, H, F, E, k), dtype=torch.uint8, device=dev)
+    res = {"tokens_per_step": T}
+    expert_b = shape.gate_stride * 2 + shape.down_stride
+    flops = 2.0 * T * k * (2 * F * H + H * F)
+    for name, inputs in variants.items():
+        def step(i, inputs=inputs):
+            xv, rv = inputs[i % len(inputs)]
+            q3.q3moe_route(xv, rv, k, idx, wts, workspace=ws_r)
+            q3.q3moe_expert_ffn(xv, idx, wts, *experts[i % len(experts)], F=F, out=out, workspace=ws_f)
+
+        def ffn_only(i, inputs=inputs):
+            xv, _ = inputs[i % len(inputs)]
+            q3.q3moe_expert_ffn(xv, idx, wts, *experts[i % len(experts)], F=F, out=out, workspace=ws_f)
+
+        n = len(layers)
+        for i in range(n):
+            step(i)
+        torch.cuda.synchronize()
+        distinct = []
+        for i in range(n):                                  # experts each step touches
+            step(i)
+            distinct.append(int(torch.unique(idx).numel()))
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                step(i)
+        gf = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gf):
+            for i in range(n):
+                ffn_only(i)
+        g.replay(); gf.replay()
+        torch.cuda.synchronize()
+        reps = 3
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        step_ms = a.elapsed_time(b) / (reps * n)
+        a.record()
+        for _ in range(reps):
+            gf.replay()
+        b.record()
+        torch.cuda.synchronize()
+        ffn_us = a.elapsed_time(b) * 1000.0 / (reps * n)
+        d_avg = sum(distinct) / len(distinct)
+        ffn_bytes = d_avg * expert_b + 2 * T * H * 4
+        res[name] = {
+            "tokens_per_s": round(T / (step_ms * 1e-3), 1),
+            "ms_per_step": round(step_ms, 4),
+            "ffn_us": round(ffn_us, 2),
+            "distinct_experts_per_step": round(d_avg, 2),
+            "ffn_hbm_gbps": round(ffn_bytes / (ffn_us * 1e-6) / 1e9, 1),
+            "ffn_hbm_frac": round(ffn_bytes / (ffn_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "ffn_tflops": round(flops / (ffn_us * 1e-6) / 1e12, 2),
+            "ffn_mfma_frac": round(flops / (ffn_us * 1e-6) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+        }
+        del g, gf
+    res["note"] = ("bf16 matrix-core tiles with the activations split into bf16 pieces (3 for "
+                   "gate/up, 2 for down), so the MFMA work is 2.5x the algorithmic flops")
+    return res
 
 
 def cpu_baseline(args, torch, gen, layers, xs, outs, shape):

@@ -10,7 +10,7 @@
 //   2. pieces of the hidden rows: bf16 hi + mid + lo (x to 2^-27; the
 //      gate/up outputs amplify the input's rounding most) and the f32 sum of
 //      every 16 values;
-//   3. gate/up: one workgroup per (expert tile, 64 features).  Per super-block
+//   3. gate/up: one workgroup per (64 features, expert tile).  Per super-block
 //      the tile's activation pieces and both weight tiles are gathered into
 //      LDS with direct-to-LDS loads.  Each 16-wide k step runs
 //      v_mfma_f32_16x16x16 on exact bf16 weights (128 + q) with each
@@ -18,7 +18,7 @@
 //      the 128 offset and the Q4_K min are removed through the group sums.
 //      h = silu(g) * u goes to the workspace in grouped row order;
 //   4. pieces of h (hi + lo);
-//   5. down: one workgroup per (expert tile, 64 output rows), Q6_K or Q4_K,
+//   5. down: one workgroup per (64 output rows, expert tile), Q6_K or Q4_K,
 //      the whole row tile of the expert's down matrix resident in LDS;
 //      rows go to Y indexed by pair;
 //   6. combine: out[t] = [out +] sum over slots in slot order of w * Y.
@@ -143,15 +143,15 @@ __device__ __forceinline__ int pf_tile_expert(const int32_t* tile_off, int32_t E
 }
 
 // ---------------------------------------------------------------- gate/up --
-// LDS: activation pieces hi, mid, lo [32 rows][256] bf16, group sums
-// [32][16] f32, gate and up weight tiles [64 rows][144 B] of the current
-// super-block.
+// LDS: activation pieces hi, mid, lo of the 32 rows x 256 values (k-major:
+// 16-byte chunk c of row i at (c * 32 + i) * 16), group sums [16][32] f32,
+// gate and up weight tiles [64 rows][144 B] of the current super-block.
 constexpr int kGuXBytes = kPfRows * kQK * 2;                  // 16 KiB per piece array
 constexpr int kGuSBytes = kPfRows * 16 * 4;
 constexpr int kGuWBytes = kPfCols * kQ4KBytes;                // 9216
 constexpr int kGuLds = 3 * kGuXBytes + kGuSBytes + 2 * kGuWBytes;
 
-__global__ __launch_bounds__(kPfThreads) void pf_gateup_kernel(
+__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2))) void pf_gateup_kernel(
     const uint16_t* __restrict__ xhi, const uint16_t* __restrict__ xmid,
     const uint16_t* __restrict__ xlo, const float* __restrict__ xs16, int64_t H, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ tile_off, const int32_t* __restrict__ pairs, int32_t E, int32_t k,
@@ -165,26 +165,23 @@ __global__ __launch_bounds__(kPfThreads) void pf_gateup_kernel(
     uint8_t* lwg = smem + 3 * kGuXBytes + kGuSBytes;
     uint8_t* lwu = lwg + kGuWBytes;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int slot = blockIdx.x;
+    const int slot = blockIdx.y;          // feature tiles run fastest: neighbours share the rows
     if (slot >= tile_off[E]) return;                          // uniform: an unused tile slot
     const int e = pf_tile_expert(tile_off, E, slot);
     const int64_t row0 = offsets[e] + (int64_t)(slot - tile_off[e]) * kPfRows;
     const int nrows = (int)min((int64_t)kPfRows, (int64_t)offsets[e + 1] - row0);
-    const int64_t f0 = (int64_t)blockIdx.y * kPfCols;
+    const int64_t f0 = (int64_t)blockIdx.x * kPfCols;
     const int64_t nsb = H / kQK;
     const int64_t rowb = nsb * kQ4KBytes;                     // bytes per gate/up row
     const uint8_t* gexp = gbase + (int64_t)e * gstride + f0 * rowb;
     const uint8_t* uexp = ubase + (int64_t)e * ustride + f0 * rowb;
 
-    // the token of each row this thread stages (piece loads: row = q >> 5)
-    int64_t tok[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int i = (j * kPfThreads + tid) >> 5;
-        tok[j] = i < nrows ? pairs[row0 + i] / k : -1;
-    }
-    const int64_t tok_s = (tid < 128 && (tid >> 2) < nrows) ? pairs[row0 + (tid >> 2)] / k : -1;
-
+    // activation pieces are staged k-major: 16-byte chunk c (8 values) of row
+    // i at LDS (c * 32 + i) * 16, so the 16 rows an MFMA operand read touches
+    // are 16 consecutive chunks (no bank conflicts); thread tid stages row
+    // tid % 32.  Group sums are staged as [group][row] with 4-byte loads.
+    const int my_row = tid & 31;
+    const int64_t my_tok = my_row < nrows ? pairs[row0 + my_row] / k : -1;
     const int col = lane & 15, kq = lane >> 4;               // MFMA column / k quarter
     const int frow = wave * 16 + col;                        // this lane's weight row in the tile
     f32x4_t acc[2][2];
@@ -194,11 +191,11 @@ __global__ __launch_bounds__(kPfThreads) void pf_gateup_kernel(
 
     for (int64_t sb = 0; sb < nsb; ++sb) {
         __syncthreads();                                      // the previous stage is consumed
+        if (my_tok >= 0) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {                         // 32 rows x 32 pieces of 16 B
-            const int q = j * kPfThreads + tid;
-            if (tok[j] >= 0) {
-                const int64_t off = (tok[j] * H + sb * kQK) * 2 + (q & 31) * 16;
+            for (int j = 0; j < 4; ++j) {                     // 32 chunks x 32 rows of 16 B
+                const int c = (j * kPfThreads + tid) >> 5;
+                const int64_t off = (my_tok * H + sb * kQK) * 2 + c * 16;
                 const int lo16 = (j * kPfThreads + wave * kWave) * 16;
                 __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(xhi) + off,
                                                  (lds_ptr_t)(lx_hi + lo16), 16, 0, 0);
@@ -207,10 +204,14 @@ __global__ __launch_bounds__(kPfThreads) void pf_gateup_kernel(
                 __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(xlo) + off,
                                                  (lds_ptr_t)(lx_lo + lo16), 16, 0, 0);
             }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {                     // 16 groups x 32 rows of 4 B
+                const int g = (j * kPfThreads + tid) >> 5;
+                __builtin_amdgcn_global_load_lds(xs16 + my_tok * (H / 16) + sb * 16 + g,
+                                                 (lds_ptr_t)(smem + 3 * kGuXBytes + (j * kPfThreads + wave * kWave) * 4),
+                                                 4, 0, 0);
+            }
         }
-        if (tok_s >= 0)                                       // 32 rows x 4 pieces of group sums
-            __builtin_amdgcn_global_load_lds(xs16 + tok_s * (H / 16) + sb * 16 + (tid & 3) * 4,
-                                             (lds_ptr_t)(smem + 3 * kGuXBytes + wave * kWave * 16), 16, 0, 0);
 #pragma unroll
         for (int j = 0; j < 3; ++j) {                         // 64 rows x 9 pieces per matrix
             const int q = j * kPfThreads + tid;
@@ -237,10 +238,12 @@ __global__ __launch_bounds__(kPfThreads) void pf_gateup_kernel(
             const s16x4_t bu = pf_bf16x4(((*reinterpret_cast<const uint32_t*>(lwu + qoff) >> (4 * h)) << 3) & 0x78787878u);
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) {
-                const int xoff = ((rb * 16 + col) * kQK + kk) * 2;
+                const int xoff = ((kk >> 3) * kPfRows + rb * 16 + col) * 16 + (kk & 7) * 2;
                 const s16x4_t ah = *reinterpret_cast<const s16x4_t*>(lx_hi + xoff);
                 const s16x4_t am = *reinterpret_cast<const s16x4_t*>(lx_mid + xoff);
                 const s16x4_t al = *reinterpret_cast<const s16x4_t*>(lx_lo + xoff);
+                const float4 S4 = *reinterpret_cast<const float4*>(ls16 + s * kPfRows + rb * 16 + 4 * kq);
+                const float Sv[4] = {S4.x, S4.y, S4.z, S4.w};
                 f32x4_t tg = pf_mfma(ah, bg, f32x4_t{0.f, 0.f, 0.f, 0.f});
                 tg = pf_mfma(am, bg, tg);
                 tg = pf_mfma(al, bg, tg);
@@ -249,9 +252,8 @@ __global__ __launch_bounds__(kPfThreads) void pf_gateup_kernel(
                 tu = pf_mfma(al, bu, tu);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float S = ls16[(rb * 16 + 4 * kq + r) * 16 + s];
-                    acc[rb][0][r] += gs[j] * tg[r] - gb[j] * S;
-                    acc[rb][1][r] += us[j] * tu[r] - ub[j] * S;
+                    acc[rb][0][r] += gs[j] * tg[r] - gb[j] * Sv[r];
+                    acc[rb][1][r] += us[j] * tu[r] - ub[j] * Sv[r];
                 }
             }
         }
@@ -268,15 +270,17 @@ __global__ __launch_bounds__(kPfThreads) void pf_gateup_kernel(
 // ------------------------------------------------------------------- down --
 // LDS: the expert's down rows h0..h0+63 (all F/256 blocks, contiguous in HBM,
 // + 16 bytes of padding for the unaligned Q6_K reads), then the h pieces of
-// the tile for the current super-block and their group sums.
+// the tile for the current super-block (k-major), their group sums [16][32],
+// and the (scale, offset) of every (row, 16-wide group) of the super-block.
 __host__ __device__ inline int pf_down_wbytes(int64_t F, int32_t qtype) {
     return (int)(kPfCols * (F / kQK) * (qtype == 2 ? kQ6KBytes : kQ4KBytes));
 }
+constexpr int kDnFacBytes = kPfCols * 16 * 8;                 // (scale, offset) per row and group
 __host__ __device__ inline int pf_down_lds(int64_t F, int32_t qtype) {
-    return pf_down_wbytes(F, qtype) + 16 + 2 * kGuXBytes + kGuSBytes;
+    return pf_down_wbytes(F, qtype) + 16 + 2 * kGuXBytes + kGuSBytes + kDnFacBytes;
 }
 
-__global__ __launch_bounds__(kPfThreads) void pf_down_kernel(
+__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2))) void pf_down_kernel(
     const uint16_t* __restrict__ hhi, const uint16_t* __restrict__ hlo,
     const float* __restrict__ hs16, int64_t F, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ tile_off, const int32_t* __restrict__ pairs, int32_t E,
@@ -284,12 +288,12 @@ __global__ __launch_bounds__(kPfThreads) void pf_down_kernel(
     float* __restrict__ Y) {
     extern __shared__ __align__(16) uint8_t smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int slot = blockIdx.x;
+    const int slot = blockIdx.y;          // output-row tiles run fastest: neighbours share h
     if (slot >= tile_off[E]) return;
     const int e = pf_tile_expert(tile_off, E, slot);
     const int64_t row0 = offsets[e] + (int64_t)(slot - tile_off[e]) * kPfRows;
     const int nrows = (int)min((int64_t)kPfRows, (int64_t)offsets[e + 1] - row0);
-    const int64_t h0 = (int64_t)blockIdx.y * kPfCols;
+    const int64_t h0 = (int64_t)blockIdx.x * kPfCols;
     const bool q6 = qtype == 2;
     const int bb = q6 ? kQ6KBytes : kQ4KBytes;
     const int64_t nsb = F / kQK;
@@ -299,6 +303,7 @@ __global__ __launch_bounds__(kPfThreads) void pf_down_kernel(
     uint8_t* lx_hi = smem + wbytes + 16;
     uint8_t* lx_lo = lx_hi + kGuXBytes;
     const float* ls16 = reinterpret_cast<const float*>(lx_lo + kGuXBytes);
+    float2* lfac = reinterpret_cast<float2*>(lx_lo + kGuXBytes + kGuSBytes);   // [row][group]
 
     // the whole row tile of the down matrix, once
     {
@@ -310,6 +315,7 @@ __global__ __launch_bounds__(kPfThreads) void pf_down_kernel(
                                                  kCachePolicyNt);
     }
 
+    const int my_row = tid & 31;
     const int col = lane & 15, kq = lane >> 4;
     const int frow = wave * 16 + col;
     const uint8_t* wrow = lw + frow * rowb;
@@ -317,45 +323,61 @@ __global__ __launch_bounds__(kPfThreads) void pf_down_kernel(
 
     for (int64_t sb = 0; sb < nsb; ++sb) {
         __syncthreads();
+        if (my_row < nrows) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {                         // 32 rows x 32 pieces of 16 B
-            const int q = j * kPfThreads + tid;
-            const int i = q >> 5;
-            if (i < nrows) {
-                const int64_t off = ((row0 + i) * F + sb * kQK) * 2 + (q & 31) * 16;
+            for (int j = 0; j < 4; ++j) {                     // 32 chunks x 32 rows of 16 B, k-major
+                const int c = (j * kPfThreads + tid) >> 5;
+                const int64_t off = ((row0 + my_row) * F + sb * kQK) * 2 + c * 16;
+                const int lo16 = (j * kPfThreads + wave * kWave) * 16;
                 __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(hhi) + off,
-                                                 (lds_ptr_t)(lx_hi + (j * kPfThreads + wave * kWave) * 16), 16, 0, 0);
+                                                 (lds_ptr_t)(lx_hi + lo16), 16, 0, 0);
                 __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(hlo) + off,
-                                                 (lds_ptr_t)(lx_lo + (j * kPfThreads + wave * kWave) * 16), 16, 0, 0);
+                                                 (lds_ptr_t)(lx_lo + lo16), 16, 0, 0);
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {                     // 16 groups x 32 rows of 4 B
+                const int g = (j * kPfThreads + tid) >> 5;
+                __builtin_amdgcn_global_load_lds(hs16 + (row0 + my_row) * (F / 16) + sb * 16 + g,
+                                                 (lds_ptr_t)(lx_lo + kGuXBytes + (j * kPfThreads + wave * kWave) * 4),
+                                                 4, 0, 0);
             }
         }
-        if (tid < 128 && (tid >> 2) < nrows)
-            __builtin_amdgcn_global_load_lds(hs16 + (row0 + (tid >> 2)) * (F / 16) + sb * 16 + (tid & 3) * 4,
-                                             (lds_ptr_t)(lx_lo + kGuXBytes + wave * kWave * 16), 16, 0, 0);
         wait_all_loads();
         __syncthreads();
 
-        const uint8_t* blk = wrow + sb * bb;
-        float fs[16], fb[16];                                 // per 16-wide group of this row
-        if (q6) {
-            const float d = half_bits_to_float(blk[208] | (blk[209] << 8));
-#pragma unroll
-            for (int g = 0; g < 16; ++g) {
-                fs[g] = d * (float)(int8_t)blk[192 + g];
-                fb[g] = 160.f * fs[g];                        // (128 + q) - 160 = q - 32
+        // (scale, offset) of every (row, 16-wide group) of this super-block
+        for (int f = tid; f < kPfCols * 16; f += kPfThreads) {
+            const int r = f >> 4, g = f & 15;
+            const uint8_t* b = lw + r * rowb + sb * bb;
+            float sc, off;
+            if (q6) {
+                sc = half_bits_to_float(b[208] | (b[209] << 8)) * (float)(int8_t)b[192 + g];
+                off = 160.f * sc;                             // (128 + q) - 160 = q - 32
+            } else {
+                const uint4 hdr = *reinterpret_cast<const uint4*>(b);
+                int scj, mj;
+                const int j = g >> 1;
+                const uint32_t s0 = hdr.y, s1 = hdr.z, s2 = hdr.w;
+                if (j < 4) {
+                    scj = (s0 >> (8 * j)) & 63;
+                    mj = (s1 >> (8 * j)) & 63;
+                } else {
+                    const int jj = j - 4;
+                    scj = ((s2 >> (8 * jj)) & 15) | (((s0 >> (8 * jj + 6)) & 3) << 4);
+                    mj = ((s2 >> (8 * jj + 4)) & 15) | (((s1 >> (8 * jj + 6)) & 3) << 4);
+                }
+                sc = 0.125f * half_bits_to_float(hdr.x & 0xffffu) * (float)scj;   // 128 + 8q
+                off = 128.f * sc + half_bits_to_float(hdr.x >> 16) * (float)mj;
             }
-        } else {
-            float s8[8], b8[8];
-            pf_q4k_factors(blk, s8, b8);
-#pragma unroll
-            for (int g = 0; g < 16; ++g) {
-                fs[g] = s8[g >> 1];
-                fb[g] = b8[g >> 1];
-            }
+            lfac[f] = make_float2(sc, off);
         }
-#pragma unroll
+        __syncthreads();
+
+        const uint8_t* blk = wrow + sb * bb;
+#pragma unroll 4
         for (int s = 0; s < 16; ++s) {
             const int kk = 16 * s + 4 * kq;
+            const float2 fac = lfac[frow * 16 + s];
             uint32_t q;
             if (q6) {
                 const int n = kk >> 7, r = (kk >> 5) & 3, lp = kk & 31;
@@ -369,12 +391,14 @@ __global__ __launch_bounds__(kPfThreads) void pf_down_kernel(
             const s16x4_t bw = pf_bf16x4(q);
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) {
-                const int xoff = ((rb * 16 + col) * kQK + kk) * 2;
+                const int xoff = ((kk >> 3) * kPfRows + rb * 16 + col) * 16 + (kk & 7) * 2;
                 f32x4_t t = pf_mfma(*reinterpret_cast<const s16x4_t*>(lx_hi + xoff), bw, f32x4_t{0.f, 0.f, 0.f, 0.f});
                 t = pf_mfma(*reinterpret_cast<const s16x4_t*>(lx_lo + xoff), bw, t);
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    acc[rb][r] += fs[s] * t[r] - fb[s] * ls16[(rb * 16 + 4 * kq + r) * 16 + s];
+                const float4 S4 = *reinterpret_cast<const float4*>(ls16 + s * kPfRows + rb * 16 + 4 * kq);
+                acc[rb][0] += fac.x * t[0] - fac.y * S4.x;
+                acc[rb][1] += fac.x * t[1] - fac.y * S4.y;
+                acc[rb][2] += fac.x * t[2] - fac.y * S4.z;
+                acc[rb][3] += fac.x * t[3] - fac.y * S4.w;
             }
         }
     }
@@ -482,7 +506,7 @@ hipError_t launch_prefill_ffn(const float* hidden, int64_t T, int64_t H, int64_t
     static LdsLimit gu_lds;
     if ((err = ensure_lds(reinterpret_cast<const void*>(pf_gateup_kernel), gu_lds, kGuLds)) != hipSuccess)
         return err;
-    hipLaunchKernelGGL(pf_gateup_kernel, dim3(slots, (unsigned)(F / kPfCols)), dim3(kPfThreads), kGuLds,
+    hipLaunchKernelGGL(pf_gateup_kernel, dim3((unsigned)(F / kPfCols), slots), dim3(kPfThreads), kGuLds,
                        stream, reinterpret_cast<const uint16_t*>(base + L.xhi),
                        reinterpret_cast<const uint16_t*>(base + L.xmid),
                        reinterpret_cast<const uint16_t*>(base + L.xlo),
@@ -502,7 +526,7 @@ hipError_t launch_prefill_ffn(const float* hidden, int64_t T, int64_t H, int64_t
     if ((err = ensure_lds(reinterpret_cast<const void*>(pf_down_kernel), down_lds, dl)) != hipSuccess)
         return err;
     float* Y = reinterpret_cast<float*>(base + L.y);
-    hipLaunchKernelGGL(pf_down_kernel, dim3(slots, (unsigned)(H / kPfCols)), dim3(kPfThreads), dl, stream,
+    hipLaunchKernelGGL(pf_down_kernel, dim3((unsigned)(H / kPfCols), slots), dim3(kPfThreads), dl, stream,
                        reinterpret_cast<const uint16_t*>(base + L.hhi),
                        reinterpret_cast<const uint16_t*>(base + L.hlo),
                        reinterpret_cast<const float*>(base + L.hs16), F, offsets, tile_off, pairs, E,
