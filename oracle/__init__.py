@@ -19,6 +19,13 @@ Parity status per function (how each is pinned is listed in the tests):
   rope_neox                       NEOX-vs-interleaved discriminator
   group_by_expert                 pinned: a library sort of (expert, pair),
                                   a hand-worked example, count/offset invariants
+  bf16 conversions                pinned: all 65,536 bf16 patterns and a sweep of
+                                  f32 values against torch.bfloat16
+  bf16_gemv                       pinned: dense NumPy product, one-hot probes
+  kv_write                        pinned: torch.bfloat16 rounding, untouched slots
+  gqa_attention                   pinned: brute-force NumPy softmax per head,
+                                  one-position and equal-key closed forms,
+                                  one-hot kv-head probe of the GQA mapping
 Agreement with real GGUF files is not pinned (no files; the bit layout is
 the GGUF k-quant reading).
 """
@@ -77,6 +84,12 @@ def _declare(lib):
                                           _P, ctypes.c_int, _I64, _P, ctypes.c_int]),
         "orc_rmsnorm": (ctypes.c_int, [_P, _I64, _I64, _P, ctypes.c_float, _P]),
         "orc_group_by_expert": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _P, _P]),
+        "orc_bf16_to_double": (ctypes.c_double, [ctypes.c_uint16]),
+        "orc_float_to_bf16": (ctypes.c_uint16, [ctypes.c_float]),
+        "orc_bf16_gemv": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _P, ctypes.c_int]),
+        "orc_kv_write": (ctypes.c_int, [_P, _P, _I64, _I32, _I32, _P, _P, _P, _I64]),
+        "orc_gqa_attention": (ctypes.c_int, [_P, _I64, _I32, _I32, _I32, _P, _P, _I64, _P,
+                                             ctypes.c_double, _P]),
         "orc_rope_neox": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, ctypes.c_double]),
         "orc_attn_prologue": (ctypes.c_int, [_P, _P, _I64, _I32, _I32, _I32, _P, _P, _P,
                                              ctypes.c_float, ctypes.c_float]),
@@ -181,6 +194,48 @@ class Oracle:
         assert self.lib.orc_group_by_expert(_p(idx), T, k, E, _p(counts), _p(offsets),
                                             _p(pairs)) == 0
         return counts, offsets, pairs[:offsets[E]].copy()
+
+    def float_to_bf16(self, f: float) -> int:
+        return self.lib.orc_float_to_bf16(f)
+
+    def bf16_to_double(self, b: int) -> float:
+        return self.lib.orc_bf16_to_double(b)
+
+    def bf16_gemv(self, W: np.ndarray, x: np.ndarray, y: np.ndarray | None = None,
+                  accumulate: bool = False) -> np.ndarray:
+        """W uint16 bf16 bits [N, K], x f32 [T, K] -> f32 [T, N] (y + W x when accumulating)."""
+        W = _c(W, np.uint16)
+        x = _c(x, np.float32)
+        N, K = W.shape
+        T = x.shape[0]
+        out = np.zeros((T, N), np.float32) if y is None else _c(y, np.float32).copy()
+        assert self.lib.orc_bf16_gemv(_p(W), N, K, _p(x), T, _p(out), 1 if accumulate else 0) == 0
+        return out
+
+    def kv_write(self, k_new, v_new, pos, kcache, vcache):
+        """In place on copies of kcache / vcache (uint16 [B, n_kv, S_max, D]); returns them."""
+        k_new = _c(k_new, np.float32)
+        v_new = _c(v_new, np.float32)
+        pos = _c(pos, np.int32)
+        kc = _c(kcache, np.uint16).copy()
+        vc = _c(vcache, np.uint16).copy()
+        B, n_kv, S_max, D = kc.shape
+        assert self.lib.orc_kv_write(_p(k_new), _p(v_new), B, n_kv, D, _p(pos), _p(kc), _p(vc),
+                                     S_max) == 0
+        return kc, vc
+
+    def gqa_attention(self, q, kcache, vcache, lengths, scale: float) -> np.ndarray:
+        """q f32 [B, n_q, D]; caches uint16 [B, n_kv, S_max, D]; lengths int32 [B]."""
+        q = _c(q, np.float32)
+        kc = _c(kcache, np.uint16)
+        vc = _c(vcache, np.uint16)
+        lengths = _c(lengths, np.int32)
+        B, n_q, D = q.shape
+        n_kv, S_max = kc.shape[1], kc.shape[2]
+        out = np.empty_like(q)
+        assert self.lib.orc_gqa_attention(_p(q), B, n_q, n_kv, D, _p(kc), _p(vc), S_max,
+                                          _p(lengths), float(scale), _p(out)) == 0
+        return out
 
     def _ffn_args(self, x, idx, w, gate, up, down, F, E):
         x = _c(x, np.float32)

@@ -42,6 +42,13 @@
  *  - RMSNorm: y = g * x / sqrt(mean(x^2) + eps).
  *  - RoPE frequencies: theta_i = pos * base^(-2i/D), i < D/2, all D dims
  *    rotated.
+ *  - Decoder-layer pieces (the projections and the attention around the MoE
+ *    block): bf16 weights of N output rows x K inputs stored row-major; no
+ *    projection bias; the KV cache of a sequence holds bf16 k and v
+ *    [n_kv][S_max][D]; a decode step writes the new token's k and v at its
+ *    position p (round to nearest even) and attends over positions 0..p;
+ *    query head h reads kv head h / (n_q / n_kv); scores are scaled by the
+ *    given scale (1/sqrt(D) in the layer).
  */
 #include <math.h>
 #include <stdint.h>
@@ -303,6 +310,102 @@ int orc_group_by_expert(const int32_t *idx, int64_t T, int32_t k, int32_t E,
         counts[e] = (int32_t)(pos - offsets[e]);
     }
     offsets[E] = (int32_t)pos;
+    return 0;
+}
+
+/* IEEE 754 bfloat16 (the top 16 bits of a binary32) -> double, and binary32
+ * -> bfloat16 rounding to nearest, ties to even, both from the format. */
+double orc_bf16_to_double(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+uint16_t orc_float_to_bf16(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu))
+        return (uint16_t)((u >> 16) | 0x40);                 /* NaN stays NaN */
+    uint32_t rest = u & 0xffffu, keep = u >> 16;
+    if (rest > 0x8000u || (rest == 0x8000u && (keep & 1u))) keep += 1;
+    return (uint16_t)keep;
+}
+
+/* y[t][n] = sum_k W[n][k] x[t][k] with W bf16 [N][K] (the attention
+ * projections of the decoder layer), in double, rounded to f32; with
+ * accumulate the product is added to y (the residual add after O). */
+int orc_bf16_gemv(const uint16_t *W, int64_t N, int64_t K, const float *x, int64_t T,
+                  float *y, int accumulate)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; n++)
+        for (int64_t t = 0; t < T; t++) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; k++)
+                acc += orc_bf16_to_double(W[n * K + k]) * (double)x[t * K + k];
+            y[t * N + n] = (float)((accumulate ? (double)y[t * N + n] : 0.0) + acc);
+        }
+    return 0;
+}
+
+/* Write the new token's k and v (f32 [B][n_kv][D]) into each sequence's
+ * bf16 cache [B][n_kv][S_max][D] at position pos[b]. */
+int orc_kv_write(const float *k_new, const float *v_new, int64_t B, int32_t n_kv, int32_t D,
+                 const int32_t *pos, uint16_t *kcache, uint16_t *vcache, int64_t S_max)
+{
+    for (int64_t b = 0; b < B; b++) {
+        if (pos[b] < 0 || pos[b] >= S_max) return -1;
+        for (int32_t g = 0; g < n_kv; g++)
+            for (int32_t i = 0; i < D; i++) {
+                int64_t src = (b * n_kv + g) * (int64_t)D + i;
+                int64_t dst = ((b * n_kv + g) * S_max + pos[b]) * (int64_t)D + i;
+                kcache[dst] = orc_float_to_bf16(k_new[src]);
+                vcache[dst] = orc_float_to_bf16(v_new[src]);
+            }
+    }
+    return 0;
+}
+
+/* Grouped-query decode attention: for sequence b and query head h (kv head
+ * g = h / (n_q / n_kv)), over positions j < len[b]:
+ *   s_j = scale * q . k_j,  p = softmax(s),  out = sum_j p_j v_j,
+ * all in double (max subtracted), rounded to f32. */
+int orc_gqa_attention(const float *q, int64_t B, int32_t n_q, int32_t n_kv, int32_t D,
+                      const uint16_t *kcache, const uint16_t *vcache, int64_t S_max,
+                      const int32_t *len, double scale, float *out)
+{
+    if (n_q % n_kv) return -1;
+    int32_t group = n_q / n_kv;
+    for (int64_t b = 0; b < B; b++)
+        if (len[b] < 1 || len[b] > S_max) return -1;
+    #pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t b = 0; b < B; b++)
+        for (int32_t h = 0; h < n_q; h++) {
+            int32_t g = h / group;
+            int64_t L = len[b];
+            const float *qh = q + (b * n_q + h) * (int64_t)D;
+            const uint16_t *K = kcache + (b * n_kv + g) * S_max * (int64_t)D;
+            const uint16_t *V = vcache + (b * n_kv + g) * S_max * (int64_t)D;
+            double *sc = (double *)malloc(sizeof(double) * L);
+            double mx = -INFINITY;
+            for (int64_t j = 0; j < L; j++) {
+                double d = 0.0;
+                for (int32_t i = 0; i < D; i++) d += (double)qh[i] * orc_bf16_to_double(K[j * D + i]);
+                sc[j] = scale * d;
+                if (sc[j] > mx) mx = sc[j];
+            }
+            double den = 0.0;
+            for (int64_t j = 0; j < L; j++) { sc[j] = exp(sc[j] - mx); den += sc[j]; }
+            for (int32_t i = 0; i < D; i++) {
+                double acc = 0.0;
+                for (int64_t j = 0; j < L; j++) acc += sc[j] * orc_bf16_to_double(V[j * D + i]);
+                out[(b * n_q + h) * (int64_t)D + i] = (float)(acc / den);
+            }
+            free(sc);
+        }
     return 0;
 }
 

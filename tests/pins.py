@@ -566,4 +566,135 @@ def pin_group_skewed_routing(o):
         assert counts[e] >= T // 2
 
 
+# ------------------------------------------------- decoder-layer pieces --
+
+def _torch_bf16_bits(a) -> np.ndarray:
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def _bits_to_f64(b) -> np.ndarray:
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(b, np.uint16).view(np.int16)).view(
+        torch.bfloat16).double().numpy()
+
+
+def pin_bf16_all_patterns(o):
+    """All 65,536 bfloat16 patterns against torch's own bfloat16 widening."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = _bits_to_f64(bits)
+    got = np.array([o.bf16_to_double(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+def pin_float_to_bf16_rounding(o):
+    """Round to nearest even against torch.bfloat16 on random values, exact
+    ties (odd and even), values that round up into the next binade, and
+    signed zeros / infinities."""
+    rng = np.random.default_rng(41)
+    vals = list(rng.standard_normal(2000).astype(np.float32) * 10.0 ** rng.integers(-6, 6, 2000))
+    for base in (1.0, 1.5, 3.0, -2.25, 1e-3, 6e4):
+        b = np.float32(base).view(np.uint32)
+        for low in (0x7fff, 0x8000, 0x8001, 0x18000, 0xffff):
+            vals.append(np.uint32((int(b) & 0xffff0000) | low).view(np.float32))
+    vals += [np.float32(0.0), np.float32(-0.0), np.float32(np.inf), np.float32(-np.inf)]
+    vals = np.array(vals, np.float32)
+    got = np.array([o.float_to_bf16(float(v)) for v in vals], np.uint16)
+    assert np.array_equal(got, _torch_bf16_bits(vals))
+
+
+def pin_bf16_gemv_dense(o):
+    """Random bf16 weights against a dense NumPy product; one-hot probes pin
+    the orientation (y[t][n] reads row n of W and x[t]); accumulate adds."""
+    rng = np.random.default_rng(42)
+    N, K, T = 48, 96, 3
+    W = _torch_bf16_bits(rng.standard_normal((N, K)).astype(np.float32) * 0.05)
+    x = rng.standard_normal((T, K)).astype(np.float32)
+    _close(o.bf16_gemv(W, x), x.astype(np.float64) @ _bits_to_f64(W).T, 1e-7, "bf16 gemv")
+    one = np.zeros((N, K), np.uint16)
+    one[7, 30] = _torch_bf16_bits(np.array([1.0]))[0]
+    y = o.bf16_gemv(one, x)
+    assert np.array_equal(y[:, 7], x[:, 30]) and np.count_nonzero(y) == np.count_nonzero(x[:, 30])
+    prev = rng.standard_normal((T, N)).astype(np.float32)
+    _close(o.bf16_gemv(W, x, prev, accumulate=True),
+           prev + x.astype(np.float64) @ _bits_to_f64(W).T, 1e-7, "bf16 gemv accumulate")
+
+
+def pin_kv_write(o):
+    """The new k, v land at each sequence's position as torch.bfloat16 bits;
+    every other slot is untouched."""
+    rng = np.random.default_rng(43)
+    B, nkv, S, D = 3, 2, 7, 8
+    kc = rng.integers(0, 65535, (B, nkv, S, D)).astype(np.uint16)
+    vc = rng.integers(0, 65535, (B, nkv, S, D)).astype(np.uint16)
+    kn = rng.standard_normal((B, nkv, D)).astype(np.float32)
+    vn = rng.standard_normal((B, nkv, D)).astype(np.float32)
+    pos = np.array([0, 6, 3], np.int32)
+    k2, v2 = o.kv_write(kn, vn, pos, kc, vc)
+    for b in range(B):
+        assert np.array_equal(k2[b, :, pos[b]], _torch_bf16_bits(kn[b]))
+        assert np.array_equal(v2[b, :, pos[b]], _torch_bf16_bits(vn[b]))
+    mask = np.ones((B, nkv, S), bool)
+    mask[np.arange(B), :, pos] = False
+    assert np.array_equal(k2[mask], kc[mask]) and np.array_equal(v2[mask], vc[mask])
+
+
+def _attention_numpy(q, kc, vc, lengths, scale):
+    B, nq, D = q.shape
+    nkv = kc.shape[1]
+    K, V = _bits_to_f64(kc), _bits_to_f64(vc)
+    out = np.empty((B, nq, D))
+    for b in range(B):
+        for h in range(nq):
+            g = h // (nq // nkv)
+            L = lengths[b]
+            sc = scale * (K[b, g, :L] @ q[b, h].astype(np.float64))
+            p = scipy.special.softmax(sc)
+            out[b, h] = p @ V[b, g, :L]
+    return out
+
+
+def pin_attention_bruteforce(o):
+    rng = np.random.default_rng(44)
+    B, nq, nkv, D, S = 2, 8, 2, 16, 12
+    q = rng.standard_normal((B, nq, D)).astype(np.float32)
+    kc = _torch_bf16_bits(rng.standard_normal((B, nkv, S, D)).astype(np.float32))
+    vc = _torch_bf16_bits(rng.standard_normal((B, nkv, S, D)).astype(np.float32))
+    lengths = np.array([5, 12], np.int32)
+    scale = 1.0 / math.sqrt(D)
+    _close(o.gqa_attention(q, kc, vc, lengths, scale), _attention_numpy(q, kc, vc, lengths, scale),
+           1e-7, "gqa attention")
+
+
+def pin_attention_closed_forms(o):
+    """One position: the output is that position's v.  Equal keys: uniform
+    weights, the mean of v over the positions."""
+    rng = np.random.default_rng(45)
+    B, nq, nkv, D, S = 1, 4, 1, 8, 6
+    q = rng.standard_normal((B, nq, D)).astype(np.float32)
+    kc = _torch_bf16_bits(rng.standard_normal((B, nkv, S, D)).astype(np.float32))
+    vc = _torch_bf16_bits(rng.standard_normal((B, nkv, S, D)).astype(np.float32))
+    out1 = o.gqa_attention(q, kc, vc, np.array([1], np.int32), 0.3)
+    assert np.array_equal(out1[0], np.broadcast_to(_bits_to_f64(vc[0, 0, 0]).astype(np.float32), (nq, D)))
+    kc_eq = np.broadcast_to(kc[:, :, :1], kc.shape).copy()
+    outm = o.gqa_attention(q, kc_eq, vc, np.array([S], np.int32), 0.3)
+    _close(outm[0], np.broadcast_to(_bits_to_f64(vc[0, 0]).mean(0), (nq, D)), 1e-7, "equal keys")
+
+
+def pin_attention_gqa_mapping(o):
+    """v of kv head g is the constant g: query head h must read g = h / (n_q / n_kv)."""
+    B, nq, nkv, D, S = 1, 8, 4, 4, 3
+    rng = np.random.default_rng(46)
+    q = rng.standard_normal((B, nq, D)).astype(np.float32)
+    kc = _torch_bf16_bits(rng.standard_normal((B, nkv, S, D)).astype(np.float32))
+    vc = np.zeros((B, nkv, S, D), np.float32)
+    for g in range(nkv):
+        vc[0, g] = g
+    out = o.gqa_attention(q, kc, _torch_bf16_bits(vc), np.array([S], np.int32), 0.5)
+    assert np.allclose(out[0, :, 0], np.arange(nq) // (nq // nkv))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

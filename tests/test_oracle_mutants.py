@@ -54,6 +54,15 @@ MUTANTS = [
     ("group_keeps_last_pair_out", "for (int64_t p = 0; p < n; p++)\n            if (idx[p] == e)", "for (int64_t p = 0; p + 1 < n; p++)\n            if (idx[p] == e)"),
     ("group_token_not_pair", "if (idx[p] == e) pairs[pos++] = (int32_t)p;", "if (idx[p] == e) pairs[pos++] = (int32_t)(p / k);"),
     ("group_reverse_order", "for (int64_t p = 0; p < n; p++)\n            if (idx[p] == e)", "for (int64_t p = n - 1; p >= 0; p--)\n            if (idx[p] == e)"),
+    ("bf16_round_truncates", "if (rest > 0x8000u || (rest == 0x8000u && (keep & 1u))) keep += 1;", "if (rest > 0x8000u) keep += 1;"),
+    ("bf16_widen_wrong_shift", "uint32_t u = (uint32_t)b << 16;", "uint32_t u = (uint32_t)b << 15;"),
+    ("gemv_column_major", "orc_bf16_to_double(W[n * K + k])", "orc_bf16_to_double(W[k * N + n])"),
+    ("gemv_accumulate_ignored", "(accumulate ? (double)y[t * N + n] : 0.0)", "0.0"),
+    ("kv_write_wrong_slot", "int64_t dst = ((b * n_kv + g) * S_max + pos[b]) * (int64_t)D + i;", "int64_t dst = ((b * n_kv + g) * S_max + pos[b] - (pos[b] > 0)) * (int64_t)D + i;"),
+    ("gqa_interleaved_heads", "int32_t g = h / group;", "int32_t g = h % n_kv;"),
+    ("attention_scale_dropped", "sc[j] = scale * d;", "sc[j] = d;"),
+    ("attention_one_past_length", "int64_t L = len[b];", "int64_t L = len[b] < S_max ? len[b] + 1 : len[b];"),
+    ("attention_k_as_v", "acc += sc[j] * orc_bf16_to_double(V[j * D + i]);", "acc += sc[j] * orc_bf16_to_double(K[j * D + i]);"),
     ("prologue_head_dim_halved", "rmsnorm_vec(v, D, g, (double)eps, y);", "rmsnorm_vec(v, D / 2, g, (double)eps, y); rmsnorm_vec(v + D / 2, D / 2, g, (double)eps, y + D / 2);"),
 ]
 
