@@ -205,6 +205,66 @@ q3moe_status q3moe_attn_prologue(float *q, float *k, int64_t T, int32_t n_q_head
 q3moe_status q3moe_rmsnorm(const float *x, int64_t T, int64_t n, const float *gain,
                            float eps, float *out, void *stream);
 
+/* ------------------------------------------------- decoder layer: attention --
+ * The attention side of the full Qwen3-MoE decoder layer that the MoE block
+ * sits in (aprender issue #3714: "File facts" gives 32 query heads, 4 kv
+ * heads, head_dim 128, hidden 2048; gap G3 asks for a device-resident model
+ * with a per-layer KV cache and Qwen3 attention).  One decode step of a
+ * layer, per sequence b at position p = pos[b]:
+ *   xn = rmsnorm(x); q = Wq xn; k = Wk xn; v = Wv xn      (q3moe_bf16_gemv)
+ *   per-head Q/K RMSNorm + NEOX RoPE at p                  (q3moe_attn_prologue)
+ *   k, v -> cache slot p                                   (q3moe_kv_write)
+ *   a = attention(q, cache[0..p])                          (q3moe_gqa_attention)
+ *   x += Wo a                                              (q3moe_bf16_gemv, accumulate)
+ *   then rmsnorm, route and the expert FFN with accumulate.
+ * The projections have no bias. */
+
+/* y[t][n] = (accumulate ? y[t][n] : 0) + sum_k W[n][k] * x[t][k].
+ *   W [N x K] bf16 (raw bits, row-major), 16-byte aligned; x [T x K] f32,
+ *   16-byte aligned; y [T x N] f32 (must not overlap W or x).
+ * Products and sums are formed in f32 (each bf16 weight is exact in f32).
+ * The weights are read once per 16 tokens.
+ * Limits: K % 8 == 0, 8 <= K <= 2^30, 1 <= N <= 2^30, accumulate 0 or 1.
+ * Errors: E_NULL, E_SHAPE, E_ALIGN, E_ALIAS, E_HIP. */
+q3moe_status q3moe_bf16_gemv(const uint16_t *W, int64_t N, int64_t K, const float *x, int64_t T,
+                             float *y, int32_t accumulate, void *stream);
+
+/* Store the new token's keys and values in the bf16 KV caches:
+ *   k_cache[b][g][pos[b]][i] = bf16(k_new[b][g][i]), likewise v,
+ * for b < B, g < n_kv_heads, i < head_dim.  Caches are
+ * [B x n_kv_heads x S_max x head_dim] bf16 (raw bits); conversion rounds to
+ * nearest, ties to even (NaN stays NaN).  positions is a device array; an
+ * entry outside [0, S_max) writes nothing for that sequence.
+ * Limits: n_kv_heads * head_dim <= 65536, S_max >= 1.
+ * Errors: E_NULL, E_SHAPE, E_ALIAS (caches overlap each other or an input),
+ * E_HIP. */
+q3moe_status q3moe_kv_write(const float *k_new, const float *v_new, int64_t B,
+                            int32_t n_kv_heads, int32_t head_dim, const int32_t *positions,
+                            uint16_t *k_cache, uint16_t *v_cache, int64_t S_max, void *stream);
+
+/* Grouped-query decode attention.  For sequence b and query head h, with
+ * kv head g = h / (n_q_heads / n_kv_heads) and L = lengths[b]:
+ *   s_j = scale * q[b][h] . k_cache[b][g][j],  j < L
+ *   out[b][h] = sum_j softmax(s)_j * v_cache[b][g][j]
+ *   q [B x n_q_heads x head_dim] f32, 16-byte aligned; caches as for
+ *   q3moe_kv_write, 16-byte aligned; out like q, 4-byte aligned.
+ * Scores, the softmax and the sums are f32.  lengths is a device array; a
+ * length outside [1, S_max] gives NaN outputs for that sequence and reads no
+ * cache row.  No mask beyond the length (decode attends to every cached
+ * position); the usual scale is 1/sqrt(head_dim).
+ * workspace: at least q3moe_gqa_attention_workspace_bytes(...) bytes,
+ * 16-byte aligned, for per-chunk partial results; no state survives a call.
+ * Limits: head_dim in {64, 128, 256}; n_q_heads % n_kv_heads == 0;
+ * n_q_heads / n_kv_heads <= 16; B <= 65535; scale finite.
+ * Errors: E_NULL, E_SHAPE, E_ALIGN, E_WORKSPACE, E_ALIAS, E_HIP. */
+size_t q3moe_gqa_attention_workspace_bytes(int64_t B, int32_t n_q_heads, int32_t n_kv_heads,
+                                           int32_t head_dim, int64_t S_max);
+q3moe_status q3moe_gqa_attention(const float *q, int64_t B, int32_t n_q_heads,
+                                 int32_t n_kv_heads, int32_t head_dim, const uint16_t *k_cache,
+                                 const uint16_t *v_cache, int64_t S_max, const int32_t *lengths,
+                                 float scale, float *out, void *workspace,
+                                 size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

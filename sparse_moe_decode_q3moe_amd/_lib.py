@@ -22,7 +22,8 @@ EXPORTS = (
     "q3moe_status_string", "q3moe_qtype_block_bytes", "q3moe_expert_matrix_bytes",
     "q3moe_route_workspace_bytes", "q3moe_route", "q3moe_group_by_expert",
     "q3moe_expert_ffn_workspace_bytes", "q3moe_expert_ffn_status_offset", "q3moe_expert_ffn",
-    "q3moe_attn_prologue", "q3moe_rmsnorm",
+    "q3moe_attn_prologue", "q3moe_rmsnorm", "q3moe_bf16_gemv", "q3moe_kv_write",
+    "q3moe_gqa_attention_workspace_bytes", "q3moe_gqa_attention",
 )
 
 
@@ -51,6 +52,11 @@ _SIGS = {
                                 _Experts, _P, _I32, _P, ctypes.c_size_t, _P]),
     "q3moe_attn_prologue": (_I32, [_P, _P, _I64, _I32, _I32, _I32, _P, _P, _P, _F, _F, _P]),
     "q3moe_rmsnorm": (_I32, [_P, _I64, _I64, _P, _F, _P, _P]),
+    "q3moe_bf16_gemv": (_I32, [_P, _I64, _I64, _P, _I64, _P, _I32, _P]),
+    "q3moe_kv_write": (_I32, [_P, _P, _I64, _I32, _I32, _P, _P, _P, _I64, _P]),
+    "q3moe_gqa_attention_workspace_bytes": (ctypes.c_size_t, [_I64, _I32, _I32, _I32, _I64]),
+    "q3moe_gqa_attention": (_I32, [_P, _I64, _I32, _I32, _I32, _P, _P, _I64, _P, _F, _P, _P,
+                                   ctypes.c_size_t, _P]),
 }
 
 _lib = None
@@ -240,4 +246,75 @@ def q3moe_rmsnorm(x: torch.Tensor, gain: torch.Tensor, eps: float,
     _need(out, "out", torch.float32, 2)
     _check("q3moe_rmsnorm", library().q3moe_rmsnorm(
         _ptr(x), T, n, _ptr(gain), eps, _ptr(out), _stream(stream)))
+    return out
+
+
+def q3moe_bf16_gemv(W: torch.Tensor, x: torch.Tensor, out: Optional[torch.Tensor] = None,
+                    accumulate: bool = False, stream=None) -> torch.Tensor:
+    """out [T, N] (+)= x [T, K] @ W[N, K]^T with W bfloat16, x and out f32."""
+    _need(W, "W", torch.bfloat16, 2)
+    _need(x, "x", torch.float32, 2)
+    N, K = W.shape
+    T = x.shape[0]
+    if x.shape[1] != K:
+        raise ValueError("x must be [T, K] with K = W.shape[1]")
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate=True needs an existing out tensor")
+        out = torch.empty((T, N), dtype=torch.float32, device=x.device)
+    _need(out, "out", torch.float32, 2)
+    if tuple(out.shape) != (T, N):
+        raise ValueError("out must be [T, N]")
+    _check("q3moe_bf16_gemv", library().q3moe_bf16_gemv(
+        _ptr(W), N, K, _ptr(x), T, _ptr(out), 1 if accumulate else 0, _stream(stream)))
+    return out
+
+
+def q3moe_kv_write(k_new: torch.Tensor, v_new: torch.Tensor, positions: torch.Tensor,
+                   k_cache: torch.Tensor, v_cache: torch.Tensor, stream=None) -> None:
+    """Write k_new / v_new f32 [B, n_kv, D] into the bfloat16 caches
+    [B, n_kv, S_max, D] at positions int32 [B]."""
+    _need(k_new, "k_new", torch.float32, 3)
+    _need(v_new, "v_new", torch.float32, 3)
+    _need(positions, "positions", torch.int32, 1)
+    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    _need(v_cache, "v_cache", torch.bfloat16, 4)
+    B, nkv, D = k_new.shape
+    S_max = k_cache.shape[2]
+    if tuple(v_new.shape) != (B, nkv, D) or positions.numel() != B \
+            or tuple(k_cache.shape) != (B, nkv, S_max, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("inconsistent KV-write shapes")
+    _check("q3moe_kv_write", library().q3moe_kv_write(
+        _ptr(k_new), _ptr(v_new), B, nkv, D, _ptr(positions), _ptr(k_cache), _ptr(v_cache),
+        S_max, _stream(stream)))
+
+
+def q3moe_gqa_attention_workspace_bytes(B: int, n_q: int, n_kv: int, D: int, S_max: int) -> int:
+    return library().q3moe_gqa_attention_workspace_bytes(B, n_q, n_kv, D, S_max)
+
+
+def q3moe_gqa_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                        lengths: torch.Tensor, scale: float, out: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Decode attention of q f32 [B, n_q, D] over the first lengths[b]
+    positions of the bfloat16 caches [B, n_kv, S_max, D]; returns out f32
+    [B, n_q, D]."""
+    _need(q, "q", torch.float32, 3)
+    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    _need(v_cache, "v_cache", torch.bfloat16, 4)
+    _need(lengths, "lengths", torch.int32, 1)
+    B, nq, D = q.shape
+    nkv, S_max = k_cache.shape[1], k_cache.shape[2]
+    if tuple(k_cache.shape) != (B, nkv, S_max, D) or v_cache.shape != k_cache.shape \
+            or lengths.numel() != B:
+        raise ValueError("inconsistent attention shapes")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.float32, 3)
+    nbytes = q3moe_gqa_attention_workspace_bytes(B, nq, nkv, D, S_max)
+    ws = workspace if workspace is not None else torch.empty(
+        max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    _check("q3moe_gqa_attention", library().q3moe_gqa_attention(
+        _ptr(q), B, nq, nkv, D, _ptr(k_cache), _ptr(v_cache), S_max, _ptr(lengths), scale,
+        _ptr(out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
     return out

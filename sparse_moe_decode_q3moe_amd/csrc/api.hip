@@ -163,4 +163,70 @@ q3moe_status q3moe_rmsnorm(const float* x, int64_t T, int64_t n, const float* ga
     return from_hip(q3moe::launch_rmsnorm(x, T, n, gain, eps, out, as_stream(stream)));
 }
 
+q3moe_status q3moe_bf16_gemv(const uint16_t* W, int64_t N, int64_t K, const float* x, int64_t T,
+                             float* y, int32_t accumulate, void* stream) {
+    if (T < 0 || T > 0x7fffffff || N < 1 || N > ((int64_t)1 << 30) || K < 8 || (K & 7) ||
+        K > ((int64_t)1 << 30) || (accumulate != 0 && accumulate != 1))
+        return Q3MOE_E_SHAPE;
+    if (T == 0) return Q3MOE_OK;
+    if (!W || !x || !y) return Q3MOE_E_NULL;
+    if (!aligned16(W) || !aligned16(x) || (reinterpret_cast<uintptr_t>(y) & 3u)) return Q3MOE_E_ALIGN;
+    const size_t ny = (size_t)T * (size_t)N * sizeof(float);
+    if (overlaps(y, ny, W, (size_t)N * (size_t)K * 2) || overlaps(y, ny, x, (size_t)T * (size_t)K * sizeof(float)))
+        return Q3MOE_E_ALIAS;
+    return from_hip(q3moe::launch_bf16_gemv(W, N, K, x, T, y, accumulate, as_stream(stream)));
+}
+
+q3moe_status q3moe_kv_write(const float* k_new, const float* v_new, int64_t B, int32_t n_kv_heads,
+                            int32_t head_dim, const int32_t* positions, uint16_t* k_cache,
+                            uint16_t* v_cache, int64_t S_max, void* stream) {
+    if (B < 0 || B > 0x7fffffff || n_kv_heads < 1 || head_dim < 1 ||
+        (int64_t)n_kv_heads * head_dim > 65536 || S_max < 1)
+        return Q3MOE_E_SHAPE;
+    if (B == 0) return Q3MOE_OK;
+    if (!k_new || !v_new || !positions || !k_cache || !v_cache) return Q3MOE_E_NULL;
+    const size_t nc = (size_t)B * n_kv_heads * (size_t)S_max * head_dim * 2;
+    const size_t nn = (size_t)B * n_kv_heads * head_dim * sizeof(float);
+    if (overlaps(k_cache, nc, v_cache, nc) || overlaps(k_cache, nc, k_new, nn) ||
+        overlaps(k_cache, nc, v_new, nn) || overlaps(v_cache, nc, k_new, nn) ||
+        overlaps(v_cache, nc, v_new, nn) || overlaps(k_cache, nc, positions, (size_t)B * 4) ||
+        overlaps(v_cache, nc, positions, (size_t)B * 4))
+        return Q3MOE_E_ALIAS;
+    return from_hip(q3moe::launch_kv_write(k_new, v_new, B, n_kv_heads, head_dim, positions, k_cache,
+                                           v_cache, S_max, as_stream(stream)));
+}
+
+size_t q3moe_gqa_attention_workspace_bytes(int64_t B, int32_t n_q_heads, int32_t n_kv_heads,
+                                           int32_t head_dim, int64_t S_max) {
+    if (B < 0 || n_q_heads < 1 || S_max < 1 || !q3moe::gqa_attention_supported(n_q_heads, n_kv_heads, head_dim))
+        return 0;
+    return q3moe::gqa_attention_workspace_bytes(B, n_q_heads, n_kv_heads, head_dim, S_max);
+}
+
+q3moe_status q3moe_gqa_attention(const float* q, int64_t B, int32_t n_q_heads, int32_t n_kv_heads,
+                                 int32_t head_dim, const uint16_t* k_cache, const uint16_t* v_cache,
+                                 int64_t S_max, const int32_t* lengths, float scale, float* out,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+    if (B < 0 || B > 65535 || S_max < 1 || S_max > 0x7fffffff ||
+        !q3moe::gqa_attention_supported(n_q_heads, n_kv_heads, head_dim) || !(scale == scale) ||
+        scale == __builtin_inff() || scale == -__builtin_inff())
+        return Q3MOE_E_SHAPE;
+    if (B == 0) return Q3MOE_OK;
+    if (!q || !k_cache || !v_cache || !lengths || !out) return Q3MOE_E_NULL;
+    if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(workspace) ||
+        (reinterpret_cast<uintptr_t>(q) & 15u) || (reinterpret_cast<uintptr_t>(out) & 3u))
+        return Q3MOE_E_ALIGN;
+    const size_t need = q3moe::gqa_attention_workspace_bytes(B, n_q_heads, n_kv_heads, head_dim, S_max);
+    if (!workspace || workspace_bytes < need) return Q3MOE_E_WORKSPACE;
+    const size_t nq = (size_t)B * n_q_heads * head_dim * sizeof(float);
+    const size_t nc = (size_t)B * n_kv_heads * (size_t)S_max * head_dim * 2;
+    if (overlaps(out, nq, q, nq) || overlaps(out, nq, workspace, need) || overlaps(out, nq, k_cache, nc) ||
+        overlaps(out, nq, v_cache, nc) || overlaps(workspace, need, q, nq) ||
+        overlaps(workspace, need, k_cache, nc) || overlaps(workspace, need, v_cache, nc) ||
+        overlaps(workspace, need, lengths, (size_t)B * 4) || overlaps(out, nq, lengths, (size_t)B * 4))
+        return Q3MOE_E_ALIAS;
+    return from_hip(q3moe::launch_gqa_attention(q, B, n_q_heads, n_kv_heads, head_dim, k_cache, v_cache,
+                                                S_max, lengths, scale, out, workspace, as_stream(stream)));
+}
+
 }  // extern "C"

@@ -85,6 +85,19 @@ hipError_t launch_expert_ffn(const float* hidden, int64_t T, int64_t H, int64_t 
                              const ExpertTensor& down, float* out, int accumulate, void* ws,
                              hipStream_t stream);
 
+// layer.hip: the attention side of the decoder layer
+hipError_t launch_bf16_gemv(const uint16_t* W, int64_t N, int64_t K, const float* x, int64_t T,
+                            float* y, int accumulate, hipStream_t stream);
+hipError_t launch_kv_write(const float* k_new, const float* v_new, int64_t B, int32_t n_kv,
+                           int32_t D, const int32_t* pos, uint16_t* kcache, uint16_t* vcache,
+                           int64_t S_max, hipStream_t stream);
+bool gqa_attention_supported(int32_t n_q, int32_t n_kv, int32_t D);
+size_t gqa_attention_workspace_bytes(int64_t B, int32_t n_q, int32_t n_kv, int32_t D, int64_t S_max);
+hipError_t launch_gqa_attention(const float* q, int64_t B, int32_t n_q, int32_t n_kv, int32_t D,
+                                const uint16_t* kcache, const uint16_t* vcache, int64_t S_max,
+                                const int32_t* len, float scale, float* out, void* ws,
+                                hipStream_t stream);
+
 // norm.hip
 hipError_t launch_rmsnorm(const float* x, int64_t T, int64_t n, const float* gain, float eps,
                           float* out, hipStream_t stream);

@@ -19,6 +19,13 @@ for the real GGUF files, which are not available):
 * Q6_K super-blocks: every byte uniform (the 16 scales read as int8), then
   the fp16 ``d`` field overwritten with U[1e-3, 1e-2] rounded to fp16.
 
+The attention side of the full decoder layer (the same "File facts"):
+
+* projection weights W_q [4096 x 2048], W_k and W_v [512 x 2048], W_o
+  [2048 x 4096] ~ N(0, 0.02) drawn in f32, then stored as bf16 (nearest-even);
+* RMSNorm gains (input, post-attention, per-head q and k) ~ U[0.5, 1.5];
+* the cached keys and values of earlier positions ~ N(0, 1) as bf16.
+
 Generators are ``torch.Generator`` objects on the device the tensor is made
 on; a tensor made on the GPU is copied to the host before the oracle sees it.
 """
@@ -163,3 +170,66 @@ def skewed_hidden_and_router(layer: MoeLayer, hidden: torch.Tensor, seed: int,
     r = layer.router.clone()
     r[list(hot)] += delta * v
     return x, r
+
+
+@dataclasses.dataclass(frozen=True)
+class AttnShape:
+    """The attention half of a decoder layer: hidden H, n_q query heads,
+    n_kv key/value heads, head_dim D, KV-cache capacity S_max."""
+    H: int = 2048
+    n_q: int = 32
+    n_kv: int = 4
+    D: int = 128
+    S_max: int = 4096
+    eps: float = 1e-6
+    rope_base: float = 1e7
+
+
+QWEN3_30B_A3B_ATTN = AttnShape()
+
+
+def bf16_normal(shape, std: float, gen, device="cpu") -> torch.Tensor:
+    """N(0, std^2) drawn in f32 and stored as bfloat16 (nearest-even)."""
+    return normal_f32(shape, std, gen, device).to(torch.bfloat16)
+
+
+@dataclasses.dataclass
+class AttnLayer:
+    shape: AttnShape
+    wq: torch.Tensor              # bf16 [n_q*D, H]
+    wk: torch.Tensor              # bf16 [n_kv*D, H]
+    wv: torch.Tensor              # bf16 [n_kv*D, H]
+    wo: torch.Tensor              # bf16 [H, n_q*D]
+    in_norm: torch.Tensor         # f32 [H]
+    post_norm: torch.Tensor       # f32 [H]
+    q_norm: torch.Tensor          # f32 [D]
+    k_norm: torch.Tensor          # f32 [D]
+
+    def to(self, device) -> "AttnLayer":
+        return AttnLayer(self.shape, *(t.to(device) for t in (
+            self.wq, self.wk, self.wv, self.wo, self.in_norm, self.post_norm, self.q_norm,
+            self.k_norm)))
+
+
+def attn_layer(shape: AttnShape, seed: int, device="cpu") -> AttnLayer:
+    gen = make_generator(seed, device)
+    qd, kd = shape.n_q * shape.D, shape.n_kv * shape.D
+    wq = bf16_normal((qd, shape.H), 0.02, gen, device)
+    wk = bf16_normal((kd, shape.H), 0.02, gen, device)
+    wv = bf16_normal((kd, shape.H), 0.02, gen, device)
+    wo = bf16_normal((shape.H, qd), 0.02, gen, device)
+    gains = [uniform_f32((n,), 0.5, 1.5, gen, device) for n in (shape.H, shape.H, shape.D, shape.D)]
+    return AttnLayer(shape, wq, wk, wv, wo, *gains)
+
+
+def kv_caches(B: int, shape: AttnShape, seed: int, device="cpu"):
+    """(k_cache, v_cache) bf16 [B, n_kv, S_max, D] ~ N(0, 1)."""
+    gen = make_generator(seed, device)
+    dims = (B, shape.n_kv, shape.S_max, shape.D)
+    return bf16_normal(dims, 1.0, gen, device), bf16_normal(dims, 1.0, gen, device)
+
+
+def bf16_bits(t: torch.Tensor):
+    """The raw uint16 bits of a bfloat16 tensor, as a host NumPy array."""
+    import numpy as np
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)

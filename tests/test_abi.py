@@ -19,7 +19,7 @@ OK, E_NULL, E_SHAPE, E_QTYPE, E_ALIGN, E_WORKSPACE, E_HIP, E_ALIAS = range(8)
 
 def declared_functions():
     text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
-    return sorted(set(re.findall(r"\b(q3moe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(q3moe_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -29,7 +29,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(_lib.EXPORTS) == names
@@ -152,6 +152,77 @@ def test_prologue_and_rmsnorm_validation(lib):
     assert R(FAKE, 1, 0, FAKE, 1e-6, FAKE, None) == E_SHAPE
     assert R(FAKE, 1, 2048, None, 1e-6, FAKE, None) == E_NULL
     assert R(FAKE, 2, 2048, FAKE, 1e-6, ctypes.c_void_p(0x10000 + 64), None) == E_ALIAS
+
+
+def test_gemv_validation(lib):
+    G = lib.q3moe_bf16_gemv
+    W, x, y = FAKE, ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000)
+    assert G(W, 64, 64, x, 0, y, 0, None) == OK
+    assert G(W, 64, 64, x, -1, y, 0, None) == E_SHAPE
+    assert G(W, 0, 64, x, 1, y, 0, None) == E_SHAPE
+    assert G(W, 64, 60, x, 1, y, 0, None) == E_SHAPE          # K % 8
+    assert G(W, 64, 0, x, 1, y, 0, None) == E_SHAPE
+    assert G(W, 64, 64, x, 1, y, 2, None) == E_SHAPE          # accumulate in {0, 1}
+    assert G(None, 64, 64, x, 1, y, 0, None) == E_NULL
+    assert G(W, 64, 64, None, 1, y, 0, None) == E_NULL
+    assert G(W, 64, 64, x, 1, None, 0, None) == E_NULL
+    assert G(FAKE_MIS, 64, 64, x, 1, y, 0, None) == E_ALIGN
+    assert G(W, 64, 64, ctypes.c_void_p(0x100004), 1, y, 0, None) == E_ALIGN
+    assert G(W, 64, 64, x, 1, ctypes.c_void_p(0x200002), 0, None) == E_ALIGN
+    assert G(W, 64, 64, x, 1, ctypes.c_void_p(0x10000 + 512), 0, None) == E_ALIAS   # y inside W
+    assert G(W, 64, 64, x, 4, ctypes.c_void_p(0x100000 + 256), 0, None) == E_ALIAS  # y inside x
+
+
+def test_kv_write_validation(lib):
+    K = lib.q3moe_kv_write
+    kn, vn, pos = FAKE, ctypes.c_void_p(0x20000), ctypes.c_void_p(0x30000)
+    kc, vc = ctypes.c_void_p(0x1000000), ctypes.c_void_p(0x2000000)
+
+    def kv(B=1, nkv=4, D=128, S=4096, k_new=kn, v_new=vn, p=pos, k_c=kc, v_c=vc):
+        return K(k_new, v_new, B, nkv, D, p, k_c, v_c, S, None)
+
+    assert kv(B=0) == OK
+    assert kv(B=-1) == E_SHAPE
+    assert kv(nkv=0) == E_SHAPE
+    assert kv(D=0) == E_SHAPE
+    assert kv(S=0) == E_SHAPE
+    assert kv(nkv=1024, D=128) == E_SHAPE
+    assert kv(p=None) == E_NULL
+    assert kv(k_c=None) == E_NULL
+    assert kv(v_c=ctypes.c_void_p(0x1000000 + 4096)) == E_ALIAS     # caches overlap
+    assert kv(k_c=ctypes.c_void_p(0x20000 - 64)) == E_ALIAS         # cache covers v_new
+
+
+def test_attention_validation(lib):
+    A = lib.q3moe_gqa_attention
+    WS = lib.q3moe_gqa_attention_workspace_bytes
+    assert WS(1, 32, 4, 128, 4096) == 32 * 64 * 130 * 4
+    assert WS(16, 32, 4, 128, 4096) == 16 * 32 * 16 * 130 * 4      # 4 tiles per workgroup
+    assert WS(1, 32, 4, 96, 4096) == 0                              # unsupported head_dim
+    assert WS(1, 30, 4, 128, 4096) == 0
+    q, kc, vc = FAKE, ctypes.c_void_p(0x1000000), ctypes.c_void_p(0x2000000)
+    ln, out, ws = ctypes.c_void_p(0x30000), ctypes.c_void_p(0x40000), ctypes.c_void_p(0x4000000)
+    need = WS(1, 32, 4, 128, 4096)
+
+    def at(B=1, nq=32, nkv=4, D=128, S=4096, scale=0.088, qp=q, k_c=kc, v_c=vc, lens=ln, o=out,
+           w=ws, nbytes=need):
+        return A(qp, B, nq, nkv, D, k_c, v_c, S, lens, scale, o, w, nbytes, None)
+
+    assert at(B=0) == OK
+    assert at(D=96) == E_SHAPE
+    assert at(nq=30) == E_SHAPE
+    assert at(nq=128, nkv=4) == E_SHAPE                             # group 32 > 16
+    assert at(S=0) == E_SHAPE
+    assert at(scale=float("nan")) == E_SHAPE
+    assert at(scale=float("inf")) == E_SHAPE
+    assert at(lens=None) == E_NULL
+    assert at(o=None) == E_NULL
+    assert at(k_c=ctypes.c_void_p(0x1000008)) == E_ALIGN
+    assert at(qp=FAKE_MIS) == E_ALIGN
+    assert at(w=None) == E_WORKSPACE
+    assert at(nbytes=need - 1) == E_WORKSPACE
+    assert at(o=ctypes.c_void_p(0x10000 + 256)) == E_ALIAS          # out overlaps q
+    assert at(w=ctypes.c_void_p(0x40000 + 512)) == E_ALIAS          # workspace overlaps out
 
 
 def test_binding_refuses_host_tensors():
