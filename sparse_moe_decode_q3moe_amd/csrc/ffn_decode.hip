@@ -657,6 +657,25 @@ __host__ __device__ inline FusedLds fused_lds(int64_t T, int64_t F, int32_t qtyp
     return L;
 }
 
+// The activations of the T tokens as pieces in LDS: thread tid converts
+// values 4*tid .. 4*tid+3 of every token (hi/mid slots, lo piece, group sums).
+template <int MT>
+__device__ __forceinline__ void build_x_pieces(const float4 (&xv)[MT], int64_t T, uint8_t* smem,
+                                               int xp_bytes, int tid) {
+#pragma unroll
+    for (int j = 0; j < MT; ++j) {
+        if (j < T) {                                           // whole workgroup in or out
+            uint8_t* xp = smem + j * xp_bytes;
+            const Pieces4x3 pc = make_pieces4x3(xv[j]);
+            *reinterpret_cast<uint4*>(xp + piece_slot_off(tid)) = pc.slot;
+            *reinterpret_cast<uint2*>(xp + kFzNB * kBlockPieceStride + kFzNB * 16 * 4 + piece_lo_off(tid)) = pc.lo;
+            float g = pc.sum + __shfl_xor(pc.sum, 1, kWave);
+            g += __shfl_xor(g, 2, kWave);
+            if ((tid & 3) == 0) reinterpret_cast<float*>(xp + kFzNB * kBlockPieceStride)[tid >> 2] = g;
+        }
+    }
+}
+
 // Value of lane `src` (wave-uniform) of v.
 __device__ __forceinline__ int lane_value(int v, int src) { return __builtin_amdgcn_readlane(v, src); }
 
@@ -689,69 +708,84 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
     const int64_t gu_step = (int64_t)grid * kFzGu;
     const bool is_gu = wave < kFzGu;
 
-    // ---- (1) routing, then the activations of all T tokens as pieces in LDS
-    // (one float4 per thread and token), built once for all waves
+    // ---- (1) routing; each gate/up wave requests its first task's weights;
+    // then the activations of all T tokens as pieces in LDS (one float4 per
+    // thread and token), built once for all waves.  Every load here is
+    // unconditional (clamped), so the pieces wait only for the activations
+    // and not for the weight requests issued after them.
     const int nr = (int)(T * k);
     const int my_idx = lane < nr ? idx[lane] : -1;
     const float my_w = lane < nr ? w[lane] : 0.f;
     float4 xv[kFzMaxTokens];
 #pragma unroll
     for (int j = 0; j < kFzMaxTokens; ++j)
-        if (j < T) xv[j] = reinterpret_cast<const float4*>(hidden + j * G::H)[tid];
-    if (tid == 0) *gu_ctr = 0;
-#pragma unroll
-    for (int j = 0; j < kFzMaxTokens; ++j) {
-        if (j < T) {                                           // whole workgroup in or out
-            uint8_t* xp = smem + j * L.xp_bytes;
-            const Pieces4x3 pc = make_pieces4x3(xv[j]);
-            *reinterpret_cast<uint4*>(xp + piece_slot_off(tid)) = pc.slot;
-            *reinterpret_cast<uint2*>(xp + kFzNB * kBlockPieceStride + kFzNB * 16 * 4 + piece_lo_off(tid)) = pc.lo;
-            float g = pc.sum + __shfl_xor(pc.sum, 1, kWave);
-            g += __shfl_xor(g, 2, kWave);
-            if ((tid & 3) == 0) reinterpret_cast<float*>(xp + kFzNB * kBlockPieceStride)[tid >> 2] = g;
-        }
+        xv[j] = reinterpret_cast<const float4*>(hidden + (j < T ? j : T - 1) * G::H)[tid];
+    if (tid == 0) gu_ctr[0] = 0;
+
+    int64_t tau = (int64_t)wg * kFzGu + wave;
+    int64_t p = (tau < n_gu ? tau : 0) / tiles, r0 = ((tau < n_gu ? tau : 0) % tiles) * G::R;
+    GuRows rows;
+    if (is_gu) {
+        gu_rows_load(rows, lane_value(my_idx, (int)p), E, gbase, gstride, ubase, ustride, r0, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        build_x_pieces<kFzMaxTokens>(xv, T, smem, L.xp_bytes, tid);
+        // keeps the two builds apart: merged after the branch, the stores
+        // would wait for the weight requests as well
+        __builtin_amdgcn_sched_barrier(0);
+    } else {
+        build_x_pieces<kFzMaxTokens>(xv, T, smem, L.xp_bytes, tid);
     }
     __syncthreads();                          // no direct-to-LDS load is in flight yet
 
     int64_t unit = wg;
     if (is_gu) {
-        // gate/up tasks: request the weights, then read the token's pieces
+        // gate/up tasks: the first task's weights are on their way; read the
+        // token's pieces, compute, and request the next task's weights
         int64_t xc = -1;                      // token whose pieces x holds
         XCols x;
-        for (int64_t tau = (int64_t)wg * kFzGu + wave; tau < n_gu; tau += gu_step) {
-            const int64_t p = tau / tiles, t = p / k, r0 = (tau % tiles) * G::R;
-            const int e = lane_value(my_idx, (int)p);
-            GuRows rows;
-            gu_rows_load(rows, e, E, gbase, gstride, ubase, ustride, r0, lane);
+        while (tau < n_gu) {
+            const int64_t t = p / k;
             if (t != xc) {
                 const uint8_t* xp = smem + t * L.xp_bytes;
                 x = load_xcols(xp, reinterpret_cast<const float*>(xp + kFzNB * kBlockPieceStride),
                                xp + kFzNB * kBlockPieceStride + kFzNB * 16 * 4, lane);
                 xc = t;
             }
-            gu_rows_finish(rows, x, lane, hpieces, p * F + r0);
+            const int64_t pv = p * F + r0;
+            gu_rows_finish(rows, x, lane, hpieces, pv);
+            tau += gu_step;
+            if (tau < n_gu) {
+                p = tau / tiles;
+                r0 = (tau % tiles) * G::R;
+                gu_rows_load(rows, lane_value(my_idx, (int)p), E, gbase, gstride, ubase, ustride, r0, lane);
+            }
         }
         wait_all_loads();                     // this wave's h stores have completed
-        if (lane == 0) {
-            const int before = __hip_atomic_fetch_add(gu_ctr, 1, __ATOMIC_RELAXED,
-                                                      __HIP_MEMORY_SCOPE_WORKGROUP);
-            if (before == kFzGu - 1)          // the workgroup's last gate/up wave
+        int before = 0;
+        if (lane == 0)
+            before = __hip_atomic_fetch_add(gu_ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        before = __builtin_amdgcn_readfirstlane(before);
+        if (before == kFzGu - 1) {
+            // the workgroup's last gate/up wave signals, then (having no
+            // request of its own in flight) polls for every workgroup's h
+            if (lane == 0)
                 __hip_atomic_fetch_add(sync + kSyncGuDone + (wg % kStripes) * kLineInts, 1,
                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (unit < n_dn) wait_all_gate_up(sync, grid, status, lane);
         }
     } else if (unit < n_dn) {
-        // down waves: request the first unit's tiles for all slots
+        // down waves: request the first unit's tiles for all slots (after the
+        // barrier, so behind every gate/up request of the workgroup)
         const int dw = wave - kFzGu;
-        const int64_t t = unit / row_units, r0 = (unit % row_units) * kDnRows;
+        const int64_t t = unit / row_units, r0d = (unit % row_units) * kDnRows;
         for (int s = dw; s < k; s += kFzDn) {
             const int e = lane_value(my_idx, (int)(t * k + s));
             if (e >= 0 && e < E)
-                dn_issue_weights(smem + L.dn_off + s * dg.tile_pad, dg, dbase, dstride, e, r0, lane);
+                dn_issue_weights(smem + L.dn_off + s * dg.tile_pad, dg, dbase, dstride, e, r0d, lane);
         }
     }
 
-    // ---- (2) one down wave waits until every workgroup's h is out
-    if (wave == kFzGu && unit < n_dn) wait_all_gate_up(sync, grid, status, lane);
+    // ---- (2) every wave waits until the poller has seen all h
     __syncthreads();
 
     // ---- (3) down projection and combine, all waves

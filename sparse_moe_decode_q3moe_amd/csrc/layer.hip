@@ -10,8 +10,8 @@
 //       TT <= 16 tokens per pass, W bf16 [N][K].  A wave owns R rows and the
 //       lanes split k in 16-byte pieces (8 weights), so every load is a
 //       1 KiB coalesced row segment.  x is staged in LDS in chunks and shared
-//       by the workgroup's 4 waves; the next chunk's weights are loaded while
-//       the current one is multiplied.  One transposed butterfly finally gives
+//       by the workgroup's 4 waves; the next chunk's weights and activations
+//       are loaded into registers while the current one is multiplied.  One transposed butterfly finally gives
 //       every lane group one (row, token) total.
 //   kv_write_kernel: the new token's k and v, rounded to bf16 (nearest even),
 //       into each sequence's cache at its position.
@@ -96,17 +96,34 @@ __device__ __forceinline__ void gv_load_chunk(uint4 (&wb)[S][R], const uint16_t*
     }
 }
 
+// The activation chunk [TT][KC] moves through registers: each thread loads
+// NX float4 of the next chunk while the current one is multiplied, then
+// stores them to LDS after the barrier.
 template <int TT, int R>
-__device__ __forceinline__ void gv_stage_x(float* xs, const float* x, int64_t K, int64_t T,
-                                           int64_t t0, int64_t k0, int tid) {
+struct GvX {
+    static constexpr int KC = GvShape<TT, R>::KC;
+    static constexpr int NX = TT * KC / 4 / kGvThreads;
+    static_assert(NX * 4 * kGvThreads == TT * KC, "chunk must split evenly over the threads");
+};
+
+template <int TT, int R, int NX>
+__device__ __forceinline__ void gv_load_x(float4 (&xr)[NX], const float* x, int64_t K, int64_t T,
+                                          int64_t t0, int64_t k0, int tid) {
     constexpr int KC = GvShape<TT, R>::KC;
-    for (int i = tid; i < TT * (KC / 4); i += kGvThreads) {
+#pragma unroll
+    for (int u = 0; u < NX; ++u) {
+        const int i = tid + u * kGvThreads;
         const int t = i / (KC / 4), c = i % (KC / 4);
         const int64_t k = k0 + 4 * c;
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (t0 + t < T && k < K) v = *reinterpret_cast<const float4*>(x + (t0 + t) * K + k);
-        *reinterpret_cast<float4*>(xs + t * KC + 4 * c) = v;
+        xr[u] = (t0 + t < T && k < K) ? *reinterpret_cast<const float4*>(x + (t0 + t) * K + k)
+                                      : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+}
+
+template <int NX>
+__device__ __forceinline__ void gv_store_x(float* xs, const float4 (&xr)[NX], int tid) {
+#pragma unroll
+    for (int u = 0; u < NX; ++u) *reinterpret_cast<float4*>(xs + 4 * (tid + u * kGvThreads)) = xr[u];
 }
 
 template <int TT, int R, int S>
@@ -155,18 +172,27 @@ __global__ __launch_bounds__(kGvThreads) void bf16_gemv_kernel(
     for (int i = 0; i < V; ++i) acc[i] = 0.f;
 
     uint4 wa[S][R], wb[S][R];
+    constexpr int NX = GvX<TT, R>::NX;
+    float4 xr[NX];
     gv_load_chunk<S, R>(wa, W, N, K, n0, 0, lane);
+    gv_load_x<TT, R, NX>(xr, x, K, T, t0, 0, tid);
     for (int64_t k0 = 0; k0 < K; k0 += 2 * KC) {
         __syncthreads();
-        gv_stage_x<TT, R>(xs, x, K, T, t0, k0, tid);
+        gv_store_x<NX>(xs, xr, tid);
         __syncthreads();
-        if (k0 + KC < K) gv_load_chunk<S, R>(wb, W, N, K, n0, k0 + KC, lane);
+        if (k0 + KC < K) {
+            gv_load_chunk<S, R>(wb, W, N, K, n0, k0 + KC, lane);
+            gv_load_x<TT, R, NX>(xr, x, K, T, t0, k0 + KC, tid);
+        }
         gv_mul_chunk<TT, R, S>(acc, wa, xs, lane);
         if (k0 + KC >= K) break;
         __syncthreads();
-        gv_stage_x<TT, R>(xs, x, K, T, t0, k0 + KC, tid);
+        gv_store_x<NX>(xs, xr, tid);
         __syncthreads();
-        if (k0 + 2 * KC < K) gv_load_chunk<S, R>(wa, W, N, K, n0, k0 + 2 * KC, lane);
+        if (k0 + 2 * KC < K) {
+            gv_load_chunk<S, R>(wa, W, N, K, n0, k0 + 2 * KC, lane);
+            gv_load_x<TT, R, NX>(xr, x, K, T, t0, k0 + 2 * KC, tid);
+        }
         gv_mul_chunk<TT, R, S>(acc, wb, xs, lane);
     }
 
@@ -235,6 +261,7 @@ constexpr int kAtTile = 64;                // positions per LDS tile (one per la
 constexpr int kAtThreads = 256;
 constexpr int kAtWaves = kAtThreads / kWave;
 constexpr int kAtMaxGroup = 16;            // query heads per kv head
+constexpr int kAtMaxD = 256;
 constexpr int kDppQuadXor1 = 0xb1, kDppQuadXor2 = 0x4e, kDppRowRor4 = 0x124, kDppRowRor8 = 0x128;
 
 template <int CTRL>
@@ -364,6 +391,7 @@ __global__ __launch_bounds__(kAtThreads) void attn_partial_kernel(
             lp[lane * HPW + h] = p;
         }
         // p-weighted V rows: lane owns d = DPL*lane .. +DPL
+#pragma unroll 8
         for (int j = 0; j < nj; ++j) {
             float pj[HPW];
 #pragma unroll
@@ -400,28 +428,53 @@ __global__ __launch_bounds__(kAtThreads) void attn_partial_kernel(
     }
 }
 
-// grid: (n_q, B); one thread per output value.  A record with m = -inf
-// (a chunk past the sequence end) adds nothing; a sequence without any
-// valid record yields 0 / 0.
+// grid: (n_q, B); one thread per output value, with the chunk weights
+// exp(m_c - M) and the denominator formed once in LDS.  A record with
+// m = -inf (a chunk past the sequence end) adds nothing; a sequence without
+// any valid record yields 0 / 0.
+constexpr int kCbChunks = 256;             // chunk weights held in LDS per pass
+
 __global__ void attn_combine_kernel(const float* __restrict__ part, int32_t n_q, int32_t D,
                                     int nchunks, float* __restrict__ out) {
-    const int h = blockIdx.x;
+    __shared__ float fw[kCbChunks];
+    __shared__ float red[kAtMaxD / kWave];
+    __shared__ float sM;
+    const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t b = blockIdx.y;
     const int rec = D + 2;
     const float* pr = part + (b * n_q + h) * (int64_t)nchunks * rec;
+    const int nw = (blockDim.x + kWave - 1) / kWave;
     float M = -__builtin_inff();
-    for (int c = 0; c < nchunks; ++c) M = fmaxf(M, pr[c * rec]);
-    for (int d = threadIdx.x; d < D; d += blockDim.x) {
-        float Ls = 0.f, a = 0.f;
-        for (int c = 0; c < nchunks; ++c) {
-            const float mc = pr[c * rec];
-            if (mc == -__builtin_inff()) continue;
-            const float f = expf(mc - M);
-            Ls = fmaf(pr[c * rec + 1], f, Ls);
-            a = fmaf(pr[c * rec + 2 + d], f, a);
-        }
-        out[(b * n_q + h) * (int64_t)D + d] = a / Ls;
+    for (int c = tid; c < nchunks; c += blockDim.x) M = fmaxf(M, pr[c * rec]);
+    M = wave_max_dpp(M);
+    if (lane == 0) red[wave] = M;
+    __syncthreads();
+    if (tid == 0) {
+        float m = red[0];
+        for (int w = 1; w < nw; ++w) m = fmaxf(m, red[w]);
+        sM = m;
     }
+    __syncthreads();
+    M = sM;
+    float Ls = 0.f, a = 0.f;
+    for (int c0 = 0; c0 < nchunks; c0 += kCbChunks) {
+        const int nc = nchunks - c0 < kCbChunks ? nchunks - c0 : kCbChunks;
+        __syncthreads();
+        for (int c = tid; c < nc; c += blockDim.x) {
+            const float mc = pr[(c0 + c) * rec];
+            fw[c] = mc == -__builtin_inff() ? 0.f : expf(mc - M);
+        }
+        __syncthreads();
+        if (tid < D) {
+#pragma unroll 8
+            for (int c = 0; c < nc; ++c) {
+                const float f = fw[c];
+                Ls = fmaf(pr[(c0 + c) * rec + 1], f, Ls);
+                a = fmaf(pr[(c0 + c) * rec + 2 + tid], f, a);
+            }
+        }
+    }
+    if (tid < D) out[(b * n_q + h) * (int64_t)D + tid] = a / Ls;
 }
 
 // Tiles per workgroup: one while the (sequence, kv head, tile) triples do

@@ -129,6 +129,19 @@ __global__ __launch_bounds__(256) void pf_pieces_kernel(const float* __restrict_
     }
 }
 
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup w runs on
+// XCD w % 8), each with its own L2.  Tile slot s goes to XCD s % 8 and all
+// its column tiles to consecutive workgroups there, so the workgroups that
+// share a token tile's activations meet in one L2, and the used slots (a
+// prefix of the slot range) spread evenly over the XCDs.  The grid is
+// ctiles * nslots workgroups with nslots a multiple of 8.
+constexpr int kXcds = 8;
+__device__ __forceinline__ void pf_xcd_tile(int w, int ctiles, int& slot, int& ctile) {
+    const int x = w % kXcds, local = w / kXcds;
+    slot = (local / ctiles) * kXcds + x;
+    ctile = local % ctiles;
+}
+
 // The expert and tile index of tile slot `slot` (tile_off: exclusive prefix
 // of per-expert tile counts, tile_off[E] = total): the last e with
 // tile_off[e] <= slot.
@@ -165,12 +178,13 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
     uint8_t* lwg = smem + 3 * kGuXBytes + kGuSBytes;
     uint8_t* lwu = lwg + kGuWBytes;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int slot = blockIdx.y;          // feature tiles run fastest: neighbours share the rows
+    int slot, ftile;
+    pf_xcd_tile((int)blockIdx.x, (int)(F / kPfCols), slot, ftile);
     if (slot >= tile_off[E]) return;                          // uniform: an unused tile slot
     const int e = pf_tile_expert(tile_off, E, slot);
     const int64_t row0 = offsets[e] + (int64_t)(slot - tile_off[e]) * kPfRows;
     const int nrows = (int)min((int64_t)kPfRows, (int64_t)offsets[e + 1] - row0);
-    const int64_t f0 = (int64_t)blockIdx.x * kPfCols;
+    const int64_t f0 = (int64_t)ftile * kPfCols;
     const int64_t nsb = H / kQK;
     const int64_t rowb = nsb * kQ4KBytes;                     // bytes per gate/up row
     const uint8_t* gexp = gbase + (int64_t)e * gstride + f0 * rowb;
@@ -288,12 +302,13 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
     float* __restrict__ Y) {
     extern __shared__ __align__(16) uint8_t smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int slot = blockIdx.y;          // output-row tiles run fastest: neighbours share h
+    int slot, htile;
+    pf_xcd_tile((int)blockIdx.x, (int)(H / kPfCols), slot, htile);
     if (slot >= tile_off[E]) return;
     const int e = pf_tile_expert(tile_off, E, slot);
     const int64_t row0 = offsets[e] + (int64_t)(slot - tile_off[e]) * kPfRows;
     const int nrows = (int)min((int64_t)kPfRows, (int64_t)offsets[e + 1] - row0);
-    const int64_t h0 = (int64_t)blockIdx.x * kPfCols;
+    const int64_t h0 = (int64_t)htile * kPfCols;
     const bool q6 = qtype == 2;
     const int bb = q6 ? kQ6KBytes : kQ4KBytes;
     const int64_t nsb = F / kQK;
@@ -303,7 +318,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
     uint8_t* lx_hi = smem + wbytes + 16;
     uint8_t* lx_lo = lx_hi + kGuXBytes;
     const float* ls16 = reinterpret_cast<const float*>(lx_lo + kGuXBytes);
-    float2* lfac = reinterpret_cast<float2*>(lx_lo + kGuXBytes + kGuSBytes);   // [row][group]
+    float2* lfac = reinterpret_cast<float2*>(lx_lo + kGuXBytes + kGuSBytes);   // [group][row]
 
     // the whole row tile of the down matrix, once
     {
@@ -369,7 +384,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
                 sc = 0.125f * half_bits_to_float(hdr.x & 0xffffu) * (float)scj;   // 128 + 8q
                 off = 128.f * sc + half_bits_to_float(hdr.x >> 16) * (float)mj;
             }
-            lfac[f] = make_float2(sc, off);
+            lfac[g * kPfCols + r] = make_float2(sc, off);
         }
         __syncthreads();
 
@@ -377,7 +392,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
 #pragma unroll 4
         for (int s = 0; s < 16; ++s) {
             const int kk = 16 * s + 4 * kq;
-            const float2 fac = lfac[frow * 16 + s];
+            const float2 fac = lfac[s * kPfCols + frow];
             uint32_t q;
             if (q6) {
                 const int n = kk >> 7, r = (kk >> 5) & 3, lp = kk & 31;
@@ -502,11 +517,11 @@ hipError_t launch_prefill_ffn(const float* hidden, int64_t T, int64_t H, int64_t
                        reinterpret_cast<uint32_t*>(base + L.xlo), reinterpret_cast<float*>(base + L.xs16));
     if ((err = hipGetLastError()) != hipSuccess) return err;
 
-    const unsigned slots = (unsigned)((n + kPfRows - 1) / kPfRows + E);
+    const unsigned slots = (unsigned)(((n + kPfRows - 1) / kPfRows + E + 7) / 8 * 8);
     static LdsLimit gu_lds;
     if ((err = ensure_lds(reinterpret_cast<const void*>(pf_gateup_kernel), gu_lds, kGuLds)) != hipSuccess)
         return err;
-    hipLaunchKernelGGL(pf_gateup_kernel, dim3((unsigned)(F / kPfCols), slots), dim3(kPfThreads), kGuLds,
+    hipLaunchKernelGGL(pf_gateup_kernel, dim3((unsigned)(F / kPfCols) * slots), dim3(kPfThreads), kGuLds,
                        stream, reinterpret_cast<const uint16_t*>(base + L.xhi),
                        reinterpret_cast<const uint16_t*>(base + L.xmid),
                        reinterpret_cast<const uint16_t*>(base + L.xlo),
@@ -526,7 +541,7 @@ hipError_t launch_prefill_ffn(const float* hidden, int64_t T, int64_t H, int64_t
     if ((err = ensure_lds(reinterpret_cast<const void*>(pf_down_kernel), down_lds, dl)) != hipSuccess)
         return err;
     float* Y = reinterpret_cast<float*>(base + L.y);
-    hipLaunchKernelGGL(pf_down_kernel, dim3((unsigned)(H / kPfCols), slots), dim3(kPfThreads), dl, stream,
+    hipLaunchKernelGGL(pf_down_kernel, dim3((unsigned)(H / kPfCols) * slots), dim3(kPfThreads), dl, stream,
                        reinterpret_cast<const uint16_t*>(base + L.hhi),
                        reinterpret_cast<const uint16_t*>(base + L.hlo),
                        reinterpret_cast<const float*>(base + L.hs16), F, offsets, tile_off, pairs, E,
