@@ -6,25 +6,29 @@
 //
 // Pipeline (all on the caller's stream, all grids fixed at launch):
 //   1. group: (token, slot) pairs ordered by (expert, pair), per-expert
-//      offsets and tile offsets for tiles of kPfRows pairs;
+//      offsets and tile offsets for tiles of 64 pairs (so an expert with up
+//      to 64 pairs reads its weights once);
 //   2. pieces of the hidden rows: bf16 hi + mid + lo (x to 2^-27; the
 //      gate/up outputs amplify the input's rounding most) and the f32 sum of
 //      every 16 values;
-//   3. gate/up: one workgroup per (64 features, expert tile).  Per super-block
-//      the tile's activation pieces and both weight tiles are gathered into
-//      LDS with direct-to-LDS loads.  Each 16-wide k step runs
-//      v_mfma_f32_16x16x16 on exact bf16 weights (128 + q) with each
-//      activation piece.  Each step's result is scaled per (feature, group), and
-//      the 128 offset and the Q4_K min are removed through the group sums.
+//   3. gate/up: one workgroup per (128 h features, pair tile), k in stages
+//      of 128 staged through LDS one stage ahead; v_mfma_f32_16x16x32_bf16
+//      per Q4_K sub-block on exact bf16 weights 128 + 8q with each piece;
 //      h = silu(g) * u goes to the workspace in grouped row order;
 //   4. pieces of h (hi + lo);
-//   5. down: one workgroup per (64 output rows, expert tile), Q6_K or Q4_K,
-//      the whole row tile of the expert's down matrix resident in LDS;
+//   5. down: one workgroup per (64 output rows, pair tile), Q6_K or Q4_K,
+//      the row tile of the expert's down matrix resident in LDS, h staged per
+//      128-wide stage; v_mfma_f32_16x16x16bf16_1k per 16-wide scale group;
 //      rows go to Y indexed by pair;
 //   6. combine: out[t] = [out +] sum over slots in slot order of w * Y.
+// In both matrix kernels the weights' offset (and the Q4_K min) times the
+// activation sums leaves once per stage as v_mfma_f32_16x16x4_f32 rank-4
+// steps.  Workgroups are mapped so that the ones sharing a pair tile run on
+// one XCD (one L2).
 // MFMA operand layouts (checked on the device): A lane l holds row l % 16,
-// k = 4 (l / 16) .. + 3; B lane l holds column l % 16 at the same k;
-// C lane l holds rows 4 (l / 16) + r, r = 0..3, column l % 16.
+// k = K (l / 16) .. + K - 1 (K = 4, 8 or 1 values for the 16-, 32-wide bf16
+// and the f32 forms); B lane l holds column l % 16 at the same k; C lane l
+// holds rows 4 (l / 16) + r, r = 0..3, column l % 16.
 #include "device_common.h"
 #include "internal.h"
 
@@ -35,9 +39,7 @@ namespace {
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kPfRows = 32;                 // grouped pairs per tile (two 16-row MFMA blocks)
-constexpr int kPfCols = 64;                 // output features per workgroup (16 per wave)
-constexpr int kPfThreads = 256;
+constexpr int kPfRows = 64;                 // grouped pairs per tile (four 16-row MFMA blocks)
 constexpr uint32_t kPfBias8 = 0x43434343u;
 
 __device__ __forceinline__ float pf_silu(float z) { return z / (1.0f + expf(-z)); }
@@ -67,22 +69,22 @@ __device__ __forceinline__ uint32_t pf_lds_u32_a2(const uint8_t* lds, int off) {
 // Q4_K scale factors of one block header (d, dmin, 12 packed bytes) for
 // the 8 sub-blocks, for weights encoded as bf16 128 + 8q: s[j] = d*sc_j/8,
 // b[j] = 128*s[j] + dmin*m_j (removes the offset and applies the min).
-__device__ __forceinline__ void pf_q4k_factors(const uint8_t* blk, float s[8], float b[8]) {
-    const uint4 hdr = *reinterpret_cast<const uint4*>(blk);
+__device__ __forceinline__ void pf_q4k_factors_hdr(uint4 hdr, float s[8], float b[8]) {
     const float d = half_bits_to_float(hdr.x & 0xffffu);
     const float dmin = half_bits_to_float(hdr.x >> 16);
-    const uint8_t* S = blk + 4;
+    const uint32_t s0 = hdr.y, s1 = hdr.z, s2 = hdr.w;        // packed bytes 0-3, 4-7, 8-11
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         int sc, m;
         if (j < 4) {
-            sc = S[j] & 63;
-            m = S[j + 4] & 63;
+            sc = (s0 >> (8 * j)) & 63;
+            m = (s1 >> (8 * j)) & 63;
         } else {
-            sc = (S[j + 4] & 15) | ((S[j - 4] >> 6) << 4);
-            m = (S[j + 4] >> 4) | ((S[j] >> 6) << 4);
+            const int jj = j - 4;
+            sc = ((s2 >> (8 * jj)) & 15) | (((s0 >> (8 * jj + 6)) & 3) << 4);
+            m = ((s2 >> (8 * jj + 4)) & 15) | (((s1 >> (8 * jj + 6)) & 3) << 4);
         }
-        s[j] = 0.125f * d * (float)sc;                    // weights enter as 128 + 8q
+        s[j] = 0.125f * d * (float)sc;                        // weights enter as 128 + 8q
         b[j] = 128.f * s[j] + dmin * (float)m;
     }
 }
@@ -155,146 +157,249 @@ __device__ __forceinline__ int pf_tile_expert(const int32_t* tile_off, int32_t E
     return lo;
 }
 
-// ---------------------------------------------------------------- gate/up --
-// LDS: activation pieces hi, mid, lo of the 32 rows x 256 values (k-major:
-// 16-byte chunk c of row i at (c * 32 + i) * 16), group sums [16][32] f32,
-// gate and up weight tiles [64 rows][144 B] of the current super-block.
-constexpr int kGuXBytes = kPfRows * kQK * 2;                  // 16 KiB per piece array
-constexpr int kGuSBytes = kPfRows * 16 * 4;
-constexpr int kGuWBytes = kPfCols * kQ4KBytes;                // 9216
-constexpr int kGuLds = 3 * kGuXBytes + kGuSBytes + 2 * kGuWBytes;
+// ------------------------------------------------------- staged operands --
+// Both matrix kernels work on a tile of up to 64 grouped pairs (four 16-row
+// MFMA blocks) and walk k in stages of 128 (half a super-block).  Every
+// operand of a stage is loaded by plain coalesced 16-byte loads into
+// registers one stage ahead and stored into LDS after the barrier, so the
+// next stage's memory traffic overlaps this stage's matrix work.  Activation
+// rows sit in LDS row-major with 16 bytes of padding (272 bytes per row and
+// piece), which makes the 16 rows an MFMA operand read start in 16 distinct
+// bank quads.
+constexpr int kStageK = 128;
+constexpr int kXRowB = kStageK * 2 + 16;                      // 272
+constexpr int kXPieceB = kPfRows * kXRowB;                    // 17408
 
-__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2))) void pf_gateup_kernel(
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4v_t __attribute__((ext_vector_type(4)));
+
+// v_mfma_f32_16x16x4_f32: A lane l holds row l % 16, k = l / 16; B lane l
+// holds column l % 16 at the same k; C as for the bf16 forms.
+__device__ __forceinline__ f32x4_t pf_mfma_f32(float a, float b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4_t pf_mfma32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Eight Q4_K nibbles (sub-block half h of 8 quant bytes) as bf16 128 + 8q.
+__device__ __forceinline__ bf16x8_t pf_q4k_b8(uint2 w, int h) {
+    const uint32_t v0 = (h ? (w.x >> 1) : (w.x << 3)) & 0x78787878u;
+    const uint32_t v1 = (h ? (w.y >> 1) : (w.y << 3)) & 0x78787878u;
+    const u32x4v_t r = {__builtin_amdgcn_perm(kPfBias8, v0, 0x04010400u),
+                        __builtin_amdgcn_perm(kPfBias8, v0, 0x04030402u),
+                        __builtin_amdgcn_perm(kPfBias8, v1, 0x04010400u),
+                        __builtin_amdgcn_perm(kPfBias8, v1, 0x04030402u)};
+    return __builtin_bit_cast(bf16x8_t, r);
+}
+
+// ---------------------------------------------------------------- gate/up --
+// One workgroup per (128 h features, pair tile): 256 weight rows, gate rows
+// f0.. then up rows f0..  8 waves: wave w owns token blocks 2 (w >> 2) and
+// 2 (w >> 2) + 1 and features 32 (w & 3)..+31 of both matrices, so
+// silu(g) * u is formed in registers and each wave reads half the tile's
+// activations per step.  Each k step covers one Q4_K sub-block
+// (v_mfma_f32_16x16x32_bf16 on exact bf16 weights 128 + 8q with each of the
+// three activation pieces) and is scaled by that sub-block's d*sc/8.  The 128
+// offset and the min, (128 s + dmin m) times each sub-block's activation sum
+// S, leave once per stage as one f32 rank-4 matrix step per tile.
+// LDS per stage: pieces hi/mid/lo [64 rows][272]; weight quant bytes as
+// planes of 8-byte pieces [chunk 2][group 4][256 rows] (each plane padded by
+// 128 bytes, so the two groups a half-wave reads land in different banks);
+// the (s, b) factors [4 sub-blocks][256 rows]; the sums S [4][64].
+constexpr int kGuFeat = 128;
+constexpr int kGuWRows = 2 * kGuFeat;                         // 256
+constexpr int kGuThreads = 512;
+constexpr int kGuPlaneB = kGuWRows * 8 + 128;                 // 2176
+constexpr int kGuWOff = 3 * kXPieceB;                         // 52224
+constexpr int kGuFacOff = kGuWOff + 8 * kGuPlaneB;            // 69632
+constexpr int kGuSOff = kGuFacOff + 4 * kGuWRows * 8;         // 77824
+constexpr int kGuLds = kGuSOff + 4 * kPfRows * 4;             // 78848
+
+__global__ __launch_bounds__(kGuThreads) void pf_gateup_kernel(
     const uint16_t* __restrict__ xhi, const uint16_t* __restrict__ xmid,
-    const uint16_t* __restrict__ xlo, const float* __restrict__ xs16, int64_t H, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ tile_off, const int32_t* __restrict__ pairs, int32_t E, int32_t k,
-    const uint8_t* __restrict__ gbase, int64_t gstride, const uint8_t* __restrict__ ubase,
-    int64_t ustride, int64_t F, float* __restrict__ hbuf) {
+    const uint16_t* __restrict__ xlo, const float* __restrict__ xs16, int64_t H,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_off,
+    const int32_t* __restrict__ pairs, int32_t E, int32_t k, const uint8_t* __restrict__ gbase,
+    int64_t gstride, const uint8_t* __restrict__ ubase, int64_t ustride, int64_t F,
+    float* __restrict__ hbuf) {
     extern __shared__ __align__(16) uint8_t smem[];
-    uint8_t* lx_hi = smem;
-    uint8_t* lx_mid = smem + kGuXBytes;
-    uint8_t* lx_lo = smem + 2 * kGuXBytes;
-    const float* ls16 = reinterpret_cast<const float*>(smem + 3 * kGuXBytes);
-    uint8_t* lwg = smem + 3 * kGuXBytes + kGuSBytes;
-    uint8_t* lwu = lwg + kGuWBytes;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int slot, ftile;
-    pf_xcd_tile((int)blockIdx.x, (int)(F / kPfCols), slot, ftile);
+    pf_xcd_tile((int)blockIdx.x, (int)(F / kGuFeat), slot, ftile);
     if (slot >= tile_off[E]) return;                          // uniform: an unused tile slot
     const int e = pf_tile_expert(tile_off, E, slot);
     const int64_t row0 = offsets[e] + (int64_t)(slot - tile_off[e]) * kPfRows;
     const int nrows = (int)min((int64_t)kPfRows, (int64_t)offsets[e + 1] - row0);
-    const int64_t f0 = (int64_t)ftile * kPfCols;
-    const int64_t nsb = H / kQK;
-    const int64_t rowb = nsb * kQ4KBytes;                     // bytes per gate/up row
+    const int64_t f0 = (int64_t)ftile * kGuFeat;
+    const int64_t rowb = (H / kQK) * kQ4KBytes;               // bytes per gate/up row
     const uint8_t* gexp = gbase + (int64_t)e * gstride + f0 * rowb;
     const uint8_t* uexp = ubase + (int64_t)e * ustride + f0 * rowb;
+    const int nst = (int)(H / kStageK);
 
-    // activation pieces are staged k-major: 16-byte chunk c (8 values) of row
-    // i at LDS (c * 32 + i) * 16, so the 16 rows an MFMA operand read touches
-    // are 16 consecutive chunks (no bank conflicts); thread tid stages row
-    // tid % 32.  Group sums are staged as [group][row] with 4-byte loads.
-    const int my_row = tid & 31;
-    const int64_t my_tok = my_row < nrows ? pairs[row0 + my_row] / k : -1;
-    const int col = lane & 15, kq = lane >> 4;               // MFMA column / k quarter
-    const int frow = wave * 16 + col;                        // this lane's weight row in the tile
-    f32x4_t acc[2][2];
+    // staging roles.  Activations: 3 pieces x 64 rows x 16 chunks of 16 B,
+    // item q = u * 512 + tid (u < 6): piece u >> 1, row tid/16 (u even) or
+    // 32 + tid/16 (u odd), chunk tid & 15.  Weights: 256 rows x 4 parts of
+    // 16 B (q = u * 512 + tid, u < 2: row q >> 2, part q & 3); headers:
+    // thread tid < 256 reads row tid's.  Sums: thread tid < 256 reads the S
+    // of row tid >> 2, sub-block tid & 3.
+    const int ra = tid >> 4, rb2 = 32 + (tid >> 4), xc = tid & 15;
+    const int64_t toka = ra < nrows ? pairs[row0 + ra] / k : -1;
+    const int64_t tokb = rb2 < nrows ? pairs[row0 + rb2] / k : -1;
+    const int64_t toks = tid < 4 * kPfRows && (tid >> 2) < nrows ? pairs[row0 + (tid >> 2)] / k : -1;
+    uint4 rx[6], rw[2], rh;
+    float rs = 0.f;
+    auto wrow = [&](int r) -> const uint8_t* { return r < kGuFeat ? gexp + r * rowb : uexp + (r - kGuFeat) * rowb; };
+    auto load_stage = [&](int st) {
+        const int64_t k0 = (int64_t)st * kStageK;
+        const int64_t sb = st >> 1;
+        const int half = st & 1;
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-        for (int m = 0; m < 2; ++m) acc[rb][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int u = 0; u < 6; ++u) {
+            const int64_t tok = (u & 1) ? tokb : toka;
+            const uint16_t* xs = u < 2 ? xhi : u < 4 ? xmid : xlo;
+            rx[u] = tok >= 0 ? *reinterpret_cast<const uint4*>(xs + tok * H + k0 + 8 * xc)
+                             : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int q = u * kGuThreads + tid;
+            rw[u] = *reinterpret_cast<const uint4*>(wrow(q >> 2) + sb * kQ4KBytes + 16 + 64 * half + 16 * (q & 3));
+        }
+        if (tid < kGuWRows) rh = *reinterpret_cast<const uint4*>(wrow(tid) + sb * kQ4KBytes);
+        if (tid < 4 * kPfRows) {
+            const int64_t g16 = (k0 >> 4) + 2 * (tid & 3);
+            rs = toks >= 0 ? xs16[toks * (H / 16) + g16] + xs16[toks * (H / 16) + g16 + 1] : 0.f;
+        }
+    };
+    auto store_stage = [&](int half) {
+#pragma unroll
+        for (int u = 0; u < 6; ++u) {
+            const int r = (u & 1) ? rb2 : ra;
+            *reinterpret_cast<uint4*>(smem + (u >> 1) * kXPieceB + r * kXRowB + xc * 16) = rx[u];
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int q = u * kGuThreads + tid, r = q >> 2, part = q & 3;
+            const int c = part >> 1, g0 = 2 * (part & 1);         // 16 B = groups g0, g0 + 1 of chunk c
+            *reinterpret_cast<uint2*>(smem + kGuWOff + (c * 4 + g0) * kGuPlaneB + r * 8) = make_uint2(rw[u].x, rw[u].y);
+            *reinterpret_cast<uint2*>(smem + kGuWOff + (c * 4 + g0 + 1) * kGuPlaneB + r * 8) = make_uint2(rw[u].z, rw[u].w);
+        }
+        if (tid < kGuWRows) {
+            float sj[8], bj[8];
+            pf_q4k_factors_hdr(rh, sj, bj);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                reinterpret_cast<float2*>(smem + kGuFacOff)[j * kGuWRows + tid] =
+                    half ? make_float2(sj[4 + j], bj[4 + j]) : make_float2(sj[j], bj[j]);
+        }
+        if (tid < 4 * kPfRows)
+            reinterpret_cast<float*>(smem + kGuSOff)[(tid & 3) * kPfRows + (tid >> 2)] = rs;
+    };
 
-    for (int64_t sb = 0; sb < nsb; ++sb) {
+    const int col = lane & 15, g = lane >> 4;
+    const int th = wave >> 2, fq = wave & 3;
+    const int frow0 = 32 * fq + col;                          // gate rows frow0, frow0 + 16; up rows + 128
+    f32x4_t acc[2][2][2];                                     // [token block][feature block][gate, up]
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int fb = 0; fb < 2; ++fb) {
+            acc[i][fb][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            acc[i][fb][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+
+    load_stage(0);
+    for (int st = 0; st < nst; ++st) {
         __syncthreads();                                      // the previous stage is consumed
-        if (my_tok >= 0) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {                     // 32 chunks x 32 rows of 16 B
-                const int c = (j * kPfThreads + tid) >> 5;
-                const int64_t off = (my_tok * H + sb * kQK) * 2 + c * 16;
-                const int lo16 = (j * kPfThreads + wave * kWave) * 16;
-                __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(xhi) + off,
-                                                 (lds_ptr_t)(lx_hi + lo16), 16, 0, 0);
-                __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(xmid) + off,
-                                                 (lds_ptr_t)(lx_mid + lo16), 16, 0, 0);
-                __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(xlo) + off,
-                                                 (lds_ptr_t)(lx_lo + lo16), 16, 0, 0);
-            }
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {                     // 16 groups x 32 rows of 4 B
-                const int g = (j * kPfThreads + tid) >> 5;
-                __builtin_amdgcn_global_load_lds(xs16 + my_tok * (H / 16) + sb * 16 + g,
-                                                 (lds_ptr_t)(smem + 3 * kGuXBytes + (j * kPfThreads + wave * kWave) * 4),
-                                                 4, 0, 0);
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < 3; ++j) {                         // 64 rows x 9 pieces per matrix
-            const int q = j * kPfThreads + tid;
-            if (q < kPfCols * 9) {
-                const int64_t off = (int64_t)(q / 9) * rowb + sb * kQ4KBytes + (q % 9) * 16;
-                __builtin_amdgcn_global_load_lds(gexp + off, (lds_ptr_t)(lwg + (j * kPfThreads + wave * kWave) * 16),
-                                                 16, 0, kCachePolicyNt);
-                __builtin_amdgcn_global_load_lds(uexp + off, (lds_ptr_t)(lwu + (j * kPfThreads + wave * kWave) * 16),
-                                                 16, 0, kCachePolicyNt);
-            }
-        }
-        wait_all_loads();
+        store_stage(st & 1);
         __syncthreads();
-
-        float gs[8], gb[8], us[8], ub[8];
-        pf_q4k_factors(lwg + frow * kQ4KBytes, gs, gb);
-        pf_q4k_factors(lwu + frow * kQ4KBytes, us, ub);
+        if (st + 1 < nst) load_stage(st + 1);
 #pragma unroll
-        for (int s = 0; s < 16; ++s) {                        // 16-wide k steps
-            const int kk = 16 * s + 4 * kq;                   // this lane's first k in the block
-            const int c = kk >> 6, h = (kk >> 5) & 1, lp = kk & 31, j = s >> 1;
-            const int qoff = frow * kQ4KBytes + 16 + 32 * c + lp;
-            const s16x4_t bg = pf_bf16x4(((*reinterpret_cast<const uint32_t*>(lwg + qoff) >> (4 * h)) << 3) & 0x78787878u);
-            const s16x4_t bu = pf_bf16x4(((*reinterpret_cast<const uint32_t*>(lwu + qoff) >> (4 * h)) << 3) & 0x78787878u);
+        for (int j = 0; j < 4; ++j) {                         // one sub-block per k step
+            const int c = j >> 1, h = j & 1;
+            const uint8_t* plane = smem + kGuWOff + (c * 4 + g) * kGuPlaneB;
+            bf16x8_t B[2][2];
+            float fs[2][2];
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
-                const int xoff = ((kk >> 3) * kPfRows + rb * 16 + col) * 16 + (kk & 7) * 2;
-                const s16x4_t ah = *reinterpret_cast<const s16x4_t*>(lx_hi + xoff);
-                const s16x4_t am = *reinterpret_cast<const s16x4_t*>(lx_mid + xoff);
-                const s16x4_t al = *reinterpret_cast<const s16x4_t*>(lx_lo + xoff);
-                const float4 S4 = *reinterpret_cast<const float4*>(ls16 + s * kPfRows + rb * 16 + 4 * kq);
-                const float Sv[4] = {S4.x, S4.y, S4.z, S4.w};
-                f32x4_t tg = pf_mfma(ah, bg, f32x4_t{0.f, 0.f, 0.f, 0.f});
-                tg = pf_mfma(am, bg, tg);
-                tg = pf_mfma(al, bg, tg);
-                f32x4_t tu = pf_mfma(ah, bu, f32x4_t{0.f, 0.f, 0.f, 0.f});
-                tu = pf_mfma(am, bu, tu);
-                tu = pf_mfma(al, bu, tu);
+            for (int fb = 0; fb < 2; ++fb) {
+                const int gr = frow0 + 16 * fb, ur = kGuFeat + gr;
+                B[fb][0] = pf_q4k_b8(*reinterpret_cast<const uint2*>(plane + gr * 8), h);
+                B[fb][1] = pf_q4k_b8(*reinterpret_cast<const uint2*>(plane + ur * 8), h);
+                fs[fb][0] = reinterpret_cast<const float2*>(smem + kGuFacOff)[j * kGuWRows + gr].x;
+                fs[fb][1] = reinterpret_cast<const float2*>(smem + kGuFacOff)[j * kGuWRows + ur].x;
+            }
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    acc[rb][0][r] += gs[j] * tg[r] - gb[j] * Sv[r];
-                    acc[rb][1][r] += us[j] * tu[r] - ub[j] * Sv[r];
-                }
+            for (int i = 0; i < 2; ++i) {
+                const int tb = 2 * th + i;
+                const int xo = (16 * tb + col) * kXRowB + (32 * j + 8 * g) * 2;
+                const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(smem + xo);
+                const bf16x8_t am = *reinterpret_cast<const bf16x8_t*>(smem + kXPieceB + xo);
+                const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(smem + 2 * kXPieceB + xo);
+#pragma unroll
+                for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+                    for (int m = 0; m < 2; ++m) {
+                        f32x4_t t = pf_mfma32(ah, B[fb][m], f32x4_t{0.f, 0.f, 0.f, 0.f});
+                        t = pf_mfma32(am, B[fb][m], t);
+                        t = pf_mfma32(al, B[fb][m], t);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) acc[i][fb][m][r] += fs[fb][m] * t[r];
+                    }
+            }
+        }
+        // offset and min of the stage's 4 sub-blocks: acc -= S . b, a rank-4
+        // product per tile, as one f32 matrix step (k = sub-block = lane / 16)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const float sa = reinterpret_cast<const float*>(smem + kGuSOff)[g * kPfRows + 16 * (2 * th + i) + col];
+#pragma unroll
+            for (int fb = 0; fb < 2; ++fb) {
+                const int gr = frow0 + 16 * fb;
+                const float nbg = -reinterpret_cast<const float2*>(smem + kGuFacOff)[g * kGuWRows + gr].y;
+                const float nbu = -reinterpret_cast<const float2*>(smem + kGuFacOff)[g * kGuWRows + kGuFeat + gr].y;
+                acc[i][fb][0] = pf_mfma_f32(sa, nbg, acc[i][fb][0]);
+                acc[i][fb][1] = pf_mfma_f32(sa, nbu, acc[i][fb][1]);
             }
         }
     }
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int i = rb * 16 + 4 * kq + r;
-            if (i < nrows) hbuf[(row0 + i) * F + f0 + frow] = pf_silu(acc[rb][0][r]) * acc[rb][1][r];
-        }
+        for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * (2 * th + i) + 4 * g + r;
+                if (t < nrows)
+                    hbuf[(row0 + t) * F + f0 + frow0 + 16 * fb] = pf_silu(acc[i][fb][0][r]) * acc[i][fb][1][r];
+            }
 }
 
 // ------------------------------------------------------------------- down --
-// LDS: the expert's down rows h0..h0+63 (all F/256 blocks, contiguous in HBM,
-// + 16 bytes of padding for the unaligned Q6_K reads), then the h pieces of
-// the tile for the current super-block (k-major), their group sums [16][32],
-// and the (scale, offset) of every (row, 16-wide group) of the super-block.
+// One workgroup per (64 output rows, pair tile).  The expert's 64-row tile
+// of the down matrix (all F/256 blocks, contiguous in HBM) is staged once
+// with the first stage; the h pieces (hi, lo) and their 16-value sums are
+// staged per 128-wide k stage.  8 waves: wave w owns output rows
+// 16 (w & 3).. and token blocks 2 (w >> 2), 2 (w >> 2) + 1.  Each k step is
+// one 16-wide scale group (v_mfma_f32_16x16x16bf16_1k on exact bf16 weights
+// 128 + q (Q6_K) or 128 + 8q (Q4_K) with each h piece), scaled by the
+// group's factor; the offset (and the Q4_K min) times each group's h sum
+// leaves once per stage as f32 rank-4 matrix steps.
+constexpr int kDnOut = 64;
+constexpr int kDnThreads = 512;
+constexpr int kDnMaxW16 = 10;                                 // F <= 1536: <= 5040 16-byte pieces
 __host__ __device__ inline int pf_down_wbytes(int64_t F, int32_t qtype) {
-    return (int)(kPfCols * (F / kQK) * (qtype == 2 ? kQ6KBytes : kQ4KBytes));
+    return (int)(kDnOut * (F / kQK) * (qtype == 2 ? kQ6KBytes : kQ4KBytes));
 }
-constexpr int kDnFacBytes = kPfCols * 16 * 8;                 // (scale, offset) per row and group
+__host__ __device__ inline int pf_down_hoff(int64_t F, int32_t qtype) {
+    return (pf_down_wbytes(F, qtype) + 16 + 15) & ~15;       // + padding for the unaligned Q6_K reads
+}
 __host__ __device__ inline int pf_down_lds(int64_t F, int32_t qtype) {
-    return pf_down_wbytes(F, qtype) + 16 + 2 * kGuXBytes + kGuSBytes + kDnFacBytes;
+    return pf_down_hoff(F, qtype) + 2 * kXPieceB + 8 * kPfRows * 4;
 }
 
-__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2))) void pf_down_kernel(
+__global__ __launch_bounds__(kDnThreads) void pf_down_kernel(
     const uint16_t* __restrict__ hhi, const uint16_t* __restrict__ hlo,
     const float* __restrict__ hs16, int64_t F, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ tile_off, const int32_t* __restrict__ pairs, int32_t E,
@@ -303,126 +408,145 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
     extern __shared__ __align__(16) uint8_t smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int slot, htile;
-    pf_xcd_tile((int)blockIdx.x, (int)(H / kPfCols), slot, htile);
+    pf_xcd_tile((int)blockIdx.x, (int)(H / kDnOut), slot, htile);
     if (slot >= tile_off[E]) return;
     const int e = pf_tile_expert(tile_off, E, slot);
     const int64_t row0 = offsets[e] + (int64_t)(slot - tile_off[e]) * kPfRows;
     const int nrows = (int)min((int64_t)kPfRows, (int64_t)offsets[e + 1] - row0);
-    const int64_t h0 = (int64_t)htile * kPfCols;
+    const int64_t h0 = (int64_t)htile * kDnOut;
     const bool q6 = qtype == 2;
     const int bb = q6 ? kQ6KBytes : kQ4KBytes;
-    const int64_t nsb = F / kQK;
-    const int rowb = (int)(nsb * bb);
-    const int wbytes = kPfCols * rowb;
-    uint8_t* lw = smem;
-    uint8_t* lx_hi = smem + wbytes + 16;
-    uint8_t* lx_lo = lx_hi + kGuXBytes;
-    const float* ls16 = reinterpret_cast<const float*>(lx_lo + kGuXBytes);
-    float2* lfac = reinterpret_cast<float2*>(lx_lo + kGuXBytes + kGuSBytes);   // [group][row]
+    const int nb = (int)(F / kQK);
+    const int rowb = nb * bb;
+    const int wbytes = kDnOut * rowb;                         // a multiple of 16
+    const int hoff = pf_down_hoff(F, qtype);
+    const int soff = hoff + 2 * kXPieceB;
+    const int nst = (int)(F / kStageK);
 
-    // the whole row tile of the down matrix, once
-    {
-        const uint8_t* src = dbase + (int64_t)e * dstride + h0 * rowb;
-        const int n16 = wbytes >> 4;
-        for (int base = wave * kWave; base < n16; base += kPfThreads)
-            if (base + lane < n16)
-                __builtin_amdgcn_global_load_lds(src + (int64_t)(base + lane) * 16, (lds_ptr_t)(lw + base * 16), 16, 0,
-                                                 kCachePolicyNt);
+    // staging roles: the weight tile (n16 pieces of 16 B over 512 threads,
+    // with the first stage); h pieces 2 x 64 rows x 16 chunks (u < 4: piece
+    // u >> 1, rows tid/16 and 32 + tid/16); sums 8 groups x 64 rows (one per
+    // thread: row tid >> 3, group tid & 7).
+    const u32x4v_t* wsrc = reinterpret_cast<const u32x4v_t*>(dbase + (int64_t)e * dstride + h0 * rowb);
+    const int n16 = wbytes >> 4;
+    u32x4v_t rwt[kDnMaxW16];                                  // the weight tile, with stage 0
+#pragma unroll
+    for (int u = 0; u < kDnMaxW16; ++u) {
+        const int q = u * kDnThreads + tid;
+        if (q < n16) rwt[u] = __builtin_nontemporal_load(wsrc + q);
     }
+    const int ra = tid >> 4, rb2 = 32 + (tid >> 4), hc = tid & 15;
+    const int64_t pa = ra < nrows ? row0 + ra : -1;
+    const int64_t pb = rb2 < nrows ? row0 + rb2 : -1;
+    const int srow = tid >> 3, sgrp = tid & 7;
+    const int64_t ps = srow < nrows ? row0 + srow : -1;
+    const uint16_t* hsrc[2] = {hhi, hlo};
+    uint4 rx[4];
+    float rs = 0.f;
+    auto load_stage = [&](int st) {
+        const int64_t k0 = (int64_t)st * kStageK;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t pr = (u & 1) ? pb : pa;
+            rx[u] = pr >= 0 ? *reinterpret_cast<const uint4*>(hsrc[u >> 1] + pr * F + k0 + 8 * hc)
+                            : make_uint4(0, 0, 0, 0);
+        }
+        rs = ps >= 0 ? hs16[ps * (F / 16) + (k0 >> 4) + sgrp] : 0.f;
+    };
+    auto store_stage = [&]() {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int r = (u & 1) ? rb2 : ra;
+            *reinterpret_cast<uint4*>(smem + hoff + (u >> 1) * kXPieceB + r * kXRowB + hc * 16) = rx[u];
+        }
+        reinterpret_cast<float*>(smem + soff)[sgrp * kPfRows + srow] = rs;
+    };
 
-    const int my_row = tid & 31;
-    const int col = lane & 15, kq = lane >> 4;
-    const int frow = wave * 16 + col;
-    const uint8_t* wrow = lw + frow * rowb;
+    const int col = lane & 15, g = lane >> 4;
+    const int orow = 16 * (wave & 3) + col;                   // this lane's output row in the tile
+    const int tb0 = 2 * (wave >> 2);
     f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
 
-    for (int64_t sb = 0; sb < nsb; ++sb) {
-        __syncthreads();
-        if (my_row < nrows) {
+    load_stage(0);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {                     // 32 chunks x 32 rows of 16 B, k-major
-                const int c = (j * kPfThreads + tid) >> 5;
-                const int64_t off = ((row0 + my_row) * F + sb * kQK) * 2 + c * 16;
-                const int lo16 = (j * kPfThreads + wave * kWave) * 16;
-                __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(hhi) + off,
-                                                 (lds_ptr_t)(lx_hi + lo16), 16, 0, 0);
-                __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(hlo) + off,
-                                                 (lds_ptr_t)(lx_lo + lo16), 16, 0, 0);
-            }
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {                     // 16 groups x 32 rows of 4 B
-                const int g = (j * kPfThreads + tid) >> 5;
-                __builtin_amdgcn_global_load_lds(hs16 + (row0 + my_row) * (F / 16) + sb * 16 + g,
-                                                 (lds_ptr_t)(lx_lo + kGuXBytes + (j * kPfThreads + wave * kWave) * 4),
-                                                 4, 0, 0);
-            }
-        }
-        wait_all_loads();
+    for (int u = 0; u < kDnMaxW16; ++u) {
+        const int q = u * kDnThreads + tid;
+        if (q < n16) *reinterpret_cast<u32x4v_t*>(smem + 16 * q) = rwt[u];
+    }
+    for (int st = 0; st < nst; ++st) {
         __syncthreads();
-
-        // (scale, offset) of every (row, 16-wide group) of this super-block
-        for (int f = tid; f < kPfCols * 16; f += kPfThreads) {
-            const int r = f >> 4, g = f & 15;
-            const uint8_t* b = lw + r * rowb + sb * bb;
-            float sc, off;
-            if (q6) {
-                sc = half_bits_to_float(b[208] | (b[209] << 8)) * (float)(int8_t)b[192 + g];
-                off = 160.f * sc;                             // (128 + q) - 160 = q - 32
-            } else {
-                const uint4 hdr = *reinterpret_cast<const uint4*>(b);
-                int scj, mj;
-                const int j = g >> 1;
-                const uint32_t s0 = hdr.y, s1 = hdr.z, s2 = hdr.w;
-                if (j < 4) {
-                    scj = (s0 >> (8 * j)) & 63;
-                    mj = (s1 >> (8 * j)) & 63;
-                } else {
-                    const int jj = j - 4;
-                    scj = ((s2 >> (8 * jj)) & 15) | (((s0 >> (8 * jj + 6)) & 3) << 4);
-                    mj = ((s2 >> (8 * jj + 4)) & 15) | (((s1 >> (8 * jj + 6)) & 3) << 4);
-                }
-                sc = 0.125f * half_bits_to_float(hdr.x & 0xffffu) * (float)scj;   // 128 + 8q
-                off = 128.f * sc + half_bits_to_float(hdr.x >> 16) * (float)mj;
-            }
-            lfac[g * kPfCols + r] = make_float2(sc, off);
-        }
+        store_stage();
         __syncthreads();
-
-        const uint8_t* blk = wrow + sb * bb;
-#pragma unroll 4
-        for (int s = 0; s < 16; ++s) {
-            const int kk = 16 * s + 4 * kq;
-            const float2 fac = lfac[s * kPfCols + frow];
+        if (st + 1 < nst) load_stage(st + 1);
+        const int sb = st >> 1, half = st & 1;
+        const int boff = orow * rowb + sb * bb;               // this lane's block in the tile
+        const uint8_t* blk = smem + boff;
+        float dq = 0.f, dm = 0.f;
+        uint4 hdr = make_uint4(0, 0, 0, 0);
+        if (q6) {
+            dq = half_bits_to_float(blk[208] | (blk[209] << 8));
+        } else {
+            hdr = *reinterpret_cast<const uint4*>(blk);
+            dq = 0.125f * half_bits_to_float(hdr.x & 0xffffu);   // weights enter as 128 + 8q
+            dm = half_bits_to_float(hdr.x >> 16);
+        }
+#pragma unroll 2
+        for (int G = 0; G < 8; ++G) {                         // one 16-wide group per k step
+            const int gi = 8 * half + G;                      // group within the super-block
             uint32_t q;
+            float sc;
             if (q6) {
-                const int n = kk >> 7, r = (kk >> 5) & 3, lp = kk & 31;
-                const uint32_t ql = pf_lds_u32_a2(blk, 64 * n + 32 * (r & 1) + lp);
-                const uint32_t qh = pf_lds_u32_a2(blk, 128 + 32 * n + lp);
+                const int r = (gi >> 1) & 3, lp = 16 * (gi & 1) + 4 * g;
+                const uint32_t ql = pf_lds_u32_a2(smem, boff + 64 * half + 32 * (r & 1) + lp);
+                const uint32_t qh = pf_lds_u32_a2(smem, boff + 128 + 32 * half + lp);
                 q = ((ql >> (4 * (r >> 1))) & 0x0f0f0f0fu) | (((qh >> (2 * r)) & 0x03030303u) << 4);
+                sc = dq * (float)(int8_t)blk[192 + gi];
             } else {
-                const int c = kk >> 6, h = (kk >> 5) & 1, lp = kk & 31;
+                const int J = gi >> 1, c = J >> 1, h = J & 1, lp = 16 * (gi & 1) + 4 * g;
                 q = ((*reinterpret_cast<const uint32_t*>(blk + 16 + 32 * c + lp) >> (4 * h)) << 3) & 0x78787878u;
+                int scj, mj;
+                q4k_scale_min(blk + 4, J, scj, mj);
+                sc = dq * (float)scj;
             }
             const s16x4_t bw = pf_bf16x4(q);
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
-                const int xoff = ((kk >> 3) * kPfRows + rb * 16 + col) * 16 + (kk & 7) * 2;
-                f32x4_t t = pf_mfma(*reinterpret_cast<const s16x4_t*>(lx_hi + xoff), bw, f32x4_t{0.f, 0.f, 0.f, 0.f});
-                t = pf_mfma(*reinterpret_cast<const s16x4_t*>(lx_lo + xoff), bw, t);
-                const float4 S4 = *reinterpret_cast<const float4*>(ls16 + s * kPfRows + rb * 16 + 4 * kq);
-                acc[rb][0] += fac.x * t[0] - fac.y * S4.x;
-                acc[rb][1] += fac.x * t[1] - fac.y * S4.y;
-                acc[rb][2] += fac.x * t[2] - fac.y * S4.z;
-                acc[rb][3] += fac.x * t[3] - fac.y * S4.w;
+            for (int i = 0; i < 2; ++i) {
+                const int tb = tb0 + i;
+                const int xo = hoff + (16 * tb + col) * kXRowB + (16 * G + 4 * g) * 2;
+                f32x4_t t = pf_mfma(*reinterpret_cast<const s16x4_t*>(smem + xo), bw, f32x4_t{0.f, 0.f, 0.f, 0.f});
+                t = pf_mfma(*reinterpret_cast<const s16x4_t*>(smem + kXPieceB + xo), bw, t);
+                acc[i][0] += sc * t[0];
+                acc[i][1] += sc * t[1];
+                acc[i][2] += sc * t[2];
+                acc[i][3] += sc * t[3];
+            }
+        }
+        // the offset (and the Q4_K min) of the stage's 8 groups: acc -= S . off,
+        // two f32 rank-4 matrix steps per tile (k = group = 4 * p + lane / 16)
+#pragma unroll
+        for (int pq = 0; pq < 2; ++pq) {
+            const int gi = 8 * half + 4 * pq + g;             // this lane's group (its k slot)
+            float off;
+            if (q6) {
+                off = 160.f * dq * (float)(int8_t)blk[192 + gi];   // (128 + q) - 160 = q - 32
+            } else {
+                int scj, mj;
+                q4k_scale_min(blk + 4, gi >> 1, scj, mj);
+                off = 128.f * dq * (float)scj + dm * (float)mj;
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const float sa = reinterpret_cast<const float*>(smem + soff)[(4 * pq + g) * kPfRows + 16 * (tb0 + i) + col];
+                acc[i] = pf_mfma_f32(sa, -off, acc[i]);
             }
         }
     }
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int i = rb * 16 + 4 * kq + r;
-            if (i < nrows) Y[(int64_t)pairs[row0 + i] * H + h0 + frow] = acc[rb][r];
+            const int t = 16 * (tb0 + i) + 4 * g + r;
+            if (t < nrows) Y[(int64_t)pairs[row0 + t] * H + h0 + orow] = acc[i][r];
         }
 }
 
@@ -521,7 +645,7 @@ hipError_t launch_prefill_ffn(const float* hidden, int64_t T, int64_t H, int64_t
     static LdsLimit gu_lds;
     if ((err = ensure_lds(reinterpret_cast<const void*>(pf_gateup_kernel), gu_lds, kGuLds)) != hipSuccess)
         return err;
-    hipLaunchKernelGGL(pf_gateup_kernel, dim3((unsigned)(F / kPfCols) * slots), dim3(kPfThreads), kGuLds,
+    hipLaunchKernelGGL(pf_gateup_kernel, dim3((unsigned)(F / kGuFeat) * slots), dim3(kGuThreads), kGuLds,
                        stream, reinterpret_cast<const uint16_t*>(base + L.xhi),
                        reinterpret_cast<const uint16_t*>(base + L.xmid),
                        reinterpret_cast<const uint16_t*>(base + L.xlo),
@@ -541,7 +665,7 @@ hipError_t launch_prefill_ffn(const float* hidden, int64_t T, int64_t H, int64_t
     if ((err = ensure_lds(reinterpret_cast<const void*>(pf_down_kernel), down_lds, dl)) != hipSuccess)
         return err;
     float* Y = reinterpret_cast<float*>(base + L.y);
-    hipLaunchKernelGGL(pf_down_kernel, dim3((unsigned)(H / kPfCols) * slots), dim3(kPfThreads), dl, stream,
+    hipLaunchKernelGGL(pf_down_kernel, dim3((unsigned)(H / kDnOut) * slots), dim3(kDnThreads), dl, stream,
                        reinterpret_cast<const uint16_t*>(base + L.hhi),
                        reinterpret_cast<const uint16_t*>(base + L.hlo),
                        reinterpret_cast<const float*>(base + L.hs16), F, offsets, tile_off, pairs, E,
