@@ -50,6 +50,8 @@ def parse():
                     help="replays of the FFN-only graph used for kernel timing")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the 512-token prefill measurement")
+    ap.add_argument("--no-layer", action="store_true",
+                    help="skip the full decoder-layer measurement (batch 1 and 16)")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="for hardware-counter runs: a few eager steps (no graph), then one "
                          "device-to-device copy of PMC_COPY_BYTES that calibrates the "
@@ -66,8 +68,8 @@ PMC_STEPS = 16
 # in profiles/ffn_fused8_kernel_a3b_decode_b1_traffic.md.  The figure belongs
 # to the kernel sources it was measured on; when they change it is reported
 # as null until the counters are taken again.
-TRAFFIC_BYTES_PER_LAUNCH = 25_612_842
-TRAFFIC_SOURCES_SHA256 = "cd6f7a62a956e2e4516b974e6470497fc028956f9876feb614eb6ce1b650fef3"
+TRAFFIC_BYTES_PER_LAUNCH = 25_630_800
+TRAFFIC_SOURCES_SHA256 = "94d1cefbf3f42f35843992217ca78e7f6679856e36b5321d187896b40c19da39"
 TRAFFIC_SOURCES = ("sparse_moe_decode_q3moe_amd/csrc/ffn_decode.hip",
                    "sparse_moe_decode_q3moe_amd/csrc/device_common.h")
 
@@ -239,6 +241,9 @@ def main():
     if not args.no_prefill:
         result["prefill_512"] = prefill_bench(torch, q3, gen, layers, experts, shape, dev)
 
+    if not args.no_layer:
+        result["decoder_layer"] = decoder_bench(torch, q3, gen, layers, experts, shape, dev)
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, torch, gen, layers, xs, outs, shape)
 
@@ -331,6 +336,110 @@ def prefill_bench(torch, q3, gen, layers, experts, shape, dev):
         del g, gf
     res["note"] = ("bf16 matrix-core tiles with the activations split into bf16 pieces (3 for "
                    "gate/up, 2 for down), so the MFMA work is 2.5x the algorithmic flops")
+    return res
+
+
+def decoder_bench(torch, q3, gen, layers, experts, shape, dev):
+    """The whole Qwen3-30B-A3B decoder layer at decode: input RMSNorm, bf16
+    Q/K/V projections, Q/K norm + RoPE, KV write, GQA attention over 4096
+    cached positions (sequence b at position 4095 - 211 b), O projection with
+    the residual, post-attention RMSNorm, route, expert FFN with the
+    residual.  Batch 1 and 16; attention layer copies (36 MB of bf16 weights
+    each, plus their KV caches) and the 16 MoE layer copies rotate, so the
+    Infinity Cache does not serve repeated bytes.  Reported: time per layer
+    step, tokens/s, and the algorithmic HBM bytes per step over that time; and
+    the attention half alone (norm through O projection)."""
+    s_ = gen.QWEN3_30B_A3B_ATTN
+    H, E, k, F = shape.H, shape.E, shape.k, shape.F
+    nq, nkv, D, S = s_.n_q, s_.n_kv, s_.D, s_.S_max
+    res = {"attention_weight_bytes": (2 * nq * D * H + 2 * nkv * D * H) * 2}
+    for B, ncopies in ((1, 8), (16, 4)):
+        atts = [gen.attn_layer(s_, 200 + c, device=dev) for c in range(ncopies)]
+        caches = [gen.kv_caches(B, s_, 300 + c, device=dev) for c in range(ncopies)]
+        x = gen.hidden_states(B, H, 9, device=dev)
+        pos = torch.tensor([S - 1 - 211 * b for b in range(B)], dtype=torch.int32, device=dev)
+        lens = pos + 1
+        xn = torch.empty((B, H), device=dev)
+        q = torch.empty((B, nq * D), device=dev)
+        kk = torch.empty((B, nkv * D), device=dev)
+        vv = torch.empty((B, nkv * D), device=dev)
+        ao = torch.empty((B, nq, D), device=dev)
+        x1 = torch.empty((B, H), device=dev)
+        hn = torch.empty((B, H), device=dev)
+        out = torch.empty((B, H), device=dev)
+        idx = torch.empty((B, k), dtype=torch.int32, device=dev)
+        wts = torch.empty((B, k), device=dev)
+        ws_a = torch.empty(q3.q3moe_gqa_attention_workspace_bytes(B, nq, nkv, D, S), dtype=torch.uint8, device=dev)
+        ws_r = torch.zeros(q3.q3moe_route_workspace_bytes(B, E), dtype=torch.uint8, device=dev)
+        ws_f = torch.zeros(q3.q3moe_expert_ffn_workspace_bytes(B, H, F, E, k), dtype=torch.uint8, device=dev)
+
+        def attention(i):
+            A = atts[i % ncopies]
+            kc, vc = caches[i % ncopies]
+            q3.q3moe_rmsnorm(x, A.in_norm, s_.eps, out=xn)
+            q3.q3moe_bf16_gemv(A.wq, xn, out=q)
+            q3.q3moe_bf16_gemv(A.wk, xn, out=kk)
+            q3.q3moe_bf16_gemv(A.wv, xn, out=vv)
+            q3.q3moe_attn_prologue(q.view(B, nq, D), kk.view(B, nkv, D), A.q_norm, A.k_norm, pos,
+                                   s_.eps, s_.rope_base)
+            q3.q3moe_kv_write(kk.view(B, nkv, D), vv.view(B, nkv, D), pos, kc, vc)
+            q3.q3moe_gqa_attention(q.view(B, nq, D), kc, vc, lens, 1.0 / math.sqrt(D), out=ao,
+                                   workspace=ws_a)
+            x1.copy_(x)
+            q3.q3moe_bf16_gemv(A.wo, ao.view(B, nq * D), out=x1, accumulate=True)
+
+        def layer(i):
+            attention(i)
+            L = layers[i % len(layers)]
+            q3.q3moe_rmsnorm(x1, atts[i % ncopies].post_norm, s_.eps, out=hn)
+            q3.q3moe_route(hn, L.router, k, idx, wts, workspace=ws_r)
+            out.copy_(x1)
+            q3.q3moe_expert_ffn(hn, idx, wts, *experts[i % len(experts)], F=F, out=out, accumulate=True,
+                                workspace=ws_f)
+
+        n = 16
+        for i in range(n):
+            layer(i)
+        torch.cuda.synchronize()
+        distinct = []
+        for i in range(n):
+            layer(i)
+            distinct.append(int(torch.unique(idx).numel()))
+        graphs = {}
+        for name, fn in (("layer", layer), ("attention", attention)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(n):
+                    fn(i)
+            g.replay()
+            graphs[name] = g
+        torch.cuda.synchronize()
+        times = {}
+        for name, g in graphs.items():
+            reps = 10
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(reps):
+                g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            times[name] = a.elapsed_time(b) * 1000.0 / (reps * n)
+        kv_bytes = int(2 * nkv * D * 2 * lens.sum().item())      # K and V rows read
+        att_bytes = res["attention_weight_bytes"] + kv_bytes + 2 * B * nkv * D * 2
+        d_avg = sum(distinct) / len(distinct)
+        moe_bytes = d_avg * (2 * shape.gate_stride + shape.down_stride) + E * H * 4
+        layer_bytes = att_bytes + moe_bytes
+        res[f"batch_{B}"] = {
+            "layer_us": round(times["layer"], 2),
+            "tokens_per_s": round(B / (times["layer"] * 1e-6), 1),
+            "layer_hbm_bytes": int(layer_bytes),
+            "layer_hbm_gbps": round(layer_bytes / (times["layer"] * 1e-6) / 1e9, 1),
+            "attention_us": round(times["attention"], 2),
+            "attention_hbm_gbps": round(att_bytes / (times["attention"] * 1e-6) / 1e9, 1),
+            "distinct_experts_per_step": round(d_avg, 2),
+        }
+        del graphs, atts, caches
+        torch.cuda.empty_cache()
     return res
 
 
