@@ -242,70 +242,97 @@ __device__ __forceinline__ void gu_compute(const uint8_t* wg, const uint8_t* xp,
 // per task) with each lane owning a column chunk: lane = b*8 + c*2 + hp owns
 // quant bytes 32c + 16hp .. +15 of super-block b, i.e. 16 weights of
 // sub-block 2c (low nibbles) and 16 of sub-block 2c+1 (high nibbles).  The
-// lane loads its 32 activations and its weights straight into registers
-// (16 quant bytes and the 16-byte block header per row), so nothing goes
-// through LDS and each row is consumed as soon as its loads land.  The 8 row
-// partials are folded across the wave with a transposed butterfly: after it,
-// lanes 8q..8q+7 hold row q (q < 4 gate row q, else up row q-4).
+// lane loads its weights straight into registers (16 quant bytes and the
+// 16-byte block header per row), so nothing goes through LDS and each row is
+// consumed as soon as its loads land.  The 8 row partials are folded across
+// the wave with a transposed butterfly: after it, lanes 8q..8q+7 hold row q
+// (q < 4 gate row q, else up row q-4).
+//
+// Activations enter as three int8 pieces per value: for each 32-value group
+// (one Q4_K sub-block) a power of two s with max|x| / s < 127.5 and
+//   x = s * (p1 + p2 / 2^7 + p3 / 2^14) + r,   |r| <= s * 2^-15,
+// p1 in [-127, 127], p2 and p3 in [-64, 64] (each a rounded residual, all
+// steps exact in f32).  The nibbles are int8 values 0..15, so v_dot4_i32_i8
+// gives each piece's dot product over 4 weights exactly in int32, and
+// 2^14 S1 + 2^7 S2 + S3 (< 2^30 for 16 weights) is the whole sub-block dot
+// in units of s * 2^-14, exact until its one conversion to f32.  The min
+// term uses the exact f32 sums of the activations.
+//
+// Per token in LDS (kI8TokenBytes): piece P at P * kI8PieceBytes as
+// [half][lane][16 bytes] (half 0: the lane's low-nibble values, 1: its
+// high-nibble values), then the 64 group scales s * 2^-14 (f32, group
+// b*8 + j), then the 16-value sums as [half][lane] (f32).
+constexpr int kI8PieceBytes = 2 * kWave * 16;
+constexpr int kI8ScaleOff = 3 * kI8PieceBytes;
+constexpr int kI8SumOff = kI8ScaleOff + 64 * 4;
+constexpr int kI8TokenBytes = kI8SumOff + 2 * kWave * 4;
+
 struct XCols {
-    uint4 lo[4], hi[4];      // (hi, mid) pieces of the low-nibble and high-nibble values
-    uint2 lo3[4], hi3[4];    // their third pieces
-    float slo, shi;          // their sums (one 16-value group each)
+    uint4 p[3][2];           // [piece][half]: 16 int8 pieces each
+    float sa, sb;            // group scales (times 2^-14) of the two halves
+    float slo, shi;          // sums of the lane's 16 low-nibble / high-nibble values
+    uint32_t sel;            // byte selector of the lane's two sub-blocks' scale bytes
+    uint32_t shh;            // 4 (sub-blocks 0-3) or 6 (4-7): where their top scale bits sit
+    bool hiform;             // sub-blocks 4-7: low scale bits in the third scale dword
 };
 
-// The lane's 32 activations of one token from the token's piece blocks in
-// LDS (xp: 8 blocks of kBlockPieceStride bytes; gs: the 16-value group sums;
-// xlo: the third pieces, 8 blocks of kBlockLoStride bytes).
-__device__ __forceinline__ XCols load_xcols(const uint8_t* xp, const float* gs, const uint8_t* xlo,
-                                            int lane) {
-    const int b = lane >> 3, c = (lane >> 1) & 3, hp = lane & 1;
-    const uint8_t* xb = xp + b * kBlockPieceStride;
-    const uint8_t* xl = xlo + b * kBlockLoStride;
+__device__ __forceinline__ XCols load_xcols(const uint8_t* xt, int lane) {
+    const int b = lane >> 3, c = (lane >> 1) & 3;
     XCols x;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        x.lo[q] = *reinterpret_cast<const uint4*>(xb + (16 * c + 4 * hp + q) * kSlotBytes);
-        x.hi[q] = *reinterpret_cast<const uint4*>(xb + (16 * c + 8 + 4 * hp + q) * kSlotBytes);
-        x.lo3[q] = *reinterpret_cast<const uint2*>(xl + (16 * c + 4 * hp + q) * 8);
-        x.hi3[q] = *reinterpret_cast<const uint2*>(xl + (16 * c + 8 + 4 * hp + q) * 8);
-    }
-    x.slo = gs[b * 16 + 4 * c + hp];
-    x.shi = gs[b * 16 + 4 * c + 2 + hp];
+    for (int q = 0; q < 3; ++q)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            x.p[q][h] = *reinterpret_cast<const uint4*>(xt + q * kI8PieceBytes + h * (kWave * 16) + lane * 16);
+    const float* sc = reinterpret_cast<const float*>(xt + kI8ScaleOff);
+    const float* sm = reinterpret_cast<const float*>(xt + kI8SumOff);
+    x.sa = sc[b * 8 + 2 * c];
+    x.sb = sc[b * 8 + 2 * c + 1];
+    x.slo = sm[lane];
+    x.shi = sm[kWave + lane];
+    const uint32_t jx = (2 * c) & 3, jy = jx + 1;
+    x.sel = jx | ((jx + 4) << 8) | (jy << 16) | ((jy + 4) << 24);
+    x.hiform = c >= 2;
+    x.shh = x.hiform ? 6 : 4;
     return x;
+}
+
+__device__ __forceinline__ int sdot4(uint32_t a, uint32_t b, int c) {
+    return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
 }
 
 // One row's contribution of this lane: hdr = the block header (d, dmin, 12
 // scale bytes), qv = the lane's 16 quant bytes.
-__device__ __forceinline__ float q4k_cols_row(uint4 hdr, uint4 qv, const XCols& x, int lane) {
-    const int c = (lane >> 1) & 3;
+__device__ __forceinline__ float q4k_cols_row(uint4 hdr, uint4 qv, const XCols& x) {
     const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
-    float A = 0.f, B = 0.f;
+    int a1 = 0, a2 = 0, a3 = 0, b1 = 0, b2 = 0, b3 = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const uint32_t lo = (qw[q] << 3) & 0x78787878u;       // 8 * low nibbles of the 4 bytes
-        const uint32_t hi = (qw[q] >> 1) & 0x78787878u;       // 8 * high nibbles
-        const uint32_t p0 = bf16_pair_even(lo), p1 = bf16_pair_odd(lo);
-        const uint32_t p2 = bf16_pair_even(hi), p3 = bf16_pair_odd(hi);
-        A = dot2_bf16(p0, x.lo[q].x, A);
-        A = dot2_bf16(p1, x.lo[q].y, A);
-        A = dot2_bf16(p0, x.lo[q].z, A);
-        A = dot2_bf16(p1, x.lo[q].w, A);
-        B = dot2_bf16(p2, x.hi[q].x, B);
-        B = dot2_bf16(p3, x.hi[q].y, B);
-        B = dot2_bf16(p2, x.hi[q].z, B);
-        B = dot2_bf16(p3, x.hi[q].w, B);
-        A = dot2_bf16(p0, x.lo3[q].x, A);
-        A = dot2_bf16(p1, x.lo3[q].y, A);
-        B = dot2_bf16(p2, x.hi3[q].x, B);
-        B = dot2_bf16(p3, x.hi3[q].y, B);
+        const uint32_t lo = qw[q] & 0x0f0f0f0fu;               // 4 weights of sub-block 2c
+        const uint32_t hi = (qw[q] >> 4) & 0x0f0f0f0fu;        // 4 weights of sub-block 2c+1
+        const uint32_t xl[3] = {(&x.p[0][0].x)[q], (&x.p[1][0].x)[q], (&x.p[2][0].x)[q]};
+        const uint32_t xh[3] = {(&x.p[0][1].x)[q], (&x.p[1][1].x)[q], (&x.p[2][1].x)[q]};
+        a1 = sdot4(lo, xl[0], a1);
+        a2 = sdot4(lo, xl[1], a2);
+        a3 = sdot4(lo, xl[2], a3);
+        b1 = sdot4(hi, xh[0], b1);
+        b2 = sdot4(hi, xh[1], b2);
+        b3 = sdot4(hi, xh[2], b3);
     }
-    int sc0, mn0, sc1, mn1;
-    q4k_sm_var(hdr.y, hdr.z, hdr.w, 2 * c, sc0, mn0);
-    q4k_sm_var(hdr.y, hdr.z, hdr.w, 2 * c + 1, sc1, mn1);
+    const int A = a1 * 16384 + a2 * 128 + a3;
+    const int B = b1 * 16384 + b2 * 128 + b3;
+    // [sc(2c), mn(2c), sc(2c+1), mn(2c+1)] as bytes, branch-free: the low four
+    // bits come from the first two scale dwords (sub-blocks 0-3) or from the
+    // third one's nibbles (4-7), the top two from bits 4-5 or 6-7 of the first two
+    const uint32_t q = __builtin_amdgcn_perm(hdr.z, hdr.y, x.sel);
+    const uint32_t r = __builtin_amdgcn_perm(hdr.w >> 4, hdr.w, x.sel);
+    const uint32_t low4 = (x.hiform ? r : q) & 0x0f0f0f0fu;
+    const uint32_t sm = low4 | (((q >> x.shh) & 0x03030303u) << 4);
     const float d = half_bits_to_float(hdr.x & 0xffffu);
     const float dmin = half_bits_to_float(hdr.x >> 16);
-    return 0.125f * d * ((float)sc0 * (A - 128.f * x.slo) + (float)sc1 * (B - 128.f * x.shi)) -
-           dmin * ((float)mn0 * x.slo + (float)mn1 * x.shi);
+    const float sc0 = (float)(sm & 0xffu), mn0 = (float)((sm >> 8) & 0xffu);
+    const float sc1 = (float)((sm >> 16) & 0xffu), mn1 = (float)(sm >> 24);
+    return d * (sc0 * ((float)A * x.sa) + sc1 * ((float)B * x.sb)) - dmin * (mn0 * x.slo + mn1 * x.shi);
 }
 
 // Sum v[0..7] over the 64 lanes; returns row (lane >> 3)'s total.
@@ -540,7 +567,6 @@ __global__ __launch_bounds__(kDnWaves * kWave) void down_decode_kernel(
 // and the lane's 16 quant bytes of gate rows r0..r0+3, then of up rows.
 struct GuRows {
     uint4 hdr[8], qv[8];
-    bool valid;
 };
 
 // Loads are unconditional (an out-of-range expert reads expert 0's rows and
@@ -553,8 +579,7 @@ __device__ __forceinline__ void gu_rows_load(GuRows& g, int e, int32_t E,
     using G = GuTask<8>;
     const int b = lane >> 3, c = (lane >> 1) & 3, hp = lane & 1;
     const int qoff = 16 + 32 * c + 16 * hp;
-    g.valid = e >= 0 && e < E;
-    const int64_t es = g.valid ? e : 0;
+    const int64_t es = e >= 0 && e < E ? e : 0;
     const uint8_t* g0 = gbase + es * gstride + r0 * G::ROWB + b * kQ4KBytes;
     const uint8_t* u0 = ubase + es * ustride + r0 * G::ROWB + b * kQ4KBytes;
 #pragma unroll
@@ -569,9 +594,16 @@ __device__ __forceinline__ void gu_rows_load(GuRows& g, int e, int32_t E,
 // value index value_base (a multiple of 4) with device-scope stores.
 __device__ __forceinline__ void gu_rows_finish(const GuRows& g, const XCols& x, int lane,
                                                uint8_t* __restrict__ hpieces, int64_t value_base) {
+    // rows in load order, each fenced off so that it waits only for its own
+    // loads (they complete in order).  A pair whose expert is out of range
+    // computes on expert 0's rows; its h is never read (the down stage and
+    // the combine skip that slot).
     float v[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = g.valid ? q4k_cols_row(g.hdr[i], g.qv[i], x, lane) : 0.f;
+    for (int i = 0; i < 8; ++i) {
+        v[i] = q4k_cols_row(g.hdr[i], g.qv[i], x);
+        __builtin_amdgcn_sched_barrier(0);
+    }
     const float r = fold8_rows(v, lane);               // lanes 8q..: row q
     const float up = __shfl_xor(r, 32, kWave);          // lane 8q (q < 4) gets up row q
     const float h = silu_f(r) * up;
@@ -648,7 +680,7 @@ struct FusedLds {
 __host__ __device__ inline FusedLds fused_lds(int64_t T, int64_t F, int32_t qtype) {
     const DnGeom d(F, qtype);
     FusedLds L;
-    L.xp_bytes = kFzNB * kBlockPieceStride + kFzNB * 16 * 4 + kFzNB * kBlockLoStride;       // pieces + group sums per token
+    L.xp_bytes = kI8TokenBytes;                                     // int8 pieces, scales, sums per token
     L.dn_off = (int)T * L.xp_bytes;                                 // down tiles, one per slot
     L.hp_off = L.dn_off + kFzMaxSlots * d.tile_pad;                 // h pieces + group sums per slot
     L.res_off = L.hp_off + kFzMaxSlots * (d.pieces + d.sums);       // [slot][block][row] partials
@@ -657,21 +689,67 @@ __host__ __device__ inline FusedLds fused_lds(int64_t T, int64_t F, int32_t qtyp
     return L;
 }
 
-// The activations of the T tokens as pieces in LDS: thread tid converts
-// values 4*tid .. 4*tid+3 of every token (hi/mid slots, lo piece, group sums).
+// The activations of the T tokens as int8 pieces in LDS (layout at
+// kI8PieceBytes): thread tid converts values 4*tid .. 4*tid+3 of every token;
+// 8 consecutive threads hold one 32-value group, 4 one 16-value half.  A
+// group whose maximum is not finite gets a NaN scale, so it poisons the rows
+// that read it as the plain products would.
+__device__ __forceinline__ uint32_t pack_i8x4(float a, float b, float c, float d) {
+    return ((uint32_t)(int)a & 0xffu) | (((uint32_t)(int)b & 0xffu) << 8) |
+           (((uint32_t)(int)c & 0xffu) << 16) | ((uint32_t)(int)d << 24);
+}
+
 template <int MT>
 __device__ __forceinline__ void build_x_pieces(const float4 (&xv)[MT], int64_t T, uint8_t* smem,
-                                               int xp_bytes, int tid) {
+                                               int tid) {
+    const int v0 = 4 * tid, bl = v0 >> 8, w = v0 & 255, j = w >> 5;
+    const int lane = bl * 8 + (j >> 1) * 2 + ((w >> 4) & 1), half = j & 1;
+    const int off = half * (kWave * 16) + lane * 16 + (w & 15);
 #pragma unroll
-    for (int j = 0; j < MT; ++j) {
-        if (j < T) {                                           // whole workgroup in or out
-            uint8_t* xp = smem + j * xp_bytes;
-            const Pieces4x3 pc = make_pieces4x3(xv[j]);
-            *reinterpret_cast<uint4*>(xp + piece_slot_off(tid)) = pc.slot;
-            *reinterpret_cast<uint2*>(xp + kFzNB * kBlockPieceStride + kFzNB * 16 * 4 + piece_lo_off(tid)) = pc.lo;
-            float g = pc.sum + __shfl_xor(pc.sum, 1, kWave);
+    for (int t = 0; t < MT; ++t) {
+        if (t < T) {                                           // whole workgroup in or out
+            uint8_t* xt = smem + t * kI8TokenBytes;
+            const float4 v = xv[t];
+            float m = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+            // 1 where a value is NaN or infinite (fmaxf would drop a NaN)
+            float bad = (fabsf(v.x) <= 3.4028235e38f && fabsf(v.y) <= 3.4028235e38f &&
+                         fabsf(v.z) <= 3.4028235e38f && fabsf(v.w) <= 3.4028235e38f) ? 0.f : 1.f;
+#pragma unroll
+            for (int sh = 1; sh < 8; sh <<= 1) {
+                m = fmaxf(m, __shfl_xor(m, sh, kWave));
+                bad = fmaxf(bad, __shfl_xor(bad, sh, kWave));
+            }
+            const bool finite = bad == 0.f;
+            // s = 2^e with m / s in [63.75, 127.5): e from the exponent of m
+            int e = finite && m > 0.f ? __builtin_amdgcn_frexp_expf(m) - 7 : 0;
+            if (ldexpf(m, -e) >= 127.5f) ++e;
+            const float vv[4] = {v.x, v.y, v.z, v.w};
+            float p1[4], p2[4], p3[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float q = ldexpf(vv[i], -e);
+                p1[i] = finite ? rintf(q) : 0.f;
+                const float r1 = (q - p1[i]) * 128.f;
+                p2[i] = finite ? rintf(r1) : 0.f;
+                const float r2 = (r1 - p2[i]) * 128.f;
+                p3[i] = finite ? rintf(r2) : 0.f;
+            }
+            *reinterpret_cast<uint32_t*>(xt + off) = pack_i8x4(p1[0], p1[1], p1[2], p1[3]);
+            *reinterpret_cast<uint32_t*>(xt + kI8PieceBytes + off) = pack_i8x4(p2[0], p2[1], p2[2], p2[3]);
+            *reinterpret_cast<uint32_t*>(xt + 2 * kI8PieceBytes + off) = pack_i8x4(p3[0], p3[1], p3[2], p3[3]);
+            float g = (v.x + v.y) + (v.z + v.w);
+            g += __shfl_xor(g, 1, kWave);
             g += __shfl_xor(g, 2, kWave);
-            if ((tid & 3) == 0) reinterpret_cast<float*>(xp + kFzNB * kBlockPieceStride)[tid >> 2] = g;
+            if ((tid & 3) == 0)
+                reinterpret_cast<float*>(xt + kI8SumOff)[half * kWave + lane] = g;
+            if ((tid & 7) == 0)
+                reinterpret_cast<float*>(xt + kI8ScaleOff)[bl * 8 + j] =
+                    finite ? ldexpf(1.f, e - 14) : __builtin_nanf("");
+        } else {
+            // consume the (clamped) load anyway, so that every path has
+            // waited for it and its registers can be reused without a
+            // conservative wait for all later loads
+            asm volatile("" ::"v"(xv[t].x), "v"(xv[t].y), "v"(xv[t].z), "v"(xv[t].w));
         }
     }
 }
@@ -693,7 +771,9 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
     using G = GuTask<kFzNB>;
     constexpr int kThr = kFzWaves * kWave;
     extern __shared__ __align__(16) uint8_t smem[];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // the wave index as a scalar, so that the gate/up and down branches are
+    // uniform and each keeps exact counts of its own outstanding loads
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int grid = (int)gridDim.x, wg = (int)blockIdx.x;
     const FusedLds L = fused_lds(T, F, dqtype);
     const DnGeom dg(F, dqtype);
@@ -701,11 +781,11 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
     float* res = reinterpret_cast<float*>(smem + L.res_off);
     int32_t* gu_ctr = reinterpret_cast<int32_t*>(smem + L.ctr_off);
 
-    const int64_t tiles = F / G::R;
-    const int64_t n_gu = T * k * tiles;
+    const int tiles = (int)(F / G::R);                      // T*k*tiles < 2^31 (T <= 4, k <= 8)
+    const int n_gu = (int)T * k * tiles;
     const int64_t row_units = G::H / kDnRows;
     const int64_t n_dn = T * row_units;
-    const int64_t gu_step = (int64_t)grid * kFzGu;
+    const int gu_step = grid * kFzGu;
     const bool is_gu = wave < kFzGu;
 
     // ---- (1) routing; each gate/up wave requests its first task's weights;
@@ -722,42 +802,40 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
         xv[j] = reinterpret_cast<const float4*>(hidden + (j < T ? j : T - 1) * G::H)[tid];
     if (tid == 0) gu_ctr[0] = 0;
 
-    int64_t tau = (int64_t)wg * kFzGu + wave;
-    int64_t p = (tau < n_gu ? tau : 0) / tiles, r0 = ((tau < n_gu ? tau : 0) % tiles) * G::R;
+    int tau = wg * kFzGu + wave;
+    int p = (tau < n_gu ? tau : 0) / tiles, r0 = ((tau < n_gu ? tau : 0) % tiles) * G::R;
     GuRows rows;
     if (is_gu) {
         gu_rows_load(rows, lane_value(my_idx, (int)p), E, gbase, gstride, ubase, ustride, r0, lane);
         __builtin_amdgcn_sched_barrier(0);
-        build_x_pieces<kFzMaxTokens>(xv, T, smem, L.xp_bytes, tid);
+        build_x_pieces<kFzMaxTokens>(xv, T, smem, tid);
         // keeps the two builds apart: merged after the branch, the stores
         // would wait for the weight requests as well
         __builtin_amdgcn_sched_barrier(0);
     } else {
-        build_x_pieces<kFzMaxTokens>(xv, T, smem, L.xp_bytes, tid);
+        build_x_pieces<kFzMaxTokens>(xv, T, smem, tid);
     }
     __syncthreads();                          // no direct-to-LDS load is in flight yet
 
     int64_t unit = wg;
     if (is_gu) {
         // gate/up tasks: the first task's weights are on their way; read the
-        // token's pieces, compute, and request the next task's weights
-        int64_t xc = -1;                      // token whose pieces x holds
-        XCols x;
-        while (tau < n_gu) {
-            const int64_t t = p / k;
-            if (t != xc) {
-                const uint8_t* xp = smem + t * L.xp_bytes;
-                x = load_xcols(xp, reinterpret_cast<const float*>(xp + kFzNB * kBlockPieceStride),
-                               xp + kFzNB * kBlockPieceStride + kFzNB * 16 * 4, lane);
-                xc = t;
-            }
-            const int64_t pv = p * F + r0;
-            gu_rows_finish(rows, x, lane, hpieces, pv);
-            tau += gu_step;
-            if (tau < n_gu) {
+        // token's pieces and compute it (outside the loop, so the waits for
+        // its rows are counted exactly), then load and compute the rest
+        if (tau < n_gu) {
+            int xc = p / k;                   // token whose pieces x holds
+            XCols x = load_xcols(smem + xc * kI8TokenBytes, lane);
+            gu_rows_finish(rows, x, lane, hpieces, (int64_t)p * F + r0);
+            for (tau += gu_step; tau < n_gu; tau += gu_step) {
                 p = tau / tiles;
                 r0 = (tau % tiles) * G::R;
-                gu_rows_load(rows, lane_value(my_idx, (int)p), E, gbase, gstride, ubase, ustride, r0, lane);
+                gu_rows_load(rows, lane_value(my_idx, p), E, gbase, gstride, ubase, ustride, r0, lane);
+                const int t = p / k;
+                if (t != xc) {
+                    x = load_xcols(smem + t * kI8TokenBytes, lane);
+                    xc = t;
+                }
+                gu_rows_finish(rows, x, lane, hpieces, (int64_t)p * F + r0);
             }
         }
         wait_all_loads();                     // this wave's h stores have completed
@@ -773,7 +851,14 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (unit < n_dn) wait_all_gate_up(sync, grid, status, lane);
         }
-    } else if (unit < n_dn) {
+    }
+    // A separate branch after the gate/up one, on a condition the compiler
+    // cannot relate to is_gu: merged into an else, the direct-to-LDS loads
+    // issued here would appear pending on the gate/up path and cost its
+    // weight waits their exact counts.
+    int dn_wave = __builtin_amdgcn_readfirstlane(is_gu ? 0 : 1);
+    asm volatile("" : "+s"(dn_wave));
+    if (dn_wave && unit < n_dn) {
         // down waves: request the first unit's tiles for all slots (after the
         // barrier, so behind every gate/up request of the workgroup)
         const int dw = wave - kFzGu;
