@@ -147,8 +147,9 @@ size_t down_lds(int64_t F, int32_t qtype) {
 size_t expert_ffn_workspace_bytes(int64_t T, int64_t H, int64_t F, int32_t E, int32_t k) {
     const int64_t t = T > 0 ? T : 0;
     if (t >= kPrefillMinTokens) return prefill_workspace_bytes(t, H, F, E, k);
-    // synchronisation words, then h (f32 or activation pieces, 4 bytes/value)
-    const size_t h = (size_t)t * (size_t)k * (size_t)F * sizeof(float);
+    // synchronisation words, then h: 8 bytes per value (the fused decode
+    // kernel's tagged words; the other decode kernels use 4)
+    const size_t h = (size_t)t * (size_t)k * (size_t)F * sizeof(uint64_t);
     return kFfnSyncBytes + ((h + 255) & ~(size_t)255);
 }
 

@@ -335,7 +335,20 @@ __device__ __forceinline__ float q4k_cols_row(uint4 hdr, uint4 qv, const XCols& 
     return d * (sc0 * ((float)A * x.sa) + sc1 * ((float)B * x.sb)) - dmin * (mn0 * x.slo + mn1 * x.shi);
 }
 
-// Sum v[0..7] over the 64 lanes; returns row (lane >> 3)'s total.
+// A float moved across lanes by a DPP pattern within rows of 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppXor1 = 0xb1;          // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4e;          // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;   // lane i <-> 7 - i within each 8 lanes
+constexpr int kDppRor8 = 0x128;         // row_ror:8, i.e. lane i <-> i ^ 8 within a row
+
+// Sum v[0..7] over the 64 lanes; returns row (lane >> 3)'s total.  A
+// transposed butterfly: each exchange halves the values a lane carries
+// (xor 32 and 16 across rows through the LDS crossbar, xor 8 by DPP), then
+// the 8 lanes of a row group add their values with three DPP steps.
 __device__ __forceinline__ float fold8_rows(const float v[8], int lane) {
     const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8;
     float a[4], c[2];
@@ -352,10 +365,10 @@ __device__ __forceinline__ float fold8_rows(const float v[8], int lane) {
         c[i] = keep + __shfl_xor(send, 16, kWave);
     }
     const float send = b3 ? c[0] : c[1];
-    float r = (b3 ? c[1] : c[0]) + __shfl_xor(send, 8, kWave);
-    r += __shfl_xor(r, 4, kWave);
-    r += __shfl_xor(r, 2, kWave);
-    r += __shfl_xor(r, 1, kWave);
+    float r = (b3 ? c[1] : c[0]) + dpp_f32<kDppRor8>(send);
+    r += dpp_f32<kDppXor1>(r);
+    r += dpp_f32<kDppXor2>(r);
+    r += dpp_f32<kDppHalfMirror>(r);
     return r;
 }
 
@@ -590,14 +603,16 @@ __device__ __forceinline__ void gu_rows_load(GuRows& g, int e, int32_t E,
     }
 }
 
-// h = silu(gate) * up of the task's 4 rows, stored as one piece slot at
-// value index value_base (a multiple of 4) with device-scope stores.
+// h = silu(gate) * up of the task's 4 rows, published as tagged words: the
+// f32 value in the low half and this call's tag in the high half of one
+// 64-bit device-scope store, so a reader that sees the tag sees the value.
 __device__ __forceinline__ void gu_rows_finish(const GuRows& g, const XCols& x, int lane,
-                                               uint8_t* __restrict__ hpieces, int64_t value_base) {
+                                               uint64_t* __restrict__ hbuf, int64_t value_base,
+                                               uint32_t tag) {
     // rows in load order, each fenced off so that it waits only for its own
     // loads (they complete in order).  A pair whose expert is out of range
-    // computes on expert 0's rows; its h is never read (the down stage and
-    // the combine skip that slot).
+    // computes on expert 0's rows; its h is never read (the down stage skips
+    // that slot).
     float v[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -607,32 +622,32 @@ __device__ __forceinline__ void gu_rows_finish(const GuRows& g, const XCols& x, 
     const float r = fold8_rows(v, lane);               // lanes 8q..: row q
     const float up = __shfl_xor(r, 32, kWave);          // lane 8q (q < 4) gets up row q
     const float h = silu_f(r) * up;
-    const float h1 = __shfl(h, 8, kWave), h2 = __shfl(h, 16, kWave), h3 = __shfl(h, 24, kWave);
-    if (lane == 0) store_h_slot(hpieces, value_base, make_pieces4(make_float4(h, h1, h2, h3)).slot);
+    if (lane < 32 && (lane & 7) == 0)
+        __hip_atomic_store(hbuf + value_base + (lane >> 3),
+                           ((uint64_t)tag << 32) | __float_as_uint(h), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------ fused path --
 //
 // One persistent kernel for the whole expert FFN of a few tokens at H = 2048.
 // Each workgroup (one per CU) has 8 waves: 6 compute gate/up tasks from
-// registers, 2 request the workgroup's down tiles into LDS at once, so the
-// down weights stream while gate/up computes; all 8 then share the down
-// projection of the workgroup's output rows.
+// registers, 2 request the workgroup's down tiles (8 output rows of every
+// selected expert) into LDS, so the down weights stream while gate/up
+// computes; all 8 then share the down projection of those rows.
 //
-// Hand-off of h between workgroups: gate/up waves store h pieces with
-// device-scope (write-through) stores and wait for them to complete; each
-// then counts itself on an LDS counter, and the last of the workgroup adds 1
-// to one of 16 global counters, each in its own 128-byte line (workgroup g
-// uses stripe g % 16).  One down wave per workgroup polls the 16 stripes
-// with device-scope loads until every stripe has counted all of its
-// workgroups; then all waves read the slots' h pieces with device-scope
-// loads.  No L2 write-back or invalidate is needed because every access that
-// crosses CUs is coherent at device scope.  Every s_barrier is reached by all
-// waves of the workgroup.  Exit: each workgroup counts itself on its stripe
-// of a second counter set; the workgroup that completes a stripe counts on a
-// top counter, and the one that completes the top counter zeroes everything
-// for the next call.  All waits are bounded: one that runs out sets the
-// status word instead of hanging.
+// Hand-off of h between workgroups without counters: every h value is
+// published as one 64-bit word, its f32 bits beside a tag that identifies
+// this call (derived from an epoch counter in the workspace).  A down thread
+// keeps re-reading the 16 words it needs, with device-scope loads, until all
+// carry this call's tag, so the data itself is the signal and no write has
+// to be acknowledged before another can be issued.  While they wait, the
+// down threads have already turned their share of the down tiles into f32
+// weights in registers, so what remains after h arrives is 16 FMAs per row
+// and the cross-lane sum.  Exit: each workgroup counts itself on a stripe of
+// exit counters; the workgroup that completes the count advances the epoch
+// and zeroes the counters for the next call.  Every wait is bounded: one that
+// runs out sets the status word instead of hanging.
 constexpr int kFzGu = 6;
 constexpr int kFzDn = 2;
 constexpr int kFzWaves = kFzGu + kFzDn;
@@ -642,8 +657,8 @@ constexpr int kStripes = 16;
 constexpr int kLineInts = 32;                          // 128-byte spacing of counters
 // int32 offsets inside the workspace's synchronisation header
 constexpr int kSyncStatus = 0;
-constexpr int kSyncGuDone = 64;                        // + kLineInts * stripe
-constexpr int kSyncExit = kSyncGuDone + kStripes * kLineInts;
+constexpr int kSyncEpoch = 32;                         // calls completed on this workspace
+constexpr int kSyncExit = 64;                          // + kLineInts * stripe
 constexpr int kSyncExitTop = kSyncExit + kStripes * kLineInts;
 static_assert((kSyncExitTop + 1) * 4 <= (int)kFfnSyncBytes, "sync header too small");
 
@@ -651,30 +666,21 @@ __device__ __forceinline__ int stripe_members(int stripe, int grid) {
     return grid / kStripes + (stripe < grid % kStripes ? 1 : 0);
 }
 
-// Poll the gate/up completion stripes until all `grid` workgroups counted.
-__device__ __forceinline__ bool wait_all_gate_up(const int32_t* sync, int grid, int32_t* status,
-                                                 int lane) {
-    const bool mine = lane < kStripes;
-    const int need = mine ? stripe_members(lane, grid) : 0;
-    const int32_t* ctr = sync + kSyncGuDone + (mine ? lane : 0) * kLineInts;
-    int spins = 0;
-    while (true) {
-        const int v = mine ? __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
-        if (__all(v >= need)) return true;
-        __builtin_amdgcn_s_sleep(2);
-        if (++spins > kSpinLimit) {
-            if (lane == 0) __hip_atomic_fetch_or(status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            return false;
-        }
-    }
+// The tag of the call that runs with epoch counter value `epoch`: odd, so it
+// never equals the zero high half of a cleared workspace, and different for
+// consecutive calls; the constant keeps it unlike small integers left in
+// memory by other uses.
+__device__ __forceinline__ uint32_t h_tag(uint32_t epoch) {
+    return (2u * epoch + 1u) ^ 0x6a09e666u;
 }
 
 constexpr int kFzMaxSlots = 8;                        // the fused path serves k <= 8
 constexpr int kFzMaxTokens = 4;                        // and T <= 4 (T*k routing entries <= 32)
+constexpr int kDnGroup = 16;                           // columns per down thread unit
 static_assert(kFzWaves * kWave * 4 == kFzNB * kQK, "one float4 of activations per thread and token");
 
 struct FusedLds {
-    int xp_bytes, dn_off, hp_off, res_off, ctr_off, total;
+    int xp_bytes, dn_off, h_off, res_off, total;
 };
 
 __host__ __device__ inline FusedLds fused_lds(int64_t T, int64_t F, int32_t qtype) {
@@ -682,11 +688,93 @@ __host__ __device__ inline FusedLds fused_lds(int64_t T, int64_t F, int32_t qtyp
     FusedLds L;
     L.xp_bytes = kI8TokenBytes;                                     // int8 pieces, scales, sums per token
     L.dn_off = (int)T * L.xp_bytes;                                 // down tiles, one per slot
-    L.hp_off = L.dn_off + kFzMaxSlots * d.tile_pad;                 // h pieces + group sums per slot
-    L.res_off = L.hp_off + kFzMaxSlots * (d.pieces + d.sums);       // [slot][block][row] partials
-    L.ctr_off = L.res_off + kFzMaxSlots * d.nb * kDnRows * 4;       // gate/up waves done
-    L.total = L.ctr_off + 16;
+    L.h_off = L.dn_off + kFzMaxSlots * d.tile_pad;                  // h of the unit's token, f32 [slot][F]
+    L.res_off = L.h_off + kFzMaxSlots * (int)F * 4;                 // [wave][row] partial sums
+    L.total = L.res_off + kFzWaves * kDnRows * 4;
     return L;
+}
+
+// Down-stage unit of a thread: 16 consecutive columns (one Q6_K scale group,
+// half a Q4_K sub-block) of one slot's tile, for all 8 rows.  Their weights
+// a * q + b (exact products rounded once to f32) come out of the raw tile in
+// LDS into w[row][i].
+__device__ __forceinline__ void dn_unit_weights(const uint8_t* tile, const DnGeom& g, int grp,
+                                                float (&w)[kDnRows][kDnGroup]) {
+    const int b = grp / (kQK / kDnGroup), j = grp % (kQK / kDnGroup);
+#pragma unroll
+    for (int rho = 0; rho < kDnRows; ++rho) {
+        const int boff = rho * g.rowb + b * g.bb;
+        uint32_t q[4];
+        float a, c;
+        if (g.q6) {
+            // group j: weights 16j..16j+15 with scale j; low four bits in nibble
+            // r/2 of ql bytes 64n + 32(r%2) + 16lh + i, top two bits at 2r of
+            // qh byte 32n + 16lh + i (n = j/8, r = (j/2)%4, lh = j%2)
+            const int n = j >> 3, r = (j >> 1) & 3, lh = j & 1;
+            const uint4 ql = lds_read16_a2(tile, boff + 64 * n + 32 * (r & 1) + 16 * lh);
+            const uint4 qh = lds_read16_a2(tile, boff + 128 + 32 * n + 16 * lh);
+            const uint32_t l4[4] = {ql.x, ql.y, ql.z, ql.w}, h4[4] = {qh.x, qh.y, qh.z, qh.w};
+            const int ls = 4 * (r >> 1), hs = 2 * r;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                q[i] = ((l4[i] >> ls) & 0x0f0f0f0fu) | (((h4[i] >> hs) & 0x03030303u) << 4);
+            const float d = half_bits_to_float(tile[boff + 208] | (tile[boff + 209] << 8));
+            a = d * (float)(int8_t)tile[boff + 192 + j];
+            c = -32.f * a;
+        } else {
+            // half j%2 of sub-block j/2: nibble (j/2)%2 of qs bytes 32(j/4) + 16(j%2) + i
+            const int sb = j >> 1;
+            const uint4 hdr = *reinterpret_cast<const uint4*>(tile + boff);
+            const uint4 qs = *reinterpret_cast<const uint4*>(tile + boff + 16 + 32 * (sb >> 1) + 16 * (j & 1));
+            const uint32_t q4[4] = {qs.x, qs.y, qs.z, qs.w};
+            const int sh = 4 * (sb & 1);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) q[i] = (q4[i] >> sh) & 0x0f0f0f0fu;
+            int sc, mn;
+            q4k_sm_var(hdr.y, hdr.z, hdr.w, sb, sc, mn);
+            a = half_bits_to_float(hdr.x & 0xffffu) * (float)sc;
+            c = -half_bits_to_float(hdr.x >> 16) * (float)mn;
+        }
+#pragma unroll
+        for (int i = 0; i < kDnGroup; ++i)
+            w[rho][i] = fmaf(a, (float)((q[i >> 2] >> (8 * (i & 3))) & 0xffu), c);
+    }
+}
+
+// All n h words of one token (its k slots, contiguous from src) into LDS as
+// f32, once each carries `tag`.  Thread tid reads words tid + i * kThr with
+// device-scope 64-bit loads, so each load instruction of a wave covers 512
+// consecutive bytes; a wave re-reads its words until all of them carry the
+// tag.  A wait that runs out sets bit 1 of the status word.
+constexpr int kPollWords = 12;                         // words per thread and round
+template <int kThr>
+__device__ __forceinline__ void dn_wait_h(const uint64_t* src, int n, uint32_t tag, float* hl,
+                                          int tid, int32_t* status) {
+    for (int c0 = 0; c0 < n; c0 += kThr * kPollWords) {
+        uint64_t v[kPollWords];
+        int spins = 0;
+        while (true) {
+            bool ok = true;
+#pragma unroll
+            for (int i = 0; i < kPollWords; ++i) {
+                const int wi = c0 + tid + i * kThr;
+                v[i] = __hip_atomic_load(src + (wi < n ? wi : n - 1), __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+                ok = ok && (wi >= n || (uint32_t)(v[i] >> 32) == tag);
+            }
+            if (__all(ok)) break;
+            if (++spins > kSpinLimit) {
+                if (!ok) __hip_atomic_fetch_or(status, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+#pragma unroll
+        for (int i = 0; i < kPollWords; ++i) {
+            const int wi = c0 + tid + i * kThr;
+            if (wi < n) hl[wi] = __uint_as_float((uint32_t)v[i]);
+        }
+    }
 }
 
 // The activations of the T tokens as int8 pieces in LDS (layout at
@@ -766,7 +854,7 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
     const int32_t* __restrict__ idx, const float* __restrict__ w,
     const uint8_t* __restrict__ gbase, int64_t gstride, const uint8_t* __restrict__ ubase,
     int64_t ustride, const uint8_t* __restrict__ dbase, int32_t dqtype, int64_t dstride,
-    float* __restrict__ out, int accumulate, uint8_t* __restrict__ hpieces,
+    float* __restrict__ out, int accumulate, uint64_t* __restrict__ hbuf,
     int32_t* __restrict__ sync) {
     using G = GuTask<kFzNB>;
     constexpr int kThr = kFzWaves * kWave;
@@ -779,7 +867,6 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
     const DnGeom dg(F, dqtype);
     int32_t* status = sync + kSyncStatus;
     float* res = reinterpret_cast<float*>(smem + L.res_off);
-    int32_t* gu_ctr = reinterpret_cast<int32_t*>(smem + L.ctr_off);
 
     const int tiles = (int)(F / G::R);                      // T*k*tiles < 2^31 (T <= 4, k <= 8)
     const int n_gu = (int)T * k * tiles;
@@ -796,11 +883,15 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
     const int nr = (int)(T * k);
     const int my_idx = lane < nr ? idx[lane] : -1;
     const float my_w = lane < nr ? w[lane] : 0.f;
+    // this call's epoch: every workgroup reads it here, and only the last
+    // workgroup to finish advances it
+    const uint32_t epoch = (uint32_t)__hip_atomic_load(sync + kSyncEpoch, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t tag = h_tag(epoch);
     float4 xv[kFzMaxTokens];
 #pragma unroll
     for (int j = 0; j < kFzMaxTokens; ++j)
         xv[j] = reinterpret_cast<const float4*>(hidden + (j < T ? j : T - 1) * G::H)[tid];
-    if (tid == 0) gu_ctr[0] = 0;
 
     int tau = wg * kFzGu + wave;
     int p = (tau < n_gu ? tau : 0) / tiles, r0 = ((tau < n_gu ? tau : 0) % tiles) * G::R;
@@ -825,7 +916,7 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
         if (tau < n_gu) {
             int xc = p / k;                   // token whose pieces x holds
             XCols x = load_xcols(smem + xc * kI8TokenBytes, lane);
-            gu_rows_finish(rows, x, lane, hpieces, (int64_t)p * F + r0);
+            gu_rows_finish(rows, x, lane, hbuf, (int64_t)p * F + r0, tag);
             for (tau += gu_step; tau < n_gu; tau += gu_step) {
                 p = tau / tiles;
                 r0 = (tau % tiles) * G::R;
@@ -835,21 +926,8 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
                     x = load_xcols(smem + t * kI8TokenBytes, lane);
                     xc = t;
                 }
-                gu_rows_finish(rows, x, lane, hpieces, (int64_t)p * F + r0);
+                gu_rows_finish(rows, x, lane, hbuf, (int64_t)p * F + r0, tag);
             }
-        }
-        wait_all_loads();                     // this wave's h stores have completed
-        int before = 0;
-        if (lane == 0)
-            before = __hip_atomic_fetch_add(gu_ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        before = __builtin_amdgcn_readfirstlane(before);
-        if (before == kFzGu - 1) {
-            // the workgroup's last gate/up wave signals, then (having no
-            // request of its own in flight) polls for every workgroup's h
-            if (lane == 0)
-                __hip_atomic_fetch_add(sync + kSyncGuDone + (wg % kStripes) * kLineInts, 1,
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (unit < n_dn) wait_all_gate_up(sync, grid, status, lane);
         }
     }
     // A separate branch after the gate/up one, on a condition the compiler
@@ -868,14 +946,14 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
             if (e >= 0 && e < E)
                 dn_issue_weights(smem + L.dn_off + s * dg.tile_pad, dg, dbase, dstride, e, r0d, lane);
         }
+        wait_all_loads();                     // the tiles are in LDS
     }
 
-    // ---- (2) every wave waits until the poller has seen all h
-    __syncthreads();
-
-    // ---- (3) down projection and combine, all waves
-    const int ih = lane >> 5, rho = (lane >> 2) & 7, u = lane & 3;
-    const int items = k * dg.nb;
+    // ---- (2) down projection and combine, all waves.  Thread unit u =
+    // (slot u / G, column group u % G) for the 8 rows of the workgroup's
+    // output unit.
+    const int groups = (int)(F / kDnGroup);
+    const int n_units = k * groups;
     for (int j = 0; unit < n_dn; unit += grid, ++j) {
         const int64_t t = unit / row_units, r0 = (unit % row_units) * kDnRows;
         if (j > 0) {
@@ -884,72 +962,57 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
                 if (e >= 0 && e < E)
                     dn_issue_weights(smem + L.dn_off + s * dg.tile_pad, dg, dbase, dstride, e, r0, lane);
             }
+            wait_all_loads();
         }
-        for (int q = wave; q < items; q += kFzWaves) {        // one 1 KiB piece block per step
-            const int s = q / dg.nb, b = q % dg.nb;
-            const int e = lane_value(my_idx, (int)(t * k + s));
-            if (e >= 0 && e < E)
-                wave_copy_to_lds_coherent(smem + L.hp_off + s * (dg.pieces + dg.sums) + b * kBlockPieceStride,
-                                          hpieces + ((t * k + s) * F + b * kQK) * 4, 1024, lane);
-        }
-        wait_all_loads();
-        __syncthreads();
-        for (int gi = tid; gi < k * dg.nb * 16; gi += kThr) {  // group sums of the h pieces
-            const int s = gi / (dg.nb * 16), g = gi % (dg.nb * 16);
-            const uint8_t* xs = smem + L.hp_off + s * (dg.pieces + dg.sums);
-            float v = 0.f;
+        __syncthreads();                      // this unit's tiles are in LDS
+        float acc[kDnRows];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                v += slot_sum(*reinterpret_cast<const uint4*>(xs + piece_slot_off(4 * g + i)));
-            reinterpret_cast<float*>(smem + L.hp_off + s * (dg.pieces + dg.sums) + dg.pieces)[g] = v;
-        }
-        __syncthreads();
-        for (int it = 2 * wave; it < items; it += 2 * kFzWaves) {
-            const int item = it + ih;
-            const int sa = it / dg.nb, sb = (it + 1 < items ? it + 1 : it) / dg.nb;
-            const int ea = lane_value(my_idx, (int)(t * k + sa));
-            const int eb = lane_value(my_idx, (int)(t * k + sb));
-            const int s = ih ? sb : sa, b = item % dg.nb;
-            const int e = ih ? eb : ea;
-            const bool valid = item < items && e >= 0 && e < E;
-            float y = 0.f;
-            if (valid) {
-                const uint8_t* tile = smem + L.dn_off + s * dg.tile_pad;
-                const uint8_t* xs = smem + L.hp_off + s * (dg.pieces + dg.sums);
-                const float* gs = reinterpret_cast<const float*>(xs + dg.pieces) + b * 16;
-                const int boff = rho * dg.rowb + b * dg.bb;
-                y = dg.q6 ? q6k_lane_dot(tile, boff, u >> 1, u & 1, xs + b * kBlockPieceStride, gs)
-                          : q4k_lane_dot(tile + boff, u, xs + b * kBlockPieceStride, gs);
+        for (int rho = 0; rho < kDnRows; ++rho) acc[rho] = 0.f;
+        float* hl = reinterpret_cast<float*>(smem + L.h_off);
+        const int iters = (n_units + kThr - 1) / kThr;   // the same for every wave
+        for (int it = 0; it < iters; ++it) {
+            const int u = tid + it * kThr;
+            const bool active = u < n_units;
+            const int uc = active ? u : 0;
+            const int s = uc / groups, grp = uc % groups;
+            const int e = __shfl(my_idx, (int)(t * k) + s, kWave);
+            const float ws = __shfl(my_w, (int)(t * k) + s, kWave);
+            const bool valid = active && e >= 0 && e < E;
+            float wt[kDnRows][kDnGroup];
+            dn_unit_weights(smem + L.dn_off + s * dg.tile_pad, dg, grp, wt);
+            if (it == 0) {
+                // the token's h: every slot's F values, published by gate/up
+                // waves anywhere on the device
+                dn_wait_h<kThr>(hbuf + t * k * F, k * (int)F, tag, hl, tid, status);
+                __syncthreads();
             }
-            y += __shfl_xor(y, 1, kWave);
-            y += __shfl_xor(y, 2, kWave);
-            if (item < items && u == 0) res[(s * dg.nb + b) * kDnRows + rho] = y;
-        }
-        __syncthreads();
-        if (wave == 0) {                      // lane = slot * 8 + row; fixed-order tree over slots
-            const int s = lane >> 3, row = lane & 7;
-            const int src = (int)(t * k) + (s < k ? s : 0);
-            const int e = __shfl(my_idx, src, kWave);
-            const float ws = __shfl(my_w, src, kWave);
-            float acc = 0.f;
-            if (s < k && e >= 0 && e < E) {
-                float ys = 0.f;
-                for (int b = 0; b < dg.nb; ++b) ys += res[(s * dg.nb + b) * kDnRows + row];
-                acc = ws * ys;
+            float hv[kDnGroup];
+#pragma unroll
+            for (int i = 0; i < kDnGroup; i += 4) {
+                const float4 h4 = *reinterpret_cast<const float4*>(hl + s * F + grp * kDnGroup + i);
+                hv[i] = h4.x; hv[i + 1] = h4.y; hv[i + 2] = h4.z; hv[i + 3] = h4.w;
             }
-            acc += __shfl_xor(acc, 8, kWave);
-            acc += __shfl_xor(acc, 16, kWave);
-            acc += __shfl_xor(acc, 32, kWave);
-            if (lane < kDnRows) {
-                float* o = out + t * G::H + r0 + lane;
-                *o = accumulate ? *o + acc : acc;
+#pragma unroll
+            for (int rho = 0; rho < kDnRows; ++rho) {
+                float y = 0.f;
+#pragma unroll
+                for (int i = 0; i < kDnGroup; ++i) y = fmaf(wt[rho][i], hv[i], y);
+                acc[rho] += valid ? ws * y : 0.f;
             }
         }
+        const float r = fold8_rows(acc, lane);            // lanes 8q..: row q of this wave
+        if ((lane & 7) == 0) res[wave * kDnRows + (lane >> 3)] = r;
         __syncthreads();
+        if (wave == 0 && lane < kDnRows) {                // fixed order over the waves
+            float o = 0.f;
+#pragma unroll
+            for (int wv = 0; wv < kFzWaves; ++wv) o += res[wv * kDnRows + lane];
+            float* dst = out + t * G::H + r0 + lane;
+            *dst = accumulate ? *dst + o : o;
+        }
     }
 
-    // ---- exit: the last workgroup zeroes the counters for the next call
-    wait_all_loads();                         // this thread's counter atomics have completed
+    // ---- exit: the last workgroup advances the epoch and zeroes the counters
     if (tid == 0) {
         const int st = wg % kStripes;
         const int32_t done = __hip_atomic_fetch_add(sync + kSyncExit + st * kLineInts, 1,
@@ -959,13 +1022,12 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
             const int32_t top = __hip_atomic_fetch_add(sync + kSyncExitTop, 1, __ATOMIC_RELAXED,
                                                        __HIP_MEMORY_SCOPE_AGENT);
             if (top == used - 1) {                            // every workgroup has finished
-                for (int i = 0; i < kStripes; ++i) {
-                    __hip_atomic_store(sync + kSyncGuDone + i * kLineInts, 0, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
+                for (int i = 0; i < kStripes; ++i)
                     __hip_atomic_store(sync + kSyncExit + i * kLineInts, 0, __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT);
-                }
                 __hip_atomic_store(sync + kSyncExitTop, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(sync + kSyncEpoch, (int32_t)(epoch + 1u), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
             }
         }
     }
@@ -1040,8 +1102,8 @@ hipError_t launch_fused8(const float* hidden, int64_t T, int64_t F, int32_t E, i
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(ffn_fused8_kernel, dim3((unsigned)grid), dim3(kFzWaves * kWave),
                        (size_t)L.total, stream, hidden, T, F, E, k, idx, w, gate.base, gate.stride,
-                       up.base, up.stride, down.base, down.qtype, down.stride, out, accumulate, hp,
-                       sync);
+                       up.base, up.stride, down.base, down.qtype, down.stride, out, accumulate,
+                       reinterpret_cast<uint64_t*>(hp), sync);
     return hipGetLastError();
 }
 
