@@ -137,7 +137,8 @@ q3moe_status q3moe_group_by_expert(const int32_t *topk_idx, int64_t T, int32_t t
  *   g = Wg[e] x_t, u = Wu[e] x_t         (F values each; gate/up are F x H)
  *   h = silu(g) * u, silu(z) = z / (1 + exp(-z))
  *   y = Wd[e] h                          (H values; down is H x F)
- *   out[t] = [out[t] +] sum over s in slot order of topk_w[t*k+s] * y
+ *   out[t] = [out[t] +] sum over s of topk_w[t*k+s] * y
+ *            (summed in a fixed order, so results are deterministic)
  *   hidden   [T x H] f32, 16-byte aligned (the FFN input)
  *   topk_idx [T x k] int32, each in [0, E); an index outside that range
  *            makes that slot contribute zero (caller error, not reported)
@@ -151,18 +152,19 @@ q3moe_status q3moe_group_by_expert(const int32_t *topk_idx, int64_t T, int32_t t
  * Limits: H % 256 == 0, F % 256 == 0, 256 <= H <= 4096, 256 <= F <= 1536,
  * 1 <= k <= 32, k <= E.
  * workspace: at least q3moe_expert_ffn_workspace_bytes(T, H, F, E, k)
- * bytes, 16-byte aligned.  Its first 8 KiB hold synchronisation words
- * and must be zero before the first call that uses the workspace (e.g. one
- * hipMemset after allocation); every call leaves its counters at zero
- * again, so a workspace can be reused by later calls of any size on the
- * same stream.  Calls that overlap in time (different streams) need
- * different workspaces.
+ * bytes, 16-byte aligned, all of it zero before the first call that uses
+ * it (e.g. one hipMemset after allocation).  Its first 8 KiB hold
+ * synchronisation words (counters that every call leaves at zero again, and
+ * a call counter); the rest holds the intermediate h, which the batch-1..4
+ * kernel publishes as 64-bit words tagged with the call counter.  A
+ * workspace can be reused by later calls of any size on the same stream.
+ * Calls that overlap in time (different streams) need different workspaces.
  * For small T the library runs the whole FFN as one persistent kernel with
- * at most one workgroup per compute unit, whose down-projection waves wait
- * on counters in the workspace; each wait is bounded.  The int32 at byte
- * offset q3moe_expert_ffn_status_offset(...) of the workspace is a sticky
- * status word: it stays 0 unless a bounded wait ran out, in which case that
- * call's output is invalid.
+ * at most one workgroup per compute unit, whose down-projection threads wait
+ * for h words carrying the current tag; each wait is bounded.  The int32 at
+ * byte offset q3moe_expert_ffn_status_offset(...) of the workspace is a
+ * sticky status word: it stays 0 unless a bounded wait ran out, in which
+ * case that call's output is invalid.
  * Errors: E_NULL, E_SHAPE, E_QTYPE, E_ALIGN, E_WORKSPACE, E_ALIAS, E_HIP. */
 size_t q3moe_expert_ffn_workspace_bytes(int64_t T, int64_t H, int64_t F,
                                         int32_t E, int32_t top_k);

@@ -680,7 +680,7 @@ constexpr int kDnGroup = 16;                           // columns per down threa
 static_assert(kFzWaves * kWave * 4 == kFzNB * kQK, "one float4 of activations per thread and token");
 
 struct FusedLds {
-    int xp_bytes, dn_off, h_off, res_off, total;
+    int xp_bytes, dn_off, h_off, res_off, flag_off, total;
 };
 
 __host__ __device__ inline FusedLds fused_lds(int64_t T, int64_t F, int32_t qtype) {
@@ -690,7 +690,8 @@ __host__ __device__ inline FusedLds fused_lds(int64_t T, int64_t F, int32_t qtyp
     L.dn_off = (int)T * L.xp_bytes;                                 // down tiles, one per slot
     L.h_off = L.dn_off + kFzMaxSlots * d.tile_pad;                  // h of the unit's token, f32 [slot][F]
     L.res_off = L.h_off + kFzMaxSlots * (int)F * 4;                 // [wave][row] partial sums
-    L.total = L.res_off + kFzWaves * kDnRows * 4;
+    L.flag_off = L.res_off + kFzWaves * kDnRows * 4;                // down waves whose tiles landed
+    L.total = L.flag_off + 16;
     return L;
 }
 
@@ -875,44 +876,66 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
     const int gu_step = grid * kFzGu;
     const bool is_gu = wave < kFzGu;
 
-    // ---- (1) routing; each gate/up wave requests its first task's weights;
-    // then the activations of all T tokens as pieces in LDS (one float4 per
-    // thread and token), built once for all waves.  Every load here is
-    // unconditional (clamped), so the pieces wait only for the activations
-    // and not for the weight requests issued after them.
+    // ---- (1) routing and this call's epoch (every workgroup reads it here;
+    // only the last workgroup to finish advances it).  The down waves
+    // request the first unit's tiles at once.  Each gate/up wave requests its
+    // first task's weights and its activations, and the six gate/up waves
+    // turn the T tokens' activations into pieces in LDS (waves 0 and 1 also
+    // take the last quarter of the vector).  The activation loads are
+    // unconditional (clamped), so the pieces wait only for them and not for
+    // the weight requests issued after them.
     const int nr = (int)(T * k);
-    const int my_idx = lane < nr ? idx[lane] : -1;
-    const float my_w = lane < nr ? w[lane] : 0.f;
-    // this call's epoch: every workgroup reads it here, and only the last
-    // workgroup to finish advances it
+    const int ri = lane < nr ? lane : nr - 1;             // loads without a branch
+    const int my_idx = lane < nr ? idx[ri] : -1;
+    const float my_w = lane < nr ? w[ri] : 0.f;
     const uint32_t epoch = (uint32_t)__hip_atomic_load(sync + kSyncEpoch, __ATOMIC_RELAXED,
                                                        __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t tag = h_tag(epoch);
-    float4 xv[kFzMaxTokens];
-#pragma unroll
-    for (int j = 0; j < kFzMaxTokens; ++j)
-        xv[j] = reinterpret_cast<const float4*>(hidden + (j < T ? j : T - 1) * G::H)[tid];
+    // the tag as a scalar now, while only these small loads are in flight
+    const uint32_t tag = __builtin_amdgcn_readfirstlane(h_tag(epoch));
+    // LDS counters: gate/up waves whose activation pieces are written, down
+    // waves whose tiles have landed
+    int32_t* x_ready = reinterpret_cast<int32_t*>(smem + L.flag_off);
+    int32_t* dn_ready = x_ready + 1;
+    if (tid == 0) {
+        *x_ready = 0;
+        *dn_ready = 0;
+    }
+    __syncthreads();                          // the counters are zero before anyone counts
 
+    int64_t unit = wg;
     int tau = wg * kFzGu + wave;
     int p = (tau < n_gu ? tau : 0) / tiles, r0 = ((tau < n_gu ? tau : 0) % tiles) * G::R;
     GuRows rows;
     if (is_gu) {
+        constexpr int kXThr = kFzGu * kWave;              // 384 threads, one float4 each
+        constexpr int kXRest = kFzNB * kQK / 4 - kXThr;   // 128 float4 left for waves 0 and 1
+        const bool second = tid < kXRest;
+        float4 xv[kFzMaxTokens], xw[kFzMaxTokens];
+#pragma unroll
+        for (int j = 0; j < kFzMaxTokens; ++j) {
+            const float4* hx = reinterpret_cast<const float4*>(hidden + (j < T ? j : T - 1) * G::H);
+            xv[j] = hx[tid];
+            xw[j] = hx[kXThr + (second ? tid : 0)];
+        }
         gu_rows_load(rows, lane_value(my_idx, (int)p), E, gbase, gstride, ubase, ustride, r0, lane);
         __builtin_amdgcn_sched_barrier(0);
         build_x_pieces<kFzMaxTokens>(xv, T, smem, tid);
-        // keeps the two builds apart: merged after the branch, the stores
-        // would wait for the weight requests as well
+        if (second) build_x_pieces<kFzMaxTokens>(xw, T, smem, kXThr + tid);
+        else asm volatile("" ::"v"(xw[0].x), "v"(xw[1].x), "v"(xw[2].x), "v"(xw[3].x));
         __builtin_amdgcn_sched_barrier(0);
-    } else {
-        build_x_pieces<kFzMaxTokens>(xv, T, smem, tid);
-    }
-    __syncthreads();                          // no direct-to-LDS load is in flight yet
+        // the six gate/up waves meet on an LDS counter (the down waves, busy
+        // with their tiles, are not part of this)
+        if (lane == 0) __hip_atomic_fetch_add(x_ready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        int spins = 0;
+        while (__hip_atomic_load(x_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < kFzGu &&
+               ++spins <= kSpinLimit)
+            __builtin_amdgcn_s_sleep(1);
 
-    int64_t unit = wg;
-    if (is_gu) {
         // gate/up tasks: the first task's weights are on their way; read the
-        // token's pieces and compute it (outside the loop, so the waits for
-        // its rows are counted exactly), then load and compute the rest
+        // token's pieces and compute it, then load and compute the rest.
+        // Raised issue priority: the gate/up waves are the critical path, and
+        // two SIMDs also run a down wave's weight extraction beside them.
+        __builtin_amdgcn_s_setprio(2);
         if (tau < n_gu) {
             int xc = p / k;                   // token whose pieces x holds
             XCols x = load_xcols(smem + xc * kI8TokenBytes, lane);
@@ -929,31 +952,41 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
                 gu_rows_finish(rows, x, lane, hbuf, (int64_t)p * F + r0, tag);
             }
         }
+        __builtin_amdgcn_s_setprio(0);
     }
-    // A separate branch after the gate/up one, on a condition the compiler
-    // cannot relate to is_gu: merged into an else, the direct-to-LDS loads
-    // issued here would appear pending on the gate/up path and cost its
-    // weight waits their exact counts.
+    // The down waves request the first unit's tiles and count themselves
+    // ready once they have landed.  A separate branch after the gate/up one,
+    // on a condition the compiler cannot relate to is_gu: merged with it, the
+    // direct-to-LDS loads would appear pending on the gate/up path and turn
+    // its waits for single loads into waits for all of them.
     int dn_wave = __builtin_amdgcn_readfirstlane(is_gu ? 0 : 1);
     asm volatile("" : "+s"(dn_wave));
-    if (dn_wave && unit < n_dn) {
-        // down waves: request the first unit's tiles for all slots (after the
-        // barrier, so behind every gate/up request of the workgroup)
-        const int dw = wave - kFzGu;
-        const int64_t t = unit / row_units, r0d = (unit % row_units) * kDnRows;
-        for (int s = dw; s < k; s += kFzDn) {
-            const int e = lane_value(my_idx, (int)(t * k + s));
-            if (e >= 0 && e < E)
-                dn_issue_weights(smem + L.dn_off + s * dg.tile_pad, dg, dbase, dstride, e, r0d, lane);
+    if (dn_wave) {
+        if (unit < n_dn) {
+            const int dw = wave - kFzGu;
+            const int64_t t = unit / row_units, r0d = (unit % row_units) * kDnRows;
+            for (int s = dw; s < k; s += kFzDn) {
+                const int e = lane_value(my_idx, (int)(t * k + s));
+                if (e >= 0 && e < E)
+                    dn_issue_weights(smem + L.dn_off + s * dg.tile_pad, dg, dbase, dstride, e, r0d, lane);
+            }
         }
-        wait_all_loads();                     // the tiles are in LDS
+        wait_all_loads();
+        if (lane == 0)
+            __hip_atomic_fetch_add(dn_ready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
 
-    // ---- (2) down projection and combine, all waves.  Thread unit u =
-    // (slot u / G, column group u % G) for the 8 rows of the workgroup's
-    // output unit.
+    // ---- (2) down projection and combine.  The down units are shared by
+    // waves 0-3 (gate/up done first) and the two down waves, 64 per wave:
+    // unit u = (slot u / G, 16-column group u % G) for the 8 rows of the
+    // workgroup's output unit.  Waves 4 and 5, still on gate/up, only help
+    // read h.
     const int groups = (int)(F / kDnGroup);
     const int n_units = k * groups;
+    constexpr int kUnitThr = (kFzWaves - 2) * kWave;
+    const int uw = wave < 4 ? wave : (wave >= kFzGu ? wave - 2 : -1);
+    const int iters = (n_units + kUnitThr - 1) / kUnitThr;   // the same for every wave
+    float* hl = reinterpret_cast<float*>(smem + L.h_off);
     for (int j = 0; unit < n_dn; unit += grid, ++j) {
         const int64_t t = unit / row_units, r0 = (unit % row_units) * kDnRows;
         if (j > 0) {
@@ -963,41 +996,47 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
                     dn_issue_weights(smem + L.dn_off + s * dg.tile_pad, dg, dbase, dstride, e, r0, lane);
             }
             wait_all_loads();
+            __syncthreads();                  // this unit's tiles are in LDS
+        } else if (uw >= 0) {
+            // the first unit's tiles: wait until both down waves report them
+            int spins = 0;
+            while (__hip_atomic_load(dn_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < kFzDn &&
+                   ++spins <= kSpinLimit)
+                __builtin_amdgcn_s_sleep(1);
         }
-        __syncthreads();                      // this unit's tiles are in LDS
         float acc[kDnRows];
 #pragma unroll
         for (int rho = 0; rho < kDnRows; ++rho) acc[rho] = 0.f;
-        float* hl = reinterpret_cast<float*>(smem + L.h_off);
-        const int iters = (n_units + kThr - 1) / kThr;   // the same for every wave
         for (int it = 0; it < iters; ++it) {
-            const int u = tid + it * kThr;
-            const bool active = u < n_units;
+            const int u = uw * kWave + lane + it * kUnitThr;
+            const bool active = uw >= 0 && u < n_units;
             const int uc = active ? u : 0;
             const int s = uc / groups, grp = uc % groups;
             const int e = __shfl(my_idx, (int)(t * k) + s, kWave);
             const float ws = __shfl(my_w, (int)(t * k) + s, kWave);
             const bool valid = active && e >= 0 && e < E;
             float wt[kDnRows][kDnGroup];
-            dn_unit_weights(smem + L.dn_off + s * dg.tile_pad, dg, grp, wt);
+            if (uw >= 0) dn_unit_weights(smem + L.dn_off + s * dg.tile_pad, dg, grp, wt);
             if (it == 0) {
                 // the token's h: every slot's F values, published by gate/up
                 // waves anywhere on the device
                 dn_wait_h<kThr>(hbuf + t * k * F, k * (int)F, tag, hl, tid, status);
                 __syncthreads();
             }
-            float hv[kDnGroup];
+            if (uw >= 0) {
+                float hv[kDnGroup];
 #pragma unroll
-            for (int i = 0; i < kDnGroup; i += 4) {
-                const float4 h4 = *reinterpret_cast<const float4*>(hl + s * F + grp * kDnGroup + i);
-                hv[i] = h4.x; hv[i + 1] = h4.y; hv[i + 2] = h4.z; hv[i + 3] = h4.w;
-            }
+                for (int i = 0; i < kDnGroup; i += 4) {
+                    const float4 h4 = *reinterpret_cast<const float4*>(hl + s * F + grp * kDnGroup + i);
+                    hv[i] = h4.x; hv[i + 1] = h4.y; hv[i + 2] = h4.z; hv[i + 3] = h4.w;
+                }
 #pragma unroll
-            for (int rho = 0; rho < kDnRows; ++rho) {
-                float y = 0.f;
+                for (int rho = 0; rho < kDnRows; ++rho) {
+                    float y = 0.f;
 #pragma unroll
-                for (int i = 0; i < kDnGroup; ++i) y = fmaf(wt[rho][i], hv[i], y);
-                acc[rho] += valid ? ws * y : 0.f;
+                    for (int i = 0; i < kDnGroup; ++i) y = fmaf(wt[rho][i], hv[i], y);
+                    acc[rho] += valid ? ws * y : 0.f;
+                }
             }
         }
         const float r = fold8_rows(acc, lane);            // lanes 8q..: row q of this wave
