@@ -2,10 +2,13 @@
 """Benchmark: one Qwen3-30B-A3B sparse-MoE FFN layer at batch-1 decode.
 
 A step is one pass of the whole hot path over one token: the router GEMV
-with on-device top-8 and renormalisation (q3moe_route), then the expert FFN
-on the selected Q4_K/Q6_K experts with SwiGLU and the weighted combine
-(q3moe_expert_ffn).  Shape: hidden 2048, 128 experts, top-8, expert FFN 768,
-gate/up Q4_K (884,736 B/expert), down Q6_K (1,290,240 B/expert).
+with on-device top-8 and renormalisation, then the expert FFN on the
+selected Q4_K/Q6_K experts with SwiGLU and the weighted combine, as one
+q3moe_moe_ffn call (a single persistent kernel that routes inside).  The
+same step through the two entry points (q3moe_route, then
+q3moe_expert_ffn) is reported beside it.  Shape: hidden 2048, 128 experts,
+top-8, expert FFN 768, gate/up Q4_K (884,736 B/expert), down Q6_K
+(1,290,240 B/expert).
 
 Weights and inputs are seeded synthetic data (no trained checkpoint exists
 here), already resident in HBM when timing starts.  To keep the 256 MB
@@ -15,10 +18,10 @@ one replay of the captured graph touches ~1.6 GB of expert bytes.  Steps
 are captured in a HIP graph (the host issues one launch per 64 steps) and
 replayed; the timed region is bracketed by device synchronisation.
 
-The dominant kernel work, the expert FFN, is additionally timed with HIP
-events over a graph of FFN-only launches on the same stream, giving its
-average duration per launch and its achieved HBM bandwidth against the
-MI355X peak of 8 TB/s.  The CPU baseline times the oracle (test
+The step is one kernel launch, so the HIP events around the timed region
+give its average duration per launch and its achieved HBM bandwidth against
+the MI355X peak of 8 TB/s; the expert FFN alone (routing given) is timed the
+same way over a graph of FFN-only launches.  The CPU baseline times the oracle (test
 infrastructure, plain scalar C) on a bounded sample of the same workload on
 the host cores, and checks the GPU outputs of the sampled steps against it.
 
@@ -117,6 +120,8 @@ def main():
     ws_route = torch.zeros(q3.q3moe_route_workspace_bytes(1, E), dtype=torch.uint8, device=dev)
     ws_ffn = torch.zeros(q3.q3moe_expert_ffn_workspace_bytes(1, H, F, E, k), dtype=torch.uint8,
                          device=dev)
+    ws_moe = torch.zeros(q3.q3moe_moe_ffn_workspace_bytes(1, H, F, E, k), dtype=torch.uint8,
+                         device=dev)
 
     def route(i):
         L = layers[i % N_LAYER_COPIES]
@@ -126,7 +131,12 @@ def main():
         q3.q3moe_expert_ffn(xs[i], idx[i], wts[i], *experts[i % N_LAYER_COPIES], F=F,
                             out=outs[i], workspace=ws_ffn)
 
-    def step(i):
+    def step(i):                                   # the block in one call
+        L = layers[i % N_LAYER_COPIES]
+        q3.q3moe_moe_ffn(xs[i], L.router, k, *experts[i % N_LAYER_COPIES], F=F, out=outs[i],
+                         topk_idx=idx[i], topk_w=wts[i], workspace=ws_moe)
+
+    def step_two_calls(i):
         route(i)
         ffn(i)
 
@@ -154,10 +164,13 @@ def main():
                 fn(i)
         return g
 
+    for i in range(GRAPH_STEPS):                   # load the two-call kernels too
+        step_two_calls(i)
     g_main = capture(step, GRAPH_STEPS)
     rem = args.steps % GRAPH_STEPS
     g_rem = capture(step, rem) if rem else None
     g_ffn = capture(ffn, GRAPH_STEPS)
+    g_two = capture(step_two_calls, GRAPH_STEPS)
 
     # warmup: at least W steps, and every graph launched once before timing
     for _ in range(max(1, math.ceil(args.warmup / GRAPH_STEPS))):
@@ -165,6 +178,7 @@ def main():
     if g_rem is not None:
         g_rem.replay()
     g_ffn.replay()
+    g_two.replay()
     torch.cuda.synchronize()
 
     # timed region: exactly K steps
@@ -193,6 +207,14 @@ def main():
     kb.record()
     torch.cuda.synchronize()
     ffn_us = ka.elapsed_time(kb) * 1000.0 / (args.kernel_reps * GRAPH_STEPS)
+    ka.record()
+    for _ in range(args.kernel_reps):
+        g_two.replay()
+    kb.record()
+    torch.cuda.synchronize()
+    two_us = ka.elapsed_time(kb) * 1000.0 / (args.kernel_reps * GRAPH_STEPS)
+    # the steps of the timed region are one kernel launch each
+    block_us = ms_per_step * 1000.0
 
     gate_b = shape.gate_stride
     down_b = shape.down_stride
@@ -200,7 +222,7 @@ def main():
     act_bytes = 2 * H * 4                             # hidden in, block output out
     ffn_bytes = expert_bytes + act_bytes
     step_bytes = ffn_bytes + E * H * 4                # + the f32 router
-    achieved = ffn_bytes / (ffn_us * 1e-6) / 1e9
+    achieved = step_bytes / (block_us * 1e-6) / 1e9
 
     result = {
         "metric": "MoE-layer tokens/sec at batch 1 and 512; achieved HBM GB/s vs peak",
@@ -227,14 +249,22 @@ def main():
         "wall_s_timed_region": round(wall, 4),
         "roofline": {
             "bound": "hbm",
-            "kernel": "expert FFN (q3moe_expert_ffn: one persistent kernel, ffn_fused8_kernel)",
+            "kernel": "MoE block (q3moe_moe_ffn: one persistent kernel, ffn_fused8_kernel<true>: "
+                      "router, top-8, expert FFN)",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": measured_traffic(),
-            "bytes_per_launch": ffn_bytes,
-            "avg_launch_us": round(ffn_us, 3),
+            "bytes_per_launch": step_bytes,
+            "avg_launch_us": round(block_us, 3),
+        },
+        "two_calls": {
+            "note": "the same step as q3moe_route + q3moe_expert_ffn (two launches)",
+            "us_per_step": round(two_us, 3),
+            "tokens_per_s": round(1e6 / two_us, 1),
+            "expert_ffn_us": round(ffn_us, 3),
+            "expert_ffn_hbm_gbps": round(ffn_bytes / (ffn_us * 1e-6) / 1e9, 1),
         },
     }
 
@@ -370,8 +400,7 @@ def decoder_bench(torch, q3, gen, layers, experts, shape, dev):
         idx = torch.empty((B, k), dtype=torch.int32, device=dev)
         wts = torch.empty((B, k), device=dev)
         ws_a = torch.empty(q3.q3moe_gqa_attention_workspace_bytes(B, nq, nkv, D, S), dtype=torch.uint8, device=dev)
-        ws_r = torch.zeros(q3.q3moe_route_workspace_bytes(B, E), dtype=torch.uint8, device=dev)
-        ws_f = torch.zeros(q3.q3moe_expert_ffn_workspace_bytes(B, H, F, E, k), dtype=torch.uint8, device=dev)
+        ws_m = torch.zeros(q3.q3moe_moe_ffn_workspace_bytes(B, H, F, E, k), dtype=torch.uint8, device=dev)
 
         def attention(i):
             A = atts[i % ncopies]
@@ -392,10 +421,9 @@ def decoder_bench(torch, q3, gen, layers, experts, shape, dev):
             attention(i)
             L = layers[i % len(layers)]
             q3.q3moe_rmsnorm(x1, atts[i % ncopies].post_norm, s_.eps, out=hn)
-            q3.q3moe_route(hn, L.router, k, idx, wts, workspace=ws_r)
             out.copy_(x1)
-            q3.q3moe_expert_ffn(hn, idx, wts, *experts[i % len(experts)], F=F, out=out, accumulate=True,
-                                workspace=ws_f)
+            q3.q3moe_moe_ffn(hn, L.router, k, *experts[i % len(experts)], F=F, out=out, accumulate=True,
+                             topk_idx=idx, topk_w=wts, workspace=ws_m)
 
         n = 16
         for i in range(n):

@@ -177,6 +177,35 @@ q3moe_status q3moe_expert_ffn(const float *hidden, int64_t T, int64_t H, int64_t
                               float *out, int32_t accumulate,
                               void *workspace, size_t workspace_bytes, void *stream);
 
+/* ------------------------------------------------------------ MoE block --
+ * The whole sparse MoE block of the tokens in one call: q3moe_route on
+ * (hidden, router), then q3moe_expert_ffn with that routing (issue #3714,
+ * gap G3 and the fused decode plan K1-K3 under G8).  topk_idx, topk_w and out
+ * receive what the two calls produce, except that the router logits are
+ * summed in another order (still in double, so the selection differs only
+ * at logits equal to about 1e-16 relative).  Arguments as for the two calls;
+ * topk_idx and topk_w are outputs here and must not overlap hidden, out or
+ * each other.  Router input is the FFN input (hidden).
+ * For T <= 4, H = 2048, top_k <= 8 and E <= 256 this is one persistent
+ * kernel: each workgroup computes a slice of the router dot products and
+ * publishes it as tagged words, every workgroup selects the top-k from all
+ * slices and goes on into the expert FFN.  Other shapes run the route and
+ * expert-FFN kernels back to back.
+ * workspace: at least q3moe_moe_ffn_workspace_bytes(T, H, F, E, k) bytes,
+ * 16-byte aligned, all of it zero before the first call that uses it; it can
+ * be reused by later calls of any size on the same stream.  Its first bytes
+ * are an expert-FFN workspace, so the status word is at
+ * q3moe_expert_ffn_status_offset(...) (bit 2 set: the in-kernel routing
+ * waited in vain).
+ * Errors: E_NULL, E_SHAPE, E_QTYPE, E_ALIGN, E_WORKSPACE, E_ALIAS, E_HIP. */
+size_t q3moe_moe_ffn_workspace_bytes(int64_t T, int64_t H, int64_t F, int32_t E,
+                                     int32_t top_k);
+q3moe_status q3moe_moe_ffn(const float *hidden, int64_t T, int64_t H, int64_t F,
+                           int32_t E, int32_t top_k, const float *router,
+                           q3moe_experts gate, q3moe_experts up, q3moe_experts down,
+                           int32_t *topk_idx, float *topk_w, float *out, int32_t accumulate,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
 /* ------------------------------------------------------ attention prologue --
  * In place on q [T x n_q_heads x head_dim] and k [T x n_kv_heads x head_dim]
  * (f32, row-major): for every head slice, RMSNorm with the gain vector shared

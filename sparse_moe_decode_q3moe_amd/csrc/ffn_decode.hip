@@ -23,6 +23,7 @@
 
 #include "device_common.h"
 #include "internal.h"
+#include "route_common.h"
 
 namespace q3moe {
 
@@ -677,10 +678,13 @@ __device__ __forceinline__ uint32_t h_tag(uint32_t epoch) {
 constexpr int kFzMaxSlots = 8;                        // the fused path serves k <= 8
 constexpr int kFzMaxTokens = 4;                        // and T <= 4 (T*k routing entries <= 32)
 constexpr int kDnGroup = 16;                           // columns per down thread unit
+constexpr int kFzMaxUnits = 256;                       // router units (expert x column part) in the kernel
+constexpr int kFzRouteNper = 4;                        // experts per lane in the in-kernel top-k: E <= 256
 static_assert(kFzWaves * kWave * 4 == kFzNB * kQK, "one float4 of activations per thread and token");
 
 struct FusedLds {
-    int xp_bytes, dn_off, h_off, res_off, flag_off, total;
+    int xp_bytes, dn_off, h_off, res_off, flag_off, route_off, rp_off, rl_off, lg_off, key_off,
+        key32_off, sel_off, total;
 };
 
 __host__ __device__ inline FusedLds fused_lds(int64_t T, int64_t F, int32_t qtype) {
@@ -691,7 +695,17 @@ __host__ __device__ inline FusedLds fused_lds(int64_t T, int64_t F, int32_t qtyp
     L.h_off = L.dn_off + kFzMaxSlots * d.tile_pad;                  // h of the unit's token, f32 [slot][F]
     L.res_off = L.h_off + kFzMaxSlots * (int)F * 4;                 // [wave][row] partial sums
     L.flag_off = L.res_off + kFzWaves * kDnRows * 4;                // down waves whose tiles landed
-    L.total = L.flag_off + 16;
+    // routing in the kernel: the T*k (expert, weight) table, per-wave router
+    // sums [wave][token] and the partial logits [token][unit] (at most one
+    // unit per workgroup, so at most kFzMaxUnits)
+    L.route_off = L.flag_off + 16;
+    L.rp_off = L.route_off + kFzMaxTokens * kFzMaxSlots * 8;
+    L.rl_off = L.rp_off + kFzWaves * kFzMaxTokens * 8;
+    L.lg_off = L.rl_off + kFzMaxTokens * kFzMaxUnits * 8;              // [token][expert] logits
+    L.key_off = L.lg_off + kFzMaxTokens * kFzRouteNper * kWave * 8;    // their order keys
+    L.key32_off = L.key_off + kFzMaxTokens * kFzRouteNper * kWave * 8; // and 32-bit screen keys
+    L.sel_off = L.key32_off + kFzMaxTokens * kFzRouteNper * kWave * 4; // top-k: idx, value
+    L.total = L.sel_off + kFzMaxTokens * kFzMaxSlots * 12;
     return L;
 }
 
@@ -742,15 +756,15 @@ __device__ __forceinline__ void dn_unit_weights(const uint8_t* tile, const DnGeo
     }
 }
 
-// All n h words of one token (its k slots, contiguous from src) into LDS as
-// f32, once each carries `tag`.  Thread tid reads words tid + i * kThr with
+// n tagged words from src into LDS (their 32-bit payloads, dst[i] for word
+// i), once each carries `tag`.  Thread tid reads words tid + i * kThr with
 // device-scope 64-bit loads, so each load instruction of a wave covers 512
 // consecutive bytes; a wave re-reads its words until all of them carry the
-// tag.  A wait that runs out sets bit 1 of the status word.
+// tag.  A wait that runs out ORs `bit` into the status word.
 constexpr int kPollWords = 12;                         // words per thread and round
 template <int kThr>
-__device__ __forceinline__ void dn_wait_h(const uint64_t* src, int n, uint32_t tag, float* hl,
-                                          int tid, int32_t* status) {
+__device__ __forceinline__ void wait_tagged(const uint64_t* src, int n, uint32_t tag,
+                                            uint32_t* dst, int tid, int32_t* status, int bit) {
     for (int c0 = 0; c0 < n; c0 += kThr * kPollWords) {
         uint64_t v[kPollWords];
         int spins = 0;
@@ -765,7 +779,7 @@ __device__ __forceinline__ void dn_wait_h(const uint64_t* src, int n, uint32_t t
             }
             if (__all(ok)) break;
             if (++spins > kSpinLimit) {
-                if (!ok) __hip_atomic_fetch_or(status, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (!ok) __hip_atomic_fetch_or(status, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 break;
             }
             __builtin_amdgcn_s_sleep(1);
@@ -773,7 +787,7 @@ __device__ __forceinline__ void dn_wait_h(const uint64_t* src, int n, uint32_t t
 #pragma unroll
         for (int i = 0; i < kPollWords; ++i) {
             const int wi = c0 + tid + i * kThr;
-            if (wi < n) hl[wi] = __uint_as_float((uint32_t)v[i]);
+            if (wi < n) dst[wi] = (uint32_t)v[i];
         }
     }
 }
@@ -850,13 +864,15 @@ __device__ __forceinline__ int lane_value(int v, int src) { return __builtin_amd
 // workspace's synchronisation header: its counters are zero when the kernel
 // starts and zero again when it ends.  The routing entries (T*k <= 32) live
 // in one register per lane of every wave and are read with readlane.
+template <bool kRoute>
 __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
     const float* __restrict__ hidden, int64_t T, int64_t F, int32_t E, int32_t k,
     const int32_t* __restrict__ idx, const float* __restrict__ w,
     const uint8_t* __restrict__ gbase, int64_t gstride, const uint8_t* __restrict__ ubase,
     int64_t ustride, const uint8_t* __restrict__ dbase, int32_t dqtype, int64_t dstride,
     float* __restrict__ out, int accumulate, uint64_t* __restrict__ hbuf,
-    int32_t* __restrict__ sync) {
+    int32_t* __restrict__ sync, const float* __restrict__ router, int32_t P,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, uint64_t* __restrict__ rbuf) {
     using G = GuTask<kFzNB>;
     constexpr int kThr = kFzWaves * kWave;
     extern __shared__ __align__(16) uint8_t smem[];
@@ -876,21 +892,12 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
     const int gu_step = grid * kFzGu;
     const bool is_gu = wave < kFzGu;
 
-    // ---- (1) routing and this call's epoch (every workgroup reads it here;
-    // only the last workgroup to finish advances it).  The down waves
-    // request the first unit's tiles at once.  Each gate/up wave requests its
-    // first task's weights and its activations, and the six gate/up waves
-    // turn the T tokens' activations into pieces in LDS (waves 0 and 1 also
-    // take the last quarter of the vector).  The activation loads are
-    // unconditional (clamped), so the pieces wait only for them and not for
-    // the weight requests issued after them.
+    // ---- (1) this call's epoch (every workgroup reads it here; only the
+    // last workgroup to finish advances it), routing, activation pieces.
     const int nr = (int)(T * k);
-    const int ri = lane < nr ? lane : nr - 1;             // loads without a branch
-    const int my_idx = lane < nr ? idx[ri] : -1;
-    const float my_w = lane < nr ? w[ri] : 0.f;
     const uint32_t epoch = (uint32_t)__hip_atomic_load(sync + kSyncEpoch, __ATOMIC_RELAXED,
                                                        __HIP_MEMORY_SCOPE_AGENT);
-    // the tag as a scalar now, while only these small loads are in flight
+    // the tag as a scalar now, while only this small load is in flight
     const uint32_t tag = __builtin_amdgcn_readfirstlane(h_tag(epoch));
     // LDS counters: gate/up waves whose activation pieces are written, down
     // waves whose tiles have landed
@@ -906,7 +913,12 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
     int tau = wg * kFzGu + wave;
     int p = (tau < n_gu ? tau : 0) / tiles, r0 = ((tau < n_gu ? tau : 0) % tiles) * G::R;
     GuRows rows;
-    if (is_gu) {
+
+    // The T tokens' activations as pieces in LDS, built by the six gate/up
+    // waves (waves 0 and 1 also take the last quarter of the vector).  The
+    // activation loads are unconditional (clamped), so the build waits only
+    // for them and not for weight requests issued after them.
+    auto build_pieces = [&](bool issue_weights, int e0) {
         constexpr int kXThr = kFzGu * kWave;              // 384 threads, one float4 each
         constexpr int kXRest = kFzNB * kQK / 4 - kXThr;   // 128 float4 left for waves 0 and 1
         const bool second = tid < kXRest;
@@ -917,20 +929,120 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
             xv[j] = hx[tid];
             xw[j] = hx[kXThr + (second ? tid : 0)];
         }
-        gu_rows_load(rows, lane_value(my_idx, (int)p), E, gbase, gstride, ubase, ustride, r0, lane);
+        if (issue_weights)
+            gu_rows_load(rows, e0, E, gbase, gstride, ubase, ustride, r0, lane);
         __builtin_amdgcn_sched_barrier(0);
         build_x_pieces<kFzMaxTokens>(xv, T, smem, tid);
         if (second) build_x_pieces<kFzMaxTokens>(xw, T, smem, kXThr + tid);
         else asm volatile("" ::"v"(xw[0].x), "v"(xw[1].x), "v"(xw[2].x), "v"(xw[3].x));
         __builtin_amdgcn_sched_barrier(0);
-        // the six gate/up waves meet on an LDS counter (the down waves, busy
-        // with their tiles, are not part of this)
-        if (lane == 0) __hip_atomic_fetch_add(x_ready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-        int spins = 0;
-        while (__hip_atomic_load(x_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < kFzGu &&
-               ++spins <= kSpinLimit)
-            __builtin_amdgcn_s_sleep(1);
+    };
 
+    int my_idx;
+    float my_w;
+    if constexpr (kRoute) {
+        // Routing in the kernel (the route entry point's result, computed
+        // redundantly by every workgroup from shared partial logits).
+        int32_t* r_idx = reinterpret_cast<int32_t*>(smem + L.route_off);
+        float* r_w = reinterpret_cast<float*>(r_idx + kFzMaxTokens * kFzMaxSlots);
+        double* rp = reinterpret_cast<double*>(smem + L.rp_off);      // [wave][token]
+        uint32_t* rl = reinterpret_cast<uint32_t*>(smem + L.rl_off);  // [token][unit] f64 halves
+        const int U = E * P, HP = (int)(G::H / P), nq = HP / 4;
+        // (a) this workgroup's router unit(s): expert u / P, column part u % P;
+        // f64 sums of the exact f32 products, published as two tagged words
+        for (int u = wg; u < U; u += grid) {
+            const int e = u / P, c0 = (u % P) * HP;
+            double acc[kFzMaxTokens];
+#pragma unroll
+            for (int t = 0; t < kFzMaxTokens; ++t) acc[t] = 0.0;
+            if (tid < nq) {
+                const float4 r = reinterpret_cast<const float4*>(router + (int64_t)e * G::H + c0)[tid];
+#pragma unroll
+                for (int t = 0; t < kFzMaxTokens; ++t) {
+                    if (t < T) {
+                        const float4 x4 = reinterpret_cast<const float4*>(hidden + t * G::H + c0)[tid];
+                        double a = fma((double)r.x, (double)x4.x, 0.0);
+                        a = fma((double)r.y, (double)x4.y, a);
+                        a = fma((double)r.z, (double)x4.z, a);
+                        acc[t] = fma((double)r.w, (double)x4.w, a);
+                    }
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < kFzMaxTokens; ++t) {
+                if (t < T) {
+                    const double sw = wave_sum_dpp_f64(acc[t]);
+                    if (lane == 0) rp[wave * kFzMaxTokens + t] = sw;
+                }
+            }
+            __syncthreads();
+            if (tid < T) {
+                double sum = 0.0;
+#pragma unroll
+                for (int wv = 0; wv < kFzWaves; ++wv) sum += rp[wv * kFzMaxTokens + tid];
+                const uint64_t bits = __builtin_bit_cast(uint64_t, sum);
+                uint64_t* dst = rbuf + ((int64_t)tid * U + u) * 2;
+                __hip_atomic_store(dst, ((uint64_t)tag << 32) | (uint32_t)bits, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(dst + 1, ((uint64_t)tag << 32) | (uint32_t)(bits >> 32),
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            __syncthreads();
+        }
+        // the activation pieces, while the partial logits travel
+        if (is_gu) build_pieces(false, 0);
+        // (b) every partial logit of every token, then (c) the top-k of token
+        // t on wave t; logit = the sum of the expert's parts in part order
+        wait_tagged<kThr>(rbuf, (int)T * U * 2, tag, rl, tid, status, 4);
+        __syncthreads();
+        // logits of every token (the sum of an expert's parts in part order),
+        // then the top-k by rank counting over the whole workgroup
+        double* lgt = reinterpret_cast<double*>(smem + L.lg_off);     // [token][expert]
+        uint64_t* keys = reinterpret_cast<uint64_t*>(smem + L.key_off);
+        uint32_t* keys32 = reinterpret_cast<uint32_t*>(smem + L.key32_off);
+        int32_t* sel_idx = reinterpret_cast<int32_t*>(smem + L.sel_off);
+        double* sel_val = reinterpret_cast<double*>(sel_idx + kFzMaxTokens * kFzMaxSlots);
+        for (int i = tid; i < (int)T * E; i += kThr) {
+            const int t = i / E, e = i % E;
+            const double* pl = reinterpret_cast<const double*>(rl) + t * U + e * P;
+            double sum = 0.0;
+            for (int q = 0; q < P; ++q) sum += pl[q];
+            lgt[i] = sum;
+            keys[i] = order_key(sum);
+            keys32[i] = order_key32(sum);
+        }
+        __syncthreads();
+        topk_rank_select<kThr>(lgt, keys, keys32, (int)T, E, k, tid, sel_idx, sel_val);
+        __syncthreads();
+        if (wave < T)
+            topk_weights(sel_idx + wave * k, sel_val + wave * k, k, lane, r_idx + wave * k,
+                         r_w + wave * k);
+        __syncthreads();
+        my_idx = lane < nr ? r_idx[lane] : -1;
+        my_w = lane < nr ? r_w[lane] : 0.f;
+        if (wg == 0 && tid < nr) {
+            topk_idx[tid] = r_idx[tid];
+            topk_w[tid] = r_w[tid];
+        }
+        if (is_gu)
+            gu_rows_load(rows, lane_value(my_idx, p), E, gbase, gstride, ubase, ustride, r0, lane);
+    } else {
+        const int ri = lane < nr ? lane : nr - 1;         // loads without a branch
+        my_idx = lane < nr ? idx[ri] : -1;
+        my_w = lane < nr ? w[ri] : 0.f;
+        if (is_gu) {
+            build_pieces(true, lane_value(my_idx, p));
+            // the six gate/up waves meet on an LDS counter (the down waves,
+            // busy with their tiles, are not part of this)
+            if (lane == 0) __hip_atomic_fetch_add(x_ready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+            int spins = 0;
+            while (__hip_atomic_load(x_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < kFzGu &&
+                   ++spins <= kSpinLimit)
+                __builtin_amdgcn_s_sleep(1);
+        }
+    }
+
+    if (is_gu) {
         // gate/up tasks: the first task's weights are on their way; read the
         // token's pieces and compute it, then load and compute the rest.
         // Raised issue priority: the gate/up waves are the critical path, and
@@ -1020,7 +1132,7 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
             if (it == 0) {
                 // the token's h: every slot's F values, published by gate/up
                 // waves anywhere on the device
-                dn_wait_h<kThr>(hbuf + t * k * F, k * (int)F, tag, hl, tid, status);
+                wait_tagged<kThr>(hbuf + t * k * F, k * (int)F, tag, reinterpret_cast<uint32_t*>(hl), tid, status, 2);
                 __syncthreads();
             }
             if (uw >= 0) {
@@ -1131,19 +1243,46 @@ hipError_t launch_down(const float* w, int64_t T, int64_t H, int64_t F, int32_t 
     return hipGetLastError();
 }
 
+template <bool kRoute>
 hipError_t launch_fused8(const float* hidden, int64_t T, int64_t F, int32_t E, int32_t k,
                          const int32_t* idx, const float* w, const ExpertTensor& gate,
                          const ExpertTensor& up, const ExpertTensor& down, float* out,
-                         int accumulate, uint8_t* hp, int32_t* sync, int grid, hipStream_t stream) {
+                         int accumulate, uint8_t* hp, int32_t* sync, int grid,
+                         const float* router, int P, int32_t* topk_idx, float* topk_w,
+                         uint64_t* rbuf, hipStream_t stream) {
     const FusedLds L = fused_lds(T, F, down.qtype);
     static LdsLimit lds_set;
-    hipError_t err = ensure_lds(reinterpret_cast<const void*>(ffn_fused8_kernel), lds_set, L.total);
+    hipError_t err = ensure_lds(reinterpret_cast<const void*>(ffn_fused8_kernel<kRoute>), lds_set, L.total);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(ffn_fused8_kernel, dim3((unsigned)grid), dim3(kFzWaves * kWave),
+    hipLaunchKernelGGL(ffn_fused8_kernel<kRoute>, dim3((unsigned)grid), dim3(kFzWaves * kWave),
                        (size_t)L.total, stream, hidden, T, F, E, k, idx, w, gate.base, gate.stride,
                        up.base, up.stride, down.base, down.qtype, down.stride, out, accumulate,
-                       reinterpret_cast<uint64_t*>(hp), sync);
+                       reinterpret_cast<uint64_t*>(hp), sync, router, (int32_t)P, topk_idx, topk_w,
+                       rbuf);
     return hipGetLastError();
+}
+
+// Workgroups of the fused kernel for this shape (one per compute unit at
+// most), or 0 when the shape is outside it.
+int fused_grid(int64_t T, int64_t H, int64_t F, int32_t k, int32_t dqtype) {
+    if (H != (int64_t)kFzNB * kQK || k > kFzMaxSlots || T > kFzMaxTokens || T < 1) return 0;
+    if ((size_t)fused_lds(T, F, dqtype).total > kMaxLdsPerWorkgroup) return 0;
+    const int cus = cu_count();
+    if (cus <= 0) return 0;
+    const int64_t tiles = F / GuTask<kFzNB>::R;
+    const int64_t need = (T * k * tiles + kFzGu - 1) / kFzGu;
+    const int64_t units = T * (H / kDnRows);
+    const int64_t want = need > units ? need : units;
+    return (int)(want < cus ? want : cus);
+}
+
+// Column parts per router row in the fused kernel: the largest power of two
+// up to 8 that keeps E * P within the workgroup count (one router unit per
+// workgroup) and the unit table.
+int route_parts(int32_t E, int grid) {
+    int P = 1;
+    while (P < 8 && (int64_t)E * P * 2 <= grid && (int64_t)E * P * 2 <= kFzMaxUnits) P *= 2;
+    return P;
 }
 
 template <int NB>
@@ -1152,16 +1291,10 @@ hipError_t launch_decode_nb(const float* hidden, int64_t T, int64_t H, int64_t F
                             const ExpertTensor& up, const ExpertTensor& down, float* out,
                             int accumulate, uint8_t* hp, int32_t* sync, hipStream_t stream) {
     if constexpr (NB == kFzNB) {
-        const int cus = cu_count();
-        const int64_t tiles = F / GuTask<NB>::R;
-        const int64_t need = (T * k * tiles + kFzGu - 1) / kFzGu;
-        const int64_t units = T * (H / kDnRows);
-        const int64_t want = need > units ? need : units;
-        const int64_t grid = want < cus ? want : cus;
-        if (k <= kFzMaxSlots && T <= kFzMaxTokens && cus > 0 &&
-            (size_t)fused_lds(T, F, down.qtype).total <= kMaxLdsPerWorkgroup)
-            return launch_fused8(hidden, T, F, E, k, idx, w, gate, up, down, out, accumulate, hp,
-                                 sync, (int)grid, stream);
+        const int grid = fused_grid(T, H, F, k, down.qtype);
+        if (grid > 0)
+            return launch_fused8<false>(hidden, T, F, E, k, idx, w, gate, up, down, out, accumulate,
+                                        hp, sync, grid, nullptr, 1, nullptr, nullptr, nullptr, stream);
     }
     hipError_t err = launch_gu<NB>(hidden, T, F, E, k, idx, gate, up, hp, stream);
     if (err != hipSuccess) return err;
@@ -1191,6 +1324,28 @@ hipError_t launch_decode_ffn(const float* hidden, int64_t T, int64_t H, int64_t 
         case 16: return launch_decode_nb<16>(hidden, T, H, F, E, k, idx, w, gate, up, down, out, accumulate, hp, sync, stream);
         default: return hipErrorInvalidValue;
     }
+}
+
+bool moe_decode_fused(int64_t T, int64_t H, int64_t F, int32_t E, int32_t k, int32_t dqtype) {
+    return E <= kFzRouteNper * kWave && fused_grid(T, H, F, k, dqtype) > 0;
+}
+
+size_t moe_route_words_bytes(int64_t T, int32_t E) {
+    return (size_t)(T > 0 ? T : 0) * (size_t)E * 8 * 2 * sizeof(uint64_t);   // up to 8 parts
+}
+
+hipError_t launch_moe_decode(const float* hidden, int64_t T, int64_t H, int64_t F, int32_t E,
+                             int32_t k, const float* router, int32_t* topk_idx, float* topk_w,
+                             const ExpertTensor& gate, const ExpertTensor& up,
+                             const ExpertTensor& down, float* out, int accumulate, void* ffn_ws,
+                             void* route_words, hipStream_t stream) {
+    const int grid = fused_grid(T, H, F, k, down.qtype);
+    if (grid <= 0 || E > kFzRouteNper * kWave) return hipErrorInvalidValue;
+    int32_t* sync = static_cast<int32_t*>(ffn_ws);
+    uint8_t* hp = static_cast<uint8_t*>(ffn_ws) + kFfnSyncBytes;
+    return launch_fused8<true>(hidden, T, F, E, k, nullptr, nullptr, gate, up, down, out, accumulate,
+                               hp, sync, grid, router, route_parts(E, grid), topk_idx, topk_w,
+                               static_cast<uint64_t*>(route_words), stream);
 }
 
 }  // namespace q3moe

@@ -11,13 +11,15 @@
 // every token.  Larger batches run a logits kernel over (expert, 8-token
 // tile) and a top-k kernel with one wave per token.
 //
-// Selection (both paths): k rounds of a wave-wide argmax over the token's
-// logits, larger value first and equal values broken by the lower expert
-// index; weights are the softmax over the selected logits in double (the
-// first selected logit subtracted), normalised by their sum taken in rank
-// order, then rounded to f32.
+// Selection (both paths, topk_wave): k rounds of a wave-wide argmax over the
+// token's logits, larger value first and equal values broken by the lower
+// expert index, each round screened in f32 and decided exactly; weights are
+// the softmax over the selected logits in double (the first selected logit
+// subtracted), normalised by their sum taken in rank order, then rounded to
+// f32.
 #include "device_common.h"
 #include "internal.h"
+#include "route_common.h"
 
 namespace q3moe {
 
@@ -30,49 +32,6 @@ constexpr int kRouteChunk = 4;                         // float4 per thread and 
 
 // Workspace: kRouteSyncBytes holding the arrival counter (zero between
 // calls), then the logits [T x E] doubles.
-
-// Lane `src` (wave-uniform) of a double.
-__device__ __forceinline__ double readlane_f64(double v, int src) {
-    const uint64_t b = __builtin_bit_cast(uint64_t, v);
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, src);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), src);
-    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
-}
-
-// A double moved across lanes by a DPP pattern (both halves; lanes without a
-// source keep their own value).
-template <int CTRL>
-__device__ __forceinline__ double dpp_f64(double v) {
-    const uint64_t b = __builtin_bit_cast(uint64_t, v);
-    const int lo = (int)(uint32_t)b, hi = (int)(uint32_t)(b >> 32);
-    const uint32_t nlo = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, CTRL, 0xf, 0xf, false);
-    const uint32_t nhi = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, CTRL, 0xf, 0xf, false);
-    return __builtin_bit_cast(double, ((uint64_t)nhi << 32) | nlo);
-}
-constexpr int kDppQuadXor1 = 0xb1;        // quad_perm [1,0,3,2]
-constexpr int kDppQuadXor2 = 0x4e;        // quad_perm [2,3,0,1]
-constexpr int kDppRowRor4 = 0x124;
-constexpr int kDppRowRor8 = 0x128;
-
-// Wave-wide max / sum of a double, uniform in every lane: DPP inside each row
-// of 16 lanes, then the four row results combined in a fixed order.  No LDS
-// round trips on the dependent chain.
-__device__ __forceinline__ double wave_max_f64(double v) {
-    v = fmax(v, dpp_f64<kDppQuadXor1>(v));
-    v = fmax(v, dpp_f64<kDppQuadXor2>(v));
-    v = fmax(v, dpp_f64<kDppRowRor4>(v));
-    v = fmax(v, dpp_f64<kDppRowRor8>(v));
-    return fmax(fmax(readlane_f64(v, 0), readlane_f64(v, 16)),
-                fmax(readlane_f64(v, 32), readlane_f64(v, 48)));
-}
-
-__device__ __forceinline__ double wave_sum_dpp_f64(double v) {
-    v += dpp_f64<kDppQuadXor1>(v);
-    v += dpp_f64<kDppQuadXor2>(v);
-    v += dpp_f64<kDppRowRor4>(v);
-    v += dpp_f64<kDppRowRor8>(v);
-    return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
-}
 
 // This thread's share of row e of the router dotted with tokens t0..t0+ntok-1
 // (ntok <= 8), accumulated in double.  Loads use clamped indices and a zero
@@ -134,67 +93,6 @@ __device__ __forceinline__ double workgroup_token_sums(double acc[kRouteTokTile]
         for (int w = 0; w < kRouteWaves; ++w) s += part[tid][w];
     }
     return s;
-}
-
-// One wave: top-k and weights of one token whose logits lane e % 64 holds in
-// v[e / 64] (experts beyond E are never chosen).  Each round takes the
-// wave-wide max of the live logits, then the lowest expert index holding it
-// (ballots over j = 0, 1, ...: index 64j + lane grows with j, then lane).
-// Writes idx[0..k), w[0..k).
-template <int NPER>
-__device__ __forceinline__ void topk_wave(const double v_in[NPER], int32_t E, int32_t k,
-                                          int lane, int32_t* __restrict__ idx,
-                                          float* __restrict__ w) {
-    double v[NPER];
-    bool live[NPER];
-#pragma unroll
-    for (int j = 0; j < NPER; ++j) {
-        v[j] = v_in[j];
-        live[j] = lane + kWave * j < E;
-    }
-    double my_v = 0.0, top = 0.0;
-    int my_i = 0;
-    for (int r = 0; r < k; ++r) {
-        double lm = -__builtin_inf();
-#pragma unroll
-        for (int j = 0; j < NPER; ++j)
-            if (live[j]) lm = fmax(lm, v[j]);
-        const double m = wave_max_f64(lm);
-        int win = -1;
-#pragma unroll
-        for (int j = 0; j < NPER; ++j) {
-            const uint64_t hit = __ballot(live[j] && v[j] == m);
-            if (win < 0 && hit) win = kWave * j + __builtin_ctzll(hit);
-        }
-        if (win < 0) {                        // only NaN left: the lowest live index
-#pragma unroll
-            for (int j = 0; j < NPER; ++j) {
-                const uint64_t hit = __ballot(live[j]);
-                if (win < 0 && hit) win = kWave * j + __builtin_ctzll(hit);
-            }
-        }
-        double val = m;
-#pragma unroll
-        for (int j = 0; j < NPER; ++j)
-            if (win >> 6 == j) val = readlane_f64(v[j], win & 63);
-        if (r == 0) top = val;
-        if (lane == r) {
-            my_v = val;
-            my_i = win;
-        }
-#pragma unroll
-        for (int j = 0; j < NPER; ++j)
-            if (lane + kWave * j == win) live[j] = false;
-    }
-    // lane r < k holds rank r; normaliser summed in rank order
-    const double ex = lane < k ? exp(my_v - top) : 0.0;
-    double den = 0.0;
-    for (int r = 0; r < k; ++r)
-        den += readlane_f64(ex, r);
-    if (lane < k) {
-        idx[lane] = my_i;
-        w[lane] = (float)(ex / den);
-    }
 }
 
 // ------------------------------------------------------------ T <= 8 --

@@ -29,7 +29,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(_lib.EXPORTS) == names
@@ -92,6 +92,39 @@ def test_expert_ffn_validation(lib):
     assert _ffn(lib, ws=None) == E_WORKSPACE
     assert _ffn(lib, ws_bytes=100) == E_WORKSPACE
     assert _ffn(lib, ws=FAKE_MIS) == E_ALIGN
+
+
+def _moe(lib, T=1, H=2048, F=768, E=128, k=8, hidden=FAKE, router=ctypes.c_void_p(0x70000),
+         idx=ctypes.c_void_p(0x50000), w=ctypes.c_void_p(0x60000), out=ctypes.c_void_p(0x40000),
+         acc=0, ws=ctypes.c_void_p(0x80000), ws_bytes=1 << 30, gate=None, down=None):
+    gate = gate or _experts()
+    down = down or _experts(qtype=q3.Q6_K, stride=1290240)
+    return lib.q3moe_moe_ffn(hidden, T, H, F, E, k, router, gate, _experts(), down, idx, w, out,
+                             acc, ws, ws_bytes, None)
+
+
+def test_moe_ffn_validation(lib):
+    """The one-call route + expert FFN checks the union of both calls'
+    arguments, and its routing outputs for aliasing."""
+    assert _moe(lib, T=0) == OK
+    assert _moe(lib, H=2000) == E_SHAPE
+    assert _moe(lib, E=1025) == E_SHAPE
+    assert _moe(lib, k=9, E=8) == E_SHAPE
+    assert _moe(lib, acc=2) == E_SHAPE
+    assert _moe(lib, router=None) == E_NULL
+    assert _moe(lib, idx=None) == E_NULL
+    assert _moe(lib, w=None) == E_NULL
+    assert _moe(lib, gate=_experts(qtype=q3.Q6_K, stride=1 << 21)) == E_QTYPE
+    assert _moe(lib, router=FAKE_MIS) == E_ALIGN
+    assert _moe(lib, idx=ctypes.c_void_p(0x40000 + 64)) == E_ALIAS     # routing into out
+    assert _moe(lib, w=ctypes.c_void_p(0x50000 + 16)) == E_ALIAS       # weights over indices
+    assert _moe(lib, idx=ctypes.c_void_p(0x10000 + 32)) == E_ALIAS     # routing into hidden
+    assert _moe(lib, ws=None) == E_WORKSPACE
+    need = lib.q3moe_moe_ffn_workspace_bytes(1, 2048, 768, 128, 8)
+    assert need >= lib.q3moe_expert_ffn_workspace_bytes(1, 2048, 768, 128, 8) + \
+        lib.q3moe_route_workspace_bytes(1, 128)
+    assert _moe(lib, ws_bytes=need - 1) == E_WORKSPACE
+    assert _moe(lib, ws=FAKE_MIS) == E_ALIGN
 
 
 def _route(lib, T=1, H=2048, E=128, k=8, hidden=FAKE, router=FAKE, idx=FAKE, w=FAKE, ws=FAKE,

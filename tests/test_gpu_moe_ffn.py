@@ -1,0 +1,155 @@
+"""The one-call MoE block (q3moe_moe_ffn: route + expert FFN) vs the oracle.
+
+For at most 4 tokens at H = 2048 the whole block is one persistent kernel
+that routes inside (every workgroup computes a slice of the router logits,
+publishes it as tagged words and selects the top-k from all slices); other
+shapes run the route and expert-FFN kernels back to back.  Indices
+bit-exact, routing weights to 1e-6 relative, outputs within 1e-4 relative
+L2 per token.  Repeated calls through one workspace check that each call's
+tags keep it from reading an earlier call's partial results.
+"""
+import numpy as np
+import pytest
+import torch
+
+import sparse_moe_decode_q3moe_amd as q3
+from sparse_moe_decode_q3moe_amd import inputs as gen
+from parity import assert_indices_equal, assert_rows_close, experts_of, oracle_moe, say
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+CASES = {  # name: (shape, seed); the first five take the one-kernel path
+    "a3b_T1": (gen.QWEN3_30B_A3B, 41),
+    "a3b_T2": (gen.MoeShape(T=2, H=2048, E=128, k=8, F=768, down_qtype=gen.Q6_K), 42),
+    "a3b_q4k_down_T3": (gen.MoeShape(T=3, H=2048, E=128, k=8, F=768, down_qtype=gen.Q4_K), 43),
+    "a3b_T4": (gen.MoeShape(T=4, H=2048, E=128, k=8, F=768, down_qtype=gen.Q6_K), 44),
+    "E256_k4_F512_T2": (gen.MoeShape(T=2, H=2048, E=256, k=4, F=512, down_qtype=gen.Q6_K), 45),
+    "E64_k1_T1": (gen.MoeShape(T=1, H=2048, E=64, k=1, F=256, down_qtype=gen.Q4_K), 46),
+    # two launches: more tokens, other hidden sizes, more experts
+    "a3b_T5": (gen.MoeShape(T=5, H=2048, E=128, k=8, F=768, down_qtype=gen.Q6_K), 47),
+    "tiny_T4": (gen.TINY, 48),
+    "E300_T1": (gen.MoeShape(T=1, H=2048, E=300, k=8, F=256, down_qtype=gen.Q6_K), 49),
+    "prefill_T40": (gen.MoeShape(T=40, H=2048, E=128, k=8, F=768, down_qtype=gen.Q6_K), 50),
+}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device visible")
+    q3.library()
+
+
+@pytest.fixture(scope="module")
+def layers():
+    cache = {}
+
+    def get(name):
+        if name not in cache:
+            shape, seed = CASES[name]
+            cpu = gen.moe_layer(shape, seed)
+            x = gen.hidden_states(shape.T, shape.H, seed + 500)
+            cache[name] = (cpu, cpu.to(DEV), x)
+        return cache[name]
+    return get
+
+
+def _check(cpu, got, x, what, out=None, accumulate=False):
+    s = cpu.shape
+    ref_idx, ref_w, logits, ref = oracle_moe(cpu, x.numpy(), out=out, accumulate=accumulate)
+    o, idx, w = got
+    torch.cuda.synchronize()
+    assert_indices_equal(idx.cpu().numpy(), ref_idx, logits, s.k, what)
+    np.testing.assert_allclose(w.cpu().numpy(), ref_w, rtol=1e-6, atol=0)
+    return assert_rows_close(o.cpu().numpy(), ref, what=what)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_moe_ffn_parity(layers, name):
+    cpu, dev, x = layers(name)
+    s = cpu.shape
+    say(f"moe_ffn {name}: T={s.T} H={s.H} E={s.E} k={s.k} F={s.F} down={s.down_qtype}")
+    ws = torch.zeros(q3.q3moe_moe_ffn_workspace_bytes(s.T, s.H, s.F, s.E, s.k),
+                     dtype=torch.uint8, device=DEV)
+    got = q3.q3moe_moe_ffn(x.to(DEV), dev.router, s.k, *experts_of(dev), F=s.F, workspace=ws)
+    err = _check(cpu, got, x, name)
+    assert q3.expert_ffn_status(ws, s.T, s.H, s.F, s.E, s.k) == 0
+    say(f"  max rel L2 {err:.2e}")
+
+
+@pytest.mark.parametrize("name", ["a3b_T1", "a3b_q4k_down_T3", "tiny_T4"])
+def test_moe_ffn_accumulate(layers, name):
+    cpu, dev, x = layers(name)
+    s = cpu.shape
+    say(f"moe_ffn accumulate {name}")
+    prev = (x * 100.0).contiguous()
+    out = prev.to(DEV)
+    got = q3.q3moe_moe_ffn(x.to(DEV), dev.router, s.k, *experts_of(dev), F=s.F, out=out,
+                           accumulate=True)
+    _check(cpu, got, x, f"{name} accumulate", out=prev.numpy(), accumulate=True)
+
+
+def test_moe_ffn_workspace_reuse(layers):
+    """One zeroed workspace through a sequence of calls with different
+    inputs and token counts: every call must see only its own tagged words."""
+    cpu1, dev1, x1 = layers("a3b_T1")
+    cpu4, dev4, x4 = layers("a3b_T4")
+    s4 = cpu4.shape
+    ws = torch.zeros(q3.q3moe_moe_ffn_workspace_bytes(s4.T, s4.H, s4.F, s4.E, s4.k),
+                     dtype=torch.uint8, device=DEV)
+    g = gen.make_generator(77)
+    for i in range(6):
+        cpu, dev, x = (cpu1, dev1, x1) if i % 2 == 0 else (cpu4, dev4, x4)
+        if i >= 2:                                  # fresh activations, same weights
+            x = gen.normal_f32(tuple(x.shape), 1.0, g)
+        s = cpu.shape
+        say(f"workspace reuse call {i}: T={s.T}")
+        got = q3.q3moe_moe_ffn(x.to(DEV), dev.router, s.k, *experts_of(dev), F=s.F, workspace=ws)
+        _check(cpu, got, x, f"reuse call {i}")
+    assert q3.expert_ffn_status(ws, s4.T, s4.H, s4.F, s4.E, s4.k) == 0
+
+
+def test_moe_ffn_matches_two_calls(layers):
+    """The one-kernel block and the two entry points agree on the routing
+    and, to the last bits allowed by the summation orders, on the output."""
+    cpu, dev, x = layers("a3b_T2")
+    s = cpu.shape
+    say("moe_ffn vs route + expert_ffn")
+    xd = x.to(DEV)
+    out, idx, w = q3.q3moe_moe_ffn(xd, dev.router, s.k, *experts_of(dev), F=s.F)
+    idx2, w2 = q3.q3moe_route(xd, dev.router, s.k)
+    out2 = q3.q3moe_expert_ffn(xd, idx2, w2, *experts_of(dev), F=s.F)
+    torch.cuda.synchronize()
+    assert torch.equal(idx.cpu(), idx2.cpu())
+    np.testing.assert_allclose(w.cpu().numpy(), w2.cpu().numpy(), rtol=1e-6, atol=0)
+    assert_rows_close(out.cpu().numpy(), out2.cpu().numpy().astype(np.float64), what="two calls")
+
+
+def test_moe_ffn_routing_ties_and_specials(layers):
+    """In-kernel routing on exactly equal logits, on two logits that differ
+    by far less than an f32 ulp, and on a token whose input holds +inf (a
+    run of equal infinite logits): the oracle's choices (the larger logit
+    first, equal logits by the lower index)."""
+    cpu, dev, x = layers("a3b_T2")
+    s = cpu.shape
+    say("moe_ffn routing ties")
+    R = cpu.router.clone()
+    x1 = x.clone()
+    sgn = torch.sign(x1[0])
+    R[[5, 9, 30, 101]] = 0.01 * sgn                 # four identical top logits of token 0
+    R[77] = 0.01 * sgn
+    j = int(torch.argmax(x1[0].abs()))
+    R[77, j] += 1e-7 * sgn[j] / x1[0, j].abs()      # above them by ~1e-7 (an f32 ulp is ~2e-6)
+    x1[1, 0] = float("inf")                         # token 1: +inf logits wherever R[e, 0] > 0
+    lay = gen.MoeLayer(s, R, cpu.gate, cpu.up, cpu.down)
+    lay_dev = gen.MoeLayer(s, R.to(DEV), dev.gate, dev.up, dev.down)
+    out, idx, w = q3.q3moe_moe_ffn(x1.to(DEV), lay_dev.router, s.k, *experts_of(lay_dev), F=s.F)
+    torch.cuda.synchronize()
+    ref_idx, ref_w, logits, ref = oracle_moe(lay, x1.numpy())
+    got = idx.cpu().numpy()
+    assert ref_idx[0, :5].tolist() == [77, 5, 9, 30, 101], ref_idx[0]
+    assert np.array_equal(got, ref_idx), (got, ref_idx)
+    np.testing.assert_allclose(w.cpu().numpy(), ref_w, rtol=1e-6, atol=0)
+    assert_rows_close(out.cpu().numpy()[:1], ref[:1], what="ties, token 0")
