@@ -65,15 +65,16 @@ def parse():
 PMC_COPY_BYTES = 256 << 20
 PMC_STEPS = 16
 
-# HBM bytes per expert-FFN launch measured with the FETCH_SIZE and
+# HBM bytes per MoE-block launch measured with the FETCH_SIZE and
 # WRITE_SIZE counters (two rocprofv3 --pmc runs of `bench.py --pmc-pass`,
 # each scaled by what the counter reads for the calibration copy), summarised
 # in profiles/ffn_fused8_kernel_a3b_decode_b1_traffic.md.  The figure belongs
 # to the kernel sources it was measured on; when they change it is reported
 # as null until the counters are taken again.
-TRAFFIC_BYTES_PER_LAUNCH = 25_630_800
-TRAFFIC_SOURCES_SHA256 = "94d1cefbf3f42f35843992217ca78e7f6679856e36b5321d187896b40c19da39"
+TRAFFIC_BYTES_PER_LAUNCH = 26_813_932
+TRAFFIC_SOURCES_SHA256 = "0c793c3e22417d3925023d1632b8ca8168ed372667f99b3b8609c74a12a6d2d5"
 TRAFFIC_SOURCES = ("sparse_moe_decode_q3moe_amd/csrc/ffn_decode.hip",
+                   "sparse_moe_decode_q3moe_amd/csrc/route_common.h",
                    "sparse_moe_decode_q3moe_amd/csrc/device_common.h")
 
 
