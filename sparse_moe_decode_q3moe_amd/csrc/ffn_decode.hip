@@ -757,26 +757,38 @@ __device__ __forceinline__ void dn_unit_weights(const uint8_t* tile, const DnGeo
 }
 
 // n tagged words from src into LDS (their 32-bit payloads, dst[i] for word
-// i), once each carries `tag`.  Thread tid reads words tid + i * kThr with
-// device-scope 64-bit loads, so each load instruction of a wave covers 512
-// consecutive bytes; a wave re-reads its words until all of them carry the
-// tag.  A wait that runs out ORs `bit` into the status word.
-constexpr int kPollWords = 12;                         // words per thread and round
+// i), once each carries `tag`.  n is even and src 16-byte aligned: thread tid
+// reads word pairs tid + i * kThr with 16-byte device-scope loads (sc1, the
+// coherence of the compiler's device-scope atomic loads; a 16-byte load moves
+// a CU's share in fewer, wider requests than 8-byte atomics), so each load
+// instruction of a wave covers 1 KiB of consecutive words; a wave re-reads
+// its words until all of them carry the tag.  A wait that runs out ORs
+// `bit` into the status word.
+constexpr int kPollPairs = 6;                          // word pairs per thread and round
 template <int kThr>
 __device__ __forceinline__ void wait_tagged(const uint64_t* src, int n, uint32_t tag,
                                             uint32_t* dst, int tid, int32_t* status, int bit) {
-    for (int c0 = 0; c0 < n; c0 += kThr * kPollWords) {
-        uint64_t v[kPollWords];
+    const int np = n >> 1;
+    for (int c0 = 0; c0 < np; c0 += kThr * kPollPairs) {
+        u32x4_t v[kPollPairs];
         int spins = 0;
         while (true) {
+#pragma unroll
+            for (int i = 0; i < kPollPairs; ++i) {
+                const int pi = c0 + tid + i * kThr;
+                const uint64_t* p = src + 2 * (pi < np ? pi : np - 1);
+                asm volatile("global_load_dwordx4 %0, %1, off sc1" : "=v"(v[i]) : "v"(p) : "memory");
+            }
+            // the loads above are not known to the compiler: wait for them
+            // here, before any use of their registers
+            asm volatile("s_waitcnt vmcnt(0)"
+                         : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5])
+                         :
+                         : "memory");
             bool ok = true;
 #pragma unroll
-            for (int i = 0; i < kPollWords; ++i) {
-                const int wi = c0 + tid + i * kThr;
-                v[i] = __hip_atomic_load(src + (wi < n ? wi : n - 1), __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-                ok = ok && (wi >= n || (uint32_t)(v[i] >> 32) == tag);
-            }
+            for (int i = 0; i < kPollPairs; ++i)
+                ok = ok && (c0 + tid + i * kThr >= np || (v[i].y == tag && v[i].w == tag));
             if (__all(ok)) break;
             if (++spins > kSpinLimit) {
                 if (!ok) __hip_atomic_fetch_or(status, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -785,12 +797,13 @@ __device__ __forceinline__ void wait_tagged(const uint64_t* src, int n, uint32_t
             __builtin_amdgcn_s_sleep(1);
         }
 #pragma unroll
-        for (int i = 0; i < kPollWords; ++i) {
-            const int wi = c0 + tid + i * kThr;
-            if (wi < n) dst[wi] = (uint32_t)v[i];
+        for (int i = 0; i < kPollPairs; ++i) {
+            const int pi = c0 + tid + i * kThr;
+            if (pi < np) *reinterpret_cast<uint2*>(dst + 2 * pi) = make_uint2(v[i].x, v[i].z);
         }
     }
 }
+static_assert(kPollPairs == 6, "the wait above names each of its registers");
 
 // The activations of the T tokens as int8 pieces in LDS (layout at
 // kI8PieceBytes): thread tid converts values 4*tid .. 4*tid+3 of every token;

@@ -20,13 +20,14 @@ pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
 
-CASES = {  # name: (shape, seed); the first five take the one-kernel path
+CASES = {  # name: (shape, seed); the first seven take the one-kernel path
     "a3b_T1": (gen.QWEN3_30B_A3B, 41),
     "a3b_T2": (gen.MoeShape(T=2, H=2048, E=128, k=8, F=768, down_qtype=gen.Q6_K), 42),
     "a3b_q4k_down_T3": (gen.MoeShape(T=3, H=2048, E=128, k=8, F=768, down_qtype=gen.Q4_K), 43),
     "a3b_T4": (gen.MoeShape(T=4, H=2048, E=128, k=8, F=768, down_qtype=gen.Q6_K), 44),
     "E256_k4_F512_T2": (gen.MoeShape(T=2, H=2048, E=256, k=4, F=512, down_qtype=gen.Q6_K), 45),
     "E64_k1_T1": (gen.MoeShape(T=1, H=2048, E=64, k=1, F=256, down_qtype=gen.Q4_K), 46),
+    "E72_k6_T3": (gen.MoeShape(T=3, H=2048, E=72, k=6, F=512, down_qtype=gen.Q4_K), 51),
     # two launches: more tokens, other hidden sizes, more experts
     "a3b_T5": (gen.MoeShape(T=5, H=2048, E=128, k=8, F=768, down_qtype=gen.Q6_K), 47),
     "tiny_T4": (gen.TINY, 48),
