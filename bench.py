@@ -71,8 +71,8 @@ PMC_STEPS = 16
 # in profiles/ffn_fused8_kernel_a3b_decode_b1_traffic.md.  The figure belongs
 # to the kernel sources it was measured on; when they change it is reported
 # as null until the counters are taken again.
-TRAFFIC_BYTES_PER_LAUNCH = 26_813_932
-TRAFFIC_SOURCES_SHA256 = "0c793c3e22417d3925023d1632b8ca8168ed372667f99b3b8609c74a12a6d2d5"
+TRAFFIC_BYTES_PER_LAUNCH = 26_809_078
+TRAFFIC_SOURCES_SHA256 = "4d081af1e424ef0ae328e9b7f74f1cc0c96e3b09474d5f8accad2eaef503a7f1"
 TRAFFIC_SOURCES = ("sparse_moe_decode_q3moe_amd/csrc/ffn_decode.hip",
                    "sparse_moe_decode_q3moe_amd/csrc/route_common.h",
                    "sparse_moe_decode_q3moe_amd/csrc/device_common.h")
