@@ -72,7 +72,7 @@ PMC_STEPS = 16
 # to the kernel sources it was measured on; when they change it is reported
 # as null until the counters are taken again.
 TRAFFIC_BYTES_PER_LAUNCH = 26_809_078
-TRAFFIC_SOURCES_SHA256 = "4d081af1e424ef0ae328e9b7f74f1cc0c96e3b09474d5f8accad2eaef503a7f1"
+TRAFFIC_SOURCES_SHA256 = "c49f46334068c2b5d45b5f71beeb8f0a0c4069c58930f461a4ecef7041db77fa"
 TRAFFIC_SOURCES = ("sparse_moe_decode_q3moe_amd/csrc/ffn_decode.hip",
                    "sparse_moe_decode_q3moe_amd/csrc/route_common.h",
                    "sparse_moe_decode_q3moe_amd/csrc/device_common.h")

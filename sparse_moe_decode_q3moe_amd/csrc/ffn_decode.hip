@@ -1,7 +1,15 @@
 // Expert FFN for decode-sized batches (aprender issue #3714: "File facts"
 // fixes the expert layout, gap G3 the steps, G8 the device-side gather and
-// weighted accumulate).  Two kernels per call:
+// weighted accumulate).
 //
+// ffn_fused8_kernel (H = 2048, T <= 4, k <= 8): the whole expert FFN in one
+// persistent launch, optionally with the routing inside (the MoE block of
+// q3moe_moe_ffn); workgroups hand the router partial sums and h to each
+// other as tagged words.  Gate/up take the activations as three int8
+// pieces (exact int32 dot products); down uses f32 weights.  Described in
+// detail at the kernel.
+//
+// Other shapes, two kernels per call:
 //   gu_decode_kernel   one wave per task = (token-slot pair, R rows of the
 //                      selected expert's gate AND up matrices): direct
 //                      HBM->LDS loads of both R-row tiles, dequantise in
@@ -12,13 +20,12 @@
 //                      those slots' h pieces, dequantises, multiplies by the
 //                      routing weight, and the workgroup sums the slots in
 //                      slot order (deterministic, no atomics).
+//   Weights as exact small integers (bf16 128 + q); the gate/up input as
+//   three bf16 pieces (hi + mid + lo) and h as two (hi + lo);
+//   v_dot2_f32_bf16 with f32 accumulation; the per-block scales, the Q4_K
+//   min term and the integer offsets are applied per 16/32 group in f32.
 //
-// Weights are never repacked: tiles are read in place at base + e*stride
-// with 16-byte coalesced direct-to-LDS loads, all issued before any wait.
-// Arithmetic: weights as exact small integers (bf16 128 + q); the gate/up
-// input as three bf16 pieces (hi + mid + lo) and h as two (hi + lo);
-// v_dot2_f32_bf16 with f32 accumulation; the per-block scales, the Q4_K min
-// term and the integer offsets are applied per 16/32 group in f32.
+// Weights are never repacked: tiles are read in place at base + e*stride.
 #include <atomic>
 
 #include "device_common.h"
