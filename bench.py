@@ -55,6 +55,8 @@ def parse():
                     help="skip the 512-token prefill measurement")
     ap.add_argument("--no-layer", action="store_true",
                     help="skip the full decoder-layer measurement (batch 1 and 16)")
+    ap.add_argument("--no-stack", action="store_true",
+                    help="skip the 48-layer stacked decode measurement")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="for hardware-counter runs: a few eager steps (no graph), then one "
                          "device-to-device copy of PMC_COPY_BYTES that calibrates the "
@@ -275,6 +277,9 @@ def main():
     if not args.no_layer:
         result["decoder_layer"] = decoder_bench(torch, q3, gen, layers, experts, shape, dev)
 
+    if not args.no_stack:
+        result["stack_48"] = stack_bench(torch, q3, gen, shape, dev)
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, torch, gen, layers, xs, outs, shape)
 
@@ -396,8 +401,6 @@ def decoder_bench(torch, q3, gen, layers, experts, shape, dev):
         vv = torch.empty((B, nkv * D), device=dev)
         ao = torch.empty((B, nq, D), device=dev)
         x1 = torch.empty((B, H), device=dev)
-        hn = torch.empty((B, H), device=dev)
-        out = torch.empty((B, H), device=dev)
         idx = torch.empty((B, k), dtype=torch.int32, device=dev)
         wts = torch.empty((B, k), device=dev)
         ws_a = torch.empty(q3.q3moe_gqa_attention_workspace_bytes(B, nq, nkv, D, S), dtype=torch.uint8, device=dev)
@@ -419,12 +422,13 @@ def decoder_bench(torch, q3, gen, layers, experts, shape, dev):
             q3.q3moe_bf16_gemv(A.wo, ao.view(B, nq * D), out=x1, accumulate=True)
 
         def layer(i):
+            # attention, then x1 += MoE(RMSNorm(x1)) in place: the
+            # post-attention norm runs inside the MoE block's kernel
             attention(i)
             L = layers[i % len(layers)]
-            q3.q3moe_rmsnorm(x1, atts[i % ncopies].post_norm, s_.eps, out=hn)
-            out.copy_(x1)
-            q3.q3moe_moe_ffn(hn, L.router, k, *experts[i % len(experts)], F=F, out=out, accumulate=True,
-                             topk_idx=idx, topk_w=wts, workspace=ws_m)
+            q3.q3moe_moe_ffn_prenorm(x1, atts[i % ncopies].post_norm, s_.eps, L.router, k,
+                                     *experts[i % len(experts)], F=F, out=x1, accumulate=True,
+                                     topk_idx=idx, topk_w=wts, workspace=ws_m)
 
         n = 16
         for i in range(n):
@@ -469,6 +473,97 @@ def decoder_bench(torch, q3, gen, layers, experts, shape, dev):
         }
         del graphs, atts, caches
         torch.cuda.empty_cache()
+    return res
+
+
+STACK_LAYERS = 48
+STACK_TOKENS = 8
+
+
+def stack_bench(torch, q3, gen, shape, dev):
+    """48 stacked MoE layers at the same shape, batch-1 decode: down Q6_K in
+    layers 0-23 and Q4_K in 24-47 (17.55 GB of seeded expert weights
+    resident in HBM, far beyond the 256 MB Infinity Cache, so nothing is
+    rotated).  Between layers the residual stream is x <- x + MoE(RMSNorm(x))
+    with unit gain and eps 1e-6: per layer one q3moe_moe_ffn_prenorm call
+    (norm, routing and expert FFN in one kernel, updating x in place); the
+    same stack with the norm as its own launch is timed beside it.  A token starts from
+    its own seeded hidden vector and passes through all 48 layers; the graph
+    holds STACK_TOKENS such tokens.  Reported: per-token latency, tokens/s,
+    and the algorithmic HBM bytes per token (router + the 8 selected
+    experts of every layer + activations) over that time."""
+    H, E, k, F = shape.H, shape.E, shape.k, shape.F
+    EPS = 1e-6
+    stack = []
+    for l in range(STACK_LAYERS):
+        s_l = gen.MoeShape(T=1, H=H, E=E, k=k, F=F, down_qtype=gen.stack_down_qtype(l))
+        L = gen.moe_layer(s_l, 500 + l, device=dev)
+        stack.append((L.router, q3.Experts(L.gate, gen.Q4_K), q3.Experts(L.up, gen.Q4_K),
+                      q3.Experts(L.down, s_l.down_qtype), L))
+    torch.cuda.synchronize()
+    x0 = gen.hidden_states(STACK_TOKENS, H, 11, device=dev).view(STACK_TOKENS, 1, H).contiguous()
+    x = torch.empty((1, H), device=dev)
+    xn = torch.empty((1, H), device=dev)
+    ones = torch.ones(H, device=dev)
+    idx = torch.empty((1, k), dtype=torch.int32, device=dev)
+    wts = torch.empty((1, k), dtype=torch.float32, device=dev)
+    ws = torch.zeros(q3.q3moe_moe_ffn_workspace_bytes(1, H, F, E, k), dtype=torch.uint8, device=dev)
+
+    def token(i):                                  # one call per layer, in place on x
+        x.copy_(x0[i])
+        for router, g_, u_, d_, _ in stack:
+            q3.q3moe_moe_ffn_prenorm(x, ones, EPS, router, k, g_, u_, d_, F=F, out=x,
+                                     accumulate=True, topk_idx=idx, topk_w=wts, workspace=ws)
+
+    def token_two_calls(i):                        # the norm as its own launch
+        x.copy_(x0[i])
+        for router, g_, u_, d_, _ in stack:
+            q3.q3moe_rmsnorm(x, ones, EPS, out=xn)
+            q3.q3moe_moe_ffn(xn, router, k, g_, u_, d_, F=F, out=x, accumulate=True,
+                             topk_idx=idx, topk_w=wts, workspace=ws)
+
+    def time_tokens(fn):
+        for i in range(STACK_TOKENS):
+            fn(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(STACK_TOKENS):
+                fn(i)
+        g.replay()
+        torch.cuda.synchronize()
+        reps = 12
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        del g
+        return a.elapsed_time(b) * 1000.0 / (reps * STACK_TOKENS)
+
+    two_us = time_tokens(token_two_calls)
+    tok_us = time_tokens(token)
+    finite = bool(torch.isfinite(x).all().item())
+    expert_bytes = sum(k * (2 * shape.gate_stride + L.down[0].numel()) for *_, L in stack)
+    tok_bytes = expert_bytes + STACK_LAYERS * (E * H * 4 + 3 * H * 4 * 2)
+    res = {
+        "layers": STACK_LAYERS,
+        "resident_expert_bytes": int(sum(L.gate.numel() + L.up.numel() + L.down.numel()
+                                         for *_, L in stack)),
+        "token_latency_us": round(tok_us, 2),
+        "tokens_per_s": round(1e6 / tok_us, 1),
+        "layer_us": round(tok_us / STACK_LAYERS, 3),
+        "token_hbm_bytes": int(tok_bytes),
+        "hbm_gbps": round(tok_bytes / (tok_us * 1e-6) / 1e9, 1),
+        "hbm_frac": round(tok_bytes / (tok_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+        "output_finite": finite,
+        "note": "per layer one q3moe_moe_ffn_prenorm call (RMSNorm with unit gain inside the "
+                "MoE block's kernel), updating x in place",
+        "norm_as_own_launch_token_us": round(two_us, 2),
+    }
+    del stack
+    torch.cuda.empty_cache()
     return res
 
 

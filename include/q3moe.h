@@ -206,6 +206,31 @@ q3moe_status q3moe_moe_ffn(const float *hidden, int64_t T, int64_t H, int64_t F,
                            int32_t *topk_idx, float *topk_w, float *out, int32_t accumulate,
                            void *workspace, size_t workspace_bytes, void *stream);
 
+/* ------------------------------------------------- MoE block after RMSNorm --
+ * The MoE block of a pre-norm decoder layer: its input is the token's hidden
+ * row x normalised as
+ *   xn = norm_gain * x / sqrt(mean(x^2) + eps)
+ * (the post-attention RMSNorm that feeds the sparse MoE FFN in the Qwen3-MoE
+ * layer of aprender issue #3714, "File facts" and gap G3, and the norm between
+ * stacked layers), then exactly q3moe_moe_ffn on xn: out = [out +] MoE(xn),
+ * routing outputs in topk_idx / topk_w.  out may be hidden itself: with
+ * accumulate = 1 that is the residual update x += MoE(RMSNorm(x)) in one
+ * call.  Any other overlap of out with hidden, topk_idx, topk_w or norm_gain
+ * is E_ALIAS.  The squares are summed in double and each xn value formed in
+ * double and rounded once to f32, as q3moe_rmsnorm does.
+ * For the one-kernel shapes of q3moe_moe_ffn the norm runs inside that
+ * kernel (every workgroup normalises the rows it reads); other shapes run
+ * q3moe_rmsnorm into the workspace first.
+ * norm_gain: H f32 values, 16-byte aligned; eps >= 0 and finite.
+ * workspace: as for q3moe_moe_ffn (the same size query).
+ * Errors: E_NULL, E_SHAPE, E_QTYPE, E_ALIGN, E_WORKSPACE, E_ALIAS, E_HIP. */
+q3moe_status q3moe_moe_ffn_prenorm(const float *hidden, int64_t T, int64_t H, int64_t F,
+                                   int32_t E, int32_t top_k, const float *norm_gain, float eps,
+                                   const float *router, q3moe_experts gate, q3moe_experts up,
+                                   q3moe_experts down, int32_t *topk_idx, float *topk_w,
+                                   float *out, int32_t accumulate, void *workspace,
+                                   size_t workspace_bytes, void *stream);
+
 /* ------------------------------------------------------ attention prologue --
  * In place on q [T x n_q_heads x head_dim] and k [T x n_kv_heads x head_dim]
  * (f32, row-major): for every head slice, RMSNorm with the gain vector shared
@@ -229,8 +254,9 @@ q3moe_status q3moe_attn_prologue(float *q, float *k, int64_t T, int32_t n_q_head
 
 /* --------------------------------------------------------------- RMSNorm --
  * out[t] = gain * x[t] / sqrt(mean(x[t]^2) + eps) for x [T x n] f32; the
- * per-layer input / post-attention norm of the decoder layer.  out may equal
- * x (in place) but must not partially overlap it.
+ * per-layer input / post-attention norm of the decoder layer.  The squares
+ * are summed in double and each output formed in double and rounded once to
+ * f32.  out may equal x (in place) but must not partially overlap it.
  * Limits: 1 <= n <= 65536, eps >= 0.
  * Errors: E_NULL, E_SHAPE, E_ALIAS, E_HIP. */
 q3moe_status q3moe_rmsnorm(const float *x, int64_t T, int64_t n, const float *gain,

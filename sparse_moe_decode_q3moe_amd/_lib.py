@@ -24,7 +24,7 @@ EXPORTS = (
     "q3moe_expert_ffn_workspace_bytes", "q3moe_expert_ffn_status_offset", "q3moe_expert_ffn",
     "q3moe_attn_prologue", "q3moe_rmsnorm", "q3moe_bf16_gemv", "q3moe_kv_write",
     "q3moe_gqa_attention_workspace_bytes", "q3moe_gqa_attention",
-    "q3moe_moe_ffn_workspace_bytes", "q3moe_moe_ffn",
+    "q3moe_moe_ffn_workspace_bytes", "q3moe_moe_ffn", "q3moe_moe_ffn_prenorm",
 )
 
 
@@ -61,6 +61,9 @@ _SIGS = {
     "q3moe_moe_ffn_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64, _I32, _I32]),
     "q3moe_moe_ffn": (_I32, [_P, _I64, _I64, _I64, _I32, _I32, _P, _Experts, _Experts, _Experts,
                              _P, _P, _P, _I32, _P, ctypes.c_size_t, _P]),
+    "q3moe_moe_ffn_prenorm": (_I32, [_P, _I64, _I64, _I64, _I32, _I32, _P, _F, _P, _Experts,
+                                     _Experts, _Experts, _P, _P, _P, _I32, _P, ctypes.c_size_t,
+                                     _P]),
 }
 
 _lib = None
@@ -254,6 +257,43 @@ def q3moe_moe_ffn(hidden: torch.Tensor, router: torch.Tensor, top_k: int, gate: 
     _check("q3moe_moe_ffn", library().q3moe_moe_ffn(
         _ptr(hidden), T, H, F, E, top_k, _ptr(router), gate.c(), up.c(), down.c(),
         _ptr(topk_idx), _ptr(topk_w), _ptr(out), 1 if accumulate else 0,
+        _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return out, topk_idx, topk_w
+
+
+def q3moe_moe_ffn_prenorm(hidden: torch.Tensor, norm_gain: torch.Tensor, eps: float,
+                          router: torch.Tensor, top_k: int, gate: Experts, up: Experts,
+                          down: Experts, F: int, out: Optional[torch.Tensor] = None,
+                          accumulate: bool = False, topk_idx: Optional[torch.Tensor] = None,
+                          topk_w: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None, stream=None):
+    """RMSNorm of hidden (gain, eps), then the MoE block on it; out may be
+    hidden itself (with accumulate: x += MoE(RMSNorm(x))).  -> (out,
+    topk_idx, topk_w), each allocated if None."""
+    _need(hidden, "hidden", torch.float32, 2)
+    _need(norm_gain, "norm_gain", torch.float32, 1)
+    _need(router, "router", torch.float32, 2)
+    T, H = hidden.shape
+    E = router.shape[0]
+    if router.shape[1] != H or norm_gain.numel() != H:
+        raise ValueError("router must be [E, H] and norm_gain [H]")
+    dev = hidden.device
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate=True needs an existing out tensor")
+        out = torch.empty((T, H), dtype=torch.float32, device=dev)
+    if topk_idx is None:
+        topk_idx = torch.empty((T, top_k), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((T, top_k), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, 2)
+    _need(topk_idx, "topk_idx", torch.int32, 2)
+    _need(topk_w, "topk_w", torch.float32, 2)
+    nbytes = q3moe_moe_ffn_workspace_bytes(T, H, F, E, top_k)
+    ws = _workspace(nbytes, dev, workspace)
+    _check("q3moe_moe_ffn_prenorm", library().q3moe_moe_ffn_prenorm(
+        _ptr(hidden), T, H, F, E, top_k, _ptr(norm_gain), eps, _ptr(router), gate.c(), up.c(),
+        down.c(), _ptr(topk_idx), _ptr(topk_w), _ptr(out), 1 if accumulate else 0,
         _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
     return out, topk_idx, topk_w
 

@@ -140,32 +140,47 @@ size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
 }  // namespace
 
 size_t q3moe_moe_ffn_workspace_bytes(int64_t T, int64_t H, int64_t F, int32_t E, int32_t top_k) {
+    // expert-FFN workspace, route workspace, the fused kernel's tagged
+    // router words, and (for the pre-norm form on the multi-kernel path) the
+    // normalised input rows
     return round256(q3moe::expert_ffn_workspace_bytes(T, H, F, E, top_k)) +
-           round256(q3moe::route_workspace_bytes(T, E)) + q3moe::moe_route_words_bytes(T, E);
+           round256(q3moe::route_workspace_bytes(T, E)) + round256(q3moe::moe_route_words_bytes(T, E)) +
+           (size_t)(T > 0 ? T : 0) * (size_t)(H > 0 ? H : 0) * sizeof(float);
 }
 
-q3moe_status q3moe_moe_ffn(const float* hidden, int64_t T, int64_t H, int64_t F, int32_t E,
-                           int32_t top_k, const float* router, q3moe_experts gate,
-                           q3moe_experts up, q3moe_experts down, int32_t* topk_idx,
-                           float* topk_w, float* out, int32_t accumulate, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+namespace {
+
+// The MoE block, with (norm_gain != null) or without the input RMSNorm.
+// With the norm, out may be hidden itself; any other overlap is rejected.
+q3moe_status moe_ffn_impl(const float* hidden, int64_t T, int64_t H, int64_t F, int32_t E,
+                          int32_t top_k, bool want_norm, const float* norm_gain, float eps,
+                          const float* router,
+                          q3moe_experts gate, q3moe_experts up, q3moe_experts down,
+                          int32_t* topk_idx, float* topk_w, float* out, int32_t accumulate,
+                          void* workspace, size_t workspace_bytes, void* stream) {
     if (T < 0 || H % 256 || F % 256 || H < 256 || H > 4096 || F < 256 || F > 1536 || E < 1 ||
         E > q3moe::kMaxExperts || top_k < 1 || top_k > q3moe::kMaxTopK || top_k > E ||
-        (accumulate != 0 && accumulate != 1) || T * top_k > 0x7fffffff)
+        (accumulate != 0 && accumulate != 1) || T * top_k > 0x7fffffff || !(eps >= 0.0f) ||
+        !(eps <= 3.4028235e38f))
         return Q3MOE_E_SHAPE;
     if (T == 0) return Q3MOE_OK;
-    if (!hidden || !router || !topk_idx || !topk_w || !out) return Q3MOE_E_NULL;
+    if (!hidden || !router || !topk_idx || !topk_w || !out || (want_norm && !norm_gain))
+        return Q3MOE_E_NULL;
     ExpertTensor g, u, d;
     q3moe_status st;
     if ((st = check_experts(gate, F, H, false, g)) != Q3MOE_OK) return st;
     if ((st = check_experts(up, F, H, false, u)) != Q3MOE_OK) return st;
     if ((st = check_experts(down, H, F, true, d)) != Q3MOE_OK) return st;
-    if (!aligned16(hidden) || !aligned16(router) || !aligned16(out)) return Q3MOE_E_ALIGN;
+    if (!aligned16(hidden) || !aligned16(router) || !aligned16(out) ||
+        (norm_gain && !aligned16(norm_gain)))
+        return Q3MOE_E_ALIGN;
     const size_t act = (size_t)T * (size_t)H * sizeof(float);
     const size_t rt = (size_t)T * (size_t)top_k * 4;
-    if (overlaps(hidden, act, out, act) || overlaps(topk_idx, rt, out, act) ||
+    const bool in_place = norm_gain && static_cast<const void*>(hidden) == static_cast<const void*>(out);
+    if ((!in_place && overlaps(hidden, act, out, act)) || overlaps(topk_idx, rt, out, act) ||
         overlaps(topk_w, rt, out, act) || overlaps(topk_idx, rt, topk_w, rt) ||
-        overlaps(topk_idx, rt, hidden, act) || overlaps(topk_w, rt, hidden, act))
+        overlaps(topk_idx, rt, hidden, act) || overlaps(topk_w, rt, hidden, act) ||
+        (norm_gain && overlaps(norm_gain, (size_t)H * sizeof(float), out, act)))
         return Q3MOE_E_ALIAS;
     if (!workspace || workspace_bytes < q3moe_moe_ffn_workspace_bytes(T, H, F, E, top_k))
         return Q3MOE_E_WORKSPACE;
@@ -173,14 +188,43 @@ q3moe_status q3moe_moe_ffn(const float* hidden, int64_t T, int64_t H, int64_t F,
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     uint8_t* ws_route = ws + round256(q3moe::expert_ffn_workspace_bytes(T, H, F, E, top_k));
     uint8_t* ws_words = ws_route + round256(q3moe::route_workspace_bytes(T, E));
+    float* ws_norm = reinterpret_cast<float*>(ws_words + round256(q3moe::moe_route_words_bytes(T, E)));
     const hipStream_t s = as_stream(stream);
     if (q3moe::moe_decode_fused(T, H, F, E, top_k, d.qtype))
         return from_hip(q3moe::launch_moe_decode(hidden, T, H, F, E, top_k, router, topk_idx, topk_w,
-                                                 g, u, d, out, accumulate, ws, ws_words, s));
-    hipError_t e = q3moe::launch_route(hidden, T, H, router, E, top_k, topk_idx, topk_w, ws_route, s);
+                                                 g, u, d, out, accumulate, ws, ws_words, norm_gain,
+                                                 eps, s));
+    const float* x = hidden;
+    if (norm_gain) {                          // normalised rows into the workspace first
+        hipError_t e = q3moe::launch_rmsnorm(hidden, T, H, norm_gain, eps, ws_norm, s);
+        if (e != hipSuccess) return from_hip(e);
+        x = ws_norm;
+    }
+    hipError_t e = q3moe::launch_route(x, T, H, router, E, top_k, topk_idx, topk_w, ws_route, s);
     if (e != hipSuccess) return from_hip(e);
-    return from_hip(q3moe::launch_expert_ffn(hidden, T, H, F, E, top_k, topk_idx, topk_w, g, u, d,
+    return from_hip(q3moe::launch_expert_ffn(x, T, H, F, E, top_k, topk_idx, topk_w, g, u, d,
                                              out, accumulate, ws, s));
+}
+
+}  // namespace
+
+q3moe_status q3moe_moe_ffn(const float* hidden, int64_t T, int64_t H, int64_t F, int32_t E,
+                           int32_t top_k, const float* router, q3moe_experts gate,
+                           q3moe_experts up, q3moe_experts down, int32_t* topk_idx,
+                           float* topk_w, float* out, int32_t accumulate, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    return moe_ffn_impl(hidden, T, H, F, E, top_k, false, nullptr, 0.0f, router, gate, up, down, topk_idx,
+                        topk_w, out, accumulate, workspace, workspace_bytes, stream);
+}
+
+q3moe_status q3moe_moe_ffn_prenorm(const float* hidden, int64_t T, int64_t H, int64_t F,
+                                   int32_t E, int32_t top_k, const float* norm_gain, float eps,
+                                   const float* router, q3moe_experts gate, q3moe_experts up,
+                                   q3moe_experts down, int32_t* topk_idx, float* topk_w,
+                                   float* out, int32_t accumulate, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+    return moe_ffn_impl(hidden, T, H, F, E, top_k, true, norm_gain, eps, router, gate, up, down, topk_idx,
+                        topk_w, out, accumulate, workspace, workspace_bytes, stream);
 }
 
 q3moe_status q3moe_attn_prologue(float* q, float* k, int64_t T, int32_t n_q_heads,

@@ -884,15 +884,22 @@ __device__ __forceinline__ int lane_value(int v, int src) { return __builtin_amd
 // workspace's synchronisation header: its counters are zero when the kernel
 // starts and zero again when it ends.  The routing entries (T*k <= 32) live
 // in one register per lane of every wave and are read with readlane.
+// With the routing inside, norm_gain (if not null) applies the input
+// RMSNorm first: the FFN input is gain * x / sqrt(mean(x^2) + eps) of the
+// token's hidden row x.  hidden and out may then be the same buffer (the
+// residual update x += MoE(RMSNorm(x))): every workgroup has read all of
+// hidden before it publishes its router partials, and no workgroup writes
+// out before it has seen all of them.  Hence neither pointer is restrict.
 template <bool kRoute>
 __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
-    const float* __restrict__ hidden, int64_t T, int64_t F, int32_t E, int32_t k,
+    const float* hidden, int64_t T, int64_t F, int32_t E, int32_t k,
     const int32_t* __restrict__ idx, const float* __restrict__ w,
     const uint8_t* __restrict__ gbase, int64_t gstride, const uint8_t* __restrict__ ubase,
     int64_t ustride, const uint8_t* __restrict__ dbase, int32_t dqtype, int64_t dstride,
-    float* __restrict__ out, int accumulate, uint64_t* __restrict__ hbuf,
+    float* out, int accumulate, uint64_t* __restrict__ hbuf,
     int32_t* __restrict__ sync, const float* __restrict__ router, int32_t P,
-    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, uint64_t* __restrict__ rbuf) {
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, uint64_t* __restrict__ rbuf,
+    const float* __restrict__ norm_gain, float eps) {
     using G = GuTask<kFzNB>;
     constexpr int kThr = kFzWaves * kWave;
     extern __shared__ __align__(16) uint8_t smem[];
@@ -967,20 +974,58 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
         float* r_w = reinterpret_cast<float*>(r_idx + kFzMaxTokens * kFzMaxSlots);
         double* rp = reinterpret_cast<double*>(smem + L.rp_off);      // [wave][token]
         uint32_t* rl = reinterpret_cast<uint32_t*>(smem + L.rl_off);  // [token][unit] f64 halves
-        const int U = E * P, HP = (int)(G::H / P), nq = HP / 4;
-        // (a) this workgroup's router unit(s): expert u / P, column part u % P;
-        // f64 sums of the exact f32 products, published as two tagged words
+        const int U = E * P, HP = (int)(G::H / P);
+        // (a0) thread tid holds values 4*tid .. 4*tid+3 of every token's
+        // input (H = 2048 = 4 x 512 threads); with the norm they become
+        // gain * x * inv, inv = 1 / sqrt(mean(x^2) + eps), the squares summed
+        // in double and each value formed in double and rounded once.
+        float4 xv[kFzMaxTokens];
+#pragma unroll
+        for (int t = 0; t < kFzMaxTokens; ++t)
+            xv[t] = reinterpret_cast<const float4*>(hidden + (t < T ? t : T - 1) * G::H)[tid];
+        if (norm_gain) {
+            const float4 g4 = reinterpret_cast<const float4*>(norm_gain)[tid];
+#pragma unroll
+            for (int t = 0; t < kFzMaxTokens; ++t) {
+                if (t < T) {
+                    const float4 v = xv[t];
+                    double ss = (double)v.x * v.x;
+                    ss = fma((double)v.y, (double)v.y, ss);
+                    ss = fma((double)v.z, (double)v.z, ss);
+                    ss = fma((double)v.w, (double)v.w, ss);
+                    const double sw = wave_sum_dpp_f64(ss);
+                    if (lane == 0) rp[wave * kFzMaxTokens + t] = sw;
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int t = 0; t < kFzMaxTokens; ++t) {
+                if (t < T) {
+                    double tot = 0.0;
+#pragma unroll
+                    for (int wv = 0; wv < kFzWaves; ++wv) tot += rp[wv * kFzMaxTokens + t];
+                    const double inv = 1.0 / sqrt(tot / (double)G::H + (double)eps);
+                    const float4 v = xv[t];
+                    xv[t] = make_float4((float)((double)g4.x * v.x * inv), (float)((double)g4.y * v.y * inv),
+                                        (float)((double)g4.z * v.z * inv), (float)((double)g4.w * v.w * inv));
+                }
+            }
+            __syncthreads();                  // rp is reused by the router sums
+        }
+        // (a) this workgroup's router unit(s): expert u / P, column part u % P
+        // (the threads holding that part's columns); f64 sums of the exact
+        // f32 products, published as two tagged words
         for (int u = wg; u < U; u += grid) {
-            const int e = u / P, c0 = (u % P) * HP;
+            const int e = u / P, part = u % P;
             double acc[kFzMaxTokens];
 #pragma unroll
             for (int t = 0; t < kFzMaxTokens; ++t) acc[t] = 0.0;
-            if (tid < nq) {
-                const float4 r = reinterpret_cast<const float4*>(router + (int64_t)e * G::H + c0)[tid];
+            if ((4 * tid) / HP == part) {
+                const float4 r = reinterpret_cast<const float4*>(router + (int64_t)e * G::H)[tid];
 #pragma unroll
                 for (int t = 0; t < kFzMaxTokens; ++t) {
                     if (t < T) {
-                        const float4 x4 = reinterpret_cast<const float4*>(hidden + t * G::H + c0)[tid];
+                        const float4 x4 = xv[t];
                         double a = fma((double)r.x, (double)x4.x, 0.0);
                         a = fma((double)r.y, (double)x4.y, a);
                         a = fma((double)r.z, (double)x4.z, a);
@@ -1009,8 +1054,9 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
             }
             __syncthreads();
         }
-        // the activation pieces, while the partial logits travel
-        if (is_gu) build_pieces(false, 0);
+        // the activation pieces, by every wave, while the partial logits
+        // travel (thread tid converts the values it holds)
+        build_x_pieces<kFzMaxTokens>(xv, T, smem, tid);
         // (b) every partial logit of every token, then (c) the top-k of token
         // t on wave t; logit = the sum of the expert's parts in part order
         wait_tagged<kThr>(rbuf, (int)T * U * 2, tag, rl, tid, status, 4);
@@ -1269,7 +1315,7 @@ hipError_t launch_fused8(const float* hidden, int64_t T, int64_t F, int32_t E, i
                          const ExpertTensor& up, const ExpertTensor& down, float* out,
                          int accumulate, uint8_t* hp, int32_t* sync, int grid,
                          const float* router, int P, int32_t* topk_idx, float* topk_w,
-                         uint64_t* rbuf, hipStream_t stream) {
+                         uint64_t* rbuf, const float* norm_gain, float eps, hipStream_t stream) {
     const FusedLds L = fused_lds(T, F, down.qtype);
     static LdsLimit lds_set;
     hipError_t err = ensure_lds(reinterpret_cast<const void*>(ffn_fused8_kernel<kRoute>), lds_set, L.total);
@@ -1278,7 +1324,7 @@ hipError_t launch_fused8(const float* hidden, int64_t T, int64_t F, int32_t E, i
                        (size_t)L.total, stream, hidden, T, F, E, k, idx, w, gate.base, gate.stride,
                        up.base, up.stride, down.base, down.qtype, down.stride, out, accumulate,
                        reinterpret_cast<uint64_t*>(hp), sync, router, (int32_t)P, topk_idx, topk_w,
-                       rbuf);
+                       rbuf, norm_gain, eps);
     return hipGetLastError();
 }
 
@@ -1314,7 +1360,8 @@ hipError_t launch_decode_nb(const float* hidden, int64_t T, int64_t H, int64_t F
         const int grid = fused_grid(T, H, F, k, down.qtype);
         if (grid > 0)
             return launch_fused8<false>(hidden, T, F, E, k, idx, w, gate, up, down, out, accumulate,
-                                        hp, sync, grid, nullptr, 1, nullptr, nullptr, nullptr, stream);
+                                        hp, sync, grid, nullptr, 1, nullptr, nullptr, nullptr, nullptr,
+                                        0.f, stream);
     }
     hipError_t err = launch_gu<NB>(hidden, T, F, E, k, idx, gate, up, hp, stream);
     if (err != hipSuccess) return err;
@@ -1358,14 +1405,14 @@ hipError_t launch_moe_decode(const float* hidden, int64_t T, int64_t H, int64_t 
                              int32_t k, const float* router, int32_t* topk_idx, float* topk_w,
                              const ExpertTensor& gate, const ExpertTensor& up,
                              const ExpertTensor& down, float* out, int accumulate, void* ffn_ws,
-                             void* route_words, hipStream_t stream) {
+                             void* route_words, const float* norm_gain, float eps, hipStream_t stream) {
     const int grid = fused_grid(T, H, F, k, down.qtype);
     if (grid <= 0 || E > kFzRouteNper * kWave) return hipErrorInvalidValue;
     int32_t* sync = static_cast<int32_t*>(ffn_ws);
     uint8_t* hp = static_cast<uint8_t*>(ffn_ws) + kFfnSyncBytes;
     return launch_fused8<true>(hidden, T, F, E, k, nullptr, nullptr, gate, up, down, out, accumulate,
                                hp, sync, grid, router, route_parts(E, grid), topk_idx, topk_w,
-                               static_cast<uint64_t*>(route_words), stream);
+                               static_cast<uint64_t*>(route_words), norm_gain, eps, stream);
 }
 
 }  // namespace q3moe

@@ -79,14 +79,17 @@ hipError_t launch_decode_ffn(const float* hidden, int64_t T, int64_t H, int64_t 
 // Route + expert FFN of a few tokens in one launch (H = 2048, T <= 4, k <= 8,
 // E <= 256): moe_decode_fused tells whether the shape qualifies.  ffn_ws is
 // an expert-FFN workspace, route_words moe_route_words_bytes(T, E) of zeroed
-// memory that the kernel's routing step uses for its tagged partial logits.
+// memory that the kernel's routing step uses for its tagged partial logits;
+// norm_gain (or null) applies the input RMSNorm inside the kernel, and then
+// hidden may equal out.
 bool moe_decode_fused(int64_t T, int64_t H, int64_t F, int32_t E, int32_t k, int32_t dqtype);
 size_t moe_route_words_bytes(int64_t T, int32_t E);
 hipError_t launch_moe_decode(const float* hidden, int64_t T, int64_t H, int64_t F, int32_t E,
                              int32_t k, const float* router, int32_t* topk_idx, float* topk_w,
                              const ExpertTensor& gate, const ExpertTensor& up,
                              const ExpertTensor& down, float* out, int accumulate, void* ffn_ws,
-                             void* route_words, hipStream_t stream);
+                             void* route_words, const float* norm_gain, float eps,
+                             hipStream_t stream);
 
 // ffn.hip: dispatch, and the generic path for any H, F multiple of 256
 size_t expert_ffn_workspace_bytes(int64_t T, int64_t H, int64_t F, int32_t E, int32_t k);

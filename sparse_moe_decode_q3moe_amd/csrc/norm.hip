@@ -12,23 +12,26 @@ namespace {
 
 constexpr int kNormThreads = 256;
 
-// One workgroup per row: out = gain * x / sqrt(mean(x^2) + eps).
-__global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(const float* __restrict__ x,
-                                                               int64_t n,
+// One workgroup per row: out = gain * x / sqrt(mean(x^2) + eps), the
+// squares summed in double (f32 squares are exact there) and each output
+// formed in double and rounded once to f32.  x and out may be the same row:
+// after the barrier each thread reads and writes only its own elements.
+__global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(const float* x, int64_t n,
                                                                const float* __restrict__ gain,
                                                                float eps, float* out) {
     const int64_t t = blockIdx.x;
     const int tid = threadIdx.x;
     const float* xr = x + t * n;
-    __shared__ float part[kNormThreads / kWave];
-    float ss = 0.f;
-    for (int64_t i = tid; i < n; i += kNormThreads) ss = fmaf(xr[i], xr[i], ss);
-    ss = wave_sum(ss);
+    __shared__ double part[kNormThreads / kWave];
+    double ss = 0.0;
+    for (int64_t i = tid; i < n; i += kNormThreads) ss = fma((double)xr[i], (double)xr[i], ss);
+    ss = wave_sum_f64(ss);
     if ((tid & 63) == 0) part[tid >> 6] = ss;
     __syncthreads();
-    const float tot = (part[0] + part[1]) + (part[2] + part[3]);
-    const float inv = 1.0f / sqrtf(tot / (float)n + eps);
-    for (int64_t i = tid; i < n; i += kNormThreads) out[t * n + i] = gain[i] * (xr[i] * inv);
+    const double tot = (part[0] + part[1]) + (part[2] + part[3]);
+    const double inv = 1.0 / sqrt(tot / (double)n + (double)eps);
+    for (int64_t i = tid; i < n; i += kNormThreads)
+        out[t * n + i] = (float)((double)gain[i] * (double)xr[i] * inv);
 }
 
 // One wave per (token, head): lane i owns the NEOX pair (i, i + D/2) for

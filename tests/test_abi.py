@@ -29,7 +29,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(_lib.EXPORTS) == names
@@ -125,6 +125,38 @@ def test_moe_ffn_validation(lib):
         lib.q3moe_route_workspace_bytes(1, 128)
     assert _moe(lib, ws_bytes=need - 1) == E_WORKSPACE
     assert _moe(lib, ws=FAKE_MIS) == E_ALIGN
+
+
+def _moe_pre(lib, T=1, H=2048, F=768, E=128, k=8, hidden=FAKE, gain=ctypes.c_void_p(0x90000),
+             eps=1e-6, router=ctypes.c_void_p(0x70000), idx=ctypes.c_void_p(0x50000),
+             w=ctypes.c_void_p(0x60000), out=ctypes.c_void_p(0x40000), acc=1,
+             ws=ctypes.c_void_p(0x80000), ws_bytes=1 << 30):
+    down = _experts(qtype=q3.Q6_K, stride=1290240)
+    return lib.q3moe_moe_ffn_prenorm(hidden, T, H, F, E, k, gain, eps, router, _experts(),
+                                     _experts(), down, idx, w, out, acc, ws, ws_bytes, None)
+
+
+def test_moe_ffn_prenorm_validation(lib):
+    """The pre-norm MoE block checks what q3moe_moe_ffn checks, plus the gain
+    and eps; out may be hidden itself, but no other overlap is accepted.
+    (Calls that would pass validation are not made here: they would launch.)"""
+    assert _moe_pre(lib, T=0) == OK
+    assert _moe_pre(lib, gain=None) == E_NULL
+    assert _moe_pre(lib, T=0, gain=None) == OK
+    assert _moe_pre(lib, eps=-1e-6) == E_SHAPE
+    assert _moe_pre(lib, eps=float("nan")) == E_SHAPE
+    assert _moe_pre(lib, eps=float("inf")) == E_SHAPE
+    assert _moe_pre(lib, H=2000) == E_SHAPE
+    assert _moe_pre(lib, gain=ctypes.c_void_p(0x90004)) == E_ALIGN
+    assert _moe_pre(lib, out=ctypes.c_void_p(0x10000 + 16)) == E_ALIAS     # out partly over hidden
+    assert _moe_pre(lib, gain=ctypes.c_void_p(0x40000 + 256)) == E_ALIAS   # gain inside out
+    assert _moe_pre(lib, out=FAKE, idx=ctypes.c_void_p(0x10000 + 32)) == E_ALIAS
+    assert _moe_pre(lib, ws=None) == E_WORKSPACE
+    need = lib.q3moe_moe_ffn_workspace_bytes(3, 2048, 768, 128, 8)
+    assert _moe_pre(lib, T=3, ws_bytes=need - 1) == E_WORKSPACE
+    # the workspace also holds the normalised rows of the multi-kernel path
+    assert need >= lib.q3moe_expert_ffn_workspace_bytes(3, 2048, 768, 128, 8) + \
+        lib.q3moe_route_workspace_bytes(3, 128) + 3 * 2048 * 4
 
 
 def _route(lib, T=1, H=2048, E=128, k=8, hidden=FAKE, router=FAKE, idx=FAKE, w=FAKE, ws=FAKE,

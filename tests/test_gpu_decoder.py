@@ -204,7 +204,7 @@ def oracle_layer(o, att, moe, x, kc, vc, pos):
     return dict(a=a, x1=x1, idx=idx, logits=logits, out=out, kc=kc, vc=vc)
 
 
-def gpu_layer(att, moe, x, kc, vc, pos):
+def gpu_layer(att, moe, x, kc, vc, pos, form="separate"):
     s = att.shape
     B = x.shape[0]
     xn = q3.q3moe_rmsnorm(x, att.in_norm, s.eps)
@@ -216,17 +216,22 @@ def gpu_layer(att, moe, x, kc, vc, pos):
     a = q3.q3moe_gqa_attention(q, kc, vc, pos + 1, 1.0 / np.sqrt(s.D))
     x1 = x.clone()
     q3.q3moe_bf16_gemv(att.wo, a.view(B, -1), out=x1, accumulate=True)
-    h = q3.q3moe_rmsnorm(x1, att.post_norm, s.eps)
     ms = moe.shape
-    idx, w = q3.q3moe_route(h, moe.router, ms.k)
     out = x1.clone()
+    if form == "prenorm":                # norm + route + FFN in one call, in place
+        _, idx, _ = q3.q3moe_moe_ffn_prenorm(out, att.post_norm, s.eps, moe.router, ms.k,
+                                             *experts_of(moe), F=ms.F, out=out, accumulate=True)
+        return dict(a=a, x1=x1, idx=idx, out=out)
+    h = q3.q3moe_rmsnorm(x1, att.post_norm, s.eps)
+    idx, w = q3.q3moe_route(h, moe.router, ms.k)
     q3.q3moe_expert_ffn(h, idx, w, *experts_of(moe), F=ms.F, out=out, accumulate=True)
     return dict(a=a, x1=x1, idx=idx, out=out)
 
 
+@pytest.mark.parametrize("form", ["separate", "prenorm"])
 @pytest.mark.parametrize("B", [1, 16])
-def test_decoder_layer_parity(B):
-    say(f"decoder layer B={B}")
+def test_decoder_layer_parity(B, form):
+    say(f"decoder layer B={B} form={form}")
     att = gen.attn_layer(gen.QWEN3_30B_A3B_ATTN, 61)
     moe = gen.moe_layer(gen.QWEN3_30B_A3B, 62)
     s = att.shape
@@ -235,7 +240,7 @@ def test_decoder_layer_parity(B):
     pos = _positions(B, s.S_max)
     ref = oracle_layer(oracle.oracle(), att, moe, x.numpy(), _bits(kc), _bits(vc), pos)
     got = gpu_layer(att.to(DEV), moe.to(DEV), x.to(DEV), kc.to(DEV), vc.to(DEV),
-                    torch.from_numpy(pos).to(DEV))
+                    torch.from_numpy(pos).to(DEV), form)
     torch.cuda.synchronize()
     assert_rows_close(got["a"].cpu().numpy().reshape(B, -1), ref["a"].reshape(B, -1), what="attention")
     assert_rows_close(got["x1"].cpu().numpy(), ref["x1"], what="residual after O")

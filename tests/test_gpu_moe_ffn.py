@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import sparse_moe_decode_q3moe_amd as q3
 from sparse_moe_decode_q3moe_amd import inputs as gen
 from parity import assert_indices_equal, assert_rows_close, experts_of, oracle_moe, say
@@ -154,3 +155,52 @@ def test_moe_ffn_routing_ties_and_specials(layers):
     assert np.array_equal(got, ref_idx), (got, ref_idx)
     np.testing.assert_allclose(w.cpu().numpy(), ref_w, rtol=1e-6, atol=0)
     assert_rows_close(out.cpu().numpy()[:1], ref[:1], what="ties, token 0")
+
+
+EPS = 1e-6
+PRENORM_CASES = ["a3b_T1", "a3b_T4", "E72_k6_T3", "a3b_T5", "tiny_T4", "prefill_T40"]
+
+
+def _gain(H, seed):
+    return gen.uniform_f32((H,), 0.5, 1.5, gen.make_generator(seed))
+
+
+@pytest.mark.parametrize("name", PRENORM_CASES)
+def test_moe_ffn_prenorm_in_place(layers, name):
+    """q3moe_moe_ffn_prenorm with out = hidden and accumulate: the residual
+    update x += MoE(RMSNorm(x)) in one call (the norm inside the one-kernel
+    block for the first three cases, a norm kernel first for the others),
+    against the oracle's RMSNorm, routing and expert FFN."""
+    cpu, dev, x = layers(name)
+    s = cpu.shape
+    say(f"moe_ffn_prenorm in place {name}: T={s.T} E={s.E} k={s.k}")
+    g = _gain(s.H, 7 + s.T)
+    xd = x.to(DEV).clone()
+    out, idx, w = q3.q3moe_moe_ffn_prenorm(xd, g.to(DEV), EPS, dev.router, s.k, *experts_of(dev),
+                                           F=s.F, out=xd, accumulate=True)
+    assert out.data_ptr() == xd.data_ptr()
+    xn = oracle.oracle().rmsnorm(x.numpy(), g.numpy(), EPS)
+    err = _check(cpu, (out, idx, w), torch.from_numpy(xn), f"{name} prenorm in place",
+                 out=x.numpy().copy(), accumulate=True)
+    say(f"  max rel L2 {err:.2e}")
+
+
+@pytest.mark.parametrize("name", ["a3b_T2", "a3b_T5"])
+def test_moe_ffn_prenorm_matches_norm_then_block(layers, name):
+    """The pre-norm block (out of place, no accumulate) equals q3moe_rmsnorm
+    followed by q3moe_moe_ffn: the same routing, outputs to the summation
+    orders; and q3moe_rmsnorm's rows equal the oracle's to the last bit."""
+    cpu, dev, x = layers(name)
+    s = cpu.shape
+    say(f"moe_ffn_prenorm vs rmsnorm + moe_ffn {name}")
+    g = _gain(s.H, 99).to(DEV)
+    xd = x.to(DEV)
+    out, idx, w = q3.q3moe_moe_ffn_prenorm(xd, g, EPS, dev.router, s.k, *experts_of(dev), F=s.F)
+    xn = q3.q3moe_rmsnorm(xd, g, EPS)
+    out2, idx2, w2 = q3.q3moe_moe_ffn(xn, dev.router, s.k, *experts_of(dev), F=s.F)
+    torch.cuda.synchronize()
+    ref_xn = oracle.oracle().rmsnorm(x.numpy(), g.cpu().numpy(), EPS)
+    assert np.array_equal(xn.cpu().numpy().view(np.uint32), ref_xn.view(np.uint32))
+    assert torch.equal(idx.cpu(), idx2.cpu())
+    np.testing.assert_allclose(w.cpu().numpy(), w2.cpu().numpy(), rtol=1e-6, atol=0)
+    assert_rows_close(out.cpu().numpy(), out2.cpu().numpy().astype(np.float64), what="prenorm vs two steps")

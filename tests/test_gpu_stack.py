@@ -4,7 +4,9 @@ expert weights resident in HBM), batch-1 decode: down is Q6_K in layers
 the residual stream is x <- x + MoE(RMSNorm(x)) with unit gain and eps 1e-6.
 Routing is compared at every layer (the layer-47 divergence named in gap G2
 of the same issue is exactly what a last-layer-only check would miss), and
-the residual stream after every layer within 1e-4 relative L2."""
+the residual stream after every layer within 1e-4 relative L2.  Each layer
+runs either as three calls (norm, route, expert FFN) or as one
+q3moe_moe_ffn_prenorm call that updates the stream in place."""
 import numpy as np
 import pytest
 import torch
@@ -37,12 +39,24 @@ def _oracle_layer(o, layer_dev: gen.MoeLayer, x: np.ndarray):
     return idx, logits, out
 
 
-def _gpu_layer(layer_dev: gen.MoeLayer, x: torch.Tensor, ones: torch.Tensor):
+def _gpu_layer(layer_dev: gen.MoeLayer, x: torch.Tensor, ones: torch.Tensor, form: str, ws=None):
+    """One stacked layer on the GPU, in place on x: as three calls (norm,
+    route, expert FFN) or as one q3moe_moe_ffn_prenorm call with out = x."""
     s = layer_dev.shape
+    if form == "prenorm":
+        _, idx, _ = q3.q3moe_moe_ffn_prenorm(x, ones, EPS, layer_dev.router, s.k,
+                                             *experts_of(layer_dev), F=s.F, out=x,
+                                             accumulate=True, workspace=ws)
+        return idx
     xn = q3.q3moe_rmsnorm(x, ones, EPS)
     idx, w = q3.q3moe_route(xn, layer_dev.router, s.k)
     q3.q3moe_expert_ffn(xn, idx, w, *experts_of(layer_dev), F=s.F, out=x, accumulate=True)
     return idx
+
+
+def _ws(T):
+    return torch.zeros(q3.q3moe_moe_ffn_workspace_bytes(T, 2048, 768, 128, 8), dtype=torch.uint8,
+                       device=DEV)
 
 
 def _make_layers(T, n_layers):
@@ -55,28 +69,31 @@ def _make_layers(T, n_layers):
     return layers
 
 
+@pytest.mark.parametrize("form", ["three_calls", "prenorm"])
 @pytest.mark.parametrize("T,n_layers", [(1, 48), (3, 4)])
-def test_each_layer_on_the_oracle_stream(T, n_layers):
+def test_each_layer_on_the_oracle_stream(T, n_layers, form):
     """Every layer of the stack, fed the oracle's residual stream: routing
     equal and the layer output within 1e-4 relative L2, per layer."""
     if not torch.cuda.is_available():
         pytest.skip("no HIP device visible")
     o = oracle.oracle()
-    say(f"stack (per layer) T={T} layers={n_layers}")
+    say(f"stack (per layer) T={T} layers={n_layers} form={form}")
     layers = _make_layers(T, n_layers)
     ones = torch.ones(2048, device=DEV)
+    ws = _ws(T)
     x_ref = gen.hidden_states(T, 2048, 77).numpy()
     for l, layer in enumerate(layers):
         x_gpu = torch.from_numpy(x_ref).to(DEV)
-        idx = _gpu_layer(layer, x_gpu, ones)
+        idx = _gpu_layer(layer, x_gpu, ones, form, ws)
         torch.cuda.synchronize()
         ref_idx, logits, x_ref = _oracle_layer(o, layer, x_ref)
         assert_indices_equal(idx.cpu().numpy(), ref_idx, logits, 8, f"layer {l}")
         assert_rows_close(x_gpu.cpu().numpy(), x_ref, what=f"layer {l}")
 
 
+@pytest.mark.parametrize("form", ["three_calls", "prenorm"])
 @pytest.mark.parametrize("T,n_layers", [(1, 48), (3, 4)])
-def test_free_running_stack(T, n_layers):
+def test_free_running_stack(T, n_layers, form):
     """The GPU runs the whole stack on its own residual stream.  Routing must
     be identical at every layer.  The stream itself drifts from the oracle's
     by the f32 rounding of each layer amplified through the later layers
@@ -87,17 +104,18 @@ def test_free_running_stack(T, n_layers):
     if not torch.cuda.is_available():
         pytest.skip("no HIP device visible")
     o = oracle.oracle()
-    say(f"stack (free running) T={T} layers={n_layers}")
+    say(f"stack (free running) T={T} layers={n_layers} form={form}")
     layers = _make_layers(T, n_layers)
     x0 = gen.hidden_states(T, 2048, 77).numpy()
     rng = np.random.default_rng(5)
     x_pert = (x0 * (1.0 + 1e-6 * rng.standard_normal(x0.shape))).astype(np.float32)
     x_gpu = torch.from_numpy(x0).to(DEV)
     ones = torch.ones(2048, device=DEV)
+    ws = _ws(T)
     x_ref = x0.copy()
     worst = 0.0
     for l, layer in enumerate(layers):
-        idx = _gpu_layer(layer, x_gpu, ones)
+        idx = _gpu_layer(layer, x_gpu, ones, form, ws)
         torch.cuda.synchronize()
         ref_idx, logits, x_ref = _oracle_layer(o, layer, x_ref)
         _, _, x_pert = _oracle_layer(o, layer, x_pert)
