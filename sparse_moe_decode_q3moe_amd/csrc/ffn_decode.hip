@@ -6,8 +6,8 @@
 // persistent launch, optionally with the routing inside (the MoE block of
 // q3moe_moe_ffn); workgroups hand the router partial sums and h to each
 // other as tagged words.  Gate/up take the activations as three int8
-// pieces (exact int32 dot products); down uses f32 weights.  Described in
-// detail at the kernel.
+// pieces (exact int32 dot products); down takes each 16-weight group as
+// a * sum(q h) + c * sum(h) in f32.  Described in detail at the kernel.
 //
 // Other shapes, two kernels per call:
 //   gu_decode_kernel   one wave per task = (token-slot pair, R rows of the
@@ -649,10 +649,11 @@ __device__ __forceinline__ void gu_rows_finish(const GuRows& g, const XCols& x, 
 // this call (derived from an epoch counter in the workspace).  A down thread
 // keeps re-reading the 16 words it needs, with device-scope loads, until all
 // carry this call's tag, so the data itself is the signal and no write has
-// to be acknowledged before another can be issued.  While they wait, the
-// down threads have already turned their share of the down tiles into f32
-// weights in registers, so what remains after h arrives is 16 FMAs per row
-// and the cross-lane sum.  Exit: each workgroup counts itself on a stripe of
+// to be acknowledged before another can be issued.  Before they read h, the
+// down threads have already pulled their share of the down tiles out of LDS
+// as quant bytes and per-row group factors (a, c) in registers; after h
+// arrives each row takes 16 byte conversions, 16 FMAs and one a, c step,
+// then the cross-lane sum.  Exit: each workgroup counts itself on a stripe of
 // exit counters; the workgroup that completes the count advances the epoch
 // and zeroes the counters for the next call.  Every wait is bounded: one that
 // runs out sets the status word instead of hanging.
@@ -717,17 +718,19 @@ __host__ __device__ inline FusedLds fused_lds(int64_t T, int64_t F, int32_t qtyp
 }
 
 // Down-stage unit of a thread: 16 consecutive columns (one Q6_K scale group,
-// half a Q4_K sub-block) of one slot's tile, for all 8 rows.  Their weights
-// a * q + b (exact products rounded once to f32) come out of the raw tile in
-// LDS into w[row][i].
-__device__ __forceinline__ void dn_unit_weights(const uint8_t* tile, const DnGeom& g, int grp,
-                                                float (&w)[kDnRows][kDnGroup]) {
+// half a Q4_K sub-block) of one slot's tile, for all 8 rows.  Each weight is
+// a * q + c with the row's group factors (Q6_K: a = d * scale, c = -32 a;
+// Q4_K: a = d * sc, c = -dmin * m): the 16 quants q (0..63) come out of the
+// raw tile in LDS as bytes, four per word in column order (q[row][i / 4]
+// byte i % 4), and a, c as f32.  The row's dot product with h is then
+// a * sum(q h) + c * sum(h).
+__device__ __forceinline__ void dn_unit_quants(const uint8_t* tile, const DnGeom& g, int grp,
+                                               uint32_t (&q)[kDnRows][4], float (&a)[kDnRows],
+                                               float (&c)[kDnRows]) {
     const int b = grp / (kQK / kDnGroup), j = grp % (kQK / kDnGroup);
 #pragma unroll
     for (int rho = 0; rho < kDnRows; ++rho) {
         const int boff = rho * g.rowb + b * g.bb;
-        uint32_t q[4];
-        float a, c;
         if (g.q6) {
             // group j: weights 16j..16j+15 with scale j; low four bits in nibble
             // r/2 of ql bytes 64n + 32(r%2) + 16lh + i, top two bits at 2r of
@@ -739,10 +742,10 @@ __device__ __forceinline__ void dn_unit_weights(const uint8_t* tile, const DnGeo
             const int ls = 4 * (r >> 1), hs = 2 * r;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                q[i] = ((l4[i] >> ls) & 0x0f0f0f0fu) | (((h4[i] >> hs) & 0x03030303u) << 4);
+                q[rho][i] = ((l4[i] >> ls) & 0x0f0f0f0fu) | (((h4[i] >> hs) & 0x03030303u) << 4);
             const float d = half_bits_to_float(tile[boff + 208] | (tile[boff + 209] << 8));
-            a = d * (float)(int8_t)tile[boff + 192 + j];
-            c = -32.f * a;
+            a[rho] = d * (float)(int8_t)tile[boff + 192 + j];
+            c[rho] = -32.f * a[rho];
         } else {
             // half j%2 of sub-block j/2: nibble (j/2)%2 of qs bytes 32(j/4) + 16(j%2) + i
             const int sb = j >> 1;
@@ -751,15 +754,12 @@ __device__ __forceinline__ void dn_unit_weights(const uint8_t* tile, const DnGeo
             const uint32_t q4[4] = {qs.x, qs.y, qs.z, qs.w};
             const int sh = 4 * (sb & 1);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) q[i] = (q4[i] >> sh) & 0x0f0f0f0fu;
+            for (int i = 0; i < 4; ++i) q[rho][i] = (q4[i] >> sh) & 0x0f0f0f0fu;
             int sc, mn;
             q4k_sm_var(hdr.y, hdr.z, hdr.w, sb, sc, mn);
-            a = half_bits_to_float(hdr.x & 0xffffu) * (float)sc;
-            c = -half_bits_to_float(hdr.x >> 16) * (float)mn;
+            a[rho] = half_bits_to_float(hdr.x & 0xffffu) * (float)sc;
+            c[rho] = -half_bits_to_float(hdr.x >> 16) * (float)mn;
         }
-#pragma unroll
-        for (int i = 0; i < kDnGroup; ++i)
-            w[rho][i] = fmaf(a, (float)((q[i >> 2] >> (8 * (i & 3))) & 0xffu), c);
     }
 }
 
@@ -1112,7 +1112,7 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
         // gate/up tasks: the first task's weights are on their way; read the
         // token's pieces and compute it, then load and compute the rest.
         // Raised issue priority: the gate/up waves are the critical path, and
-        // two SIMDs also run a down wave's weight extraction beside them.
+        // two SIMDs also run a down wave's quant extraction beside them.
         __builtin_amdgcn_s_setprio(2);
         if (tau < n_gu) {
             int xc = p / k;                   // token whose pieces x holds
@@ -1193,8 +1193,9 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
             const int e = __shfl(my_idx, (int)(t * k) + s, kWave);
             const float ws = __shfl(my_w, (int)(t * k) + s, kWave);
             const bool valid = active && e >= 0 && e < E;
-            float wt[kDnRows][kDnGroup];
-            if (uw >= 0) dn_unit_weights(smem + L.dn_off + s * dg.tile_pad, dg, grp, wt);
+            uint32_t qb[kDnRows][4];
+            float fa[kDnRows], fc[kDnRows];
+            if (uw >= 0) dn_unit_quants(smem + L.dn_off + s * dg.tile_pad, dg, grp, qb, fa, fc);
             if (it == 0) {
                 // the token's h: every slot's F values, published by gate/up
                 // waves anywhere on the device
@@ -1208,11 +1209,16 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
                     const float4 h4 = *reinterpret_cast<const float4*>(hl + s * F + grp * kDnGroup + i);
                     hv[i] = h4.x; hv[i + 1] = h4.y; hv[i + 2] = h4.z; hv[i + 3] = h4.w;
                 }
+                float hsum = 0.f;
+#pragma unroll
+                for (int i = 0; i < kDnGroup; ++i) hsum += hv[i];
 #pragma unroll
                 for (int rho = 0; rho < kDnRows; ++rho) {
-                    float y = 0.f;
+                    float sq = 0.f;
 #pragma unroll
-                    for (int i = 0; i < kDnGroup; ++i) y = fmaf(wt[rho][i], hv[i], y);
+                    for (int i = 0; i < kDnGroup; ++i)
+                        sq = fmaf((float)((qb[rho][i >> 2] >> (8 * (i & 3))) & 0xffu), hv[i], sq);
+                    const float y = fmaf(fa[rho], sq, fc[rho] * hsum);
                     acc[rho] += valid ? ws * y : 0.f;
                 }
             }
