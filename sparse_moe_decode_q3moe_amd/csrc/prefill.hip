@@ -225,7 +225,7 @@ __global__ __launch_bounds__(kGuThreads) void pf_gateup_kernel(
     int64_t gstride, const uint8_t* __restrict__ ubase, int64_t ustride, int64_t F,
     float* __restrict__ hbuf) {
     extern __shared__ __align__(16) uint8_t smem[];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     int slot, ftile;
     pf_xcd_tile((int)blockIdx.x, (int)(F / kGuFeat), slot, ftile);
     if (slot >= tile_off[E]) return;                          // uniform: an unused tile slot
@@ -316,6 +316,7 @@ __global__ __launch_bounds__(kGuThreads) void pf_gateup_kernel(
         store_stage(st & 1);
         __syncthreads();
         if (st + 1 < nst) load_stage(st + 1);
+        if (32 * th >= nrows) continue;                       // both of this wave's token blocks empty
 #pragma unroll
         for (int j = 0; j < 4; ++j) {                         // one sub-block per k step
             const int c = j >> 1, h = j & 1;
@@ -333,6 +334,7 @@ __global__ __launch_bounds__(kGuThreads) void pf_gateup_kernel(
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int tb = 2 * th + i;
+                if (16 * tb >= nrows) continue;               // no pairs in this token block
                 const int xo = (16 * tb + col) * kXRowB + (32 * j + 8 * g) * 2;
                 const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(smem + xo);
                 const bf16x8_t am = *reinterpret_cast<const bf16x8_t*>(smem + kXPieceB + xo);
@@ -353,6 +355,7 @@ __global__ __launch_bounds__(kGuThreads) void pf_gateup_kernel(
         // product per tile, as one f32 matrix step (k = sub-block = lane / 16)
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
+            if (16 * (2 * th + i) >= nrows) continue;
             const float sa = reinterpret_cast<const float*>(smem + kGuSOff)[g * kPfRows + 16 * (2 * th + i) + col];
 #pragma unroll
             for (int fb = 0; fb < 2; ++fb) {
@@ -406,7 +409,7 @@ __global__ __launch_bounds__(kDnThreads) void pf_down_kernel(
     const uint8_t* __restrict__ dbase, int32_t qtype, int64_t dstride, int64_t H,
     float* __restrict__ Y) {
     extern __shared__ __align__(16) uint8_t smem[];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     int slot, htile;
     pf_xcd_tile((int)blockIdx.x, (int)(H / kDnOut), slot, htile);
     if (slot >= tile_off[E]) return;
@@ -478,6 +481,7 @@ __global__ __launch_bounds__(kDnThreads) void pf_down_kernel(
         store_stage();
         __syncthreads();
         if (st + 1 < nst) load_stage(st + 1);
+        if (16 * tb0 >= nrows) continue;                      // both of this wave's token blocks empty
         const int sb = st >> 1, half = st & 1;
         const int boff = orow * rowb + sb * bb;               // this lane's block in the tile
         const uint8_t* blk = smem + boff;
@@ -512,6 +516,7 @@ __global__ __launch_bounds__(kDnThreads) void pf_down_kernel(
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int tb = tb0 + i;
+                if (16 * tb >= nrows) continue;               // no pairs in this token block
                 const int xo = hoff + (16 * tb + col) * kXRowB + (16 * G + 4 * g) * 2;
                 f32x4_t t = pf_mfma(*reinterpret_cast<const s16x4_t*>(smem + xo), bw, f32x4_t{0.f, 0.f, 0.f, 0.f});
                 t = pf_mfma(*reinterpret_cast<const s16x4_t*>(smem + kXPieceB + xo), bw, t);
@@ -536,6 +541,7 @@ __global__ __launch_bounds__(kDnThreads) void pf_down_kernel(
             }
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
+                if (16 * (tb0 + i) >= nrows) continue;
                 const float sa = reinterpret_cast<const float*>(smem + soff)[(4 * pq + g) * kPfRows + 16 * (tb0 + i) + col];
                 acc[i] = pf_mfma_f32(sa, -off, acc[i]);
             }
