@@ -196,8 +196,10 @@ __device__ __forceinline__ bf16x8_t pf_q4k_b8(uint2 w, int h) {
 
 // ---------------------------------------------------------------- gate/up --
 // One workgroup per (128 h features, pair tile): 256 weight rows, gate rows
-// f0.. then up rows f0..  8 waves: wave w owns token blocks 2 (w >> 2) and
-// 2 (w >> 2) + 1 and features 32 (w & 3)..+31 of both matrices, so
+// f0.. then up rows f0..  8 waves: wave w owns token blocks w >> 2 and
+// (w >> 2) + 2 (interleaved, so that waves w and w + 4, which share a SIMD,
+// both have work when a tile holds 32 pairs or fewer; blocks with no pairs
+// are skipped) and features 32 (w & 3)..+31 of both matrices, so
 // silu(g) * u is formed in registers and each wave reads half the tile's
 // activations per step.  Each k step covers one Q4_K sub-block
 // (v_mfma_f32_16x16x32_bf16 on exact bf16 weights 128 + 8q with each of the
@@ -316,7 +318,7 @@ __global__ __launch_bounds__(kGuThreads) void pf_gateup_kernel(
         store_stage(st & 1);
         __syncthreads();
         if (st + 1 < nst) load_stage(st + 1);
-        if (32 * th >= nrows) continue;                       // both of this wave's token blocks empty
+        if (16 * th >= nrows) continue;                       // both of this wave's token blocks empty
 #pragma unroll
         for (int j = 0; j < 4; ++j) {                         // one sub-block per k step
             const int c = j >> 1, h = j & 1;
@@ -333,7 +335,7 @@ __global__ __launch_bounds__(kGuThreads) void pf_gateup_kernel(
             }
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                const int tb = 2 * th + i;
+                const int tb = th + 2 * i;
                 if (16 * tb >= nrows) continue;               // no pairs in this token block
                 const int xo = (16 * tb + col) * kXRowB + (32 * j + 8 * g) * 2;
                 const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(smem + xo);
@@ -355,8 +357,8 @@ __global__ __launch_bounds__(kGuThreads) void pf_gateup_kernel(
         // product per tile, as one f32 matrix step (k = sub-block = lane / 16)
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            if (16 * (2 * th + i) >= nrows) continue;
-            const float sa = reinterpret_cast<const float*>(smem + kGuSOff)[g * kPfRows + 16 * (2 * th + i) + col];
+            if (16 * (th + 2 * i) >= nrows) continue;
+            const float sa = reinterpret_cast<const float*>(smem + kGuSOff)[g * kPfRows + 16 * (th + 2 * i) + col];
 #pragma unroll
             for (int fb = 0; fb < 2; ++fb) {
                 const int gr = frow0 + 16 * fb;
@@ -373,7 +375,7 @@ __global__ __launch_bounds__(kGuThreads) void pf_gateup_kernel(
         for (int fb = 0; fb < 2; ++fb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int t = 16 * (2 * th + i) + 4 * g + r;
+                const int t = 16 * (th + 2 * i) + 4 * g + r;
                 if (t < nrows)
                     hbuf[(row0 + t) * F + f0 + frow0 + 16 * fb] = pf_silu(acc[i][fb][0][r]) * acc[i][fb][1][r];
             }
@@ -384,7 +386,8 @@ __global__ __launch_bounds__(kGuThreads) void pf_gateup_kernel(
 // of the down matrix (all F/256 blocks, contiguous in HBM) is staged once
 // with the first stage; the h pieces (hi, lo) and their 16-value sums are
 // staged per 128-wide k stage.  8 waves: wave w owns output rows
-// 16 (w & 3).. and token blocks 2 (w >> 2), 2 (w >> 2) + 1.  Each k step is
+// 16 (w & 3).. and token blocks w >> 2, (w >> 2) + 2 (interleaved as in the
+// gate/up kernel; empty ones skipped).  Each k step is
 // one 16-wide scale group (v_mfma_f32_16x16x16bf16_1k on exact bf16 weights
 // 128 + q (Q6_K) or 128 + 8q (Q4_K) with each h piece), scaled by the
 // group's factor; the offset (and the Q4_K min) times each group's h sum
@@ -467,7 +470,7 @@ __global__ __launch_bounds__(kDnThreads) void pf_down_kernel(
 
     const int col = lane & 15, g = lane >> 4;
     const int orow = 16 * (wave & 3) + col;                   // this lane's output row in the tile
-    const int tb0 = 2 * (wave >> 2);
+    const int tb0 = wave >> 2;                                // token blocks tb0, tb0 + 2
     f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
 
     load_stage(0);
@@ -515,7 +518,7 @@ __global__ __launch_bounds__(kDnThreads) void pf_down_kernel(
             const s16x4_t bw = pf_bf16x4(q);
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                const int tb = tb0 + i;
+                const int tb = tb0 + 2 * i;
                 if (16 * tb >= nrows) continue;               // no pairs in this token block
                 const int xo = hoff + (16 * tb + col) * kXRowB + (16 * G + 4 * g) * 2;
                 f32x4_t t = pf_mfma(*reinterpret_cast<const s16x4_t*>(smem + xo), bw, f32x4_t{0.f, 0.f, 0.f, 0.f});
@@ -541,8 +544,8 @@ __global__ __launch_bounds__(kDnThreads) void pf_down_kernel(
             }
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                if (16 * (tb0 + i) >= nrows) continue;
-                const float sa = reinterpret_cast<const float*>(smem + soff)[(4 * pq + g) * kPfRows + 16 * (tb0 + i) + col];
+                if (16 * (tb0 + 2 * i) >= nrows) continue;
+                const float sa = reinterpret_cast<const float*>(smem + soff)[(4 * pq + g) * kPfRows + 16 * (tb0 + 2 * i) + col];
                 acc[i] = pf_mfma_f32(sa, -off, acc[i]);
             }
         }
@@ -551,7 +554,7 @@ __global__ __launch_bounds__(kDnThreads) void pf_down_kernel(
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int t = 16 * (tb0 + i) + 4 * g + r;
+            const int t = 16 * (tb0 + 2 * i) + 4 * g + r;
             if (t < nrows) Y[(int64_t)pairs[row0 + t] * H + h0 + orow] = acc[i][r];
         }
 }
