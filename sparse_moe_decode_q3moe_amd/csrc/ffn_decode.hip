@@ -691,8 +691,8 @@ constexpr int kFzRouteNper = 4;                        // experts per lane in th
 static_assert(kFzWaves * kWave * 4 == kFzNB * kQK, "one float4 of activations per thread and token");
 
 struct FusedLds {
-    int xp_bytes, dn_off, h_off, res_off, flag_off, route_off, rp_off, rl_off, lg_off, key_off,
-        key32_off, sel_off, total;
+    int xp_bytes, dn_off, h_off, res_off, flag_off, rp_off, rl_off, lg_off, key_off,
+        key32_off, sel_off, scnt_off, total;
 };
 
 __host__ __device__ inline FusedLds fused_lds(int64_t T, int64_t F, int32_t qtype) {
@@ -703,17 +703,17 @@ __host__ __device__ inline FusedLds fused_lds(int64_t T, int64_t F, int32_t qtyp
     L.h_off = L.dn_off + kFzMaxSlots * d.tile_pad;                  // h of the unit's token, f32 [slot][F]
     L.res_off = L.h_off + kFzMaxSlots * (int)F * 4;                 // [wave][row] partial sums
     L.flag_off = L.res_off + kFzWaves * kDnRows * 4;                // down waves whose tiles landed
-    // routing in the kernel: the T*k (expert, weight) table, per-wave router
-    // sums [wave][token] and the partial logits [token][unit] (at most one
-    // unit per workgroup, so at most kFzMaxUnits)
-    L.route_off = L.flag_off + 16;
-    L.rp_off = L.route_off + kFzMaxTokens * kFzMaxSlots * 8;
+    // routing in the kernel: per-wave router sums [wave][token] and the
+    // partial logits [token][unit] (at most one unit per workgroup, so at
+    // most kFzMaxUnits)
+    L.rp_off = L.flag_off + 16;
     L.rl_off = L.rp_off + kFzWaves * kFzMaxTokens * 8;
     L.lg_off = L.rl_off + kFzMaxTokens * kFzMaxUnits * 8;              // [token][expert] logits
     L.key_off = L.lg_off + kFzMaxTokens * kFzRouteNper * kWave * 8;    // their order keys
     L.key32_off = L.key_off + kFzMaxTokens * kFzRouteNper * kWave * 8; // and 32-bit screen keys
     L.sel_off = L.key32_off + kFzMaxTokens * kFzRouteNper * kWave * 4; // top-k: idx, value
-    L.total = L.sel_off + kFzMaxTokens * kFzMaxSlots * 12;
+    L.scnt_off = L.sel_off + kFzMaxTokens * kFzMaxSlots * 12;         // top-k slot counters
+    L.total = L.scnt_off + kFzMaxTokens * kFzMaxSlots * 4;
     return L;
 }
 
@@ -970,8 +970,6 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
     if constexpr (kRoute) {
         // Routing in the kernel (the route entry point's result, computed
         // redundantly by every workgroup from shared partial logits).
-        int32_t* r_idx = reinterpret_cast<int32_t*>(smem + L.route_off);
-        float* r_w = reinterpret_cast<float*>(r_idx + kFzMaxTokens * kFzMaxSlots);
         double* rp = reinterpret_cast<double*>(smem + L.rp_off);      // [wave][token]
         uint32_t* rl = reinterpret_cast<uint32_t*>(smem + L.rl_off);  // [token][unit] f64 halves
         const int U = E * P, HP = (int)(G::H / P);
@@ -1068,6 +1066,8 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
         uint32_t* keys32 = reinterpret_cast<uint32_t*>(smem + L.key32_off);
         int32_t* sel_idx = reinterpret_cast<int32_t*>(smem + L.sel_off);
         double* sel_val = reinterpret_cast<double*>(sel_idx + kFzMaxTokens * kFzMaxSlots);
+        int32_t* slot_cnt = reinterpret_cast<int32_t*>(smem + L.scnt_off);
+        if (tid < nr) slot_cnt[tid] = 0;
         for (int i = tid; i < (int)T * E; i += kThr) {
             const int t = i / E, e = i % E;
             const double* pl = reinterpret_cast<const double*>(rl) + t * U + e * P;
@@ -1078,20 +1078,41 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
             keys32[i] = order_key32(sum);
         }
         __syncthreads();
-        topk_rank_select<kThr>(lgt, keys, keys32, (int)T, E, k, tid, sel_idx, sel_val);
+        // the top-k on the screen keys; if equal screen keys reach the chosen
+        // (a slot counter other than 1, the same verdict in every wave) the
+        // exact selection replaces it
+        topk_rank_screen<kThr>(lgt, keys32, (int)T, E, k, tid, sel_idx, sel_val, slot_cnt);
         __syncthreads();
-        if (wave < T)
-            topk_weights(sel_idx + wave * k, sel_val + wave * k, k, lane, r_idx + wave * k,
-                         r_w + wave * k);
-        __syncthreads();
-        my_idx = lane < nr ? r_idx[lane] : -1;
-        my_w = lane < nr ? r_w[lane] : 0.f;
-        if (wg == 0 && tid < nr) {
-            topk_idx[tid] = r_idx[tid];
-            topk_w[tid] = r_w[tid];
+        if (!__all(lane >= nr || slot_cnt[lane] == 1)) {
+            topk_rank_select<kThr>(lgt, keys, keys32, (int)T, E, k, tid, sel_idx, sel_val);
+            __syncthreads();
         }
+        // the chosen experts first: the gate/up weight requests need only
+        // them, so they go out before the routing weights are formed
+        my_idx = lane < nr ? sel_idx[lane] : -1;
         if (is_gu)
             gu_rows_load(rows, lane_value(my_idx, p), E, gbase, gstride, ubase, ustride, r0, lane);
+        // every wave forms all T*k routing weights itself (lane l < T*k:
+        // token l / k, rank l % k) while those loads are in flight: the
+        // softmax over the token's chosen logits in double, its rank-0 logit
+        // subtracted, normalised by their sum in rank order and rounded to
+        // f32, as topk_wave does
+        {
+            const int tl = lane < nr ? lane / k : 0;
+            const double top = sel_val[tl * k];
+            const double ex = lane < nr ? exp(sel_val[lane] - top) : 0.0;
+            double den = 0.0;
+            for (int tt = 0; tt < T; ++tt) {
+                double d = 0.0;
+                for (int r = 0; r < k; ++r) d += readlane_f64(ex, tt * k + r);
+                if (tt == tl) den = d;
+            }
+            my_w = lane < nr ? (float)(ex / den) : 0.f;
+        }
+        if (wg == 0 && tid < nr) {
+            topk_idx[tid] = my_idx;
+            topk_w[tid] = my_w;
+        }
     } else {
         const int ri = lane < nr ? lane : nr - 1;         // loads without a branch
         my_idx = lane < nr ? idx[ri] : -1;

@@ -166,8 +166,8 @@ __device__ __forceinline__ uint32_t order_key32(double v) {
 
 // The top-k of T tokens' logits by rank counting, with every thread of the
 // workgroup: lg[t*E + e] holds the logits, key[] their order_key and key32[]
-// their order_key32 (all in LDS).  4 consecutive threads count, over a
-// quarter of the experts each, how many experts rank above expert e of
+// their order_key32 (all in LDS).  4 consecutive threads count, over every
+// fourth expert each, how many experts rank above expert e of
 // token t: every larger screen key counts, equal screen keys are decided on
 // the exact keys and indices.  The expert whose count c is below k is the
 // token's rank-c choice (sel_idx/sel_val[t*k + c] in LDS).  The same
@@ -184,31 +184,33 @@ __device__ __forceinline__ void topk_rank_select(const double* lg, const uint64_
         const int t = item / E, e = item % E;
         const uint32_t* row = key32 + t * E;
         const uint32_t me = row[e];
-        const int j0 = (E * qtr) >> 2, j1 = (E * (qtr + 1)) >> 2;
+        // quarter q takes the keys j = q + 4i (four banks per read step)
+        const int nj = (E - qtr + 3) >> 2;
+        const uint32_t* rq = row + qtr;
         int gt = 0, ge = 0;
-        int j = j0;
-        for (; j + 8 <= j1; j += 8) {                   // 8 reads in flight, no branches
+        int i = 0;
+        for (; i + 8 <= nj; i += 8) {                   // 8 reads in flight, no branches
             uint32_t kj[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) kj[i] = row[j + i];
+            for (int m = 0; m < 8; ++m) kj[m] = rq[4 * (i + m)];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                gt += (int)(kj[i] > me);
-                ge += (int)(kj[i] >= me);
+            for (int m = 0; m < 8; ++m) {
+                gt += (int)(kj[m] > me);
+                ge += (int)(kj[m] >= me);
             }
         }
-        for (; j < j1; ++j) {
-            const uint32_t kj = row[j];
+        for (; i < nj; ++i) {
+            const uint32_t kj = rq[4 * i];
             gt += (int)(kj > me);
             ge += (int)(kj >= me);
         }
         // equal screen keys other than e itself: decide those exactly
-        const bool self_here = e >= j0 && e < j1;
+        const bool self_here = (e & 3) == qtr;
         if (__any(ge - gt > (self_here ? 1 : 0))) {
             const uint64_t* krow = key + t * E;
             const uint64_t mk = krow[e];
             int tie = 0;
-            for (int jj = j0; jj < j1; ++jj) {
+            for (int jj = qtr; jj < E; jj += 4) {
                 const uint64_t kj = krow[jj];
                 tie += (row[jj] == me && jj != e && (kj > mk || (kj == mk && jj < e))) ? 1 : 0;
             }
@@ -224,18 +226,51 @@ __device__ __forceinline__ void topk_rank_select(const double* lg, const uint64_
     }
 }
 
-// Weights of one token's k selected logits (rank order in sel_val), on one
-// wave: the softmax over the selection, exactly as topk_wave computes it.
-__device__ __forceinline__ void topk_weights(const int32_t* sel_idx, const double* sel_val, int k,
-                                             int lane, int32_t* idx, float* w) {
-    const double top = sel_val[0];
-    const double ex = lane < k ? exp(sel_val[lane < k ? lane : 0] - top) : 0.0;
-    double den = 0.0;
-    for (int r = 0; r < k; ++r)
-        den += readlane_f64(ex, r);
-    if (lane < k) {
-        idx[lane] = sel_idx[lane];
-        w[lane] = (float)(ex / den);
+// The same selection when no two of the chosen screen keys are equal, at
+// half the comparisons: 4 consecutive threads count, over every fourth
+// expert each, only the experts whose screen key is strictly larger than
+// expert e's.  Distinct screen keys order the logits exactly (rounding is
+// monotonic), so an expert whose count c is below k is the token's rank-c
+// choice; it also adds one to slot c's counter (slot_cnt, zero on entry).
+// Equal screen keys at or above the k-th place give two experts the same
+// count, so some slot counter ends other than 1; the caller then runs
+// topk_rank_select, which decides equal screen keys exactly.
+template <int kThr>
+__device__ __forceinline__ void topk_rank_screen(const double* lg, const uint32_t* key32, int T,
+                                                 int E, int k, int tid, int32_t* sel_idx,
+                                                 double* sel_val, int32_t* slot_cnt) {
+    const int units = T * E * 4;
+    for (int u0 = 0; u0 < units; u0 += kThr) {
+        const int u = u0 + tid;
+        const bool act = u < units;
+        const int item = act ? (u >> 2) : 0, qtr = u & 3;
+        const int t = T == 1 ? 0 : item / E, e = item - t * E;
+        const uint32_t* row = key32 + t * E;
+        const uint32_t me = row[e];
+        // quarter q takes the keys j = q + 4i: at every step the four
+        // quarters of a wave read four consecutive words (four banks, each
+        // read broadcast to its 16 lanes); quarters of 32 consecutive keys
+        // would all fall in one bank
+        const int nj = (E - qtr + 3) >> 2;
+        const uint32_t* rq = row + qtr;
+        int gt = 0;
+        int i = 0;
+        for (; i + 8 <= nj; i += 8) {                   // 8 reads in flight, no branches
+            uint32_t kj[8];
+#pragma unroll
+            for (int m = 0; m < 8; ++m) kj[m] = rq[4 * (i + m)];
+#pragma unroll
+            for (int m = 0; m < 8; ++m) gt += (int)(kj[m] > me);
+        }
+        for (; i < nj; ++i) gt += (int)(rq[4 * i] > me);
+        // the 4 quarter counts of an expert sit in one quad of lanes
+        int cnt = gt + __builtin_amdgcn_update_dpp(0, gt, kDppQuadXor1, 0xf, 0xf, false);
+        cnt += __builtin_amdgcn_update_dpp(0, cnt, kDppQuadXor2, 0xf, 0xf, false);
+        if (act && qtr == 0 && cnt < k) {
+            sel_idx[t * k + cnt] = e;
+            sel_val[t * k + cnt] = lg[t * E + e];
+            __hip_atomic_fetch_add(slot_cnt + t * k + cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
     }
 }
 
