@@ -380,7 +380,11 @@ def decoder_bench(torch, q3, gen, layers, experts, shape, dev):
     Q/K/V projections, Q/K norm + RoPE, KV write, GQA attention over 4096
     cached positions (sequence b at position 4095 - 211 b), O projection with
     the residual, post-attention RMSNorm, route, expert FFN with the
-    residual.  Batch 1 and 16; attention layer copies (36 MB of bf16 weights
+    residual.  The residual stream is updated in place, as a decode step
+    does; at batch 1 the input norm and the Q/K/V projections are one
+    q3moe_bf16_gemv3 launch (at batch 16 four launches, q3moe_rmsnorm and
+    three q3moe_bf16_gemv, measure faster), the post-attention norm, route
+    and expert FFN one q3moe_moe_ffn_prenorm call.  Batch 1 and 16; attention layer copies (36 MB of bf16 weights
     each, plus their KV caches) and the 16 MoE layer copies rotate, so the
     Infinity Cache does not serve repeated bytes.  Reported: time per layer
     step, tokens/s, and the algorithmic HBM bytes per step over that time; and
@@ -400,34 +404,37 @@ def decoder_bench(torch, q3, gen, layers, experts, shape, dev):
         kk = torch.empty((B, nkv * D), device=dev)
         vv = torch.empty((B, nkv * D), device=dev)
         ao = torch.empty((B, nq, D), device=dev)
-        x1 = torch.empty((B, H), device=dev)
         idx = torch.empty((B, k), dtype=torch.int32, device=dev)
         wts = torch.empty((B, k), device=dev)
         ws_a = torch.empty(q3.q3moe_gqa_attention_workspace_bytes(B, nq, nkv, D, S), dtype=torch.uint8, device=dev)
         ws_m = torch.zeros(q3.q3moe_moe_ffn_workspace_bytes(B, H, F, E, k), dtype=torch.uint8, device=dev)
 
+        # the residual stream x is updated in place, as a decode step does:
+        # x += attention(RMSNorm(x)), then x += MoE(RMSNorm(x))
         def attention(i):
             A = atts[i % ncopies]
             kc, vc = caches[i % ncopies]
-            q3.q3moe_rmsnorm(x, A.in_norm, s_.eps, out=xn)
-            q3.q3moe_bf16_gemv(A.wq, xn, out=q)
-            q3.q3moe_bf16_gemv(A.wk, xn, out=kk)
-            q3.q3moe_bf16_gemv(A.wv, xn, out=vv)
+            if B <= 4:                                     # input norm + Q/K/V, one launch
+                q3.q3moe_bf16_gemv3([A.wq, A.wk, A.wv], x, norm_gain=A.in_norm, eps=s_.eps,
+                                    outs=[q, kk, vv])
+            else:                                          # faster as four launches at 16 tokens
+                q3.q3moe_rmsnorm(x, A.in_norm, s_.eps, out=xn)
+                q3.q3moe_bf16_gemv(A.wq, xn, out=q)
+                q3.q3moe_bf16_gemv(A.wk, xn, out=kk)
+                q3.q3moe_bf16_gemv(A.wv, xn, out=vv)
             q3.q3moe_attn_prologue(q.view(B, nq, D), kk.view(B, nkv, D), A.q_norm, A.k_norm, pos,
                                    s_.eps, s_.rope_base)
             q3.q3moe_kv_write(kk.view(B, nkv, D), vv.view(B, nkv, D), pos, kc, vc)
             q3.q3moe_gqa_attention(q.view(B, nq, D), kc, vc, lens, 1.0 / math.sqrt(D), out=ao,
                                    workspace=ws_a)
-            x1.copy_(x)
-            q3.q3moe_bf16_gemv(A.wo, ao.view(B, nq * D), out=x1, accumulate=True)
+            q3.q3moe_bf16_gemv(A.wo, ao.view(B, nq * D), out=x, accumulate=True)
 
         def layer(i):
-            # attention, then x1 += MoE(RMSNorm(x1)) in place: the
-            # post-attention norm runs inside the MoE block's kernel
+            # the post-attention norm runs inside the MoE block's kernel
             attention(i)
             L = layers[i % len(layers)]
-            q3.q3moe_moe_ffn_prenorm(x1, atts[i % ncopies].post_norm, s_.eps, L.router, k,
-                                     *experts[i % len(experts)], F=F, out=x1, accumulate=True,
+            q3.q3moe_moe_ffn_prenorm(x, atts[i % ncopies].post_norm, s_.eps, L.router, k,
+                                     *experts[i % len(experts)], F=F, out=x, accumulate=True,
                                      topk_idx=idx, topk_w=wts, workspace=ws_m)
 
         n = 16

@@ -286,6 +286,24 @@ q3moe_status q3moe_rmsnorm(const float *x, int64_t T, int64_t n, const float *ga
 q3moe_status q3moe_bf16_gemv(const uint16_t *W, int64_t N, int64_t K, const float *x, int64_t T,
                              float *y, int32_t accumulate, void *stream);
 
+/* The Q, K and V projections of the decoder layer in one launch, after the
+ * layer's input RMSNorm (the first two steps of the layer above):
+ *   xn = norm_gain ? norm_gain * x / sqrt(mean(x^2) + eps) : x
+ *   y0 = W0 xn [T x N0], y1 = W1 xn [T x N1], y2 = W2 xn [T x N2]
+ * (no accumulate).  N1 or N2 may be 0 (that matrix and output are then not
+ * used and may be null).  The norm is formed as q3moe_rmsnorm forms it
+ * (squares summed in double, each value formed in double and rounded once
+ * to f32) on the way into the projections; products and sums as for
+ * q3moe_bf16_gemv.  W0..W2, x and norm_gain 16-byte aligned; outputs 4-byte
+ * aligned and overlapping no input or each other.
+ * Limits: as q3moe_bf16_gemv for each matrix; with the norm, K <= 16384 and
+ * eps >= 0 and finite.
+ * Errors: E_NULL, E_SHAPE, E_ALIGN, E_ALIAS, E_HIP. */
+q3moe_status q3moe_bf16_gemv3(const uint16_t *W0, int64_t N0, const uint16_t *W1, int64_t N1,
+                              const uint16_t *W2, int64_t N2, int64_t K, const float *x, int64_t T,
+                              const float *norm_gain, float eps, float *y0, float *y1, float *y2,
+                              void *stream);
+
 /* Store the new token's keys and values in the bf16 KV caches:
  *   k_cache[b][g][pos[b]][i] = bf16(k_new[b][g][i]), likewise v,
  * for b < B, g < n_kv_heads, i < head_dim.  Caches are

@@ -24,7 +24,7 @@ EXPORTS = (
     "q3moe_expert_ffn_workspace_bytes", "q3moe_expert_ffn_status_offset", "q3moe_expert_ffn",
     "q3moe_attn_prologue", "q3moe_rmsnorm", "q3moe_bf16_gemv", "q3moe_kv_write",
     "q3moe_gqa_attention_workspace_bytes", "q3moe_gqa_attention",
-    "q3moe_moe_ffn_workspace_bytes", "q3moe_moe_ffn", "q3moe_moe_ffn_prenorm",
+    "q3moe_moe_ffn_workspace_bytes", "q3moe_moe_ffn", "q3moe_moe_ffn_prenorm", "q3moe_bf16_gemv3",
 )
 
 
@@ -54,6 +54,7 @@ _SIGS = {
     "q3moe_attn_prologue": (_I32, [_P, _P, _I64, _I32, _I32, _I32, _P, _P, _P, _F, _F, _P]),
     "q3moe_rmsnorm": (_I32, [_P, _I64, _I64, _P, _F, _P, _P]),
     "q3moe_bf16_gemv": (_I32, [_P, _I64, _I64, _P, _I64, _P, _I32, _P]),
+    "q3moe_bf16_gemv3": (_I32, [_P, _I64, _P, _I64, _P, _I64, _I64, _P, _I64, _P, _F, _P, _P, _P, _P]),
     "q3moe_kv_write": (_I32, [_P, _P, _I64, _I32, _I32, _P, _P, _P, _I64, _P]),
     "q3moe_gqa_attention_workspace_bytes": (ctypes.c_size_t, [_I64, _I32, _I32, _I32, _I64]),
     "q3moe_gqa_attention": (_I32, [_P, _I64, _I32, _I32, _I32, _P, _P, _I64, _P, _F, _P, _P,
@@ -314,6 +315,38 @@ def q3moe_attn_prologue(q: torch.Tensor, k: torch.Tensor, q_norm: torch.Tensor,
     _check("q3moe_attn_prologue", library().q3moe_attn_prologue(
         _ptr(q), _ptr(k), T, nq, k.shape[1], D, _ptr(q_norm), _ptr(k_norm), _ptr(positions),
         eps, rope_base, _stream(stream)))
+
+
+def q3moe_bf16_gemv3(Ws, x: torch.Tensor, norm_gain: Optional[torch.Tensor] = None,
+                     eps: float = 0.0, outs=None, stream=None):
+    """Up to three bf16 projections of one input in one launch, optionally
+    after its RMSNorm: Ws a list of 1-3 bf16 [N_i, K] tensors; -> list of
+    f32 [T, N_i] outputs (allocated where outs is None)."""
+    Ws = list(Ws)
+    if not 1 <= len(Ws) <= 3:
+        raise ValueError("one to three matrices")
+    _need(x, "x", torch.float32, 2)
+    T, K = x.shape
+    for i, W in enumerate(Ws):
+        _need(W, f"W{i}", torch.bfloat16, 2)
+        if W.shape[1] != K:
+            raise ValueError("every W must be [N, K] with K = x.shape[1]")
+    if norm_gain is not None:
+        _need(norm_gain, "norm_gain", torch.float32, 1)
+        if norm_gain.numel() != K:
+            raise ValueError("norm_gain must have K elements")
+    if outs is None:
+        outs = [torch.empty((T, W.shape[0]), dtype=torch.float32, device=x.device) for W in Ws]
+    outs = list(outs)
+    for i, o in enumerate(outs):
+        _need(o, f"y{i}", torch.float32, 2)
+    Wp = [_ptr(W) for W in Ws] + [None] * (3 - len(Ws))
+    Np = [W.shape[0] for W in Ws] + [0] * (3 - len(Ws))
+    yp = [_ptr(o) for o in outs] + [None] * (3 - len(outs))
+    _check("q3moe_bf16_gemv3", library().q3moe_bf16_gemv3(
+        Wp[0], Np[0], Wp[1], Np[1], Wp[2], Np[2], K, _ptr(x), T, _ptr(norm_gain), eps,
+        yp[0], yp[1], yp[2], _stream(stream)))
+    return outs
 
 
 def q3moe_rmsnorm(x: torch.Tensor, gain: torch.Tensor, eps: float,

@@ -269,6 +269,42 @@ q3moe_status q3moe_bf16_gemv(const uint16_t* W, int64_t N, int64_t K, const floa
     return from_hip(q3moe::launch_bf16_gemv(W, N, K, x, T, y, accumulate, as_stream(stream)));
 }
 
+q3moe_status q3moe_bf16_gemv3(const uint16_t* W0, int64_t N0, const uint16_t* W1, int64_t N1,
+                              const uint16_t* W2, int64_t N2, int64_t K, const float* x, int64_t T,
+                              const float* norm_gain, float eps, float* y0, float* y1, float* y2,
+                              void* stream) {
+    const int64_t lim = (int64_t)1 << 30;
+    if (T < 0 || T > 0x7fffffff || N0 < 1 || N0 > lim || N1 < 0 || N1 > lim || N2 < 0 || N2 > lim ||
+        K < 8 || (K & 7) || K > lim || (norm_gain && (K > q3moe::kGemvNormMaxK || !(eps >= 0.0f) ||
+                                                       !(eps <= 3.4028235e38f))))
+        return Q3MOE_E_SHAPE;
+    if (T == 0) return Q3MOE_OK;
+    if (!W0 || !x || !y0 || (N1 && (!W1 || !y1)) || (N2 && (!W2 || !y2))) return Q3MOE_E_NULL;
+    if (!aligned16(W0) || (N1 && !aligned16(W1)) || (N2 && !aligned16(W2)) || !aligned16(x) ||
+        (norm_gain && !aligned16(norm_gain)) || (reinterpret_cast<uintptr_t>(y0) & 3u) ||
+        (N1 && (reinterpret_cast<uintptr_t>(y1) & 3u)) || (N2 && (reinterpret_cast<uintptr_t>(y2) & 3u)))
+        return Q3MOE_E_ALIGN;
+    const uint16_t* Ws[3] = {W0, W1, W2};
+    float* ys[3] = {y0, y1, y2};
+    const int64_t Ns[3] = {N0, N1, N2};
+    const size_t nx = (size_t)T * (size_t)K * sizeof(float);
+    for (int i = 0; i < 3; ++i) {
+        if (!Ns[i]) continue;
+        const size_t ny = (size_t)T * (size_t)Ns[i] * sizeof(float);
+        if (overlaps(ys[i], ny, x, nx) || (norm_gain && overlaps(ys[i], ny, norm_gain, (size_t)K * 4)))
+            return Q3MOE_E_ALIAS;
+        for (int j = 0; j < 3; ++j) {
+            if (!Ns[j]) continue;
+            if (overlaps(ys[i], ny, Ws[j], (size_t)Ns[j] * (size_t)K * 2)) return Q3MOE_E_ALIAS;
+            if (j != i && overlaps(ys[i], ny, ys[j], (size_t)T * (size_t)Ns[j] * sizeof(float)))
+                return Q3MOE_E_ALIAS;
+        }
+    }
+    return from_hip(q3moe::launch_bf16_gemv3(W0, N0, N1 ? W1 : nullptr, N1, N2 ? W2 : nullptr, N2, K,
+                                             x, T, norm_gain, eps, y0, N1 ? y1 : nullptr,
+                                             N2 ? y2 : nullptr, as_stream(stream)));
+}
+
 q3moe_status q3moe_kv_write(const float* k_new, const float* v_new, int64_t B, int32_t n_kv_heads,
                             int32_t head_dim, const int32_t* positions, uint16_t* k_cache,
                             uint16_t* v_cache, int64_t S_max, void* stream) {

@@ -103,6 +103,13 @@ hipError_t launch_expert_ffn(const float* hidden, int64_t T, int64_t H, int64_t 
 // layer.hip: the attention side of the decoder layer
 hipError_t launch_bf16_gemv(const uint16_t* W, int64_t N, int64_t K, const float* x, int64_t T,
                             float* y, int accumulate, hipStream_t stream);
+// Up to three matrices on one input in one launch (N1 or N2 may be 0), with
+// the input RMSNorm inside when gain is not null (K <= kGemvNormMaxK).
+constexpr int64_t kGemvNormMaxK = 16384;
+hipError_t launch_bf16_gemv3(const uint16_t* W0, int64_t N0, const uint16_t* W1, int64_t N1,
+                             const uint16_t* W2, int64_t N2, int64_t K, const float* x, int64_t T,
+                             const float* gain, float eps, float* y0, float* y1, float* y2,
+                             hipStream_t stream);
 hipError_t launch_kv_write(const float* k_new, const float* v_new, int64_t B, int32_t n_kv,
                            int32_t D, const int32_t* pos, uint16_t* kcache, uint16_t* vcache,
                            int64_t S_max, hipStream_t stream);

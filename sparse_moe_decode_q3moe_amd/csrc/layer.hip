@@ -26,6 +26,7 @@
 //   attn_combine_kernel: merges the chunk records with the log-sum-exp rule.
 #include "device_common.h"
 #include "internal.h"
+#include "route_common.h"
 
 namespace q3moe {
 
@@ -126,6 +127,29 @@ __device__ __forceinline__ void gv_store_x(float* xs, const float4 (&xr)[NX], in
     for (int u = 0; u < NX; ++u) *reinterpret_cast<float4*>(xs + 4 * (tid + u * kGvThreads)) = xr[u];
 }
 
+// The same with the input RMSNorm applied on the way into LDS: value k of
+// token t becomes gain[k] * x * inv[t], formed in double and rounded once to
+// f32 (gs: the gain in LDS, inv: the tokens' 1 / rms in LDS).
+template <int TT, int R, int NX>
+__device__ __forceinline__ void gv_store_x_norm(float* xs, const float4 (&xr)[NX], int tid, int64_t k0,
+                                                const float* gs, const double* inv, int64_t K) {
+    constexpr int KC = GvShape<TT, R>::KC;
+#pragma unroll
+    for (int u = 0; u < NX; ++u) {
+        const int i = tid + u * kGvThreads;
+        const int t = i / (KC / 4), c = i % (KC / 4);
+        const int64_t k = k0 + 4 * c;
+        float4 v = xr[u];
+        if (k < K) {
+            const double s = inv[t];
+            const float4 g = *reinterpret_cast<const float4*>(gs + k);
+            v = make_float4((float)((double)g.x * v.x * s), (float)((double)g.y * v.y * s),
+                            (float)((double)g.z * v.z * s), (float)((double)g.w * v.w * s));
+        }
+        *reinterpret_cast<float4*>(xs + 4 * i) = v;
+    }
+}
+
 template <int TT, int R, int S>
 __device__ __forceinline__ void gv_mul_chunk(float (&acc)[R * TT], const uint4 (&wb)[S][R], const float* xs,
                                              int lane) {
@@ -158,15 +182,41 @@ __device__ __forceinline__ void gv_mul_chunk(float (&acc)[R * TT], const uint4 (
     }
 }
 
+// Up to three matrices sharing one input: workgroups [0, b1) work on
+// matrix 0, [b1, b2) on matrix 1, the rest on matrix 2.  gain (or null) is
+// the input RMSNorm's gain.
+struct GvJob {
+    const uint16_t* W0;
+    const uint16_t* W1;
+    const uint16_t* W2;
+    float* y0;
+    float* y1;
+    float* y2;
+    int64_t N0, N1, N2;
+    int64_t b1, b2;
+    const float* gain;
+    float eps;
+};
+
 template <int TT, int R>
-__global__ __launch_bounds__(kGvThreads) void bf16_gemv_kernel(
-    const uint16_t* __restrict__ W, int64_t N, int64_t K, const float* __restrict__ x, int64_t T,
-    int64_t t0, float* __restrict__ y, int accumulate) {
+__global__ __launch_bounds__(kGvThreads) void bf16_gemv_kernel(GvJob job, int64_t K,
+                                                               const float* __restrict__ x, int64_t T,
+                                                               int64_t t0, int accumulate) {
     constexpr int KC = GvShape<TT, R>::KC, S = GvShape<TT, R>::S;
     constexpr int V = R * TT;
     __shared__ __align__(16) float xs[TT * KC];
+    __shared__ double inv[TT];
+    __shared__ double part[kGvWaves][TT];
+    extern __shared__ __align__(16) float gs[];              // the gain, K values (norm only)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t n0 = ((int64_t)blockIdx.x * kGvWaves + wave) * R;
+    const int64_t bx = blockIdx.x;
+    const int m = bx < job.b1 ? 0 : (bx < job.b2 ? 1 : 2);
+    const uint16_t* __restrict__ W = m == 0 ? job.W0 : (m == 1 ? job.W1 : job.W2);
+    float* __restrict__ y = m == 0 ? job.y0 : (m == 1 ? job.y1 : job.y2);
+    const int64_t N = m == 0 ? job.N0 : (m == 1 ? job.N1 : job.N2);
+    const int64_t blk = bx - (m == 0 ? 0 : (m == 1 ? job.b1 : job.b2));
+    const int64_t n0 = (blk * kGvWaves + wave) * R;
+    const bool norm = job.gain != nullptr;
     float acc[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) acc[i] = 0.f;
@@ -175,10 +225,46 @@ __global__ __launch_bounds__(kGvThreads) void bf16_gemv_kernel(
     constexpr int NX = GvX<TT, R>::NX;
     float4 xr[NX];
     gv_load_chunk<S, R>(wa, W, N, K, n0, 0, lane);
+    if (norm) {
+        // the gain into LDS and each token's 1 / rms: squares summed in
+        // double (exact f32 squares) over the whole row, in a fixed order
+        for (int64_t kk = tid; kk < K; kk += kGvThreads) gs[kk] = job.gain[kk];
+        // every token's float4 of a chunk in flight together
+        double ss[TT];
+#pragma unroll
+        for (int t = 0; t < TT; ++t) ss[t] = 0.0;
+        for (int64_t c = tid; c < K / 4; c += kGvThreads) {
+            float4 v[TT];
+#pragma unroll
+            for (int t = 0; t < TT; ++t)
+                v[t] = t0 + t < T ? reinterpret_cast<const float4*>(x + (t0 + t) * K)[c]
+                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int t = 0; t < TT; ++t) {
+                double a = fma((double)v[t].x, (double)v[t].x, ss[t]);
+                a = fma((double)v[t].y, (double)v[t].y, a);
+                a = fma((double)v[t].z, (double)v[t].z, a);
+                ss[t] = fma((double)v[t].w, (double)v[t].w, a);
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+            const double w = wave_sum_dpp_f64(ss[t]);
+            if (lane == 0) part[wave][t] = w;
+        }
+        __syncthreads();
+        if (tid < TT) {
+            double tot = 0.0;
+#pragma unroll
+            for (int w = 0; w < kGvWaves; ++w) tot += part[w][tid];
+            inv[tid] = 1.0 / sqrt(tot / (double)K + (double)job.eps);
+        }
+    }
     gv_load_x<TT, R, NX>(xr, x, K, T, t0, 0, tid);
     for (int64_t k0 = 0; k0 < K; k0 += 2 * KC) {
         __syncthreads();
-        gv_store_x<NX>(xs, xr, tid);
+        if (norm) gv_store_x_norm<TT, R, NX>(xs, xr, tid, k0, gs, inv, K);
+        else gv_store_x<NX>(xs, xr, tid);
         __syncthreads();
         if (k0 + KC < K) {
             gv_load_chunk<S, R>(wb, W, N, K, n0, k0 + KC, lane);
@@ -187,7 +273,8 @@ __global__ __launch_bounds__(kGvThreads) void bf16_gemv_kernel(
         gv_mul_chunk<TT, R, S>(acc, wa, xs, lane);
         if (k0 + KC >= K) break;
         __syncthreads();
-        gv_store_x<NX>(xs, xr, tid);
+        if (norm) gv_store_x_norm<TT, R, NX>(xs, xr, tid, k0 + KC, gs, inv, K);
+        else gv_store_x<NX>(xs, xr, tid);
         __syncthreads();
         if (k0 + 2 * KC < K) {
             gv_load_chunk<S, R>(wa, W, N, K, n0, k0 + 2 * KC, lane);
@@ -210,13 +297,23 @@ __global__ __launch_bounds__(kGvThreads) void bf16_gemv_kernel(
 }
 
 template <int TT, int R>
-hipError_t launch_gemv_rt(const uint16_t* W, int64_t N, int64_t K, const float* x, int64_t T,
-                          float* y, int accumulate, hipStream_t stream) {
+hipError_t launch_gemv_rt(GvJob job, int64_t K, const float* x, int64_t T, int accumulate,
+                          hipStream_t stream) {
     const int64_t rows_per_wg = (int64_t)kGvWaves * R;
-    const unsigned grid = (unsigned)((N + rows_per_wg - 1) / rows_per_wg);
+    auto blocks = [&](int64_t n) { return (n + rows_per_wg - 1) / rows_per_wg; };
+    job.b1 = blocks(job.N0);
+    job.b2 = job.b1 + blocks(job.N1);
+    const unsigned grid = (unsigned)(job.b2 + blocks(job.N2));
+    const size_t lds = job.gain ? (size_t)K * sizeof(float) : 0;
+    if (lds) {
+        static LdsLimit lds_set;
+        const hipError_t e = ensure_lds(reinterpret_cast<const void*>(bf16_gemv_kernel<TT, R>), lds_set,
+                                        (int)lds);
+        if (e != hipSuccess) return e;
+    }
     for (int64_t t0 = 0; t0 < T; t0 += TT) {
-        hipLaunchKernelGGL((bf16_gemv_kernel<TT, R>), dim3(grid), dim3(kGvThreads), 0, stream, W, N, K, x,
-                           T, t0, y, accumulate);
+        hipLaunchKernelGGL((bf16_gemv_kernel<TT, R>), dim3(grid), dim3(kGvThreads), lds, stream, job, K, x,
+                           T, t0, accumulate);
         const hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
@@ -224,12 +321,22 @@ hipError_t launch_gemv_rt(const uint16_t* W, int64_t N, int64_t K, const float* 
 }
 
 template <int TT>
-hipError_t launch_gemv_tt(const uint16_t* W, int64_t N, int64_t K, const float* x, int64_t T,
-                          float* y, int accumulate, hipStream_t stream) {
+hipError_t launch_gemv_tt(const GvJob& job, int64_t K, const float* x, int64_t T, int accumulate,
+                          hipStream_t stream) {
     // rows per wave: keep about 1024 waves or more in flight
-    if (N >= 4096) return launch_gemv_rt<TT, 4>(W, N, K, x, T, y, accumulate, stream);
-    if (N >= 2048) return launch_gemv_rt<TT, 2>(W, N, K, x, T, y, accumulate, stream);
-    return launch_gemv_rt<TT, 1>(W, N, K, x, T, y, accumulate, stream);
+    const int64_t N = job.N0 + job.N1 + job.N2;
+    if (N >= 4096) return launch_gemv_rt<TT, 4>(job, K, x, T, accumulate, stream);
+    if (N >= 2048) return launch_gemv_rt<TT, 2>(job, K, x, T, accumulate, stream);
+    return launch_gemv_rt<TT, 1>(job, K, x, T, accumulate, stream);
+}
+
+hipError_t launch_gemv_job(const GvJob& job, int64_t K, const float* x, int64_t T, int accumulate,
+                           hipStream_t stream) {
+    if (T <= 1) return launch_gemv_tt<1>(job, K, x, T, accumulate, stream);
+    if (T <= 2) return launch_gemv_tt<2>(job, K, x, T, accumulate, stream);
+    if (T <= 4) return launch_gemv_tt<4>(job, K, x, T, accumulate, stream);
+    if (T <= 8) return launch_gemv_tt<8>(job, K, x, T, accumulate, stream);
+    return launch_gemv_tt<16>(job, K, x, T, accumulate, stream);
 }
 
 // ------------------------------------------------------------- KV write --
@@ -528,11 +635,16 @@ hipError_t launch_attn_d(const float* q, int64_t B, int32_t n_q, int32_t n_kv, c
 
 hipError_t launch_bf16_gemv(const uint16_t* W, int64_t N, int64_t K, const float* x, int64_t T,
                             float* y, int accumulate, hipStream_t stream) {
-    if (T <= 1) return launch_gemv_tt<1>(W, N, K, x, T, y, accumulate, stream);
-    if (T <= 2) return launch_gemv_tt<2>(W, N, K, x, T, y, accumulate, stream);
-    if (T <= 4) return launch_gemv_tt<4>(W, N, K, x, T, y, accumulate, stream);
-    if (T <= 8) return launch_gemv_tt<8>(W, N, K, x, T, y, accumulate, stream);
-    return launch_gemv_tt<16>(W, N, K, x, T, y, accumulate, stream);
+    GvJob job{W, nullptr, nullptr, y, nullptr, nullptr, N, 0, 0, 0, 0, nullptr, 0.f};
+    return launch_gemv_job(job, K, x, T, accumulate, stream);
+}
+
+hipError_t launch_bf16_gemv3(const uint16_t* W0, int64_t N0, const uint16_t* W1, int64_t N1,
+                             const uint16_t* W2, int64_t N2, int64_t K, const float* x, int64_t T,
+                             const float* gain, float eps, float* y0, float* y1, float* y2,
+                             hipStream_t stream) {
+    GvJob job{W0, W1, W2, y0, y1, y2, N0, N1, N2, 0, 0, gain, eps};
+    return launch_gemv_job(job, K, x, T, 0, stream);
 }
 
 hipError_t launch_kv_write(const float* k_new, const float* v_new, int64_t B, int32_t n_kv,

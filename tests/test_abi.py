@@ -29,7 +29,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(_lib.EXPORTS) == names
@@ -157,6 +157,36 @@ def test_moe_ffn_prenorm_validation(lib):
     # the workspace also holds the normalised rows of the multi-kernel path
     assert need >= lib.q3moe_expert_ffn_workspace_bytes(3, 2048, 768, 128, 8) + \
         lib.q3moe_route_workspace_bytes(3, 128) + 3 * 2048 * 4
+
+
+def _gemv3(lib, T=1, N0=64, N1=8, N2=8, K=64, W0=FAKE, W1=ctypes.c_void_p(0x20000),
+           W2=ctypes.c_void_p(0x30000), x=ctypes.c_void_p(0x40000), gain=ctypes.c_void_p(0x50000),
+           eps=1e-6, y0=ctypes.c_void_p(0x60000), y1=ctypes.c_void_p(0x70000),
+           y2=ctypes.c_void_p(0x80000)):
+    return lib.q3moe_bf16_gemv3(W0, N0, W1, N1, W2, N2, K, x, T, gain, eps, y0, y1, y2, None)
+
+
+def test_bf16_gemv3_validation(lib):
+    """The fused projections check every matrix and output; with the norm,
+    K <= 16384 and a finite eps >= 0.  (Calls that would pass validation are
+    not made here: they would launch.)"""
+    assert _gemv3(lib, T=0) == OK
+    assert _gemv3(lib, N0=0) == E_SHAPE
+    assert _gemv3(lib, N1=-1) == E_SHAPE
+    assert _gemv3(lib, K=60) == E_SHAPE
+    assert _gemv3(lib, K=16392) == E_SHAPE                                # too long for the norm
+    assert _gemv3(lib, eps=-1.0) == E_SHAPE
+    assert _gemv3(lib, eps=float("nan")) == E_SHAPE
+    assert _gemv3(lib, W1=None) == E_NULL
+    assert _gemv3(lib, y2=None) == E_NULL
+    assert _gemv3(lib, x=None) == E_NULL
+    assert _gemv3(lib, W2=ctypes.c_void_p(0x30008)) == E_ALIGN
+    assert _gemv3(lib, gain=ctypes.c_void_p(0x50004)) == E_ALIGN
+    assert _gemv3(lib, y1=ctypes.c_void_p(0x70002)) == E_ALIGN
+    assert _gemv3(lib, y1=ctypes.c_void_p(0x60000 + 128)) == E_ALIAS     # y1 inside y0
+    assert _gemv3(lib, y2=ctypes.c_void_p(0x40000 + 64)) == E_ALIAS      # y2 over x
+    assert _gemv3(lib, y0=ctypes.c_void_p(0x20000 + 32)) == E_ALIAS      # y0 over W1
+    assert _gemv3(lib, y0=ctypes.c_void_p(0x50000 - 16)) == E_ALIAS      # y0 over the gain
 
 
 def _route(lib, T=1, H=2048, E=128, k=8, hidden=FAKE, router=FAKE, idx=FAKE, w=FAKE, ws=FAKE,

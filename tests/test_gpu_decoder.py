@@ -66,6 +66,36 @@ def test_bf16_gemv_parity(T, N, K, acc, seed):
     assert_rows_close(got.cpu().numpy(), ref, what=f"gemv T={T} N={N} K={K}")
 
 
+GEMV3_CASES = [  # T, (N0, N1, N2), K, norm, seed
+    (1, (4096, 512, 512), 2048, True, 21),     # the layer's Q/K/V after its input norm, batch 1
+    (16, (4096, 512, 512), 2048, True, 22),    # batch 16
+    (3, (4096, 512, 512), 2048, False, 23),    # no norm
+    (5, (100, 37, 0), 1032, True, 24),         # ragged rows, two matrices, K not a multiple of 512
+    (17, (300, 0, 0), 2056, True, 25),         # more than 16 tokens: two passes, one matrix
+    (2, (3000, 64, 8), 8200, True, 26),        # K beyond one staged chunk
+    (1, (1, 1, 1), 8, True, 27),               # the smallest shape
+]
+
+
+@pytest.mark.parametrize("T,Ns,K,norm,seed", GEMV3_CASES)
+def test_bf16_gemv3_parity(T, Ns, K, norm, seed):
+    """Up to three projections in one launch, with the input RMSNorm inside:
+    each output against the oracle's RMSNorm then its bf16 GEMV."""
+    say(f"gemv3 T={T} N={Ns} K={K} norm={norm} seed={seed}")
+    g = gen.make_generator(seed)
+    Ws = [gen.bf16_normal((n, K), 0.02, g) for n in Ns if n]
+    x = gen.normal_f32((T, K), 1.0, g)
+    gain = gen.uniform_f32((K,), 0.5, 1.5, g)
+    o = oracle.oracle()
+    xn = o.rmsnorm(x.numpy(), gain.numpy(), 1e-6) if norm else x.numpy()
+    got = q3.q3moe_bf16_gemv3([W.to(DEV) for W in Ws], x.to(DEV),
+                              norm_gain=gain.to(DEV) if norm else None, eps=1e-6)
+    torch.cuda.synchronize()
+    for i, W in enumerate(Ws):
+        ref = o.bf16_gemv(_bits(W), xn)
+        assert_rows_close(got[i].cpu().numpy(), ref, what=f"gemv3 output {i}")
+
+
 def test_bf16_gemv_zero_tokens():
     W = torch.zeros((64, 64), dtype=torch.bfloat16, device=DEV)
     x = torch.zeros((0, 64), dtype=torch.float32, device=DEV)
@@ -207,10 +237,14 @@ def oracle_layer(o, att, moe, x, kc, vc, pos):
 def gpu_layer(att, moe, x, kc, vc, pos, form="separate"):
     s = att.shape
     B = x.shape[0]
-    xn = q3.q3moe_rmsnorm(x, att.in_norm, s.eps)
-    q = q3.q3moe_bf16_gemv(att.wq, xn).view(B, s.n_q, s.D)
-    k = q3.q3moe_bf16_gemv(att.wk, xn).view(B, s.n_kv, s.D)
-    v = q3.q3moe_bf16_gemv(att.wv, xn).view(B, s.n_kv, s.D)
+    if form == "prenorm":                # input norm + Q/K/V in one launch
+        q, k, v = q3.q3moe_bf16_gemv3([att.wq, att.wk, att.wv], x, norm_gain=att.in_norm, eps=s.eps)
+        q, k, v = q.view(B, s.n_q, s.D), k.view(B, s.n_kv, s.D), v.view(B, s.n_kv, s.D)
+    else:
+        xn = q3.q3moe_rmsnorm(x, att.in_norm, s.eps)
+        q = q3.q3moe_bf16_gemv(att.wq, xn).view(B, s.n_q, s.D)
+        k = q3.q3moe_bf16_gemv(att.wk, xn).view(B, s.n_kv, s.D)
+        v = q3.q3moe_bf16_gemv(att.wv, xn).view(B, s.n_kv, s.D)
     q3.q3moe_attn_prologue(q, k, att.q_norm, att.k_norm, pos, s.eps, s.rope_base)
     q3.q3moe_kv_write(k, v, pos, kc, vc)
     a = q3.q3moe_gqa_attention(q, kc, vc, pos + 1, 1.0 / np.sqrt(s.D))
