@@ -250,9 +250,12 @@ __device__ __forceinline__ void gu_compute(const uint8_t* wg, const uint8_t* xp,
 // per task) with each lane owning a column chunk: lane = b*8 + c*2 + hp owns
 // quant bytes 32c + 16hp .. +15 of super-block b, i.e. 16 weights of
 // sub-block 2c (low nibbles) and 16 of sub-block 2c+1 (high nibbles).  The
-// lane loads its weights straight into registers (16 quant bytes and the
-// 16-byte block header per row), so nothing goes through LDS and each row is
-// consumed as soon as its loads land.  The 8 row partials are folded across
+// lane loads its weights straight into registers (16 quant bytes and one
+// dword of the 16-byte block header per row, the four lanes of a quad
+// fetching the four dwords and DPP broadcasts rebuilding the header: a
+// quarter of the address work of a 16-byte header load in every lane), so
+// nothing goes through LDS and each row is consumed as soon as its loads
+// land.  The 8 row partials are folded across
 // the wave with a transposed butterfly: after it, lanes 8q..8q+7 hold row q
 // (q < 4 gate row q, else up row q-4).
 //
@@ -586,9 +589,22 @@ __global__ __launch_bounds__(kDnWaves * kWave) void down_decode_kernel(
 
 // The 8 rows of one gate/up task as this lane's registers: the block header
 // and the lane's 16 quant bytes of gate rows r0..r0+3, then of up rows.
+// hw[i]: dword lane % 4 of row i's 16-byte block header (the quad's four
+// lanes hold the whole header; DPP broadcasts rebuild it in every lane).
 struct GuRows {
-    uint4 hdr[8], qv[8];
+    uint32_t hw[8];
+    uint4 qv[8];
 };
+
+__device__ __forceinline__ uint32_t load_stream4(const uint8_t* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
+
+// Lane k of each quad, in every lane of the quad.
+template <int K>
+__device__ __forceinline__ uint32_t quad_bcast(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, K * 0x55, 0xf, 0xf, false);
+}
 
 // Loads are unconditional (an out-of-range expert reads expert 0's rows and
 // its result is dropped), so they form one straight-line group that the
@@ -603,10 +619,11 @@ __device__ __forceinline__ void gu_rows_load(GuRows& g, int e, int32_t E,
     const int64_t es = e >= 0 && e < E ? e : 0;
     const uint8_t* g0 = gbase + es * gstride + r0 * G::ROWB + b * kQ4KBytes;
     const uint8_t* u0 = ubase + es * ustride + r0 * G::ROWB + b * kQ4KBytes;
+    const int hoff = 4 * (lane & 3);          // the quad shares one block: 4 B each
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const uint8_t* row = (i < 4 ? g0 : u0) + (i & 3) * G::ROWB;
-        g.hdr[i] = load_stream16(row);
+        g.hw[i] = load_stream4(row + hoff);
         g.qv[i] = load_stream16(row + qoff);
     }
 }
@@ -624,7 +641,9 @@ __device__ __forceinline__ void gu_rows_finish(const GuRows& g, const XCols& x, 
     float v[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        v[i] = q4k_cols_row(g.hdr[i], g.qv[i], x);
+        const uint4 hdr = make_uint4(quad_bcast<0>(g.hw[i]), quad_bcast<1>(g.hw[i]),
+                                     quad_bcast<2>(g.hw[i]), quad_bcast<3>(g.hw[i]));
+        v[i] = q4k_cols_row(hdr, g.qv[i], x);
         __builtin_amdgcn_sched_barrier(0);
     }
     const float r = fold8_rows(v, lane);               // lanes 8q..: row q
