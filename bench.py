@@ -383,8 +383,9 @@ def decoder_bench(torch, q3, gen, layers, experts, shape, dev):
     residual.  The residual stream is updated in place, as a decode step
     does; at batch 1 the input norm and the Q/K/V projections are one
     q3moe_bf16_gemv3 launch (at batch 16 four launches, q3moe_rmsnorm and
-    three q3moe_bf16_gemv, measure faster), the post-attention norm, route
-    and expert FFN one q3moe_moe_ffn_prenorm call.  Batch 1 and 16; attention layer copies (36 MB of bf16 weights
+    three q3moe_bf16_gemv, measure faster), Q/K norm + RoPE and the KV write
+    one q3moe_attn_prologue_kv launch, the post-attention norm, route and
+    expert FFN one q3moe_moe_ffn_prenorm call.  Batch 1 and 16; attention layer copies (36 MB of bf16 weights
     each, plus their KV caches) and the 16 MoE layer copies rotate, so the
     Infinity Cache does not serve repeated bytes.  Reported: time per layer
     step, tokens/s, and the algorithmic HBM bytes per step over that time; and
@@ -422,9 +423,8 @@ def decoder_bench(torch, q3, gen, layers, experts, shape, dev):
                 q3.q3moe_bf16_gemv(A.wq, xn, out=q)
                 q3.q3moe_bf16_gemv(A.wk, xn, out=kk)
                 q3.q3moe_bf16_gemv(A.wv, xn, out=vv)
-            q3.q3moe_attn_prologue(q.view(B, nq, D), kk.view(B, nkv, D), A.q_norm, A.k_norm, pos,
-                                   s_.eps, s_.rope_base)
-            q3.q3moe_kv_write(kk.view(B, nkv, D), vv.view(B, nkv, D), pos, kc, vc)
+            q3.q3moe_attn_prologue_kv(q.view(B, nq, D), kk.view(B, nkv, D), vv.view(B, nkv, D),
+                                      A.q_norm, A.k_norm, pos, s_.eps, s_.rope_base, kc, vc)
             q3.q3moe_gqa_attention(q.view(B, nq, D), kc, vc, lens, 1.0 / math.sqrt(D), out=ao,
                                    workspace=ws_a)
             q3.q3moe_bf16_gemv(A.wo, ao.view(B, nq * D), out=x, accumulate=True)

@@ -252,6 +252,22 @@ q3moe_status q3moe_attn_prologue(float *q, float *k, int64_t T, int32_t n_q_head
                                  const int32_t *positions, float eps, float rope_base,
                                  void *stream);
 
+/* The attention prologue and the KV write of the decode step in one launch:
+ * q3moe_attn_prologue on q and k (in place), then, for sequence t (one new
+ * token each, t < T = B), the rotated k and the untouched v rounded to bf16
+ * into cache slot positions[t], exactly as q3moe_kv_write stores them
+ * (a position outside [0, S_max) writes nothing).  Arguments as for those
+ * two calls; v [T x n_kv_heads x head_dim] f32.
+ * Limits: those of both calls; n_q_heads + 2 n_kv_heads <= 65535.
+ * Errors: E_NULL, E_SHAPE, E_ALIAS (any two of q, k, v, the caches and
+ * positions overlap), E_HIP. */
+q3moe_status q3moe_attn_prologue_kv(float *q, float *k, const float *v, int64_t T,
+                                    int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                    const float *q_norm, const float *k_norm,
+                                    const int32_t *positions, float eps, float rope_base,
+                                    uint16_t *k_cache, uint16_t *v_cache, int64_t S_max,
+                                    void *stream);
+
 /* --------------------------------------------------------------- RMSNorm --
  * out[t] = gain * x[t] / sqrt(mean(x[t]^2) + eps) for x [T x n] f32; the
  * per-layer input / post-attention norm of the decoder layer.  The squares

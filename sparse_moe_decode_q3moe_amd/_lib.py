@@ -25,6 +25,7 @@ EXPORTS = (
     "q3moe_attn_prologue", "q3moe_rmsnorm", "q3moe_bf16_gemv", "q3moe_kv_write",
     "q3moe_gqa_attention_workspace_bytes", "q3moe_gqa_attention",
     "q3moe_moe_ffn_workspace_bytes", "q3moe_moe_ffn", "q3moe_moe_ffn_prenorm", "q3moe_bf16_gemv3",
+    "q3moe_attn_prologue_kv",
 )
 
 
@@ -56,6 +57,8 @@ _SIGS = {
     "q3moe_bf16_gemv": (_I32, [_P, _I64, _I64, _P, _I64, _P, _I32, _P]),
     "q3moe_bf16_gemv3": (_I32, [_P, _I64, _P, _I64, _P, _I64, _I64, _P, _I64, _P, _F, _P, _P, _P, _P]),
     "q3moe_kv_write": (_I32, [_P, _P, _I64, _I32, _I32, _P, _P, _P, _I64, _P]),
+    "q3moe_attn_prologue_kv": (_I32, [_P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _P, _F, _F, _P, _P,
+                                      _I64, _P]),
     "q3moe_gqa_attention_workspace_bytes": (ctypes.c_size_t, [_I64, _I32, _I32, _I32, _I64]),
     "q3moe_gqa_attention": (_I32, [_P, _I64, _I32, _I32, _I32, _P, _P, _I64, _P, _F, _P, _P,
                                    ctypes.c_size_t, _P]),
@@ -402,6 +405,33 @@ def q3moe_kv_write(k_new: torch.Tensor, v_new: torch.Tensor, positions: torch.Te
     _check("q3moe_kv_write", library().q3moe_kv_write(
         _ptr(k_new), _ptr(v_new), B, nkv, D, _ptr(positions), _ptr(k_cache), _ptr(v_cache),
         S_max, _stream(stream)))
+
+
+def q3moe_attn_prologue_kv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                           q_norm: torch.Tensor, k_norm: torch.Tensor, positions: torch.Tensor,
+                           eps: float, rope_base: float, k_cache: torch.Tensor,
+                           v_cache: torch.Tensor, stream=None) -> None:
+    """q3moe_attn_prologue on q [B, n_q, D] and k [B, n_kv, D] in place, then
+    the rotated k and v [B, n_kv, D] into the bfloat16 caches [B, n_kv, S_max,
+    D] at positions int32 [B], in one launch."""
+    _need(q, "q", torch.float32, 3)
+    _need(k, "k", torch.float32, 3)
+    _need(v, "v", torch.float32, 3)
+    _need(q_norm, "q_norm", torch.float32, 1)
+    _need(k_norm, "k_norm", torch.float32, 1)
+    _need(positions, "positions", torch.int32, 1)
+    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    _need(v_cache, "v_cache", torch.bfloat16, 4)
+    B, nq, D = q.shape
+    nkv = k.shape[1]
+    S_max = k_cache.shape[2]
+    if tuple(k.shape) != (B, nkv, D) or tuple(v.shape) != (B, nkv, D) or positions.numel() != B \
+            or q_norm.numel() != D or k_norm.numel() != D \
+            or tuple(k_cache.shape) != (B, nkv, S_max, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("inconsistent prologue / KV-write shapes")
+    _check("q3moe_attn_prologue_kv", library().q3moe_attn_prologue_kv(
+        _ptr(q), _ptr(k), _ptr(v), B, nq, nkv, D, _ptr(q_norm), _ptr(k_norm), _ptr(positions),
+        eps, rope_base, _ptr(k_cache), _ptr(v_cache), S_max, _stream(stream)))
 
 
 def q3moe_gqa_attention_workspace_bytes(B: int, n_q: int, n_kv: int, D: int, S_max: int) -> int:

@@ -245,6 +245,34 @@ q3moe_status q3moe_attn_prologue(float* q, float* k, int64_t T, int32_t n_q_head
                                                 as_stream(stream)));
 }
 
+q3moe_status q3moe_attn_prologue_kv(float* q, float* k, const float* v, int64_t T,
+                                    int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                    const float* q_norm, const float* k_norm,
+                                    const int32_t* positions, float eps, float rope_base,
+                                    uint16_t* k_cache, uint16_t* v_cache, int64_t S_max,
+                                    void* stream) {
+    if (T < 0 || T > 0x7fffffff || n_q_heads < 1 || n_kv_heads < 1 ||
+        n_q_heads % n_kv_heads != 0 || head_dim < 2 || head_dim > 512 || (head_dim & 1) ||
+        !(eps >= 0.0f) || !(rope_base > 0.0f) || (int64_t)n_q_heads + 2 * (int64_t)n_kv_heads > 65535 ||
+        S_max < 1)
+        return Q3MOE_E_SHAPE;
+    if (T == 0) return Q3MOE_OK;
+    if (!q || !k || !v || !q_norm || !k_norm || !positions || !k_cache || !v_cache) return Q3MOE_E_NULL;
+    const size_t nqb = (size_t)T * n_q_heads * head_dim * sizeof(float);
+    const size_t nkb = (size_t)T * n_kv_heads * head_dim * sizeof(float);
+    const size_t nc = (size_t)T * n_kv_heads * (size_t)S_max * head_dim * 2;
+    if (overlaps(q, nqb, k, nkb) || overlaps(q, nqb, v, nkb) || overlaps(k, nkb, v, nkb) ||
+        overlaps(k_cache, nc, v_cache, nc) || overlaps(k_cache, nc, q, nqb) ||
+        overlaps(k_cache, nc, k, nkb) || overlaps(k_cache, nc, v, nkb) ||
+        overlaps(v_cache, nc, q, nqb) || overlaps(v_cache, nc, k, nkb) ||
+        overlaps(v_cache, nc, v, nkb) || overlaps(k_cache, nc, positions, (size_t)T * 4) ||
+        overlaps(v_cache, nc, positions, (size_t)T * 4))
+        return Q3MOE_E_ALIAS;
+    return from_hip(q3moe::launch_attn_prologue_kv(q, k, v, T, n_q_heads, n_kv_heads, head_dim, q_norm,
+                                                   k_norm, positions, eps, rope_base, k_cache, v_cache,
+                                                   S_max, as_stream(stream)));
+}
+
 q3moe_status q3moe_rmsnorm(const float* x, int64_t T, int64_t n, const float* gain, float eps,
                            float* out, void* stream) {
     if (T < 0 || T > 0x7fffffff || n < 1 || n > 65536 || !(eps >= 0.0f)) return Q3MOE_E_SHAPE;

@@ -145,6 +145,13 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// f32 -> bf16 bits, round to nearest even; a NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint16_t float_to_bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (uint16_t)((u >> 16) | 0x40);
+    return (uint16_t)bf16_rne_bits(f);
+}
+
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t b) { return __uint_as_float(b << 16); }
 
 struct Pieces4 {

@@ -126,5 +126,9 @@ hipError_t launch_rmsnorm(const float* x, int64_t T, int64_t n, const float* gai
 hipError_t launch_attn_prologue(float* q, float* k, int64_t T, int32_t nq, int32_t nkv,
                                 int32_t D, const float* qn, const float* kn,
                                 const int32_t* pos, float eps, float base, hipStream_t stream);
+hipError_t launch_attn_prologue_kv(float* q, float* k, const float* v, int64_t T, int32_t nq,
+                                   int32_t nkv, int32_t D, const float* qn, const float* kn,
+                                   const int32_t* pos, float eps, float base, uint16_t* kc,
+                                   uint16_t* vc, int64_t S_max, hipStream_t stream);
 
 }  // namespace q3moe

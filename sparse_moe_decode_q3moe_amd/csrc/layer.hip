@@ -340,11 +340,6 @@ hipError_t launch_gemv_job(const GvJob& job, int64_t K, const float* x, int64_t 
 }
 
 // ------------------------------------------------------------- KV write --
-__device__ __forceinline__ uint16_t float_to_bf16_rne(float f) {
-    const uint32_t u = __float_as_uint(f);
-    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (uint16_t)((u >> 16) | 0x40);
-    return (uint16_t)bf16_rne_bits(f);
-}
 
 // grid: B workgroups.  A position outside [0, S_max) writes nothing.
 __global__ void kv_write_kernel(const float* __restrict__ k_new, const float* __restrict__ v_new,

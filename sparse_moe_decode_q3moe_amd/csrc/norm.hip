@@ -38,15 +38,28 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(const float* x, i
 // i = lane, lane + 64, ... < D/2.  RMSNorm over the whole head, then the
 // rotation by pos * base^(-2i/D), with the angle and its sine/cosine in
 // double precision (at position 4095 an f32 angle would carry ~2e-4 rad of
-// rounding error).
+// rounding error).  With caches (kc not null) the kernel also does the KV
+// write of the token: heads nq..nq+nkv-1 store their rotated k, rounded to
+// bf16, at cache slot pos[t] of sequence t, and nkv more waves (heads
+// nq+nkv..) store v there; a position outside [0, S_max) writes nothing.
 constexpr int kMaxPairsPerLane = 4;   // head_dim <= 512
 
 __global__ __launch_bounds__(kWave) void attn_prologue_kernel(
-    float* q, float* k, int32_t nq, int32_t nkv, int32_t D, const float* __restrict__ qn,
-    const float* __restrict__ kn, const int32_t* __restrict__ pos, float eps, float base) {
+    float* q, float* k, const float* __restrict__ v, int32_t nq, int32_t nkv, int32_t D,
+    const float* __restrict__ qn, const float* __restrict__ kn, const int32_t* __restrict__ pos,
+    float eps, float base, uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, int64_t S_max) {
     const int h = blockIdx.y;
     const int64_t t = blockIdx.x;
     const int lane = threadIdx.x;
+    const int slot = kc ? pos[t] : -1;
+    const bool write_kv = kc && slot >= 0 && slot < S_max;
+    if (h >= nq + nkv) {                      // v head: the cache write alone
+        const int64_t g = h - nq - nkv;
+        if (write_kv)
+            for (int i = lane; i < D; i += kWave)
+                vc[((t * nkv + g) * S_max + slot) * D + i] = float_to_bf16_rne(v[(t * nkv + g) * D + i]);
+        return;
+    }
     const bool isq = h < nq;
     float* p = isq ? q + (t * nq + h) * (int64_t)D : k + (t * nkv + (h - nq)) * (int64_t)D;
     const float* g = isq ? qn : kn;
@@ -74,8 +87,14 @@ __global__ __launch_bounds__(kWave) void attn_prologue_kernel(
             double sd, cd;
             sincos(theta, &sd, &cd);
             const float c = (float)cd, s = (float)sd;
-            p[i] = ya * c - yb * s;
-            p[i + half] = ya * s + yb * c;
+            const float ra = ya * c - yb * s, rb = ya * s + yb * c;
+            p[i] = ra;
+            p[i + half] = rb;
+            if (!isq && write_kv) {
+                uint16_t* dst = kc + ((t * nkv + (h - nq)) * S_max + slot) * (int64_t)D;
+                dst[i] = float_to_bf16_rne(ra);
+                dst[i + half] = float_to_bf16_rne(rb);
+            }
         }
     }
 }
@@ -93,7 +112,17 @@ hipError_t launch_attn_prologue(float* q, float* k, int64_t T, int32_t nq, int32
                                 int32_t D, const float* qn, const float* kn, const int32_t* pos,
                                 float eps, float base, hipStream_t stream) {
     hipLaunchKernelGGL(attn_prologue_kernel, dim3((unsigned)T, (unsigned)(nq + nkv)), dim3(kWave),
-                       0, stream, q, k, nq, nkv, D, qn, kn, pos, eps, base);
+                       0, stream, q, k, nullptr, nq, nkv, D, qn, kn, pos, eps, base, nullptr, nullptr,
+                       (int64_t)0);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_prologue_kv(float* q, float* k, const float* v, int64_t T, int32_t nq,
+                                   int32_t nkv, int32_t D, const float* qn, const float* kn,
+                                   const int32_t* pos, float eps, float base, uint16_t* kc,
+                                   uint16_t* vc, int64_t S_max, hipStream_t stream) {
+    hipLaunchKernelGGL(attn_prologue_kernel, dim3((unsigned)T, (unsigned)(nq + 2 * nkv)), dim3(kWave),
+                       0, stream, q, k, v, nq, nkv, D, qn, kn, pos, eps, base, kc, vc, S_max);
     return hipGetLastError();
 }
 

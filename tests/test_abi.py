@@ -29,7 +29,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 19, names
+    assert len(names) == 20, names
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(_lib.EXPORTS) == names
@@ -187,6 +187,28 @@ def test_bf16_gemv3_validation(lib):
     assert _gemv3(lib, y2=ctypes.c_void_p(0x40000 + 64)) == E_ALIAS      # y2 over x
     assert _gemv3(lib, y0=ctypes.c_void_p(0x20000 + 32)) == E_ALIAS      # y0 over W1
     assert _gemv3(lib, y0=ctypes.c_void_p(0x50000 - 16)) == E_ALIAS      # y0 over the gain
+
+
+def _pro_kv(lib, T=1, nq=8, nkv=2, D=64, q=FAKE, k=ctypes.c_void_p(0x20000),
+            v=ctypes.c_void_p(0x30000), pos=ctypes.c_void_p(0x40000), kc=ctypes.c_void_p(0x100000),
+            vc=ctypes.c_void_p(0x200000), S=16, eps=1e-6, base=1e6):
+    g = ctypes.c_void_p(0x50000)
+    return lib.q3moe_attn_prologue_kv(q, k, v, T, nq, nkv, D, g, g, pos, eps, base, kc, vc, S, None)
+
+
+def test_attn_prologue_kv_validation(lib):
+    """The fused prologue + KV write checks the union of both calls'
+    arguments.  (Calls that would pass validation are not made here.)"""
+    assert _pro_kv(lib, T=0) == OK
+    assert _pro_kv(lib, nq=6, nkv=4) == E_SHAPE
+    assert _pro_kv(lib, D=63) == E_SHAPE
+    assert _pro_kv(lib, S=0) == E_SHAPE
+    assert _pro_kv(lib, base=0.0) == E_SHAPE
+    assert _pro_kv(lib, v=None) == E_NULL
+    assert _pro_kv(lib, kc=None) == E_NULL
+    assert _pro_kv(lib, v=ctypes.c_void_p(0x20000 + 64)) == E_ALIAS           # v over k
+    assert _pro_kv(lib, vc=ctypes.c_void_p(0x100000 + 256)) == E_ALIAS        # caches overlap
+    assert _pro_kv(lib, pos=ctypes.c_void_p(0x200000 + 8)) == E_ALIAS         # positions in a cache
 
 
 def _route(lib, T=1, H=2048, E=128, k=8, hidden=FAKE, router=FAKE, idx=FAKE, w=FAKE, ws=FAKE,

@@ -104,6 +104,37 @@ def test_bf16_gemv_zero_tokens():
     assert y.shape == (0, 64)
 
 
+# ------------------------------------------------- prologue + KV write --
+
+@pytest.mark.parametrize("B,pos_list", [(1, [4095]), (16, None), (3, [5, -1, 4096])])
+def test_attn_prologue_kv_matches_two_calls(B, pos_list):
+    """The fused prologue + KV write equals q3moe_attn_prologue followed by
+    q3moe_kv_write bit for bit (q, k and both caches), including positions
+    outside the cache (nothing written)."""
+    say(f"prologue+kv B={B}")
+    s = gen.QWEN3_30B_A3B_ATTN
+    g = gen.make_generator(70 + B)
+    q = gen.normal_f32((B, s.n_q, s.D), 1.0, g)
+    k = gen.normal_f32((B, s.n_kv, s.D), 1.0, g)
+    v = gen.normal_f32((B, s.n_kv, s.D), 1.0, g)
+    qn = gen.uniform_f32((s.D,), 0.5, 1.5, g)
+    kn = gen.uniform_f32((s.D,), 0.5, 1.5, g)
+    pos = torch.tensor(pos_list if pos_list else [s.S_max - 1 - 211 * b for b in range(B)],
+                       dtype=torch.int32)
+    kc, vc = gen.kv_caches(B, s, 80 + B)
+    q1, k1, kc1, vc1 = q.to(DEV), k.to(DEV), kc.to(DEV), vc.to(DEV)
+    q3.q3moe_attn_prologue(q1, k1, qn.to(DEV), kn.to(DEV), pos.to(DEV), s.eps, s.rope_base)
+    q3.q3moe_kv_write(k1, v.to(DEV), pos.to(DEV), kc1, vc1)
+    q2, k2, kc2, vc2 = q.to(DEV), k.to(DEV), kc.to(DEV), vc.to(DEV)
+    q3.q3moe_attn_prologue_kv(q2, k2, v.to(DEV), qn.to(DEV), kn.to(DEV), pos.to(DEV), s.eps,
+                              s.rope_base, kc2, vc2)
+    torch.cuda.synchronize()
+    assert torch.equal(q1.cpu().view(torch.int32), q2.cpu().view(torch.int32))
+    assert torch.equal(k1.cpu().view(torch.int32), k2.cpu().view(torch.int32))
+    assert np.array_equal(_bits(kc1), _bits(kc2))
+    assert np.array_equal(_bits(vc1), _bits(vc2))
+
+
 # --------------------------------------------------------------- KV write --
 
 def test_kv_write_bit_exact():
@@ -245,8 +276,11 @@ def gpu_layer(att, moe, x, kc, vc, pos, form="separate"):
         q = q3.q3moe_bf16_gemv(att.wq, xn).view(B, s.n_q, s.D)
         k = q3.q3moe_bf16_gemv(att.wk, xn).view(B, s.n_kv, s.D)
         v = q3.q3moe_bf16_gemv(att.wv, xn).view(B, s.n_kv, s.D)
-    q3.q3moe_attn_prologue(q, k, att.q_norm, att.k_norm, pos, s.eps, s.rope_base)
-    q3.q3moe_kv_write(k, v, pos, kc, vc)
+    if form == "prenorm":                # prologue and KV write in one launch
+        q3.q3moe_attn_prologue_kv(q, k, v, att.q_norm, att.k_norm, pos, s.eps, s.rope_base, kc, vc)
+    else:
+        q3.q3moe_attn_prologue(q, k, att.q_norm, att.k_norm, pos, s.eps, s.rope_base)
+        q3.q3moe_kv_write(k, v, pos, kc, vc)
     a = q3.q3moe_gqa_attention(q, kc, vc, pos + 1, 1.0 / np.sqrt(s.D))
     x1 = x.clone()
     q3.q3moe_bf16_gemv(att.wo, a.view(B, -1), out=x1, accumulate=True)
