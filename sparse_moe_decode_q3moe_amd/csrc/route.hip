@@ -8,8 +8,8 @@
 // Decode-sized batches (T <= 8) run as ONE kernel: workgroup e computes
 // expert e's logits for every token, and the last workgroup to finish
 // (found with striped completion counters, no waiting) selects the top-k of
-// every token.  Larger batches run a logits kernel over (expert, 8-token
-// tile) and a top-k kernel with one wave per token.
+// every token.  Larger batches run a logits kernel over (4-expert, 16-token)
+// tiles and a top-k kernel with one wave per token.
 //
 // Selection (both paths, topk_wave): k rounds of a wave-wide argmax over the
 // token's logits, larger value first and equal values broken by the lower
@@ -140,18 +140,96 @@ __global__ __launch_bounds__(kRouteThreads) void route_small_kernel(
 }
 
 // ------------------------------------------------------------- T > 8 --
-// grid: (E, ceil(T / 8)).
-__global__ __launch_bounds__(kRouteThreads) void router_logits_kernel(
+// grid: (ceil(E / 4), ceil(T / 8)).  A workgroup computes the logits of 4
+// experts x 8 tokens: each thread takes float4 columns i = tid, tid + 256,
+// ... of the 4 router rows and the 8 token rows and accumulates the 32
+// exact f32 x f32 products per column in double (32 independent sums); the
+// wave then folds its 32 sums over its 64 lanes with a transposed butterfly
+// (lanes 2v, 2v + 1 end with sum v), and the 4 waves' results are added in
+// a fixed order.  Each router row is read once per 8 tokens and each token
+// row once per 4 experts (an expert x 8-token tile read the token rows once
+// per expert: ~590 MB of L2 reads at 512 tokens instead of ~200 MB).
+constexpr int kRtExp = 4, kRtTok = 8;
+constexpr int kRtV = kRtExp * kRtTok;          // 32 sums per thread
+
+// Sum of v[0..32) over the 64 lanes, transposed: lanes 2j and 2j + 1 end
+// with the total of value j.
+__device__ __forceinline__ double transposed_sum32_f64(double (&v)[kRtV], int lane) {
+#pragma unroll
+    for (int lev = 0; lev < 5; ++lev) {
+        const int half = kRtV >> (lev + 1);
+        const int bit = 5 - lev;
+        const bool up = (lane >> bit) & 1;
+        const uint64_t m = up ? ~0ull : 0ull;
+#pragma unroll
+        for (int i = 0; i < half; ++i) {
+            // the selects act on the values' bits: a select between two
+            // array elements would become a select between their addresses
+            // and keep the array out of registers
+            const uint64_t a = __builtin_bit_cast(uint64_t, v[i]);
+            const uint64_t b = __builtin_bit_cast(uint64_t, v[i + half]);
+            const double send = __builtin_bit_cast(double, (a & m) | (b & ~m));
+            const double keep = __builtin_bit_cast(double, (b & m) | (a & ~m));
+            v[i] = keep + __shfl_xor(send, 1 << bit, kWave);
+        }
+    }
+    return v[0] + __shfl_xor(v[0], 1, kWave);
+}
+
+__global__ __launch_bounds__(kRouteThreads) void router_tile_kernel(
     const float* __restrict__ hidden, int64_t T, int64_t H, const float* __restrict__ router,
     int32_t E, double* __restrict__ logits) {
-    const int e = blockIdx.x;
-    const int64_t t0 = (int64_t)blockIdx.y * kRouteTokTile;
-    const int tid = threadIdx.x;
-    const int ntok = (int)((T - t0) < kRouteTokTile ? (T - t0) : kRouteTokTile);
-    double acc[kRouteTokTile];
-    router_row_dots(hidden, t0, ntok, H, router + (int64_t)e * H, tid, acc);
-    const double s = workgroup_token_sums(acc, ntok, tid);
-    if (tid < ntok) logits[(t0 + tid) * E + e] = s;
+    const int64_t e0 = (int64_t)blockIdx.x * kRtExp, t0 = (int64_t)blockIdx.y * kRtTok;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t n4 = H / 4;
+    const float4* r4 = reinterpret_cast<const float4*>(router);
+    const float4* x4 = reinterpret_cast<const float4*>(hidden);
+    // rows past E or T read the last valid row and are multiplied by zero
+    double rkeep[kRtExp], xkeep[kRtTok];
+    int64_t rrow[kRtExp], xrow[kRtTok];
+#pragma unroll
+    for (int e = 0; e < kRtExp; ++e) {
+        rkeep[e] = e0 + e < E ? 1.0 : 0.0;
+        rrow[e] = (e0 + e < E ? e0 + e : E - 1) * n4;
+    }
+#pragma unroll
+    for (int t = 0; t < kRtTok; ++t) {
+        xkeep[t] = t0 + t < T ? 1.0 : 0.0;
+        xrow[t] = (t0 + t < T ? t0 + t : T - 1) * n4;
+    }
+    double acc[kRtV];
+#pragma unroll
+    for (int i = 0; i < kRtV; ++i) acc[i] = 0.0;
+    for (int64_t i = tid; i < n4; i += kRouteThreads) {
+        float4 rv[kRtExp], xv[kRtTok];
+#pragma unroll
+        for (int e = 0; e < kRtExp; ++e) rv[e] = r4[rrow[e] + i];
+#pragma unroll
+        for (int t = 0; t < kRtTok; ++t) xv[t] = x4[xrow[t] + i];
+#pragma unroll
+        for (int e = 0; e < kRtExp; ++e) {
+            const double rx = (double)rv[e].x * rkeep[e], ry = (double)rv[e].y * rkeep[e];
+            const double rz = (double)rv[e].z * rkeep[e], rw = (double)rv[e].w * rkeep[e];
+#pragma unroll
+            for (int t = 0; t < kRtTok; ++t) {
+                double a = fma(rx, (double)xv[t].x * xkeep[t], acc[e * kRtTok + t]);
+                a = fma(ry, (double)xv[t].y * xkeep[t], a);
+                a = fma(rz, (double)xv[t].z * xkeep[t], a);
+                acc[e * kRtTok + t] = fma(rw, (double)xv[t].w * xkeep[t], a);
+            }
+        }
+    }
+    __shared__ double part[kRouteWaves][kRtV];
+    const double ws = transposed_sum32_f64(acc, lane);
+    if ((lane & 1) == 0) part[wave][lane >> 1] = ws;
+    __syncthreads();
+    if (tid < kRtV) {
+        double s = 0.0;
+#pragma unroll
+        for (int w = 0; w < kRouteWaves; ++w) s += part[w][tid];
+        const int64_t e = e0 + tid / kRtTok, t = t0 + tid % kRtTok;
+        if (e < E && t < T) logits[t * E + e] = s;
+    }
 }
 
 // grid: ceil(T / 4) workgroups, one wave per token.
@@ -181,8 +259,8 @@ hipError_t launch_route_nper(const float* hidden, int64_t T, int64_t H, const fl
                            stream, hidden, (int32_t)T, H, router, E, k, idx, w, sync, logits);
         return hipGetLastError();
     }
-    dim3 g1((unsigned)E, (unsigned)((T + kRouteTokTile - 1) / kRouteTokTile));
-    hipLaunchKernelGGL(router_logits_kernel, g1, dim3(kRouteThreads), 0, stream, hidden, T, H,
+    dim3 g1((unsigned)((E + kRtExp - 1) / kRtExp), (unsigned)((T + kRtTok - 1) / kRtTok));
+    hipLaunchKernelGGL(router_tile_kernel, g1, dim3(kRouteThreads), 0, stream, hidden, T, H,
                        router, E, logits);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
