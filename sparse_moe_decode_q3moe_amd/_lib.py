@@ -341,8 +341,12 @@ def q3moe_bf16_gemv3(Ws, x: torch.Tensor, norm_gain: Optional[torch.Tensor] = No
     if outs is None:
         outs = [torch.empty((T, W.shape[0]), dtype=torch.float32, device=x.device) for W in Ws]
     outs = list(outs)
+    if len(outs) != len(Ws):
+        raise ValueError("one output per matrix")
     for i, o in enumerate(outs):
         _need(o, f"y{i}", torch.float32, 2)
+        if tuple(o.shape) != (T, Ws[i].shape[0]):
+            raise ValueError(f"y{i} must be [T, N{i}]")
     Wp = [_ptr(W) for W in Ws] + [None] * (3 - len(Ws))
     Np = [W.shape[0] for W in Ws] + [0] * (3 - len(Ws))
     yp = [_ptr(o) for o in outs] + [None] * (3 - len(outs))

@@ -257,7 +257,8 @@ __global__ __launch_bounds__(kGvThreads) void bf16_gemv_kernel(GvJob job, int64_
             double tot = 0.0;
 #pragma unroll
             for (int w = 0; w < kGvWaves; ++w) tot += part[w][tid];
-            inv[tid] = 1.0 / sqrt(tot / (double)K + (double)job.eps);
+            // slots past T (a partial last pass) are zeros and stay zeros
+            inv[tid] = t0 + tid < T ? 1.0 / sqrt(tot / (double)K + (double)job.eps) : 0.0;
         }
     }
     gv_load_x<TT, R, NX>(xr, x, K, T, t0, 0, tid);
