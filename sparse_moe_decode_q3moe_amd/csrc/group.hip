@@ -24,6 +24,32 @@ constexpr int kGrpThreads = 1024;
 constexpr int kGrpWaves = kGrpThreads / kWave;
 constexpr int kGrpIndexBits = 10;                       // E <= 1024
 
+// Inclusive scan of v over the workgroup's threads in thread order: each
+// wave scans its 64 values with shuffles, wave 0 scans the wave totals
+// (wsum, kGrpWaves ints of LDS), every wave adds the totals before it.  Two
+// barriers; every thread of the workgroup must call it.
+__device__ __forceinline__ int32_t block_inclusive_scan(int32_t v, int32_t* wsum, int tid) {
+    const int lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int32_t t = __shfl_up(v, off, kWave);
+        if (lane >= off) v += t;
+    }
+    if (lane == kWave - 1) wsum[wave] = v;
+    __syncthreads();
+    if (wave == 0) {
+        int32_t w = lane < kGrpWaves ? wsum[lane] : 0;
+#pragma unroll
+        for (int off = 1; off < kGrpWaves; off <<= 1) {
+            const int32_t t = __shfl_up(w, off, kWave);
+            if (lane >= off) w += t;
+        }
+        if (lane < kGrpWaves) wsum[lane] = w;
+    }
+    __syncthreads();
+    return wave > 0 ? v + wsum[wave - 1] : v;
+}
+
 __global__ __launch_bounds__(kGrpThreads) void group_by_expert_kernel(
     const int32_t* __restrict__ idx, int64_t n, int32_t E, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ pairs, int32_t* __restrict__ tile_off,
@@ -55,34 +81,20 @@ __global__ __launch_bounds__(kGrpThreads) void group_by_expert_kernel(
         }
         total = run;
     }
-    scan[tid] = total;
-    __syncthreads();
-    for (int off = 1; off < kGrpThreads; off <<= 1) {  // inclusive scan over experts
-        const int32_t v = tid >= off ? scan[tid - off] : 0;
-        __syncthreads();
-        scan[tid] += v;
-        __syncthreads();
-    }
+    const int32_t incl = block_inclusive_scan(total, scan, tid);   // over experts
     if (tid < E) {
-        const int32_t excl = scan[tid] - total;
+        const int32_t excl = incl - total;
         counts[tid] = total;
         offsets[tid] = excl;
         for (int w = 0; w < kGrpWaves; ++w) hist[w * E + tid] += excl;
     }
-    if (tid == kGrpThreads - 1) offsets[E] = scan[tid];
-    __syncthreads();
+    if (tid == kGrpThreads - 1) offsets[E] = incl;
+    __syncthreads();                                    // wsum is reused below
     if (tile_off) {                                     // tiles of tile_rows pairs per expert
         const int32_t tiles = (total + tile_rows - 1) / tile_rows;
-        scan[tid] = tiles;
-        __syncthreads();
-        for (int off = 1; off < kGrpThreads; off <<= 1) {
-            const int32_t v = tid >= off ? scan[tid - off] : 0;
-            __syncthreads();
-            scan[tid] += v;
-            __syncthreads();
-        }
-        if (tid < E) tile_off[tid] = scan[tid] - tiles;
-        if (tid == kGrpThreads - 1) tile_off[E] = scan[tid];
+        const int32_t tincl = block_inclusive_scan(tiles, scan, tid);
+        if (tid < E) tile_off[tid] = tincl - tiles;
+        if (tid == kGrpThreads - 1) tile_off[E] = tincl;
     }
 
     const uint64_t lower = (1ull << lane) - 1ull;
