@@ -11,8 +11,11 @@
 //       lanes split k in 16-byte pieces (8 weights), so every load is a
 //       1 KiB coalesced row segment.  x is staged in LDS in chunks and shared
 //       by the workgroup's 4 waves; the next chunk's weights and activations
-//       are loaded into registers while the current one is multiplied.  One transposed butterfly finally gives
-//       every lane group one (row, token) total.
+//       are loaded into registers while the current one is multiplied.  One
+//       transposed butterfly finally gives every lane group one (row, token)
+//       total.  One launch can serve up to three matrices on the same input
+//       (workgroups split by matrix) and apply the input RMSNorm on the way
+//       into LDS (the Q/K/V projections after the layer's input norm).
 //   kv_write_kernel: the new token's k and v, rounded to bf16 (nearest even),
 //       into each sequence's cache at its position.
 //   attn_partial_kernel<D, HPW>: flash-decode.  A workgroup per (position

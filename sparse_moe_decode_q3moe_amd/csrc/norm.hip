@@ -1,5 +1,5 @@
 // RMSNorm and the fused attention prologue (per-head Q/K RMSNorm, then NEOX
-// RoPE).  Sources: aprender PR #1228 "The fix" (per-head norm with one gain
+// RoPE, optionally followed by the token's KV-cache write).  Sources: aprender PR #1228 "The fix" (per-head norm with one gain
 // vector per projection, after the bias and before RoPE); SharpInference
 // issue #6 closing comment (NEOX pairing i <-> i + head_dim/2); aprender
 // issue #479 "Fix Applied" (head_dim explicit, not hidden/heads).
