@@ -710,7 +710,7 @@ constexpr int kFzRouteNper = 4;                        // experts per lane in th
 static_assert(kFzWaves * kWave * 4 == kFzNB * kQK, "one float4 of activations per thread and token");
 
 struct FusedLds {
-    int xp_bytes, dn_off, h_off, res_off, flag_off, rp_off, rl_off, lg_off, key_off,
+    int xp_bytes, dn_off, h_off, res_off, flag_off, rp_off, lg_off, key_off,
         key32_off, sel_off, scnt_off, total;
 };
 
@@ -722,12 +722,10 @@ __host__ __device__ inline FusedLds fused_lds(int64_t T, int64_t F, int32_t qtyp
     L.h_off = L.dn_off + kFzMaxSlots * d.tile_pad;                  // h of the unit's token, f32 [slot][F]
     L.res_off = L.h_off + kFzMaxSlots * (int)F * 4;                 // [wave][row] partial sums
     L.flag_off = L.res_off + kFzWaves * kDnRows * 4;                // down waves whose tiles landed
-    // routing in the kernel: per-wave router sums [wave][token] and the
-    // partial logits [token][unit] (at most one unit per workgroup, so at
-    // most kFzMaxUnits)
+    // routing in the kernel: per-wave router sums [wave][token], then the
+    // logits, their keys and the selection
     L.rp_off = L.flag_off + 16;
-    L.rl_off = L.rp_off + kFzWaves * kFzMaxTokens * 8;
-    L.lg_off = L.rl_off + kFzMaxTokens * kFzMaxUnits * 8;              // [token][expert] logits
+    L.lg_off = L.rp_off + kFzWaves * kFzMaxTokens * 8;                 // [token][expert] logits
     L.key_off = L.lg_off + kFzMaxTokens * kFzRouteNper * kWave * 8;    // their order keys
     L.key32_off = L.key_off + kFzMaxTokens * kFzRouteNper * kWave * 8; // and 32-bit screen keys
     L.sel_off = L.key32_off + kFzMaxTokens * kFzRouteNper * kWave * 4; // top-k: idx, value
@@ -791,41 +789,83 @@ __device__ __forceinline__ void dn_unit_quants(const uint8_t* tile, const DnGeom
 // its words until all of them carry the tag.  A wait that runs out ORs
 // `bit` into the status word.
 constexpr int kPollPairs = 6;                          // word pairs per thread and round
+
+// One chunk of that wait: the word pairs c0 + tid + i * kThr (i <
+// kPollPairs, those below np) into v, re-read until this wave's all carry
+// the tag (or the spin limit runs out: `bit` into the status word).
+template <int kThr>
+__device__ __forceinline__ void poll_pairs(const uint64_t* src, int np, int c0, uint32_t tag,
+                                           int tid, u32x4_t (&v)[kPollPairs], int32_t* status,
+                                           int bit) {
+    int spins = 0;
+    while (true) {
+#pragma unroll
+        for (int i = 0; i < kPollPairs; ++i) {
+            const int pi = c0 + tid + i * kThr;
+            const uint64_t* p = src + 2 * (pi < np ? pi : np - 1);
+            asm volatile("global_load_dwordx4 %0, %1, off sc1" : "=v"(v[i]) : "v"(p) : "memory");
+        }
+        // the loads above are not known to the compiler: wait for them
+        // here, before any use of their registers
+        asm volatile("s_waitcnt vmcnt(0)"
+                     : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5])
+                     :
+                     : "memory");
+        bool ok = true;
+#pragma unroll
+        for (int i = 0; i < kPollPairs; ++i)
+            ok = ok && (c0 + tid + i * kThr >= np || (v[i].y == tag && v[i].w == tag));
+        if (__all(ok)) break;
+        if (++spins > kSpinLimit) {
+            if (!ok) __hip_atomic_fetch_or(status, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
 template <int kThr>
 __device__ __forceinline__ void wait_tagged(const uint64_t* src, int n, uint32_t tag,
                                             uint32_t* dst, int tid, int32_t* status, int bit) {
     const int np = n >> 1;
     for (int c0 = 0; c0 < np; c0 += kThr * kPollPairs) {
         u32x4_t v[kPollPairs];
-        int spins = 0;
-        while (true) {
-#pragma unroll
-            for (int i = 0; i < kPollPairs; ++i) {
-                const int pi = c0 + tid + i * kThr;
-                const uint64_t* p = src + 2 * (pi < np ? pi : np - 1);
-                asm volatile("global_load_dwordx4 %0, %1, off sc1" : "=v"(v[i]) : "v"(p) : "memory");
-            }
-            // the loads above are not known to the compiler: wait for them
-            // here, before any use of their registers
-            asm volatile("s_waitcnt vmcnt(0)"
-                         : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5])
-                         :
-                         : "memory");
-            bool ok = true;
-#pragma unroll
-            for (int i = 0; i < kPollPairs; ++i)
-                ok = ok && (c0 + tid + i * kThr >= np || (v[i].y == tag && v[i].w == tag));
-            if (__all(ok)) break;
-            if (++spins > kSpinLimit) {
-                if (!ok) __hip_atomic_fetch_or(status, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                break;
-            }
-            __builtin_amdgcn_s_sleep(1);
-        }
+        poll_pairs<kThr>(src, np, c0, tag, tid, v, status, bit);
 #pragma unroll
         for (int i = 0; i < kPollPairs; ++i) {
             const int pi = c0 + tid + i * kThr;
             if (pi < np) *reinterpret_cast<uint2*>(dst + 2 * pi) = make_uint2(v[i].x, v[i].z);
+        }
+    }
+}
+
+// The router logits of the in-kernel routing from the tagged partial sums:
+// pair t * U + u (U = E * P units, u = e * P + part) holds part `part` of
+// expert e's logit for token t as a double in two tagged words.  The pairs
+// are polled as by wait_tagged (np = T * U <= kThr * kPollPairs, one chunk);
+// the P parts of an expert then sit in P consecutive lanes of one wave (P a
+// power of two <= 8), and the lane holding part 0 sums them in part order,
+// starting from 0.0 as a loop over the parts would, and stores the logit with
+// its order keys.  No LDS round trip of the partials.
+template <int kThr>
+__device__ __forceinline__ void router_logits_from_partials(const uint64_t* src, int np, int P,
+                                                            int E, int U, uint32_t tag, int tid,
+                                                            int lane, int32_t* status, double* lgt,
+                                                            uint64_t* keys, uint32_t* keys32) {
+    u32x4_t v[kPollPairs];
+    poll_pairs<kThr>(src, np, 0, tag, tid, v, status, 4);
+#pragma unroll
+    for (int i = 0; i < kPollPairs; ++i) {
+        if (i * kThr >= np) break;                      // uniform
+        const int pi = tid + i * kThr;
+        const double d = __builtin_bit_cast(double, ((uint64_t)v[i].z << 32) | v[i].x);
+        double sum = 0.0;
+        for (int q = 0; q < P; ++q) sum += __shfl(d, (lane + q) & (kWave - 1), kWave);
+        if (pi < np && (pi & (P - 1)) == 0) {
+            const int t = pi / U, e = (pi - t * U) / P;
+            lgt[t * E + e] = sum;
+            keys[t * E + e] = order_key(sum);
+            keys32[t * E + e] = order_key32(sum);
         }
     }
 }
@@ -990,7 +1030,6 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
         // Routing in the kernel (the route entry point's result, computed
         // redundantly by every workgroup from shared partial logits).
         double* rp = reinterpret_cast<double*>(smem + L.rp_off);      // [wave][token]
-        uint32_t* rl = reinterpret_cast<uint32_t*>(smem + L.rl_off);  // [token][unit] f64 halves
         const int U = E * P, HP = (int)(G::H / P);
         // (a0) thread tid holds values 4*tid .. 4*tid+3 of every token's
         // input (H = 2048 = 4 x 512 threads); with the norm they become
@@ -1076,10 +1115,9 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
         build_x_pieces<kFzMaxTokens>(xv, T, smem, tid);
         // (b) every partial logit of every token, then (c) the top-k of token
         // t on wave t; logit = the sum of the expert's parts in part order
-        wait_tagged<kThr>(rbuf, (int)T * U * 2, tag, rl, tid, status, 4);
-        __syncthreads();
-        // logits of every token (the sum of an expert's parts in part order),
-        // then the top-k by rank counting over the whole workgroup
+        // logits of every token (the sum of an expert's parts in part order)
+        // straight from the polled registers, then the top-k by rank
+        // counting over the whole workgroup
         double* lgt = reinterpret_cast<double*>(smem + L.lg_off);     // [token][expert]
         uint64_t* keys = reinterpret_cast<uint64_t*>(smem + L.key_off);
         uint32_t* keys32 = reinterpret_cast<uint32_t*>(smem + L.key32_off);
@@ -1087,15 +1125,8 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
         double* sel_val = reinterpret_cast<double*>(sel_idx + kFzMaxTokens * kFzMaxSlots);
         int32_t* slot_cnt = reinterpret_cast<int32_t*>(smem + L.scnt_off);
         if (tid < nr) slot_cnt[tid] = 0;
-        for (int i = tid; i < (int)T * E; i += kThr) {
-            const int t = i / E, e = i % E;
-            const double* pl = reinterpret_cast<const double*>(rl) + t * U + e * P;
-            double sum = 0.0;
-            for (int q = 0; q < P; ++q) sum += pl[q];
-            lgt[i] = sum;
-            keys[i] = order_key(sum);
-            keys32[i] = order_key32(sum);
-        }
+        router_logits_from_partials<kThr>(rbuf, (int)T * U, P, E, U, tag, tid, lane, status, lgt,
+                                          keys, keys32);
         __syncthreads();
         // the top-k on the screen keys; if equal screen keys reach the chosen
         // (a slot counter other than 1, the same verdict in every wave) the
