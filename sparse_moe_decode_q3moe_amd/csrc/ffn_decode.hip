@@ -1236,6 +1236,7 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
     const int uw = wave < 4 ? wave : (wave >= kFzGu ? wave - 2 : -1);
     const int iters = (n_units + kUnitThr - 1) / kUnitThr;   // the same for every wave
     float* hl = reinterpret_cast<float*>(smem + L.h_off);
+    int32_t exit_ticket = -1;                 // thread 0: this workgroup's count on its exit stripe
     for (int j = 0; unit < n_dn; unit += grid, ++j) {
         const int64_t t = unit / row_units, r0 = (unit % row_units) * kDnRows;
         if (j > 0) {
@@ -1271,6 +1272,19 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
                 // the token's h: every slot's F values, published by gate/up
                 // waves anywhere on the device
                 wait_tagged<kThr>(hbuf + t * k * F, k * (int)F, tag, reinterpret_cast<uint32_t*>(hl), tid, status, 2);
+                // the workgroup's last read of this call's tagged words: it
+                // counts itself on its exit stripe now, and the atomic's
+                // round trip overlaps the rest (its result is used at exit).
+                // The offset `lane0` (zero in a vector register the compiler
+                // cannot see through) keeps the wave-level atomic rewrite,
+                // whose combining step would wait for the return here, off
+                // this one-lane atomic.
+                if (tid == 0 && unit + grid >= n_dn) {
+                    int lane0 = 0;
+                    asm volatile("" : "+v"(lane0));
+                    exit_ticket = __hip_atomic_fetch_add(sync + kSyncExit + (wg % kStripes) * kLineInts + lane0, 1,
+                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
                 __syncthreads();
             }
             if (uw >= 0) {
@@ -1307,10 +1321,14 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
     }
 
     // ---- exit: the last workgroup advances the epoch and zeroes the counters
+    // (a workgroup counted itself after its last read of tagged words; one
+    // without a down unit counts here)
     if (tid == 0) {
         const int st = wg % kStripes;
-        const int32_t done = __hip_atomic_fetch_add(sync + kSyncExit + st * kLineInts, 1,
-                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int32_t done = exit_ticket >= 0
+                                 ? exit_ticket
+                                 : __hip_atomic_fetch_add(sync + kSyncExit + st * kLineInts, 1,
+                                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (done == stripe_members(st, grid) - 1) {           // this stripe is complete
             const int used = grid < kStripes ? grid : kStripes;
             const int32_t top = __hip_atomic_fetch_add(sync + kSyncExitTop, 1, __ATOMIC_RELAXED,
