@@ -247,22 +247,43 @@ __device__ __forceinline__ void topk_rank_screen(const double* lg, const uint32_
         const int t = T == 1 ? 0 : item / E, e = item - t * E;
         const uint32_t* row = key32 + t * E;
         const uint32_t me = row[e];
-        // quarter q takes the keys j = q + 4i: at every step the four
-        // quarters of a wave read four consecutive words (four banks, each
-        // read broadcast to its 16 lanes); quarters of 32 consecutive keys
-        // would all fall in one bank
-        const int nj = (E - qtr + 3) >> 2;
-        const uint32_t* rq = row + qtr;
         int gt = 0;
-        int i = 0;
-        for (; i + 8 <= nj; i += 8) {                   // 8 reads in flight, no branches
-            uint32_t kj[8];
+        if ((E & 15) == 0) {
+            // quarter q takes the 4-key chunks j = 16i + 4q + c: at every
+            // step the four quarters of a wave read four consecutive 16-byte
+            // chunks (16 banks, each read broadcast to its 16 lanes)
+            const uint4* rq = reinterpret_cast<const uint4*>(row) + qtr;
+            const int nb = E >> 4;
+            int i = 0;
+            for (; i + 8 <= nb; i += 8) {               // 8 reads (32 keys) in flight, no branches
+                uint4 kj[8];
 #pragma unroll
-            for (int m = 0; m < 8; ++m) kj[m] = rq[4 * (i + m)];
+                for (int m = 0; m < 8; ++m) kj[m] = rq[4 * (i + m)];
 #pragma unroll
-            for (int m = 0; m < 8; ++m) gt += (int)(kj[m] > me);
+                for (int m = 0; m < 8; ++m)
+                    gt += (int)(kj[m].x > me) + (int)(kj[m].y > me) + (int)(kj[m].z > me) +
+                          (int)(kj[m].w > me);
+            }
+            for (; i < nb; ++i) {
+                const uint4 kv = rq[4 * i];
+                gt += (int)(kv.x > me) + (int)(kv.y > me) + (int)(kv.z > me) + (int)(kv.w > me);
+            }
+        } else {
+            // quarter q takes the keys j = q + 4i (four consecutive words,
+            // four banks, at every step of a wave); quarters of 32
+            // consecutive keys would all fall in one bank
+            const int nj = (E - qtr + 3) >> 2;
+            const uint32_t* rq = row + qtr;
+            int i = 0;
+            for (; i + 8 <= nj; i += 8) {               // 8 reads in flight, no branches
+                uint32_t kj[8];
+#pragma unroll
+                for (int m = 0; m < 8; ++m) kj[m] = rq[4 * (i + m)];
+#pragma unroll
+                for (int m = 0; m < 8; ++m) gt += (int)(kj[m] > me);
+            }
+            for (; i < nj; ++i) gt += (int)(rq[4 * i] > me);
         }
-        for (; i < nj; ++i) gt += (int)(rq[4 * i] > me);
         // the 4 quarter counts of an expert sit in one quad of lanes
         int cnt = gt + __builtin_amdgcn_update_dpp(0, gt, kDppQuadXor1, 0xf, 0xf, false);
         cnt += __builtin_amdgcn_update_dpp(0, cnt, kDppQuadXor2, 0xf, 0xf, false);
