@@ -21,9 +21,13 @@ replayed; the timed region is bracketed by device synchronisation.
 The step is one kernel launch, so the HIP events around the timed region
 give its average duration per launch and its achieved HBM bandwidth against
 the MI355X peak of 8 TB/s; the expert FFN alone (routing given) is timed the
-same way over a graph of FFN-only launches.  The CPU baseline times the oracle (test
-infrastructure, plain scalar C) on a bounded sample of the same workload on
-the host cores, and checks the GPU outputs of the sampled steps against it.
+same way over a graph of FFN-only launches.  The outputs and expert indices
+the timed launches leave are copied right after the timed region and
+checked against the oracle; the status word of every timed workspace is
+read (non-zero: a bounded wait ran out), and either failure makes the run
+exit non-zero.  The CPU baseline times the oracle (test infrastructure,
+plain scalar C) on bounded samples of every configuration on the host cores
+(threaded and, for the headline, on one thread), with the CPU model.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -199,6 +203,11 @@ def main():
     wall = time.perf_counter() - t0
     ms = ev0.elapsed_time(ev1)
     ms_per_step = ms / args.steps
+    # what the timed launches left, before the FFN-only and two-call graphs
+    # overwrite the same buffers: the correctness guard checks these
+    timed = {"out": outs.clone(), "idx": idx.clone(), "w": wts.clone()}
+    status = {"moe_block_workspace": q3.expert_ffn_status(ws_moe, 1, H, F, E, k)}
+    persistent = q3.q3moe_persistent_path(1, H, F, E, k, shape.down_qtype, True)
 
     # expert-FFN launches alone (routing already in idx/wts), timed with HIP
     # events on the stream the graph runs on
@@ -216,6 +225,8 @@ def main():
     kb.record()
     torch.cuda.synchronize()
     two_us = ka.elapsed_time(kb) * 1000.0 / (args.kernel_reps * GRAPH_STEPS)
+    status["expert_ffn_workspace"] = q3.expert_ffn_status(ws_ffn, 1, H, F, E, k)
+    ceiling = stream_ceiling(torch, dev)
     # the steps of the timed region are one kernel launch each
     block_us = ms_per_step * 1000.0
 
@@ -261,7 +272,9 @@ def main():
             "traffic": measured_traffic(),
             "bytes_per_launch": step_bytes,
             "avg_launch_us": round(block_us, 3),
+            "persistent_path": persistent,
         },
+        "same_box_stream_ceiling": ceiling,
         "two_calls": {
             "note": "the same step as q3moe_route + q3moe_expert_ffn (two launches)",
             "us_per_step": round(two_us, 3),
@@ -271,28 +284,94 @@ def main():
         },
     }
 
+    cpu = None if args.no_cpu_baseline else CpuLeg()
+
     if not args.no_prefill:
-        result["prefill_512"] = prefill_bench(torch, q3, gen, layers, experts, shape, dev)
+        result["prefill_512"] = prefill_bench(torch, q3, gen, layers, experts, shape, dev, cpu, status)
 
     if not args.no_layer:
-        result["decoder_layer"] = decoder_bench(torch, q3, gen, layers, experts, shape, dev)
+        result["decoder_layer"] = decoder_bench(torch, q3, gen, layers, experts, shape, dev, cpu,
+                                                status)
 
     if not args.no_stack:
-        result["stack_48"] = stack_bench(torch, q3, gen, shape, dev)
+        result["stack_48"] = stack_bench(torch, q3, gen, shape, dev, cpu, status)
 
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(args, torch, gen, layers, xs, outs, shape)
+    if cpu is not None:
+        result["cpu_baseline"] = cpu_baseline(args, cpu, torch, gen, layers, xs, timed, shape)
 
+    result["status_words"] = status
+    bad_status = {n: v for n, v in status.items() if v != 0}
     print(json.dumps(result), flush=True)
-    if result.get("cpu_baseline", {}).get("guard_ok") is False:
+    if bad_status:
+        print(f"bench.py: a bounded wait ran out (status words {bad_status}); the outputs of "
+              "those calls are invalid", file=sys.stderr)
         sys.exit(1)
+    if result.get("cpu_baseline", {}).get("guard_ok") is False:
+        print("bench.py: the timed kernel's outputs differ from the oracle", file=sys.stderr)
+        sys.exit(1)
+
+
+def stream_ceiling(torch, dev):
+    """A same-box practical ceiling for context (the roofline fraction stays
+    against the 8 TB/s specification): torch's own device copy of 1 GiB
+    (bytes read + written per second) and its full sum over 2 GiB of f32
+    (bytes read per second), median of 5 timed runs each."""
+    res = {}
+    a = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    c = torch.empty(1 << 29, dtype=torch.float32, device=dev).fill_(1.0)
+    for name, fn, nbytes in (("copy_1GiB_read_plus_write", lambda: b.copy_(a), 2 * a.numel() * 4),
+                             ("sum_2GiB_read", lambda: c.sum(), c.numel() * 4)):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ts.sort()
+        res[name + "_gbps"] = round(nbytes / (ts[2] * 1e-3) / 1e9, 1)
+    del a, b, c
+    torch.cuda.empty_cache()
+    return res
+
+
+class CpuLeg:
+    """Oracle timings and guards that the configuration benches record while
+    their device data is alive; cpu_baseline() reports them."""
+
+    def __init__(self):
+        import oracle
+        self.o = oracle.oracle()
+        self.configs = {}
+        self.guards = {}
+
+    def timed(self, fn):
+        t0 = time.perf_counter()
+        r = fn()
+        return r, time.perf_counter() - t0
+
+
+def rel_l2_max(got, ref):
+    import numpy as np
+    got = np.asarray(got, np.float64).reshape(len(got), -1)
+    ref = np.asarray(ref, np.float64).reshape(len(ref), -1)
+    return float((np.linalg.norm(got - ref, axis=1) / np.maximum(np.linalg.norm(ref, axis=1), 1e-30)).max())
+
+
+def host_tensors(gen, L, down_qtype):
+    return ((L.gate.cpu().numpy(), gen.Q4_K), (L.up.cpu().numpy(), gen.Q4_K),
+            (L.down.cpu().numpy(), down_qtype))
 
 
 PREFILL_T = 512
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 
 
-def prefill_bench(torch, q3, gen, layers, experts, shape, dev):
+def prefill_bench(torch, q3, gen, layers, experts, shape, dev, cpu=None, status=None):
     """The same layer at T = 512 tokens per step (the batched path: grouping
     by expert and matrix-core tiles), uniform and skewed routing.  Steps
     rotate through the 16 layer copies; each step touches (almost) every
@@ -357,6 +436,8 @@ def prefill_bench(torch, q3, gen, layers, experts, shape, dev):
         b.record()
         torch.cuda.synchronize()
         ffn_us = a.elapsed_time(b) * 1000.0 / (reps * n)
+        if name == "uniform":                      # the last step's results, for the guard
+            snap = (out.clone(), idx.clone(), (n - 1) % len(layers))
         d_avg = sum(distinct) / len(distinct)
         ffn_bytes = d_avg * expert_b + 2 * T * H * 4
         res[name] = {
@@ -372,10 +453,26 @@ def prefill_bench(torch, q3, gen, layers, experts, shape, dev):
         del g, gf
     res["note"] = ("bf16 matrix-core tiles with the activations split into bf16 pieces (3 for "
                    "gate/up, 2 for down), so the MFMA work is 2.5x the algorithmic flops")
+    if status is not None:
+        status["prefill_workspace"] = q3.expert_ffn_status(ws_f, T, H, F, E, k)
+    if cpu is not None:                            # the oracle on all 512 tokens of that step
+        import numpy as np
+        g_out, g_idx, li = snap
+        L = layers[li]
+        router = L.router.cpu().numpy()
+        tens = host_tensors(gen, L, shape.down_qtype)
+        xh = x_uni.cpu().numpy()
+        (ref, ridx, _, _), t = cpu.timed(lambda: cpu.o.moe_block(xh, router, k, *tens, F=F, E=E))
+        cpu.configs["prefill_512_uniform"] = {
+            "tokens_per_s": round(T / t, 2), "tokens": T, "oracle_s": round(t, 2)}
+        err = rel_l2_max(g_out.cpu().numpy(), ref)
+        same = bool(np.array_equal(g_idx.cpu().numpy(), ridx))
+        cpu.guards["prefill_512_uniform"] = {"indices_equal": same, "max_rel_l2": err,
+                                             "ok": same and err <= 1e-4}
     return res
 
 
-def decoder_bench(torch, q3, gen, layers, experts, shape, dev):
+def decoder_bench(torch, q3, gen, layers, experts, shape, dev, cpu=None, status=None):
     """The whole Qwen3-30B-A3B decoder layer at decode: input RMSNorm, bf16
     Q/K/V projections, Q/K norm + RoPE, KV write, GQA attention over 4096
     cached positions (sequence b at position 4095 - 211 b), O projection with
@@ -437,6 +534,27 @@ def decoder_bench(torch, q3, gen, layers, experts, shape, dev):
                                      *experts[i % len(experts)], F=F, out=x, accumulate=True,
                                      topk_idx=idx, topk_w=wts, workspace=ws_m)
 
+        if cpu is not None:                        # inputs of one eager layer step, for the guard
+            x_in = x.cpu().numpy()
+            kc_in, vc_in = (gen.bf16_bits(c) for c in caches[0])
+            layer(0)
+            torch.cuda.synchronize()
+            got = (x.cpu().numpy(), idx.cpu().numpy())
+            A, L = atts[0], layers[0]
+            w_bits = [gen.bf16_bits(t) for t in (A.wq, A.wk, A.wv, A.wo)]
+            gains = [t.cpu().numpy() for t in (A.in_norm, A.post_norm, A.q_norm, A.k_norm)]
+            tens = host_tensors(gen, L, shape.down_qtype)
+            router = L.router.cpu().numpy()
+            pos_h = pos.cpu().numpy()
+            (ref, ridx, _, _, _), t = cpu.timed(lambda: cpu.o.decoder_layer(
+                x_in, *w_bits, *gains, kc_in, vc_in, pos_h, nq, nkv, D, s_.eps, s_.rope_base,
+                router, k, *tens, F=F, E=E))
+            cpu.configs[f"decoder_layer_batch_{B}"] = {
+                "tokens_per_s": round(B / t, 2), "tokens": B, "oracle_s": round(t, 3)}
+            err = rel_l2_max(got[0], ref)
+            same = bool((got[1] == ridx).all())
+            cpu.guards[f"decoder_layer_batch_{B}"] = {"indices_equal": same, "max_rel_l2": err,
+                                                      "ok": same and err <= 1e-4}
         n = 16
         for i in range(n):
             layer(i)
@@ -478,6 +596,8 @@ def decoder_bench(torch, q3, gen, layers, experts, shape, dev):
             "attention_hbm_gbps": round(att_bytes / (times["attention"] * 1e-6) / 1e9, 1),
             "distinct_experts_per_step": round(d_avg, 2),
         }
+        if status is not None:
+            status[f"decoder_layer_batch_{B}_moe_workspace"] = q3.expert_ffn_status(ws_m, B, H, F, E, k)
         del graphs, atts, caches
         torch.cuda.empty_cache()
     return res
@@ -487,7 +607,7 @@ STACK_LAYERS = 48
 STACK_TOKENS = 8
 
 
-def stack_bench(torch, q3, gen, shape, dev):
+def stack_bench(torch, q3, gen, shape, dev, cpu=None, status=None):
     """48 stacked MoE layers at the same shape, batch-1 decode: down Q6_K in
     layers 0-23 and Q4_K in 24-47 (17.55 GB of seeded expert weights
     resident in HBM, far beyond the 256 MB Infinity Cache, so nothing is
@@ -552,6 +672,10 @@ def stack_bench(torch, q3, gen, shape, dev):
     two_us = time_tokens(token_two_calls)
     tok_us = time_tokens(token)
     finite = bool(torch.isfinite(x).all().item())
+    if status is not None:
+        status["stack_48_workspace"] = q3.expert_ffn_status(ws, 1, H, F, E, k)
+    if cpu is not None:
+        stack_oracle(torch, q3, gen, shape, cpu, stack, x0, x, ones, idx, wts, ws, EPS)
     expert_bytes = sum(k * (2 * shape.gate_stride + L.down[0].numel()) for *_, L in stack)
     tok_bytes = expert_bytes + STACK_LAYERS * (E * H * 4 + 3 * H * 4 * 2)
     res = {
@@ -574,46 +698,137 @@ def stack_bench(torch, q3, gen, shape, dev):
     return res
 
 
-def cpu_baseline(args, torch, gen, layers, xs, outs, shape):
-    """The oracle on a bounded sample of the same workload: layer copy 0
-    (copied to the host once, untimed) on the graph steps that used it plus
-    fresh seeded hidden vectors, until ~cpu_seconds of oracle time.  The GPU
-    outputs of the graph steps in the sample are checked against it."""
-    import numpy as np
-    import oracle
+STACK_ORACLE_TOKENS = 2
 
-    o = oracle.oracle()
+
+def stack_oracle(torch, q3, gen, shape, cpu, stack, x0, x, ones, idx, wts, ws, eps):
+    """The oracle through all 48 layers for the first STACK_ORACLE_TOKENS
+    tokens (each layer's tensors copied to the host once, untimed; only the
+    oracle's own calls are timed), beside an eager GPU pass of the same
+    tokens with the timed entry point, recording every layer's routing."""
+    import numpy as np
+    H, E, k, F = shape.H, shape.E, shape.k, shape.F
+    nt = STACK_ORACLE_TOKENS
+    g_idx = np.empty((nt, len(stack), k), np.int32)
+    g_out = np.empty((nt, H), np.float32)
+    for i in range(nt):
+        x.copy_(x0[i])
+        for l, (router, g_, u_, d_, _) in enumerate(stack):
+            q3.q3moe_moe_ffn_prenorm(x, ones, eps, router, k, g_, u_, d_, F=F, out=x,
+                                     accumulate=True, topk_idx=idx, topk_w=wts, workspace=ws)
+            g_idx[i, l] = idx.cpu().numpy()[0]
+        g_out[i] = x.cpu().numpy()[0]
+    xh = x0[:nt].cpu().numpy().reshape(nt, H)
+    gain = np.ones(H, np.float32)
+    t_orc = 0.0
+    same_layers = 0
+    for l, (router, _, _, _, L) in enumerate(stack):
+        tens = host_tensors(gen, L, gen.stack_down_qtype(l))
+        rh = router.cpu().numpy()
+        (xh, ridx, _, _), t = cpu.timed(lambda: cpu.o.moe_block(
+            xh, rh, k, *tens, F=F, E=E, norm_gain=gain, eps=eps, residual=True))
+        t_orc += t
+        same_layers += int(np.array_equal(g_idx[:, l], ridx))
+    cpu.configs["stack_48_decode"] = {
+        "tokens_per_s": round(nt / t_orc, 3), "tokens": nt, "layers": len(stack),
+        "oracle_s": round(t_orc, 2)}
+    err = rel_l2_max(g_out, xh)
+    cpu.guards["stack_48_decode"] = {
+        "layers_with_equal_routing": same_layers, "final_max_rel_l2": err,
+        "ok": same_layers == len(stack) and err <= 1e-3,
+        "note": "free-running chains on both sides; routing compared at every layer"}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(args, cpu, torch, gen, layers, xs, timed, shape):
+    """The oracle (plain scalar C, double accumulation; a correctness
+    reference, not a tuned CPU kernel) on the host cores, on bounded samples
+    of the same workloads.  Headline (batch-1 decode, one layer): layer copy 0
+    (copied to the host once, untimed) on the timed graph's own steps that
+    used it, then fresh seeded hidden vectors, until ~cpu_seconds of oracle
+    time with every thread the process may use, and ~cpu_seconds/3 on one
+    thread.  The guard compares the timed launches' outputs and expert
+    indices (copied right after the timed region) with the oracle.  The other
+    configurations' oracle timings and guards were taken by their benches."""
+    import numpy as np
+
+    o = cpu.o
+    threads = o.max_threads()
     L0 = layers[0]
     router = L0.router.cpu().numpy()
-    tens = ((L0.gate.cpu().numpy(), gen.Q4_K), (L0.up.cpu().numpy(), gen.Q4_K),
-            (L0.down.cpu().numpy(), shape.down_qtype))
+    tens = host_tensors(gen, L0, shape.down_qtype)
     guard_steps = list(range(0, GRAPH_STEPS, N_LAYER_COPIES))
     extra = gen.hidden_states(4096, shape.H, 99).numpy()
-    max_err = 0.0
-    n = 0
-    t_cpu = 0.0
-    while t_cpu < args.cpu_seconds and n < 4096 + len(guard_steps):
-        x = xs[guard_steps[n]].cpu().numpy() if n < len(guard_steps) else extra[n - len(guard_steps)][None]
-        t0 = time.perf_counter()
-        idx, w, _ = o.route(x, router, shape.k)
-        y = o.expert_ffn(x, idx, w, *tens, F=shape.F, E=shape.E)
-        t_cpu += time.perf_counter() - t0
-        if n < len(guard_steps):
-            g = outs[guard_steps[n]].cpu().numpy().astype(np.float64)
-            err = np.linalg.norm(g - y) / np.linalg.norm(y)
-            max_err = max(max_err, float(err))
-        n += 1
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    max_err, idx_ok = 0.0, True
+
+    def run(budget, guard):
+        nonlocal max_err, idx_ok
+        n, t_cpu = 0, 0.0
+        while t_cpu < budget and n < 4096:
+            use_guard = guard and n < len(guard_steps)
+            x = xs[guard_steps[n]].cpu().numpy() if use_guard else extra[n][None]
+            (y, ridx, _, _), t = cpu.timed(lambda: o.moe_block(x, router, shape.k, *tens,
+                                                               F=shape.F, E=shape.E))
+            t_cpu += t
+            if use_guard:
+                g = timed["out"][guard_steps[n]].cpu().numpy()
+                max_err = max(max_err, rel_l2_max(g, y))
+                idx_ok = idx_ok and bool(np.array_equal(timed["idx"][guard_steps[n]].cpu().numpy(), ridx))
+            n += 1
+        return n, t_cpu
+
+    n, t_cpu = run(args.cpu_seconds, True)
+    o.set_threads(1)
+    try:
+        n1, t1 = run(max(1.0, args.cpu_seconds / 3), False)
+    finally:
+        o.set_threads(threads)
+
+    # the tiny layer (4 tokens, 8 experts, top-2) in full
+    tiny = gen.moe_layer(gen.TINY, 2024)
+    xt = gen.hidden_states(gen.TINY.T, gen.TINY.H, 2025).numpy()
+    tt = host_tensors(gen, tiny, gen.TINY.down_qtype)
+    reps, t_tiny = 0, 0.0
+    while t_tiny < 0.5:
+        _, t = cpu.timed(lambda: o.moe_block(xt, tiny.router.numpy(), gen.TINY.k, *tt,
+                                             F=gen.TINY.F, E=gen.TINY.E))
+        t_tiny += t
+        reps += 1
+    cpu.configs["tiny_T4"] = {"tokens_per_s": round(reps * gen.TINY.T / t_tiny, 1),
+                              "tokens": reps * gen.TINY.T}
+
+    headline_ok = bool(max_err <= 1e-4 and idx_ok)
+    others_ok = all(g["ok"] for name, g in cpu.guards.items() if name != "stack_48_decode")
     return {
         "value": round(n / t_cpu, 2),
         "unit": "tokens/s",
         "cores": threads,
         "kind": "oracle",
         "sample": f"{n} batch-1 decode tokens through one seeded 30B-A3B MoE layer "
-                  f"({len(guard_steps)} of them the GPU graph's own steps), "
-                  f"{t_cpu:.1f} s of oracle time, OpenMP over rows",
+                  f"({len(guard_steps)} of them the timed graph's own steps), {t_cpu:.1f} s of "
+                  f"oracle time, OpenMP over rows with {threads} threads",
+        "cpu_model": cpu_model(),
+        "logical_cpus_visible": len(os.sched_getaffinity(0)),
+        "single_thread": {"value": round(n1 / t1, 2), "unit": "tokens/s", "cores": 1,
+                          "sample": f"{n1} batch-1 decode tokens, {t1:.1f} s"},
+        "configs": cpu.configs,
         "guard_max_rel_l2": max_err,
-        "guard_ok": bool(max_err <= 1e-4),
+        "guard_indices_equal": idx_ok,
+        "guard_ok": headline_ok and others_ok,
+        "guards": cpu.guards,
+        "note": "the oracle is the correctness reference (double accumulation), not a tuned "
+                "CPU kernel",
     }
 
 

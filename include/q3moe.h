@@ -13,7 +13,14 @@
  *    must stay alive until the stream has passed the work.
  *  - The library keeps no pointer after a call returns and holds no mutable
  *    global state; concurrent calls on different streams with disjoint
- *    buffers are safe.
+ *    buffers are safe, with one exception: two calls that each run as the
+ *    persistent kernel (q3moe_persistent_path returns 1) must not overlap in
+ *    time on one device.  That kernel's workgroups wait on each other, so
+ *    all of them must be resident at once; two such launches could each
+ *    hold part of the compute units and wait for workgroups that cannot
+ *    start.  Their waits are bounded, so neither hangs, but the output is
+ *    then invalid and the status word of the workspace says so.  Issue
+ *    such calls on one stream (or otherwise ordered).
  *  - T = 0 (no tokens) is valid and enqueues nothing.
  *  - Q3MOE_E_HIP reports a failed kernel launch (hipGetLastError).
  *
@@ -161,7 +168,11 @@ q3moe_status q3moe_group_by_expert(const int32_t *topk_idx, int64_t T, int32_t t
  * Calls that overlap in time (different streams) need different workspaces.
  * For small T the library runs the whole FFN as one persistent kernel with
  * at most one workgroup per compute unit, whose down-projection threads wait
- * for h words carrying the current tag; each wait is bounded.  The int32 at
+ * for h words carrying the current tag; each wait is bounded.  Its
+ * workgroups must all be resident at once: the grid is sized from the
+ * compute-unit count and the occupancy calculator, and a device that cannot
+ * hold one workgroup per unit gets the separate kernels instead; overlapping
+ * persistent calls are excluded by the common contract above.  The int32 at
  * byte offset q3moe_expert_ffn_status_offset(...) of the workspace is a
  * sticky status word: it stays 0 unless a bounded wait ran out, in which
  * case that call's output is invalid.
@@ -205,6 +216,17 @@ q3moe_status q3moe_moe_ffn(const float *hidden, int64_t T, int64_t H, int64_t F,
                            q3moe_experts gate, q3moe_experts up, q3moe_experts down,
                            int32_t *topk_idx, float *topk_w, float *out, int32_t accumulate,
                            void *workspace, size_t workspace_bytes, void *stream);
+
+/* Which form q3moe_moe_ffn / q3moe_moe_ffn_prenorm (with_route = 1) or
+ * q3moe_expert_ffn (with_route = 0) takes for this shape on the CURRENT
+ * device: 1 = the one persistent kernel (its workgroups wait on each other
+ * and must all be resident at once; see the common contract), 0 = separate
+ * kernels that never wait on each other (also for T = 0), -1 = arguments
+ * the calls would reject (down_qtype is Q3MOE_Q4_K or Q3MOE_Q6_K).  The
+ * answer depends on the device's compute-unit count and on how many
+ * workgroups of the kernel one unit holds (registers, waves, LDS). */
+int32_t q3moe_persistent_path(int64_t T, int64_t H, int64_t F, int32_t E, int32_t top_k,
+                              int32_t down_qtype, int32_t with_route);
 
 /* ------------------------------------------------- MoE block after RMSNorm --
  * The MoE block of a pre-norm decoder layer: its input is the token's hidden

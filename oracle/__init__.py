@@ -65,6 +65,8 @@ _I32 = ctypes.c_int32
 
 def _declare(lib):
     sig = {
+        "orc_max_threads": (ctypes.c_int, []),
+        "orc_set_threads": (None, [ctypes.c_int]),
         "orc_half_to_double": (ctypes.c_double, [ctypes.c_uint16]),
         "orc_block_bytes": (ctypes.c_int, [ctypes.c_int]),
         "orc_dequant_block": (ctypes.c_int, [ctypes.c_int, _P, _P]),
@@ -129,6 +131,14 @@ class Oracle:
 
     def __init__(self, lib=None):
         self.lib = lib if lib is not None else load()
+
+    def max_threads(self) -> int:
+        """Threads the oracle's parallel loops use now."""
+        return self.lib.orc_max_threads()
+
+    def set_threads(self, n: int) -> None:
+        """Set the thread count of the parallel loops (results do not depend on it)."""
+        self.lib.orc_set_threads(int(n))
 
     def half_to_double(self, bits: int) -> float:
         return self.lib.orc_half_to_double(bits)
@@ -299,6 +309,39 @@ class Oracle:
                                         _p(_c(pos, np.int32)), eps, rope_base)
         assert rc == 0
         return q, k
+
+
+    def moe_block(self, x, router, k: int, gate, up, down, F: int, E: int,
+                  norm_gain=None, eps: float = 0.0, residual: bool = False):
+        """The MoE block as the layer runs it: optional RMSNorm of x, route,
+        expert FFN; with residual the block output is added to x.
+        -> (out f32 [T, H], idx, w, logits)."""
+        h = x if norm_gain is None else self.rmsnorm(x, norm_gain, eps)
+        idx, w, logits = self.route(h, router, k)
+        out = self.expert_ffn(h, idx, w, gate, up, down, F=F, E=E,
+                              out=x if residual else None, accumulate=residual)
+        return out, idx, w, logits
+
+    def decoder_layer(self, x, wq, wk, wv, wo, in_norm, post_norm, q_norm, k_norm, kcache,
+                      vcache, pos, n_q: int, n_kv: int, D: int, eps: float, rope_base: float,
+                      router, k: int, gate, up, down, F: int, E: int):
+        """One decode step of the Qwen3-MoE decoder layer for B sequences:
+        x += Wo attention(QKnorm+RoPE(Wq,Wk,Wv RMSNorm(x))), then
+        x += MoE(RMSNorm(x)).  Weights are bf16 bits [N, K]; caches uint16
+        [B, n_kv, S_max, D] (copies are written, the inputs are left alone).
+        -> (x_out f32 [B, H], idx, w, kcache, vcache)."""
+        B = x.shape[0]
+        xn = self.rmsnorm(x, in_norm, eps)
+        q = self.bf16_gemv(wq, xn).reshape(B, n_q, D)
+        kk = self.bf16_gemv(wk, xn).reshape(B, n_kv, D)
+        vv = self.bf16_gemv(wv, xn).reshape(B, n_kv, D)
+        q, kk = self.attn_prologue(q, kk, q_norm, k_norm, pos, eps, rope_base)
+        kc, vc = self.kv_write(kk, vv, pos, kcache, vcache)
+        a = self.gqa_attention(q, kc, vc, np.asarray(pos, np.int32) + 1, 1.0 / np.sqrt(D))
+        x1 = self.bf16_gemv(wo, a.reshape(B, -1), x, accumulate=True)
+        out, idx, w, _ = self.moe_block(x1, router, k, gate, up, down, F, E,
+                                        norm_gain=post_norm, eps=eps, residual=True)
+        return out, idx, w, kc, vc
 
 
 _default = None

@@ -51,6 +51,7 @@
  *    given scale (1/sqrt(D) in the layer).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -58,6 +59,12 @@
 #define ORC_Q4_K 1
 #define ORC_Q6_K 2
 #define ORC_QK 256
+
+/* Threads the OpenMP loops below may use: infrastructure for timing the
+ * oracle (single-threaded and on every host core); no result depends on it,
+ * since every output element is computed by one thread in a fixed order. */
+int orc_max_threads(void) { return omp_get_max_threads(); }
+void orc_set_threads(int n) { if (n >= 1) omp_set_num_threads(n); }
 
 /* IEEE 754 binary16 -> double, from the format definition. */
 double orc_half_to_double(uint16_t h)

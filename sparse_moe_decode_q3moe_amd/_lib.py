@@ -25,7 +25,7 @@ EXPORTS = (
     "q3moe_attn_prologue", "q3moe_rmsnorm", "q3moe_bf16_gemv", "q3moe_kv_write",
     "q3moe_gqa_attention_workspace_bytes", "q3moe_gqa_attention",
     "q3moe_moe_ffn_workspace_bytes", "q3moe_moe_ffn", "q3moe_moe_ffn_prenorm", "q3moe_bf16_gemv3",
-    "q3moe_attn_prologue_kv",
+    "q3moe_attn_prologue_kv", "q3moe_persistent_path",
 )
 
 
@@ -68,6 +68,7 @@ _SIGS = {
     "q3moe_moe_ffn_prenorm": (_I32, [_P, _I64, _I64, _I64, _I32, _I32, _P, _F, _P, _Experts,
                                      _Experts, _Experts, _P, _P, _P, _I32, _P, ctypes.c_size_t,
                                      _P]),
+    "q3moe_persistent_path": (_I32, [_I64, _I64, _I64, _I32, _I32, _I32, _I32]),
 }
 
 _lib = None
@@ -225,6 +226,14 @@ def q3moe_expert_ffn(hidden: torch.Tensor, topk_idx: torch.Tensor, topk_w: torch
         gate.c(), up.c(), down.c(), _ptr(out), 1 if accumulate else 0,
         _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
     return out
+
+
+def q3moe_persistent_path(T: int, H: int, F: int, E: int, top_k: int, down_qtype: int,
+                          with_route: bool) -> int:
+    """1 when the MoE block (with_route) or the expert FFN of this shape runs
+    as the one persistent kernel on the current device, 0 for separate
+    kernels, -1 for a shape the calls reject."""
+    return library().q3moe_persistent_path(T, H, F, E, top_k, down_qtype, 1 if with_route else 0)
 
 
 def q3moe_moe_ffn_workspace_bytes(T: int, H: int, F: int, E: int, top_k: int) -> int:

@@ -78,8 +78,11 @@ q3moe_status q3moe_route(const float* hidden, int64_t T, int64_t H, const float*
     if (!workspace || workspace_bytes < q3moe_route_workspace_bytes(T, E))
         return Q3MOE_E_WORKSPACE;
     if (!aligned16(workspace)) return Q3MOE_E_ALIGN;
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
     return from_hip(q3moe::launch_route(hidden, T, H, router, E, top_k, topk_idx, topk_w,
-                                        workspace, as_stream(stream)));
+                                        reinterpret_cast<int32_t*>(ws),
+                                        reinterpret_cast<double*>(ws + q3moe::kRouteSyncBytes),
+                                        as_stream(stream)));
 }
 
 q3moe_status q3moe_group_by_expert(const int32_t* topk_idx, int64_t T, int32_t top_k,
@@ -200,7 +203,12 @@ q3moe_status moe_ffn_impl(const float* hidden, int64_t T, int64_t H, int64_t F, 
         if (e != hipSuccess) return from_hip(e);
         x = ws_norm;
     }
-    hipError_t e = q3moe::launch_route(x, T, H, router, E, top_k, topk_idx, topk_w, ws_route, s);
+    // The route's arrival counter lives in the expert-FFN header at a fixed
+    // offset: ws_route moves with T, H, F and k, and a region that a larger
+    // call filled with data must never serve as a counter that has to be zero.
+    hipError_t e = q3moe::launch_route(x, T, H, router, E, top_k, topk_idx, topk_w,
+                                       reinterpret_cast<int32_t*>(ws + q3moe::kFfnRouteSyncOffset),
+                                       reinterpret_cast<double*>(ws_route + q3moe::kRouteSyncBytes), s);
     if (e != hipSuccess) return from_hip(e);
     return from_hip(q3moe::launch_expert_ffn(x, T, H, F, E, top_k, topk_idx, topk_w, g, u, d,
                                              out, accumulate, ws, s));
@@ -225,6 +233,17 @@ q3moe_status q3moe_moe_ffn_prenorm(const float* hidden, int64_t T, int64_t H, in
                                    size_t workspace_bytes, void* stream) {
     return moe_ffn_impl(hidden, T, H, F, E, top_k, true, norm_gain, eps, router, gate, up, down, topk_idx,
                         topk_w, out, accumulate, workspace, workspace_bytes, stream);
+}
+
+int32_t q3moe_persistent_path(int64_t T, int64_t H, int64_t F, int32_t E, int32_t top_k,
+                              int32_t down_qtype, int32_t with_route) {
+    if (T < 0 || H % 256 || F % 256 || H < 256 || H > 4096 || F < 256 || F > 1536 || E < 1 ||
+        E > q3moe::kMaxExperts || top_k < 1 || top_k > q3moe::kMaxTopK || top_k > E ||
+        (down_qtype != Q3MOE_Q4_K && down_qtype != Q3MOE_Q6_K) || (with_route != 0 && with_route != 1))
+        return -1;
+    if (T == 0) return 0;
+    return with_route ? (q3moe::moe_decode_fused(T, H, F, E, top_k, down_qtype) ? 1 : 0)
+                      : (q3moe::expert_ffn_fused(T, H, F, top_k, down_qtype) ? 1 : 0);
 }
 
 q3moe_status q3moe_attn_prologue(float* q, float* k, int64_t T, int32_t n_q_heads,

@@ -688,7 +688,7 @@ constexpr int kSyncStatus = 0;
 constexpr int kSyncEpoch = 32;                         // calls completed on this workspace
 constexpr int kSyncExit = 64;                          // + kLineInts * stripe
 constexpr int kSyncExitTop = kSyncExit + kStripes * kLineInts;
-static_assert((kSyncExitTop + 1) * 4 <= (int)kFfnSyncBytes, "sync header too small");
+static_assert((kSyncExitTop + 1) * 4 <= (int)kFfnRouteSyncOffset, "sync header too small");
 
 __device__ __forceinline__ int stripe_members(int stripe, int grid) {
     return grid / kStripes + (stripe < grid % kStripes ? 1 : 0);
@@ -1423,13 +1423,44 @@ hipError_t launch_fused8(const float* hidden, int64_t T, int64_t F, int32_t E, i
     return hipGetLastError();
 }
 
+// Workgroups of ffn_fused8_kernel<kRoute> that one compute unit of the
+// current device holds at once with `lds` bytes of dynamic LDS (the
+// occupancy calculator's answer for this kernel's registers, waves and LDS),
+// cached per (device, LDS size); 0 when the device cannot run it.
+template <bool kRoute>
+int fused_blocks_per_cu(int lds) {
+    static std::atomic<int64_t> cache[kMaxDevices];   // (lds << 16) | (blocks + 1)
+    static LdsLimit lds_set;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+    if (dev < kMaxDevices) {
+        const int64_t c = cache[dev].load(std::memory_order_relaxed);
+        if (c != 0 && (c >> 16) == lds) return (int)(c & 0xffff) - 1;
+    }
+    const void* fn = reinterpret_cast<const void*>(ffn_fused8_kernel<kRoute>);
+    if (ensure_lds(fn, lds_set, lds) != hipSuccess) return 0;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, kFzWaves * kWave, (size_t)lds) != hipSuccess ||
+        n < 0)
+        n = 0;
+    if (dev < kMaxDevices) cache[dev].store(((int64_t)lds << 16) | (int64_t)(n + 1), std::memory_order_relaxed);
+    return n;
+}
+
 // Workgroups of the fused kernel for this shape (one per compute unit at
-// most), or 0 when the shape is outside it.
-int fused_grid(int64_t T, int64_t H, int64_t F, int32_t k, int32_t dqtype) {
+// most), or 0 when the shape is outside it.  The kernel's workgroups wait on
+// each other, so all of them must be resident at once: the grid never
+// exceeds the compute units times the workgroups one unit holds (the
+// occupancy calculator's figure), and a device that holds none at this LDS
+// size takes the two-kernel path.
+int fused_grid(int64_t T, int64_t H, int64_t F, int32_t k, int32_t dqtype, bool route) {
     if (H != (int64_t)kFzNB * kQK || k > kFzMaxSlots || T > kFzMaxTokens || T < 1) return 0;
-    if ((size_t)fused_lds(T, F, dqtype).total > kMaxLdsPerWorkgroup) return 0;
+    const int lds = fused_lds(T, F, dqtype).total;
+    if ((size_t)lds > kMaxLdsPerWorkgroup) return 0;
     const int cus = cu_count();
     if (cus <= 0) return 0;
+    const int per_cu = route ? fused_blocks_per_cu<true>(lds) : fused_blocks_per_cu<false>(lds);
+    if (per_cu < 1) return 0;
     const int64_t tiles = F / GuTask<kFzNB>::R;
     const int64_t need = (T * k * tiles + kFzGu - 1) / kFzGu;
     const int64_t units = T * (H / kDnRows);
@@ -1452,7 +1483,7 @@ hipError_t launch_decode_nb(const float* hidden, int64_t T, int64_t H, int64_t F
                             const ExpertTensor& up, const ExpertTensor& down, float* out,
                             int accumulate, uint8_t* hp, int32_t* sync, hipStream_t stream) {
     if constexpr (NB == kFzNB) {
-        const int grid = fused_grid(T, H, F, k, down.qtype);
+        const int grid = fused_grid(T, H, F, k, down.qtype, false);
         if (grid > 0)
             return launch_fused8<false>(hidden, T, F, E, k, idx, w, gate, up, down, out, accumulate,
                                         hp, sync, grid, nullptr, 1, nullptr, nullptr, nullptr, nullptr,
@@ -1488,8 +1519,13 @@ hipError_t launch_decode_ffn(const float* hidden, int64_t T, int64_t H, int64_t 
     }
 }
 
+bool expert_ffn_fused(int64_t T, int64_t H, int64_t F, int32_t k, int32_t dqtype) {
+    return T < kPrefillMinTokens && decode_ffn_supported(H, F, k) && H / kQK == kFzNB &&
+           fused_grid(T, H, F, k, dqtype, false) > 0;
+}
+
 bool moe_decode_fused(int64_t T, int64_t H, int64_t F, int32_t E, int32_t k, int32_t dqtype) {
-    return E <= kFzRouteNper * kWave && fused_grid(T, H, F, k, dqtype) > 0;
+    return E <= kFzRouteNper * kWave && fused_grid(T, H, F, k, dqtype, true) > 0;
 }
 
 size_t moe_route_words_bytes(int64_t T, int32_t E) {
@@ -1501,7 +1537,7 @@ hipError_t launch_moe_decode(const float* hidden, int64_t T, int64_t H, int64_t 
                              const ExpertTensor& gate, const ExpertTensor& up,
                              const ExpertTensor& down, float* out, int accumulate, void* ffn_ws,
                              void* route_words, const float* norm_gain, float eps, hipStream_t stream) {
-    const int grid = fused_grid(T, H, F, k, down.qtype);
+    const int grid = fused_grid(T, H, F, k, down.qtype, true);
     if (grid <= 0 || E > kFzRouteNper * kWave) return hipErrorInvalidValue;
     int32_t* sync = static_cast<int32_t*>(ffn_ws);
     uint8_t* hp = static_cast<uint8_t*>(ffn_ws) + kFfnSyncBytes;

@@ -57,12 +57,14 @@ hipError_t launch_prefill_ffn(const float* hidden, int64_t T, int64_t H, int64_t
 
 // route.hip.  The route workspace starts with kRouteSyncBytes of completion
 // counters (zero before the first call; every call leaves them zero), then
-// holds the logits.
+// holds the logits.  launch_route takes the counter and the logits apart, so
+// a caller that embeds the route in a larger workspace can keep the counter
+// at an offset that does not depend on the call's sizes.
 constexpr size_t kRouteSyncBytes = 4096;
 size_t route_workspace_bytes(int64_t T, int32_t E);
 hipError_t launch_route(const float* hidden, int64_t T, int64_t H, const float* router,
-                        int32_t E, int32_t k, int32_t* idx, float* w, void* ws,
-                        hipStream_t stream);
+                        int32_t E, int32_t k, int32_t* idx, float* w, int32_t* sync,
+                        double* logits, hipStream_t stream);
 
 // ffn_decode.hip: the decode-batch path (H/256 in {1, 2, 4, 8, 16})
 bool decode_ffn_supported(int64_t H, int64_t F, int32_t k);
@@ -70,6 +72,11 @@ bool decode_ffn_supported(int64_t H, int64_t F, int32_t k);
 // words (the status word, then line-spaced completion counters of the fused
 // kernel), then holds the intermediate h from that offset on.
 constexpr size_t kFfnSyncBytes = 8192;
+// Byte offset, inside that header, of the route kernel's arrival counter when
+// the route runs as part of the MoE block (the header's first half holds the
+// expert FFN's own words).  Fixed, so the counter sits at one address for
+// calls of every size through one workspace.
+constexpr size_t kFfnRouteSyncOffset = 4096;
 hipError_t launch_decode_ffn(const float* hidden, int64_t T, int64_t H, int64_t F, int32_t E,
                              int32_t k, const int32_t* idx, const float* w,
                              const ExpertTensor& gate, const ExpertTensor& up,
@@ -83,6 +90,8 @@ hipError_t launch_decode_ffn(const float* hidden, int64_t T, int64_t H, int64_t 
 // norm_gain (or null) applies the input RMSNorm inside the kernel, and then
 // hidden may equal out.
 bool moe_decode_fused(int64_t T, int64_t H, int64_t F, int32_t E, int32_t k, int32_t dqtype);
+// Whether launch_expert_ffn runs this shape as the one persistent kernel.
+bool expert_ffn_fused(int64_t T, int64_t H, int64_t F, int32_t k, int32_t dqtype);
 size_t moe_route_words_bytes(int64_t T, int32_t E);
 hipError_t launch_moe_decode(const float* hidden, int64_t T, int64_t H, int64_t F, int32_t E,
                              int32_t k, const float* router, int32_t* topk_idx, float* topk_w,

@@ -276,10 +276,8 @@ size_t route_workspace_bytes(int64_t T, int32_t E) {
 }
 
 hipError_t launch_route(const float* hidden, int64_t T, int64_t H, const float* router,
-                        int32_t E, int32_t k, int32_t* idx, float* w, void* ws,
-                        hipStream_t stream) {
-    int32_t* sync = static_cast<int32_t*>(ws);
-    double* logits = reinterpret_cast<double*>(static_cast<uint8_t*>(ws) + kRouteSyncBytes);
+                        int32_t E, int32_t k, int32_t* idx, float* w, int32_t* sync,
+                        double* logits, hipStream_t stream) {
     if (E <= 64) return launch_route_nper<1>(hidden, T, H, router, E, k, idx, w, sync, logits, stream);
     if (E <= 128) return launch_route_nper<2>(hidden, T, H, router, E, k, idx, w, sync, logits, stream);
     if (E <= 256) return launch_route_nper<4>(hidden, T, H, router, E, k, idx, w, sync, logits, stream);

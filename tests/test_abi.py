@@ -29,10 +29,27 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 20, names
+    assert len(names) == 21, names
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(_lib.EXPORTS) == names
+
+
+def test_persistent_path_query(lib):
+    """Shapes the block rejects answer -1; T = 0 and shapes outside the
+    persistent kernel's range (more than 4 tokens, H != 2048) answer 0 on
+    any machine.  Whether a decode shape takes the persistent kernel depends
+    on the device, so the GPU tests check that case."""
+    f = lib.q3moe_persistent_path
+    assert f(1, 2000, 768, 128, 8, q3.Q6_K, 1) == -1        # H % 256
+    assert f(1, 2048, 768, 128, 8, 7, 1) == -1               # unknown down qtype
+    assert f(1, 2048, 768, 128, 8, q3.Q6_K, 2) == -1
+    assert f(-1, 2048, 768, 128, 8, q3.Q6_K, 1) == -1
+    assert f(0, 2048, 768, 128, 8, q3.Q6_K, 1) == 0
+    assert f(5, 2048, 768, 128, 8, q3.Q6_K, 1) == 0
+    assert f(512, 2048, 768, 128, 8, q3.Q6_K, 0) == 0
+    assert f(1, 4096, 768, 128, 8, q3.Q6_K, 1) == 0
+    assert f(1, 2048, 768, 128, 9, q3.Q6_K, 1) == 0
 
 
 def test_byte_counts(lib):

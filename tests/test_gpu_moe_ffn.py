@@ -204,3 +204,48 @@ def test_moe_ffn_prenorm_matches_norm_then_block(layers, name):
     assert torch.equal(idx.cpu(), idx2.cpu())
     np.testing.assert_allclose(w.cpu().numpy(), w2.cpu().numpy(), rtol=1e-6, atol=0)
     assert_rows_close(out.cpu().numpy(), out2.cpu().numpy().astype(np.float64), what="prenorm vs two steps")
+
+
+def test_moe_ffn_workspace_reuse_across_paths(layers):
+    """One workspace, sized for 512 tokens, through calls that take every
+    path: the batched prefill kernels (512 tokens fill the workspace with
+    grouping data and activation pieces), the two-launch decode form (6 and
+    8 tokens: its route kernel's arrival counter must be zero at launch) and
+    the one-kernel block (1 token).  The route counter sits at one fixed
+    offset for every size, so no call finds a larger call's data there."""
+    full = gen.MoeShape(T=512, H=2048, E=128, k=8, F=768, down_qtype=gen.Q6_K)
+    cpu, dev, _ = layers("a3b_T1")
+    ws = torch.zeros(q3.q3moe_moe_ffn_workspace_bytes(full.T, full.H, full.F, full.E, full.k),
+                     dtype=torch.uint8, device=DEV)
+    g = gen.make_generator(4242)
+    for T in (512, 6, 1, 8, 5, 2):
+        s = gen.MoeShape(T=T, H=2048, E=128, k=8, F=768, down_qtype=gen.Q6_K)
+        lay = gen.MoeLayer(s, cpu.router, cpu.gate, cpu.up, cpu.down)
+        x = gen.normal_f32((T, 2048), 1.0, g)
+        say(f"workspace reuse across paths: T={T}, persistent="
+            f"{q3.q3moe_persistent_path(T, 2048, 768, 128, 8, gen.Q6_K, True)}")
+        got = q3.q3moe_moe_ffn(x.to(DEV), dev.router, 8, *experts_of(dev), F=768, workspace=ws)
+        _check(lay, got, x, f"reuse across paths T={T}")
+        assert q3.expert_ffn_status(ws, T, 2048, 768, 128, 8) == 0
+
+
+def test_persistent_path_is_taken_at_decode(layers):
+    """At the 30B-A3B decode shape (1 token) the MoE block is the one
+    persistent kernel on this device: the occupancy check passes, the call
+    advances the workspace's call counter (only that kernel does), and the
+    status word stays zero."""
+    cpu, dev, x = layers("a3b_T1")
+    s = cpu.shape
+    assert q3.q3moe_persistent_path(1, 2048, 768, 128, 8, gen.Q6_K, True) == 1
+    assert q3.q3moe_persistent_path(1, 2048, 768, 128, 8, gen.Q6_K, False) == 1
+    assert q3.q3moe_persistent_path(5, 2048, 768, 128, 8, gen.Q6_K, True) == 0
+    assert q3.q3moe_persistent_path(512, 2048, 768, 128, 8, gen.Q6_K, False) == 0
+    assert q3.q3moe_persistent_path(1, 2000, 768, 128, 8, gen.Q6_K, True) == -1
+    ws = torch.zeros(q3.q3moe_moe_ffn_workspace_bytes(s.T, s.H, s.F, s.E, s.k),
+                     dtype=torch.uint8, device=DEV)
+    counter = lambda: int(ws[128:132].view(torch.int32).item())   # noqa: E731
+    before = counter()
+    got = q3.q3moe_moe_ffn(x.to(DEV), dev.router, s.k, *experts_of(dev), F=s.F, workspace=ws)
+    _check(cpu, got, x, "persistent path")
+    assert counter() == before + 1
+    assert q3.expert_ffn_status(ws, s.T, s.H, s.F, s.E, s.k) == 0
