@@ -228,6 +228,33 @@ q3moe_status q3moe_moe_ffn(const float *hidden, int64_t T, int64_t H, int64_t F,
 int32_t q3moe_persistent_path(int64_t T, int64_t H, int64_t F, int32_t E, int32_t top_k,
                               int32_t down_qtype, int32_t with_route);
 
+/* ------------------------------------------------------ MoE block, no-alloc --
+ * For callers that cannot allocate device memory or hold a workspace of their
+ * own (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): exactly q3moe_moe_ffn, with the workspace taken from a
+ * file-scope device array of Q3MOE_NOALLOC_SCRATCH_BYTES (4 MiB) inside the
+ * library instead of an argument.  Each GPU the library runs on holds its own
+ * copy of the array until the process ends; the call allocates nothing (no
+ * hipMalloc, no allocating library routine).  The caller still passes every
+ * input and output.
+ *  - Sizes: a shape whose q3moe_moe_ffn_workspace_bytes(T, H, F, E, k)
+ *    exceeds Q3MOE_NOALLOC_SCRATCH_BYTES returns Q3MOE_E_WORKSPACE and
+ *    enqueues nothing (at the 30B-A3B layer shape that admits up to 31 tokens).
+ *  - State: every call on a device shares that device's array and leaves its
+ *    counters at zero; the first calls on a device also enqueue a zero fill
+ *    of the array ahead of the block (until one call made outside graph
+ *    capture has done so; a graph captured before then replays the fill).
+ *  - Calls that overlap in time on one device (different streams, threads or
+ *    graphs) race on the array and give wrong results: order them.
+ * Errors: those of q3moe_moe_ffn, and E_HIP if the array's device address
+ * cannot be obtained. */
+#define Q3MOE_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+q3moe_status q3moe_moe_ffn_noalloc(const float *hidden, int64_t T, int64_t H, int64_t F,
+                                   int32_t E, int32_t top_k, const float *router,
+                                   q3moe_experts gate, q3moe_experts up, q3moe_experts down,
+                                   int32_t *topk_idx, float *topk_w, float *out,
+                                   int32_t accumulate, void *stream);
+
 /* ------------------------------------------------- MoE block after RMSNorm --
  * The MoE block of a pre-norm decoder layer: its input is the token's hidden
  * row x normalised as

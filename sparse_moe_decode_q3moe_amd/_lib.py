@@ -25,7 +25,7 @@ EXPORTS = (
     "q3moe_attn_prologue", "q3moe_rmsnorm", "q3moe_bf16_gemv", "q3moe_kv_write",
     "q3moe_gqa_attention_workspace_bytes", "q3moe_gqa_attention",
     "q3moe_moe_ffn_workspace_bytes", "q3moe_moe_ffn", "q3moe_moe_ffn_prenorm", "q3moe_bf16_gemv3",
-    "q3moe_attn_prologue_kv", "q3moe_persistent_path",
+    "q3moe_attn_prologue_kv", "q3moe_persistent_path", "q3moe_moe_ffn_noalloc",
 )
 
 
@@ -69,6 +69,8 @@ _SIGS = {
                                      _Experts, _Experts, _P, _P, _P, _I32, _P, ctypes.c_size_t,
                                      _P]),
     "q3moe_persistent_path": (_I32, [_I64, _I64, _I64, _I32, _I32, _I32, _I32]),
+    "q3moe_moe_ffn_noalloc": (_I32, [_P, _I64, _I64, _I64, _I32, _I32, _P, _Experts, _Experts,
+                                     _Experts, _P, _P, _P, _I32, _P]),
 }
 
 _lib = None
@@ -271,6 +273,37 @@ def q3moe_moe_ffn(hidden: torch.Tensor, router: torch.Tensor, top_k: int, gate: 
         _ptr(hidden), T, H, F, E, top_k, _ptr(router), gate.c(), up.c(), down.c(),
         _ptr(topk_idx), _ptr(topk_w), _ptr(out), 1 if accumulate else 0,
         _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return out, topk_idx, topk_w
+
+
+def q3moe_moe_ffn_noalloc(hidden: torch.Tensor, router: torch.Tensor, top_k: int, gate: Experts,
+                          up: Experts, down: Experts, F: int, out: Optional[torch.Tensor] = None,
+                          accumulate: bool = False, topk_idx: Optional[torch.Tensor] = None,
+                          topk_w: Optional[torch.Tensor] = None, stream=None):
+    """q3moe_moe_ffn with the library's own device scratch as its workspace
+    (no workspace argument, nothing allocated by the call beyond the outputs
+    created here when None); -> (out, topk_idx, topk_w)."""
+    _need(hidden, "hidden", torch.float32, 2)
+    _need(router, "router", torch.float32, 2)
+    T, H = hidden.shape
+    E = router.shape[0]
+    if router.shape[1] != H:
+        raise ValueError("router must be [E, H]")
+    dev = hidden.device
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate=True needs an existing out tensor")
+        out = torch.empty((T, H), dtype=torch.float32, device=dev)
+    if topk_idx is None:
+        topk_idx = torch.empty((T, top_k), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((T, top_k), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, 2)
+    _need(topk_idx, "topk_idx", torch.int32, 2)
+    _need(topk_w, "topk_w", torch.float32, 2)
+    _check("q3moe_moe_ffn_noalloc", library().q3moe_moe_ffn_noalloc(
+        _ptr(hidden), T, H, F, E, top_k, _ptr(router), gate.c(), up.c(), down.c(),
+        _ptr(topk_idx), _ptr(topk_w), _ptr(out), 1 if accumulate else 0, _stream(stream)))
     return out, topk_idx, topk_w
 
 
