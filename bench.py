@@ -147,6 +147,11 @@ def main():
         route(i)
         ffn(i)
 
+    def step_q8(i):                                # the block with int8 gate/up activations
+        L = layers[i % N_LAYER_COPIES]
+        q3.q3moe_moe_ffn(xs[i], L.router, k, *experts[i % N_LAYER_COPIES], F=F, out=outs[i],
+                         topk_idx=idx[i], topk_w=wts[i], workspace=ws_moe, int8_activations=True)
+
     # eager pass (also loads every kernel), then capture
     for i in range(GRAPH_STEPS):
         step(i)
@@ -171,13 +176,15 @@ def main():
                 fn(i)
         return g
 
-    for i in range(GRAPH_STEPS):                   # load the two-call kernels too
+    for i in range(GRAPH_STEPS):                   # load the two-call and int8 kernels too
         step_two_calls(i)
+        step_q8(i)
     g_main = capture(step, GRAPH_STEPS)
     rem = args.steps % GRAPH_STEPS
     g_rem = capture(step, rem) if rem else None
     g_ffn = capture(ffn, GRAPH_STEPS)
     g_two = capture(step_two_calls, GRAPH_STEPS)
+    g_q8 = capture(step_q8, GRAPH_STEPS)
 
     # warmup: at least W steps, and every graph launched once before timing
     for _ in range(max(1, math.ceil(args.warmup / GRAPH_STEPS))):
@@ -186,6 +193,7 @@ def main():
         g_rem.replay()
     g_ffn.replay()
     g_two.replay()
+    g_q8.replay()
     torch.cuda.synchronize()
 
     # timed region: exactly K steps
@@ -226,6 +234,14 @@ def main():
     torch.cuda.synchronize()
     two_us = ka.elapsed_time(kb) * 1000.0 / (args.kernel_reps * GRAPH_STEPS)
     status["expert_ffn_workspace"] = q3.expert_ffn_status(ws_ffn, 1, H, F, E, k)
+    ka.record()
+    for _ in range(args.kernel_reps):
+        g_q8.replay()
+    kb.record()
+    torch.cuda.synchronize()
+    q8_us = ka.elapsed_time(kb) * 1000.0 / (args.kernel_reps * GRAPH_STEPS)
+    timed_q8 = {"out": outs.clone(), "idx": idx.clone()}
+    status["moe_block_int8_workspace"] = q3.expert_ffn_status(ws_moe, 1, H, F, E, k)
     ceiling = stream_ceiling(torch, dev)
     # the steps of the timed region are one kernel launch each
     block_us = ms_per_step * 1000.0
@@ -275,6 +291,14 @@ def main():
             "persistent_path": persistent,
         },
         "same_box_stream_ceiling": ceiling,
+        "int8_activations": {
+            "note": "the same step as q3moe_moe_ffn_q8: gate/up on one int8 value per activation "
+                    "(d = max|x|/127 per 32 values), routing and down as in the f32 block",
+            "us_per_step": round(q8_us, 3),
+            "tokens_per_s": round(1e6 / q8_us, 1),
+            "hbm_gbps": round(step_bytes / (q8_us * 1e-6) / 1e9, 1),
+            "hbm_frac": round(step_bytes / (q8_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+        },
         "two_calls": {
             "note": "the same step as q3moe_route + q3moe_expert_ffn (two launches)",
             "us_per_step": round(two_us, 3),
@@ -298,6 +322,9 @@ def main():
 
     if cpu is not None:
         result["cpu_baseline"] = cpu_baseline(args, cpu, torch, gen, layers, xs, timed, shape)
+        result["int8_activations"]["guard"] = q8_guard(cpu, gen, layers, xs, timed_q8, shape)
+        if not result["int8_activations"]["guard"]["ok"]:
+            result["cpu_baseline"]["guard_ok"] = False
 
     result["status_words"] = status
     bad_status = {n: v for n, v in status.items() if v != 0}
@@ -737,6 +764,34 @@ def stack_oracle(torch, q3, gen, shape, cpu, stack, x0, x, ones, idx, wts, ws, e
         "layers_with_equal_routing": same_layers, "final_max_rel_l2": err,
         "ok": same_layers == len(stack) and err <= 1e-3,
         "note": "free-running chains on both sides; routing compared at every layer"}
+
+
+def q8_guard(cpu, gen, layers, xs, timed_q8, shape):
+    """The int8-activation steps that used layer copy 0, against the oracle
+    that quantises the same way (1e-4) and against the f32 oracle (the
+    mode's error budget, 3e-2 per token)."""
+    import numpy as np
+    o = cpu.o
+    L0 = layers[0]
+    router = L0.router.cpu().numpy()
+    tens = host_tensors(gen, L0, shape.down_qtype)
+    err_q8, err_f32, same = 0.0, 0.0, True
+    gs, rs = [], []
+    for i in range(0, GRAPH_STEPS, N_LAYER_COPIES):
+        x = xs[i].cpu().numpy()
+        ridx, rw, _ = o.route(x, router, shape.k)
+        ref_q8 = o.expert_ffn_q8(x, ridx, rw, *tens, F=shape.F, E=shape.E)
+        ref = o.expert_ffn(x, ridx, rw, *tens, F=shape.F, E=shape.E)
+        g = timed_q8["out"][i].cpu().numpy()
+        err_q8 = max(err_q8, rel_l2_max(g, ref_q8))
+        err_f32 = max(err_f32, rel_l2_max(g, ref))
+        gs.append(g.astype(np.float64))
+        rs.append(ref.astype(np.float64))
+        same = same and bool(np.array_equal(timed_q8["idx"][i].cpu().numpy(), ridx))
+    agg = float(np.linalg.norm(np.concatenate(gs) - np.concatenate(rs)) / np.linalg.norm(np.concatenate(rs)))
+    return {"indices_equal": same, "max_rel_l2_vs_int8_oracle": err_q8,
+            "max_rel_l2_vs_f32_oracle": err_f32, "batch_rel_l2_vs_f32_oracle": agg,
+            "ok": same and err_q8 <= 1e-4 and err_f32 <= 0.25 and agg <= 2e-2}
 
 
 def cpu_model() -> str:

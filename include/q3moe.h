@@ -217,6 +217,32 @@ q3moe_status q3moe_moe_ffn(const float *hidden, int64_t T, int64_t H, int64_t F,
                            int32_t *topk_idx, float *topk_w, float *out, int32_t accumulate,
                            void *workspace, size_t workspace_bytes, void *stream);
 
+/* ------------------------------------------- MoE block, int8 activations --
+ * q3moe_moe_ffn with the gate/up GEMVs on int8 activations, the DP4A-style
+ * route the pages keep for the expert GEMVs (issue #3714, gap G8: an
+ * alternative Q4_K GEMV measured about 4x slower than the DP4A one) and
+ * judge against FP32 activations (R1 receipt, "The Q8_K point").  Routing
+ * is the f32/double routing of q3moe_moe_ffn (identical indices and
+ * weights); the down projection reads h in f32.  For every group of 32
+ * consecutive input values (one Q4_K sub-block) d = max|x| / 127 (f32) and
+ * p = rint(x / d) (f32 quotient, ties to even): the gate and up GEMVs see
+ * d * p, each sub-block's dot product an exact int32 sum of 4-bit quant x
+ * int8 products (v_dot4), one piece per value instead of the three of the
+ * f32 block.  Error budget against the f32 block: each input value moves by
+ * at most d/2 (at most 0.4 % of its group's largest value), which gives
+ * about 0.5-1 % relative L2 on the block output over a batch of tokens
+ * (bound held by the tests: 2e-2 over a batch, 0.25 for a single token,
+ * whose output can nearly cancel); against a reference that quantises the
+ * same way, the f32 rounding of the rest only (1e-4).
+ * Available for the one-kernel shapes of q3moe_moe_ffn only
+ * (q3moe_persistent_path(..., 1) == 1 on this device); other shapes return
+ * Q3MOE_E_SHAPE.  Arguments, workspace and errors as for q3moe_moe_ffn. */
+q3moe_status q3moe_moe_ffn_q8(const float *hidden, int64_t T, int64_t H, int64_t F, int32_t E,
+                              int32_t top_k, const float *router,
+                              q3moe_experts gate, q3moe_experts up, q3moe_experts down,
+                              int32_t *topk_idx, float *topk_w, float *out, int32_t accumulate,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
 /* Which form q3moe_moe_ffn / q3moe_moe_ffn_prenorm (with_route = 1) or
  * q3moe_expert_ffn (with_route = 0) takes for this shape on the CURRENT
  * device: 1 = the one persistent kernel (its workgroups wait on each other

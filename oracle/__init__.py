@@ -15,6 +15,9 @@ Parity status per function (how each is pinned is listed in the tests):
                                   closed forms, ties, shift invariance
   expert_ffn                      pinned: dense-over-all-experts brute force,
                                   single-expert dense MLP, zero cases
+  quantize_act_q8 / expert_ffn_q8 pinned: hand-worked groups (ties to even,
+                                  all-zero, non-finite), |x - d p| <= d/2,
+                                  the f64 block on the dequantised values
   rmsnorm / attn_prologue /       pinned: RMS closed form, rotation invariants,
   rope_neox                       NEOX-vs-interleaved discriminator
   group_by_expert                 pinned: a library sort of (expert, pair),
@@ -84,6 +87,11 @@ def _declare(lib):
                                           _P, ctypes.c_int, _I64,
                                           _P, ctypes.c_int, _I64,
                                           _P, ctypes.c_int, _I64, _P, ctypes.c_int]),
+        "orc_expert_ffn_q8": (ctypes.c_int, [_P, _I64, _I64, _I64, _I32, _I32, _P, _P,
+                                             _P, ctypes.c_int, _I64,
+                                             _P, ctypes.c_int, _I64,
+                                             _P, ctypes.c_int, _I64, _P, ctypes.c_int]),
+        "orc_quantize_act_q8": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
         "orc_rmsnorm": (ctypes.c_int, [_P, _I64, _I64, _P, ctypes.c_float, _P]),
         "orc_group_by_expert": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _P, _P]),
         "orc_bf16_to_double": (ctypes.c_double, [ctypes.c_uint16]),
@@ -270,6 +278,29 @@ class Oracle:
         rc = self.lib.orc_expert_ffn(_p(x), T, H, F, E, k, _p(idx), _p(w),
                                      _p(g), gq, gs, _p(u), uq, us, _p(d), dq, ds,
                                      _p(res), 1 if accumulate else 0)
+        assert rc == 0, rc
+        return res
+
+    def quantize_act_q8(self, x: np.ndarray):
+        """x f32 [T, H] -> (p int8 [T, H], d f32 [T, H/32], values d*p f64 [T, H])."""
+        x = _c(x, np.float32)
+        T, H = x.shape
+        p = np.empty((T, H), np.int8)
+        d = np.empty((T, H // 32), np.float32)
+        xq = np.empty((T, H), np.float64)
+        assert self.lib.orc_quantize_act_q8(_p(x), T, H, _p(p), _p(d), _p(xq)) == 0
+        return p, d, xq
+
+    def expert_ffn_q8(self, x, idx, w, gate, up, down, F: int, E: int,
+                      out: np.ndarray | None = None, accumulate: bool = False) -> np.ndarray:
+        """The expert FFN with the gate/up activations in the int8 form of
+        quantize_act_q8.  -> f32 [T, H]."""
+        x, idx, w, T, H, k, tens = self._ffn_args(x, idx, w, gate, up, down, F, E)
+        res = np.zeros((T, H), np.float32) if out is None else _c(out, np.float32).copy()
+        (g, gq, gs), (u, uq, us), (d, dq, ds) = tens
+        rc = self.lib.orc_expert_ffn_q8(_p(x), T, H, F, E, k, _p(idx), _p(w),
+                                        _p(g), gq, gs, _p(u), uq, us, _p(d), dq, ds,
+                                        _p(res), 1 if accumulate else 0)
         assert rc == 0, rc
         return res
 

@@ -248,24 +248,25 @@ static double silu(double z) { return z / (1.0 + exp(-z)); }
 /* Sparse expert FFN for T tokens (gap G3 of issue #3714):
  *   for each selected slot: g = Wg[e] x, u = Wu[e] x, h = silu(g) * u,
  *   y = Wd[e] h; out[t] = sum over slots (in slot order) of w * y.
- * Expert e's matrices start at base + e * stride.  out is double here. */
-int orc_expert_ffn_f64(const float *x, int64_t T, int64_t H, int64_t F, int32_t E, int32_t k,
-                       const int32_t *idx, const float *w,
-                       const uint8_t *gate, int gate_qt, int64_t gate_stride,
-                       const uint8_t *up, int up_qt, int64_t up_stride,
-                       const uint8_t *down, int down_qt, int64_t down_stride,
-                       double *out)
+ * Expert e's matrices start at base + e * stride.  out is double here.
+ * The gate/up input is taken from xin (double [T x H]); see the two entry
+ * points below. */
+static int expert_ffn_on(const double *xin, int64_t T, int64_t H, int64_t F, int32_t E, int32_t k,
+                         const int32_t *idx, const float *w,
+                         const uint8_t *gate, int gate_qt, int64_t gate_stride,
+                         const uint8_t *up, int up_qt, int64_t up_stride,
+                         const uint8_t *down, int down_qt, int64_t down_stride,
+                         double *out)
 {
     if (H % ORC_QK || F % ORC_QK) return -1;
     for (int64_t i = 0; i < T * k; i++)
         if (idx[i] < 0 || idx[i] >= E) return -2;
-    double *xd = (double *)malloc(sizeof(double) * H);
     double *g = (double *)malloc(sizeof(double) * F);
     double *u = (double *)malloc(sizeof(double) * F);
     double *h = (double *)malloc(sizeof(double) * F);
     double *y = (double *)malloc(sizeof(double) * H);
     for (int64_t t = 0; t < T; t++) {
-        for (int64_t c = 0; c < H; c++) xd[c] = x[t * H + c];
+        const double *xd = xin + t * H;
         for (int64_t c = 0; c < H; c++) out[t * H + c] = 0.0;
         for (int32_t s = 0; s < k; s++) {
             int64_t e = idx[t * k + s];
@@ -277,8 +278,83 @@ int orc_expert_ffn_f64(const float *x, int64_t T, int64_t H, int64_t F, int32_t 
             for (int64_t c = 0; c < H; c++) out[t * H + c] += ws * y[c];
         }
     }
-    free(xd); free(g); free(u); free(h); free(y);
+    free(g); free(u); free(h); free(y);
     return 0;
+}
+
+/* The block on the f32 activations as given (each exact in double). */
+int orc_expert_ffn_f64(const float *x, int64_t T, int64_t H, int64_t F, int32_t E, int32_t k,
+                       const int32_t *idx, const float *w,
+                       const uint8_t *gate, int gate_qt, int64_t gate_stride,
+                       const uint8_t *up, int up_qt, int64_t up_stride,
+                       const uint8_t *down, int down_qt, int64_t down_stride,
+                       double *out)
+{
+    double *xd = (double *)malloc(sizeof(double) * (T * H > 0 ? T * H : 1));
+    for (int64_t i = 0; i < T * H; i++) xd[i] = x[i];
+    int rc = expert_ffn_on(xd, T, H, F, E, k, idx, w, gate, gate_qt, gate_stride,
+                           up, up_qt, up_stride, down, down_qt, down_stride, out);
+    free(xd);
+    return rc;
+}
+
+/* Activations as one int8 value per element, the int8-activation route of
+ * the expert GEMVs (issue #3714, G8: the expert GEMVs stay on DP4A; R1
+ * receipt: the Q8_K point).  Reading: for every group of 32 consecutive
+ * values of a row (one Q4_K sub-block), amax = max |x| in f32, the group
+ * scale d = amax / 127 (one f32 division, rounded to nearest), and
+ * p = rintf(x / d) (an f32 quotient, rounded to the nearest integer with
+ * ties to even), so |p| <= 127; the GEMV then sees d * p, exact in double.
+ * A group of zeros gets d = 0 and p = 0; a group holding a NaN or an
+ * infinity gets d = NaN (every value of the group NaN).  Outputs: p [T x H],
+ * d [T x H/32] and the values d * p [T x H]; H % 32 == 0. */
+int orc_quantize_act_q8(const float *x, int64_t T, int64_t H, int8_t *p, float *d, double *xq)
+{
+    if (H % 32) return -1;
+    for (int64_t t = 0; t < T; t++)
+        for (int64_t g0 = 0; g0 < H; g0 += 32) {
+            const float *v = x + t * H + g0;
+            float amax = 0.0f;
+            int finite = 1;
+            for (int i = 0; i < 32; i++) {
+                if (!isfinite(v[i])) finite = 0;
+                else if (fabsf(v[i]) > amax) amax = fabsf(v[i]);
+            }
+            float dg = finite ? amax / 127.0f : NAN;
+            d[t * (H / 32) + g0 / 32] = dg;
+            for (int i = 0; i < 32; i++) {
+                float q = (finite && amax > 0.0f) ? rintf(v[i] / dg) : 0.0f;
+                p[t * H + g0 + i] = (int8_t)q;
+                xq[t * H + g0 + i] = finite ? (double)dg * (double)q : NAN;
+            }
+        }
+    return 0;
+}
+
+/* The block with the gate/up activations taken in the int8 form above; the
+ * down projection reads h as computed (f32 activations only enter gate/up).
+ * accumulate as for orc_expert_ffn; out f32. */
+int orc_expert_ffn_q8(const float *x, int64_t T, int64_t H, int64_t F, int32_t E, int32_t k,
+                      const int32_t *idx, const float *w,
+                      const uint8_t *gate, int gate_qt, int64_t gate_stride,
+                      const uint8_t *up, int up_qt, int64_t up_stride,
+                      const uint8_t *down, int down_qt, int64_t down_stride,
+                      float *out, int accumulate)
+{
+    int64_t n = T * H > 0 ? T * H : 1;
+    int8_t *p = (int8_t *)malloc((size_t)n);
+    float *dg = (float *)malloc(sizeof(float) * (n / 32 + 1));
+    double *xq = (double *)malloc(sizeof(double) * n);
+    double *o = (double *)malloc(sizeof(double) * n);
+    int rc = orc_quantize_act_q8(x, T, H, p, dg, xq);
+    if (rc == 0)
+        rc = expert_ffn_on(xq, T, H, F, E, k, idx, w, gate, gate_qt, gate_stride,
+                           up, up_qt, up_stride, down, down_qt, down_stride, o);
+    if (rc == 0)
+        for (int64_t i = 0; i < T * H; i++)
+            out[i] = (float)(o[i] + (accumulate != 0 ? (double)out[i] : 0.0));
+    free(p); free(dg); free(xq); free(o);
+    return rc;
 }
 
 /* As above with the f32 output a caller sees; accumulate = 1 adds the

@@ -25,7 +25,7 @@ EXPORTS = (
     "q3moe_attn_prologue", "q3moe_rmsnorm", "q3moe_bf16_gemv", "q3moe_kv_write",
     "q3moe_gqa_attention_workspace_bytes", "q3moe_gqa_attention",
     "q3moe_moe_ffn_workspace_bytes", "q3moe_moe_ffn", "q3moe_moe_ffn_prenorm", "q3moe_bf16_gemv3",
-    "q3moe_attn_prologue_kv", "q3moe_persistent_path", "q3moe_moe_ffn_noalloc",
+    "q3moe_attn_prologue_kv", "q3moe_persistent_path", "q3moe_moe_ffn_noalloc", "q3moe_moe_ffn_q8",
 )
 
 
@@ -69,6 +69,8 @@ _SIGS = {
                                      _Experts, _Experts, _P, _P, _P, _I32, _P, ctypes.c_size_t,
                                      _P]),
     "q3moe_persistent_path": (_I32, [_I64, _I64, _I64, _I32, _I32, _I32, _I32]),
+    "q3moe_moe_ffn_q8": (_I32, [_P, _I64, _I64, _I64, _I32, _I32, _P, _Experts, _Experts, _Experts,
+                                _P, _P, _P, _I32, _P, ctypes.c_size_t, _P]),
     "q3moe_moe_ffn_noalloc": (_I32, [_P, _I64, _I64, _I64, _I32, _I32, _P, _Experts, _Experts,
                                      _Experts, _P, _P, _P, _I32, _P]),
 }
@@ -246,9 +248,10 @@ def q3moe_moe_ffn(hidden: torch.Tensor, router: torch.Tensor, top_k: int, gate: 
                   up: Experts, down: Experts, F: int, out: Optional[torch.Tensor] = None,
                   accumulate: bool = False, topk_idx: Optional[torch.Tensor] = None,
                   topk_w: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                  stream=None):
+                  stream=None, int8_activations: bool = False):
     """Route + expert FFN in one call; -> (out f32 [T, H], topk_idx int32
-    [T, k], topk_w f32 [T, k]), each allocated if None."""
+    [T, k], topk_w f32 [T, k]), each allocated if None.  int8_activations
+    calls q3moe_moe_ffn_q8 (gate/up on int8 activations) instead."""
     _need(hidden, "hidden", torch.float32, 2)
     _need(router, "router", torch.float32, 2)
     T, H = hidden.shape
@@ -269,7 +272,8 @@ def q3moe_moe_ffn(hidden: torch.Tensor, router: torch.Tensor, top_k: int, gate: 
     _need(topk_w, "topk_w", torch.float32, 2)
     nbytes = q3moe_moe_ffn_workspace_bytes(T, H, F, E, top_k)
     ws = _workspace(nbytes, dev, workspace)
-    _check("q3moe_moe_ffn", library().q3moe_moe_ffn(
+    name = "q3moe_moe_ffn_q8" if int8_activations else "q3moe_moe_ffn"
+    _check(name, getattr(library(), name)(
         _ptr(hidden), T, H, F, E, top_k, _ptr(router), gate.c(), up.c(), down.c(),
         _ptr(topk_idx), _ptr(topk_w), _ptr(out), 1 if accumulate else 0,
         _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))

@@ -160,7 +160,8 @@ q3moe_status moe_ffn_impl(const float* hidden, int64_t T, int64_t H, int64_t F, 
                           const float* router,
                           q3moe_experts gate, q3moe_experts up, q3moe_experts down,
                           int32_t* topk_idx, float* topk_w, float* out, int32_t accumulate,
-                          void* workspace, size_t workspace_bytes, void* stream) {
+                          void* workspace, size_t workspace_bytes, void* stream,
+                          int act_pieces = 3) {
     if (T < 0 || H % 256 || F % 256 || H < 256 || H > 4096 || F < 256 || F > 1536 || E < 1 ||
         E > q3moe::kMaxExperts || top_k < 1 || top_k > q3moe::kMaxTopK || top_k > E ||
         (accumulate != 0 && accumulate != 1) || T * top_k > 0x7fffffff || !(eps >= 0.0f) ||
@@ -193,10 +194,11 @@ q3moe_status moe_ffn_impl(const float* hidden, int64_t T, int64_t H, int64_t F, 
     uint8_t* ws_words = ws_route + round256(q3moe::route_workspace_bytes(T, E));
     float* ws_norm = reinterpret_cast<float*>(ws_words + round256(q3moe::moe_route_words_bytes(T, E)));
     const hipStream_t s = as_stream(stream);
-    if (q3moe::moe_decode_fused(T, H, F, E, top_k, d.qtype))
+    if (q3moe::moe_decode_fused(T, H, F, E, top_k, d.qtype, act_pieces))
         return from_hip(q3moe::launch_moe_decode(hidden, T, H, F, E, top_k, router, topk_idx, topk_w,
                                                  g, u, d, out, accumulate, ws, ws_words, norm_gain,
-                                                 eps, s));
+                                                 eps, s, act_pieces));
+    if (act_pieces != 3) return Q3MOE_E_SHAPE;      // the int8 mode has only the one-kernel form
     const float* x = hidden;
     if (norm_gain) {                          // normalised rows into the workspace first
         hipError_t e = q3moe::launch_rmsnorm(hidden, T, H, norm_gain, eps, ws_norm, s);
@@ -225,6 +227,15 @@ q3moe_status q3moe_moe_ffn(const float* hidden, int64_t T, int64_t H, int64_t F,
                         topk_w, out, accumulate, workspace, workspace_bytes, stream);
 }
 
+q3moe_status q3moe_moe_ffn_q8(const float* hidden, int64_t T, int64_t H, int64_t F, int32_t E,
+                              int32_t top_k, const float* router, q3moe_experts gate,
+                              q3moe_experts up, q3moe_experts down, int32_t* topk_idx,
+                              float* topk_w, float* out, int32_t accumulate, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    return moe_ffn_impl(hidden, T, H, F, E, top_k, false, nullptr, 0.0f, router, gate, up, down, topk_idx,
+                        topk_w, out, accumulate, workspace, workspace_bytes, stream, 1);
+}
+
 q3moe_status q3moe_moe_ffn_prenorm(const float* hidden, int64_t T, int64_t H, int64_t F,
                                    int32_t E, int32_t top_k, const float* norm_gain, float eps,
                                    const float* router, q3moe_experts gate, q3moe_experts up,
@@ -242,7 +253,7 @@ int32_t q3moe_persistent_path(int64_t T, int64_t H, int64_t F, int32_t E, int32_
         (down_qtype != Q3MOE_Q4_K && down_qtype != Q3MOE_Q6_K) || (with_route != 0 && with_route != 1))
         return -1;
     if (T == 0) return 0;
-    return with_route ? (q3moe::moe_decode_fused(T, H, F, E, top_k, down_qtype) ? 1 : 0)
+    return with_route ? (q3moe::moe_decode_fused(T, H, F, E, top_k, down_qtype, 3) ? 1 : 0)
                       : (q3moe::expert_ffn_fused(T, H, F, top_k, down_qtype) ? 1 : 0);
 }
 

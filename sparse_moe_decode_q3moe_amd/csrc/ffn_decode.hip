@@ -287,11 +287,12 @@ struct XCols {
     bool hiform;             // sub-blocks 4-7: low scale bits in the third scale dword
 };
 
+template <int NP>
 __device__ __forceinline__ XCols load_xcols(const uint8_t* xt, int lane) {
     const int b = lane >> 3, c = (lane >> 1) & 3;
     XCols x;
 #pragma unroll
-    for (int q = 0; q < 3; ++q)
+    for (int q = 0; q < NP; ++q)
 #pragma unroll
         for (int h = 0; h < 2; ++h)
             x.p[q][h] = *reinterpret_cast<const uint4*>(xt + q * kI8PieceBytes + h * (kWave * 16) + lane * 16);
@@ -313,7 +314,10 @@ __device__ __forceinline__ int sdot4(uint32_t a, uint32_t b, int c) {
 }
 
 // One row's contribution of this lane: hdr = the block header (d, dmin, 12
-// scale bytes), qv = the lane's 16 quant bytes.
+// scale bytes), qv = the lane's 16 quant bytes.  NP = 3: the three pieces
+// of the exact form, A and B in units of s * 2^-14; NP = 1: the single int8
+// piece of the int8-activation mode, in units of its group scale.
+template <int NP>
 __device__ __forceinline__ float q4k_cols_row(uint4 hdr, uint4 qv, const XCols& x) {
     const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
     int a1 = 0, a2 = 0, a3 = 0, b1 = 0, b2 = 0, b3 = 0;
@@ -321,17 +325,17 @@ __device__ __forceinline__ float q4k_cols_row(uint4 hdr, uint4 qv, const XCols& 
     for (int q = 0; q < 4; ++q) {
         const uint32_t lo = qw[q] & 0x0f0f0f0fu;               // 4 weights of sub-block 2c
         const uint32_t hi = (qw[q] >> 4) & 0x0f0f0f0fu;        // 4 weights of sub-block 2c+1
-        const uint32_t xl[3] = {(&x.p[0][0].x)[q], (&x.p[1][0].x)[q], (&x.p[2][0].x)[q]};
-        const uint32_t xh[3] = {(&x.p[0][1].x)[q], (&x.p[1][1].x)[q], (&x.p[2][1].x)[q]};
-        a1 = sdot4(lo, xl[0], a1);
-        a2 = sdot4(lo, xl[1], a2);
-        a3 = sdot4(lo, xl[2], a3);
-        b1 = sdot4(hi, xh[0], b1);
-        b2 = sdot4(hi, xh[1], b2);
-        b3 = sdot4(hi, xh[2], b3);
+        a1 = sdot4(lo, (&x.p[0][0].x)[q], a1);
+        b1 = sdot4(hi, (&x.p[0][1].x)[q], b1);
+        if constexpr (NP == 3) {
+            a2 = sdot4(lo, (&x.p[1][0].x)[q], a2);
+            a3 = sdot4(lo, (&x.p[2][0].x)[q], a3);
+            b2 = sdot4(hi, (&x.p[1][1].x)[q], b2);
+            b3 = sdot4(hi, (&x.p[2][1].x)[q], b3);
+        }
     }
-    const int A = a1 * 16384 + a2 * 128 + a3;
-    const int B = b1 * 16384 + b2 * 128 + b3;
+    const int A = NP == 3 ? a1 * 16384 + a2 * 128 + a3 : a1;
+    const int B = NP == 3 ? b1 * 16384 + b2 * 128 + b3 : b1;
     // [sc(2c), mn(2c), sc(2c+1), mn(2c+1)] as bytes, branch-free: the low four
     // bits come from the first two scale dwords (sub-blocks 0-3) or from the
     // third one's nibbles (4-7), the top two from bits 4-5 or 6-7 of the first two
@@ -631,6 +635,7 @@ __device__ __forceinline__ void gu_rows_load(GuRows& g, int e, int32_t E,
 // h = silu(gate) * up of the task's 4 rows, published as tagged words: the
 // f32 value in the low half and this call's tag in the high half of one
 // 64-bit device-scope store, so a reader that sees the tag sees the value.
+template <int NP>
 __device__ __forceinline__ void gu_rows_finish(const GuRows& g, const XCols& x, int lane,
                                                uint64_t* __restrict__ hbuf, int64_t value_base,
                                                uint32_t tag) {
@@ -643,7 +648,7 @@ __device__ __forceinline__ void gu_rows_finish(const GuRows& g, const XCols& x, 
     for (int i = 0; i < 8; ++i) {
         const uint4 hdr = make_uint4(quad_bcast<0>(g.hw[i]), quad_bcast<1>(g.hw[i]),
                                      quad_bcast<2>(g.hw[i]), quad_bcast<3>(g.hw[i]));
-        v[i] = q4k_cols_row(hdr, g.qv[i], x);
+        v[i] = q4k_cols_row<NP>(hdr, g.qv[i], x);
         __builtin_amdgcn_sched_barrier(0);
     }
     const float r = fold8_rows(v, lane);               // lanes 8q..: row q
@@ -881,7 +886,11 @@ __device__ __forceinline__ uint32_t pack_i8x4(float a, float b, float c, float d
            (((uint32_t)(int)c & 0xffu) << 16) | ((uint32_t)(int)d << 24);
 }
 
-template <int MT>
+// NP = 1 (the int8-activation mode) stores one piece per value instead: for
+// each 32-value group d = max|x| / 127 and p = rint(x / d) (both quotients
+// correctly rounded f32 divisions, ties to even; d = 0 and p = 0 for an
+// all-zero group), the group scale d and the 16-value sums d * sum(p).
+template <int MT, int NP>
 __device__ __forceinline__ void build_x_pieces(const float4 (&xv)[MT], int64_t T, uint8_t* smem,
                                                int tid) {
     const int v0 = 4 * tid, bl = v0 >> 8, w = v0 & 255, j = w >> 5;
@@ -902,6 +911,20 @@ __device__ __forceinline__ void build_x_pieces(const float4 (&xv)[MT], int64_t T
                 bad = fmaxf(bad, __shfl_xor(bad, sh, kWave));
             }
             const bool finite = bad == 0.f;
+            if constexpr (NP == 1) {
+                const float d = finite ? __fdiv_rn(m, 127.f) : __builtin_nanf("");
+                const bool q = finite && m > 0.f;
+                const float p0 = q ? rintf(__fdiv_rn(v.x, d)) : 0.f, p1 = q ? rintf(__fdiv_rn(v.y, d)) : 0.f;
+                const float p2 = q ? rintf(__fdiv_rn(v.z, d)) : 0.f, p3 = q ? rintf(__fdiv_rn(v.w, d)) : 0.f;
+                *reinterpret_cast<uint32_t*>(xt + off) = pack_i8x4(p0, p1, p2, p3);
+                int is = (int)p0 + (int)p1 + (int)p2 + (int)p3;
+                is += __shfl_xor(is, 1, kWave);
+                is += __shfl_xor(is, 2, kWave);
+                if ((tid & 3) == 0)
+                    reinterpret_cast<float*>(xt + kI8SumOff)[half * kWave + lane] = (float)is * d;
+                if ((tid & 7) == 0) reinterpret_cast<float*>(xt + kI8ScaleOff)[bl * 8 + j] = d;
+                continue;
+            }
             // s = 2^e with m / s in [63.75, 127.5): e from the exponent of m
             int e = finite && m > 0.f ? __builtin_amdgcn_frexp_expf(m) - 7 : 0;
             if (ldexpf(m, -e) >= 127.5f) ++e;
@@ -949,7 +972,7 @@ __device__ __forceinline__ int lane_value(int v, int src) { return __builtin_amd
 // residual update x += MoE(RMSNorm(x))): every workgroup has read all of
 // hidden before it publishes its router partials, and no workgroup writes
 // out before it has seen all of them.  Hence neither pointer is restrict.
-template <bool kRoute>
+template <bool kRoute, int NP>
 __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
     const float* hidden, int64_t T, int64_t F, int32_t E, int32_t k,
     const int32_t* __restrict__ idx, const float* __restrict__ w,
@@ -1018,8 +1041,8 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
         if (issue_weights)
             gu_rows_load(rows, e0, E, gbase, gstride, ubase, ustride, r0, lane);
         __builtin_amdgcn_sched_barrier(0);
-        build_x_pieces<kFzMaxTokens>(xv, T, smem, tid);
-        if (second) build_x_pieces<kFzMaxTokens>(xw, T, smem, kXThr + tid);
+        build_x_pieces<kFzMaxTokens, NP>(xv, T, smem, tid);
+        if (second) build_x_pieces<kFzMaxTokens, NP>(xw, T, smem, kXThr + tid);
         else asm volatile("" ::"v"(xw[0].x), "v"(xw[1].x), "v"(xw[2].x), "v"(xw[3].x));
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -1112,7 +1135,7 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
         }
         // the activation pieces, by every wave, while the partial logits
         // travel (thread tid converts the values it holds)
-        build_x_pieces<kFzMaxTokens>(xv, T, smem, tid);
+        build_x_pieces<kFzMaxTokens, NP>(xv, T, smem, tid);
         // (b) every partial logit of every token, then (c) the top-k of token
         // t on wave t; logit = the sum of the expert's parts in part order
         // logits of every token (the sum of an expert's parts in part order)
@@ -1187,18 +1210,18 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
         __builtin_amdgcn_s_setprio(2);
         if (tau < n_gu) {
             int xc = p / k;                   // token whose pieces x holds
-            XCols x = load_xcols(smem + xc * kI8TokenBytes, lane);
-            gu_rows_finish(rows, x, lane, hbuf, (int64_t)p * F + r0, tag);
+            XCols x = load_xcols<NP>(smem + xc * kI8TokenBytes, lane);
+            gu_rows_finish<NP>(rows, x, lane, hbuf, (int64_t)p * F + r0, tag);
             for (tau += gu_step; tau < n_gu; tau += gu_step) {
                 p = tau / tiles;
                 r0 = (tau % tiles) * G::R;
                 gu_rows_load(rows, lane_value(my_idx, p), E, gbase, gstride, ubase, ustride, r0, lane);
                 const int t = p / k;
                 if (t != xc) {
-                    x = load_xcols(smem + t * kI8TokenBytes, lane);
+                    x = load_xcols<NP>(smem + t * kI8TokenBytes, lane);
                     xc = t;
                 }
-                gu_rows_finish(rows, x, lane, hbuf, (int64_t)p * F + r0, tag);
+                gu_rows_finish<NP>(rows, x, lane, hbuf, (int64_t)p * F + r0, tag);
             }
         }
         __builtin_amdgcn_s_setprio(0);
@@ -1404,7 +1427,7 @@ hipError_t launch_down(const float* w, int64_t T, int64_t H, int64_t F, int32_t 
     return hipGetLastError();
 }
 
-template <bool kRoute>
+template <bool kRoute, int NP>
 hipError_t launch_fused8(const float* hidden, int64_t T, int64_t F, int32_t E, int32_t k,
                          const int32_t* idx, const float* w, const ExpertTensor& gate,
                          const ExpertTensor& up, const ExpertTensor& down, float* out,
@@ -1413,9 +1436,9 @@ hipError_t launch_fused8(const float* hidden, int64_t T, int64_t F, int32_t E, i
                          uint64_t* rbuf, const float* norm_gain, float eps, hipStream_t stream) {
     const FusedLds L = fused_lds(T, F, down.qtype);
     static LdsLimit lds_set;
-    hipError_t err = ensure_lds(reinterpret_cast<const void*>(ffn_fused8_kernel<kRoute>), lds_set, L.total);
+    hipError_t err = ensure_lds(reinterpret_cast<const void*>(ffn_fused8_kernel<kRoute, NP>), lds_set, L.total);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(ffn_fused8_kernel<kRoute>, dim3((unsigned)grid), dim3(kFzWaves * kWave),
+    hipLaunchKernelGGL((ffn_fused8_kernel<kRoute, NP>), dim3((unsigned)grid), dim3(kFzWaves * kWave),
                        (size_t)L.total, stream, hidden, T, F, E, k, idx, w, gate.base, gate.stride,
                        up.base, up.stride, down.base, down.qtype, down.stride, out, accumulate,
                        reinterpret_cast<uint64_t*>(hp), sync, router, (int32_t)P, topk_idx, topk_w,
@@ -1427,7 +1450,7 @@ hipError_t launch_fused8(const float* hidden, int64_t T, int64_t F, int32_t E, i
 // current device holds at once with `lds` bytes of dynamic LDS (the
 // occupancy calculator's answer for this kernel's registers, waves and LDS),
 // cached per (device, LDS size); 0 when the device cannot run it.
-template <bool kRoute>
+template <bool kRoute, int NP>
 int fused_blocks_per_cu(int lds) {
     static std::atomic<int64_t> cache[kMaxDevices];   // (lds << 16) | (blocks + 1)
     static LdsLimit lds_set;
@@ -1437,7 +1460,7 @@ int fused_blocks_per_cu(int lds) {
         const int64_t c = cache[dev].load(std::memory_order_relaxed);
         if (c != 0 && (c >> 16) == lds) return (int)(c & 0xffff) - 1;
     }
-    const void* fn = reinterpret_cast<const void*>(ffn_fused8_kernel<kRoute>);
+    const void* fn = reinterpret_cast<const void*>(ffn_fused8_kernel<kRoute, NP>);
     if (ensure_lds(fn, lds_set, lds) != hipSuccess) return 0;
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, kFzWaves * kWave, (size_t)lds) != hipSuccess ||
@@ -1453,13 +1476,14 @@ int fused_blocks_per_cu(int lds) {
 // exceeds the compute units times the workgroups one unit holds (the
 // occupancy calculator's figure), and a device that holds none at this LDS
 // size takes the two-kernel path.
-int fused_grid(int64_t T, int64_t H, int64_t F, int32_t k, int32_t dqtype, bool route) {
+int fused_grid(int64_t T, int64_t H, int64_t F, int32_t k, int32_t dqtype, bool route, int np = 3) {
     if (H != (int64_t)kFzNB * kQK || k > kFzMaxSlots || T > kFzMaxTokens || T < 1) return 0;
     const int lds = fused_lds(T, F, dqtype).total;
     if ((size_t)lds > kMaxLdsPerWorkgroup) return 0;
     const int cus = cu_count();
     if (cus <= 0) return 0;
-    const int per_cu = route ? fused_blocks_per_cu<true>(lds) : fused_blocks_per_cu<false>(lds);
+    const int per_cu = !route ? fused_blocks_per_cu<false, 3>(lds)
+                       : np == 1 ? fused_blocks_per_cu<true, 1>(lds) : fused_blocks_per_cu<true, 3>(lds);
     if (per_cu < 1) return 0;
     const int64_t tiles = F / GuTask<kFzNB>::R;
     const int64_t need = (T * k * tiles + kFzGu - 1) / kFzGu;
@@ -1485,7 +1509,7 @@ hipError_t launch_decode_nb(const float* hidden, int64_t T, int64_t H, int64_t F
     if constexpr (NB == kFzNB) {
         const int grid = fused_grid(T, H, F, k, down.qtype, false);
         if (grid > 0)
-            return launch_fused8<false>(hidden, T, F, E, k, idx, w, gate, up, down, out, accumulate,
+            return launch_fused8<false, 3>(hidden, T, F, E, k, idx, w, gate, up, down, out, accumulate,
                                         hp, sync, grid, nullptr, 1, nullptr, nullptr, nullptr, nullptr,
                                         0.f, stream);
     }
@@ -1524,8 +1548,9 @@ bool expert_ffn_fused(int64_t T, int64_t H, int64_t F, int32_t k, int32_t dqtype
            fused_grid(T, H, F, k, dqtype, false) > 0;
 }
 
-bool moe_decode_fused(int64_t T, int64_t H, int64_t F, int32_t E, int32_t k, int32_t dqtype) {
-    return E <= kFzRouteNper * kWave && fused_grid(T, H, F, k, dqtype, true) > 0;
+bool moe_decode_fused(int64_t T, int64_t H, int64_t F, int32_t E, int32_t k, int32_t dqtype,
+                      int act_pieces) {
+    return E <= kFzRouteNper * kWave && fused_grid(T, H, F, k, dqtype, true, act_pieces) > 0;
 }
 
 size_t moe_route_words_bytes(int64_t T, int32_t E) {
@@ -1536,14 +1561,22 @@ hipError_t launch_moe_decode(const float* hidden, int64_t T, int64_t H, int64_t 
                              int32_t k, const float* router, int32_t* topk_idx, float* topk_w,
                              const ExpertTensor& gate, const ExpertTensor& up,
                              const ExpertTensor& down, float* out, int accumulate, void* ffn_ws,
-                             void* route_words, const float* norm_gain, float eps, hipStream_t stream) {
-    const int grid = fused_grid(T, H, F, k, down.qtype, true);
+                             void* route_words, const float* norm_gain, float eps, hipStream_t stream,
+                             int act_pieces) {
+    if (act_pieces != 1 && act_pieces != 3) return hipErrorInvalidValue;
+    const int grid = fused_grid(T, H, F, k, down.qtype, true, act_pieces);
     if (grid <= 0 || E > kFzRouteNper * kWave) return hipErrorInvalidValue;
     int32_t* sync = static_cast<int32_t*>(ffn_ws);
     uint8_t* hp = static_cast<uint8_t*>(ffn_ws) + kFfnSyncBytes;
-    return launch_fused8<true>(hidden, T, F, E, k, nullptr, nullptr, gate, up, down, out, accumulate,
-                               hp, sync, grid, router, route_parts(E, grid), topk_idx, topk_w,
-                               static_cast<uint64_t*>(route_words), norm_gain, eps, stream);
+    auto* rw = static_cast<uint64_t*>(route_words);
+    const int P = route_parts(E, grid);
+    if (act_pieces == 1)
+        return launch_fused8<true, 1>(hidden, T, F, E, k, nullptr, nullptr, gate, up, down, out,
+                                      accumulate, hp, sync, grid, router, P, topk_idx, topk_w, rw,
+                                      norm_gain, eps, stream);
+    return launch_fused8<true, 3>(hidden, T, F, E, k, nullptr, nullptr, gate, up, down, out, accumulate,
+                                  hp, sync, grid, router, P, topk_idx, topk_w, rw, norm_gain, eps,
+                                  stream);
 }
 
 }  // namespace q3moe

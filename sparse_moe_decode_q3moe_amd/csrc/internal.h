@@ -89,7 +89,10 @@ hipError_t launch_decode_ffn(const float* hidden, int64_t T, int64_t H, int64_t 
 // memory that the kernel's routing step uses for its tagged partial logits;
 // norm_gain (or null) applies the input RMSNorm inside the kernel, and then
 // hidden may equal out.
-bool moe_decode_fused(int64_t T, int64_t H, int64_t F, int32_t E, int32_t k, int32_t dqtype);
+// act_pieces: 3 = the gate/up activations as three exact int8 pieces (the
+// f32 block), 1 = one int8 piece per value (the int8-activation mode).
+bool moe_decode_fused(int64_t T, int64_t H, int64_t F, int32_t E, int32_t k, int32_t dqtype,
+                      int act_pieces = 3);
 // Whether launch_expert_ffn runs this shape as the one persistent kernel.
 bool expert_ffn_fused(int64_t T, int64_t H, int64_t F, int32_t k, int32_t dqtype);
 size_t moe_route_words_bytes(int64_t T, int32_t E);
@@ -98,7 +101,7 @@ hipError_t launch_moe_decode(const float* hidden, int64_t T, int64_t H, int64_t 
                              const ExpertTensor& gate, const ExpertTensor& up,
                              const ExpertTensor& down, float* out, int accumulate, void* ffn_ws,
                              void* route_words, const float* norm_gain, float eps,
-                             hipStream_t stream);
+                             hipStream_t stream, int act_pieces = 3);
 
 // ffn.hip: dispatch, and the generic path for any H, F multiple of 256
 size_t expert_ffn_workspace_bytes(int64_t T, int64_t H, int64_t F, int32_t E, int32_t k);

@@ -430,6 +430,76 @@ def pin_ffn_expert_stride(o):
 
 # --------------------------------------------------------- norm and RoPE -----
 
+# ------------------------------------------------- int8 activations (Q8) -----
+
+def pin_q8_hand_group(o):
+    """A hand-worked 32-value group: max |x| = 127 gives d = 1 exactly, so
+    p = x rounded to the nearest integer with ties to even (63.5 -> 64,
+    -63.5 -> -64, 0.5 -> 0, 1.5 -> 2, 2.5 -> 2, -2.5 -> -2); a second group
+    scaled by 2^-3 gives d = 2^-3 and the same integers; an all-zero group
+    gives d = 0, p = 0; a group holding +inf or NaN gives NaN values."""
+    g = np.array([127, 63.5, -63.5, 0.5, 1.5, 2.5, -2.5, -127, 3.25, -0.75] + [0.0] * 22, np.float32)
+    want = np.array([127, 64, -64, 0, 2, 2, -2, -127, 3, -1] + [0] * 22, np.int8)
+    zero = np.zeros(32, np.float32)
+    bad = g.copy()
+    bad[5] = np.inf
+    nan = g.copy()
+    nan[9] = np.nan
+    x = np.stack([np.concatenate([g, g / 8]), np.concatenate([zero, bad]),
+                  np.concatenate([nan, g])])
+    p, d, xq = o.quantize_act_q8(x)
+    assert np.array_equal(p[0, :32], want) and np.array_equal(p[0, 32:], want)
+    assert d[0, 0] == 1.0 and d[0, 1] == 0.125
+    assert np.array_equal(xq[0, :32], want.astype(np.float64))
+    assert d[1, 0] == 0.0 and np.all(p[1, :32] == 0) and np.all(xq[1, :32] == 0.0)
+    assert np.isnan(d[1, 1]) and np.all(np.isnan(xq[1, 32:]))
+    assert np.isnan(d[2, 0]) and np.all(np.isnan(xq[2, :32]))
+    assert np.array_equal(p[2, 32:], want)
+
+
+def pin_q8_bounds(o):
+    """On N(0, 1) rows: d = max|x| / 127 rounded to f32 (NumPy's own f32
+    division), |p| <= 127 with the largest value at +-127, and every value
+    within half a step of its group's scale: |x - d p| <= d / 2 (plus the
+    f32 rounding of x / d)."""
+    x = gen.hidden_states(3, 2048, 77).numpy()
+    p, d, xq = o.quantize_act_q8(x)
+    g = x.reshape(3, 64, 32)
+    amax = np.abs(g).max(axis=2)
+    assert np.array_equal(d, (amax / np.float32(127)).astype(np.float32))
+    assert np.abs(p.astype(np.int32)).max() <= 127
+    pg = p.reshape(3, 64, 32).astype(np.int32)
+    top = np.take_along_axis(pg, np.abs(g).argmax(axis=2)[..., None], axis=2)[..., 0]
+    assert np.all(np.abs(top) == 127)
+    err = np.abs(x.astype(np.float64) - xq).reshape(3, 64, 32)
+    assert np.all(err <= d[..., None].astype(np.float64) * (0.5 + 1e-6))
+    assert np.array_equal(xq, d.repeat(32, axis=1).astype(np.float64) * p)
+
+
+def pin_q8_ffn_is_block_on_quantised_input(o):
+    """The int8-activation block equals the dense NumPy block evaluated on
+    the dequantised activations d * p for gate and up (the down projection
+    on h as computed), summed over the selected experts with their weights."""
+    shape = gen.MoeShape(T=3, H=256, E=6, k=3, F=512, down_qtype=Q6_K)
+    layer, x = _ffn_case(shape, 38)
+    idx, w, _ = o.route(x, layer.router.numpy(), shape.k)
+    _, _, xq = o.quantize_act_q8(x)
+    Wg = _dense_experts(o, layer.gate.numpy(), Q4_K, shape.E, shape.F, shape.H)
+    Wu = _dense_experts(o, layer.up.numpy(), Q4_K, shape.E, shape.F, shape.H)
+    Wd = _dense_experts(o, layer.down.numpy(), Q6_K, shape.E, shape.H, shape.F)
+    ref = np.zeros((shape.T, shape.H))
+    for t in range(shape.T):
+        for s_ in range(shape.k):
+            e = idx[t, s_]
+            ref[t] += w[t, s_] * ((_silu(Wg[e] @ xq[t]) * (Wu[e] @ xq[t])) @ Wd[e].T)
+    got = o.expert_ffn_q8(x, idx, w, *_tensors(layer), F=shape.F, E=shape.E)
+    _close(got, ref.astype(np.float32), 1e-6, "int8-activation block")
+    prev = (x * 2.0).astype(np.float32)
+    acc = o.expert_ffn_q8(x, idx, w, *_tensors(layer), F=shape.F, E=shape.E, out=prev,
+                          accumulate=True)
+    _close(acc, prev.astype(np.float64) + ref, 1e-6, "int8-activation block, accumulate")
+
+
 def pin_rmsnorm_closed_form(o):
     """With unit gain, RMS(y)^2 = ms / (ms + eps); gains multiply
     elementwise; with eps = 0 the result is scale invariant."""

@@ -249,3 +249,93 @@ def test_persistent_path_is_taken_at_decode(layers):
     _check(cpu, got, x, "persistent path")
     assert counter() == before + 1
     assert q3.expert_ffn_status(ws, s.T, s.H, s.F, s.E, s.k) == 0
+
+
+# Error budget of the int8 activations against the f32 block (relative L2):
+# over a batch of tokens 2e-2 (the oracle shows 0.5-0.6 % at the 30B-A3B
+# shape), per token 0.25 (a token whose block output nearly cancels, as the
+# large min offsets of random Q4_K down weights make some do, reaches ~15 %).
+Q8_BUDGET_BATCH = 2e-2
+Q8_BUDGET_TOKEN = 0.25
+
+
+@pytest.mark.parametrize("name", ["a3b_T1", "a3b_T4", "a3b_q4k_down_T3", "E72_k6_T3"])
+def test_moe_ffn_int8_activations(layers, name):
+    """q3moe_moe_ffn_q8: routing identical to the f32 block; outputs within
+    1e-4 of the oracle that quantises the gate/up input the same way (one
+    int8 value per element, d = max|x|/127 per 32 values), and within the
+    stated error budget of the f32 oracle."""
+    cpu, dev, x = layers(name)
+    s = cpu.shape
+    say(f"moe_ffn int8 activations {name}")
+    got = q3.q3moe_moe_ffn(x.to(DEV), dev.router, s.k, *experts_of(dev), F=s.F, int8_activations=True)
+    torch.cuda.synchronize()
+    o = oracle.oracle()
+    ref_idx, ref_w, logits = o.route(x.numpy(), cpu.router.numpy(), s.k)
+    from parity import oracle_tensors, rel_l2_rows
+    ref_q8 = o.expert_ffn_q8(x.numpy(), ref_idx, ref_w, *oracle_tensors(cpu), F=s.F, E=s.E)
+    ref_f32 = o.expert_ffn(x.numpy(), ref_idx, ref_w, *oracle_tensors(cpu), F=s.F, E=s.E)
+    out, idx, w = got
+    assert_indices_equal(idx.cpu().numpy(), ref_idx, logits, s.k, name)
+    np.testing.assert_allclose(w.cpu().numpy(), ref_w, rtol=1e-6, atol=0)
+    err = assert_rows_close(out.cpu().numpy(), ref_q8, what=f"{name} int8 vs its oracle")
+    budget = rel_l2_rows(out.cpu().numpy(), ref_f32)
+    say(f"  vs the int8 oracle {err:.2e}; vs the f32 oracle max {budget.max():.2e}")
+    assert budget.max() <= Q8_BUDGET_TOKEN
+    # the mode really quantises: it is not the f32 block
+    assert budget.min() > 1e-4
+
+
+def test_moe_ffn_int8_activations_budget(layers):
+    """64 tokens (16 calls of 4) through the int8 mode at the 30B-A3B shape
+    with Q6_K and with Q4_K down: the relative L2 error against the f32
+    oracle over the batch within 2e-2 and per token within 0.25, and every
+    token within 1e-4 of the oracle that quantises the same way."""
+    from parity import oracle_tensors, rel_l2_rows
+    o = oracle.oracle()
+    for name in ("a3b_T4", "a3b_q4k_down_T3"):
+        cpu, dev, _ = layers(name)
+        s = cpu.shape
+        x = gen.hidden_states(64, 2048, 777 + s.down_qtype)
+        outs = []
+        for c in range(16):
+            xc = x[4 * c:4 * c + 4].contiguous()
+            out, _, _ = q3.q3moe_moe_ffn(xc.to(DEV), dev.router, s.k, *experts_of(dev), F=s.F,
+                                         int8_activations=True)
+            outs.append(out)
+        got = torch.cat(outs).cpu().numpy().astype(np.float64)
+        ridx, rw, _ = o.route(x.numpy(), cpu.router.numpy(), s.k)
+        ref_q8 = o.expert_ffn_q8(x.numpy(), ridx, rw, *oracle_tensors(cpu), F=s.F, E=s.E)
+        ref = o.expert_ffn(x.numpy(), ridx, rw, *oracle_tensors(cpu), F=s.F, E=s.E).astype(np.float64)
+        assert_rows_close(got, ref_q8, what=f"{name} int8 batch vs its oracle")
+        per = rel_l2_rows(got, ref)
+        agg = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+        say(f"int8 budget {name}: batch {agg:.2e}, per token max {per.max():.2e} median {np.median(per):.2e}")
+        assert agg <= Q8_BUDGET_BATCH and per.max() <= Q8_BUDGET_TOKEN
+
+
+def test_moe_ffn_int8_activations_edge_cases(layers):
+    """A group of zeros, a group of evenly spaced values, and a group whose
+    values sit exactly on half steps (ties go to even)."""
+    cpu, dev, x = layers("a3b_T2")
+    s = cpu.shape
+    x1 = x.clone()
+    x1[0, :32] = 0.0
+    x1[0, 32:64] = torch.arange(32, dtype=torch.float32) - 15.5       # d = 16.5/127
+    x1[0, 64:96] = torch.tensor([127.0, 0.5, 1.5, 2.5] * 8)           # d = 1: ties to even
+    got = q3.q3moe_moe_ffn(x1.to(DEV), dev.router, s.k, *experts_of(dev), F=s.F, int8_activations=True)
+    torch.cuda.synchronize()
+    o = oracle.oracle()
+    from parity import oracle_tensors
+    ref_idx, ref_w, logits = o.route(x1.numpy(), cpu.router.numpy(), s.k)
+    ref = o.expert_ffn_q8(x1.numpy(), ref_idx, ref_w, *oracle_tensors(cpu), F=s.F, E=s.E)
+    assert_indices_equal(got[1].cpu().numpy(), ref_idx, logits, s.k, "int8 edge cases")
+    assert_rows_close(got[0].cpu().numpy(), ref, what="int8 edge cases")
+
+
+def test_moe_ffn_int8_activations_rejects_other_shapes(layers):
+    cpu, dev, x = layers("a3b_T5")
+    s = cpu.shape
+    with pytest.raises(q3.Q3MoeError) as e:
+        q3.q3moe_moe_ffn(x.to(DEV), dev.router, s.k, *experts_of(dev), F=s.F, int8_activations=True)
+    assert e.value.status == 2

@@ -114,6 +114,7 @@ def test_free_running_stack(T, n_layers, form):
     ws = _ws(T)
     x_ref = x0.copy()
     worst = 0.0
+    trace = []                                     # per layer: (GPU std, oracle std, GPU rms, oracle rms)
     for l, layer in enumerate(layers):
         idx = _gpu_layer(layer, x_gpu, ones, form, ws)
         torch.cuda.synchronize()
@@ -123,6 +124,18 @@ def test_free_running_stack(T, n_layers, form):
         drift = float(np.max(np.linalg.norm(x_pert.astype(np.float64) - x_ref, axis=1) /
                              np.linalg.norm(x_ref, axis=1)))
         tol = max(1e-4, 100.0 * drift)
-        err = assert_rows_close(x_gpu.cpu().numpy(), x_ref, tol=tol, what=f"layer {l}")
+        xg = x_gpu.cpu().numpy()
+        err = assert_rows_close(xg, x_ref, tol=tol, what=f"layer {l}")
         worst = max(worst, err / tol)
+        # the per-layer activation trace (std-dev and RMS of each token's
+        # residual row), the diagnostic that localises a layer-wise blow-up
+        g64, r64 = xg.astype(np.float64), x_ref.astype(np.float64)
+        tr = (g64.std(axis=1), r64.std(axis=1), np.sqrt((g64 ** 2).mean(axis=1)),
+              np.sqrt((r64 ** 2).mean(axis=1)))
+        assert np.all(np.abs(tr[0] - tr[1]) <= tol * tr[1]), f"layer {l}: std-dev trace"
+        assert np.all(np.abs(tr[2] - tr[3]) <= tol * tr[3]), f"layer {l}: RMS trace"
+        trace.append([float(v[0]) for v in tr])
     say(f"  worst error / tolerance over the stack: {worst:.3f}")
+    say("  residual std-dev by layer (token 0): " +
+        " ".join(f"{l}:{trace[l][0]:.3g}" for l in range(0, len(trace), max(1, len(trace) // 8))) +
+        f" {len(trace) - 1}:{trace[-1][0]:.3g}")

@@ -63,6 +63,10 @@ MUTANTS = [
     ("attention_scale_dropped", "sc[j] = scale * d;", "sc[j] = d;"),
     ("attention_one_past_length", "int64_t L = len[b];", "int64_t L = len[b] < S_max ? len[b] + 1 : len[b];"),
     ("attention_k_as_v", "acc += sc[j] * orc_bf16_to_double(V[j * D + i]);", "acc += sc[j] * orc_bf16_to_double(K[j * D + i]);"),
+    ("q8_round_half_away", "rintf(v[i] / dg)", "roundf(v[i] / dg)"),
+    ("q8_scale_128", "amax / 127.0f", "amax / 128.0f"),
+    ("q8_output_scaled", "expert_ffn_on(xq, T, H, F, E, k, idx, w, gate, gate_qt, gate_stride,\n                           up, up_qt, up_stride, down, down_qt, down_stride, o);",
+     "expert_ffn_on(xq, T, H, F, E, k, idx, w, gate, gate_qt, gate_stride,\n                           up, up_qt, up_stride, down, down_qt, down_stride, o);\n    for (int64_t i = 0; i < T * H; i++) o[i] = (double)(float)o[i] * 1.0001;"),
     ("prologue_head_dim_halved", "rmsnorm_vec(v, D, g, (double)eps, y);", "rmsnorm_vec(v, D / 2, g, (double)eps, y); rmsnorm_vec(v + D / 2, D / 2, g, (double)eps, y + D / 2);"),
 ]
 
