@@ -343,6 +343,39 @@ q3moe_status q3moe_attn_prologue_kv(float *q, float *k, const float *v, int64_t 
                                     uint16_t *k_cache, uint16_t *v_cache, int64_t S_max,
                                     void *stream);
 
+/* ------------------------------------------------ model ends: embedding --
+ * The ends of a whole-model decode step around the decoder layers: token
+ * embedding, final RMSNorm (q3moe_rmsnorm) and the output head (the Qwen3
+ * weight loader of the atlas docs, spark_model/weight_loader/qwen3.rs, loads
+ * these three; issue #3714 "File facts": the output matrix is Q6_K).
+ *
+ * out[t] = row tokens[t] of the embedding table, dequantised:
+ *   tokens [T] int32 (device); table: V rows of H/256 k-quant super-blocks
+ *   (Q4_K or Q6_K, the row layout of the expert matrices), read in place;
+ *   out [T x H] f32.  Each value is the block formula rounded once to f32
+ *   (bit-identical to a dequantisation in exact arithmetic).  A token outside
+ *   [0, V) gives a row of NaN.
+ * Limits: H % 256 == 0, 256 <= H <= 65536, 1 <= V < 2^31.
+ * Errors: E_NULL, E_SHAPE, E_QTYPE, E_ALIAS (out overlaps tokens or table),
+ * E_HIP. */
+q3moe_status q3moe_embed(const int32_t *tokens, int64_t T, const void *table, int32_t qtype,
+                         int64_t V, int64_t H, float *out, void *stream);
+
+/* ----------------------------------------------- model ends: output head --
+ * logits[t][v] = sum_h W[v][h] x[t][h] over the V rows of a Q6_K matrix (the
+ * lm_head / output.weight of the model, read in place as one stream):
+ *   x [T x H] f32, 16-byte aligned (the final-norm output); W: V rows of
+ *   H/256 Q6_K super-blocks, 16-byte aligned; logits [T x V] f32, 4-byte
+ *   aligned.  The activations enter as three int8 pieces with a power-of-two
+ *   scale per 32 values (exact to 2^-15 of the group's largest value), each
+ *   16-weight group's dot product is an exact int32 sum, scales apply in f32.
+ *   The matrix is read once per two tokens.
+ * Limits: H = 2048, qtype Q3MOE_Q6_K, 1 <= V < 2^31.
+ * Errors: E_NULL, E_SHAPE, E_QTYPE, E_ALIGN, E_ALIAS (logits overlap x or W),
+ * E_HIP. */
+q3moe_status q3moe_output_head(const float *x, int64_t T, const void *W, int32_t qtype, int64_t V,
+                               int64_t H, float *logits, void *stream);
+
 /* --------------------------------------------------------------- RMSNorm --
  * out[t] = gain * x[t] / sqrt(mean(x[t]^2) + eps) for x [T x n] f32; the
  * per-layer input / post-attention norm of the decoder layer.  The squares

@@ -18,6 +18,9 @@ Parity status per function (how each is pinned is listed in the tests):
   quantize_act_q8 / expert_ffn_q8 pinned: hand-worked groups (ties to even,
                                   all-zero, non-finite), |x - d p| <= d/2,
                                   the f64 block on the dequantised values
+  embed / output_head             pinned: rows of the pinned dequantisation,
+                                  NaN rows out of range, dense NumPy product,
+                                  one-hot column probes
   rmsnorm / attn_prologue /       pinned: RMS closed form, rotation invariants,
   rope_neox                       NEOX-vs-interleaved discriminator
   group_by_expert                 pinned: a library sort of (expert, pair),
@@ -92,6 +95,8 @@ def _declare(lib):
                                              _P, ctypes.c_int, _I64,
                                              _P, ctypes.c_int, _I64, _P, ctypes.c_int]),
         "orc_quantize_act_q8": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
+        "orc_embed": (ctypes.c_int, [_P, _I64, _P, ctypes.c_int, _I64, _I64, _P]),
+        "orc_output_head": (ctypes.c_int, [_P, _I64, _P, ctypes.c_int, _I64, _I64, _P]),
         "orc_rmsnorm": (ctypes.c_int, [_P, _I64, _I64, _P, ctypes.c_float, _P]),
         "orc_group_by_expert": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _P, _P]),
         "orc_bf16_to_double": (ctypes.c_double, [ctypes.c_uint16]),
@@ -312,6 +317,25 @@ class Oracle:
                                          _p(g), gq, gs, _p(u), uq, us, _p(d), dq, ds, _p(res))
         assert rc == 0, rc
         return res
+
+    def embed(self, tokens: np.ndarray, table: np.ndarray, qtype: int, V: int, H: int) -> np.ndarray:
+        """tokens int32 [T]; table uint8 (V rows of H/256 blocks) -> f32 [T, H]."""
+        tokens = _c(tokens, np.int32).reshape(-1)
+        table = _c(table, np.uint8)
+        assert table.size >= V * (H // 256) * BLOCK_BYTES[qtype]
+        out = np.empty((tokens.size, H), np.float32)
+        assert self.lib.orc_embed(_p(tokens), tokens.size, _p(table), qtype, V, H, _p(out)) == 0
+        return out
+
+    def output_head(self, x: np.ndarray, W: np.ndarray, qtype: int, V: int) -> np.ndarray:
+        """x f32 [T, H]; W uint8 (V rows of H/256 blocks) -> logits f32 [T, V]."""
+        x = _c(x, np.float32)
+        W = _c(W, np.uint8)
+        T, H = x.shape
+        assert W.size >= V * (H // 256) * BLOCK_BYTES[qtype]
+        out = np.empty((T, V), np.float32)
+        assert self.lib.orc_output_head(_p(x), T, _p(W), qtype, V, H, _p(out)) == 0
+        return out
 
     def rmsnorm(self, x: np.ndarray, gain: np.ndarray, eps: float) -> np.ndarray:
         x = _c(x, np.float32)

@@ -376,6 +376,47 @@ int orc_expert_ffn(const float *x, int64_t T, int64_t H, int64_t F, int32_t E, i
     return rc;
 }
 
+/* Whole-model ends of the decode step (the token embedding and the output
+ * head around the 48 layers; issue #3714 "File facts": the output matrix is
+ * Q6_K; the embedding rows and the head rows are k-quant rows of H inputs).
+ * Embedding: out[t] = row tokens[t] of the table [V x H], dequantised and
+ * rounded once to f32; a token outside [0, V) gives a row of NaN. */
+int orc_embed(const int32_t *tokens, int64_t T, const uint8_t *table, int qtype, int64_t V,
+              int64_t H, float *out)
+{
+    if (!orc_block_bytes(qtype) || H % ORC_QK) return -1;
+    double *row = (double *)malloc(sizeof(double) * H);
+    for (int64_t t = 0; t < T; t++) {
+        int64_t v = tokens[t];
+        if (v < 0 || v >= V) {
+            for (int64_t i = 0; i < H; i++) out[t * H + i] = NAN;
+            continue;
+        }
+        orc_dequant_row(qtype, table, v, H, row);
+        for (int64_t i = 0; i < H; i++) out[t * H + i] = (float)row[i];
+    }
+    free(row);
+    return 0;
+}
+
+/* Output head: logits[t][v] = sum_h W[v][h] x[t][h] for the V rows of W
+ * (the k-quant GEMV above over the vocabulary), each logit rounded once to
+ * f32. */
+int orc_output_head(const float *x, int64_t T, const uint8_t *W, int qtype, int64_t V, int64_t H,
+                    float *logits)
+{
+    if (!orc_block_bytes(qtype) || H % ORC_QK) return -1;
+    double *xd = (double *)malloc(sizeof(double) * H);
+    double *y = (double *)malloc(sizeof(double) * (V > 0 ? V : 1));
+    for (int64_t t = 0; t < T; t++) {
+        for (int64_t i = 0; i < H; i++) xd[i] = x[t * H + i];
+        orc_qgemv(qtype, W, V, H, xd, y);
+        for (int64_t v = 0; v < V; v++) logits[t * V + v] = (float)y[v];
+    }
+    free(xd); free(y);
+    return 0;
+}
+
 /* Token -> expert grouping of the routed (token, slot) pairs (survey row
  * a3; the pages' plan groups tokens by expert for batched prefill, #3714
  * gap list).  Pair p = t*k + slot with expert idx[p].  For every expert e in

@@ -26,6 +26,7 @@ EXPORTS = (
     "q3moe_gqa_attention_workspace_bytes", "q3moe_gqa_attention",
     "q3moe_moe_ffn_workspace_bytes", "q3moe_moe_ffn", "q3moe_moe_ffn_prenorm", "q3moe_bf16_gemv3",
     "q3moe_attn_prologue_kv", "q3moe_persistent_path", "q3moe_moe_ffn_noalloc", "q3moe_moe_ffn_q8",
+    "q3moe_embed", "q3moe_output_head",
 )
 
 
@@ -69,6 +70,8 @@ _SIGS = {
                                      _Experts, _Experts, _P, _P, _P, _I32, _P, ctypes.c_size_t,
                                      _P]),
     "q3moe_persistent_path": (_I32, [_I64, _I64, _I64, _I32, _I32, _I32, _I32]),
+    "q3moe_embed": (_I32, [_P, _I64, _P, _I32, _I64, _I64, _P, _P]),
+    "q3moe_output_head": (_I32, [_P, _I64, _P, _I32, _I64, _I64, _P, _P]),
     "q3moe_moe_ffn_q8": (_I32, [_P, _I64, _I64, _I64, _I32, _I32, _P, _Experts, _Experts, _Experts,
                                 _P, _P, _P, _I32, _P, ctypes.c_size_t, _P]),
     "q3moe_moe_ffn_noalloc": (_I32, [_P, _I64, _I64, _I64, _I32, _I32, _P, _Experts, _Experts,
@@ -400,6 +403,48 @@ def q3moe_bf16_gemv3(Ws, x: torch.Tensor, norm_gain: Optional[torch.Tensor] = No
         Wp[0], Np[0], Wp[1], Np[1], Wp[2], Np[2], K, _ptr(x), T, _ptr(norm_gain), eps,
         yp[0], yp[1], yp[2], _stream(stream)))
     return outs
+
+
+def _table(W: torch.Tensor, name: str):
+    if W.dtype != torch.uint8 or not W.is_contiguous() or W.device.type != "cuda":
+        raise ValueError(f"{name} must be a contiguous uint8 tensor on a HIP device")
+
+
+def q3moe_embed(tokens: torch.Tensor, table: torch.Tensor, qtype: int, V: int, H: int,
+                out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Rows tokens[t] of a k-quant embedding table (V rows of H/256 blocks),
+    dequantised; -> out f32 [T, H]."""
+    _need(tokens, "tokens", torch.int32, 1)
+    _table(table, "table")
+    if table.numel() < V * q3moe_expert_matrix_bytes(qtype, 1, H):
+        raise ValueError("table is smaller than V rows")
+    T = tokens.shape[0]
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float32, device=tokens.device)
+    _need(out, "out", torch.float32, 2)
+    _check("q3moe_embed", library().q3moe_embed(_ptr(tokens), T, _ptr(table), qtype, V, H,
+                                                _ptr(out), _stream(stream)))
+    return out
+
+
+def q3moe_output_head(x: torch.Tensor, W: torch.Tensor, V: int, qtype: int = Q6_K,
+                      out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """logits f32 [T, V] = W x for a k-quant matrix W of V rows."""
+    _need(x, "x", torch.float32, 2)
+    _table(W, "W")
+    T, H = x.shape
+    if W.numel() < V * q3moe_expert_matrix_bytes(qtype, 1, H):
+        raise ValueError("W is smaller than V rows")
+    if out is None:
+        out = torch.empty((T, V), dtype=torch.float32, device=x.device)
+    _need(out, "out", torch.float32, 2)
+    _check("q3moe_output_head", library().q3moe_output_head(_ptr(x), T, _ptr(W), qtype, V, H,
+                                                            _ptr(out), _stream(stream)))
+    return out
+
+
+def q3moe_expert_matrix_bytes(qtype: int, rows: int, cols: int) -> int:
+    return library().q3moe_expert_matrix_bytes(qtype, rows, cols)
 
 
 def q3moe_rmsnorm(x: torch.Tensor, gain: torch.Tensor, eps: float,

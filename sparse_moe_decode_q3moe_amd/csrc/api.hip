@@ -303,6 +303,38 @@ q3moe_status q3moe_attn_prologue_kv(float* q, float* k, const float* v, int64_t 
                                                    S_max, as_stream(stream)));
 }
 
+q3moe_status q3moe_embed(const int32_t* tokens, int64_t T, const void* table, int32_t qtype,
+                         int64_t V, int64_t H, float* out, void* stream) {
+    if (T < 0 || T > 0x7fffffff || V < 1 || V > 0x7fffffff || H < 256 || H > 65536 || H % 256)
+        return Q3MOE_E_SHAPE;
+    if (qtype != Q3MOE_Q4_K && qtype != Q3MOE_Q6_K) return Q3MOE_E_QTYPE;
+    if (T == 0) return Q3MOE_OK;
+    if (!tokens || !table || !out) return Q3MOE_E_NULL;
+    const size_t no = (size_t)T * (size_t)H * sizeof(float);
+    const size_t nt = (size_t)V * (size_t)q3moe_expert_matrix_bytes(qtype, 1, H);
+    if (overlaps(out, no, table, nt) || overlaps(out, no, tokens, (size_t)T * 4)) return Q3MOE_E_ALIAS;
+    return from_hip(q3moe::launch_embed(tokens, T, static_cast<const uint8_t*>(table), qtype, V, H, out,
+                                        as_stream(stream)));
+}
+
+q3moe_status q3moe_output_head(const float* x, int64_t T, const void* W, int32_t qtype, int64_t V,
+                               int64_t H, float* logits, void* stream) {
+    if (T < 0 || T > 0x7fffffff || V < 1 || V > 0x7fffffff || H < 256 || H % 256 ||
+        (int64_t)T * V > ((int64_t)1 << 40))
+        return Q3MOE_E_SHAPE;
+    if (qtype != Q3MOE_Q6_K) return Q3MOE_E_QTYPE;
+    if (!q3moe::output_head_supported(H, qtype)) return Q3MOE_E_SHAPE;
+    if (T == 0) return Q3MOE_OK;
+    if (!x || !W || !logits) return Q3MOE_E_NULL;
+    if (!aligned16(x) || !aligned16(W) || (reinterpret_cast<uintptr_t>(logits) & 3u)) return Q3MOE_E_ALIGN;
+    const size_t nl = (size_t)T * (size_t)V * sizeof(float);
+    if (overlaps(logits, nl, x, (size_t)T * (size_t)H * sizeof(float)) ||
+        overlaps(logits, nl, W, (size_t)V * (size_t)q3moe_expert_matrix_bytes(qtype, 1, H)))
+        return Q3MOE_E_ALIAS;
+    return from_hip(q3moe::launch_output_head(x, T, static_cast<const uint8_t*>(W), V, logits,
+                                              as_stream(stream)));
+}
+
 q3moe_status q3moe_rmsnorm(const float* x, int64_t T, int64_t n, const float* gain, float eps,
                            float* out, void* stream) {
     if (T < 0 || T > 0x7fffffff || n < 1 || n > 65536 || !(eps >= 0.0f)) return Q3MOE_E_SHAPE;

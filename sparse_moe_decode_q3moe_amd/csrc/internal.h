@@ -132,6 +132,13 @@ hipError_t launch_gqa_attention(const float* q, int64_t B, int32_t n_q, int32_t 
                                 const int32_t* len, float scale, float* out, void* ws,
                                 hipStream_t stream);
 
+// model.hip: the token embedding gather and the Q6_K output head
+hipError_t launch_embed(const int32_t* tokens, int64_t T, const uint8_t* table, int32_t qtype,
+                        int64_t V, int64_t H, float* out, hipStream_t stream);
+bool output_head_supported(int64_t H, int32_t qtype);
+hipError_t launch_output_head(const float* x, int64_t T, const uint8_t* W, int64_t V, float* logits,
+                              hipStream_t stream);
+
 // norm.hip
 hipError_t launch_rmsnorm(const float* x, int64_t T, int64_t n, const float* gain, float eps,
                           float* out, hipStream_t stream);

@@ -65,6 +65,11 @@ class MoeShape:
 
 # The tiny layer (4 tokens, all Q4_K) and the Qwen3-30B-A3B decode layer.
 TINY = MoeShape(T=4, H=256, E=8, k=2, F=256, down_qtype=Q4_K)
+
+# Vocabulary of the output head and the embedding table.  The pages give no
+# size; the token ids they print (up to 151,645) need at least 151,646 rows,
+# and 151,936 is the Qwen3 family's padded vocabulary.
+QWEN3_VOCAB = 151936
 QWEN3_30B_A3B = MoeShape(T=1, H=2048, E=128, k=8, F=768, down_qtype=Q6_K)
 N_LAYERS_30B = 48               # down is Q6_K in layers 0-23, Q4_K in 24-47
 

@@ -430,6 +430,42 @@ def pin_ffn_expert_stride(o):
 
 # --------------------------------------------------------- norm and RoPE -----
 
+# ------------------------------------------------ embedding / output head -----
+
+def pin_embed_rows(o):
+    """The embedding gather returns the pinned dequantised rows of the
+    chosen tokens (first, last, repeated), rounded once to f32, for Q4_K and
+    Q6_K tables with a vocabulary that is not a multiple of anything; a token
+    outside [0, V) gives a NaN row."""
+    g = gen.make_generator(61)
+    for qt in (Q4_K, Q6_K):
+        V, H = 37, 512
+        table = gen.kquant_experts(qt, 1, V, H, g)[0].numpy()
+        dense = o.dequant_matrix(qt, table, V, H)
+        toks = np.array([0, 36, 5, 5, 17], np.int32)
+        got = o.embed(toks, table, qt, V, H)
+        assert np.array_equal(got, dense[toks].astype(np.float32))
+        bad = o.embed(np.array([3, -1, 37], np.int32), table, qt, V, H)
+        assert np.array_equal(bad[0], dense[3].astype(np.float32))
+        assert np.all(np.isnan(bad[1:]))
+
+
+def pin_output_head_dense(o):
+    """The head's logits equal a dense NumPy product of the pinned
+    dequantised Q6_K matrix with x (V = 301 rows, 2 tokens), and a one-hot x
+    reads back one column of the matrix."""
+    g = gen.make_generator(62)
+    V, H = 301, 512
+    W = gen.kquant_experts(Q6_K, 1, V, H, g)[0].numpy()
+    dense = o.dequant_matrix(Q6_K, W, V, H)
+    x = gen.hidden_states(2, H, 63).numpy()
+    got = o.output_head(x, W, Q6_K, V)
+    _close(got, (x.astype(np.float64) @ dense.T).astype(np.float32), 1e-7, "head dense product")
+    e = np.zeros((1, H), np.float32)
+    e[0, 300] = 1.0
+    assert np.array_equal(o.output_head(e, W, Q6_K, V)[0], dense[:, 300].astype(np.float32))
+
+
 # ------------------------------------------------- int8 activations (Q8) -----
 
 def pin_q8_hand_group(o):
