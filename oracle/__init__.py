@@ -18,6 +18,8 @@ Parity status per function (how each is pinned is listed in the tests):
   quantize_act_q8 / expert_ffn_q8 pinned: hand-worked groups (ties to even,
                                   all-zero, non-finite), |x - d p| <= d/2,
                                   the f64 block on the dequantised values
+  kv_write_rows /                 pinned: brute-force NumPy causal attention,
+  prefill_attention               causal-window probes, slot contents
   embed / output_head             pinned: rows of the pinned dequantisation,
                                   NaN rows out of range, dense NumPy product,
                                   one-hot column probes
@@ -95,6 +97,9 @@ def _declare(lib):
                                              _P, ctypes.c_int, _I64,
                                              _P, ctypes.c_int, _I64, _P, ctypes.c_int]),
         "orc_quantize_act_q8": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
+        "orc_kv_write_rows": (ctypes.c_int, [_P, _P, _I64, _I32, _I32, _P, _P, _P, _I64]),
+        "orc_prefill_attention": (ctypes.c_int, [_P, _I64, _I32, _I32, _I32, _P, _P, _I64, _P,
+                                                 ctypes.c_double, _P]),
         "orc_embed": (ctypes.c_int, [_P, _I64, _P, ctypes.c_int, _I64, _I64, _P]),
         "orc_output_head": (ctypes.c_int, [_P, _I64, _P, ctypes.c_int, _I64, _I64, _P]),
         "orc_rmsnorm": (ctypes.c_int, [_P, _I64, _I64, _P, ctypes.c_float, _P]),
@@ -258,6 +263,33 @@ class Oracle:
         out = np.empty_like(q)
         assert self.lib.orc_gqa_attention(_p(q), B, n_q, n_kv, D, _p(kc), _p(vc), S_max,
                                           _p(lengths), float(scale), _p(out)) == 0
+        return out
+
+    def kv_write_rows(self, k_new, v_new, pos, kcache, vcache):
+        """T rows of one sequence: k_new, v_new f32 [T, n_kv, D] into slots pos[t] of
+        copies of kcache / vcache (uint16 [n_kv, S_max, D]); returns them."""
+        k_new = _c(k_new, np.float32)
+        v_new = _c(v_new, np.float32)
+        pos = _c(pos, np.int32)
+        kc = _c(kcache, np.uint16).copy()
+        vc = _c(vcache, np.uint16).copy()
+        n_kv, S_max, D = kc.shape
+        assert self.lib.orc_kv_write_rows(_p(k_new), _p(v_new), k_new.shape[0], n_kv, D, _p(pos),
+                                          _p(kc), _p(vc), S_max) == 0
+        return kc, vc
+
+    def prefill_attention(self, q, kcache, vcache, pos, scale: float) -> np.ndarray:
+        """q f32 [T, n_q, D]; one sequence's caches uint16 [n_kv, S_max, D];
+        query t attends to positions 0..pos[t].  -> f32 [T, n_q, D]."""
+        q = _c(q, np.float32)
+        kc = _c(kcache, np.uint16)
+        vc = _c(vcache, np.uint16)
+        pos = _c(pos, np.int32)
+        T, n_q, D = q.shape
+        n_kv, S_max = kc.shape[0], kc.shape[1]
+        out = np.empty_like(q)
+        assert self.lib.orc_prefill_attention(_p(q), T, n_q, n_kv, D, _p(kc), _p(vc), S_max, _p(pos),
+                                              float(scale), _p(out)) == 0
         return out
 
     def _ffn_args(self, x, idx, w, gate, up, down, F, E):

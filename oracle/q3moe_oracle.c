@@ -376,6 +376,44 @@ int orc_expert_ffn(const float *x, int64_t T, int64_t H, int64_t F, int32_t E, i
     return rc;
 }
 
+/* The attention side of batched prefill (issue #3714, 0.70.3 gap list:
+ * prefill runs token by token; the fix batches the projections, the RoPE
+ * rows and the attention of the prompt).  T new tokens of ONE sequence sit
+ * at positions pos[t] of its caches [n_kv][S_max][D]:
+ *   - their k and v rows are written as the decode step writes one token's,
+ *     row t into slot pos[t];
+ *   - query t then attends to positions 0..pos[t] of the cache (causal), as
+ *     the decode attention of one token whose length is pos[t] + 1.
+ * So a prefill of T tokens equals T decode steps over the same cache. */
+int orc_kv_write(const float *k_new, const float *v_new, int64_t B, int32_t n_kv, int32_t D,
+                 const int32_t *pos, uint16_t *kcache, uint16_t *vcache, int64_t S_max);
+int orc_gqa_attention(const float *q, int64_t B, int32_t n_q, int32_t n_kv, int32_t D,
+                      const uint16_t *kcache, const uint16_t *vcache, int64_t S_max,
+                      const int32_t *len, double scale, float *out);
+
+int orc_kv_write_rows(const float *k_new, const float *v_new, int64_t T, int32_t n_kv, int32_t D,
+                      const int32_t *pos, uint16_t *kcache, uint16_t *vcache, int64_t S_max)
+{
+    for (int64_t t = 0; t < T; t++)
+        if (orc_kv_write(k_new + t * n_kv * (int64_t)D, v_new + t * n_kv * (int64_t)D, 1, n_kv, D,
+                         pos + t, kcache, vcache, S_max))
+            return -1;
+    return 0;
+}
+
+int orc_prefill_attention(const float *q, int64_t T, int32_t n_q, int32_t n_kv, int32_t D,
+                          const uint16_t *kcache, const uint16_t *vcache, int64_t S_max,
+                          const int32_t *pos, double scale, float *out)
+{
+    for (int64_t t = 0; t < T; t++) {
+        int32_t len = pos[t] + 1;
+        if (orc_gqa_attention(q + t * n_q * (int64_t)D, 1, n_q, n_kv, D, kcache, vcache, S_max, &len,
+                              scale, out + t * n_q * (int64_t)D))
+            return -1;
+    }
+    return 0;
+}
+
 /* Whole-model ends of the decode step (the token embedding and the output
  * head around the 48 layers; issue #3714 "File facts": the output matrix is
  * Q6_K; the embedding rows and the head rows are k-quant rows of H inputs).

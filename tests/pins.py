@@ -430,6 +430,80 @@ def pin_ffn_expert_stride(o):
 
 # --------------------------------------------------------- norm and RoPE -----
 
+# ------------------------------------------------------ prefill attention -----
+
+def _bf16_bits(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _bf16_vals(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def pin_prefill_attention_bruteforce(o):
+    """T = 7 queries of one sequence at positions 3..9 (GQA, 4 query heads
+    on 2 kv heads): each query attends to cache positions 0..pos[t]; against
+    a NumPy float64 softmax over that causal window."""
+    rng = np.random.default_rng(81)
+    T, nq, nkv, D, S = 7, 4, 2, 16, 12
+    q = rng.standard_normal((T, nq, D)).astype(np.float32)
+    kc = _bf16_bits(rng.standard_normal((nkv, S, D)))
+    vc = _bf16_bits(rng.standard_normal((nkv, S, D)))
+    pos = np.arange(3, 10, dtype=np.int32)
+    scale = 1.0 / math.sqrt(D)
+    got = o.prefill_attention(q, kc, vc, pos, scale)
+    K, Vv = _bf16_vals(kc), _bf16_vals(vc)
+    ref = np.empty((T, nq, D))
+    for t in range(T):
+        for h in range(nq):
+            g = h // (nq // nkv)
+            s_ = scale * (K[g, :pos[t] + 1] @ q[t, h].astype(np.float64))
+            p = np.exp(s_ - s_.max())
+            ref[t, h] = (p / p.sum()) @ Vv[g, :pos[t] + 1]
+    _close(got, ref.astype(np.float32), 1e-6, "prefill attention brute force")
+
+
+def pin_prefill_attention_causal_window(o):
+    """Changing cache rows after pos[t] leaves query t unchanged; changing
+    row pos[t] itself changes it; pos = 0 returns v at position 0 exactly."""
+    rng = np.random.default_rng(82)
+    nq, nkv, D, S = 2, 1, 8, 10
+    q = rng.standard_normal((3, nq, D)).astype(np.float32)
+    kc = _bf16_bits(rng.standard_normal((nkv, S, D)))
+    vc = _bf16_bits(rng.standard_normal((nkv, S, D)))
+    pos = np.array([0, 4, 6], np.int32)
+    base = o.prefill_attention(q, kc, vc, pos, 0.3)
+    kc2, vc2 = kc.copy(), vc.copy()
+    kc2[:, 7:] ^= 0x4000
+    vc2[:, 7:] ^= 0x4000
+    assert np.array_equal(o.prefill_attention(q, kc2, vc2, pos, 0.3), base)
+    vc3 = vc.copy()
+    vc3[:, 6] ^= 0x0100
+    after = o.prefill_attention(q, kc, vc3, pos, 0.3)
+    assert np.array_equal(after[:2], base[:2]) and not np.array_equal(after[2], base[2])
+    assert np.array_equal(base[0], np.broadcast_to(_bf16_vals(vc)[0, 0], (nq, D)).astype(np.float32))
+
+
+def pin_kv_write_rows(o):
+    """Row t of the new keys and values lands, rounded to bf16 (torch's
+    round to nearest even), in slot pos[t] of the one sequence's caches;
+    every other slot is untouched."""
+    rng = np.random.default_rng(83)
+    T, nkv, D, S = 3, 2, 8, 9
+    k = rng.standard_normal((T, nkv, D)).astype(np.float32)
+    v = rng.standard_normal((T, nkv, D)).astype(np.float32)
+    kc = np.arange(nkv * S * D, dtype=np.uint16).reshape(nkv, S, D)
+    vc = kc[::-1].copy()
+    pos = np.array([4, 0, 8], np.int32)
+    k2, v2 = o.kv_write_rows(k, v, pos, kc, vc)
+    for t in range(T):
+        assert np.array_equal(k2[:, pos[t]], _bf16_bits(k[t]))
+        assert np.array_equal(v2[:, pos[t]], _bf16_bits(v[t]))
+    keep = np.setdiff1d(np.arange(S), pos)
+    assert np.array_equal(k2[:, keep], kc[:, keep]) and np.array_equal(v2[:, keep], vc[:, keep])
+
+
 # ------------------------------------------------ embedding / output head -----
 
 def pin_embed_rows(o):

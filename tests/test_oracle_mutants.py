@@ -63,6 +63,8 @@ MUTANTS = [
     ("attention_scale_dropped", "sc[j] = scale * d;", "sc[j] = d;"),
     ("attention_one_past_length", "int64_t L = len[b];", "int64_t L = len[b] < S_max ? len[b] + 1 : len[b];"),
     ("attention_k_as_v", "acc += sc[j] * orc_bf16_to_double(V[j * D + i]);", "acc += sc[j] * orc_bf16_to_double(K[j * D + i]);"),
+    ("prefill_window_one_short", "int32_t len = pos[t] + 1;", "int32_t len = pos[t] > 0 ? pos[t] : 1;"),
+    ("prefill_rows_into_one_slot", "pos + t, kcache, vcache, S_max))", "pos, kcache, vcache, S_max))"),
     ("embed_row_off_by_one", "orc_dequant_row(qtype, table, v, H, row);", "orc_dequant_row(qtype, table, v > 0 ? v - 1 : v, H, row);"),
     ("embed_out_of_range_clamped", "for (int64_t i = 0; i < H; i++) out[t * H + i] = NAN;\n            continue;", "v = v < 0 ? 0 : V - 1;"),
     ("head_logit_transposed", "for (int64_t v = 0; v < V; v++) logits[t * V + v] = (float)y[v];", "for (int64_t v = 0; v < V; v++) logits[t * V + v] = (float)y[V - 1 - v];"),
