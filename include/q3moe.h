@@ -403,8 +403,10 @@ q3moe_status q3moe_rmsnorm(const float *x, int64_t T, int64_t n, const float *ga
 /* y[t][n] = (accumulate ? y[t][n] : 0) + sum_k W[n][k] * x[t][k].
  *   W [N x K] bf16 (raw bits, row-major), 16-byte aligned; x [T x K] f32,
  *   16-byte aligned; y [T x N] f32 (must not overlap W or x).
- * Products and sums are formed in f32 (each bf16 weight is exact in f32).
- * The weights are read once per 16 tokens.
+ * Up to 63 tokens: products and sums are formed in f32 (each bf16 weight is
+ * exact in f32), the weights read once per 16 tokens.  From 64 tokens on
+ * (and K % 32 == 0) a matrix-core GEMM: x enters as two bf16 pieces (x to
+ * 2^-17 relative), products exact, sums in f32.
  * Limits: K % 8 == 0, 8 <= K <= 2^30, 1 <= N <= 2^30, accumulate 0 or 1.
  * Errors: E_NULL, E_SHAPE, E_ALIGN, E_ALIAS, E_HIP. */
 q3moe_status q3moe_bf16_gemv(const uint16_t *W, int64_t N, int64_t K, const float *x, int64_t T,
@@ -420,6 +422,9 @@ q3moe_status q3moe_bf16_gemv(const uint16_t *W, int64_t N, int64_t K, const floa
  * to f32) on the way into the projections; products and sums as for
  * q3moe_bf16_gemv.  W0..W2, x and norm_gain 16-byte aligned; outputs 4-byte
  * aligned and overlapping no input or each other.
+ * Without the norm, 64 tokens or more take the matrix-core GEMM of
+ * q3moe_bf16_gemv, one launch per matrix; with it, the GEMV form (for a
+ * prompt, run q3moe_rmsnorm first and this call without the norm).
  * Limits: as q3moe_bf16_gemv for each matrix; with the norm, K <= 16384 and
  * eps >= 0 and finite.
  * Errors: E_NULL, E_SHAPE, E_ALIGN, E_ALIAS, E_HIP. */
@@ -440,6 +445,48 @@ q3moe_status q3moe_bf16_gemv3(const uint16_t *W0, int64_t N0, const uint16_t *W1
 q3moe_status q3moe_kv_write(const float *k_new, const float *v_new, int64_t B,
                             int32_t n_kv_heads, int32_t head_dim, const int32_t *positions,
                             uint16_t *k_cache, uint16_t *v_cache, int64_t S_max, void *stream);
+
+/* ------------------------------------------- prefill: the attention side --
+ * The prompt of one sequence, T tokens at once (aprender issue #3714, 0.70.3
+ * gap list: token-by-token prefill is the bottleneck; the fix batches the
+ * projections, the RoPE rows and the attention, head_dim 128).  A prefill
+ * step of a layer for positions pos[t]:
+ *   xn = rmsnorm(x)                         (q3moe_rmsnorm, T rows)
+ *   q, k, v = Wq xn, Wk xn, Wv xn           (q3moe_bf16_gemv / _gemv3; matrix cores for T >= 64)
+ *   QK-norm + RoPE at pos[t]                (q3moe_attn_prologue, T rows)
+ *   k, v -> cache slots pos[t]              (q3moe_kv_write_rows)
+ *   a = causal attention                    (q3moe_prefill_attention)
+ *   x += Wo a                               (q3moe_bf16_gemv, accumulate)
+ *   then the MoE block (q3moe_moe_ffn_prenorm; grouped prefill kernels for T >= 32).
+ *
+ * q3moe_kv_write_rows: row t of k_new and v_new ([T x n_kv x head_dim] f32),
+ * rounded to bf16 (nearest even), into slot positions[t] of ONE sequence's
+ * caches [n_kv x S_max x head_dim] (the decode write of one token, for T
+ * tokens; a position outside [0, S_max) writes nothing; two rows with one
+ * position leave either row).
+ * Limits: n_kv * head_dim <= 65536, S_max >= 1.
+ * Errors: E_NULL, E_SHAPE, E_ALIAS, E_HIP. */
+q3moe_status q3moe_kv_write_rows(const float *k_new, const float *v_new, int64_t T, int32_t n_kv,
+                                 int32_t head_dim, const int32_t *positions, uint16_t *k_cache,
+                                 uint16_t *v_cache, int64_t S_max, void *stream);
+
+/* Causal grouped-query attention of T queries of ONE sequence over its cache:
+ * query t (head h, kv head h / (n_q / n_kv)) attends to positions
+ * 0 .. positions[t] (its own row must already be in the cache), scores
+ * scale * q . k, softmax with the max subtracted, out = sum p v / sum p.  The
+ * same as q3moe_gqa_attention run for each token with length positions[t] + 1.
+ *   q [T x n_q x head_dim] f32, 16-byte aligned; caches [n_kv x S_max x
+ *   head_dim] bf16, 16-byte aligned; positions [T] int32 device array (any
+ *   order); out like q, 4-byte aligned.
+ * On the matrix cores: q and the probabilities enter as two bf16 pieces each
+ * (to 2^-17 relative), K and V as stored; sums, max and normaliser in f32.
+ * A position outside [0, S_max) gives NaN outputs for that token.
+ * Limits: head_dim = 128; n_q % n_kv == 0 and (n_q / n_kv) divides 64.
+ * Errors: E_NULL, E_SHAPE, E_ALIGN, E_ALIAS, E_HIP. */
+q3moe_status q3moe_prefill_attention(const float *q, int64_t T, int32_t n_q_heads, int32_t n_kv_heads,
+                                     int32_t head_dim, const uint16_t *k_cache, const uint16_t *v_cache,
+                                     int64_t S_max, const int32_t *positions, float scale, float *out,
+                                     void *stream);
 
 /* Grouped-query decode attention.  For sequence b and query head h, with
  * kv head g = h / (n_q_heads / n_kv_heads) and L = lengths[b]:

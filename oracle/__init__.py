@@ -431,6 +431,33 @@ class Oracle:
         return out, idx, w, kc, vc
 
 
+    def attention_prefill(self, x, wq, wk, wv, wo, in_norm, q_norm, k_norm, kcache, vcache, pos,
+                          n_q: int, n_kv: int, D: int, eps: float, rope_base: float):
+        """The attention half of a prefill step for T tokens of ONE sequence at
+        positions pos[t]: x + Wo attention(...), their k, v rows written into
+        copies of the caches (uint16 [n_kv, S_max, D]).  -> (x1, kcache, vcache)."""
+        T = x.shape[0]
+        xn = self.rmsnorm(x, in_norm, eps)
+        q = self.bf16_gemv(wq, xn).reshape(T, n_q, D)
+        kk = self.bf16_gemv(wk, xn).reshape(T, n_kv, D)
+        vv = self.bf16_gemv(wv, xn).reshape(T, n_kv, D)
+        q, kk = self.attn_prologue(q, kk, q_norm, k_norm, pos, eps, rope_base)
+        kc, vc = self.kv_write_rows(kk, vv, pos, kcache, vcache)
+        a = self.prefill_attention(q, kc, vc, pos, 1.0 / np.sqrt(D))
+        return self.bf16_gemv(wo, a.reshape(T, -1), x, accumulate=True), kc, vc
+
+    def decoder_layer_prefill(self, x, wq, wk, wv, wo, in_norm, post_norm, q_norm, k_norm, kcache,
+                              vcache, pos, n_q: int, n_kv: int, D: int, eps: float, rope_base: float,
+                              router, k: int, gate, up, down, F: int, E: int):
+        """A prefill step of the decoder layer: attention_prefill, then
+        x += MoE(RMSNorm(x)).  -> (x_out f32 [T, H], idx, w, kcache, vcache)."""
+        x1, kc, vc = self.attention_prefill(x, wq, wk, wv, wo, in_norm, q_norm, k_norm, kcache, vcache,
+                                            pos, n_q, n_kv, D, eps, rope_base)
+        out, idx, w, _ = self.moe_block(x1, router, k, gate, up, down, F, E,
+                                        norm_gain=post_norm, eps=eps, residual=True)
+        return out, idx, w, kc, vc
+
+
 _default = None
 
 

@@ -26,7 +26,7 @@ EXPORTS = (
     "q3moe_gqa_attention_workspace_bytes", "q3moe_gqa_attention",
     "q3moe_moe_ffn_workspace_bytes", "q3moe_moe_ffn", "q3moe_moe_ffn_prenorm", "q3moe_bf16_gemv3",
     "q3moe_attn_prologue_kv", "q3moe_persistent_path", "q3moe_moe_ffn_noalloc", "q3moe_moe_ffn_q8",
-    "q3moe_embed", "q3moe_output_head",
+    "q3moe_embed", "q3moe_output_head", "q3moe_kv_write_rows", "q3moe_prefill_attention",
 )
 
 
@@ -70,6 +70,8 @@ _SIGS = {
                                      _Experts, _Experts, _P, _P, _P, _I32, _P, ctypes.c_size_t,
                                      _P]),
     "q3moe_persistent_path": (_I32, [_I64, _I64, _I64, _I32, _I32, _I32, _I32]),
+    "q3moe_kv_write_rows": (_I32, [_P, _P, _I64, _I32, _I32, _P, _P, _P, _I64, _P]),
+    "q3moe_prefill_attention": (_I32, [_P, _I64, _I32, _I32, _I32, _P, _P, _I64, _P, _F, _P, _P]),
     "q3moe_embed": (_I32, [_P, _I64, _P, _I32, _I64, _I64, _P, _P]),
     "q3moe_output_head": (_I32, [_P, _I64, _P, _I32, _I64, _I64, _P, _P]),
     "q3moe_moe_ffn_q8": (_I32, [_P, _I64, _I64, _I64, _I32, _I32, _P, _Experts, _Experts, _Experts,
@@ -403,6 +405,44 @@ def q3moe_bf16_gemv3(Ws, x: torch.Tensor, norm_gain: Optional[torch.Tensor] = No
         Wp[0], Np[0], Wp[1], Np[1], Wp[2], Np[2], K, _ptr(x), T, _ptr(norm_gain), eps,
         yp[0], yp[1], yp[2], _stream(stream)))
     return outs
+
+
+def q3moe_kv_write_rows(k_new: torch.Tensor, v_new: torch.Tensor, positions: torch.Tensor,
+                        k_cache: torch.Tensor, v_cache: torch.Tensor, stream=None) -> None:
+    """Rows of k_new / v_new (f32 [T, n_kv, D]) into slots positions[t] of one
+    sequence's caches (bfloat16 [n_kv, S_max, D]), in place."""
+    _need(k_new, "k_new", torch.float32, 3)
+    _need(v_new, "v_new", torch.float32, 3)
+    _need(positions, "positions", torch.int32, 1)
+    _need(k_cache, "k_cache", torch.bfloat16, 3)
+    _need(v_cache, "v_cache", torch.bfloat16, 3)
+    T, nkv, D = k_new.shape
+    if v_new.shape != k_new.shape or k_cache.shape != v_cache.shape or k_cache.shape[0] != nkv \
+            or k_cache.shape[2] != D or positions.shape[0] != T:
+        raise ValueError("shape mismatch")
+    _check("q3moe_kv_write_rows", library().q3moe_kv_write_rows(
+        _ptr(k_new), _ptr(v_new), T, nkv, D, _ptr(positions), _ptr(k_cache), _ptr(v_cache),
+        k_cache.shape[1], _stream(stream)))
+
+
+def q3moe_prefill_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                            positions: torch.Tensor, scale: float, out: Optional[torch.Tensor] = None,
+                            stream=None) -> torch.Tensor:
+    """Causal attention of q (f32 [T, n_q, D]) over one sequence's caches
+    (bfloat16 [n_kv, S_max, D]); query t sees positions 0..positions[t]."""
+    _need(q, "q", torch.float32, 3)
+    _need(k_cache, "k_cache", torch.bfloat16, 3)
+    _need(v_cache, "v_cache", torch.bfloat16, 3)
+    _need(positions, "positions", torch.int32, 1)
+    T, nq, D = q.shape
+    nkv, S = k_cache.shape[0], k_cache.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.float32, 3)
+    _check("q3moe_prefill_attention", library().q3moe_prefill_attention(
+        _ptr(q), T, nq, nkv, D, _ptr(k_cache), _ptr(v_cache), S, _ptr(positions), scale, _ptr(out),
+        _stream(stream)))
+    return out
 
 
 def _table(W: torch.Tensor, name: str):

@@ -13,7 +13,7 @@ from pathlib import Path
 PKG = Path(__file__).resolve().parent
 CSRC = PKG / "csrc"
 LIB = PKG / "libq3moe.so"
-SOURCES = ["api.hip", "route.hip", "group.hip", "ffn.hip", "ffn_decode.hip", "prefill.hip", "norm.hip", "layer.hip", "model.hip", "noalloc.hip"]
+SOURCES = ["api.hip", "route.hip", "group.hip", "ffn.hip", "ffn_decode.hip", "prefill.hip", "norm.hip", "layer.hip", "model.hip", "attn_prefill.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 # Packed-FP32 instructions are disabled for all device code.

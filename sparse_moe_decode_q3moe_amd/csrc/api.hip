@@ -414,6 +414,49 @@ q3moe_status q3moe_kv_write(const float* k_new, const float* v_new, int64_t B, i
                                            v_cache, S_max, as_stream(stream)));
 }
 
+q3moe_status q3moe_kv_write_rows(const float* k_new, const float* v_new, int64_t T, int32_t n_kv,
+                                 int32_t head_dim, const int32_t* positions, uint16_t* k_cache,
+                                 uint16_t* v_cache, int64_t S_max, void* stream) {
+    if (T < 0 || T > 0x7fffffff || n_kv < 1 || head_dim < 1 || (int64_t)n_kv * head_dim > 65536 ||
+        S_max < 1)
+        return Q3MOE_E_SHAPE;
+    if (T == 0) return Q3MOE_OK;
+    if (!k_new || !v_new || !positions || !k_cache || !v_cache) return Q3MOE_E_NULL;
+    const size_t nc = (size_t)n_kv * (size_t)S_max * head_dim * 2;
+    const size_t nn = (size_t)T * n_kv * head_dim * sizeof(float);
+    if (overlaps(k_cache, nc, v_cache, nc) || overlaps(k_cache, nc, k_new, nn) ||
+        overlaps(k_cache, nc, v_new, nn) || overlaps(v_cache, nc, k_new, nn) ||
+        overlaps(v_cache, nc, v_new, nn) || overlaps(k_cache, nc, positions, (size_t)T * 4) ||
+        overlaps(v_cache, nc, positions, (size_t)T * 4))
+        return Q3MOE_E_ALIAS;
+    return from_hip(q3moe::launch_kv_write_rows(k_new, v_new, T, n_kv, head_dim, positions, k_cache,
+                                                v_cache, S_max, as_stream(stream)));
+}
+
+q3moe_status q3moe_prefill_attention(const float* q, int64_t T, int32_t n_q_heads, int32_t n_kv_heads,
+                                     int32_t head_dim, const uint16_t* k_cache, const uint16_t* v_cache,
+                                     int64_t S_max, const int32_t* positions, float scale, float* out,
+                                     void* stream) {
+    if (T < 0 || T > 0x7fffffff || n_q_heads < 1 || n_kv_heads < 1 || n_q_heads > 65535 ||
+        S_max < 1 || S_max > 0x7fffffff ||
+        !q3moe::prefill_attention_supported(n_q_heads, n_kv_heads, head_dim) || !(scale == scale) ||
+        scale == __builtin_inff() || scale == -__builtin_inff())
+        return Q3MOE_E_SHAPE;
+    if (T == 0) return Q3MOE_OK;
+    if (!q || !k_cache || !v_cache || !positions || !out) return Q3MOE_E_NULL;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
+        (reinterpret_cast<uintptr_t>(out) & 3u))
+        return Q3MOE_E_ALIGN;
+    const size_t nq = (size_t)T * n_q_heads * head_dim * sizeof(float);
+    const size_t nc = (size_t)n_kv_heads * (size_t)S_max * head_dim * 2;
+    if (overlaps(out, nq, q, nq) || overlaps(out, nq, k_cache, nc) || overlaps(out, nq, v_cache, nc) ||
+        overlaps(out, nq, positions, (size_t)T * 4))
+        return Q3MOE_E_ALIAS;
+    return from_hip(q3moe::launch_prefill_attention(q, T, n_q_heads, n_kv_heads, head_dim, k_cache,
+                                                    v_cache, S_max, positions, scale, out,
+                                                    as_stream(stream)));
+}
+
 size_t q3moe_gqa_attention_workspace_bytes(int64_t B, int32_t n_q_heads, int32_t n_kv_heads,
                                            int32_t head_dim, int64_t S_max) {
     if (B < 0 || n_q_heads < 1 || S_max < 1 || !q3moe::gqa_attention_supported(n_q_heads, n_kv_heads, head_dim))

@@ -1,0 +1,436 @@
+// The attention side of batched prefill (aprender issue #3714, 0.70.3 gap
+// list: prefill runs token by token; the fix batches the Q/K/V projections,
+// the RoPE rows and the attention of the prompt, head_dim 128).  Three
+// kernels; the per-row QK-norm + RoPE is attn_prologue_kernel (norm.hip),
+// which already takes T rows.
+//
+// bf16_gemm_kernel: Y[T x N] (+)= X[T x K] W[N x K]^T for the projections of
+//   many tokens, on the matrix cores.  W is bf16 (exact in the products); X
+//   is f32, split on its way into LDS into two bf16 pieces hi = bf16(x),
+//   lo = bf16(x - hi) (|x - hi - lo| <= 2^-17 |x|), so each product pair is
+//   exact and the sums run in f32.  Workgroup tile 128 tokens x 128 rows,
+//   k in stages of 32 staged through LDS one stage ahead (double buffer, one
+//   barrier per stage); each of the 4 waves owns 64 x 64 outputs as 4 x 4
+//   blocks of v_mfma_f32_16x16x32_bf16, two per block and stage (hi, lo).
+//
+// kv_rows_kernel: row t of the new keys and values, rounded to bf16, into
+//   slot pos[t] of one sequence's caches.
+//
+// prefill_attn_kernel: causal attention of T queries of one sequence over
+//   its cache (query t sees positions 0 .. pos[t]), GQA.  A workgroup of two
+//   waves takes 64 query rows = (64 / G tokens) x (the G query heads of one
+//   kv head); K and V stream through LDS in tiles of 64 positions (V
+//   transposed on the way in).  Per tile each wave forms S^T = K Q^T for its
+//   32 rows (K as the A operand, the query pieces, held in registers, as B),
+//   so a lane holds 16 scores of ONE query row and the row's online softmax
+//   needs two cross-lane steps; P = exp(S - m) (f32) is split into two bf16
+//   pieces and O += P V uses the same lane's 8 keys per 32-key step as its
+//   A operand (the k order inside a product does not matter), with the
+//   matching 8 rows of V^T as B.  O, the running max and the sum stay in
+//   f32; the output is O / sum.
+//
+// MFMA operand layouts (v_mfma_f32_16x16x32_bf16, as in prefill.hip): A lane
+// l holds row l % 16, k = 8 (l / 16) .. + 7; B lane l holds column l % 16 at
+// the same k; C lane l holds rows 4 (l / 16) + r (r = 0..3), column l % 16.
+#include "device_common.h"
+#include "internal.h"
+
+namespace q3moe {
+
+namespace {
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x4_t mfma32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// hi = bf16(x), lo = bf16(x - hi), both round to nearest even.
+__device__ __forceinline__ void split2(float x, uint32_t& hi, uint32_t& lo) {
+    hi = bf16_rne_bits(x);
+    lo = bf16_rne_bits(x - bf16_bits_to_float(hi));
+}
+
+// ----------------------------------------------------------------- GEMM --
+
+constexpr int kGmThreads = 256;
+constexpr int kGmBM = 128;                     // tokens per workgroup tile
+constexpr int kGmBN = 128;                     // rows (outputs) per workgroup tile
+constexpr int kGmBK = 32;                      // k per stage
+constexpr int kGmStride = kGmBK * 2 + 16;      // bytes per LDS row (80: 16 bytes of padding)
+constexpr int kGmArr = 128 * kGmStride;        // one [128][32] bf16 array
+constexpr int kGmBuf = 3 * kGmArr;             // A hi, A lo, B
+constexpr int kGmLds = 2 * kGmBuf;             // double buffer: 61,440 bytes
+
+// grid: (ceil(N / 128), ceil(T / 128)).  K % 32 == 0; x, W 16-byte aligned.
+__global__ __launch_bounds__(kGmThreads) void bf16_gemm_kernel(
+    const uint16_t* __restrict__ W, int64_t N, int64_t K, const float* __restrict__ x, int64_t T,
+    float* __restrict__ y, int accumulate) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t n0 = (int64_t)blockIdx.x * kGmBN, t0 = (int64_t)blockIdx.y * kGmBM;
+    const int tm = wave >> 1, tn = wave & 1;
+
+    // global -> registers: 4 float4 of X and 2 x 16 bytes of W per thread
+    float4 ax[4];
+    uint4 bw[2];
+    auto load = [&](int64_t k0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int f = tid + j * kGmThreads, tok = f >> 3, k4 = f & 7;
+            const int64_t t = t0 + tok < T ? t0 + tok : T - 1;
+            ax[j] = *reinterpret_cast<const float4*>(x + t * K + k0 + 4 * k4);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int f = tid + j * kGmThreads, row = f >> 2, k8 = f & 3;
+            const int64_t n = n0 + row < N ? n0 + row : N - 1;
+            bw[j] = *reinterpret_cast<const uint4*>(W + n * K + k0 + 8 * k8);
+        }
+    };
+    auto store = [&](uint8_t* buf) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int f = tid + j * kGmThreads, tok = f >> 3, k4 = f & 7;
+            const float v[4] = {ax[j].x, ax[j].y, ax[j].z, ax[j].w};
+            uint32_t h[4], l[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) split2(v[i], h[i], l[i]);
+            const int off = tok * kGmStride + 8 * k4;
+            *reinterpret_cast<uint2*>(buf + off) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+            *reinterpret_cast<uint2*>(buf + kGmArr + off) = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int f = tid + j * kGmThreads, row = f >> 2, k8 = f & 3;
+            *reinterpret_cast<uint4*>(buf + 2 * kGmArr + row * kGmStride + 16 * k8) = bw[j];
+        }
+    };
+
+    f32x4_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    const int stages = (int)(K / kGmBK);
+    load(0);
+    store(smem);
+    __syncthreads();
+    const int fr = lane & 15, fk = 16 * (lane >> 4);          // fragment row, byte offset of k
+    for (int s = 0; s < stages; ++s) {
+        uint8_t* cur = smem + (s & 1) * kGmBuf;
+        if (s + 1 < stages) load((int64_t)(s + 1) * kGmBK);
+        bf16x8_t bfr[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            bfr[j] = *reinterpret_cast<const bf16x8_t*>(cur + 2 * kGmArr + (64 * tn + 16 * j + fr) * kGmStride + fk);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int ro = (64 * tm + 16 * i + fr) * kGmStride + fk;
+            const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(cur + ro);
+            const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(cur + kGmArr + ro);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                acc[i][j] = mfma32(ah, bfr[j], acc[i][j]);
+                acc[i][j] = mfma32(al, bfr[j], acc[i][j]);
+            }
+        }
+        if (s + 1 < stages) store(smem + ((s + 1) & 1) * kGmBuf);
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t n = n0 + 64 * tn + 16 * j + fr;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t t = t0 + 64 * tm + 16 * i + 4 * (lane >> 4) + r;
+                if (t < T && n < N) {
+                    float* dst = y + t * N + n;
+                    *dst = accumulate ? *dst + acc[i][j][r] : acc[i][j][r];
+                }
+            }
+        }
+}
+
+// ---------------------------------------------------------------- KV rows --
+
+// grid: T workgroups of 256 threads; row t of k_new / v_new ([n_kv][D] f32)
+// into slot pos[t] of the caches [n_kv][S_max][D] (nothing for a position
+// outside [0, S_max)).
+__global__ __launch_bounds__(256) void kv_rows_kernel(const float* __restrict__ k_new,
+                                                      const float* __restrict__ v_new, int32_t nkv,
+                                                      int32_t D, const int32_t* __restrict__ pos,
+                                                      uint16_t* __restrict__ kc,
+                                                      uint16_t* __restrict__ vc, int64_t S_max) {
+    const int64_t t = blockIdx.x;
+    const int64_t p = pos[t];
+    if (p < 0 || p >= S_max) return;
+    const int n = nkv * D;
+    for (int i = threadIdx.x; i < n; i += 256) {
+        const int g = i / D, d = i % D;
+        const int64_t dst = ((int64_t)g * S_max + p) * D + d;
+        kc[dst] = float_to_bf16_rne(k_new[t * n + i]);
+        vc[dst] = float_to_bf16_rne(v_new[t * n + i]);
+    }
+}
+
+// ------------------------------------------------------- prefill attention --
+
+constexpr int kPaD = 128;                      // head_dim
+constexpr int kPaWaves = 2;
+constexpr int kPaRows = 32 * kPaWaves;         // query rows per workgroup
+constexpr int kPaKeys = 64;                    // positions per K/V tile
+constexpr int kPaKStride = kPaD * 2 + 16;      // K tile row: 272 bytes
+constexpr int kPaVStride = kPaKeys * 2 + 16;   // V^T tile row: 144 bytes
+constexpr int kPaKBytes = kPaKeys * kPaKStride;
+constexpr int kPaLds = kPaKBytes + kPaD * kPaVStride;   // 17,408 + 18,432
+
+// grid: (ceil(T / (64 / G)), n_kv); G = n_q / n_kv divides 64.  q [T][n_q][128]
+// f32 (16-byte aligned), caches [n_kv][S_max][128] bf16 of the one sequence,
+// out like q.
+__global__ __launch_bounds__(kPaWaves * 64) void prefill_attn_kernel(
+    const float* __restrict__ q, int64_t T, int32_t nq, int32_t G, const uint16_t* __restrict__ kc,
+    const uint16_t* __restrict__ vc, int64_t S_max, const int32_t* __restrict__ pos, float scale,
+    float* __restrict__ out) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    uint8_t* ks = smem;
+    uint8_t* vs = smem + kPaKBytes;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tpw = kPaRows / G;                                   // tokens per workgroup
+    // heavier tiles (later tokens) first
+    const int64_t tile = (int64_t)gridDim.x - 1 - blockIdx.x;
+    const int64_t t0 = tile * tpw;
+    const int g = blockIdx.y;
+    const uint16_t* K = kc + (int64_t)g * S_max * kPaD;
+    const uint16_t* V = vc + (int64_t)g * S_max * kPaD;
+
+    // the workgroup's key range: positions 0 .. (largest valid position) of its tokens
+    int64_t kmax = -1;
+    for (int i = 0; i < tpw; ++i) {
+        const int64_t t = t0 + i;
+        if (t < T) {
+            const int64_t p = pos[t];
+            if (p >= 0 && p < S_max && p > kmax) kmax = p;
+        }
+    }
+
+    // this lane's query row in each of its two row blocks, its position
+    // (-1 when invalid: no key passes the mask) and its query pieces
+    const int fr = lane & 15, fg = lane >> 4;
+    int64_t prow[2];
+    bf16x8_t qh[2][4], ql[2][4];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        const int row = 32 * wave + 16 * b + fr;
+        const int64_t t = t0 + row / G;
+        const int h = g * G + row % G;
+        const int64_t tc = t < T ? t : T - 1;
+        const int64_t p = t < T ? pos[tc] : -1;
+        prow[b] = p >= 0 && p < S_max ? p : -1;
+        const float* qr = q + (tc * nq + h) * kPaD;
+#pragma unroll
+        for (int ds = 0; ds < 4; ++ds) {
+            const float4 a = *reinterpret_cast<const float4*>(qr + 32 * ds + 8 * fg);
+            const float4 c = *reinterpret_cast<const float4*>(qr + 32 * ds + 8 * fg + 4);
+            const float v[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+            uint32_t hw[4], lw[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                uint32_t h0, l0, h1, l1;
+                split2(v[2 * i], h0, l0);
+                split2(v[2 * i + 1], h1, l1);
+                hw[i] = h0 | (h1 << 16);
+                lw[i] = l0 | (l1 << 16);
+            }
+            qh[b][ds] = __builtin_bit_cast(bf16x8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+            ql[b][ds] = __builtin_bit_cast(bf16x8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+        }
+    }
+
+    f32x4_t o[2][8];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[b][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m[2] = {-__builtin_inff(), -__builtin_inff()}, lsum[2] = {0.f, 0.f};
+
+    const int64_t ntiles = (kmax + kPaKeys) / kPaKeys;             // 0 when no valid row
+    for (int64_t it = 0; it < ntiles; ++it) {
+        const int64_t j0 = it * kPaKeys;
+        // stage the tile: 64 keys x 16 chunks for K and for V, 128 threads
+        __syncthreads();                                           // the previous tile is consumed
+        for (int c = tid; c < kPaKeys * 16; c += kPaWaves * 64) {
+            const int key = c >> 4, d8 = c & 15;
+            // rows past the workgroup's last position are never attended to:
+            // they enter as zeros, since a masked probability (0) times
+            // whatever such a row holds (NaN included) must contribute nothing
+            const bool live = j0 + key <= kmax;
+            const int64_t j = live ? j0 + key : 0;
+            const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+            const uint4 kv = live ? *reinterpret_cast<const uint4*>(K + j * kPaD + 8 * d8) : z;
+            const uint4 vv = live ? *reinterpret_cast<const uint4*>(V + j * kPaD + 8 * d8) : z;
+            *reinterpret_cast<uint4*>(ks + key * kPaKStride + 16 * d8) = kv;
+            const uint32_t w4[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                *reinterpret_cast<uint16_t*>(vs + (8 * d8 + 2 * i) * kPaVStride + 2 * key) = (uint16_t)(w4[i] & 0xffffu);
+                *reinterpret_cast<uint16_t*>(vs + (8 * d8 + 2 * i + 1) * kPaVStride + 2 * key) = (uint16_t)(w4[i] >> 16);
+            }
+        }
+        __syncthreads();
+        // S^T = K Q^T: s[b][kb] lane l holds keys 16 kb + 4 fg + r of query row fr of block b
+        f32x4_t s[2][4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            bf16x8_t kf[4];
+#pragma unroll
+            for (int ds = 0; ds < 4; ++ds)
+                kf[ds] = *reinterpret_cast<const bf16x8_t*>(ks + (16 * kb + fr) * kPaKStride + 64 * ds + 16 * fg);
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                f32x4_t a = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ds = 0; ds < 4; ++ds) {
+                    a = mfma32(kf[ds], qh[b][ds], a);
+                    a = mfma32(kf[ds], ql[b][ds], a);
+                }
+                s[b][kb] = a;
+            }
+        }
+        // online softmax per query row (the row's 64 scores sit in the 4
+        // lanes fr, fr + 16, fr + 32, fr + 48, 16 each)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            float tmax = -__builtin_inff();
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int64_t j = j0 + 16 * kb + 4 * fg + r;
+                    const float v = j <= prow[b] ? s[b][kb][r] * scale : -__builtin_inff();
+                    s[b][kb][r] = v;
+                    tmax = fmaxf(tmax, v);
+                }
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+            const float mnew = fmaxf(m[b], tmax);
+            const bool live = mnew > -__builtin_inff();
+            const float corr = live ? expf(m[b] - mnew) : 1.f;
+            float psum = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float p = live ? expf(s[b][kb][r] - mnew) : 0.f;
+                    s[b][kb][r] = p;
+                    psum += p;
+                }
+            psum += __shfl_xor(psum, 16, 64);
+            psum += __shfl_xor(psum, 32, 64);
+            lsum[b] = lsum[b] * corr + psum;
+            m[b] = mnew;
+            // rescale O: lane l holds rows 4 fg + r of the block, whose
+            // factor sits in lane (4 fg + r) (query row = lane % 16)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float cr = __shfl(corr, 4 * fg + r, 64);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) o[b][j][r] *= cr;
+            }
+        }
+        // O += P V: per 32-key step (blocks kb, kb + 1) this lane's 8 keys
+        // are 16 kb + 4 fg + r and 16 (kb + 1) + 4 fg + r
+#pragma unroll
+        for (int ks2 = 0; ks2 < 2; ++ks2) {
+            const int kb = 2 * ks2;
+            bf16x8_t ph[2], pl[2];
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                uint32_t hw[4], lw[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float p0 = i < 2 ? s[b][kb][2 * i] : s[b][kb + 1][2 * i - 4];
+                    const float p1 = i < 2 ? s[b][kb][2 * i + 1] : s[b][kb + 1][2 * i - 3];
+                    uint32_t h0, l0, h1, l1;
+                    split2(p0, h0, l0);
+                    split2(p1, h1, l1);
+                    hw[i] = h0 | (h1 << 16);
+                    lw[i] = l0 | (l1 << 16);
+                }
+                ph[b] = __builtin_bit_cast(bf16x8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+                pl[b] = __builtin_bit_cast(bf16x8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint8_t* vrow = vs + (16 * j + fr) * kPaVStride;
+                const uint2 va = *reinterpret_cast<const uint2*>(vrow + 2 * (16 * kb + 4 * fg));
+                const uint2 vb = *reinterpret_cast<const uint2*>(vrow + 2 * (16 * (kb + 1) + 4 * fg));
+                const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, make_uint4(va.x, va.y, vb.x, vb.y));
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+                    o[b][j] = mfma32(ph[b], vf, o[b][j]);
+                    o[b][j] = mfma32(pl[b], vf, o[b][j]);
+                }
+            }
+        }
+    }
+    // out = O / sum: lane l holds rows 4 fg + r of each block, column 16 j + fr
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int rl = 4 * fg + r;
+            const float den = __shfl(lsum[b], rl, 64);
+            const bool valid = __shfl((int)(prow[b] >= 0), rl, 64) != 0;
+            const int row = 32 * wave + 16 * b + rl;
+            const int64_t t = t0 + row / G;
+            const int h = g * G + row % G;
+            if (t < T) {
+                float* dst = out + (t * nq + h) * kPaD;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) dst[16 * j + fr] = valid ? o[b][j][r] / den : __builtin_nanf("");
+            }
+        }
+}
+
+}  // namespace
+
+bool gemm_path(int64_t T, int64_t K) { return T >= kGemmMinTokens && K % kGmBK == 0; }
+
+hipError_t launch_bf16_gemm(const uint16_t* W, int64_t N, int64_t K, const float* x, int64_t T,
+                            float* y, int accumulate, hipStream_t stream) {
+    dim3 grid((unsigned)((N + kGmBN - 1) / kGmBN), (unsigned)((T + kGmBM - 1) / kGmBM));
+    hipLaunchKernelGGL(bf16_gemm_kernel, grid, dim3(kGmThreads), kGmLds, stream, W, N, K, x, T, y,
+                       accumulate);
+    return hipGetLastError();
+}
+
+hipError_t launch_kv_write_rows(const float* k_new, const float* v_new, int64_t T, int32_t nkv,
+                                int32_t D, const int32_t* pos, uint16_t* kc, uint16_t* vc,
+                                int64_t S_max, hipStream_t stream) {
+    hipLaunchKernelGGL(kv_rows_kernel, dim3((unsigned)T), dim3(256), 0, stream, k_new, v_new, nkv, D,
+                       pos, kc, vc, S_max);
+    return hipGetLastError();
+}
+
+bool prefill_attention_supported(int32_t nq, int32_t nkv, int32_t D) {
+    return D == kPaD && nkv >= 1 && nq % nkv == 0 && kPaRows % (nq / nkv) == 0;
+}
+
+hipError_t launch_prefill_attention(const float* q, int64_t T, int32_t nq, int32_t nkv, int32_t D,
+                                    const uint16_t* kc, const uint16_t* vc, int64_t S_max,
+                                    const int32_t* pos, float scale, float* out, hipStream_t stream) {
+    (void)D;
+    const int G = nq / nkv;
+    const int tpw = kPaRows / G;
+    dim3 grid((unsigned)((T + tpw - 1) / tpw), (unsigned)nkv);
+    hipLaunchKernelGGL(prefill_attn_kernel, grid, dim3(kPaWaves * 64), kPaLds, stream, q, T, nq, G,
+                       kc, vc, S_max, pos, scale, out);
+    return hipGetLastError();
+}
+
+}  // namespace q3moe

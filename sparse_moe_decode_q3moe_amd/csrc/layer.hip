@@ -634,6 +634,7 @@ hipError_t launch_attn_d(const float* q, int64_t B, int32_t n_q, int32_t n_kv, c
 
 hipError_t launch_bf16_gemv(const uint16_t* W, int64_t N, int64_t K, const float* x, int64_t T,
                             float* y, int accumulate, hipStream_t stream) {
+    if (gemm_path(T, K)) return launch_bf16_gemm(W, N, K, x, T, y, accumulate, stream);
     GvJob job{W, nullptr, nullptr, y, nullptr, nullptr, N, 0, 0, 0, 0, nullptr, 0.f};
     return launch_gemv_job(job, K, x, T, accumulate, stream);
 }
@@ -642,6 +643,17 @@ hipError_t launch_bf16_gemv3(const uint16_t* W0, int64_t N0, const uint16_t* W1,
                              const uint16_t* W2, int64_t N2, int64_t K, const float* x, int64_t T,
                              const float* gain, float eps, float* y0, float* y1, float* y2,
                              hipStream_t stream) {
+    if (!gain && gemm_path(T, K)) {          // many tokens: one matrix-core GEMM per matrix
+        const uint16_t* Ws[3] = {W0, W1, W2};
+        float* ys[3] = {y0, y1, y2};
+        const int64_t Ns[3] = {N0, N1, N2};
+        for (int i = 0; i < 3; ++i) {
+            if (!Ns[i]) continue;
+            const hipError_t e = launch_bf16_gemm(Ws[i], Ns[i], K, x, T, ys[i], 0, stream);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
     GvJob job{W0, W1, W2, y0, y1, y2, N0, N1, N2, 0, 0, gain, eps};
     return launch_gemv_job(job, K, x, T, 0, stream);
 }
