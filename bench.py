@@ -61,6 +61,8 @@ def parse():
                     help="skip the full decoder-layer measurement (batch 1 and 16)")
     ap.add_argument("--no-stack", action="store_true",
                     help="skip the 48-layer stacked decode measurement")
+    ap.add_argument("--no-model", action="store_true",
+                    help="skip the whole-model decode measurement (embedding, 48 layers, head)")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="for hardware-counter runs: a few eager steps (no graph), then one "
                          "device-to-device copy of PMC_COPY_BYTES that calibrates the "
@@ -317,7 +319,12 @@ def main():
         result["decoder_layer"] = decoder_bench(torch, q3, gen, layers, experts, shape, dev, cpu,
                                                 status)
 
+    if not args.no_prefill:
+        result["prefill_layer_512"] = prefill_layer_bench(torch, q3, gen, layers, experts, shape, dev,
+                                                          cpu, status)
+
     if not args.no_stack:
+        stack_bench.skip_model = args.no_model
         result["stack_48"] = stack_bench(torch, q3, gen, shape, dev, cpu, status)
 
     if cpu is not None:
@@ -630,6 +637,124 @@ def decoder_bench(torch, q3, gen, layers, experts, shape, dev, cpu=None, status=
     return res
 
 
+def prefill_layer_bench(torch, q3, gen, layers, experts, shape, dev, cpu=None, status=None):
+    """A whole decoder layer over a 512-token prompt of one sequence: the
+    input RMSNorm, the Q/K/V projections (matrix-core GEMMs), QK-norm + RoPE
+    rows, the KV rows, causal attention, the O projection with the residual,
+    then the MoE block on the grouped prefill path.  From position 0 (a
+    fresh prompt) and as the last 512 tokens of a 4,096-token prompt (a
+    3,584-position prefix in the cache).  Attention layer copies and MoE
+    layer copies rotate.  Reported: time per step and per half, tokens/s,
+    and the GEMMs' and attention's matrix-core rates."""
+    s_ = gen.QWEN3_30B_A3B_ATTN
+    T, H, E, k, F = PREFILL_T, shape.H, shape.E, shape.k, shape.F
+    nq, nkv, D, S = s_.n_q, s_.n_kv, s_.D, s_.S_max
+    ncopies = 4
+    atts = [gen.attn_layer(s_, 900 + c, device=dev) for c in range(ncopies)]
+    caches = [tuple(c[0].contiguous() for c in gen.kv_caches(1, s_, 950 + c, device=dev))
+              for c in range(ncopies)]
+    x0 = gen.hidden_states(T, H, 12, device=dev)
+    x = torch.empty((T, H), device=dev)
+    xn = torch.empty((T, H), device=dev)
+    q = torch.empty((T, nq * D), device=dev)
+    kk = torch.empty((T, nkv * D), device=dev)
+    vv = torch.empty((T, nkv * D), device=dev)
+    ao = torch.empty((T, nq, D), device=dev)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    wts = torch.empty((T, k), device=dev)
+    ws_m = torch.zeros(q3.q3moe_moe_ffn_workspace_bytes(T, H, F, E, k), dtype=torch.uint8, device=dev)
+    res = {"tokens_per_step": T}
+    for name, start in (("from_position_0", 0), ("after_3584_prefix", S - T)):
+        pos = torch.arange(start, start + T, dtype=torch.int32, device=dev)
+
+        def attention(i, pos=pos):
+            A = atts[i % ncopies]
+            kc, vc = caches[i % ncopies]
+            q3.q3moe_rmsnorm(x, A.in_norm, s_.eps, out=xn)
+            q3.q3moe_bf16_gemv3([A.wq, A.wk, A.wv], xn, outs=[q, kk, vv])
+            q3.q3moe_attn_prologue(q.view(T, nq, D), kk.view(T, nkv, D), A.q_norm, A.k_norm, pos, s_.eps,
+                                   s_.rope_base)
+            q3.q3moe_kv_write_rows(kk.view(T, nkv, D), vv.view(T, nkv, D), pos, kc, vc)
+            q3.q3moe_prefill_attention(q.view(T, nq, D), kc, vc, pos, 1.0 / math.sqrt(D), out=ao)
+            q3.q3moe_bf16_gemv(A.wo, ao.view(T, nq * D), out=x, accumulate=True)
+
+        def layer(i):
+            x.copy_(x0)
+            attention(i)
+            L = layers[i % len(layers)]
+            q3.q3moe_moe_ffn_prenorm(x, atts[i % ncopies].post_norm, s_.eps, L.router, k,
+                                     *experts[i % len(experts)], F=F, out=x, accumulate=True,
+                                     topk_idx=idx, topk_w=wts, workspace=ws_m)
+
+        def gemms(i):
+            A = atts[i % ncopies]
+            q3.q3moe_bf16_gemv3([A.wq, A.wk, A.wv], xn, outs=[q, kk, vv])
+            q3.q3moe_bf16_gemv(A.wo, ao.view(T, nq * D), out=x, accumulate=True)
+
+        def attn_only(i, pos=pos):
+            kc, vc = caches[i % ncopies]
+            q3.q3moe_prefill_attention(q.view(T, nq, D), kc, vc, pos, 1.0 / math.sqrt(D), out=ao)
+
+        n = 8
+        times = {}
+        for fname, fn in (("layer", layer), ("attention_half", attention), ("gemms", gemms),
+                          ("attention_kernel", attn_only)):
+            x.copy_(x0)
+            for i in range(n):
+                fn(i)
+            torch.cuda.synchronize()
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                for i in range(n):
+                    fn(i)
+            gr.replay()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 4
+            a.record()
+            for _ in range(reps):
+                gr.replay()
+            b.record()
+            torch.cuda.synchronize()
+            times[fname] = a.elapsed_time(b) * 1000.0 / (reps * n)
+            del gr
+        gemm_flops = 2.0 * T * H * (nq * D + 2 * nkv * D) + 2.0 * T * (nq * D) * H
+        keys = sum(min(start + t + 1, S) for t in range(T))                 # attended positions
+        attn_flops = 4.0 * nq * D * keys
+        res[name] = {
+            "layer_us": round(times["layer"], 1),
+            "tokens_per_s": round(T / (times["layer"] * 1e-6), 1),
+            "attention_half_us": round(times["attention_half"], 1),
+            "gemms_us": round(times["gemms"], 1),
+            "gemm_tflops": round(gemm_flops / (times["gemms"] * 1e-6) / 1e12, 1),
+            "gemm_mfma_frac": round(gemm_flops / (times["gemms"] * 1e-6) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+            "attention_kernel_us": round(times["attention_kernel"], 1),
+            "attention_tflops": round(attn_flops / (times["attention_kernel"] * 1e-6) / 1e12, 1),
+            "attention_mfma_frac": round(attn_flops / (times["attention_kernel"] * 1e-6) / 1e12
+                                         / BF16_MFMA_PEAK_TFLOPS, 4),
+        }
+    res["note"] = ("flops are algorithmic; the matrix cores do twice that (activations and "
+                   "probabilities as two bf16 pieces)")
+    if status is not None:
+        status["prefill_layer_moe_workspace"] = q3.expert_ffn_status(ws_m, T, H, F, E, k)
+    if cpu is not None:                        # the oracle's attention half of one step
+        import numpy as np
+        A = atts[0]
+        kc, vc = caches[0]
+        bits = [gen.bf16_bits(t) for t in (A.wq, A.wk, A.wv, A.wo)]
+        xh = x0.cpu().numpy()
+        ph = np.arange(T, dtype=np.int32)
+        kh, vh = gen.bf16_bits(kc), gen.bf16_bits(vc)
+        _, t = cpu.timed(lambda: cpu.o.attention_prefill(
+            xh, *bits, A.in_norm.cpu().numpy(), A.q_norm.cpu().numpy(), A.k_norm.cpu().numpy(), kh, vh,
+            ph, nq, nkv, D, s_.eps, s_.rope_base))
+        cpu.configs["prefill_layer_512_attention_half"] = {"tokens_per_s": round(T / t, 2), "tokens": T,
+                                                           "oracle_s": round(t, 2)}
+    del atts, caches
+    torch.cuda.empty_cache()
+    return res
+
+
 STACK_LAYERS = 48
 STACK_TOKENS = 8
 
@@ -720,7 +845,120 @@ def stack_bench(torch, q3, gen, shape, dev, cpu=None, status=None):
                 "MoE block's kernel), updating x in place",
         "norm_as_own_launch_token_us": round(two_us, 2),
     }
+    if not getattr(stack_bench, "skip_model", False):
+        res["full_model_decode"] = full_model_bench(torch, q3, gen, shape, dev, stack, cpu, status)
     del stack
+    torch.cuda.empty_cache()
+    return res
+
+
+FULL_MODEL_TOKENS = 4
+
+
+def full_model_bench(torch, q3, gen, shape, dev, stack, cpu=None, status=None):
+    """A whole-model decode step of one sequence: the Q4_K embedding row of
+    the token, 48 decoder layers (input RMSNorm + Q/K/V in one launch, QK-norm
+    + RoPE + KV write in one launch, GQA attention over 4,096 cached
+    positions, O projection with the residual, then the MoE block of the
+    48-layer stack above with its post-attention RMSNorm inside), the final
+    RMSNorm and the Q6_K output head over the 151,936-row vocabulary.
+    Synthetic random weights, so the logits mean nothing; every byte a real
+    decode step reads is read.  Also times the model ends alone (embedding +
+    final norm + head) and reports the head's streaming rate."""
+    s_ = gen.QWEN3_30B_A3B_ATTN
+    H, E, k, F, V = shape.H, shape.E, shape.k, shape.F, gen.QWEN3_VOCAB
+    nq, nkv, D, S = s_.n_q, s_.n_kv, s_.D, s_.S_max
+    g = gen.make_generator(600, dev)
+    emb = gen.kquant_experts(gen.Q4_K, 1, V, H, g, dev)[0].contiguous()
+    head = gen.kquant_experts(gen.Q6_K, 1, V, H, g, dev)[0].contiguous()
+    final_norm = gen.uniform_f32((H,), 0.5, 1.5, gen.make_generator(601)).to(dev)
+    atts = [gen.attn_layer(s_, 700 + l, device=dev) for l in range(STACK_LAYERS)]
+    caches = [tuple(c[0].contiguous() for c in gen.kv_caches(1, s_, 800 + l, device=dev))
+              for l in range(STACK_LAYERS)]
+    toks = torch.tensor([17, 4242, 151000, 9], dtype=torch.int32, device=dev)
+    pos = torch.tensor([S - 1], dtype=torch.int32, device=dev)
+    lens = pos + 1
+    x = torch.empty((1, H), device=dev)
+    xn = torch.empty((1, H), device=dev)
+    q = torch.empty((1, nq * D), device=dev)
+    kk = torch.empty((1, nkv * D), device=dev)
+    vv = torch.empty((1, nkv * D), device=dev)
+    ao = torch.empty((1, nq, D), device=dev)
+    idx = torch.empty((1, k), dtype=torch.int32, device=dev)
+    wts = torch.empty((1, k), device=dev)
+    logits = torch.empty((FULL_MODEL_TOKENS, V), device=dev)
+    ws_a = torch.empty(q3.q3moe_gqa_attention_workspace_bytes(1, nq, nkv, D, S), dtype=torch.uint8, device=dev)
+    ws_m = torch.zeros(q3.q3moe_moe_ffn_workspace_bytes(1, H, F, E, k), dtype=torch.uint8, device=dev)
+
+    def ends(i):
+        q3.q3moe_embed(toks[i:i + 1], emb, gen.Q4_K, V, H, out=x)
+        q3.q3moe_rmsnorm(x, final_norm, s_.eps, out=xn)
+        q3.q3moe_output_head(xn, head, V, out=logits[i:i + 1])
+
+    def token(i):
+        q3.q3moe_embed(toks[i:i + 1], emb, gen.Q4_K, V, H, out=x)
+        for l in range(STACK_LAYERS):
+            A = atts[l]
+            kc, vc = caches[l]
+            router, g_, u_, d_, _ = stack[l]
+            q3.q3moe_bf16_gemv3([A.wq, A.wk, A.wv], x, norm_gain=A.in_norm, eps=s_.eps, outs=[q, kk, vv])
+            q3.q3moe_attn_prologue_kv(q.view(1, nq, D), kk.view(1, nkv, D), vv.view(1, nkv, D),
+                                      A.q_norm, A.k_norm, pos, s_.eps, s_.rope_base,
+                                      kc.view(1, nkv, S, D), vc.view(1, nkv, S, D))
+            q3.q3moe_gqa_attention(q.view(1, nq, D), kc.view(1, nkv, S, D), vc.view(1, nkv, S, D), lens,
+                                   1.0 / math.sqrt(D), out=ao, workspace=ws_a)
+            q3.q3moe_bf16_gemv(A.wo, ao.view(1, nq * D), out=x, accumulate=True)
+            q3.q3moe_moe_ffn_prenorm(x, A.post_norm, s_.eps, router, k, g_, u_, d_, F=F, out=x,
+                                     accumulate=True, topk_idx=idx, topk_w=wts, workspace=ws_m)
+        q3.q3moe_rmsnorm(x, final_norm, s_.eps, out=xn)
+        q3.q3moe_output_head(xn, head, V, out=logits[i:i + 1])
+
+    def timed(fn, reps):
+        for i in range(FULL_MODEL_TOKENS):
+            fn(i)
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for i in range(FULL_MODEL_TOKENS):
+                fn(i)
+        gr.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            gr.replay()
+        b.record()
+        torch.cuda.synchronize()
+        del gr
+        return a.elapsed_time(b) * 1000.0 / (reps * FULL_MODEL_TOKENS)
+
+    ends_us = timed(ends, 20)
+    tok_us = timed(token, 5)
+    head_bytes = V * (H // 256) * 210
+    emb_bytes = (H // 256) * 144
+    att_bytes = STACK_LAYERS * (2 * nq * D * H + 2 * nkv * D * H) * 2
+    kv_bytes = STACK_LAYERS * 2 * nkv * D * 2 * S
+    moe_bytes = sum(k * (2 * shape.gate_stride + L.down[0].numel()) + E * H * 4 for *_, L in stack)
+    tok_bytes = head_bytes + emb_bytes + att_bytes + kv_bytes + moe_bytes
+    if status is not None:
+        status["full_model_moe_workspace"] = q3.expert_ffn_status(ws_m, 1, H, F, E, k)
+    res = {
+        "note": "embedding + 48 x (attention over 4,096 cached positions + MoE block) + final "
+                "norm + Q6_K head over 151,936 rows, batch 1, one graph of 4 tokens",
+        "token_latency_us": round(tok_us, 1),
+        "tokens_per_s": round(1e6 / tok_us, 1),
+        "token_hbm_bytes": int(tok_bytes),
+        "hbm_gbps": round(tok_bytes / (tok_us * 1e-6) / 1e9, 1),
+        "hbm_frac": round(tok_bytes / (tok_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+        "logits_finite": bool(torch.isfinite(logits).all().item()),
+        "model_ends": {
+            "us_per_token": round(ends_us, 2),
+            "head_bytes": head_bytes,
+            "ends_hbm_gbps": round((head_bytes + emb_bytes) / (ends_us * 1e-6) / 1e9, 1),
+            "ends_hbm_frac": round((head_bytes + emb_bytes) / (ends_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+        },
+    }
+    del atts, caches, emb, head
     torch.cuda.empty_cache()
     return res
 

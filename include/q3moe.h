@@ -405,7 +405,7 @@ q3moe_status q3moe_rmsnorm(const float *x, int64_t T, int64_t n, const float *ga
  *   16-byte aligned; y [T x N] f32 (must not overlap W or x).
  * Up to 63 tokens: products and sums are formed in f32 (each bf16 weight is
  * exact in f32), the weights read once per 16 tokens.  From 64 tokens on
- * (and K % 32 == 0) a matrix-core GEMM: x enters as two bf16 pieces (x to
+ * (and K % 64 == 0) a matrix-core GEMM: x enters as two bf16 pieces (x to
  * 2^-17 relative), products exact, sums in f32.
  * Limits: K % 8 == 0, 8 <= K <= 2^30, 1 <= N <= 2^30, accumulate 0 or 1.
  * Errors: E_NULL, E_SHAPE, E_ALIGN, E_ALIAS, E_HIP. */
@@ -423,7 +423,7 @@ q3moe_status q3moe_bf16_gemv(const uint16_t *W, int64_t N, int64_t K, const floa
  * q3moe_bf16_gemv.  W0..W2, x and norm_gain 16-byte aligned; outputs 4-byte
  * aligned and overlapping no input or each other.
  * Without the norm, 64 tokens or more take the matrix-core GEMM of
- * q3moe_bf16_gemv, one launch per matrix; with it, the GEMV form (for a
+ * q3moe_bf16_gemv, all matrices in one launch; with it, the GEMV form (for a
  * prompt, run q3moe_rmsnorm first and this call without the norm).
  * Limits: as q3moe_bf16_gemv for each matrix; with the norm, K <= 16384 and
  * eps >= 0 and finite.

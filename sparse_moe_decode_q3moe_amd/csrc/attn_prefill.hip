@@ -8,10 +8,12 @@
 //   many tokens, on the matrix cores.  W is bf16 (exact in the products); X
 //   is f32, split on its way into LDS into two bf16 pieces hi = bf16(x),
 //   lo = bf16(x - hi) (|x - hi - lo| <= 2^-17 |x|), so each product pair is
-//   exact and the sums run in f32.  Workgroup tile 128 tokens x 128 rows,
-//   k in stages of 32 staged through LDS one stage ahead (double buffer, one
-//   barrier per stage); each of the 4 waves owns 64 x 64 outputs as 4 x 4
-//   blocks of v_mfma_f32_16x16x32_bf16, two per block and stage (hi, lo).
+//   exact and the sums run in f32.  Workgroup tile 64 tokens x 128 rows (64
+//   when that leaves the device short of workgroups), k in stages of 64
+//   staged through LDS one stage ahead (double buffer, one barrier per
+//   stage); each of the 4 waves owns 32 tokens x 64 (32) rows as blocks of
+//   v_mfma_f32_16x16x32_bf16, two per block and 32 k (hi, lo).  Up to three
+//   matrices on one input share one launch (the Q, K and V projections).
 //
 // kv_rows_kernel: row t of the new keys and values, rounded to bf16, into
 //   slot pos[t] of one sequence's caches.
@@ -41,6 +43,7 @@ namespace {
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4_t mfma32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -55,64 +58,87 @@ __device__ __forceinline__ void split2(float x, uint32_t& hi, uint32_t& lo) {
 // ----------------------------------------------------------------- GEMM --
 
 constexpr int kGmThreads = 256;
-constexpr int kGmBM = 128;                     // tokens per workgroup tile
-constexpr int kGmBN = 128;                     // rows (outputs) per workgroup tile
-constexpr int kGmBK = 32;                      // k per stage
-constexpr int kGmStride = kGmBK * 2 + 16;      // bytes per LDS row (80: 16 bytes of padding)
-constexpr int kGmArr = 128 * kGmStride;        // one [128][32] bf16 array
-constexpr int kGmBuf = 3 * kGmArr;             // A hi, A lo, B
-constexpr int kGmLds = 2 * kGmBuf;             // double buffer: 61,440 bytes
+constexpr int kGmBM = 64;                      // tokens per workgroup tile
+constexpr int kGmBK = 64;                      // k per stage
+constexpr int kGmStride = kGmBK * 2 + 16;      // bytes per LDS row (144: 16 bytes of padding)
+constexpr int kGmArrA = kGmBM * kGmStride;     // one [64][64] bf16 array
 
-// grid: (ceil(N / 128), ceil(T / 128)).  K % 32 == 0; x, W 16-byte aligned.
-__global__ __launch_bounds__(kGmThreads) void bf16_gemm_kernel(
-    const uint16_t* __restrict__ W, int64_t N, int64_t K, const float* __restrict__ x, int64_t T,
-    float* __restrict__ y, int accumulate) {
+template <int BN>
+struct GmGeom {
+    static constexpr int BUF = 2 * kGmArrA + BN * kGmStride;   // A hi, A lo, B
+    static constexpr int LDS = 2 * BUF;                         // double buffer
+    static constexpr int NB = BN / 32;                          // 16-row blocks per wave
+    static constexpr int BLOADS = BN / 32;                      // 16-byte W loads per thread and stage
+};
+
+// Up to three matrices on one input: workgroup x indexes the concatenated
+// row tiles of the matrices.
+struct GemmJob {
+    const uint16_t* W[3];
+    float* y[3];
+    int64_t N[3];
+    int tile_end[3];            // cumulative row-tile counts
+};
+
+// grid: (total row tiles, ceil(T / 64)).  K % 64 == 0; x, W 16-byte aligned.
+// Wave w owns tokens 32 (w / 2) .. + 31 and rows (BN / 2)(w % 2) .. of the tile.
+template <int BN>
+__global__ __launch_bounds__(kGmThreads) void bf16_gemm_kernel(GemmJob job, int64_t K,
+                                                               const float* __restrict__ x, int64_t T,
+                                                               int accumulate) {
+    using Gm = GmGeom<BN>;
     extern __shared__ __align__(16) uint8_t smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t n0 = (int64_t)blockIdx.x * kGmBN, t0 = (int64_t)blockIdx.y * kGmBM;
-    const int tm = wave >> 1, tn = wave & 1;
+    const int bx = blockIdx.x;
+    const int mi = bx < job.tile_end[0] ? 0 : bx < job.tile_end[1] ? 1 : 2;
+    const int tile = bx - (mi == 0 ? 0 : job.tile_end[mi - 1]);
+    const uint16_t* __restrict__ W = job.W[mi];
+    float* __restrict__ y = job.y[mi];
+    const int64_t N = job.N[mi];
+    const int64_t n0 = (int64_t)tile * BN, t0 = (int64_t)blockIdx.y * kGmBM;
+    const int wm = wave >> 1, wn = wave & 1;
 
-    // global -> registers: 4 float4 of X and 2 x 16 bytes of W per thread
     float4 ax[4];
-    uint4 bw[2];
+    uint4 bw[Gm::BLOADS];
     auto load = [&](int64_t k0) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int f = tid + j * kGmThreads, tok = f >> 3, k4 = f & 7;
+            const int f = tid + j * kGmThreads, tok = f >> 4, k4 = f & 15;
             const int64_t t = t0 + tok < T ? t0 + tok : T - 1;
             ax[j] = *reinterpret_cast<const float4*>(x + t * K + k0 + 4 * k4);
         }
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int f = tid + j * kGmThreads, row = f >> 2, k8 = f & 3;
+        for (int j = 0; j < Gm::BLOADS; ++j) {
+            const int f = tid + j * kGmThreads, row = f >> 3, k8 = f & 7;
             const int64_t n = n0 + row < N ? n0 + row : N - 1;
-            bw[j] = *reinterpret_cast<const uint4*>(W + n * K + k0 + 8 * k8);
+            const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(W + n * K + k0 + 8 * k8));
+            bw[j] = make_uint4(v.x, v.y, v.z, v.w);
         }
     };
     auto store = [&](uint8_t* buf) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int f = tid + j * kGmThreads, tok = f >> 3, k4 = f & 7;
+            const int f = tid + j * kGmThreads, tok = f >> 4, k4 = f & 15;
             const float v[4] = {ax[j].x, ax[j].y, ax[j].z, ax[j].w};
             uint32_t h[4], l[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) split2(v[i], h[i], l[i]);
             const int off = tok * kGmStride + 8 * k4;
             *reinterpret_cast<uint2*>(buf + off) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-            *reinterpret_cast<uint2*>(buf + kGmArr + off) = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
+            *reinterpret_cast<uint2*>(buf + kGmArrA + off) = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
         }
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int f = tid + j * kGmThreads, row = f >> 2, k8 = f & 3;
-            *reinterpret_cast<uint4*>(buf + 2 * kGmArr + row * kGmStride + 16 * k8) = bw[j];
+        for (int j = 0; j < Gm::BLOADS; ++j) {
+            const int f = tid + j * kGmThreads, row = f >> 3, k8 = f & 7;
+            *reinterpret_cast<uint4*>(buf + 2 * kGmArrA + row * kGmStride + 16 * k8) = bw[j];
         }
     };
 
-    f32x4_t acc[4][4];
+    f32x4_t acc[2][Gm::NB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < Gm::NB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     const int stages = (int)(K / kGmBK);
     load(0);
@@ -120,34 +146,38 @@ __global__ __launch_bounds__(kGmThreads) void bf16_gemm_kernel(
     __syncthreads();
     const int fr = lane & 15, fk = 16 * (lane >> 4);          // fragment row, byte offset of k
     for (int s = 0; s < stages; ++s) {
-        uint8_t* cur = smem + (s & 1) * kGmBuf;
+        const uint8_t* cur = smem + (s & 1) * Gm::BUF;
         if (s + 1 < stages) load((int64_t)(s + 1) * kGmBK);
-        bf16x8_t bfr[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            bfr[j] = *reinterpret_cast<const bf16x8_t*>(cur + 2 * kGmArr + (64 * tn + 16 * j + fr) * kGmStride + fk);
+        for (int kk = 0; kk < kGmBK / 32; ++kk) {
+            bf16x8_t bfr[Gm::NB];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int ro = (64 * tm + 16 * i + fr) * kGmStride + fk;
-            const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(cur + ro);
-            const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(cur + kGmArr + ro);
+            for (int j = 0; j < Gm::NB; ++j)
+                bfr[j] = *reinterpret_cast<const bf16x8_t*>(
+                    cur + 2 * kGmArrA + ((BN / 2) * wn + 16 * j + fr) * kGmStride + 64 * kk + fk);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                acc[i][j] = mfma32(ah, bfr[j], acc[i][j]);
-                acc[i][j] = mfma32(al, bfr[j], acc[i][j]);
+            for (int i = 0; i < 2; ++i) {
+                const int ro = (32 * wm + 16 * i + fr) * kGmStride + 64 * kk + fk;
+                const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(cur + ro);
+                const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(cur + kGmArrA + ro);
+#pragma unroll
+                for (int j = 0; j < Gm::NB; ++j) {
+                    acc[i][j] = mfma32(ah, bfr[j], acc[i][j]);
+                    acc[i][j] = mfma32(al, bfr[j], acc[i][j]);
+                }
             }
         }
-        if (s + 1 < stages) store(smem + ((s + 1) & 1) * kGmBuf);
+        if (s + 1 < stages) store(smem + ((s + 1) & 1) * Gm::BUF);
         __syncthreads();
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t n = n0 + 64 * tn + 16 * j + fr;
+        for (int j = 0; j < Gm::NB; ++j) {
+            const int64_t n = n0 + (BN / 2) * wn + 16 * j + fr;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int64_t t = t0 + 64 * tm + 16 * i + 4 * (lane >> 4) + r;
+                const int64_t t = t0 + 32 * wm + 16 * i + 4 * (lane >> 4) + r;
                 if (t < T && n < N) {
                     float* dst = y + t * N + n;
                     *dst = accumulate ? *dst + acc[i][j][r] : acc[i][j][r];
@@ -259,6 +289,7 @@ __global__ __launch_bounds__(kPaWaves * 64) void prefill_attn_kernel(
     float m[2] = {-__builtin_inff(), -__builtin_inff()}, lsum[2] = {0.f, 0.f};
 
     const int64_t ntiles = (kmax + kPaKeys) / kPaKeys;             // 0 when no valid row
+    const float scale2 = scale * 1.4426950408889634f;
     for (int64_t it = 0; it < ntiles; ++it) {
         const int64_t j0 = it * kPaKeys;
         // stage the tile: 64 keys x 16 chunks for K and for V, 128 threads
@@ -305,13 +336,14 @@ __global__ __launch_bounds__(kPaWaves * 64) void prefill_attn_kernel(
         // lanes fr, fr + 16, fr + 32, fr + 48, 16 each)
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
+            // scores in base-2 units: exp(scale s - m) = 2^(scale log2(e) s - m')
             float tmax = -__builtin_inff();
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int64_t j = j0 + 16 * kb + 4 * fg + r;
-                    const float v = j <= prow[b] ? s[b][kb][r] * scale : -__builtin_inff();
+                    const float v = j <= prow[b] ? s[b][kb][r] * scale2 : -__builtin_inff();
                     s[b][kb][r] = v;
                     tmax = fmaxf(tmax, v);
                 }
@@ -319,13 +351,13 @@ __global__ __launch_bounds__(kPaWaves * 64) void prefill_attn_kernel(
             tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
             const float mnew = fmaxf(m[b], tmax);
             const bool live = mnew > -__builtin_inff();
-            const float corr = live ? expf(m[b] - mnew) : 1.f;
+            const float corr = live ? exp2f(m[b] - mnew) : 1.f;
             float psum = 0.f;
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float p = live ? expf(s[b][kb][r] - mnew) : 0.f;
+                    const float p = live ? exp2f(s[b][kb][r] - mnew) : 0.f;
                     s[b][kb][r] = p;
                     psum += p;
                 }
@@ -401,12 +433,39 @@ __global__ __launch_bounds__(kPaWaves * 64) void prefill_attn_kernel(
 
 bool gemm_path(int64_t T, int64_t K) { return T >= kGemmMinTokens && K % kGmBK == 0; }
 
+hipError_t launch_bf16_gemm_multi(const uint16_t* const* Ws, float* const* ys, const int64_t* Ns, int nmat,
+                                  int64_t K, const float* x, int64_t T, int accumulate,
+                                  hipStream_t stream) {
+    // 128-row tiles unless that leaves the device short of workgroups
+    int64_t t128 = 0;
+    for (int i = 0; i < nmat; ++i) t128 += (Ns[i] + 127) / 128;
+    const int64_t ttiles = (T + kGmBM - 1) / kGmBM;
+    const bool wide = t128 * ttiles >= 256;
+    const int BN = wide ? 128 : 64;
+    GemmJob job{};
+    int acc_tiles = 0;
+    for (int i = 0; i < 3; ++i) {
+        if (i < nmat) {
+            job.W[i] = Ws[i];
+            job.y[i] = ys[i];
+            job.N[i] = Ns[i];
+            acc_tiles += (int)((Ns[i] + BN - 1) / BN);
+        }
+        job.tile_end[i] = acc_tiles;
+    }
+    dim3 grid((unsigned)acc_tiles, (unsigned)ttiles);
+    if (wide)
+        hipLaunchKernelGGL(bf16_gemm_kernel<128>, grid, dim3(kGmThreads), GmGeom<128>::LDS, stream, job,
+                           K, x, T, accumulate);
+    else
+        hipLaunchKernelGGL(bf16_gemm_kernel<64>, grid, dim3(kGmThreads), GmGeom<64>::LDS, stream, job,
+                           K, x, T, accumulate);
+    return hipGetLastError();
+}
+
 hipError_t launch_bf16_gemm(const uint16_t* W, int64_t N, int64_t K, const float* x, int64_t T,
                             float* y, int accumulate, hipStream_t stream) {
-    dim3 grid((unsigned)((N + kGmBN - 1) / kGmBN), (unsigned)((T + kGmBM - 1) / kGmBM));
-    hipLaunchKernelGGL(bf16_gemm_kernel, grid, dim3(kGmThreads), kGmLds, stream, W, N, K, x, T, y,
-                       accumulate);
-    return hipGetLastError();
+    return launch_bf16_gemm_multi(&W, &y, &N, 1, K, x, T, accumulate, stream);
 }
 
 hipError_t launch_kv_write_rows(const float* k_new, const float* v_new, int64_t T, int32_t nkv,

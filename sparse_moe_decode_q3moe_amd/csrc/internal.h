@@ -133,12 +133,15 @@ hipError_t launch_gqa_attention(const float* q, int64_t B, int32_t n_q, int32_t 
                                 hipStream_t stream);
 
 // attn_prefill.hip: the attention side of batched prefill.  launch_bf16_gemm
-// serves q3moe_bf16_gemv for T >= kGemmMinTokens (K % 32 == 0) on the
+// serves q3moe_bf16_gemv for T >= kGemmMinTokens (K % 64 == 0) on the
 // matrix cores.
 constexpr int64_t kGemmMinTokens = 64;
 bool gemm_path(int64_t T, int64_t K);
 hipError_t launch_bf16_gemm(const uint16_t* W, int64_t N, int64_t K, const float* x, int64_t T,
                             float* y, int accumulate, hipStream_t stream);
+hipError_t launch_bf16_gemm_multi(const uint16_t* const* Ws, float* const* ys, const int64_t* Ns,
+                                  int nmat, int64_t K, const float* x, int64_t T, int accumulate,
+                                  hipStream_t stream);
 hipError_t launch_kv_write_rows(const float* k_new, const float* v_new, int64_t T, int32_t nkv,
                                 int32_t D, const int32_t* pos, uint16_t* kc, uint16_t* vc,
                                 int64_t S_max, hipStream_t stream);

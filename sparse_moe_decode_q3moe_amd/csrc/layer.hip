@@ -643,16 +643,21 @@ hipError_t launch_bf16_gemv3(const uint16_t* W0, int64_t N0, const uint16_t* W1,
                              const uint16_t* W2, int64_t N2, int64_t K, const float* x, int64_t T,
                              const float* gain, float eps, float* y0, float* y1, float* y2,
                              hipStream_t stream) {
-    if (!gain && gemm_path(T, K)) {          // many tokens: one matrix-core GEMM per matrix
-        const uint16_t* Ws[3] = {W0, W1, W2};
-        float* ys[3] = {y0, y1, y2};
-        const int64_t Ns[3] = {N0, N1, N2};
-        for (int i = 0; i < 3; ++i) {
-            if (!Ns[i]) continue;
-            const hipError_t e = launch_bf16_gemm(Ws[i], Ns[i], K, x, T, ys[i], 0, stream);
-            if (e != hipSuccess) return e;
-        }
-        return hipSuccess;
+    if (!gain && gemm_path(T, K)) {          // many tokens: one matrix-core GEMM launch
+        const uint16_t* Ws[3];
+        float* ys[3];
+        int64_t Ns[3];
+        int n = 0;
+        const uint16_t* W_in[3] = {W0, W1, W2};
+        float* y_in[3] = {y0, y1, y2};
+        const int64_t N_in[3] = {N0, N1, N2};
+        for (int i = 0; i < 3; ++i)
+            if (N_in[i]) {
+                Ws[n] = W_in[i];
+                ys[n] = y_in[i];
+                Ns[n++] = N_in[i];
+            }
+        return launch_bf16_gemm_multi(Ws, ys, Ns, n, K, x, T, 0, stream);
     }
     GvJob job{W0, W1, W2, y0, y1, y2, N0, N1, N2, 0, 0, gain, eps};
     return launch_gemv_job(job, K, x, T, 0, stream);
