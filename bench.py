@@ -63,6 +63,9 @@ def parse():
                     help="skip the 48-layer stacked decode measurement")
     ap.add_argument("--no-model", action="store_true",
                     help="skip the whole-model decode measurement (embedding, 48 layers, head)")
+    ap.add_argument("--prefill-pmc", action="store_true",
+                    help="for hardware-counter runs of the 512-token prefill FFN: a few eager "
+                         "steps of route + expert FFN on one layer copy, then one line; no timing")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="for hardware-counter runs: a few eager steps (no graph), then one "
                          "device-to-device copy of PMC_COPY_BYTES that calibrates the "
@@ -118,6 +121,16 @@ def main():
     torch.cuda.set_device(dev)
     shape = gen.QWEN3_30B_A3B
     H, E, k, F = shape.H, shape.E, shape.k, shape.F
+
+    if args.prefill_pmc:
+        L = gen.moe_layer(shape, 100, device=dev)
+        ex = (q3.Experts(L.gate, gen.Q4_K), q3.Experts(L.up, gen.Q4_K), q3.Experts(L.down, shape.down_qtype))
+        xp = gen.hidden_states(PREFILL_T, H, 8, device=dev)
+        for _ in range(PMC_STEPS // 4):
+            q3.q3moe_moe_ffn(xp, L.router, k, *ex, F=F)
+        torch.cuda.synchronize()
+        print(json.dumps({"prefill_pmc": True, "tokens": PREFILL_T, "steps": PMC_STEPS // 4}), flush=True)
+        return
 
     layers = [gen.moe_layer(shape, 100 + l, device=dev) for l in range(N_LAYER_COPIES)]
     xs = gen.hidden_states(GRAPH_STEPS, H, 7, device=dev).view(GRAPH_STEPS, 1, H).contiguous()

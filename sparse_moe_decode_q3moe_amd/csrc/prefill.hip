@@ -401,8 +401,13 @@ __host__ __device__ inline int pf_down_wbytes(int64_t F, int32_t qtype) {
 __host__ __device__ inline int pf_down_hoff(int64_t F, int32_t qtype) {
     return (pf_down_wbytes(F, qtype) + 16 + 15) & ~15;       // + padding for the unaligned Q6_K reads
 }
+// h rows in LDS: 264 bytes (66 dwords), so the 8-byte operand reads of the
+// 16 rows of a block land on 16 distinct bank pairs (a 272-byte row put rows
+// r and r + 8 on the same banks)
+constexpr int kDnRowB = kStageK * 2 + 8;                      // 264
+constexpr int kDnPieceB = kPfRows * kDnRowB;                  // 16896
 __host__ __device__ inline int pf_down_lds(int64_t F, int32_t qtype) {
-    return pf_down_hoff(F, qtype) + 2 * kXPieceB + 8 * kPfRows * 4;
+    return pf_down_hoff(F, qtype) + 2 * kDnPieceB + 8 * kPfRows * 4;
 }
 
 __global__ __launch_bounds__(kDnThreads) void pf_down_kernel(
@@ -426,7 +431,7 @@ __global__ __launch_bounds__(kDnThreads) void pf_down_kernel(
     const int rowb = nb * bb;
     const int wbytes = kDnOut * rowb;                         // a multiple of 16
     const int hoff = pf_down_hoff(F, qtype);
-    const int soff = hoff + 2 * kXPieceB;
+    const int soff = hoff + 2 * kDnPieceB;
     const int nst = (int)(F / kStageK);
 
     // staging roles: the weight tile (n16 pieces of 16 B over 512 threads,
@@ -463,7 +468,9 @@ __global__ __launch_bounds__(kDnThreads) void pf_down_kernel(
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int r = (u & 1) ? rb2 : ra;
-            *reinterpret_cast<uint4*>(smem + hoff + (u >> 1) * kXPieceB + r * kXRowB + hc * 16) = rx[u];
+            uint8_t* d = smem + hoff + (u >> 1) * kDnPieceB + r * kDnRowB + hc * 16;   // 8-byte aligned
+            *reinterpret_cast<uint2*>(d) = make_uint2(rx[u].x, rx[u].y);
+            *reinterpret_cast<uint2*>(d + 8) = make_uint2(rx[u].z, rx[u].w);
         }
         reinterpret_cast<float*>(smem + soff)[sgrp * kPfRows + srow] = rs;
     };
@@ -520,9 +527,9 @@ __global__ __launch_bounds__(kDnThreads) void pf_down_kernel(
             for (int i = 0; i < 2; ++i) {
                 const int tb = tb0 + 2 * i;
                 if (16 * tb >= nrows) continue;               // no pairs in this token block
-                const int xo = hoff + (16 * tb + col) * kXRowB + (16 * G + 4 * g) * 2;
+                const int xo = hoff + (16 * tb + col) * kDnRowB + (16 * G + 4 * g) * 2;
                 f32x4_t t = pf_mfma(*reinterpret_cast<const s16x4_t*>(smem + xo), bw, f32x4_t{0.f, 0.f, 0.f, 0.f});
-                t = pf_mfma(*reinterpret_cast<const s16x4_t*>(smem + kXPieceB + xo), bw, t);
+                t = pf_mfma(*reinterpret_cast<const s16x4_t*>(smem + kDnPieceB + xo), bw, t);
                 acc[i][0] += sc * t[0];
                 acc[i][1] += sc * t[1];
                 acc[i][2] += sc * t[2];
