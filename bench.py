@@ -777,9 +777,12 @@ def stack_bench(torch, q3, gen, shape, dev, cpu=None, status=None):
     layers 0-23 and Q4_K in 24-47 (17.55 GB of seeded expert weights
     resident in HBM, far beyond the 256 MB Infinity Cache, so nothing is
     rotated).  Between layers the residual stream is x <- x + MoE(RMSNorm(x))
-    with unit gain and eps 1e-6: per layer one q3moe_moe_ffn_prenorm call
-    (norm, routing and expert FFN in one kernel, updating x in place); the
-    same stack with the norm as its own launch is timed beside it.  A token starts from
+    with unit gain and eps 1e-6: the whole stack as one q3moe_moe_stack call
+    (one persistent launch for all 48 layers: norm, routing and expert FFN of
+    every layer, the residual stream handed from layer to layer inside the
+    kernel); beside it the same stack as 48 q3moe_moe_ffn_prenorm calls (one
+    launch per layer, x updated in place), and as 96 launches with the norm
+    as its own launch.  A token starts from
     its own seeded hidden vector and passes through all 48 layers; the graph
     holds STACK_TOKENS such tokens.  Reported: per-token latency, tokens/s,
     and the algorithmic HBM bytes per token (router + the 8 selected
@@ -800,6 +803,16 @@ def stack_bench(torch, q3, gen, shape, dev, cpu=None, status=None):
     idx = torch.empty((1, k), dtype=torch.int32, device=dev)
     wts = torch.empty((1, k), dtype=torch.float32, device=dev)
     ws = torch.zeros(q3.q3moe_moe_ffn_workspace_bytes(1, H, F, E, k), dtype=torch.uint8, device=dev)
+    ws_stack = torch.zeros(q3.q3moe_moe_stack_workspace_bytes(1, H, F, E, k), dtype=torch.uint8,
+                           device=dev)
+    stack_layers = [q3.MoeLayer(ones, router, g_, u_, d_) for router, g_, u_, d_, _ in stack]
+    idx_all = torch.empty((STACK_LAYERS, 1, k), dtype=torch.int32, device=dev)
+    w_all = torch.empty((STACK_LAYERS, 1, k), dtype=torch.float32, device=dev)
+
+    def token_stack(i):                            # the whole stack in one call
+        x.copy_(x0[i])
+        q3.q3moe_moe_stack(x, stack_layers, k, F, EPS, topk_idx=idx_all, topk_w=w_all,
+                           workspace=ws_stack)
 
     def token(i):                                  # one call per layer, in place on x
         x.copy_(x0[i])
@@ -835,12 +848,14 @@ def stack_bench(torch, q3, gen, shape, dev, cpu=None, status=None):
         return a.elapsed_time(b) * 1000.0 / (reps * STACK_TOKENS)
 
     two_us = time_tokens(token_two_calls)
-    tok_us = time_tokens(token)
+    per_layer_us = time_tokens(token)
+    tok_us = time_tokens(token_stack)
     finite = bool(torch.isfinite(x).all().item())
     if status is not None:
         status["stack_48_workspace"] = q3.expert_ffn_status(ws, 1, H, F, E, k)
+        status["stack_48_one_launch_workspace"] = q3.expert_ffn_status(ws_stack, 1, H, F, E, k)
     if cpu is not None:
-        stack_oracle(torch, q3, gen, shape, cpu, stack, x0, x, ones, idx, wts, ws, EPS)
+        stack_oracle(torch, q3, gen, shape, cpu, stack, x0, x, token_stack, idx_all, EPS)
     expert_bytes = sum(k * (2 * shape.gate_stride + L.down[0].numel()) for *_, L in stack)
     tok_bytes = expert_bytes + STACK_LAYERS * (E * H * 4 + 3 * H * 4 * 2)
     res = {
@@ -854,8 +869,9 @@ def stack_bench(torch, q3, gen, shape, dev, cpu=None, status=None):
         "hbm_gbps": round(tok_bytes / (tok_us * 1e-6) / 1e9, 1),
         "hbm_frac": round(tok_bytes / (tok_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
         "output_finite": finite,
-        "note": "per layer one q3moe_moe_ffn_prenorm call (RMSNorm with unit gain inside the "
-                "MoE block's kernel), updating x in place",
+        "note": "one q3moe_moe_stack call per token: all 48 layers (RMSNorm with unit gain, "
+                "routing, expert FFN, residual) in one persistent launch",
+        "per_layer_calls_token_us": round(per_layer_us, 2),
         "norm_as_own_launch_token_us": round(two_us, 2),
     }
     if not getattr(stack_bench, "skip_model", False):
@@ -979,22 +995,20 @@ def full_model_bench(torch, q3, gen, shape, dev, stack, cpu=None, status=None):
 STACK_ORACLE_TOKENS = 2
 
 
-def stack_oracle(torch, q3, gen, shape, cpu, stack, x0, x, ones, idx, wts, ws, eps):
+def stack_oracle(torch, q3, gen, shape, cpu, stack, x0, x, run_token, idx_all, eps):
     """The oracle through all 48 layers for the first STACK_ORACLE_TOKENS
     tokens (each layer's tensors copied to the host once, untimed; only the
     oracle's own calls are timed), beside an eager GPU pass of the same
-    tokens with the timed entry point, recording every layer's routing."""
+    tokens with the timed entry point (run_token(i) leaves token i's output
+    in x and every layer's routing in idx_all)."""
     import numpy as np
     H, E, k, F = shape.H, shape.E, shape.k, shape.F
     nt = STACK_ORACLE_TOKENS
     g_idx = np.empty((nt, len(stack), k), np.int32)
     g_out = np.empty((nt, H), np.float32)
     for i in range(nt):
-        x.copy_(x0[i])
-        for l, (router, g_, u_, d_, _) in enumerate(stack):
-            q3.q3moe_moe_ffn_prenorm(x, ones, eps, router, k, g_, u_, d_, F=F, out=x,
-                                     accumulate=True, topk_idx=idx, topk_w=wts, workspace=ws)
-            g_idx[i, l] = idx.cpu().numpy()[0]
+        run_token(i)
+        g_idx[i] = idx_all.cpu().numpy()[:, 0]
         g_out[i] = x.cpu().numpy()[0]
     xh = x0[:nt].cpu().numpy().reshape(nt, H)
     gain = np.ones(H, np.float32)

@@ -306,6 +306,48 @@ q3moe_status q3moe_moe_ffn_prenorm(const float *hidden, int64_t T, int64_t H, in
                                    float *out, int32_t accumulate, void *workspace,
                                    size_t workspace_bytes, void *stream);
 
+/* ------------------------------------------------------ stacked MoE blocks --
+ * n_layers MoE blocks applied one after another to the residual stream x,
+ * in place:
+ *   for l = 0 .. n_layers-1:  x = x + MoE_l(RMSNorm_l(x))
+ * exactly as n_layers calls of q3moe_moe_ffn_prenorm with out = hidden = x
+ * and accumulate = 1 would (same arithmetic and rounding per layer; the
+ * stream is f32 between layers).  This is the stack of the Qwen3-30B-A3B
+ * decoder's 48 MoE layers with the attention taken out (aprender issue
+ * #3714, "File facts": 48 layers, down Q6_K in some and Q4_K in others),
+ * the post-attention RMSNorm of each layer kept between blocks.
+ * layers: HOST array of n_layers descriptors (read during the call only);
+ * each names device memory: norm_gain [H] f32 and router [E x H] f32, both
+ * 16-byte aligned, and the layer's expert tensors as for q3moe_moe_ffn
+ * (gate/up Q4_K, down Q4_K or Q6_K, may differ from layer to layer).  All
+ * layers share T, H, F, E and top_k.
+ * topk_idx / topk_w: device arrays [n_layers x T x top_k]: layer l's
+ * routing at offset l*T*top_k.
+ * For the one-kernel shapes of q3moe_moe_ffn (q3moe_persistent_path(..., 1)
+ * == 1) the whole stack runs as one persistent kernel per 48 layers: each
+ * workgroup hands the rows of x it produced to the next layer as tagged
+ * words, so the launch's ramp and drain are paid once per 48 layers instead
+ * of once per layer.  Other shapes run q3moe_moe_ffn_prenorm per layer.
+ * workspace: at least q3moe_moe_stack_workspace_bytes(T, H, F, E, k) bytes,
+ * 16-byte aligned, all zero before the first call that uses it, reusable by
+ * later calls of any size on the same stream; its first bytes are a
+ * q3moe_moe_ffn workspace (status word at q3moe_expert_ffn_status_offset;
+ * bit 8: a layer's input stream was waited for in vain).
+ * Errors: E_NULL, E_SHAPE, E_QTYPE, E_ALIGN, E_WORKSPACE, E_ALIAS (x overlaps
+ * the routing outputs or a layer's norm_gain or router, or the two routing
+ * outputs overlap), E_HIP.  n_layers = 0 or T = 0 does nothing. */
+typedef struct q3moe_moe_layer {
+    const float *norm_gain;
+    const float *router;
+    q3moe_experts gate, up, down;
+} q3moe_moe_layer;
+size_t q3moe_moe_stack_workspace_bytes(int64_t T, int64_t H, int64_t F, int32_t E,
+                                       int32_t top_k);
+q3moe_status q3moe_moe_stack(float *x, int64_t T, int64_t H, int64_t F, int32_t E,
+                             int32_t top_k, float eps, const q3moe_moe_layer *layers,
+                             int32_t n_layers, int32_t *topk_idx, float *topk_w,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
 /* ------------------------------------------------------ attention prologue --
  * In place on q [T x n_q_heads x head_dim] and k [T x n_kv_heads x head_dim]
  * (f32, row-major): for every head slice, RMSNorm with the gain vector shared

@@ -27,6 +27,7 @@ EXPORTS = (
     "q3moe_moe_ffn_workspace_bytes", "q3moe_moe_ffn", "q3moe_moe_ffn_prenorm", "q3moe_bf16_gemv3",
     "q3moe_attn_prologue_kv", "q3moe_persistent_path", "q3moe_moe_ffn_noalloc", "q3moe_moe_ffn_q8",
     "q3moe_embed", "q3moe_output_head", "q3moe_kv_write_rows", "q3moe_prefill_attention",
+    "q3moe_moe_stack_workspace_bytes", "q3moe_moe_stack",
 )
 
 
@@ -39,6 +40,11 @@ class Q3MoeError(RuntimeError):
 class _Experts(ctypes.Structure):
     _fields_ = [("base", ctypes.c_void_p), ("qtype", ctypes.c_int32),
                 ("reserved", ctypes.c_int32), ("expert_stride_bytes", ctypes.c_int64)]
+
+
+class _MoeLayer(ctypes.Structure):
+    _fields_ = [("norm_gain", ctypes.c_void_p), ("router", ctypes.c_void_p), ("gate", _Experts),
+                ("up", _Experts), ("down", _Experts)]
 
 
 _P, _I64, _I32, _F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
@@ -76,6 +82,9 @@ _SIGS = {
     "q3moe_output_head": (_I32, [_P, _I64, _P, _I32, _I64, _I64, _P, _P]),
     "q3moe_moe_ffn_q8": (_I32, [_P, _I64, _I64, _I64, _I32, _I32, _P, _Experts, _Experts, _Experts,
                                 _P, _P, _P, _I32, _P, ctypes.c_size_t, _P]),
+    "q3moe_moe_stack_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64, _I32, _I32]),
+    "q3moe_moe_stack": (_I32, [_P, _I64, _I64, _I64, _I32, _I32, _F, _P, _I32, _P, _P, _P,
+                               ctypes.c_size_t, _P]),
     "q3moe_moe_ffn_noalloc": (_I32, [_P, _I64, _I64, _I64, _I32, _I32, _P, _Experts, _Experts,
                                      _Experts, _P, _P, _P, _I32, _P]),
 }
@@ -351,6 +360,54 @@ def q3moe_moe_ffn_prenorm(hidden: torch.Tensor, norm_gain: torch.Tensor, eps: fl
         down.c(), _ptr(topk_idx), _ptr(topk_w), _ptr(out), 1 if accumulate else 0,
         _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
     return out, topk_idx, topk_w
+
+
+class MoeLayer(NamedTuple):
+    """One layer of q3moe_moe_stack: RMSNorm gain [H] f32, router [E, H]
+    f32 and the three expert tensors."""
+    norm_gain: torch.Tensor
+    router: torch.Tensor
+    gate: Experts
+    up: Experts
+    down: Experts
+
+
+def q3moe_moe_stack_workspace_bytes(T: int, H: int, F: int, E: int, top_k: int) -> int:
+    return library().q3moe_moe_stack_workspace_bytes(T, H, F, E, top_k)
+
+
+def q3moe_moe_stack(x: torch.Tensor, layers, top_k: int, F: int, eps: float,
+                    topk_idx: Optional[torch.Tensor] = None, topk_w: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None, stream=None):
+    """x <- x + MoE_l(RMSNorm_l(x)) for each MoeLayer in ``layers``, in place
+    on x [T, H]; -> (x, topk_idx int32 [L, T, k], topk_w f32 [L, T, k])."""
+    _need(x, "x", torch.float32, 2)
+    layers = list(layers)
+    T, H = x.shape
+    L = len(layers)
+    dev = x.device
+    E = layers[0].router.shape[0] if L else 1
+    arr = (_MoeLayer * max(L, 1))()
+    for i, ly in enumerate(layers):
+        _need(ly.norm_gain, "norm_gain", torch.float32, 1)
+        _need(ly.router, "router", torch.float32, 2)
+        if ly.router.shape != (E, H) or ly.norm_gain.numel() != H:
+            raise ValueError("every layer needs router [E, H] and norm_gain [H] of one shape")
+        arr[i] = _MoeLayer(ly.norm_gain.data_ptr(), ly.router.data_ptr(), ly.gate.c(), ly.up.c(),
+                           ly.down.c())
+    if topk_idx is None:
+        topk_idx = torch.empty((L, T, top_k), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((L, T, top_k), dtype=torch.float32, device=dev)
+    _need(topk_idx, "topk_idx", torch.int32, 3)
+    _need(topk_w, "topk_w", torch.float32, 3)
+    if tuple(topk_idx.shape) != (L, T, top_k) or tuple(topk_w.shape) != (L, T, top_k):
+        raise ValueError("topk_idx / topk_w must be [layers, T, top_k]")
+    ws = _workspace(q3moe_moe_stack_workspace_bytes(T, H, F, E, top_k), dev, workspace)
+    _check("q3moe_moe_stack", library().q3moe_moe_stack(
+        _ptr(x), T, H, F, E, top_k, eps, ctypes.cast(arr, ctypes.c_void_p), L, _ptr(topk_idx),
+        _ptr(topk_w), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return x, topk_idx, topk_w
 
 
 def q3moe_attn_prologue(q: torch.Tensor, k: torch.Tensor, q_norm: torch.Tensor,

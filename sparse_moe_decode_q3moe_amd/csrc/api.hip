@@ -2,6 +2,8 @@
 // caller's stream.  The contract is documented in include/q3moe.h.
 #include <hip/hip_runtime.h>
 
+#include <vector>
+
 #include "../../include/q3moe.h"
 #include "device_common.h"
 #include "internal.h"
@@ -244,6 +246,66 @@ q3moe_status q3moe_moe_ffn_prenorm(const float* hidden, int64_t T, int64_t H, in
                                    size_t workspace_bytes, void* stream) {
     return moe_ffn_impl(hidden, T, H, F, E, top_k, true, norm_gain, eps, router, gate, up, down, topk_idx,
                         topk_w, out, accumulate, workspace, workspace_bytes, stream);
+}
+
+size_t q3moe_moe_stack_workspace_bytes(int64_t T, int64_t H, int64_t F, int32_t E, int32_t top_k) {
+    // a q3moe_moe_ffn workspace, then the residual stream's tagged words
+    return round256(q3moe_moe_ffn_workspace_bytes(T, H, F, E, top_k)) + q3moe::moe_stack_xbuf_bytes(T, H);
+}
+
+q3moe_status q3moe_moe_stack(float* x, int64_t T, int64_t H, int64_t F, int32_t E, int32_t top_k,
+                             float eps, const q3moe_moe_layer* layers, int32_t n_layers,
+                             int32_t* topk_idx, float* topk_w, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+    if (T < 0 || H % 256 || F % 256 || H < 256 || H > 4096 || F < 256 || F > 1536 || E < 1 ||
+        E > q3moe::kMaxExperts || top_k < 1 || top_k > q3moe::kMaxTopK || top_k > E || n_layers < 0 ||
+        T * top_k > 0x7fffffff / (n_layers > 0 ? n_layers : 1) || !(eps >= 0.0f) || !(eps <= 3.4028235e38f))
+        return Q3MOE_E_SHAPE;
+    if (T == 0 || n_layers == 0) return Q3MOE_OK;
+    if (!x || !layers || !topk_idx || !topk_w) return Q3MOE_E_NULL;
+    if (!aligned16(x)) return Q3MOE_E_ALIGN;
+    const size_t act = (size_t)T * (size_t)H * sizeof(float);
+    const size_t rt = (size_t)n_layers * (size_t)T * (size_t)top_k * 4;
+    if (overlaps(topk_idx, rt, x, act) || overlaps(topk_w, rt, x, act) || overlaps(topk_idx, rt, topk_w, rt))
+        return Q3MOE_E_ALIAS;
+    std::vector<q3moe::MoeLayerTensors> ly((size_t)n_layers);
+    for (int32_t l = 0; l < n_layers; ++l) {
+        const q3moe_moe_layer& d = layers[l];
+        if (!d.norm_gain || !d.router) return Q3MOE_E_NULL;
+        q3moe_status st;
+        if ((st = check_experts(d.gate, F, H, false, ly[l].gate)) != Q3MOE_OK) return st;
+        if ((st = check_experts(d.up, F, H, false, ly[l].up)) != Q3MOE_OK) return st;
+        if ((st = check_experts(d.down, H, F, true, ly[l].down)) != Q3MOE_OK) return st;
+        if (!aligned16(d.norm_gain) || !aligned16(d.router)) return Q3MOE_E_ALIGN;
+        if (overlaps(d.norm_gain, (size_t)H * sizeof(float), x, act) ||
+            overlaps(d.router, (size_t)E * (size_t)H * sizeof(float), x, act) ||
+            overlaps(d.norm_gain, (size_t)H * sizeof(float), topk_idx, rt) ||
+            overlaps(d.norm_gain, (size_t)H * sizeof(float), topk_w, rt))
+            return Q3MOE_E_ALIAS;
+        ly[l].router = d.router;
+        ly[l].gain = d.norm_gain;
+    }
+    if (!workspace || workspace_bytes < q3moe_moe_stack_workspace_bytes(T, H, F, E, top_k))
+        return Q3MOE_E_WORKSPACE;
+    if (!aligned16(workspace)) return Q3MOE_E_ALIGN;
+    const hipStream_t s = as_stream(stream);
+    if (q3moe::moe_stack_fused(T, H, F, E, top_k, ly.data(), n_layers)) {
+        uint8_t* ws = static_cast<uint8_t*>(workspace);
+        uint8_t* ws_words = ws + round256(q3moe::expert_ffn_workspace_bytes(T, H, F, E, top_k)) +
+                            round256(q3moe::route_workspace_bytes(T, E));
+        uint8_t* ws_x = ws + round256(q3moe_moe_ffn_workspace_bytes(T, H, F, E, top_k));
+        return from_hip(q3moe::launch_moe_stack(x, T, H, F, E, top_k, eps, ly.data(), n_layers, topk_idx,
+                                                topk_w, ws, ws_words, ws_x, s));
+    }
+    const int64_t nr = T * top_k;
+    for (int32_t l = 0; l < n_layers; ++l) {
+        const q3moe_status st = moe_ffn_impl(x, T, H, F, E, top_k, true, layers[l].norm_gain, eps,
+                                             layers[l].router, layers[l].gate, layers[l].up, layers[l].down,
+                                             topk_idx + l * nr, topk_w + l * nr, x, 1, workspace,
+                                             workspace_bytes, stream);
+        if (st != Q3MOE_OK) return st;
+    }
+    return Q3MOE_OK;
 }
 
 int32_t q3moe_persistent_path(int64_t T, int64_t H, int64_t F, int32_t E, int32_t top_k,

@@ -1368,6 +1368,403 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
     }
 }
 
+// --------------------------------------------------------- layer stack --
+//
+// The MoE blocks of several stacked layers in ONE persistent launch: for
+// layer l = 0..nl-1, x <- x + MoE_l(RMSNorm_l(x)), each layer with its own
+// router, norm gain and expert tensors (its own down type).  Each layer runs
+// the phases of ffn_fused8_kernel<true, 3> with the input RMSNorm; between
+// layers the residual stream travels as tagged words too: the workgroup that
+// owns output rows r0..r0+7 of a token publishes x_{l+1} for them, and every
+// workgroup polls all of x_{l+1} before layer l+1's norm and router.  So the
+// launch ramp and drain are paid once per stack instead of once per layer.
+// Buffers are reused from layer to layer without counters.  The grid is
+// chosen so that every workgroup owns at least one router unit and one down
+// unit; then each rewrite waits, through a chain of tagged words, for every
+// read of the old contents:
+//   x_{l+1} row  <- every h word of its token in layer l <- (the h writer
+//                   read) every router word of layer l <- every workgroup
+//                   has read all of x_l (it publishes only after that);
+//   router words of layer l+1 <- all of x_{l+1}, i.e. every workgroup is
+//                   past its down units of layer l, and so past its reads of
+//                   layer l's router words and h words;
+//   h words of layer l+1 <- every router word of layer l+1 (as above).
+// The last layer writes x itself, after every workgroup has read it in
+// layer 0 by the first chain.  The tags (one per call and layer, with the
+// top bit set so they never equal the one-layer kernel's) tell old words
+// from new.  The layer table travels in the kernel arguments (48 layers of
+// 56 bytes); longer stacks run as several launches.
+constexpr int kMaxStackLayers = 48;
+
+struct StackLayer {
+    const float* router;
+    const float* gain;
+    const uint8_t* gate;
+    const uint8_t* up;
+    const uint8_t* down;
+    int32_t gstride, ustride, dstride;              // expert strides in bytes (< 2^31)
+    int32_t dqtype;
+};
+
+struct StackJob {
+    StackLayer layer[kMaxStackLayers];
+};
+
+__device__ __forceinline__ uint32_t stack_tag(uint32_t epoch, int l) {
+    return 0x80000000u | ((2u * (epoch * (uint32_t)(kMaxStackLayers + 1) + (uint32_t)l) + 1u) & 0x7fffffffu);
+}
+
+// 4 consecutive f32 values published as tagged words, once all carry `tag`
+// (the wave waits together; a wait that runs out ORs `bit` into the status).
+__device__ __forceinline__ float4 poll_x4(const uint64_t* src, uint32_t tag, int32_t* status, int bit) {
+    uint64_t v[4];
+    int spins = 0;
+    while (true) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        bool ok = true;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ok = ok && (uint32_t)(v[i] >> 32) == tag;
+        if (__all(ok)) break;
+        if (++spins > kSpinLimit) {
+            if (!ok) __hip_atomic_fetch_or(status, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    return make_float4(__uint_as_float((uint32_t)v[0]), __uint_as_float((uint32_t)v[1]),
+                       __uint_as_float((uint32_t)v[2]), __uint_as_float((uint32_t)v[3]));
+}
+
+// grid: at most one workgroup per CU (all resident at once), kFzWaves waves
+// each.  x [T][2048] f32 holds the input and receives the output (in place);
+// topk_idx / topk_w [nl][T][k] receive every layer's routing; xbuf holds the
+// tagged residual stream [T][2048] between layers.  The LDS layout is the
+// one-layer kernel's for a Q6_K down tile (the larger one), so every layer
+// fits it.
+__global__ __launch_bounds__(kFzWaves * kWave) void ffn_stack_kernel(
+    float* x, int64_t T_, int64_t F_, int32_t E_, int32_t k_, int32_t nl, float eps, int32_t P_,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, uint64_t* __restrict__ hbuf,
+    int32_t* __restrict__ sync, uint64_t* __restrict__ rbuf, uint64_t* __restrict__ xbuf,
+    const StackJob job) {
+    using G = GuTask<kFzNB>;
+    constexpr int kThr = kFzWaves * kWave;
+    extern __shared__ __align__(16) uint8_t smem[];
+    int32_t* status = sync + kSyncStatus;
+    const uint32_t epoch = (uint32_t)__hip_atomic_load(sync + kSyncEpoch, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT);
+    int32_t exit_ticket = -1;
+
+    for (int l = 0; l < nl; ++l) {
+        // the thread index, opaque to the compiler in each layer: otherwise
+        // every address derived from it is hoisted out of the layer loop and
+        // held in registers through the whole body; likewise the sizes and
+        // everything derived from them
+        int tid_ = (int)threadIdx.x;
+        int64_t T = T_, F = F_;
+        int32_t E = E_, k = k_, P = P_;
+        asm volatile("" : "+v"(tid_), "+s"(T), "+s"(F), "+s"(E), "+s"(k), "+s"(P));
+        const int tid = tid_, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const bool is_gu = wave < kFzGu;
+        const int grid = (int)gridDim.x, wg = (int)blockIdx.x;
+        const FusedLds L = fused_lds(T, F, 2);
+        float* res = reinterpret_cast<float*>(smem + L.res_off);
+        const int tiles = (int)(F / G::R);
+        const int n_gu = (int)T * k * tiles;
+        const int64_t row_units = G::H / kDnRows;
+        const int64_t n_dn = T * row_units;
+        const int gu_step = grid * kFzGu;
+        const int nr = (int)(T * k);
+        int32_t* x_ready = reinterpret_cast<int32_t*>(smem + L.flag_off);
+        int32_t* dn_ready = x_ready + 1;
+        double* rp = reinterpret_cast<double*>(smem + L.rp_off);      // [wave][token]
+        const int U = E * P, HP = (int)(G::H / P);
+        const StackLayer& Ly = job.layer[l];
+        const uint32_t tag = __builtin_amdgcn_readfirstlane(stack_tag(epoch, l));
+        const uint32_t xtag = __builtin_amdgcn_readfirstlane(stack_tag(epoch, l + 1));
+        const bool last = l == nl - 1;
+        const DnGeom dg(F, Ly.dqtype);
+        __syncthreads();                      // the previous layer is done with every LDS region
+        if (tid == 0) {
+            *x_ready = 0;
+            *dn_ready = 0;
+        }
+        __syncthreads();
+
+        int64_t unit = wg;
+        int tau = wg * kFzGu + wave;
+        int p = (tau < n_gu ? tau : 0) / tiles, r0 = ((tau < n_gu ? tau : 0) % tiles) * G::R;
+        GuRows rows;
+
+        // (a0) values 4*tid .. 4*tid+3 of every token's x_l: the input for
+        // layer 0, the tagged stream after it; then the layer's RMSNorm
+        float4 xv[kFzMaxTokens];
+#pragma unroll
+        for (int t = 0; t < kFzMaxTokens; ++t) {
+            const int tc = t < T ? t : (int)T - 1;
+            xv[t] = l == 0 ? reinterpret_cast<const float4*>(x + (int64_t)tc * G::H)[tid]
+                           : poll_x4(xbuf + (int64_t)tc * G::H + 4 * tid, tag, status, 8);
+        }
+        {
+            const float4 g4 = reinterpret_cast<const float4*>(Ly.gain)[tid];
+#pragma unroll
+            for (int t = 0; t < kFzMaxTokens; ++t) {
+                if (t < T) {
+                    const float4 v = xv[t];
+                    double ss = (double)v.x * v.x;
+                    ss = fma((double)v.y, (double)v.y, ss);
+                    ss = fma((double)v.z, (double)v.z, ss);
+                    ss = fma((double)v.w, (double)v.w, ss);
+                    const double sw = wave_sum_dpp_f64(ss);
+                    if (lane == 0) rp[wave * kFzMaxTokens + t] = sw;
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int t = 0; t < kFzMaxTokens; ++t) {
+                if (t < T) {
+                    double tot = 0.0;
+#pragma unroll
+                    for (int wv = 0; wv < kFzWaves; ++wv) tot += rp[wv * kFzMaxTokens + t];
+                    const double inv = 1.0 / sqrt(tot / (double)G::H + (double)eps);
+                    const float4 v = xv[t];
+                    xv[t] = make_float4((float)((double)g4.x * v.x * inv), (float)((double)g4.y * v.y * inv),
+                                        (float)((double)g4.z * v.z * inv), (float)((double)g4.w * v.w * inv));
+                }
+            }
+            __syncthreads();                  // rp is reused by the router sums
+        }
+        // (a) this workgroup's router unit(s), published as tagged words
+        for (int u = wg; u < U; u += grid) {
+            const int e = u / P, part = u % P;
+            double acc[kFzMaxTokens];
+#pragma unroll
+            for (int t = 0; t < kFzMaxTokens; ++t) acc[t] = 0.0;
+            if ((4 * tid) / HP == part) {
+                const float4 r = reinterpret_cast<const float4*>(Ly.router + (int64_t)e * G::H)[tid];
+#pragma unroll
+                for (int t = 0; t < kFzMaxTokens; ++t) {
+                    if (t < T) {
+                        const float4 x4 = xv[t];
+                        double a = fma((double)r.x, (double)x4.x, 0.0);
+                        a = fma((double)r.y, (double)x4.y, a);
+                        a = fma((double)r.z, (double)x4.z, a);
+                        acc[t] = fma((double)r.w, (double)x4.w, a);
+                    }
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < kFzMaxTokens; ++t) {
+                if (t < T) {
+                    const double sw = wave_sum_dpp_f64(acc[t]);
+                    if (lane == 0) rp[wave * kFzMaxTokens + t] = sw;
+                }
+            }
+            __syncthreads();
+            if (tid < T) {
+                double sum = 0.0;
+#pragma unroll
+                for (int wv = 0; wv < kFzWaves; ++wv) sum += rp[wv * kFzMaxTokens + tid];
+                const uint64_t bits = __builtin_bit_cast(uint64_t, sum);
+                uint64_t* dst = rbuf + ((int64_t)tid * U + u) * 2;
+                __hip_atomic_store(dst, ((uint64_t)tag << 32) | (uint32_t)bits, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(dst + 1, ((uint64_t)tag << 32) | (uint32_t)(bits >> 32),
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            __syncthreads();
+        }
+        build_x_pieces<kFzMaxTokens, 3>(xv, T, smem, tid);
+        // (b) logits from every workgroup's partial sums, the top-k
+        double* lgt = reinterpret_cast<double*>(smem + L.lg_off);
+        uint64_t* keys = reinterpret_cast<uint64_t*>(smem + L.key_off);
+        uint32_t* keys32 = reinterpret_cast<uint32_t*>(smem + L.key32_off);
+        int32_t* sel_idx = reinterpret_cast<int32_t*>(smem + L.sel_off);
+        double* sel_val = reinterpret_cast<double*>(sel_idx + kFzMaxTokens * kFzMaxSlots);
+        int32_t* slot_cnt = reinterpret_cast<int32_t*>(smem + L.scnt_off);
+        if (tid < nr) slot_cnt[tid] = 0;
+        router_logits_from_partials<kThr>(rbuf, (int)T * U, P, E, U, tag, tid, lane, status, lgt,
+                                          keys, keys32);
+        __syncthreads();
+        topk_rank_screen<kThr>(lgt, keys32, (int)T, E, k, tid, sel_idx, sel_val, slot_cnt);
+        __syncthreads();
+        if (!__all(lane >= nr || slot_cnt[lane] == 1)) {
+            topk_rank_select<kThr>(lgt, keys, keys32, (int)T, E, k, tid, sel_idx, sel_val);
+            __syncthreads();
+        }
+        const int my_idx = lane < nr ? sel_idx[lane] : -1;
+        if (is_gu)
+            gu_rows_load(rows, lane_value(my_idx, p), E, Ly.gate, Ly.gstride, Ly.up, Ly.ustride, r0, lane);
+        float my_w;
+        {
+            const int tl = lane < nr ? lane / k : 0;
+            const double top = sel_val[tl * k];
+            const double ex = lane < nr ? exp(sel_val[lane] - top) : 0.0;
+            double den = 0.0;
+            for (int tt = 0; tt < T; ++tt) {
+                double d = 0.0;
+                for (int r = 0; r < k; ++r) d += readlane_f64(ex, tt * k + r);
+                if (tt == tl) den = d;
+            }
+            my_w = lane < nr ? (float)(ex / den) : 0.f;
+        }
+        if (wg == 0 && tid < nr) {
+            topk_idx[(int64_t)l * nr + tid] = my_idx;
+            topk_w[(int64_t)l * nr + tid] = my_w;
+        }
+
+        if (is_gu) {
+            __builtin_amdgcn_s_setprio(2);
+            if (tau < n_gu) {
+                int xc = p / k;
+                XCols xcol = load_xcols<3>(smem + xc * kI8TokenBytes, lane);
+                gu_rows_finish<3>(rows, xcol, lane, hbuf, (int64_t)p * F + r0, tag);
+                for (tau += gu_step; tau < n_gu; tau += gu_step) {
+                    p = tau / tiles;
+                    r0 = (tau % tiles) * G::R;
+                    gu_rows_load(rows, lane_value(my_idx, p), E, Ly.gate, Ly.gstride, Ly.up, Ly.ustride, r0,
+                                 lane);
+                    const int t = p / k;
+                    if (t != xc) {
+                        xcol = load_xcols<3>(smem + t * kI8TokenBytes, lane);
+                        xc = t;
+                    }
+                    gu_rows_finish<3>(rows, xcol, lane, hbuf, (int64_t)p * F + r0, tag);
+                }
+            }
+            __builtin_amdgcn_s_setprio(0);
+        }
+        int dn_wave = __builtin_amdgcn_readfirstlane(is_gu ? 0 : 1);
+        asm volatile("" : "+s"(dn_wave));
+        if (dn_wave) {
+            if (unit < n_dn) {
+                const int dw = wave - kFzGu;
+                const int64_t t = unit / row_units, r0d = (unit % row_units) * kDnRows;
+                for (int s = dw; s < k; s += kFzDn) {
+                    const int e = lane_value(my_idx, (int)(t * k + s));
+                    if (e >= 0 && e < E)
+                        dn_issue_weights(smem + L.dn_off + s * dg.tile_pad, dg, Ly.down, Ly.dstride, e, r0d, lane);
+                }
+            }
+            wait_all_loads();
+            if (lane == 0)
+                __hip_atomic_fetch_add(dn_ready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+
+        // (c) down projection and combine; the residual stream goes on as
+        // tagged words (the last layer writes x)
+        const int groups = (int)(F / kDnGroup);
+        const int n_units = k * groups;
+        constexpr int kUnitThr = (kFzWaves - 2) * kWave;
+        const int uw = wave < 4 ? wave : (wave >= kFzGu ? wave - 2 : -1);
+        const int iters = (n_units + kUnitThr - 1) / kUnitThr;
+        float* hl = reinterpret_cast<float*>(smem + L.h_off);
+        for (int j = 0; unit < n_dn; unit += grid, ++j) {
+            const int64_t t = unit / row_units, r0u = (unit % row_units) * kDnRows;
+            if (j > 0) {
+                for (int s = wave; s < k; s += kFzWaves) {
+                    const int e = lane_value(my_idx, (int)(t * k + s));
+                    if (e >= 0 && e < E)
+                        dn_issue_weights(smem + L.dn_off + s * dg.tile_pad, dg, Ly.down, Ly.dstride, e, r0u, lane);
+                }
+                wait_all_loads();
+                __syncthreads();
+            } else if (uw >= 0) {
+                int spins = 0;
+                while (__hip_atomic_load(dn_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < kFzDn &&
+                       ++spins <= kSpinLimit)
+                    __builtin_amdgcn_s_sleep(1);
+            }
+            float acc[kDnRows];
+#pragma unroll
+            for (int rho = 0; rho < kDnRows; ++rho) acc[rho] = 0.f;
+            for (int it = 0; it < iters; ++it) {
+                const int u = uw * kWave + lane + it * kUnitThr;
+                const bool active = uw >= 0 && u < n_units;
+                const int uc = active ? u : 0;
+                const int s = uc / groups, grp = uc % groups;
+                const int e = __shfl(my_idx, (int)(t * k) + s, kWave);
+                const float ws = __shfl(my_w, (int)(t * k) + s, kWave);
+                const bool valid = active && e >= 0 && e < E;
+                uint32_t qb[kDnRows][4];
+                float fa[kDnRows], fc[kDnRows];
+                if (uw >= 0) dn_unit_quants(smem + L.dn_off + s * dg.tile_pad, dg, grp, qb, fa, fc);
+                if (it == 0) {
+                    wait_tagged<kThr>(hbuf + t * k * F, k * (int)F, tag, reinterpret_cast<uint32_t*>(hl), tid, status, 2);
+                    if (last && tid == 0 && unit + grid >= n_dn) {
+                        int lane0 = 0;
+                        asm volatile("" : "+v"(lane0));
+                        exit_ticket = __hip_atomic_fetch_add(sync + kSyncExit + (wg % kStripes) * kLineInts + lane0, 1,
+                                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                    __syncthreads();
+                }
+                if (uw >= 0) {
+                    float hv[kDnGroup];
+#pragma unroll
+                    for (int i = 0; i < kDnGroup; i += 4) {
+                        const float4 h4 = *reinterpret_cast<const float4*>(hl + s * F + grp * kDnGroup + i);
+                        hv[i] = h4.x; hv[i + 1] = h4.y; hv[i + 2] = h4.z; hv[i + 3] = h4.w;
+                    }
+                    float hsum = 0.f;
+#pragma unroll
+                    for (int i = 0; i < kDnGroup; ++i) hsum += hv[i];
+#pragma unroll
+                    for (int rho = 0; rho < kDnRows; ++rho) {
+                        float sq = 0.f;
+#pragma unroll
+                        for (int i = 0; i < kDnGroup; ++i)
+                            sq = fmaf((float)((qb[rho][i >> 2] >> (8 * (i & 3))) & 0xffu), hv[i], sq);
+                        const float y = fmaf(fa[rho], sq, fc[rho] * hsum);
+                        acc[rho] += valid ? ws * y : 0.f;
+                    }
+                }
+            }
+            const float r = fold8_rows(acc, lane);
+            if ((lane & 7) == 0) res[wave * kDnRows + (lane >> 3)] = r;
+            __syncthreads();
+            if (wave == 0 && lane < kDnRows) {                // fixed order over the waves
+                float o = 0.f;
+#pragma unroll
+                for (int wv = 0; wv < kFzWaves; ++wv) o += res[wv * kDnRows + lane];
+                const int64_t row = t * G::H + r0u + lane;
+                // x_l of the row: the input (layer 0) or this workgroup's own
+                // word of the stream (it owns the row in every layer)
+                const float xo = l == 0 ? x[row]
+                                        : __uint_as_float((uint32_t)__hip_atomic_load(
+                                              xbuf + row, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+                const float xn = xo + o;
+                if (last) x[row] = xn;
+                else __hip_atomic_store(xbuf + row, ((uint64_t)xtag << 32) | __float_as_uint(xn),
+                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    }
+
+    // exit: the last workgroup advances the epoch and zeroes the counters
+    if (threadIdx.x == 0) {
+        const int grid = (int)gridDim.x, wg = (int)blockIdx.x;
+        const int st = wg % kStripes;
+        const int32_t done = exit_ticket >= 0
+                                 ? exit_ticket
+                                 : __hip_atomic_fetch_add(sync + kSyncExit + st * kLineInts, 1,
+                                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (done == stripe_members(st, grid) - 1) {
+            const int used = grid < kStripes ? grid : kStripes;
+            const int32_t top = __hip_atomic_fetch_add(sync + kSyncExitTop, 1, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT);
+            if (top == used - 1) {
+                for (int i = 0; i < kStripes; ++i)
+                    __hip_atomic_store(sync + kSyncExit + i * kLineInts, 0, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(sync + kSyncExitTop, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(sync + kSyncEpoch, (int32_t)(epoch + 1u), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    }
+}
+
 constexpr size_t kMaxLdsPerWorkgroup = 160 * 1024;
 
 // Compute-unit count of the current device, cached per device (an immutable
@@ -1564,12 +1961,18 @@ hipError_t launch_moe_decode(const float* hidden, int64_t T, int64_t H, int64_t 
                              void* route_words, const float* norm_gain, float eps, hipStream_t stream,
                              int act_pieces) {
     if (act_pieces != 1 && act_pieces != 3) return hipErrorInvalidValue;
-    const int grid = fused_grid(T, H, F, k, down.qtype, true, act_pieces);
+    int grid = fused_grid(T, H, F, k, down.qtype, true, act_pieces);
     if (grid <= 0 || E > kFzRouteNper * kWave) return hipErrorInvalidValue;
     int32_t* sync = static_cast<int32_t*>(ffn_ws);
     uint8_t* hp = static_cast<uint8_t*>(ffn_ws) + kFfnSyncBytes;
     auto* rw = static_cast<uint64_t*>(route_words);
     const int P = route_parts(E, grid);
+    // In place (out == hidden), a workgroup may overwrite rows of hidden only
+    // once every workgroup has read them.  It writes after seeing every router
+    // word, and a workgroup publishes its router words only after it has read
+    // all of hidden: so every workgroup must own a router unit (route_parts
+    // gives the same P for the smaller grid).
+    if (static_cast<const void*>(hidden) == static_cast<const void*>(out) && E * P < grid) grid = E * P;
     if (act_pieces == 1)
         return launch_fused8<true, 1>(hidden, T, F, E, k, nullptr, nullptr, gate, up, down, out,
                                       accumulate, hp, sync, grid, router, P, topk_idx, topk_w, rw,
@@ -1577,6 +1980,100 @@ hipError_t launch_moe_decode(const float* hidden, int64_t T, int64_t H, int64_t 
     return launch_fused8<true, 3>(hidden, T, F, E, k, nullptr, nullptr, gate, up, down, out, accumulate,
                                   hp, sync, grid, router, P, topk_idx, topk_w, rw, norm_gain, eps,
                                   stream);
+}
+
+namespace {
+
+// Workgroups of ffn_stack_kernel one compute unit holds at once with `lds`
+// bytes of dynamic LDS (the occupancy calculator's answer), cached per
+// (device, LDS size); 0 when the device cannot run it.
+int stack_blocks_per_cu(int lds) {
+    static std::atomic<int64_t> cache[kMaxDevices];
+    static LdsLimit lds_set;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+    if (dev < kMaxDevices) {
+        const int64_t c = cache[dev].load(std::memory_order_relaxed);
+        if (c != 0 && (c >> 16) == lds) return (int)(c & 0xffff) - 1;
+    }
+    const void* fn = reinterpret_cast<const void*>(ffn_stack_kernel);
+    if (ensure_lds(fn, lds_set, lds) != hipSuccess) return 0;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, kFzWaves * kWave, (size_t)lds) != hipSuccess ||
+        n < 0)
+        n = 0;
+    if (dev < kMaxDevices) cache[dev].store(((int64_t)lds << 16) | (int64_t)(n + 1), std::memory_order_relaxed);
+    return n;
+}
+
+// Grid of the stack kernel (0: shape outside it), and its router parts.
+// At most one workgroup per compute unit (all resident), and no more
+// workgroups than down units (T * H / 8) or router units (E * P): every
+// workgroup owns one of each, which the kernel's buffer reuse relies on.
+int stack_grid(int64_t T, int64_t H, int64_t F, int32_t E, int32_t k, int* P) {
+    if (H != (int64_t)kFzNB * kQK || k > kFzMaxSlots || T > kFzMaxTokens || T < 1 ||
+        E > kFzRouteNper * kWave || F % kQK != 0)
+        return 0;
+    const int lds = fused_lds(T, F, 2).total;       // the Q6_K tile layout serves both down types
+    if ((size_t)lds > kMaxLdsPerWorkgroup) return 0;
+    const int cus = cu_count();
+    if (cus <= 0 || stack_blocks_per_cu(lds) < 1) return 0;
+    const int64_t units = T * (H / kDnRows);
+    int grid = (int)(units < cus ? units : cus);
+    *P = route_parts(E, grid);
+    if ((int64_t)E * *P < grid) grid = E * *P;
+    return grid;
+}
+
+}  // namespace
+
+bool moe_stack_fused(int64_t T, int64_t H, int64_t F, int32_t E, int32_t k, const MoeLayerTensors* layers,
+                     int32_t n_layers) {
+    for (int32_t l = 0; l < n_layers; ++l)
+        if (layers[l].gate.stride > INT32_MAX || layers[l].up.stride > INT32_MAX ||
+            layers[l].down.stride > INT32_MAX)
+            return false;
+    int P = 1;
+    return stack_grid(T, H, F, E, k, &P) > 0;
+}
+
+size_t moe_stack_xbuf_bytes(int64_t T, int64_t H) {
+    return (size_t)(T > 0 ? T : 0) * (size_t)(H > 0 ? H : 0) * sizeof(uint64_t);
+}
+
+hipError_t launch_moe_stack(float* x, int64_t T, int64_t H, int64_t F, int32_t E, int32_t k, float eps,
+                            const MoeLayerTensors* layers, int32_t n_layers, int32_t* topk_idx,
+                            float* topk_w, void* ffn_ws, void* route_words, void* xbuf,
+                            hipStream_t stream) {
+    int P = 1;
+    const int grid = stack_grid(T, H, F, E, k, &P);
+    if (grid <= 0) return hipErrorInvalidValue;
+    const FusedLds L = fused_lds(T, F, 2);
+    static LdsLimit lds_set;
+    hipError_t err = ensure_lds(reinterpret_cast<const void*>(ffn_stack_kernel), lds_set, L.total);
+    if (err != hipSuccess) return err;
+    int32_t* sync = static_cast<int32_t*>(ffn_ws);
+    auto* hb = reinterpret_cast<uint64_t*>(static_cast<uint8_t*>(ffn_ws) + kFfnSyncBytes);
+    const int64_t nr = T * k;
+    for (int32_t l0 = 0; l0 < n_layers; l0 += kMaxStackLayers) {
+        const int32_t nl = n_layers - l0 < kMaxStackLayers ? n_layers - l0 : kMaxStackLayers;
+        StackJob job{};
+        for (int32_t i = 0; i < nl; ++i) {
+            const MoeLayerTensors& s = layers[l0 + i];
+            if (s.gate.stride > INT32_MAX || s.up.stride > INT32_MAX || s.down.stride > INT32_MAX)
+                return hipErrorInvalidValue;
+            job.layer[i] = StackLayer{s.router, s.gain, s.gate.base, s.up.base, s.down.base,
+                                      (int32_t)s.gate.stride, (int32_t)s.up.stride, (int32_t)s.down.stride,
+                                      s.down.qtype};
+        }
+        hipLaunchKernelGGL(ffn_stack_kernel, dim3((unsigned)grid), dim3(kFzWaves * kWave), (size_t)L.total,
+                           stream, x, T, F, E, k, nl, eps, (int32_t)P, topk_idx + l0 * nr,
+                           topk_w + l0 * nr, hb, sync, static_cast<uint64_t*>(route_words),
+                           static_cast<uint64_t*>(xbuf), job);
+        err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    return hipSuccess;
 }
 
 }  // namespace q3moe

@@ -103,6 +103,27 @@ hipError_t launch_moe_decode(const float* hidden, int64_t T, int64_t H, int64_t 
                              void* route_words, const float* norm_gain, float eps,
                              hipStream_t stream, int act_pieces = 3);
 
+// Several stacked MoE blocks, x <- x + MoE_l(RMSNorm_l(x)) for l = 0..n-1,
+// in one persistent launch per 48 layers (shape limits of launch_moe_decode;
+// each layer its own router, gain and experts, down Q4_K or Q6_K) when
+// moe_stack_fused says so.
+// ffn_ws and route_words as for launch_moe_decode, xbuf
+// moe_stack_xbuf_bytes(T, H) of memory for the residual stream between
+// layers; topk_idx / topk_w receive [n_layers][T][k].
+struct MoeLayerTensors {
+    const float* router;
+    const float* gain;
+    ExpertTensor gate, up, down;
+};
+// (and whether every layer's expert strides fit the kernel's 32-bit fields)
+bool moe_stack_fused(int64_t T, int64_t H, int64_t F, int32_t E, int32_t k, const MoeLayerTensors* layers,
+                     int32_t n_layers);
+size_t moe_stack_xbuf_bytes(int64_t T, int64_t H);
+hipError_t launch_moe_stack(float* x, int64_t T, int64_t H, int64_t F, int32_t E, int32_t k, float eps,
+                            const MoeLayerTensors* layers, int32_t n_layers, int32_t* topk_idx,
+                            float* topk_w, void* ffn_ws, void* route_words, void* xbuf,
+                            hipStream_t stream);
+
 // ffn.hip: dispatch, and the generic path for any H, F multiple of 256
 size_t expert_ffn_workspace_bytes(int64_t T, int64_t H, int64_t F, int32_t E, int32_t k);
 size_t expert_ffn_status_offset(int64_t T, int64_t H, int64_t F, int32_t E, int32_t k);

@@ -29,7 +29,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 27, names
+    assert len(names) == 29, names
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(_lib.EXPORTS) == names
@@ -174,6 +174,52 @@ def test_moe_ffn_prenorm_validation(lib):
     # the workspace also holds the normalised rows of the multi-kernel path
     assert need >= lib.q3moe_expert_ffn_workspace_bytes(3, 2048, 768, 128, 8) + \
         lib.q3moe_route_workspace_bytes(3, 128) + 3 * 2048 * 4
+
+
+def _stack(lib, T=1, H=2048, F=768, E=128, k=8, eps=1e-6, x=FAKE, layers=None, n=None,
+           idx=ctypes.c_void_p(0x50000), w=ctypes.c_void_p(0x60000), ws=ctypes.c_void_p(0x80000),
+           ws_bytes=1 << 30, **layer_kw):
+    if layers is None:
+        kw = dict(norm_gain=0x90000, router=0x70000, gate=_experts(), up=_experts(),
+                  down=_experts(qtype=q3.Q6_K, stride=1290240))
+        kw.update(layer_kw)
+        one = _lib._MoeLayer(kw["norm_gain"], kw["router"], kw["gate"], kw["up"], kw["down"])
+        layers = (_lib._MoeLayer * 2)(one, one)
+        n = 2 if n is None else n
+    ptr = None if layers is False else ctypes.cast(layers, ctypes.c_void_p)
+    return lib.q3moe_moe_stack(x, T, H, F, E, k, eps, ptr, 0 if n is None else n, idx, w, ws,
+                               ws_bytes, None)
+
+
+def test_moe_stack_validation(lib):
+    """The layer stack checks every layer's tensors as the pre-norm block
+    does, the [layers, T, k] routing outputs for aliasing with x and each
+    other, and its larger workspace (the block's plus the residual stream's
+    words).  Calls that would pass validation are not made here."""
+    assert _stack(lib, T=0) == OK
+    assert _stack(lib, n=0) == OK
+    assert _stack(lib, n=-1) == E_SHAPE
+    assert _stack(lib, layers=False, n=2) == E_NULL
+    assert _stack(lib, x=None) == E_NULL
+    assert _stack(lib, idx=None) == E_NULL
+    assert _stack(lib, norm_gain=None) == E_NULL
+    assert _stack(lib, router=None) == E_NULL
+    assert _stack(lib, eps=-1.0) == E_SHAPE
+    assert _stack(lib, H=2000) == E_SHAPE
+    assert _stack(lib, k=9, E=8) == E_SHAPE
+    assert _stack(lib, gate=_experts(qtype=q3.Q6_K, stride=1 << 21)) == E_QTYPE
+    assert _stack(lib, x=FAKE_MIS) == E_ALIGN
+    assert _stack(lib, norm_gain=0x90004) == E_ALIGN
+    assert _stack(lib, router=0x10000 + 64) == E_ALIAS                    # router over x
+    assert _stack(lib, norm_gain=0x10000 + 256) == E_ALIAS                # gain inside x
+    # the second layer's routing (offset T*k*4 = 32 bytes) reaches into the weights
+    assert _stack(lib, w=ctypes.c_void_p(0x50000 + 48)) == E_ALIAS
+    assert _stack(lib, idx=ctypes.c_void_p(0x10000 + 32)) == E_ALIAS      # routing into x
+    assert _stack(lib, ws=None) == E_WORKSPACE
+    need = lib.q3moe_moe_stack_workspace_bytes(3, 2048, 768, 128, 8)
+    assert need >= lib.q3moe_moe_ffn_workspace_bytes(3, 2048, 768, 128, 8) + 3 * 2048 * 8
+    assert _stack(lib, T=3, ws_bytes=need - 1) == E_WORKSPACE
+    assert _stack(lib, ws=FAKE_MIS) == E_ALIGN
 
 
 def _gemv3(lib, T=1, N0=64, N1=8, N2=8, K=64, W0=FAKE, W1=ctypes.c_void_p(0x20000),
