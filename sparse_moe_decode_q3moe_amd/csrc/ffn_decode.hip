@@ -1417,14 +1417,15 @@ __device__ __forceinline__ uint32_t stack_tag(uint32_t epoch, int l) {
 // 4 consecutive f32 values published as tagged words, once all carry `tag`
 // (the wave waits together; a wait that runs out ORs `bit` into the status).
 __device__ __forceinline__ float4 poll_x4(const uint64_t* src, uint32_t tag, int32_t* status, int bit) {
-    uint64_t v[4];
+    uint64_t v0, v1, v2, v3;
     int spins = 0;
     while (true) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        bool ok = true;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ok = ok && (uint32_t)(v[i] >> 32) == tag;
+        v0 = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        v1 = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        v2 = __hip_atomic_load(src + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        v3 = __hip_atomic_load(src + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool ok = (uint32_t)(v0 >> 32) == tag && (uint32_t)(v1 >> 32) == tag &&
+                        (uint32_t)(v2 >> 32) == tag && (uint32_t)(v3 >> 32) == tag;
         if (__all(ok)) break;
         if (++spins > kSpinLimit) {
             if (!ok) __hip_atomic_fetch_or(status, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1432,8 +1433,8 @@ __device__ __forceinline__ float4 poll_x4(const uint64_t* src, uint32_t tag, int
         }
         __builtin_amdgcn_s_sleep(1);
     }
-    return make_float4(__uint_as_float((uint32_t)v[0]), __uint_as_float((uint32_t)v[1]),
-                       __uint_as_float((uint32_t)v[2]), __uint_as_float((uint32_t)v[3]));
+    return make_float4(__uint_as_float((uint32_t)v0), __uint_as_float((uint32_t)v1),
+                       __uint_as_float((uint32_t)v2), __uint_as_float((uint32_t)v3));
 }
 
 // grid: at most one workgroup per CU (all resident at once), kFzWaves waves

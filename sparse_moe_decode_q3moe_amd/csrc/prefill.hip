@@ -251,7 +251,7 @@ __global__ __launch_bounds__(kGuThreads) void pf_gateup_kernel(
     const int64_t tokb = rb2 < nrows ? pairs[row0 + rb2] / k : -1;
     const int64_t toks = tid < 4 * kPfRows && (tid >> 2) < nrows ? pairs[row0 + (tid >> 2)] / k : -1;
     uint4 rx[6], rw[2], rh;
-    float rs = 0.f;
+    float2 rs = make_float2(0.f, 0.f);
     auto wrow = [&](int r) -> const uint8_t* { return r < kGuFeat ? gexp + r * rowb : uexp + (r - kGuFeat) * rowb; };
     auto load_stage = [&](int st) {
         const int64_t k0 = (int64_t)st * kStageK;
@@ -270,10 +270,11 @@ __global__ __launch_bounds__(kGuThreads) void pf_gateup_kernel(
             rw[u] = *reinterpret_cast<const uint4*>(wrow(q >> 2) + sb * kQ4KBytes + 16 + 64 * half + 16 * (q & 3));
         }
         if (tid < kGuWRows) rh = *reinterpret_cast<const uint4*>(wrow(tid) + sb * kQ4KBytes);
-        if (tid < 4 * kPfRows) {
-            const int64_t g16 = (k0 >> 4) + 2 * (tid & 3);
-            rs = toks >= 0 ? xs16[toks * (H / 16) + g16] + xs16[toks * (H / 16) + g16 + 1] : 0.f;
-        }
+        // the sub-block's two 16-value sums, from a clamped row and added
+        // only when stored: an add here would wait for this stage's loads at
+        // once and leave nothing to overlap with the matrix work
+        const int64_t g16 = (k0 >> 4) + 2 * (tid & 3);
+        rs = *reinterpret_cast<const float2*>(xs16 + (toks >= 0 ? toks : 0) * (H / 16) + g16);
     };
     auto store_stage = [&](int half) {
 #pragma unroll
@@ -297,7 +298,7 @@ __global__ __launch_bounds__(kGuThreads) void pf_gateup_kernel(
                     half ? make_float2(sj[4 + j], bj[4 + j]) : make_float2(sj[j], bj[j]);
         }
         if (tid < 4 * kPfRows)
-            reinterpret_cast<float*>(smem + kGuSOff)[(tid & 3) * kPfRows + (tid >> 2)] = rs;
+            reinterpret_cast<float*>(smem + kGuSOff)[(tid & 3) * kPfRows + (tid >> 2)] = toks >= 0 ? rs.x + rs.y : 0.f;
     };
 
     const int col = lane & 15, g = lane >> 4;
@@ -479,6 +480,16 @@ __global__ __launch_bounds__(kDnThreads) void pf_down_kernel(
     const int orow = 16 * (wave & 3) + col;                   // this lane's output row in the tile
     const int tb0 = wave >> 2;                                // token blocks tb0, tb0 + 2
     f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+    // the pair index of each output row this lane stores, read now (reading
+    // it at the store would put a memory round trip before each of them)
+    int32_t opair[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 16 * (tb0 + 2 * i) + 4 * g + r;
+            opair[i][r] = pairs[row0 + (t < nrows ? t : 0)];
+        }
 
     load_stage(0);
 #pragma unroll
@@ -562,7 +573,7 @@ __global__ __launch_bounds__(kDnThreads) void pf_down_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = 16 * (tb0 + 2 * i) + 4 * g + r;
-            if (t < nrows) Y[(int64_t)pairs[row0 + t] * H + h0 + orow] = acc[i][r];
+            if (t < nrows) Y[(int64_t)opair[i][r] * H + h0 + orow] = acc[i][r];
         }
 }
 
