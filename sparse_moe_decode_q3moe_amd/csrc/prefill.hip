@@ -411,6 +411,7 @@ __host__ __device__ inline int pf_down_lds(int64_t F, int32_t qtype) {
     return pf_down_hoff(F, qtype) + 2 * kDnPieceB + 8 * kPfRows * 4;
 }
 
+template <bool Q6>
 __global__ __launch_bounds__(kDnThreads) void pf_down_kernel(
     const uint16_t* __restrict__ hhi, const uint16_t* __restrict__ hlo,
     const float* __restrict__ hs16, int64_t F, const int32_t* __restrict__ offsets,
@@ -426,7 +427,7 @@ __global__ __launch_bounds__(kDnThreads) void pf_down_kernel(
     const int64_t row0 = offsets[e] + (int64_t)(slot - tile_off[e]) * kPfRows;
     const int nrows = (int)min((int64_t)kPfRows, (int64_t)offsets[e + 1] - row0);
     const int64_t h0 = (int64_t)htile * kDnOut;
-    const bool q6 = qtype == 2;
+    constexpr bool q6 = Q6;                                   // the down type, fixed per instantiation
     const int bb = q6 ? kQ6KBytes : kQ4KBytes;
     const int nb = (int)(F / kQK);
     const int rowb = nb * bb;
@@ -515,7 +516,7 @@ __global__ __launch_bounds__(kDnThreads) void pf_down_kernel(
             dq = 0.125f * half_bits_to_float(hdr.x & 0xffffu);   // weights enter as 128 + 8q
             dm = half_bits_to_float(hdr.x >> 16);
         }
-#pragma unroll 2
+#pragma unroll
         for (int G = 0; G < 8; ++G) {                         // one 16-wide group per k step
             const int gi = 8 * half + G;                      // group within the super-block
             uint32_t q;
@@ -688,11 +689,13 @@ hipError_t launch_prefill_ffn(const float* hidden, int64_t T, int64_t H, int64_t
     if ((err = hipGetLastError()) != hipSuccess) return err;
 
     const int dl = pf_down_lds(F, down.qtype);
-    static LdsLimit down_lds;
-    if ((err = ensure_lds(reinterpret_cast<const void*>(pf_down_kernel), down_lds, dl)) != hipSuccess)
-        return err;
+    const void* dfn = down.qtype == 2 ? reinterpret_cast<const void*>(pf_down_kernel<true>)
+                                      : reinterpret_cast<const void*>(pf_down_kernel<false>);
+    static LdsLimit down_lds6, down_lds4;
+    if ((err = ensure_lds(dfn, down.qtype == 2 ? down_lds6 : down_lds4, dl)) != hipSuccess) return err;
     float* Y = reinterpret_cast<float*>(base + L.y);
-    hipLaunchKernelGGL(pf_down_kernel, dim3((unsigned)(H / kDnOut) * slots), dim3(kDnThreads), dl, stream,
+    auto dk = down.qtype == 2 ? pf_down_kernel<true> : pf_down_kernel<false>;
+    hipLaunchKernelGGL(dk, dim3((unsigned)(H / kDnOut) * slots), dim3(kDnThreads), dl, stream,
                        reinterpret_cast<const uint16_t*>(base + L.hhi),
                        reinterpret_cast<const uint16_t*>(base + L.hlo),
                        reinterpret_cast<const float*>(base + L.hs16), F, offsets, tile_off, pairs, E,
