@@ -498,8 +498,8 @@ def prefill_bench(torch, q3, gen, layers, experts, shape, dev, cpu=None, status=
             "ffn_mfma_frac": round(flops / (ffn_us * 1e-6) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
         }
         del g, gf
-    res["note"] = ("bf16 matrix-core tiles with the activations split into bf16 pieces (3 for "
-                   "gate/up, 2 for down), so the MFMA work is 2.5x the algorithmic flops")
+    res["note"] = ("16-bit matrix-core tiles with the activations split into two pieces (fp16 "
+                   "for gate/up, bf16 for down), so the MFMA work is 2x the algorithmic flops")
     if status is not None:
         status["prefill_workspace"] = q3.expert_ffn_status(ws_f, T, H, F, E, k)
     if cpu is not None:                            # the oracle on all 512 tokens of that step

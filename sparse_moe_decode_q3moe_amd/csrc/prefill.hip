@@ -8,13 +8,15 @@
 //   1. group: (token, slot) pairs ordered by (expert, pair), per-expert
 //      offsets and tile offsets for tiles of 64 pairs (so an expert with up
 //      to 64 pairs reads its weights once);
-//   2. pieces of the hidden rows: bf16 hi + mid + lo (x to 2^-27; the
-//      gate/up outputs amplify the input's rounding most) and the f32 sum of
-//      every 16 values;
+//   2. pieces of the hidden rows: each row scaled by a power of two and
+//      split into fp16 hi + lo (x to 2^-22), with the f32 sum of every 32
+//      values and the row's 2^-s;
 //   3. gate/up: one workgroup per (128 h features, pair tile), k in stages
-//      of 128 staged through LDS one stage ahead; v_mfma_f32_16x16x32_bf16
-//      per Q4_K sub-block on exact bf16 weights 128 + 8q with each piece;
-//      h = silu(g) * u goes to the workspace in grouped row order;
+//      of 128 through two LDS stage buffers (one barrier per stage);
+//      v_mfma_f32_16x16x32_f16 per Q4_K sub-block on the exact fp16 weights
+//      1024 + sc q (the sub-block scale folded in), accumulated over the
+//      super-block and scaled by its d once; h = silu(g) * u goes to the
+//      workspace in grouped row order;
 //   4. pieces of h (hi + lo);
 //   5. down: one workgroup per (64 output rows, pair tile), Q6_K or Q4_K,
 //      the row tile of the expert's down matrix resident in LDS, h staged per
@@ -26,9 +28,11 @@
 // steps.  Workgroups are mapped so that the ones sharing a pair tile run on
 // one XCD (one L2).
 // MFMA operand layouts (checked on the device): A lane l holds row l % 16,
-// k = K (l / 16) .. + K - 1 (K = 4, 8 or 1 values for the 16-, 32-wide bf16
-// and the f32 forms); B lane l holds column l % 16 at the same k; C lane l
-// holds rows 4 (l / 16) + r, r = 0..3, column l % 16.
+// k = K (l / 16) .. + K - 1 (K = 4, 8 or 1 values for the 16- and 32-wide
+// 16-bit and the f32 forms); B lane l holds column l % 16 at the same k;
+// C lane l holds rows 4 (l / 16) + r, r = 0..3, column l % 16.
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -66,26 +70,16 @@ __device__ __forceinline__ uint32_t pf_lds_u32_a2(const uint8_t* lds, int off) {
     return __builtin_amdgcn_alignbyte(p[1], p[0], (uint32_t)(off & 3));
 }
 
-// Q4_K scale factors of one block header (d, dmin, 12 packed bytes) for
-// the 8 sub-blocks, for weights encoded as bf16 128 + 8q: s[j] = d*sc_j/8,
-// b[j] = 128*s[j] + dmin*m_j (removes the offset and applies the min).
-__device__ __forceinline__ void pf_q4k_factors_hdr(uint4 hdr, float s[8], float b[8]) {
-    const float d = half_bits_to_float(hdr.x & 0xffffu);
-    const float dmin = half_bits_to_float(hdr.x >> 16);
-    const uint32_t s0 = hdr.y, s1 = hdr.z, s2 = hdr.w;        // packed bytes 0-3, 4-7, 8-11
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        int sc, m;
-        if (j < 4) {
-            sc = (s0 >> (8 * j)) & 63;
-            m = (s1 >> (8 * j)) & 63;
-        } else {
-            const int jj = j - 4;
-            sc = ((s2 >> (8 * jj)) & 15) | (((s0 >> (8 * jj + 6)) & 3) << 4);
-            m = ((s2 >> (8 * jj + 4)) & 15) | (((s1 >> (8 * jj + 6)) & 3) << 4);
-        }
-        s[j] = 0.125f * d * (float)sc;                        // weights enter as 128 + 8q
-        b[j] = 128.f * s[j] + dmin * (float)m;
+// Q4_K 6-bit scale and min of sub-block j (0..7) from the header's 12 packed
+// bytes held as three words (bytes 0-3, 4-7, 8-11).
+__device__ __forceinline__ void pf_q4k_scale_min(uint32_t s0, uint32_t s1, uint32_t s2, int j, int& sc, int& m) {
+    if (j < 4) {
+        sc = (s0 >> (8 * j)) & 63;
+        m = (s1 >> (8 * j)) & 63;
+    } else {
+        const int jj = j - 4;
+        sc = ((s2 >> (8 * jj)) & 15) | (((s0 >> (8 * jj + 6)) & 3) << 4);
+        m = ((s2 >> (8 * jj + 4)) & 15) | (((s1 >> (8 * jj + 6)) & 3) << 4);
     }
 }
 
@@ -170,58 +164,126 @@ constexpr int kStageK = 128;
 constexpr int kXRowB = kStageK * 2 + 16;                      // 272
 constexpr int kXPieceB = kPfRows * kXRowB;                    // 17408
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4v_t __attribute__((ext_vector_type(4)));
 
 // v_mfma_f32_16x16x4_f32: A lane l holds row l % 16, k = l / 16; B lane l
-// holds column l % 16 at the same k; C as for the bf16 forms.
+// holds column l % 16 at the same k; C as for the 16-bit forms.
 __device__ __forceinline__ f32x4_t pf_mfma_f32(float a, float b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ f32x4_t pf_mfma32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+// ------------------------------------------------------ activation pieces --
+// One workgroup per hidden row t: the row scaled by a power of two 2^s_t
+// (max |x| * 2^s_t < 2^15, so no fp16 piece overflows and the low pieces of
+// small values keep their absolute precision), then split into two fp16
+// pieces, x' = hi + lo + r with |r| <= 2^-22 |x'| (hi = fp16(x'),
+// lo = fp16(x' - hi), both round to nearest even; x' - hi is exact in f32).
+// Within every 4 values the order is 0, 2, 1, 3 (the order the gate/up
+// kernel's weight operand takes from the packed nibbles).  s32: the f32 sum
+// of hi + lo over every 32 values (a Q4_K sub-block); tinv[t] = 2^-s_t.
+constexpr int kPfXThreads = 256;
+__device__ __forceinline__ uint32_t pf_f16_bits(float x) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
+}
+__global__ __launch_bounds__(kPfXThreads) void pf_xpieces_kernel(const float* __restrict__ src, int64_t H,
+                                                                 uint32_t* __restrict__ phi,
+                                                                 uint32_t* __restrict__ plo,
+                                                                 float* __restrict__ s32,
+                                                                 float* __restrict__ tinv) {
+    __shared__ float wmax[kPfXThreads / kWave];
+    const int64_t t = blockIdx.x;
+    const int tid = threadIdx.x;
+    const float4* row = reinterpret_cast<const float4*>(src + t * H);
+    const int n4 = (int)(H / 4);                              // a multiple of 64
+    float m = 0.f;
+    for (int i = tid; i < n4; i += kPfXThreads) {
+        const float4 v = row[i];
+        m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    }
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+    if ((tid & (kWave - 1)) == 0) wmax[tid / kWave] = m;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kPfXThreads / kWave; ++w) m = fmaxf(m, wmax[w]);
+    int e = 0;
+    if (m > 0.f && m <= 3.4028235e38f) (void)frexpf(m, &e);  // m < 2^e
+    const int sh = m > 0.f && m <= 3.4028235e38f ? min(max(15 - e, -126), 126) : 0;
+    const float scale = ldexpf(1.f, sh);
+    if (tid == 0) tinv[t] = ldexpf(1.f, -sh);
+    for (int i = tid; i < n4; i += kPfXThreads) {
+        const float4 v = row[i];
+        const float x[4] = {v.x * scale, v.z * scale, v.y * scale, v.w * scale};   // order 0, 2, 1, 3
+        uint32_t hb[4], lb[4];
+        float sum = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            hb[j] = pf_f16_bits(x[j]);
+            const float hf = half_bits_to_float(hb[j]);
+            lb[j] = pf_f16_bits(x[j] - hf);
+            sum += hf + half_bits_to_float(lb[j]);
+        }
+        phi[2 * (int64_t)t * (n4) + 2 * i] = hb[0] | (hb[1] << 16);
+        phi[2 * (int64_t)t * (n4) + 2 * i + 1] = hb[2] | (hb[3] << 16);
+        plo[2 * (int64_t)t * (n4) + 2 * i] = lb[0] | (lb[1] << 16);
+        plo[2 * (int64_t)t * (n4) + 2 * i + 1] = lb[2] | (lb[3] << 16);
+        sum += __shfl_xor(sum, 1, kWave);                     // 8 neighbouring threads: 32 values
+        sum += __shfl_xor(sum, 2, kWave);
+        sum += __shfl_xor(sum, 4, kWave);
+        if ((i & 7) == 0) s32[t * (H / 32) + (i >> 3)] = sum;
+    }
 }
 
-// Eight Q4_K nibbles (sub-block half h of 8 quant bytes) as bf16 128 + 8q.
-__device__ __forceinline__ bf16x8_t pf_q4k_b8(uint2 w, int h) {
-    const uint32_t v0 = (h ? (w.x >> 1) : (w.x << 3)) & 0x78787878u;
-    const uint32_t v1 = (h ? (w.y >> 1) : (w.y << 3)) & 0x78787878u;
-    const u32x4v_t r = {__builtin_amdgcn_perm(kPfBias8, v0, 0x04010400u),
-                        __builtin_amdgcn_perm(kPfBias8, v0, 0x04030402u),
-                        __builtin_amdgcn_perm(kPfBias8, v1, 0x04010400u),
-                        __builtin_amdgcn_perm(kPfBias8, v1, 0x04030402u)};
-    return __builtin_bit_cast(bf16x8_t, r);
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x4_t pf_mfma16h(f16x8_t a, f16x8_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Eight Q4_K nibbles of one sub-block (nibble h of 8 quant bytes) times the
+// sub-block's 6-bit scale sc, as the fp16 values 1024 + sc q (sc q <= 945,
+// exact): two nibbles 16 bits apart times sc in one 24-bit multiply-add whose
+// addend 0x6400 is the fp16 pattern of 1024.  k order 0, 2, 1, 3 per 4.
+__device__ __forceinline__ f16x8_t pf_q4k_f16(uint2 w, int h, uint32_t sc) {
+    constexpr uint32_t kM = 0x000f000fu, kBias = 0x64006400u;
+    const uint32_t x = h ? (w.x >> 4) : w.x, y = h ? (w.y >> 4) : w.y;
+    const u32x4v_t r = {(x & kM) * sc + kBias, ((x >> 8) & kM) * sc + kBias,
+                        (y & kM) * sc + kBias, ((y >> 8) & kM) * sc + kBias};
+    return __builtin_bit_cast(f16x8_t, r);
 }
 
 // ---------------------------------------------------------------- gate/up --
 // One workgroup per (128 h features, pair tile): 256 weight rows, gate rows
-// f0.. then up rows f0..  8 waves: wave w owns token blocks w >> 2 and
-// (w >> 2) + 2 (interleaved, so that waves w and w + 4, which share a SIMD,
-// both have work when a tile holds 32 pairs or fewer; blocks with no pairs
-// are skipped) and features 32 (w & 3)..+31 of both matrices, so
-// silu(g) * u is formed in registers and each wave reads half the tile's
-// activations per step.  Each k step covers one Q4_K sub-block
-// (v_mfma_f32_16x16x32_bf16 on exact bf16 weights 128 + 8q with each of the
-// three activation pieces) and is scaled by that sub-block's d*sc/8.  The 128
-// offset and the min, (128 s + dmin m) times each sub-block's activation sum
-// S, leave once per stage as one f32 rank-4 matrix step per tile.
-// LDS per stage: pieces hi/mid/lo [64 rows][272]; weight quant bytes as
-// planes of 8-byte pieces [chunk 2][group 4][256 rows] (each plane padded by
-// 128 bytes, so the two groups a half-wave reads land in different banks);
-// the (s, b) factors [4 sub-blocks][256 rows]; the sums S [4][64].
+// f0.. then up rows f0..  8 waves: wave w owns features 16 w..16 w + 15 of
+// both matrices and all four 16-pair token blocks (blocks with no pairs are
+// skipped), so every weight operand is built once per workgroup and
+// silu(g) * u is formed in registers.  Each k step is one Q4_K sub-block:
+// v_mfma_f32_16x16x32_f16 of the two activation pieces with the exact fp16
+// weights 1024 + sc q, accumulated over the whole super-block and scaled by
+// its d once; the 1024 offset and the min, (1024 d + dmin m) times each
+// sub-block's activation sum, leave once per stage as one f32 rank-4 matrix
+// step per tile.  Results are in the rows' 2^s scale until the epilogue.
+// LDS per stage: pieces hi/lo [64 rows][272]; weight quant bytes as planes
+// of 8-byte pieces [chunk 2][group 4][256 rows] (each plane padded by 128
+// bytes, so the two groups a half-wave reads land in different banks); per
+// row the stage's four 6-bit scales (one byte each), d, and the offsets
+// [4 sub-blocks][256 rows]; the sums [4][64]; the rows' 2^-s.
 constexpr int kGuFeat = 128;
 constexpr int kGuWRows = 2 * kGuFeat;                         // 256
 constexpr int kGuThreads = 512;
 constexpr int kGuPlaneB = kGuWRows * 8 + 128;                 // 2176
-constexpr int kGuWOff = 3 * kXPieceB;                         // 52224
-constexpr int kGuFacOff = kGuWOff + 8 * kGuPlaneB;            // 69632
-constexpr int kGuSOff = kGuFacOff + 4 * kGuWRows * 8;         // 77824
-constexpr int kGuLds = kGuSOff + 4 * kPfRows * 4;             // 78848
+constexpr int kGuWOff = 2 * kXPieceB;                         // 34816
+constexpr int kGuScOff = kGuWOff + 8 * kGuPlaneB;             // 52224
+constexpr int kGuDOff = kGuScOff + kGuWRows * 4;              // 53248
+constexpr int kGuOffOff = kGuDOff + kGuWRows * 4;             // 54272
+constexpr int kGuSOff = kGuOffOff + 4 * kGuWRows * 4;         // 58368
+constexpr int kGuBufB = kGuSOff + 4 * kPfRows * 4;            // 59392: one stage buffer
+constexpr int kGuInvOff = 2 * kGuBufB;                        // 118784
+constexpr int kGuLds = kGuInvOff + kPfRows * 4;               // 119040
 
 __global__ __launch_bounds__(kGuThreads) void pf_gateup_kernel(
-    const uint16_t* __restrict__ xhi, const uint16_t* __restrict__ xmid,
-    const uint16_t* __restrict__ xlo, const float* __restrict__ xs16, int64_t H,
+    const uint16_t* __restrict__ xhi, const uint16_t* __restrict__ xlo,
+    const float* __restrict__ xs32, const float* __restrict__ tinv, int64_t H,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_off,
     const int32_t* __restrict__ pairs, int32_t E, int32_t k, const uint8_t* __restrict__ gbase,
     int64_t gstride, const uint8_t* __restrict__ ubase, int64_t ustride, int64_t F,
@@ -238,148 +300,195 @@ __global__ __launch_bounds__(kGuThreads) void pf_gateup_kernel(
     const int64_t rowb = (H / kQK) * kQ4KBytes;               // bytes per gate/up row
     const uint8_t* gexp = gbase + (int64_t)e * gstride + f0 * rowb;
     const uint8_t* uexp = ubase + (int64_t)e * ustride + f0 * rowb;
-    const int nst = (int)(H / kStageK);
+    const int nst = (int)(H / kStageK);                       // even (H % 256 == 0)
 
-    // staging roles.  Activations: 3 pieces x 64 rows x 16 chunks of 16 B,
-    // item q = u * 512 + tid (u < 6): piece u >> 1, row tid/16 (u even) or
-    // 32 + tid/16 (u odd), chunk tid & 15.  Weights: 256 rows x 4 parts of
-    // 16 B (q = u * 512 + tid, u < 2: row q >> 2, part q & 3); headers:
-    // thread tid < 256 reads row tid's.  Sums: thread tid < 256 reads the S
-    // of row tid >> 2, sub-block tid & 3.
+    // staging roles.  Activations: 2 pieces x 64 rows x 16 chunks of 16 B,
+    // item u < 4: piece u >> 1, row tid/16 (u even) or 32 + tid/16 (u odd),
+    // chunk tid & 15.  Weights: 256 rows x 4 parts of 16 B (q = u * 512 +
+    // tid, u < 2: row q >> 2, part q & 3); headers: thread tid reads row
+    // (tid & 255)'s (threads 256.. read them again, so every wave issues the
+    // same loads).  Sums: thread tid < 256 reads the sum of row tid >> 2,
+    // sub-block tid & 3.  Every load is unconditional (rows past the tile
+    // read token 0's and are zeroed when stored), so the loop is straight-line
+    // code.
     const int ra = tid >> 4, rb2 = 32 + (tid >> 4), xc = tid & 15;
-    const int64_t toka = ra < nrows ? pairs[row0 + ra] / k : -1;
-    const int64_t tokb = rb2 < nrows ? pairs[row0 + rb2] / k : -1;
-    const int64_t toks = tid < 4 * kPfRows && (tid >> 2) < nrows ? pairs[row0 + (tid >> 2)] / k : -1;
-    uint4 rx[6], rw[2], rh;
-    float2 rs = make_float2(0.f, 0.f);
+    const bool va = ra < nrows, vb = rb2 < nrows, vs = tid < 4 * kPfRows && (tid >> 2) < nrows;
+    const int64_t toka = va ? pairs[row0 + ra] / k : 0;
+    const int64_t tokb = vb ? pairs[row0 + rb2] / k : 0;
+    const int64_t toks = vs ? pairs[row0 + (tid >> 2)] / k : 0;
+    if (tid < kPfRows)
+        reinterpret_cast<float*>(smem + kGuInvOff)[tid] = tid < nrows ? tinv[pairs[row0 + tid] / k] : 0.f;
+    uint4 rx[4], rw[2], rh;
+    float rs;
     auto wrow = [&](int r) -> const uint8_t* { return r < kGuFeat ? gexp + r * rowb : uexp + (r - kGuFeat) * rowb; };
     auto load_stage = [&](int st) {
         const int64_t k0 = (int64_t)st * kStageK;
         const int64_t sb = st >> 1;
         const int half = st & 1;
 #pragma unroll
-        for (int u = 0; u < 6; ++u) {
+        for (int u = 0; u < 4; ++u) {
             const int64_t tok = (u & 1) ? tokb : toka;
-            const uint16_t* xs = u < 2 ? xhi : u < 4 ? xmid : xlo;
-            rx[u] = tok >= 0 ? *reinterpret_cast<const uint4*>(xs + tok * H + k0 + 8 * xc)
-                             : make_uint4(0, 0, 0, 0);
+            const uint16_t* xs = u < 2 ? xhi : xlo;
+            rx[u] = *reinterpret_cast<const uint4*>(xs + tok * H + k0 + 8 * xc);
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int q = u * kGuThreads + tid;
             rw[u] = *reinterpret_cast<const uint4*>(wrow(q >> 2) + sb * kQ4KBytes + 16 + 64 * half + 16 * (q & 3));
         }
-        if (tid < kGuWRows) rh = *reinterpret_cast<const uint4*>(wrow(tid) + sb * kQ4KBytes);
-        // the sub-block's two 16-value sums, from a clamped row and added
-        // only when stored: an add here would wait for this stage's loads at
-        // once and leave nothing to overlap with the matrix work
-        const int64_t g16 = (k0 >> 4) + 2 * (tid & 3);
-        rs = *reinterpret_cast<const float2*>(xs16 + (toks >= 0 ? toks : 0) * (H / 16) + g16);
+        rh = *reinterpret_cast<const uint4*>(wrow(tid & (kGuWRows - 1)) + sb * kQ4KBytes);
+        rs = xs32[toks * (H / 32) + 4 * st + (tid & 3)];
     };
     auto store_stage = [&](int half) {
+        uint8_t* const sbuf = smem + (half ? kGuBufB : 0);   // stage st goes to buffer st & 1
 #pragma unroll
-        for (int u = 0; u < 6; ++u) {
+        for (int u = 0; u < 4; ++u) {
             const int r = (u & 1) ? rb2 : ra;
-            *reinterpret_cast<uint4*>(smem + (u >> 1) * kXPieceB + r * kXRowB + xc * 16) = rx[u];
+            const uint32_t mk = ((u & 1) ? vb : va) ? ~0u : 0u;   // (a mask, not a select of values)
+            *reinterpret_cast<uint4*>(sbuf + (u >> 1) * kXPieceB + r * kXRowB + xc * 16) =
+                make_uint4(rx[u].x & mk, rx[u].y & mk, rx[u].z & mk, rx[u].w & mk);
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int q = u * kGuThreads + tid, r = q >> 2, part = q & 3;
             const int c = part >> 1, g0 = 2 * (part & 1);         // 16 B = groups g0, g0 + 1 of chunk c
-            *reinterpret_cast<uint2*>(smem + kGuWOff + (c * 4 + g0) * kGuPlaneB + r * 8) = make_uint2(rw[u].x, rw[u].y);
-            *reinterpret_cast<uint2*>(smem + kGuWOff + (c * 4 + g0 + 1) * kGuPlaneB + r * 8) = make_uint2(rw[u].z, rw[u].w);
+            *reinterpret_cast<uint2*>(sbuf + kGuWOff + (c * 4 + g0) * kGuPlaneB + r * 8) = make_uint2(rw[u].x, rw[u].y);
+            *reinterpret_cast<uint2*>(sbuf + kGuWOff + (c * 4 + g0 + 1) * kGuPlaneB + r * 8) = make_uint2(rw[u].z, rw[u].w);
         }
         if (tid < kGuWRows) {
-            float sj[8], bj[8];
-            pf_q4k_factors_hdr(rh, sj, bj);
+            const float d = half_bits_to_float(rh.x & 0xffffu);
+            const float dmin = half_bits_to_float(rh.x >> 16);
+            uint32_t scp = 0;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                reinterpret_cast<float2*>(smem + kGuFacOff)[j * kGuWRows + tid] =
-                    half ? make_float2(sj[4 + j], bj[4 + j]) : make_float2(sj[j], bj[j]);
+            for (int jj = 0; jj < 4; ++jj) {
+                int sc, m;
+                pf_q4k_scale_min(rh.y, rh.z, rh.w, 4 * half + jj, sc, m);
+                scp |= (uint32_t)sc << (8 * jj);
+                reinterpret_cast<float*>(sbuf + kGuOffOff)[jj * kGuWRows + tid] = 1024.f * d + dmin * (float)m;
+            }
+            reinterpret_cast<uint32_t*>(sbuf + kGuScOff)[tid] = scp;
+            reinterpret_cast<float*>(sbuf + kGuDOff)[tid] = d;
         }
         if (tid < 4 * kPfRows)
-            reinterpret_cast<float*>(smem + kGuSOff)[(tid & 3) * kPfRows + (tid >> 2)] = toks >= 0 ? rs.x + rs.y : 0.f;
+            reinterpret_cast<float*>(sbuf + kGuSOff)[(tid & 3) * kPfRows + (tid >> 2)] = vs ? rs : 0.f;
     };
 
     const int col = lane & 15, g = lane >> 4;
-    const int th = wave >> 2, fq = wave & 3;
-    const int frow0 = 32 * fq + col;                          // gate rows frow0, frow0 + 16; up rows + 128
-    f32x4_t acc[2][2][2];                                     // [token block][feature block][gate, up]
+    const int frow = 16 * wave + col;                         // gate row frow, up row 128 + frow
+    f32x4_t acc[4][2], sbk[4][2];                             // [token block][gate, up]: total, this super-block
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int fb = 0; fb < 2; ++fb) {
-            acc[i][fb][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            acc[i][fb][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int m = 0; m < 2; ++m) {
+            acc[i][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            sbk[i][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
 
-    load_stage(0);
-    for (int st = 0; st < nst; ++st) {
-        __syncthreads();                                      // the previous stage is consumed
-        store_stage(st & 1);
-        __syncthreads();
-        if (st + 1 < nst) load_stage(st + 1);
-        if (16 * th >= nrows) continue;                       // both of this wave's token blocks empty
+    // the matrix work of the stage in LDS for the tile's first NTB token
+    // blocks (the rest hold no pairs; NTB is fixed per instantiation so the
+    // body has no branches and the LDS reads of later steps can be issued
+    // ahead of the matrix work); half: which half of its super-block
+    auto compute = [&](auto ntb_c, int half) __attribute__((always_inline)) {
+        constexpr int NTB = decltype(ntb_c)::value;
+        const uint8_t* const sbuf = smem + (half ? kGuBufB : 0);
+        const uint32_t scg = reinterpret_cast<const uint32_t*>(sbuf + kGuScOff)[frow];
+        const uint32_t scu = reinterpret_cast<const uint32_t*>(sbuf + kGuScOff)[kGuFeat + frow];
+        // operands of sub-block j: weight words and the NTB activation
+        // blocks' two pieces, read one sub-block ahead of its matrix steps
+        uint2 wg[2], wu[2];
+        f16x8_t ah[2][NTB], al[2][NTB];
+        auto read = [&](int j) __attribute__((always_inline)) {
+            const int c = j >> 1, b = j & 1;
+            const uint8_t* plane = sbuf + kGuWOff + (c * 4 + g) * kGuPlaneB;
+            wg[b] = *reinterpret_cast<const uint2*>(plane + frow * 8);
+            wu[b] = *reinterpret_cast<const uint2*>(plane + (kGuFeat + frow) * 8);
+#pragma unroll
+            for (int tb = 0; tb < NTB; ++tb) {
+                const int xo = (16 * tb + col) * kXRowB + (32 * j + 8 * g) * 2;
+                ah[b][tb] = *reinterpret_cast<const f16x8_t*>(sbuf + xo);
+                al[b][tb] = *reinterpret_cast<const f16x8_t*>(sbuf + kXPieceB + xo);
+            }
+        };
+        read(0);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {                         // one sub-block per k step
-            const int c = j >> 1, h = j & 1;
-            const uint8_t* plane = smem + kGuWOff + (c * 4 + g) * kGuPlaneB;
-            bf16x8_t B[2][2];
-            float fs[2][2];
+            const int b = j & 1;
+            __builtin_amdgcn_sched_barrier(0);
+            if (j + 1 < 4) read(j + 1);
+            const f16x8_t bg = pf_q4k_f16(wg[b], j & 1, (scg >> (8 * j)) & 0xffu);
+            const f16x8_t bu = pf_q4k_f16(wu[b], j & 1, (scu >> (8 * j)) & 0xffu);
 #pragma unroll
-            for (int fb = 0; fb < 2; ++fb) {
-                const int gr = frow0 + 16 * fb, ur = kGuFeat + gr;
-                B[fb][0] = pf_q4k_b8(*reinterpret_cast<const uint2*>(plane + gr * 8), h);
-                B[fb][1] = pf_q4k_b8(*reinterpret_cast<const uint2*>(plane + ur * 8), h);
-                fs[fb][0] = reinterpret_cast<const float2*>(smem + kGuFacOff)[j * kGuWRows + gr].x;
-                fs[fb][1] = reinterpret_cast<const float2*>(smem + kGuFacOff)[j * kGuWRows + ur].x;
+            for (int tb = 0; tb < NTB; ++tb) {
+                sbk[tb][0] = pf_mfma16h(ah[b][tb], bg, sbk[tb][0]);
+                sbk[tb][1] = pf_mfma16h(ah[b][tb], bu, sbk[tb][1]);
             }
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int tb = th + 2 * i;
-                if (16 * tb >= nrows) continue;               // no pairs in this token block
-                const int xo = (16 * tb + col) * kXRowB + (32 * j + 8 * g) * 2;
-                const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(smem + xo);
-                const bf16x8_t am = *reinterpret_cast<const bf16x8_t*>(smem + kXPieceB + xo);
-                const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(smem + 2 * kXPieceB + xo);
-#pragma unroll
-                for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-                    for (int m = 0; m < 2; ++m) {
-                        f32x4_t t = pf_mfma32(ah, B[fb][m], f32x4_t{0.f, 0.f, 0.f, 0.f});
-                        t = pf_mfma32(am, B[fb][m], t);
-                        t = pf_mfma32(al, B[fb][m], t);
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) acc[i][fb][m][r] += fs[fb][m] * t[r];
-                    }
+            for (int tb = 0; tb < NTB; ++tb) {
+                sbk[tb][0] = pf_mfma16h(al[b][tb], bg, sbk[tb][0]);
+                sbk[tb][1] = pf_mfma16h(al[b][tb], bu, sbk[tb][1]);
             }
         }
-        // offset and min of the stage's 4 sub-blocks: acc -= S . b, a rank-4
+        __builtin_amdgcn_sched_barrier(0);
+        // offset and min of the stage's 4 sub-blocks: acc -= S . off, a rank-4
         // product per tile, as one f32 matrix step (k = sub-block = lane / 16)
+        const float nog = -reinterpret_cast<const float*>(sbuf + kGuOffOff)[g * kGuWRows + frow];
+        const float nou = -reinterpret_cast<const float*>(sbuf + kGuOffOff)[g * kGuWRows + kGuFeat + frow];
+        const float dg = reinterpret_cast<const float*>(sbuf + kGuDOff)[frow];
+        const float du = reinterpret_cast<const float*>(sbuf + kGuDOff)[kGuFeat + frow];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            if (16 * (th + 2 * i) >= nrows) continue;
-            const float sa = reinterpret_cast<const float*>(smem + kGuSOff)[g * kPfRows + 16 * (th + 2 * i) + col];
+        for (int tb = 0; tb < NTB; ++tb) {
+            const float sa = reinterpret_cast<const float*>(sbuf + kGuSOff)[g * kPfRows + 16 * tb + col];
+            acc[tb][0] = pf_mfma_f32(sa, nog, acc[tb][0]);
+            acc[tb][1] = pf_mfma_f32(sa, nou, acc[tb][1]);
+            if (half) {                                       // the super-block is complete
 #pragma unroll
-            for (int fb = 0; fb < 2; ++fb) {
-                const int gr = frow0 + 16 * fb;
-                const float nbg = -reinterpret_cast<const float2*>(smem + kGuFacOff)[g * kGuWRows + gr].y;
-                const float nbu = -reinterpret_cast<const float2*>(smem + kGuFacOff)[g * kGuWRows + kGuFeat + gr].y;
-                acc[i][fb][0] = pf_mfma_f32(sa, nbg, acc[i][fb][0]);
-                acc[i][fb][1] = pf_mfma_f32(sa, nbu, acc[i][fb][1]);
+                for (int r = 0; r < 4; ++r) {
+                    acc[tb][0][r] += dg * sbk[tb][0][r];
+                    acc[tb][1][r] += du * sbk[tb][1][r];
+                }
+                sbk[tb][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                sbk[tb][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             }
         }
-    }
+    };
+    const int ntb = (nrows + 15) >> 4;                        // 1..4, uniform
+    // Two LDS stage buffers (stage st in buffer st & 1) and one barrier per
+    // stage: after it, stage st is in its buffer and every wave is done with
+    // stage st - 1, so the loop stores stage st + 1 (loaded a stage earlier)
+    // into the other buffer, requests stage st + 2 and multiplies stage st,
+    // one instruction stream for the three.  Past the end the requests repeat
+    // the last stage (not used), so every trip issues the same loads.
+    // the whole stage loop for NTB token blocks (one instantiation per count,
+    // so no accumulator moves where the paths would meet)
+    auto run = [&](auto ntb_c) __attribute__((always_inline)) {
+        load_stage(0);
+        store_stage(0);
+        load_stage(1);
+        for (int st = 0; st < nst; st += 2) {
+            __syncthreads();
+            store_stage(1);
+            load_stage(min(st + 2, nst - 1));
+            compute(ntb_c, 0);
+            __syncthreads();
+            if (st + 2 < nst) store_stage(0);                 // uniform
+            load_stage(min(st + 3, nst - 1));
+            compute(ntb_c, 1);
+        }
+    };
+    if (ntb == 1) run(std::integral_constant<int, 1>{});
+    else if (ntb == 2) run(std::integral_constant<int, 2>{});
+    else if (ntb == 3) run(std::integral_constant<int, 3>{});
+    else run(std::integral_constant<int, 4>{});
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-        for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * (th + 2 * i) + 4 * g + r;
-                if (t < nrows)
-                    hbuf[(row0 + t) * F + f0 + frow0 + 16 * fb] = pf_silu(acc[i][fb][0][r]) * acc[i][fb][1][r];
+        for (int r = 0; r < 4; ++r) {
+            const int t = 16 * tb + 4 * g + r;
+            if (t < nrows) {
+                const float inv = reinterpret_cast<const float*>(smem + kGuInvOff)[t];
+                hbuf[(row0 + t) * F + f0 + frow] = pf_silu(acc[tb][0][r] * inv) * (acc[tb][1][r] * inv);
             }
+        }
 }
 
 // ------------------------------------------------------------------- down --
@@ -611,7 +720,7 @@ __global__ __launch_bounds__(256) void pf_combine_kernel(const float* __restrict
 }
 
 struct PfLayout {
-    size_t counts, offsets, tile_off, pairs, xhi, xmid, xlo, xs16, h, hhi, hlo, hs16, y, total;
+    size_t counts, offsets, tile_off, pairs, xhi, xlo, xs32, tinv, h, hhi, hlo, hs16, y, total;
 };
 
 inline size_t pf_align(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -625,9 +734,9 @@ PfLayout pf_layout(int64_t T, int64_t H, int64_t F, int32_t E, int32_t k) {
     L.tile_off = o; o += pf_align((size_t)(E + 1) * 4);
     L.pairs = o;    o += pf_align(n * 4);
     L.xhi = o;      o += pf_align((size_t)T * H * 2);
-    L.xmid = o;     o += pf_align((size_t)T * H * 2);
     L.xlo = o;      o += pf_align((size_t)T * H * 2);
-    L.xs16 = o;     o += pf_align((size_t)T * (H / 16) * 4);
+    L.xs32 = o;     o += pf_align((size_t)T * (H / 32) * 4);
+    L.tinv = o;     o += pf_align((size_t)T * 4);
     L.h = o;        o += pf_align(n * F * 4);
     L.hhi = o;      o += pf_align(n * F * 2);
     L.hlo = o;      o += pf_align(n * F * 2);
@@ -663,10 +772,9 @@ hipError_t launch_prefill_ffn(const float* hidden, int64_t T, int64_t H, int64_t
     hipError_t err = launch_group_by_expert(idx, n, E, counts, offsets, pairs, stream, tile_off, kPfRows);
     if (err != hipSuccess) return err;
 
-    const int64_t xq = T * H / 4;
-    hipLaunchKernelGGL(pf_pieces_kernel<3>, dim3(pf_pieces_grid(xq)), dim3(256), 0, stream, hidden, xq,
-                       reinterpret_cast<uint32_t*>(base + L.xhi), reinterpret_cast<uint32_t*>(base + L.xmid),
-                       reinterpret_cast<uint32_t*>(base + L.xlo), reinterpret_cast<float*>(base + L.xs16));
+    hipLaunchKernelGGL(pf_xpieces_kernel, dim3((unsigned)T), dim3(kPfXThreads), 0, stream, hidden, H,
+                       reinterpret_cast<uint32_t*>(base + L.xhi), reinterpret_cast<uint32_t*>(base + L.xlo),
+                       reinterpret_cast<float*>(base + L.xs32), reinterpret_cast<float*>(base + L.tinv));
     if ((err = hipGetLastError()) != hipSuccess) return err;
 
     const unsigned slots = (unsigned)(((n + kPfRows - 1) / kPfRows + E + 7) / 8 * 8);
@@ -675,9 +783,9 @@ hipError_t launch_prefill_ffn(const float* hidden, int64_t T, int64_t H, int64_t
         return err;
     hipLaunchKernelGGL(pf_gateup_kernel, dim3((unsigned)(F / kGuFeat) * slots), dim3(kGuThreads), kGuLds,
                        stream, reinterpret_cast<const uint16_t*>(base + L.xhi),
-                       reinterpret_cast<const uint16_t*>(base + L.xmid),
                        reinterpret_cast<const uint16_t*>(base + L.xlo),
-                       reinterpret_cast<const float*>(base + L.xs16), H, offsets, tile_off, pairs, E, k,
+                       reinterpret_cast<const float*>(base + L.xs32),
+                       reinterpret_cast<const float*>(base + L.tinv), H, offsets, tile_off, pairs, E, k,
                        gate.base, gate.stride, up.base, up.stride, F, reinterpret_cast<float*>(base + L.h));
     if ((err = hipGetLastError()) != hipSuccess) return err;
 
