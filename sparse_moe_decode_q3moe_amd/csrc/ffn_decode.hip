@@ -1416,16 +1416,20 @@ __device__ __forceinline__ uint32_t stack_tag(uint32_t epoch, int l) {
 
 // 4 consecutive f32 values published as tagged words, once all carry `tag`
 // (the wave waits together; a wait that runs out ORs `bit` into the status).
+// The four words are read as two 16-byte device-coherent loads, issued and
+// waited for in one asm block (src 16-byte aligned).
 __device__ __forceinline__ float4 poll_x4(const uint64_t* src, uint32_t tag, int32_t* status, int bit) {
-    uint64_t v0, v1, v2, v3;
+    u32x4_t a, b;
     int spins = 0;
     while (true) {
-        v0 = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        v1 = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        v2 = __hip_atomic_load(src + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        v3 = __hip_atomic_load(src + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const bool ok = (uint32_t)(v0 >> 32) == tag && (uint32_t)(v1 >> 32) == tag &&
-                        (uint32_t)(v2 >> 32) == tag && (uint32_t)(v3 >> 32) == tag;
+        asm volatile(
+            "global_load_dwordx4 %0, %2, off sc1\n\t"
+            "global_load_dwordx4 %1, %2, off offset:16 sc1\n\t"
+            "s_waitcnt vmcnt(0)"
+            : "=&v"(a), "=&v"(b)
+            : "v"(src)
+            : "memory");
+        const bool ok = a.y == tag && a.w == tag && b.y == tag && b.w == tag;
         if (__all(ok)) break;
         if (++spins > kSpinLimit) {
             if (!ok) __hip_atomic_fetch_or(status, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1433,8 +1437,7 @@ __device__ __forceinline__ float4 poll_x4(const uint64_t* src, uint32_t tag, int
         }
         __builtin_amdgcn_s_sleep(1);
     }
-    return make_float4(__uint_as_float((uint32_t)v0), __uint_as_float((uint32_t)v1),
-                       __uint_as_float((uint32_t)v2), __uint_as_float((uint32_t)v3));
+    return make_float4(__uint_as_float(a.x), __uint_as_float(a.z), __uint_as_float(b.x), __uint_as_float(b.z));
 }
 
 // grid: at most one workgroup per CU (all resident at once), kFzWaves waves
@@ -1497,6 +1500,13 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_stack_kernel(
         int p = (tau < n_gu ? tau : 0) / tiles, r0 = ((tau < n_gu ? tau : 0) % tiles) * G::R;
         GuRows rows;
 
+        // the layer's loads that do not depend on x_l, issued before its wait:
+        // the norm gain and the first router unit's row values (every thread
+        // reads its float4 of the row; only the unit's column part is used)
+        const float4 g4 = reinterpret_cast<const float4*>(Ly.gain)[tid];
+        const int e_first = (wg < U ? wg : 0) / P;
+        const float4 r_first = reinterpret_cast<const float4*>(Ly.router + (int64_t)e_first * G::H)[tid];
+
         // (a0) values 4*tid .. 4*tid+3 of every token's x_l: the input for
         // layer 0, the tagged stream after it; then the layer's RMSNorm
         float4 xv[kFzMaxTokens];
@@ -1507,7 +1517,6 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_stack_kernel(
                            : poll_x4(xbuf + (int64_t)tc * G::H + 4 * tid, tag, status, 8);
         }
         {
-            const float4 g4 = reinterpret_cast<const float4*>(Ly.gain)[tid];
 #pragma unroll
             for (int t = 0; t < kFzMaxTokens; ++t) {
                 if (t < T) {
@@ -1542,7 +1551,7 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_stack_kernel(
 #pragma unroll
             for (int t = 0; t < kFzMaxTokens; ++t) acc[t] = 0.0;
             if ((4 * tid) / HP == part) {
-                const float4 r = reinterpret_cast<const float4*>(Ly.router + (int64_t)e * G::H)[tid];
+                const float4 r = u == wg ? r_first : reinterpret_cast<const float4*>(Ly.router + (int64_t)e * G::H)[tid];
 #pragma unroll
                 for (int t = 0; t < kFzMaxTokens; ++t) {
                     if (t < T) {
