@@ -802,20 +802,27 @@ template <int kThr>
 __device__ __forceinline__ void poll_pairs(const uint64_t* src, int np, int c0, uint32_t tag,
                                            int tid, u32x4_t (&v)[kPollPairs], int32_t* status,
                                            int bit) {
+    const uint64_t* p[kPollPairs];
+#pragma unroll
+    for (int i = 0; i < kPollPairs; ++i) {
+        const int pi = c0 + tid + i * kThr;
+        p[i] = src + 2 * (pi < np ? pi : np - 1);
+    }
     int spins = 0;
     while (true) {
-#pragma unroll
-        for (int i = 0; i < kPollPairs; ++i) {
-            const int pi = c0 + tid + i * kThr;
-            const uint64_t* p = src + 2 * (pi < np ? pi : np - 1);
-            asm volatile("global_load_dwordx4 %0, %1, off sc1" : "=v"(v[i]) : "v"(p) : "memory");
-        }
-        // the loads above are not known to the compiler: wait for them
-        // here, before any use of their registers
-        asm volatile("s_waitcnt vmcnt(0)"
-                     : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5])
-                     :
-                     : "memory");
+        // the six loads and the wait for them in one asm block, so no
+        // register of a load in flight is reused before it lands
+        asm volatile(
+            "global_load_dwordx4 %0, %6, off sc1\n\t"
+            "global_load_dwordx4 %1, %7, off sc1\n\t"
+            "global_load_dwordx4 %2, %8, off sc1\n\t"
+            "global_load_dwordx4 %3, %9, off sc1\n\t"
+            "global_load_dwordx4 %4, %10, off sc1\n\t"
+            "global_load_dwordx4 %5, %11, off sc1\n\t"
+            "s_waitcnt vmcnt(0)"
+            : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5])
+            : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(p[4]), "v"(p[5])
+            : "memory");
         bool ok = true;
 #pragma unroll
         for (int i = 0; i < kPollPairs; ++i)
