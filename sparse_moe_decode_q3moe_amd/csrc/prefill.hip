@@ -496,8 +496,10 @@ __global__ __launch_bounds__(kGuThreads) void pf_gateup_kernel(
 // of the down matrix (all F/256 blocks, contiguous in HBM) is staged once
 // with the first stage; the h pieces (hi, lo) and their 16-value sums are
 // staged per 128-wide k stage.  8 waves: wave w owns output rows
-// 16 (w & 3).. and token blocks w >> 2, (w >> 2) + 2 (interleaved as in the
-// gate/up kernel; empty ones skipped).  Each k step is
+// 16 (w & 3).. and, of every stage's 8 scale groups, groups 4 (w >> 2) ..
+// + 3, for all the tile's token blocks (the two waves of a row block add
+// their halves through LDS at the end), so each weight operand is built
+// once; the stage loop is instantiated per token-block count.  Each k step is
 // one 16-wide scale group (v_mfma_f32_16x16x16bf16_1k on exact bf16 weights
 // 128 + q (Q6_K) or 128 + 8q (Q4_K) with each h piece), scaled by the
 // group's factor; the offset (and the Q4_K min) times each group's h sum
@@ -517,11 +519,13 @@ __host__ __device__ inline int pf_down_hoff(int64_t F, int32_t qtype) {
 constexpr int kDnRowB = kStageK * 2 + 8;                      // 264
 constexpr int kDnPieceB = kPfRows * kDnRowB;                  // 16896
 __host__ __device__ inline int pf_down_lds(int64_t F, int32_t qtype) {
-    return pf_down_hoff(F, qtype) + 2 * kDnPieceB + 8 * kPfRows * 4;
+    return pf_down_hoff(F, qtype) + 2 * kDnPieceB + 8 * kPfRows * 4 + kPfRows * 4;   // + the rows' pair indices
 }
 
+// Q6_K: at most 128 registers, so two workgroups (76 KB of LDS each) share a
+// compute unit; the Q4_K form's scale decode needs more registers than that.
 template <bool Q6>
-__global__ __launch_bounds__(kDnThreads) void pf_down_kernel(
+__global__ __launch_bounds__(kDnThreads) __attribute__((amdgpu_waves_per_eu(Q6 ? 4 : 2))) void pf_down_kernel(
     const uint16_t* __restrict__ hhi, const uint16_t* __restrict__ hlo,
     const float* __restrict__ hs16, int64_t F, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ tile_off, const int32_t* __restrict__ pairs, int32_t E,
@@ -588,31 +592,22 @@ __global__ __launch_bounds__(kDnThreads) void pf_down_kernel(
 
     const int col = lane & 15, g = lane >> 4;
     const int orow = 16 * (wave & 3) + col;                   // this lane's output row in the tile
-    const int tb0 = wave >> 2;                                // token blocks tb0, tb0 + 2
-    f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
-    // the pair index of each output row this lane stores, read now (reading
-    // it at the store would put a memory round trip before each of them)
-    int32_t opair[2][4];
+    const int kg = wave >> 2;                                 // this wave's half of each stage's 8 groups
+    const int ntb = (nrows + 15) >> 4;                        // token blocks holding pairs (1..4), uniform
+    f32x4_t acc[4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = 16 * (tb0 + 2 * i) + 4 * g + r;
-            opair[i][r] = pairs[row0 + (t < nrows ? t : 0)];
-        }
+    for (int i = 0; i < 4; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // the tile rows' pair indices, staged in LDS now (read at the stores,
+    // each would put a memory round trip before its store)
+    int32_t* opair = reinterpret_cast<int32_t*>(smem + soff + 8 * kPfRows * 4);
+    if (tid < kPfRows) opair[tid] = pairs[row0 + (tid < nrows ? tid : 0)];
 
-    load_stage(0);
-#pragma unroll
-    for (int u = 0; u < kDnMaxW16; ++u) {
-        const int q = u * kDnThreads + tid;
-        if (q < n16) *reinterpret_cast<u32x4v_t*>(smem + 16 * q) = rwt[u];
-    }
-    for (int st = 0; st < nst; ++st) {
-        __syncthreads();
-        store_stage();
-        __syncthreads();
-        if (st + 1 < nst) load_stage(st + 1);
-        if (16 * tb0 >= nrows) continue;                      // both of this wave's token blocks empty
+    // The matrix work of stage st for the tile's first NTB token blocks: this
+    // wave's four scale groups (4 kg .. 4 kg + 3 of the stage's eight; the
+    // other wave of the row block takes the rest), each weight operand built
+    // once and used by every token block.  NTB is fixed per instantiation.
+    auto compute = [&](auto ntb_c, int st) __attribute__((always_inline)) {
+        constexpr int NTB = decltype(ntb_c)::value;
         const int sb = st >> 1, half = st & 1;
         const int boff = orow * rowb + sb * bb;               // this lane's block in the tile
         const uint8_t* blk = smem + boff;
@@ -626,7 +621,8 @@ __global__ __launch_bounds__(kDnThreads) void pf_down_kernel(
             dm = half_bits_to_float(hdr.x >> 16);
         }
 #pragma unroll
-        for (int G = 0; G < 8; ++G) {                         // one 16-wide group per k step
+        for (int G4 = 0; G4 < 4; ++G4) {                      // one 16-wide group per k step
+            const int G = 4 * kg + G4;                        // group within the stage
             const int gi = 8 * half + G;                      // group within the super-block
             uint32_t q;
             float sc;
@@ -640,51 +636,82 @@ __global__ __launch_bounds__(kDnThreads) void pf_down_kernel(
                 const int J = gi >> 1, c = J >> 1, h = J & 1, lp = 16 * (gi & 1) + 4 * g;
                 q = ((*reinterpret_cast<const uint32_t*>(blk + 16 + 32 * c + lp) >> (4 * h)) << 3) & 0x78787878u;
                 int scj, mj;
-                q4k_scale_min(blk + 4, J, scj, mj);
+                pf_q4k_scale_min(hdr.y, hdr.z, hdr.w, J, scj, mj);
                 sc = dq * (float)scj;
             }
             const s16x4_t bw = pf_bf16x4(q);
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int tb = tb0 + 2 * i;
-                if (16 * tb >= nrows) continue;               // no pairs in this token block
+            for (int tb = 0; tb < NTB; ++tb) {
                 const int xo = hoff + (16 * tb + col) * kDnRowB + (16 * G + 4 * g) * 2;
                 f32x4_t t = pf_mfma(*reinterpret_cast<const s16x4_t*>(smem + xo), bw, f32x4_t{0.f, 0.f, 0.f, 0.f});
                 t = pf_mfma(*reinterpret_cast<const s16x4_t*>(smem + kDnPieceB + xo), bw, t);
-                acc[i][0] += sc * t[0];
-                acc[i][1] += sc * t[1];
-                acc[i][2] += sc * t[2];
-                acc[i][3] += sc * t[3];
+                acc[tb][0] += sc * t[0];
+                acc[tb][1] += sc * t[1];
+                acc[tb][2] += sc * t[2];
+                acc[tb][3] += sc * t[3];
             }
         }
-        // the offset (and the Q4_K min) of the stage's 8 groups: acc -= S . off,
-        // two f32 rank-4 matrix steps per tile (k = group = 4 * p + lane / 16)
-#pragma unroll
-        for (int pq = 0; pq < 2; ++pq) {
-            const int gi = 8 * half + 4 * pq + g;             // this lane's group (its k slot)
-            float off;
-            if (q6) {
-                off = 160.f * dq * (float)(int8_t)blk[192 + gi];   // (128 + q) - 160 = q - 32
-            } else {
-                int scj, mj;
-                q4k_scale_min(blk + 4, gi >> 1, scj, mj);
-                off = 128.f * dq * (float)scj + dm * (float)mj;
-            }
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                if (16 * (tb0 + 2 * i) >= nrows) continue;
-                const float sa = reinterpret_cast<const float*>(smem + soff)[(4 * pq + g) * kPfRows + 16 * (tb0 + 2 * i) + col];
-                acc[i] = pf_mfma_f32(sa, -off, acc[i]);
-            }
+        // the offset (and the Q4_K min) of this wave's 4 groups: acc -= S . off,
+        // one f32 rank-4 matrix step per token block (k = group = lane / 16)
+        const int gi = 8 * half + 4 * kg + g;                 // this lane's group (its k slot)
+        float off;
+        if (q6) {
+            off = 160.f * dq * (float)(int8_t)blk[192 + gi];  // (128 + q) - 160 = q - 32
+        } else {
+            int scj, mj;
+            pf_q4k_scale_min(hdr.y, hdr.z, hdr.w, gi >> 1, scj, mj);
+            off = 128.f * dq * (float)scj + dm * (float)mj;
         }
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb) {
+            const float sa = reinterpret_cast<const float*>(smem + soff)[(4 * kg + g) * kPfRows + 16 * tb + col];
+            acc[tb] = pf_mfma_f32(sa, -off, acc[tb]);
+        }
+    };
+    auto run = [&](auto ntb_c) __attribute__((always_inline)) {
+        for (int st = 0; st < nst; ++st) {
+            __syncthreads();
+            store_stage();
+            __syncthreads();
+            if (st + 1 < nst) load_stage(st + 1);
+            compute(ntb_c, st);
+        }
+    };
+
+    load_stage(0);
+#pragma unroll
+    for (int u = 0; u < kDnMaxW16; ++u) {
+        const int q = u * kDnThreads + tid;
+        if (q < n16) *reinterpret_cast<u32x4v_t*>(smem + 16 * q) = rwt[u];
     }
+    if (ntb == 1) run(std::integral_constant<int, 1>{});
+    else if (ntb == 2) run(std::integral_constant<int, 2>{});
+    else if (ntb == 3) run(std::integral_constant<int, 3>{});
+    else run(std::integral_constant<int, 4>{});
+
+    // waves 4-7 hand their half of each row's sums to waves 0-3 through LDS
+    // (the h staging area, free after the last stage), which add and store
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(smem + hoff);      // [row block][tb][r][lane]
+    if (kg == 1) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+        for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = 16 * (tb0 + 2 * i) + 4 * g + r;
-            if (t < nrows) Y[(int64_t)opair[i][r] * H + h0 + orow] = acc[i][r];
-        }
+            for (int r = 0; r < 4; ++r)
+                if (tb < ntb) red[(((wave & 3) * 4 + tb) * 4 + r) * kWave + lane] = acc[tb][r];
+    }
+    __syncthreads();
+    if (kg == 0) {
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * tb + 4 * g + r;
+                if (t < nrows)
+                    Y[(int64_t)opair[t] * H + h0 + orow] =
+                        acc[tb][r] + red[(((wave & 3) * 4 + tb) * 4 + r) * kWave + lane];
+            }
+    }
 }
 
 // ---------------------------------------------------------------- combine --
