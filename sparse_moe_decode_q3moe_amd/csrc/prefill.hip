@@ -318,10 +318,11 @@ __global__ __launch_bounds__(kGuThreads) void pf_gateup_kernel(
     const int64_t toks = vs ? pairs[row0 + (tid >> 2)] / k : 0;
     if (tid < kPfRows)
         reinterpret_cast<float*>(smem + kGuInvOff)[tid] = tid < nrows ? tinv[pairs[row0 + tid] / k] : 0.f;
-    uint4 rx[4], rw[2], rh;
-    float rs;
     auto wrow = [&](int r) -> const uint8_t* { return r < kGuFeat ? gexp + r * rowb : uexp + (r - kGuFeat) * rowb; };
-    auto load_stage = [&](int st) {
+    // a stage's operands in registers: activation chunks, weight quant
+    // chunks, the block header, the sub-block sum
+    auto load_stage = [&](uint4 (&rx)[4], uint4 (&rw)[2], uint4& rh, float& rs, int st)
+                          __attribute__((always_inline)) {
         const int64_t k0 = (int64_t)st * kStageK;
         const int64_t sb = st >> 1;
         const int half = st & 1;
@@ -339,7 +340,8 @@ __global__ __launch_bounds__(kGuThreads) void pf_gateup_kernel(
         rh = *reinterpret_cast<const uint4*>(wrow(tid & (kGuWRows - 1)) + sb * kQ4KBytes);
         rs = xs32[toks * (H / 32) + 4 * st + (tid & 3)];
     };
-    auto store_stage = [&](int half) {
+    auto store_stage = [&](const uint4 (&rx)[4], const uint4 (&rw)[2], const uint4& rh, const float& rs,
+                           int half) __attribute__((always_inline)) {
         uint8_t* const sbuf = smem + (half ? kGuBufB : 0);   // stage st goes to buffer st & 1
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -452,27 +454,35 @@ __global__ __launch_bounds__(kGuThreads) void pf_gateup_kernel(
         }
     };
     const int ntb = (nrows + 15) >> 4;                        // 1..4, uniform
-    // Two LDS stage buffers (stage st in buffer st & 1) and one barrier per
-    // stage: after it, stage st is in its buffer and every wave is done with
-    // stage st - 1, so the loop stores stage st + 1 (loaded a stage earlier)
-    // into the other buffer, requests stage st + 2 and multiplies stage st,
-    // one instruction stream for the three.  Past the end the requests repeat
-    // the last stage (not used), so every trip issues the same loads.
-    // the whole stage loop for NTB token blocks (one instantiation per count,
-    // so no accumulator moves where the paths would meet)
+    // Two LDS stage buffers (stage st in buffer st & 1), one barrier per
+    // stage and two stages in flight in registers (odd stages in set A, even
+    // ones in set B): after the barrier before stage st's matrix work, stage
+    // st is in its buffer and every wave is done with stage st - 1; stage
+    // st + 1 (loaded two stages earlier) goes into the other buffer, stage
+    // st + 3 is requested into the registers that held it, and stage st is
+    // multiplied.  Past the end the requests repeat the last stage and the
+    // stores fill the free buffer (not read), so every trip issues the same
+    // loads and stores.
     auto run = [&](auto ntb_c) __attribute__((always_inline)) {
-        load_stage(0);
-        store_stage(0);
-        load_stage(1);
+        uint4 rxA[4], rwA[2], rhA, rxB[4], rwB[2], rhB;
+        float rsA, rsB;
+        load_stage(rxA, rwA, rhA, rsA, 0);
+        store_stage(rxA, rwA, rhA, rsA, 0);
+        load_stage(rxA, rwA, rhA, rsA, min(1, nst - 1));
+        load_stage(rxB, rwB, rhB, rsB, min(2, nst - 1));
+        __syncthreads();
+        store_stage(rxA, rwA, rhA, rsA, 1);
+        // (the trip starts where only set B's loads are outstanding, so the
+        // waits at the loop head count the same on both of its entries)
         for (int st = 0; st < nst; st += 2) {
-            __syncthreads();
-            store_stage(1);
-            load_stage(min(st + 2, nst - 1));
+            load_stage(rxA, rwA, rhA, rsA, min(st + 3, nst - 1));
             compute(ntb_c, 0);
             __syncthreads();
-            if (st + 2 < nst) store_stage(0);                 // uniform
-            load_stage(min(st + 3, nst - 1));
+            store_stage(rxB, rwB, rhB, rsB, 0);
+            load_stage(rxB, rwB, rhB, rsB, min(st + 4, nst - 1));
             compute(ntb_c, 1);
+            __syncthreads();
+            store_stage(rxA, rwA, rhA, rsA, 1);
         }
     };
     if (ntb == 1) run(std::integral_constant<int, 1>{});
