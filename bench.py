@@ -82,8 +82,8 @@ PMC_STEPS = 16
 # in profiles/ffn_fused8_kernel_a3b_decode_b1_traffic.md.  The figure belongs
 # to the kernel sources it was measured on; when they change it is reported
 # as null until the counters are taken again.
-TRAFFIC_BYTES_PER_LAUNCH = 26_816_873
-TRAFFIC_SOURCES_SHA256 = "369c05259f4c767e2a2dd4e5aac809241a17b7a691d6d6e483ae45c0fadeaa9e"
+TRAFFIC_BYTES_PER_LAUNCH = 26_819_437
+TRAFFIC_SOURCES_SHA256 = "470c0d3b0c9e5cffd9300bed98172ad9992b69c05a5ed3320ceec3da2faee157"
 TRAFFIC_SOURCES = ("sparse_moe_decode_q3moe_amd/csrc/ffn_decode.hip",
                    "sparse_moe_decode_q3moe_amd/csrc/route_common.h",
                    "sparse_moe_decode_q3moe_amd/csrc/device_common.h")
