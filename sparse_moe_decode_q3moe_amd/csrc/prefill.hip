@@ -16,13 +16,13 @@
 //      v_mfma_f32_16x16x32_f16 per Q4_K sub-block on the exact fp16 weights
 //      1024 + sc q (the sub-block scale folded in), accumulated over the
 //      super-block and scaled by its d once; h = silu(g) * u goes to the
-//      workspace in grouped row order;
-//   4. pieces of h (hi + lo);
-//   5. down: one workgroup per (64 output rows, pair tile), Q6_K or Q4_K,
+//      workspace in grouped row order as two bf16 pieces (hi + lo) with the
+//      f32 sum of every 16 values;
+//   4. down: one workgroup per (64 output rows, pair tile), Q6_K or Q4_K,
 //      the row tile of the expert's down matrix resident in LDS, h staged per
 //      128-wide stage; v_mfma_f32_16x16x16bf16_1k per 16-wide scale group;
 //      rows go to Y indexed by pair;
-//   6. combine: out[t] = [out +] sum over slots in slot order of w * Y.
+//   5. combine: out[t] = [out +] sum over slots in slot order of w * Y.
 // In both matrix kernels the weights' offset (and the Q4_K min) times the
 // activation sums leaves once per stage as v_mfma_f32_16x16x4_f32 rank-4
 // steps.  Workgroups are mapped so that the ones sharing a pair tile run on
@@ -80,48 +80,6 @@ __device__ __forceinline__ void pf_q4k_scale_min(uint32_t s0, uint32_t s1, uint3
         const int jj = j - 4;
         sc = ((s2 >> (8 * jj)) & 15) | (((s0 >> (8 * jj + 6)) & 3) << 4);
         m = ((s2 >> (8 * jj + 4)) & 15) | (((s1 >> (8 * jj + 6)) & 3) << 4);
-    }
-}
-
-// ---------------------------------------------------------------- pieces --
-// rows x cols f32 (cols % 16 == 0) -> NP bf16 piece arrays [rows][cols]
-// (each round-to-nearest-even of what the previous leave: |x - sum| <=
-// 2^-18 |x| for two pieces, 2^-27 |x| for three) and s16 f32 [rows][cols/16],
-// the sums of the pieces per 16 values.  One float4 per thread per step; 4
-// neighbouring threads make one 16-value group.
-template <int NP>
-__global__ __launch_bounds__(256) void pf_pieces_kernel(const float* __restrict__ src, int64_t n4,
-                                                        uint32_t* __restrict__ p0,
-                                                        uint32_t* __restrict__ p1,
-                                                        uint32_t* __restrict__ p2,
-                                                        float* __restrict__ s16) {
-    const int64_t step = (int64_t)gridDim.x * 256;
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += step) {
-        const float4 v = reinterpret_cast<const float4*>(src)[i];
-        const float x[4] = {v.x, v.y, v.z, v.w};
-        uint32_t b[NP][4];
-        float sum = 0.f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            float r = x[j], part = 0.f;
-#pragma unroll
-            for (int q = 0; q < NP; ++q) {
-                b[q][j] = bf16_rne_bits(r);
-                const float f = bf16_bits_to_float(b[q][j]);
-                r -= f;
-                part += f;
-            }
-            sum += part;
-        }
-        float g = sum + __shfl_xor(sum, 1, kWave);           // n4 % 4 == 0: quads stay together
-        g += __shfl_xor(g, 2, kWave);
-        uint32_t* dst[3] = {p0, p1, p2};
-#pragma unroll
-        for (int q = 0; q < NP; ++q) {
-            dst[q][2 * i] = b[q][0] | (b[q][1] << 16);
-            dst[q][2 * i + 1] = b[q][2] | (b[q][3] << 16);
-        }
-        if ((i & 3) == 0) s16[i >> 2] = g;
     }
 }
 
@@ -287,7 +245,7 @@ __global__ __launch_bounds__(kGuThreads) void pf_gateup_kernel(
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_off,
     const int32_t* __restrict__ pairs, int32_t E, int32_t k, const uint8_t* __restrict__ gbase,
     int64_t gstride, const uint8_t* __restrict__ ubase, int64_t ustride, int64_t F,
-    float* __restrict__ hbuf) {
+    uint16_t* __restrict__ hhi, uint16_t* __restrict__ hlo, float* __restrict__ hs16) {
     extern __shared__ __align__(16) uint8_t smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     int slot, ftile;
@@ -489,16 +447,36 @@ __global__ __launch_bounds__(kGuThreads) void pf_gateup_kernel(
     else if (ntb == 2) run(std::integral_constant<int, 2>{});
     else if (ntb == 3) run(std::integral_constant<int, 3>{});
     else run(std::integral_constant<int, 4>{});
+    // h = silu(g) * u of the tile's rows, leaving as the down kernel's input:
+    // two bf16 pieces (hi = bf16(h), lo = bf16(h - hi)) and the f32 sum of
+    // hi + lo over each 16 consecutive features (this wave's 16, held by the
+    // 16 lanes of a lane row)
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
+    for (int tb = 0; tb < 4; ++tb) {
+        if (16 * tb >= nrows) continue;                       // uniform
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = 16 * tb + 4 * g + r;
+            float hv = 0.f;
             if (t < nrows) {
                 const float inv = reinterpret_cast<const float*>(smem + kGuInvOff)[t];
-                hbuf[(row0 + t) * F + f0 + frow] = pf_silu(acc[tb][0][r] * inv) * (acc[tb][1][r] * inv);
+                hv = pf_silu(acc[tb][0][r] * inv) * (acc[tb][1][r] * inv);
+            }
+            const uint32_t hb = bf16_rne_bits(hv);
+            const uint32_t lb = bf16_rne_bits(hv - bf16_bits_to_float(hb));
+            float sp = bf16_bits_to_float(hb) + bf16_bits_to_float(lb);
+            sp += __shfl_xor(sp, 1, kWave);
+            sp += __shfl_xor(sp, 2, kWave);
+            sp += __shfl_xor(sp, 4, kWave);
+            sp += __shfl_xor(sp, 8, kWave);
+            if (t < nrows) {
+                const int64_t o = (row0 + t) * F + f0 + frow;
+                hhi[o] = (uint16_t)hb;
+                hlo[o] = (uint16_t)lb;
+                if (col == 0) hs16[(row0 + t) * (F / 16) + (f0 >> 4) + wave] = sp;
             }
         }
+    }
 }
 
 // ------------------------------------------------------------------- down --
@@ -757,7 +735,7 @@ __global__ __launch_bounds__(256) void pf_combine_kernel(const float* __restrict
 }
 
 struct PfLayout {
-    size_t counts, offsets, tile_off, pairs, xhi, xlo, xs32, tinv, h, hhi, hlo, hs16, y, total;
+    size_t counts, offsets, tile_off, pairs, xhi, xlo, xs32, tinv, hhi, hlo, hs16, y, total;
 };
 
 inline size_t pf_align(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -774,7 +752,6 @@ PfLayout pf_layout(int64_t T, int64_t H, int64_t F, int32_t E, int32_t k) {
     L.xlo = o;      o += pf_align((size_t)T * H * 2);
     L.xs32 = o;     o += pf_align((size_t)T * (H / 32) * 4);
     L.tinv = o;     o += pf_align((size_t)T * 4);
-    L.h = o;        o += pf_align(n * F * 4);
     L.hhi = o;      o += pf_align(n * F * 2);
     L.hlo = o;      o += pf_align(n * F * 2);
     L.hs16 = o;     o += pf_align(n * (F / 16) * 4);
@@ -783,10 +760,6 @@ PfLayout pf_layout(int64_t T, int64_t H, int64_t F, int32_t E, int32_t k) {
     return L;
 }
 
-unsigned pf_pieces_grid(int64_t n4) {
-    const int64_t blocks = (n4 + 255) / 256;
-    return (unsigned)(blocks < 4096 ? (blocks > 0 ? blocks : 1) : 4096);
-}
 
 }  // namespace
 
@@ -823,14 +796,8 @@ hipError_t launch_prefill_ffn(const float* hidden, int64_t T, int64_t H, int64_t
                        reinterpret_cast<const uint16_t*>(base + L.xlo),
                        reinterpret_cast<const float*>(base + L.xs32),
                        reinterpret_cast<const float*>(base + L.tinv), H, offsets, tile_off, pairs, E, k,
-                       gate.base, gate.stride, up.base, up.stride, F, reinterpret_cast<float*>(base + L.h));
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-
-    const int64_t hq = n * F / 4;
-    hipLaunchKernelGGL(pf_pieces_kernel<2>, dim3(pf_pieces_grid(hq)), dim3(256), 0, stream,
-                       reinterpret_cast<const float*>(base + L.h), hq,
-                       reinterpret_cast<uint32_t*>(base + L.hhi), reinterpret_cast<uint32_t*>(base + L.hlo),
-                       nullptr, reinterpret_cast<float*>(base + L.hs16));
+                       gate.base, gate.stride, up.base, up.stride, F, reinterpret_cast<uint16_t*>(base + L.hhi),
+                       reinterpret_cast<uint16_t*>(base + L.hlo), reinterpret_cast<float*>(base + L.hs16));
     if ((err = hipGetLastError()) != hipSuccess) return err;
 
     const int dl = pf_down_lds(F, down.qtype);
