@@ -140,95 +140,77 @@ __global__ __launch_bounds__(kRouteThreads) void route_small_kernel(
 }
 
 // ------------------------------------------------------------- T > 8 --
-// grid: (ceil(E / 4), ceil(T / 8)).  A workgroup computes the logits of 4
-// experts x 8 tokens: each thread takes float4 columns i = tid, tid + 256,
-// ... of the 4 router rows and the 8 token rows and accumulates the 32
-// exact f32 x f32 products per column in double (32 independent sums); the
-// wave then folds its 32 sums over its 64 lanes with a transposed butterfly
-// (lanes 2v, 2v + 1 end with sum v), and the 4 waves' results are added in
-// a fixed order.  Each router row is read once per 8 tokens and each token
-// row once per 4 experts (an expert x 8-token tile read the token rows once
-// per expert: ~590 MB of L2 reads at 512 tokens instead of ~200 MB).
-constexpr int kRtExp = 4, kRtTok = 8;
-constexpr int kRtV = kRtExp * kRtTok;          // 32 sums per thread
+// grid: (ceil(E / 16), ceil(T / 16)), 16 waves.  A workgroup computes the
+// logits of 16 tokens x 16 experts on the matrix cores in double:
+// v_mfma_f64_16x16x4_f64 with the token rows as A and the router rows as B,
+// both converted from f32 (each product of two f32 values is exact in
+// double and the matrix unit accumulates in double).  The H columns go in
+// 16-column chunks, chunk c to wave c % 16; a wave requests its chunks 8 at
+// a time and feeds them to 4 independent accumulator chains (chain j % 4
+// for the j-th of the 8), so the loads are in flight together and no step
+// waits for the previous one; the chains, then the 16 waves, are added in
+// a fixed order.  Per chunk a lane loads one float4 of its token row and one
+// of its router row (lane l: row l % 16, columns 4 (l / 16) .. + 3 of the
+// chunk) and feeds them to 4 matrix steps, step s taking column 4 (l / 16)
+// + s: A and B use the same lane-to-k pairing, so every product pairs
+// x[t][c] with R[e][c].  Columns past H (a last partial chunk, H % 16 != 0)
+// and chunks past the end read column 0 and enter as zeros; rows past T or
+// E read the last valid row and their sums are not stored.
+// f64 16x16x4 layout (checked on the device): A lane l holds row l % 16 at
+// k = l / 16, B lane l column l % 16 at the same k, and result value i of
+// lane l is row 4 i + l / 16, column l % 16.
+constexpr int kRtTile = 16;
+constexpr int kRtWaves = 16;
+constexpr int kRtThreads = kRtWaves * kWave;
+constexpr int kRtBatch = 8;
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
 
-// Sum of v[0..32) over the 64 lanes, transposed: lanes 2j and 2j + 1 end
-// with the total of value j.
-__device__ __forceinline__ double transposed_sum32_f64(double (&v)[kRtV], int lane) {
-#pragma unroll
-    for (int lev = 0; lev < 5; ++lev) {
-        const int half = kRtV >> (lev + 1);
-        const int bit = 5 - lev;
-        const bool up = (lane >> bit) & 1;
-        const uint64_t m = up ? ~0ull : 0ull;
-#pragma unroll
-        for (int i = 0; i < half; ++i) {
-            // the selects act on the values' bits: a select between two
-            // array elements would become a select between their addresses
-            // and keep the array out of registers
-            const uint64_t a = __builtin_bit_cast(uint64_t, v[i]);
-            const uint64_t b = __builtin_bit_cast(uint64_t, v[i + half]);
-            const double send = __builtin_bit_cast(double, (a & m) | (b & ~m));
-            const double keep = __builtin_bit_cast(double, (b & m) | (a & ~m));
-            v[i] = keep + __shfl_xor(send, 1 << bit, kWave);
-        }
-    }
-    return v[0] + __shfl_xor(v[0], 1, kWave);
-}
-
-__global__ __launch_bounds__(kRouteThreads) void router_tile_kernel(
+__global__ __launch_bounds__(kRtThreads) void router_tile_kernel(
     const float* __restrict__ hidden, int64_t T, int64_t H, const float* __restrict__ router,
     int32_t E, double* __restrict__ logits) {
-    const int64_t e0 = (int64_t)blockIdx.x * kRtExp, t0 = (int64_t)blockIdx.y * kRtTok;
+    const int64_t e0 = (int64_t)blockIdx.x * kRtTile, t0 = (int64_t)blockIdx.y * kRtTile;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t n4 = H / 4;
-    const float4* r4 = reinterpret_cast<const float4*>(router);
-    const float4* x4 = reinterpret_cast<const float4*>(hidden);
-    // rows past E or T read the last valid row and are multiplied by zero
-    double rkeep[kRtExp], xkeep[kRtTok];
-    int64_t rrow[kRtExp], xrow[kRtTok];
+    const int r = lane & 15, q = lane >> 4;
+    const int64_t t = t0 + r < T ? t0 + r : T - 1, e = e0 + r < E ? e0 + r : E - 1;
+    const float* xrow = hidden + t * H;
+    const float* rrow = router + e * H;
+    const int64_t nch = (H + 15) / 16;
+    f64x4_t acc[4];
 #pragma unroll
-    for (int e = 0; e < kRtExp; ++e) {
-        rkeep[e] = e0 + e < E ? 1.0 : 0.0;
-        rrow[e] = (e0 + e < E ? e0 + e : E - 1) * n4;
-    }
+    for (int j = 0; j < 4; ++j) acc[j] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+    for (int64_t c0 = wave; c0 < nch; c0 += (int64_t)kRtWaves * kRtBatch) {
+        float4 xv[kRtBatch], rv[kRtBatch];
+        bool in[kRtBatch];
 #pragma unroll
-    for (int t = 0; t < kRtTok; ++t) {
-        xkeep[t] = t0 + t < T ? 1.0 : 0.0;
-        xrow[t] = (t0 + t < T ? t0 + t : T - 1) * n4;
-    }
-    double acc[kRtV];
+        for (int j = 0; j < kRtBatch; ++j) {
+            const int64_t c = c0 + (int64_t)j * kRtWaves;
+            in[j] = c < nch && 16 * c + 4 * q < H;
+            const int64_t col = in[j] ? 16 * c + 4 * q : 0;
+            xv[j] = *reinterpret_cast<const float4*>(xrow + col);
+            rv[j] = *reinterpret_cast<const float4*>(rrow + col);
+        }
 #pragma unroll
-    for (int i = 0; i < kRtV; ++i) acc[i] = 0.0;
-    for (int64_t i = tid; i < n4; i += kRouteThreads) {
-        float4 rv[kRtExp], xv[kRtTok];
-#pragma unroll
-        for (int e = 0; e < kRtExp; ++e) rv[e] = r4[rrow[e] + i];
-#pragma unroll
-        for (int t = 0; t < kRtTok; ++t) xv[t] = x4[xrow[t] + i];
-#pragma unroll
-        for (int e = 0; e < kRtExp; ++e) {
-            const double rx = (double)rv[e].x * rkeep[e], ry = (double)rv[e].y * rkeep[e];
-            const double rz = (double)rv[e].z * rkeep[e], rw = (double)rv[e].w * rkeep[e];
-#pragma unroll
-            for (int t = 0; t < kRtTok; ++t) {
-                double a = fma(rx, (double)xv[t].x * xkeep[t], acc[e * kRtTok + t]);
-                a = fma(ry, (double)xv[t].y * xkeep[t], a);
-                a = fma(rz, (double)xv[t].z * xkeep[t], a);
-                acc[e * kRtTok + t] = fma(rw, (double)xv[t].w * xkeep[t], a);
-            }
+        for (int j = 0; j < kRtBatch; ++j) {
+            const float4 x = in[j] ? xv[j] : make_float4(0.f, 0.f, 0.f, 0.f);
+            const float4 w = in[j] ? rv[j] : make_float4(0.f, 0.f, 0.f, 0.f);
+            acc[j & 3] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)x.x, (double)w.x, acc[j & 3], 0, 0, 0);
+            acc[j & 3] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)x.y, (double)w.y, acc[j & 3], 0, 0, 0);
+            acc[j & 3] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)x.z, (double)w.z, acc[j & 3], 0, 0, 0);
+            acc[j & 3] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)x.w, (double)w.w, acc[j & 3], 0, 0, 0);
         }
     }
-    __shared__ double part[kRouteWaves][kRtV];
-    const double ws = transposed_sum32_f64(acc, lane);
-    if ((lane & 1) == 0) part[wave][lane >> 1] = ws;
-    __syncthreads();
-    if (tid < kRtV) {
-        double s = 0.0;
+    const f64x4_t tot = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    __shared__ double part[kRtWaves][4][kWave];
 #pragma unroll
-        for (int w = 0; w < kRouteWaves; ++w) s += part[w][tid];
-        const int64_t e = e0 + tid / kRtTok, t = t0 + tid % kRtTok;
-        if (e < E && t < T) logits[t * E + e] = s;
+    for (int i = 0; i < 4; ++i) part[wave][i][lane] = tot[i];
+    __syncthreads();
+    if (tid < 4 * kWave) {                                    // value i = tid / 64 of lane tid % 64
+        const int i = tid >> 6, l = tid & 63;
+        double sum = 0.0;
+#pragma unroll
+        for (int w = 0; w < kRtWaves; ++w) sum += part[w][i][l];
+        const int64_t tt = t0 + 4 * i + (l >> 4), ee = e0 + (l & 15);
+        if (tt < T && ee < E) logits[tt * E + ee] = sum;
     }
 }
 
@@ -259,8 +241,8 @@ hipError_t launch_route_nper(const float* hidden, int64_t T, int64_t H, const fl
                            stream, hidden, (int32_t)T, H, router, E, k, idx, w, sync, logits);
         return hipGetLastError();
     }
-    dim3 g1((unsigned)((E + kRtExp - 1) / kRtExp), (unsigned)((T + kRtTok - 1) / kRtTok));
-    hipLaunchKernelGGL(router_tile_kernel, g1, dim3(kRouteThreads), 0, stream, hidden, T, H,
+    dim3 g1((unsigned)((E + kRtTile - 1) / kRtTile), (unsigned)((T + kRtTile - 1) / kRtTile));
+    hipLaunchKernelGGL(router_tile_kernel, g1, dim3(kRtThreads), 0, stream, hidden, T, H,
                        router, E, logits);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;

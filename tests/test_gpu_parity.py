@@ -46,6 +46,8 @@ ROUTE_CASES = [  # (T, H, E, k, seed)
     (11, 512, 1024, 32, 23),  # maximum E and k, two kernels
     (6, 512, 64, 8, 24),      # one logit per lane
     (2, 256, 1, 1, 25),       # a single expert
+    (21, 2052, 100, 6, 26),   # two kernels: partial column chunk, expert and token tiles
+    (33, 36, 20, 4, 27),      # two kernels: fewer column chunks than waves
 ]
 
 
