@@ -445,9 +445,11 @@ q3moe_status q3moe_rmsnorm(const float *x, int64_t T, int64_t n, const float *ga
 /* y[t][n] = (accumulate ? y[t][n] : 0) + sum_k W[n][k] * x[t][k].
  *   W [N x K] bf16 (raw bits, row-major), 16-byte aligned; x [T x K] f32,
  *   16-byte aligned; y [T x N] f32 (must not overlap W or x).
- * Up to 63 tokens: products and sums are formed in f32 (each bf16 weight is
- * exact in f32), the weights read once per 16 tokens.  From 64 tokens on
- * (and K % 64 == 0) a matrix-core GEMM: x enters as two bf16 pieces (x to
+ * Up to 8 tokens (and for K not a multiple of 256 or above 4096, up to 63):
+ * products and sums are formed in f32 (each bf16 weight is exact in f32),
+ * the weights read once per 16 tokens.  From 9 tokens with K % 256 == 0 and
+ * K <= 4096, a matrix-core GEMV in passes of 16 tokens, and from 64 tokens
+ * on (K % 64 == 0) a matrix-core GEMM: x enters as two bf16 pieces (x to
  * 2^-17 relative), products exact, sums in f32.
  * Limits: K % 8 == 0, 8 <= K <= 2^30, 1 <= N <= 2^30, accumulate 0 or 1.
  * Errors: E_NULL, E_SHAPE, E_ALIGN, E_ALIAS, E_HIP. */
@@ -465,8 +467,13 @@ q3moe_status q3moe_bf16_gemv(const uint16_t *W, int64_t N, int64_t K, const floa
  * q3moe_bf16_gemv.  W0..W2, x and norm_gain 16-byte aligned; outputs 4-byte
  * aligned and overlapping no input or each other.
  * Without the norm, 64 tokens or more take the matrix-core GEMM of
- * q3moe_bf16_gemv, all matrices in one launch; with it, the GEMV form (for a
- * prompt, run q3moe_rmsnorm first and this call without the norm).
+ * q3moe_bf16_gemv, all matrices in one launch.  From 9 tokens with
+ * K % 256 == 0 and K <= 4096 (with the norm also beyond 63 tokens) the
+ * matrix-core GEMV of q3moe_bf16_gemv runs all matrices in one launch per
+ * 16 tokens; with the norm it splits gain * x (rounded once to f32) into
+ * the two pieces and scales each token's sums by its 1 / rms (squares summed
+ * in double) in double, which agrees with normalising first to the pieces'
+ * 2^-17.
  * Limits: as q3moe_bf16_gemv for each matrix; with the norm, K <= 16384 and
  * eps >= 0 and finite.
  * Errors: E_NULL, E_SHAPE, E_ALIGN, E_ALIAS, E_HIP. */

@@ -343,6 +343,174 @@ hipError_t launch_gemv_job(const GvJob& job, int64_t K, const float* x, int64_t 
     return launch_gemv_tt<16>(job, K, x, T, accumulate, stream);
 }
 
+// ------------------------------------------------- GEMV, matrix cores --
+// bf16_gemv_mt_kernel: the same product for 9 or more tokens, 16 per pass,
+// on v_mfma_f32_16x16x32_bf16, for K a multiple of 256 up to 4096.  A
+// workgroup owns one block of 16 rows and all of k: K / 256 waves, each
+// taking 256 consecutive k as 8 steps of 32.  The weights are the A operand
+// straight from memory (lane l: row l % 16, the 8 weights at
+// k = 32 s + 8 (l / 16) of step s; all 8 steps requested at once, after the
+// activations); the activations are the B operand (lane l: token l % 16 at
+// the same k), read as f32 and split in registers into two bf16 pieces,
+// hi = bf16(v), lo = bf16(v - hi) (|v - hi - lo| <= 2^-17 |v|), so each
+// product pair is exact and the sums run in f32.  With the input RMSNorm
+// v = gain * x (rounded once to f32), and each token's 1 / rms (squares of
+// x summed in double as the values arrive) scales that token's sums at the
+// end, in double.  The waves' 16 x 16 partial tiles meet in LDS and are
+// added in wave order.
+constexpr int kMtSteps = 8;                          // 32-k steps per wave
+constexpr int kMtWaveK = kMtSteps * 32;              // 256
+constexpr int kMtMaxWaves = 16;                      // K <= 4096
+constexpr int64_t kMtMinTokens = 9;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+struct MtJob {
+    const uint16_t* W[3];
+    float* y[3];
+    int64_t N[3];
+    int tile_end[3];            // cumulative 16-row tile counts
+    const float* gain;          // the input RMSNorm's gain, or null
+    float eps;
+};
+
+// two f32 values -> (hi, lo) bf16 pairs, round to nearest even
+__device__ __forceinline__ void mt_split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+    const f32x2_t v = {a, b};
+    hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+    const f32x2_t r = {a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u)};
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2_t));
+}
+
+// grid: the matrices' 16-row tiles; block: K / 256 waves.  x, W, gain
+// 16-byte aligned; tokens t0 .. min(t0 + 16, T) - 1.
+__global__ __launch_bounds__(kMtMaxWaves * kWave) void bf16_gemv_mt_kernel(MtJob job, int64_t K,
+                                                                          const float* __restrict__ x,
+                                                                          int64_t T, int64_t t0,
+                                                                          int accumulate) {
+    __shared__ __align__(16) float red[kMtMaxWaves][4][kWave];
+    __shared__ double ssw[kMtMaxWaves][16];
+    extern __shared__ __align__(16) float gs[];                 // the gain's K values (norm only)
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nw = blockDim.x >> 6;
+    const int bx = blockIdx.x;
+    const int mi = bx < job.tile_end[0] ? 0 : bx < job.tile_end[1] ? 1 : 2;
+    const int tile = bx - (mi == 0 ? 0 : job.tile_end[mi - 1]);
+    const uint16_t* __restrict__ W = job.W[mi];
+    float* __restrict__ y = job.y[mi];
+    const int64_t N = job.N[mi];
+    const int64_t n0 = (int64_t)tile * 16;
+    const bool norm = job.gain != nullptr;
+    const int c = lane & 15, kb = lane >> 4;                    // A row / B column, k block
+    const int64_t kw = (int64_t)wave * kMtWaveK + 8 * kb;
+    const int64_t wrow = n0 + c < N ? n0 + c : N - 1;           // clamped; its sums are dropped
+    const int64_t tok = t0 + c < T ? t0 + c : t0;               // clamped; its column is dropped
+
+    if (norm) {
+        for (int i = tid; i < K / 4; i += blockDim.x)
+            reinterpret_cast<float4*>(gs)[i] = reinterpret_cast<const float4*>(job.gain)[i];
+    }
+    float4 xa[kMtSteps], xb[kMtSteps];
+    const float* xp = x + tok * K + kw;
+#pragma unroll
+    for (int s = 0; s < kMtSteps; ++s) {
+        xa[s] = *reinterpret_cast<const float4*>(xp + 32 * s);
+        xb[s] = *reinterpret_cast<const float4*>(xp + 32 * s + 4);
+    }
+    u32x4_t wv[kMtSteps];
+    const uint16_t* wp = W + wrow * K + kw;
+#pragma unroll
+    for (int s = 0; s < kMtSteps; ++s)
+        wv[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(wp + 32 * s));
+
+    double ss = 0.0;
+    if (norm) {
+#pragma unroll
+        for (int s = 0; s < kMtSteps; ++s) {
+            const float v[8] = {xa[s].x, xa[s].y, xa[s].z, xa[s].w, xb[s].x, xb[s].y, xb[s].z, xb[s].w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ss = fma((double)v[i], (double)v[i], ss);
+        }
+        ss += __shfl_xor(ss, 16, kWave);
+        ss += __shfl_xor(ss, 32, kWave);
+        if (kb == 0) ssw[wave][c] = ss;
+        __syncthreads();                                        // gs and ssw written
+#pragma unroll
+        for (int s = 0; s < kMtSteps; ++s) {
+            const float4 ga = *reinterpret_cast<const float4*>(gs + kw + 32 * s);
+            const float4 gb = *reinterpret_cast<const float4*>(gs + kw + 32 * s + 4);
+            xa[s] = make_float4(ga.x * xa[s].x, ga.y * xa[s].y, ga.z * xa[s].z, ga.w * xa[s].w);
+            xb[s] = make_float4(gb.x * xb[s].x, gb.y * xb[s].y, gb.z * xb[s].z, gb.w * xb[s].w);
+        }
+    }
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < kMtSteps; ++s) {
+        uint32_t h[4], l[4];
+        mt_split2(xa[s].x, xa[s].y, h[0], l[0]);
+        mt_split2(xa[s].z, xa[s].w, h[1], l[1]);
+        mt_split2(xb[s].x, xb[s].y, h[2], l[2]);
+        mt_split2(xb[s].z, xb[s].w, h[3], l[3]);
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, wv[s]);
+        const bf16x8_t bh = __builtin_bit_cast(bf16x8_t, u32x4_t{h[0], h[1], h[2], h[3]});
+        const bf16x8_t bl = __builtin_bit_cast(bf16x8_t, u32x4_t{l[0], l[1], l[2], l[3]});
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[wave][i][lane] = acc[i];
+    __syncthreads();
+    if (wave == 0) {
+        float sum[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int w = 0; w < nw; ++w)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sum[i] += red[w][i][lane];
+        const int64_t t = t0 + c;
+        double inv = 1.0;
+        if (norm) {
+            double tot = 0.0;
+            for (int w = 0; w < nw; ++w) tot += ssw[w][c];
+            inv = 1.0 / sqrt(tot / (double)K + (double)job.eps);
+        }
+        if (t < T) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t n = n0 + 4 * kb + i;
+                if (n < N) {
+                    const float v = norm ? (float)((double)sum[i] * inv) : sum[i];
+                    float* o = y + t * N + n;
+                    *o = accumulate ? *o + v : v;
+                }
+            }
+        }
+    }
+}
+
+bool mt_path(int64_t T, int64_t K) {
+    return T >= kMtMinTokens && K % kMtWaveK == 0 && K <= (int64_t)kMtMaxWaves * kMtWaveK;
+}
+
+hipError_t launch_gemv_mt(MtJob job, int64_t K, const float* x, int64_t T, int accumulate,
+                          hipStream_t stream) {
+    int tiles = 0;
+    for (int i = 0; i < 3; ++i) {
+        tiles += (int)((job.N[i] + 15) / 16);
+        job.tile_end[i] = tiles;
+    }
+    const int threads = (int)(K / kMtWaveK) * kWave;
+    const size_t lds = job.gain ? (size_t)K * sizeof(float) : 0;
+    for (int64_t t0 = 0; t0 < T; t0 += 16) {
+        hipLaunchKernelGGL(bf16_gemv_mt_kernel, dim3((unsigned)tiles), dim3(threads), lds, stream, job, K, x, T,
+                           t0, accumulate);
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    return hipSuccess;
+}
+
 // ------------------------------------------------------------- KV write --
 
 // grid: B workgroups.  A position outside [0, S_max) writes nothing.
@@ -635,6 +803,10 @@ hipError_t launch_attn_d(const float* q, int64_t B, int32_t n_q, int32_t n_kv, c
 hipError_t launch_bf16_gemv(const uint16_t* W, int64_t N, int64_t K, const float* x, int64_t T,
                             float* y, int accumulate, hipStream_t stream) {
     if (gemm_path(T, K)) return launch_bf16_gemm(W, N, K, x, T, y, accumulate, stream);
+    if (mt_path(T, K)) {
+        MtJob mj{{W, nullptr, nullptr}, {y, nullptr, nullptr}, {N, 0, 0}, {0, 0, 0}, nullptr, 0.f};
+        return launch_gemv_mt(mj, K, x, T, accumulate, stream);
+    }
     GvJob job{W, nullptr, nullptr, y, nullptr, nullptr, N, 0, 0, 0, 0, nullptr, 0.f};
     return launch_gemv_job(job, K, x, T, accumulate, stream);
 }
@@ -658,6 +830,10 @@ hipError_t launch_bf16_gemv3(const uint16_t* W0, int64_t N0, const uint16_t* W1,
                 Ns[n++] = N_in[i];
             }
         return launch_bf16_gemm_multi(Ws, ys, Ns, n, K, x, T, 0, stream);
+    }
+    if (mt_path(T, K)) {                       // 9+ tokens (with the norm also 64+)
+        MtJob mj{{W0, W1, W2}, {y0, y1, y2}, {N0, N1, N2}, {0, 0, 0}, gain, eps};
+        return launch_gemv_mt(mj, K, x, T, 0, stream);
     }
     GvJob job{W0, W1, W2, y0, y1, y2, N0, N1, N2, 0, 0, gain, eps};
     return launch_gemv_job(job, K, x, T, 0, stream);

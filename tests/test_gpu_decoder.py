@@ -49,6 +49,11 @@ GEMV_CASES = [  # (T, N, K, accumulate, seed)
     (1, 1, 8, False, 10),          # the smallest shape
     (2, 3000, 8200, False, 11),    # K beyond one staged chunk of every kernel shape
     (9, 2049, 520, True, 12),
+    # the matrix-core form (9+ tokens, K a multiple of 256 up to 4096)
+    (17, 300, 2048, False, 13),    # two passes (16 + 1), a partial row tile
+    (40, 2049, 256, True, 14),     # one wave per tile, three passes (the last of 8 tokens)
+    (63, 33, 4096, False, 15),     # sixteen waves per tile, four passes
+    (9, 16, 512, True, 16),        # the fewest tokens it takes
 ]
 
 
@@ -74,6 +79,11 @@ GEMV3_CASES = [  # T, (N0, N1, N2), K, norm, seed
     (17, (300, 0, 0), 2056, True, 25),         # more than 16 tokens: two passes, one matrix
     (2, (3000, 64, 8), 8200, True, 26),        # K beyond one staged chunk
     (1, (1, 1, 1), 8, True, 27),               # the smallest shape
+    # the matrix-core form, with and without the norm
+    (17, (300, 40, 0), 2048, True, 28),        # two passes, partial row tiles
+    (64, (128, 16, 16), 1024, True, 29),       # 64 tokens with the norm: four passes
+    (20, (50, 7, 0), 768, True, 30),           # three waves per tile, two matrices
+    (12, (4096, 512, 512), 2048, False, 31),   # no norm
 ]
 
 
