@@ -313,6 +313,15 @@ __device__ __forceinline__ int sdot4(uint32_t a, uint32_t b, int c) {
     return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
 }
 
+// The first step of a dot-product chain: the three-operand form with an
+// inline zero accumulator (the builtin picks the two-operand form, whose
+// accumulator is also its result, and first moves a zero into it).
+__device__ __forceinline__ int sdot4_first(uint32_t a, uint32_t b) {
+    int r;
+    asm("v_dot4_i32_i8 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
 // One row's contribution of this lane: hdr = the block header (d, dmin, 12
 // scale bytes), qv = the lane's 16 quant bytes.  NP = 3: the three pieces
 // of the exact form, A and B in units of s * 2^-14; NP = 1: the single int8
@@ -320,11 +329,23 @@ __device__ __forceinline__ int sdot4(uint32_t a, uint32_t b, int c) {
 template <int NP>
 __device__ __forceinline__ float q4k_cols_row(uint4 hdr, uint4 qv, const XCols& x) {
     const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
-    int a1 = 0, a2 = 0, a3 = 0, b1 = 0, b2 = 0, b3 = 0;
+    int a1, a2 = 0, a3 = 0, b1, b2 = 0, b3 = 0;
+    {
+        const uint32_t lo = qw[0] & 0x0f0f0f0fu;               // 4 weights of sub-block 2c
+        const uint32_t hi = (qw[0] >> 4) & 0x0f0f0f0fu;        // 4 weights of sub-block 2c+1
+        a1 = sdot4_first(lo, x.p[0][0].x);
+        b1 = sdot4_first(hi, x.p[0][1].x);
+        if constexpr (NP == 3) {
+            a2 = sdot4_first(lo, x.p[1][0].x);
+            a3 = sdot4_first(lo, x.p[2][0].x);
+            b2 = sdot4_first(hi, x.p[1][1].x);
+            b3 = sdot4_first(hi, x.p[2][1].x);
+        }
+    }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const uint32_t lo = qw[q] & 0x0f0f0f0fu;               // 4 weights of sub-block 2c
-        const uint32_t hi = (qw[q] >> 4) & 0x0f0f0f0fu;        // 4 weights of sub-block 2c+1
+    for (int q = 1; q < 4; ++q) {
+        const uint32_t lo = qw[q] & 0x0f0f0f0fu;
+        const uint32_t hi = (qw[q] >> 4) & 0x0f0f0f0fu;
         a1 = sdot4(lo, (&x.p[0][0].x)[q], a1);
         b1 = sdot4(hi, (&x.p[0][1].x)[q], b1);
         if constexpr (NP == 3) {
@@ -607,7 +628,7 @@ __device__ __forceinline__ uint32_t load_stream4(const uint8_t* p) {
 // Lane k of each quad, in every lane of the quad.
 template <int K>
 __device__ __forceinline__ uint32_t quad_bcast(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, K * 0x55, 0xf, 0xf, false);
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, K * 0x55, 0xf, 0xf, false);
 }
 
 // Loads are unconditional (an out-of-range expert reads expert 0's rows and

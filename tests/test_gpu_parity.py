@@ -112,6 +112,10 @@ FFN_CASES = {  # name: (shape, seed)
     "generic_H768": (gen.MoeShape(T=3, H=768, E=6, k=2, F=512, down_qtype=gen.Q6_K), 20),
     "generic_H2560_q4k_down": (gen.MoeShape(T=2, H=2560, E=4, k=2, F=256, down_qtype=gen.Q4_K), 21),
     "a3b_k1_T2": (gen.MoeShape(T=2, H=2048, E=128, k=1, F=768, down_qtype=gen.Q6_K), 22),
+    # 5 <= T < 32 at H = 2048: the decode-batch kernels grouped by expert
+    "batch_k32_T31": (gen.MoeShape(T=31, H=2048, E=64, k=32, F=256, down_qtype=gen.Q4_K), 29),
+    "batch_E300_T9": (gen.MoeShape(T=9, H=2048, E=300, k=8, F=256, down_qtype=gen.Q4_K), 30),
+    "batch_F1024_T12": (gen.MoeShape(T=12, H=2048, E=16, k=4, F=1024, down_qtype=gen.Q6_K), 31),
     # T >= 32: the batched path (grouping + matrix-core tiles)
     "a3b_prefill_T512": (gen.MoeShape(T=512, H=2048, E=128, k=8, F=768, down_qtype=gen.Q6_K), 23),
     "a3b_prefill_q4k_down_T64": (gen.MoeShape(T=64, H=2048, E=128, k=8, F=768, down_qtype=gen.Q4_K), 24),
@@ -167,7 +171,8 @@ def test_prefill_skewed_routing(layers):
     say(f"  max rel L2 {err:.2e}")
 
 
-@pytest.mark.parametrize("name", ["tiny_T4", "a3b_decode_T1", "a3b_q4k_down_T3", "prefill_tiny_T40"])
+@pytest.mark.parametrize("name", ["tiny_T4", "a3b_decode_T1", "a3b_q4k_down_T3", "a3b_batch_T16",
+                                  "prefill_tiny_T40"])
 def test_accumulate_adds_to_out(layers, name):
     cpu, dev, x = layers(name)
     s = cpu.shape
@@ -197,7 +202,7 @@ def test_expert_ffn_given_routing(layers):
     assert_rows_close(out.cpu().numpy(), ref, what="fixed routing")
 
 
-@pytest.mark.parametrize("name", ["tiny_T4", "prefill_tiny_T40"])
+@pytest.mark.parametrize("name", ["tiny_T4", "a3b_batch_T16", "prefill_tiny_T40"])
 def test_out_of_range_index_contributes_zero(layers, name):
     cpu, dev, x = layers(name)
     s = cpu.shape
