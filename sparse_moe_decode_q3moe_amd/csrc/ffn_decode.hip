@@ -698,10 +698,11 @@ __device__ __forceinline__ void gu_rows_finish(const GuRows& g, const XCols& x, 
 // down threads have already pulled their share of the down tiles out of LDS
 // as quant bytes and per-row group factors (a, c) in registers; after h
 // arrives each row takes 16 byte conversions, 16 FMAs and one a, c step,
-// then the cross-lane sum.  Exit: each workgroup counts itself on a stripe of
-// exit counters; the workgroup that completes the count advances the epoch
-// and zeroes the counters for the next call.  Every wait is bounded: one that
-// runs out sets the status word instead of hanging.
+// then the cross-lane sum.  The epoch: each workgroup reads it first and then
+// stores a presence word with the tag; workgroup 0 advances it once every
+// presence word carries the tag (the next call is a later launch, so nothing
+// of this call reads it again), and nothing is counted at exit.  Every wait
+// is bounded: one that runs out sets the status word instead of hanging.
 constexpr int kFzGu = 6;
 constexpr int kFzDn = 2;
 constexpr int kFzWaves = kFzGu + kFzDn;
@@ -715,6 +716,12 @@ constexpr int kSyncEpoch = 32;                         // calls completed on thi
 constexpr int kSyncExit = 64;                          // + kLineInts * stripe
 constexpr int kSyncExitTop = kSyncExit + kStripes * kLineInts;
 static_assert((kSyncExitTop + 1) * 4 <= (int)kFfnRouteSyncOffset, "sync header too small");
+// The one-layer kernel's presence words: workgroup w stores a tagged word at
+// kSyncPresence + w once it has read the epoch (64-bit words, in the
+// header's second half past the route counter).
+constexpr int kSyncPresence = 6144 / 8;
+constexpr int kMaxPresence = 256;
+static_assert((kSyncPresence + kMaxPresence) * 8 <= (int)kFfnSyncBytes, "presence words outside the header");
 
 __device__ __forceinline__ int stripe_members(int stripe, int grid) {
     return grid / kStripes + (stripe < grid % kStripes ? 1 : 0);
@@ -1029,13 +1036,18 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
     const int gu_step = grid * kFzGu;
     const bool is_gu = wave < kFzGu;
 
-    // ---- (1) this call's epoch (every workgroup reads it here; only the
-    // last workgroup to finish advances it), routing, activation pieces.
+    // ---- (1) this call's epoch (every workgroup reads it here and then
+    // stores its presence word; workgroup 0 advances the epoch once it has
+    // seen every presence word), routing, activation pieces.
     const int nr = (int)(T * k);
     const uint32_t epoch = (uint32_t)__hip_atomic_load(sync + kSyncEpoch, __ATOMIC_RELAXED,
                                                        __HIP_MEMORY_SCOPE_AGENT);
     // the tag as a scalar now, while only this small load is in flight
     const uint32_t tag = __builtin_amdgcn_readfirstlane(h_tag(epoch));
+    uint64_t* presence = reinterpret_cast<uint64_t*>(sync) + kSyncPresence;
+    if (tid == 0)
+        __hip_atomic_store(presence + wg, ((uint64_t)tag << 32) | (uint32_t)wg, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     // LDS counters: gate/up waves whose activation pieces are written, down
     // waves whose tiles have landed
     int32_t* x_ready = reinterpret_cast<int32_t*>(smem + L.flag_off);
@@ -1274,6 +1286,27 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
         wait_all_loads();
         if (lane == 0)
             __hip_atomic_fetch_add(dn_ready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (wg == 0 && wave == kFzWaves - 1) {
+            // Every workgroup has read this call's epoch once its presence
+            // word carries the tag; the epoch then advances for the next call
+            // (a later launch on the stream), with no count at exit.  The
+            // wait is bounded: running out sets bit 16 of the status word.
+            bool all = false;
+            for (int spins = 0; !all && spins <= kSpinLimit; ++spins) {
+                bool mine = true;
+                for (int i = lane; i < grid; i += kWave) {
+                    const uint64_t v = __hip_atomic_load(presence + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    mine = mine && (uint32_t)(v >> 32) == tag;
+                }
+                all = __all(mine);
+                if (!all) __builtin_amdgcn_s_sleep(1);
+            }
+            if (lane == 0) {
+                if (!all) __hip_atomic_fetch_or(status, 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(sync + kSyncEpoch, (int32_t)(epoch + 1u), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
     }
 
     // ---- (2) down projection and combine.  The down units are shared by
@@ -1287,7 +1320,6 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
     const int uw = wave < 4 ? wave : (wave >= kFzGu ? wave - 2 : -1);
     const int iters = (n_units + kUnitThr - 1) / kUnitThr;   // the same for every wave
     float* hl = reinterpret_cast<float*>(smem + L.h_off);
-    int32_t exit_ticket = -1;                 // thread 0: this workgroup's count on its exit stripe
     for (int j = 0; unit < n_dn; unit += grid, ++j) {
         const int64_t t = unit / row_units, r0 = (unit % row_units) * kDnRows;
         if (j > 0) {
@@ -1323,19 +1355,6 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
                 // the token's h: every slot's F values, published by gate/up
                 // waves anywhere on the device
                 wait_tagged<kThr>(hbuf + t * k * F, k * (int)F, tag, reinterpret_cast<uint32_t*>(hl), tid, status, 2);
-                // the workgroup's last read of this call's tagged words: it
-                // counts itself on its exit stripe now, and the atomic's
-                // round trip overlaps the rest (its result is used at exit).
-                // The offset `lane0` (zero in a vector register the compiler
-                // cannot see through) keeps the wave-level atomic rewrite,
-                // whose combining step would wait for the return here, off
-                // this one-lane atomic.
-                if (tid == 0 && unit + grid >= n_dn) {
-                    int lane0 = 0;
-                    asm volatile("" : "+v"(lane0));
-                    exit_ticket = __hip_atomic_fetch_add(sync + kSyncExit + (wg % kStripes) * kLineInts + lane0, 1,
-                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                }
                 __syncthreads();
             }
             if (uw >= 0) {
@@ -1371,29 +1390,6 @@ __global__ __launch_bounds__(kFzWaves * kWave) void ffn_fused8_kernel(
         }
     }
 
-    // ---- exit: the last workgroup advances the epoch and zeroes the counters
-    // (a workgroup counted itself after its last read of tagged words; one
-    // without a down unit counts here)
-    if (tid == 0) {
-        const int st = wg % kStripes;
-        const int32_t done = exit_ticket >= 0
-                                 ? exit_ticket
-                                 : __hip_atomic_fetch_add(sync + kSyncExit + st * kLineInts, 1,
-                                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (done == stripe_members(st, grid) - 1) {           // this stripe is complete
-            const int used = grid < kStripes ? grid : kStripes;
-            const int32_t top = __hip_atomic_fetch_add(sync + kSyncExitTop, 1, __ATOMIC_RELAXED,
-                                                       __HIP_MEMORY_SCOPE_AGENT);
-            if (top == used - 1) {                            // every workgroup has finished
-                for (int i = 0; i < kStripes; ++i)
-                    __hip_atomic_store(sync + kSyncExit + i * kLineInts, 0, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(sync + kSyncExitTop, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(sync + kSyncEpoch, (int32_t)(epoch + 1u), __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-            }
-        }
-    }
 }
 
 // --------------------------------------------------------- layer stack --
@@ -1924,7 +1920,8 @@ int fused_grid(int64_t T, int64_t H, int64_t F, int32_t k, int32_t dqtype, bool 
     const int64_t need = (T * k * tiles + kFzGu - 1) / kFzGu;
     const int64_t units = T * (H / kDnRows);
     const int64_t want = need > units ? need : units;
-    return (int)(want < cus ? want : cus);
+    const int64_t cap = cus < kMaxPresence ? cus : kMaxPresence;   // one presence word per workgroup
+    return (int)(want < cap ? want : cap);
 }
 
 // Column parts per router row in the fused kernel: the largest power of two
