@@ -19,11 +19,14 @@
 //   slot pos[t] of one sequence's caches.
 //
 // prefill_attn_kernel: causal attention of T queries of one sequence over
-//   its cache (query t sees positions 0 .. pos[t]), GQA.  A workgroup of two
+//   its cache (query t sees positions 0 .. pos[t]), GQA.  A workgroup of 12
 //   waves takes 64 query rows = (64 / G tokens) x (the G query heads of one
-//   kv head); K and V stream through LDS in tiles of 64 positions (V
-//   transposed on the way in).  Per tile each wave forms S^T = K Q^T for its
-//   32 rows (K as the A operand, the query pieces, held in registers, as B),
+//   kv head): 4 row waves of 16 rows each, times 3 key splits that take every
+//   third K/V tile of 64 positions, each split streaming its tiles through its
+//   own LDS buffer (V transposed on the way in); at the end the splits' O,
+//   running maximum and sum meet in LDS and are merged with the log-sum-exp
+//   rule.  Per tile each wave forms S^T = K Q^T for its
+//   16 rows (K as the A operand, the query pieces, held in registers, as B),
 //   so a lane holds 16 scores of ONE query row and the row's online softmax
 //   needs two cross-lane steps; P = exp(S - m) (f32) is split into two bf16
 //   pieces and O += P V uses the same lane's 8 keys per 32-key step as its
@@ -211,13 +214,19 @@ __global__ __launch_bounds__(256) void kv_rows_kernel(const float* __restrict__ 
 // ------------------------------------------------------- prefill attention --
 
 constexpr int kPaD = 128;                      // head_dim
-constexpr int kPaWaves = 2;
-constexpr int kPaRows = 32 * kPaWaves;         // query rows per workgroup
+constexpr int kPaBlk = 1;                      // 16-row blocks per wave
+constexpr int kPaRowWaves = 4;                 // waves across the query rows
+constexpr int kPaSplit = 3;                    // wave groups across the key tiles
+constexpr int kPaWaves = kPaRowWaves * kPaSplit;
+constexpr int kPaRows = 16 * kPaBlk * kPaRowWaves;   // query rows per workgroup
 constexpr int kPaKeys = 64;                    // positions per K/V tile
 constexpr int kPaKStride = kPaD * 2 + 16;      // K tile row: 272 bytes
 constexpr int kPaVStride = kPaKeys * 2 + 16;   // V^T tile row: 144 bytes
 constexpr int kPaKBytes = kPaKeys * kPaKStride;
-constexpr int kPaLds = kPaKBytes + kPaD * kPaVStride;   // 17,408 + 18,432
+constexpr int kPaTileLds = kPaKBytes + kPaD * kPaVStride;   // 17,408 + 18,432: one split's tile
+constexpr int kPaLds = kPaSplit * kPaTileLds;
+constexpr int kPaRecF = 34 * kPaBlk;           // merge record per lane: 32 O values, m, sum per block
+static_assert((kPaSplit - 1) * kPaRowWaves * kPaRecF * 64 * 4 <= kPaLds, "merge records exceed the tiles");
 
 // grid: (ceil(T / (64 / G)), n_kv); G = n_q / n_kv divides 64.  q [T][n_q][128]
 // f32 (16-byte aligned), caches [n_kv][S_max][128] bf16 of the one sequence,
@@ -227,9 +236,11 @@ __global__ __launch_bounds__(kPaWaves * 64) void prefill_attn_kernel(
     const uint16_t* __restrict__ vc, int64_t S_max, const int32_t* __restrict__ pos, float scale,
     float* __restrict__ out) {
     extern __shared__ __align__(16) uint8_t smem[];
-    uint8_t* ks = smem;
-    uint8_t* vs = smem + kPaKBytes;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int rw = wave % kPaRowWaves, sp = wave / kPaRowWaves;    // row wave, key split
+    uint8_t* ks = smem + sp * kPaTileLds;
+    uint8_t* vs = ks + kPaKBytes;
+    const int ts = rw * 64 + lane;                                 // thread within the split's waves
     const int tpw = kPaRows / G;                                   // tokens per workgroup
     // heavier tiles (later tokens) first
     const int64_t tile = (int64_t)gridDim.x - 1 - blockIdx.x;
@@ -251,11 +262,11 @@ __global__ __launch_bounds__(kPaWaves * 64) void prefill_attn_kernel(
     // this lane's query row in each of its two row blocks, its position
     // (-1 when invalid: no key passes the mask) and its query pieces
     const int fr = lane & 15, fg = lane >> 4;
-    int64_t prow[2];
-    bf16x8_t qh[2][4], ql[2][4];
+    int64_t prow[kPaBlk];
+    bf16x8_t qh[kPaBlk][4], ql[kPaBlk][4];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        const int row = 32 * wave + 16 * b + fr;
+    for (int b = 0; b < kPaBlk; ++b) {
+        const int row = 16 * kPaBlk * rw + 16 * b + fr;
         const int64_t t = t0 + row / G;
         const int h = g * G + row % G;
         const int64_t tc = t < T ? t : T - 1;
@@ -281,20 +292,30 @@ __global__ __launch_bounds__(kPaWaves * 64) void prefill_attn_kernel(
         }
     }
 
-    f32x4_t o[2][8];
+    f32x4_t o[kPaBlk][8];
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < kPaBlk; ++b)
 #pragma unroll
         for (int j = 0; j < 8; ++j) o[b][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m[2] = {-__builtin_inff(), -__builtin_inff()}, lsum[2] = {0.f, 0.f};
+    float m[kPaBlk], lsum[kPaBlk];
+#pragma unroll
+    for (int b = 0; b < kPaBlk; ++b) {
+        m[b] = -__builtin_inff();
+        lsum[b] = 0.f;
+    }
 
     const int64_t ntiles = (kmax + kPaKeys) / kPaKeys;             // 0 when no valid row
     const float scale2 = scale * 1.4426950408889634f;
-    for (int64_t it = 0; it < ntiles; ++it) {
+    // split sp takes tiles sp, sp + kPaSplit, ...; every wave runs the same
+    // number of rounds (a split without a tile in a round only meets the
+    // barriers)
+    for (int64_t base = 0; base < ntiles; base += kPaSplit) {
+        const int64_t it = base + sp;
+        const bool tl = it < ntiles;
         const int64_t j0 = it * kPaKeys;
-        // stage the tile: 64 keys x 16 chunks for K and for V, 128 threads
+        // stage the tile: 64 keys x 16 chunks for K and for V, the split's threads
         __syncthreads();                                           // the previous tile is consumed
-        for (int c = tid; c < kPaKeys * 16; c += kPaWaves * 64) {
+        for (int c = ts; tl && c < kPaKeys * 16; c += kPaRowWaves * 64) {
             const int key = c >> 4, d8 = c & 15;
             // rows past the workgroup's last position are never attended to:
             // they enter as zeros, since a masked probability (0) times
@@ -313,8 +334,9 @@ __global__ __launch_bounds__(kPaWaves * 64) void prefill_attn_kernel(
             }
         }
         __syncthreads();
+        if (!tl) continue;
         // S^T = K Q^T: s[b][kb] lane l holds keys 16 kb + 4 fg + r of query row fr of block b
-        f32x4_t s[2][4];
+        f32x4_t s[kPaBlk][4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
             bf16x8_t kf[4];
@@ -322,7 +344,7 @@ __global__ __launch_bounds__(kPaWaves * 64) void prefill_attn_kernel(
             for (int ds = 0; ds < 4; ++ds)
                 kf[ds] = *reinterpret_cast<const bf16x8_t*>(ks + (16 * kb + fr) * kPaKStride + 64 * ds + 16 * fg);
 #pragma unroll
-            for (int b = 0; b < 2; ++b) {
+            for (int b = 0; b < kPaBlk; ++b) {
                 f32x4_t a = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ds = 0; ds < 4; ++ds) {
@@ -335,7 +357,7 @@ __global__ __launch_bounds__(kPaWaves * 64) void prefill_attn_kernel(
         // online softmax per query row (the row's 64 scores sit in the 4
         // lanes fr, fr + 16, fr + 32, fr + 48, 16 each)
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
+        for (int b = 0; b < kPaBlk; ++b) {
             // scores in base-2 units: exp(scale s - m) = 2^(scale log2(e) s - m')
             float tmax = -__builtin_inff();
 #pragma unroll
@@ -379,9 +401,9 @@ __global__ __launch_bounds__(kPaWaves * 64) void prefill_attn_kernel(
 #pragma unroll
         for (int ks2 = 0; ks2 < 2; ++ks2) {
             const int kb = 2 * ks2;
-            bf16x8_t ph[2], pl[2];
+            bf16x8_t ph[kPaBlk], pl[kPaBlk];
 #pragma unroll
-            for (int b = 0; b < 2; ++b) {
+            for (int b = 0; b < kPaBlk; ++b) {
                 uint32_t hw[4], lw[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -403,22 +425,60 @@ __global__ __launch_bounds__(kPaWaves * 64) void prefill_attn_kernel(
                 const uint2 vb = *reinterpret_cast<const uint2*>(vrow + 2 * (16 * (kb + 1) + 4 * fg));
                 const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, make_uint4(va.x, va.y, vb.x, vb.y));
 #pragma unroll
-                for (int b = 0; b < 2; ++b) {
+                for (int b = 0; b < kPaBlk; ++b) {
                     o[b][j] = mfma32(ph[b], vf, o[b][j]);
                     o[b][j] = mfma32(pl[b], vf, o[b][j]);
                 }
             }
         }
     }
+    // the splits meet in LDS (over the tiles): splits 1.. store O, m and the
+    // sum of every lane, split 0 adds them in split order with the
+    // log-sum-exp rule
+    __syncthreads();
+    float* rec = reinterpret_cast<float*>(smem);
+    if (sp > 0) {
+        float* rr = rec + ((sp - 1) * kPaRowWaves + rw) * kPaRecF * 64;
+#pragma unroll
+        for (int b = 0; b < kPaBlk; ++b) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) rr[((b * 8 + j) * 4 + r) * 64 + lane] = o[b][j][r];
+            rr[(32 * kPaBlk + b) * 64 + lane] = m[b];
+            rr[(33 * kPaBlk + b) * 64 + lane] = lsum[b];
+        }
+    }
+    __syncthreads();
+    if (sp > 0) return;
+    for (int i = 1; i < kPaSplit; ++i) {
+        const float* rr = rec + ((i - 1) * kPaRowWaves + rw) * kPaRecF * 64;
+#pragma unroll
+        for (int b = 0; b < kPaBlk; ++b) {
+            const float mi = rr[(32 * kPaBlk + b) * 64 + lane], li = rr[(33 * kPaBlk + b) * 64 + lane];
+            const float mn = fmaxf(m[b], mi);
+            const bool lv = mn > -__builtin_inff();
+            const float ca = lv ? exp2f(m[b] - mn) : 1.f;
+            const float cb = lv ? exp2f(mi - mn) : 1.f;
+            lsum[b] = lsum[b] * ca + li * cb;
+            m[b] = mn;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float fa = __shfl(ca, 4 * fg + r, 64), fb = __shfl(cb, 4 * fg + r, 64);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) o[b][j][r] = o[b][j][r] * fa + rr[((b * 8 + j) * 4 + r) * 64 + lane] * fb;
+            }
+        }
+    }
     // out = O / sum: lane l holds rows 4 fg + r of each block, column 16 j + fr
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < kPaBlk; ++b)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int rl = 4 * fg + r;
             const float den = __shfl(lsum[b], rl, 64);
             const bool valid = __shfl((int)(prow[b] >= 0), rl, 64) != 0;
-            const int row = 32 * wave + 16 * b + rl;
+            const int row = 16 * kPaBlk * rw + 16 * b + rl;
             const int64_t t = t0 + row / G;
             const int h = g * G + row % G;
             if (t < T) {
@@ -487,6 +547,9 @@ hipError_t launch_prefill_attention(const float* q, int64_t T, int32_t nq, int32
     const int G = nq / nkv;
     const int tpw = kPaRows / G;
     dim3 grid((unsigned)((T + tpw - 1) / tpw), (unsigned)nkv);
+    static LdsLimit lds_set;
+    const hipError_t e = ensure_lds(reinterpret_cast<const void*>(prefill_attn_kernel), lds_set, kPaLds);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(prefill_attn_kernel, grid, dim3(kPaWaves * 64), kPaLds, stream, q, T, nq, G,
                        kc, vc, S_max, pos, scale, out);
     return hipGetLastError();
