@@ -23,7 +23,8 @@
 //   waves takes 64 query rows = (64 / G tokens) x (the G query heads of one
 //   kv head): 4 row waves of 16 rows each, times 3 key splits that take every
 //   third K/V tile of 64 positions, each split streaming its tiles through its
-//   own LDS buffer (V transposed on the way in); at the end the splits' O,
+//   own LDS buffer (V transposed on the way in: each thread packs one value
+//   of 4 keys into an 8-byte store); at the end the splits' O,
 //   running maximum and sum meet in LDS and are merged with the log-sum-exp
 //   rule.  Per tile each wave forms S^T = K Q^T for its
 //   16 rows (K as the A operand, the query pieces, held in registers, as B),
@@ -313,24 +314,44 @@ __global__ __launch_bounds__(kPaWaves * 64) void prefill_attn_kernel(
         const int64_t it = base + sp;
         const bool tl = it < ntiles;
         const int64_t j0 = it * kPaKeys;
-        // stage the tile: 64 keys x 16 chunks for K and for V, the split's threads
+        // stage the tile: 64 keys x 16 chunks of 8 values for K and for V,
+        // the split's 256 threads.  Rows past the workgroup's last position
+        // are never attended to: they enter as zeros, since a masked
+        // probability (0) times whatever such a row holds (NaN included) must
+        // contribute nothing.
         __syncthreads();                                           // the previous tile is consumed
-        for (int c = ts; tl && c < kPaKeys * 16; c += kPaRowWaves * 64) {
-            const int key = c >> 4, d8 = c & 15;
-            // rows past the workgroup's last position are never attended to:
-            // they enter as zeros, since a masked probability (0) times
-            // whatever such a row holds (NaN included) must contribute nothing
-            const bool live = j0 + key <= kmax;
-            const int64_t j = live ? j0 + key : 0;
+        static_assert(kPaRowWaves * 64 == kPaKeys / 4 * 16, "one V key quad per thread");
+        if (tl) {
             const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-            const uint4 kv = live ? *reinterpret_cast<const uint4*>(K + j * kPaD + 8 * d8) : z;
-            const uint4 vv = live ? *reinterpret_cast<const uint4*>(V + j * kPaD + 8 * d8) : z;
-            *reinterpret_cast<uint4*>(ks + key * kPaKStride + 16 * d8) = kv;
-            const uint32_t w4[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                *reinterpret_cast<uint16_t*>(vs + (8 * d8 + 2 * i) * kPaVStride + 2 * key) = (uint16_t)(w4[i] & 0xffffu);
-                *reinterpret_cast<uint16_t*>(vs + (8 * d8 + 2 * i + 1) * kPaVStride + 2 * key) = (uint16_t)(w4[i] >> 16);
+            for (int u = 0; u < kPaKeys * 16 / (kPaRowWaves * 64); ++u) {
+                const int c = ts + u * kPaRowWaves * 64, key = c >> 4, d8 = c & 15;
+                const bool live = j0 + key <= kmax;
+                const int64_t j = live ? j0 + key : 0;
+                const uint4 kv = live ? *reinterpret_cast<const uint4*>(K + j * kPaD + 8 * d8) : z;
+                *reinterpret_cast<uint4*>(ks + key * kPaKStride + 16 * d8) = kv;
+            }
+            // V^T: this thread's 4 keys 4 kq .. 4 kq + 3 of chunk d8; value i
+            // of the chunk for the 4 keys is one 8-byte store in row 8 d8 + i
+            const int kq = ts >> 4, d8 = ts & 15;                  // 16 lanes read a key's 256 bytes
+            uint4 vq[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int key = 4 * kq + r;
+                const bool live = j0 + key <= kmax;
+                const int64_t j = live ? j0 + key : 0;
+                vq[r] = live ? *reinterpret_cast<const uint4*>(V + j * kPaD + 8 * d8) : z;
+            }
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t a0 = (&vq[0].x)[w], a1 = (&vq[1].x)[w], a2 = (&vq[2].x)[w], a3 = (&vq[3].x)[w];
+                // value 2w: the low halves of the four keys' word w; 2w + 1: the high halves
+                const uint2 lo = make_uint2(__builtin_amdgcn_perm(a1, a0, 0x05040100u),
+                                            __builtin_amdgcn_perm(a3, a2, 0x05040100u));
+                const uint2 hi = make_uint2(__builtin_amdgcn_perm(a1, a0, 0x07060302u),
+                                            __builtin_amdgcn_perm(a3, a2, 0x07060302u));
+                *reinterpret_cast<uint2*>(vs + (8 * d8 + 2 * w) * kPaVStride + 8 * kq) = lo;
+                *reinterpret_cast<uint2*>(vs + (8 * d8 + 2 * w + 1) * kPaVStride + 8 * kq) = hi;
             }
         }
         __syncthreads();
