@@ -229,6 +229,55 @@ constexpr int kPaLds = kPaSplit * kPaTileLds;
 constexpr int kPaRecF = 34 * kPaBlk;           // merge record per lane: 32 O values, m, sum per block
 static_assert((kPaSplit - 1) * kPaRowWaves * kPaRecF * 64 * 4 <= kPaLds, "merge records exceed the tiles");
 
+// K/V staging of one split: thread ts loads K chunks ts + 256 u (key c / 16,
+// 8 values at 8 (c % 16)) and the 16-byte rows of keys 4 kq .. 4 kq + 3 at
+// chunk d8v of V, for the tile starting at position jt (keys past kmax as
+// zeros); pa_store_tile writes them to the split's LDS tile (V transposed).
+constexpr int kPaKu = kPaKeys * 16 / (kPaRowWaves * 64);           // K chunks per thread
+__device__ __forceinline__ void pa_load_tile(u32x4_t (&kr)[kPaKu], u32x4_t (&vq)[4], const uint16_t* K,
+                                             const uint16_t* V, int64_t jt, int64_t kmax, int ts, int kq,
+                                             int d8v) {
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int u = 0; u < kPaKu; ++u) {
+        const int c = ts + u * kPaRowWaves * 64, key = c >> 4, d8 = c & 15;
+        const bool live = jt + key <= kmax;
+        const int64_t j = live ? jt + key : 0;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(K + j * kPaD + 8 * d8);
+        kr[u] = live ? v : z;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int key = 4 * kq + r;
+        const bool live = jt + key <= kmax;
+        const int64_t j = live ? jt + key : 0;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(V + j * kPaD + 8 * d8v);
+        vq[r] = live ? v : z;
+    }
+}
+
+__device__ __forceinline__ void pa_store_tile(const u32x4_t (&kr)[kPaKu], const u32x4_t (&vq)[4], uint8_t* ks,
+                                              uint8_t* vs, int ts, int kq, int d8v) {
+#pragma unroll
+    for (int u = 0; u < kPaKu; ++u) {
+        const int c = ts + u * kPaRowWaves * 64, key = c >> 4, d8 = c & 15;
+        *reinterpret_cast<u32x4_t*>(ks + key * kPaKStride + 16 * d8) = kr[u];
+    }
+    // V^T: value i of chunk d8v for keys 4 kq .. 4 kq + 3 is one 8-byte
+    // store in row 8 d8v + i
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const uint32_t a0 = vq[0][w], a1 = vq[1][w], a2 = vq[2][w], a3 = vq[3][w];
+        // value 2w: the low halves of the four keys' word w; 2w + 1: the high halves
+        const uint2 lo = make_uint2(__builtin_amdgcn_perm(a1, a0, 0x05040100u),
+                                    __builtin_amdgcn_perm(a3, a2, 0x05040100u));
+        const uint2 hi = make_uint2(__builtin_amdgcn_perm(a1, a0, 0x07060302u),
+                                    __builtin_amdgcn_perm(a3, a2, 0x07060302u));
+        *reinterpret_cast<uint2*>(vs + (8 * d8v + 2 * w) * kPaVStride + 8 * kq) = lo;
+        *reinterpret_cast<uint2*>(vs + (8 * d8v + 2 * w + 1) * kPaVStride + 8 * kq) = hi;
+    }
+}
+
 // grid: (ceil(T / (64 / G)), n_kv); G = n_q / n_kv divides 64.  q [T][n_q][128]
 // f32 (16-byte aligned), caches [n_kv][S_max][128] bf16 of the one sequence,
 // out like q.
@@ -309,52 +358,26 @@ __global__ __launch_bounds__(kPaWaves * 64) void prefill_attn_kernel(
     const float scale2 = scale * 1.4426950408889634f;
     // split sp takes tiles sp, sp + kPaSplit, ...; every wave runs the same
     // number of rounds (a split without a tile in a round only meets the
-    // barriers)
+    // barriers).  Staging: 64 keys x 16 chunks of 8 values for K and for V
+    // over the split's 256 threads, the next round's tile loaded into
+    // registers while this round's is multiplied.  Rows past the
+    // workgroup's last position are never attended to: they enter as
+    // zeros, since a masked probability (0) times whatever such a row holds
+    // (NaN included) must contribute nothing.
+    static_assert(kPaRowWaves * 64 == kPaKeys / 4 * 16, "one V key quad per thread");
+    const int kq = ts >> 4, d8v = ts & 15;                         // V: 16 lanes read a key's 256 bytes
+    u32x4_t kr[kPaKu], vq[4];
+    // the loads are unconditional (a tile past the last one reads row 0 and
+    // enters as zeros), so the staged rows never live in scratch
+    pa_load_tile(kr, vq, K, V, (int64_t)sp * kPaKeys, kmax, ts, kq, d8v);
     for (int64_t base = 0; base < ntiles; base += kPaSplit) {
         const int64_t it = base + sp;
         const bool tl = it < ntiles;
         const int64_t j0 = it * kPaKeys;
-        // stage the tile: 64 keys x 16 chunks of 8 values for K and for V,
-        // the split's 256 threads.  Rows past the workgroup's last position
-        // are never attended to: they enter as zeros, since a masked
-        // probability (0) times whatever such a row holds (NaN included) must
-        // contribute nothing.
         __syncthreads();                                           // the previous tile is consumed
-        static_assert(kPaRowWaves * 64 == kPaKeys / 4 * 16, "one V key quad per thread");
-        if (tl) {
-            const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-#pragma unroll
-            for (int u = 0; u < kPaKeys * 16 / (kPaRowWaves * 64); ++u) {
-                const int c = ts + u * kPaRowWaves * 64, key = c >> 4, d8 = c & 15;
-                const bool live = j0 + key <= kmax;
-                const int64_t j = live ? j0 + key : 0;
-                const uint4 kv = live ? *reinterpret_cast<const uint4*>(K + j * kPaD + 8 * d8) : z;
-                *reinterpret_cast<uint4*>(ks + key * kPaKStride + 16 * d8) = kv;
-            }
-            // V^T: this thread's 4 keys 4 kq .. 4 kq + 3 of chunk d8; value i
-            // of the chunk for the 4 keys is one 8-byte store in row 8 d8 + i
-            const int kq = ts >> 4, d8 = ts & 15;                  // 16 lanes read a key's 256 bytes
-            uint4 vq[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int key = 4 * kq + r;
-                const bool live = j0 + key <= kmax;
-                const int64_t j = live ? j0 + key : 0;
-                vq[r] = live ? *reinterpret_cast<const uint4*>(V + j * kPaD + 8 * d8) : z;
-            }
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const uint32_t a0 = (&vq[0].x)[w], a1 = (&vq[1].x)[w], a2 = (&vq[2].x)[w], a3 = (&vq[3].x)[w];
-                // value 2w: the low halves of the four keys' word w; 2w + 1: the high halves
-                const uint2 lo = make_uint2(__builtin_amdgcn_perm(a1, a0, 0x05040100u),
-                                            __builtin_amdgcn_perm(a3, a2, 0x05040100u));
-                const uint2 hi = make_uint2(__builtin_amdgcn_perm(a1, a0, 0x07060302u),
-                                            __builtin_amdgcn_perm(a3, a2, 0x07060302u));
-                *reinterpret_cast<uint2*>(vs + (8 * d8 + 2 * w) * kPaVStride + 8 * kq) = lo;
-                *reinterpret_cast<uint2*>(vs + (8 * d8 + 2 * w + 1) * kPaVStride + 8 * kq) = hi;
-            }
-        }
+        if (tl) pa_store_tile(kr, vq, ks, vs, ts, kq, d8v);
         __syncthreads();
+        pa_load_tile(kr, vq, K, V, j0 + (int64_t)kPaSplit * kPaKeys, kmax, ts, kq, d8v);
         if (!tl) continue;
         // S^T = K Q^T: s[b][kb] lane l holds keys 16 kb + 4 fg + r of query row fr of block b
         f32x4_t s[kPaBlk][4];
