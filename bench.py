@@ -82,8 +82,8 @@ PMC_STEPS = 16
 # in profiles/ffn_fused8_kernel_a3b_decode_b1_traffic.md.  The figure belongs
 # to the kernel sources it was measured on; when they change it is reported
 # as null until the counters are taken again.
-TRAFFIC_BYTES_PER_LAUNCH = 26_819_437
-TRAFFIC_SOURCES_SHA256 = "470c0d3b0c9e5cffd9300bed98172ad9992b69c05a5ed3320ceec3da2faee157"
+TRAFFIC_BYTES_PER_LAUNCH = 26_829_498
+TRAFFIC_SOURCES_SHA256 = "c5819fc59c8cd4606edb28627b36c304264949e754d447ee3feb2a21e5da87dc"
 TRAFFIC_SOURCES = ("sparse_moe_decode_q3moe_amd/csrc/ffn_decode.hip",
                    "sparse_moe_decode_q3moe_amd/csrc/route_common.h",
                    "sparse_moe_decode_q3moe_amd/csrc/device_common.h")
@@ -525,9 +525,8 @@ def decoder_bench(torch, q3, gen, layers, experts, shape, dev, cpu=None, status=
     cached positions (sequence b at position 4095 - 211 b), O projection with
     the residual, post-attention RMSNorm, route, expert FFN with the
     residual.  The residual stream is updated in place, as a decode step
-    does; at batch 1 the input norm and the Q/K/V projections are one
-    q3moe_bf16_gemv3 launch (at batch 16 four launches, q3moe_rmsnorm and
-    three q3moe_bf16_gemv, measure faster), Q/K norm + RoPE and the KV write
+    does; the input norm and the Q/K/V projections are one
+    q3moe_bf16_gemv3 launch, Q/K norm + RoPE and the KV write
     one q3moe_attn_prologue_kv launch, the post-attention norm, route and
     expert FFN one q3moe_moe_ffn_prenorm call.  Batch 1 and 16; attention layer copies (36 MB of bf16 weights
     each, plus their KV caches) and the 16 MoE layer copies rotate, so the
@@ -544,7 +543,6 @@ def decoder_bench(torch, q3, gen, layers, experts, shape, dev, cpu=None, status=
         x = gen.hidden_states(B, H, 9, device=dev)
         pos = torch.tensor([S - 1 - 211 * b for b in range(B)], dtype=torch.int32, device=dev)
         lens = pos + 1
-        xn = torch.empty((B, H), device=dev)
         q = torch.empty((B, nq * D), device=dev)
         kk = torch.empty((B, nkv * D), device=dev)
         vv = torch.empty((B, nkv * D), device=dev)
@@ -559,14 +557,8 @@ def decoder_bench(torch, q3, gen, layers, experts, shape, dev, cpu=None, status=
         def attention(i):
             A = atts[i % ncopies]
             kc, vc = caches[i % ncopies]
-            if B <= 4:                                     # input norm + Q/K/V, one launch
-                q3.q3moe_bf16_gemv3([A.wq, A.wk, A.wv], x, norm_gain=A.in_norm, eps=s_.eps,
-                                    outs=[q, kk, vv])
-            else:                                          # faster as four launches at 16 tokens
-                q3.q3moe_rmsnorm(x, A.in_norm, s_.eps, out=xn)
-                q3.q3moe_bf16_gemv(A.wq, xn, out=q)
-                q3.q3moe_bf16_gemv(A.wk, xn, out=kk)
-                q3.q3moe_bf16_gemv(A.wv, xn, out=vv)
+            # input norm + Q/K/V, one launch (the matrix-core GEMV at 16 tokens)
+            q3.q3moe_bf16_gemv3([A.wq, A.wk, A.wv], x, norm_gain=A.in_norm, eps=s_.eps, outs=[q, kk, vv])
             q3.q3moe_attn_prologue_kv(q.view(B, nq, D), kk.view(B, nkv, D), vv.view(B, nkv, D),
                                       A.q_norm, A.k_norm, pos, s_.eps, s_.rope_base, kc, vc)
             q3.q3moe_gqa_attention(q.view(B, nq, D), kc, vc, lens, 1.0 / math.sqrt(D), out=ao,
