@@ -231,23 +231,16 @@ __device__ __forceinline__ f16x8_t pf_q4k_f16(uint2 w, int h, uint32_t sc) {
 // its d once; the 1024 offset and the min, (1024 d + dmin m) times each
 // sub-block's activation sum, leave once per stage as one f32 rank-4 matrix
 // step per tile.  Results are in the rows' 2^s scale until the epilogue.
-// LDS per stage: pieces hi/lo [64 rows][272]; weight quant bytes as planes
-// of 8-byte pieces [chunk 2][group 4][256 rows] (each plane padded by 128
-// bytes, so the two groups a half-wave reads land in different banks); per
-// row the stage's four 6-bit scales (one byte each), d, and the offsets
-// [4 sub-blocks][256 rows]; the sums [4][64]; the rows' 2^-s.
+// The weights never pass through LDS: each lane loads its row's quant words
+// and block header in the matrix operand layout and decodes the scales
+// itself (an LDS copy of the weights measured 1.6 % slower).  LDS per stage:
+// pieces hi/lo [64 rows][272], the sums [4][64]; then the rows' 2^-s.
 constexpr int kGuFeat = 128;
-constexpr int kGuWRows = 2 * kGuFeat;                         // 256
 constexpr int kGuThreads = 512;
-constexpr int kGuPlaneB = kGuWRows * 8 + 128;                 // 2176
-constexpr int kGuWOff = 2 * kXPieceB;                         // 34816
-constexpr int kGuScOff = kGuWOff + 8 * kGuPlaneB;             // 52224
-constexpr int kGuDOff = kGuScOff + kGuWRows * 4;              // 53248
-constexpr int kGuOffOff = kGuDOff + kGuWRows * 4;             // 54272
-constexpr int kGuSOff = kGuOffOff + 4 * kGuWRows * 4;         // 58368
-constexpr int kGuBufB = kGuSOff + 4 * kPfRows * 4;            // 59392: one stage buffer
-constexpr int kGuInvOff = 2 * kGuBufB;                        // 118784
-constexpr int kGuLds = kGuInvOff + kPfRows * 4;               // 119040
+constexpr int kGuSOff = 2 * kXPieceB;                         // 34816
+constexpr int kGuBufB = kGuSOff + 4 * kPfRows * 4;            // 35840: one stage buffer
+constexpr int kGuInvOff = 2 * kGuBufB;                        // 71680
+constexpr int kGuLds = kGuInvOff + kPfRows * 4;               // 71936
 
 __global__ __launch_bounds__(kGuThreads) void pf_gateup_kernel(
     const uint16_t* __restrict__ xhi, const uint16_t* __restrict__ xlo,
@@ -272,13 +265,13 @@ __global__ __launch_bounds__(kGuThreads) void pf_gateup_kernel(
 
     // staging roles.  Activations: 2 pieces x 64 rows x 16 chunks of 16 B,
     // item u < 4: piece u >> 1, row tid/16 (u even) or 32 + tid/16 (u odd),
-    // chunk tid & 15.  Weights: 256 rows x 4 parts of 16 B (q = u * 512 +
-    // tid, u < 2: row q >> 2, part q & 3); headers: thread tid reads row
-    // (tid & 255)'s (threads 256.. read them again, so every wave issues the
-    // same loads).  Sums: thread tid < 256 reads the sum of row tid >> 2,
-    // sub-block tid & 3.  Every load is unconditional (rows past the tile
-    // read token 0's and are zeroed when stored), so the loop is straight-line
-    // code.
+    // chunk tid & 15; sums: thread tid < 256 reads the sum of row tid >> 2,
+    // sub-block tid & 3.  Weights go straight into registers in the matrix
+    // operand layout: lane (col, g) of wave w holds, per stage, the 8 quant
+    // bytes 64 half + 32 c + 8 g (c = 0, 1) of gate row f0 + 16 w + col and of
+    // the same up row, and both rows' 16-byte block headers.  Every load is
+    // unconditional (rows past the tile read token 0's and are zeroed when
+    // stored), so the loop is straight-line code.
     const int ra = tid >> 4, rb2 = 32 + (tid >> 4), xc = tid & 15;
     const bool va = ra < nrows, vb = rb2 < nrows, vs = tid < 4 * kPfRows && (tid >> 2) < nrows;
     const int64_t toka = va ? pairs[row0 + ra] / k : 0;
@@ -286,30 +279,35 @@ __global__ __launch_bounds__(kGuThreads) void pf_gateup_kernel(
     const int64_t toks = vs ? pairs[row0 + (tid >> 2)] / k : 0;
     if (tid < kPfRows)
         reinterpret_cast<float*>(smem + kGuInvOff)[tid] = tid < nrows ? tinv[pairs[row0 + tid] / k] : 0.f;
-    auto wrow = [&](int r) -> const uint8_t* { return r < kGuFeat ? gexp + r * rowb : uexp + (r - kGuFeat) * rowb; };
-    // a stage's operands in registers: activation chunks, weight quant
-    // chunks, the block header, the sub-block sum
-    auto load_stage = [&](uint4 (&rx)[4], uint4 (&rw)[2], uint4& rh, float& rs, int st)
-                          __attribute__((always_inline)) {
+    const int col = lane & 15, g = lane >> 4;
+    const int frow = 16 * wave + col;                         // gate row frow, up row frow of uexp
+    const uint8_t* grow = gexp + frow * rowb;
+    const uint8_t* urow = uexp + frow * rowb;
+    // a stage's activation operands in registers: chunks and the sub-block sum
+    auto load_x = [&](uint4 (&rx)[4], float& rs, int st) __attribute__((always_inline)) {
         const int64_t k0 = (int64_t)st * kStageK;
-        const int64_t sb = st >> 1;
-        const int half = st & 1;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int64_t tok = (u & 1) ? tokb : toka;
             const uint16_t* xs = u < 2 ? xhi : xlo;
             rx[u] = *reinterpret_cast<const uint4*>(xs + tok * H + k0 + 8 * xc);
         }
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int q = u * kGuThreads + tid;
-            rw[u] = *reinterpret_cast<const uint4*>(wrow(q >> 2) + sb * kQ4KBytes + 16 + 64 * half + 16 * (q & 3));
-        }
-        rh = *reinterpret_cast<const uint4*>(wrow(tid & (kGuWRows - 1)) + sb * kQ4KBytes);
         rs = xs32[toks * (H / 32) + 4 * st + (tid & 3)];
     };
-    auto store_stage = [&](const uint4 (&rx)[4], const uint4 (&rw)[2], const uint4& rh, const float& rs,
-                           int half) __attribute__((always_inline)) {
+    // this lane's weight operands of stage st: quant words (gate c0, c1, up
+    // c0, c1) and the two block headers
+    auto load_w = [&](uint2 (&rw)[4], uint4 (&rh)[2], int st) __attribute__((always_inline)) {
+        const int64_t off = (int64_t)(st >> 1) * kQ4KBytes;
+        const int q0 = 16 + 64 * (st & 1) + 8 * g;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            rw[c] = *reinterpret_cast<const uint2*>(grow + off + q0 + 32 * c);
+            rw[2 + c] = *reinterpret_cast<const uint2*>(urow + off + q0 + 32 * c);
+        }
+        rh[0] = *reinterpret_cast<const uint4*>(grow + off);
+        rh[1] = *reinterpret_cast<const uint4*>(urow + off);
+    };
+    auto store_x = [&](const uint4 (&rx)[4], const float& rs, int half) __attribute__((always_inline)) {
         uint8_t* const sbuf = smem + (half ? kGuBufB : 0);   // stage st goes to buffer st & 1
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -318,33 +316,10 @@ __global__ __launch_bounds__(kGuThreads) void pf_gateup_kernel(
             *reinterpret_cast<uint4*>(sbuf + (u >> 1) * kXPieceB + r * kXRowB + xc * 16) =
                 make_uint4(rx[u].x & mk, rx[u].y & mk, rx[u].z & mk, rx[u].w & mk);
         }
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int q = u * kGuThreads + tid, r = q >> 2, part = q & 3;
-            const int c = part >> 1, g0 = 2 * (part & 1);         // 16 B = groups g0, g0 + 1 of chunk c
-            *reinterpret_cast<uint2*>(sbuf + kGuWOff + (c * 4 + g0) * kGuPlaneB + r * 8) = make_uint2(rw[u].x, rw[u].y);
-            *reinterpret_cast<uint2*>(sbuf + kGuWOff + (c * 4 + g0 + 1) * kGuPlaneB + r * 8) = make_uint2(rw[u].z, rw[u].w);
-        }
-        if (tid < kGuWRows) {
-            const float d = half_bits_to_float(rh.x & 0xffffu);
-            const float dmin = half_bits_to_float(rh.x >> 16);
-            uint32_t scp = 0;
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                int sc, m;
-                pf_q4k_scale_min(rh.y, rh.z, rh.w, 4 * half + jj, sc, m);
-                scp |= (uint32_t)sc << (8 * jj);
-                reinterpret_cast<float*>(sbuf + kGuOffOff)[jj * kGuWRows + tid] = 1024.f * d + dmin * (float)m;
-            }
-            reinterpret_cast<uint32_t*>(sbuf + kGuScOff)[tid] = scp;
-            reinterpret_cast<float*>(sbuf + kGuDOff)[tid] = d;
-        }
         if (tid < 4 * kPfRows)
             reinterpret_cast<float*>(sbuf + kGuSOff)[(tid & 3) * kPfRows + (tid >> 2)] = vs ? rs : 0.f;
     };
 
-    const int col = lane & 15, g = lane >> 4;
-    const int frow = 16 * wave + col;                         // gate row frow, up row 128 + frow
     f32x4_t acc[4][2], sbk[4][2];                             // [token block][gate, up]: total, this super-block
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -357,21 +332,35 @@ __global__ __launch_bounds__(kGuThreads) void pf_gateup_kernel(
     // the matrix work of the stage in LDS for the tile's first NTB token
     // blocks (the rest hold no pairs; NTB is fixed per instantiation so the
     // body has no branches and the LDS reads of later steps can be issued
-    // ahead of the matrix work); half: which half of its super-block
-    auto compute = [&](auto ntb_c, int half) __attribute__((always_inline)) {
+    // ahead of the matrix work); half: which half of its super-block; rw, rh:
+    // this lane's weight words and headers of the stage
+    auto compute = [&](auto ntb_c, int half, const uint2 (&rw)[4], const uint4 (&rh)[2])
+                       __attribute__((always_inline)) {
         constexpr int NTB = decltype(ntb_c)::value;
         const uint8_t* const sbuf = smem + (half ? kGuBufB : 0);
-        const uint32_t scg = reinterpret_cast<const uint32_t*>(sbuf + kGuScOff)[frow];
-        const uint32_t scu = reinterpret_cast<const uint32_t*>(sbuf + kGuScOff)[kGuFeat + frow];
-        // operands of sub-block j: weight words and the NTB activation
-        // blocks' two pieces, read one sub-block ahead of its matrix steps
-        uint2 wg[2], wu[2];
+        // the stage's four 6-bit scales of each row, d, and the offset
+        // 1024 d + dmin m of the lane's k slot (sub-block 4 half + g)
+        uint32_t scg = 0, scu = 0;
+        float nog, nou;
+        {
+            int sc, m;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                pf_q4k_scale_min(rh[0].y, rh[0].z, rh[0].w, 4 * half + jj, sc, m);
+                scg |= (uint32_t)sc << (8 * jj);
+                pf_q4k_scale_min(rh[1].y, rh[1].z, rh[1].w, 4 * half + jj, sc, m);
+                scu |= (uint32_t)sc << (8 * jj);
+            }
+            pf_q4k_scale_min(rh[0].y, rh[0].z, rh[0].w, 4 * half + g, sc, m);
+            nog = -(1024.f * half_bits_to_float(rh[0].x & 0xffffu) + half_bits_to_float(rh[0].x >> 16) * (float)m);
+            pf_q4k_scale_min(rh[1].y, rh[1].z, rh[1].w, 4 * half + g, sc, m);
+            nou = -(1024.f * half_bits_to_float(rh[1].x & 0xffffu) + half_bits_to_float(rh[1].x >> 16) * (float)m);
+        }
+        // the NTB activation blocks' two pieces of sub-block j, read one
+        // sub-block ahead of its matrix steps
         f16x8_t ah[2][NTB], al[2][NTB];
         auto read = [&](int j) __attribute__((always_inline)) {
-            const int c = j >> 1, b = j & 1;
-            const uint8_t* plane = sbuf + kGuWOff + (c * 4 + g) * kGuPlaneB;
-            wg[b] = *reinterpret_cast<const uint2*>(plane + frow * 8);
-            wu[b] = *reinterpret_cast<const uint2*>(plane + (kGuFeat + frow) * 8);
+            const int b = j & 1;
 #pragma unroll
             for (int tb = 0; tb < NTB; ++tb) {
                 const int xo = (16 * tb + col) * kXRowB + (32 * j + 8 * g) * 2;
@@ -385,8 +374,8 @@ __global__ __launch_bounds__(kGuThreads) void pf_gateup_kernel(
             const int b = j & 1;
             __builtin_amdgcn_sched_barrier(0);
             if (j + 1 < 4) read(j + 1);
-            const f16x8_t bg = pf_q4k_f16(wg[b], j & 1, (scg >> (8 * j)) & 0xffu);
-            const f16x8_t bu = pf_q4k_f16(wu[b], j & 1, (scu >> (8 * j)) & 0xffu);
+            const f16x8_t bg = pf_q4k_f16(rw[j >> 1], j & 1, (scg >> (8 * j)) & 0xffu);
+            const f16x8_t bu = pf_q4k_f16(rw[2 + (j >> 1)], j & 1, (scu >> (8 * j)) & 0xffu);
 #pragma unroll
             for (int tb = 0; tb < NTB; ++tb) {
                 sbk[tb][0] = pf_mfma16h(ah[b][tb], bg, sbk[tb][0]);
@@ -401,10 +390,8 @@ __global__ __launch_bounds__(kGuThreads) void pf_gateup_kernel(
         __builtin_amdgcn_sched_barrier(0);
         // offset and min of the stage's 4 sub-blocks: acc -= S . off, a rank-4
         // product per tile, as one f32 matrix step (k = sub-block = lane / 16)
-        const float nog = -reinterpret_cast<const float*>(sbuf + kGuOffOff)[g * kGuWRows + frow];
-        const float nou = -reinterpret_cast<const float*>(sbuf + kGuOffOff)[g * kGuWRows + kGuFeat + frow];
-        const float dg = reinterpret_cast<const float*>(sbuf + kGuDOff)[frow];
-        const float du = reinterpret_cast<const float*>(sbuf + kGuDOff)[kGuFeat + frow];
+        const float dg = half_bits_to_float(rh[0].x & 0xffffu);
+        const float du = half_bits_to_float(rh[1].x & 0xffffu);
 #pragma unroll
         for (int tb = 0; tb < NTB; ++tb) {
             const float sa = reinterpret_cast<const float*>(sbuf + kGuSOff)[g * kPfRows + 16 * tb + col];
@@ -422,37 +409,42 @@ __global__ __launch_bounds__(kGuThreads) void pf_gateup_kernel(
         }
     };
     const int ntb = (nrows + 15) >> 4;                        // 1..4, uniform
-    // Two LDS stage buffers (stage st in buffer st & 1), one barrier per
-    // stage and two stages in flight in registers (odd stages in set A, even
-    // ones in set B): after the barrier before stage st's matrix work, stage
-    // st is in its buffer and every wave is done with stage st - 1; stage
-    // st + 1 (loaded two stages earlier) goes into the other buffer, stage
-    // st + 3 is requested into the registers that held it, and stage st is
-    // multiplied.  Past the end the requests repeat the last stage and the
-    // stores fill the free buffer (not read), so every trip issues the same
-    // loads and stores.
+    // Two LDS stage buffers for the activations (stage st in buffer st & 1),
+    // one barrier per stage and two stages in flight in registers (odd
+    // stages in set A, even ones in set B): after the barrier before stage
+    // st's matrix work, stage st is in its buffer and every wave is done with
+    // stage st - 1; stage st + 1 (loaded two stages earlier) goes into the
+    // other buffer, stage st + 3 is requested into the registers that held
+    // it, and stage st is multiplied.  The weights go into two register sets
+    // by stage parity, each requested right after the stage that used it.
+    // Past the end the requests repeat the last stage and the stores fill the
+    // free buffer (not read), so every trip issues the same loads and stores.
     auto run = [&](auto ntb_c) __attribute__((always_inline)) {
-        uint4 rxA[4], rwA[2], rhA, rxB[4], rwB[2], rhB;
+        uint4 rxA[4], rxB[4];
         float rsA, rsB;
-        load_stage(rxA, rwA, rhA, rsA, 0);
-        store_stage(rxA, rwA, rhA, rsA, 0);
-        load_stage(rxA, rwA, rhA, rsA, min(1, nst - 1));
-        load_stage(rxB, rwB, rhB, rsB, min(2, nst - 1));
+        uint2 wA[4], wB[4];
+        uint4 hA[2], hB[2];
+        load_x(rxA, rsA, 0);
+        store_x(rxA, rsA, 0);
+        load_x(rxA, rsA, min(1, nst - 1));
+        load_x(rxB, rsB, min(2, nst - 1));
+        load_w(wA, hA, 0);
+        load_w(wB, hB, min(1, nst - 1));
         __syncthreads();
-        store_stage(rxA, rwA, rhA, rsA, 1);
-        // (the trip starts where only set B's loads are outstanding, so the
-        // waits at the loop head count the same on both of its entries)
+        store_x(rxA, rsA, 1);
         for (int st = 0; st < nst; st += 2) {
-            load_stage(rxA, rwA, rhA, rsA, min(st + 3, nst - 1));
+            load_x(rxA, rsA, min(st + 3, nst - 1));
             wave_prio(wave >= 4);
-            compute(ntb_c, 0);
+            compute(ntb_c, 0, wA, hA);
+            load_w(wA, hA, min(st + 2, nst - 1));
             __syncthreads();
-            store_stage(rxB, rwB, rhB, rsB, 0);
-            load_stage(rxB, rwB, rhB, rsB, min(st + 4, nst - 1));
+            store_x(rxB, rsB, 0);
+            load_x(rxB, rsB, min(st + 4, nst - 1));
             wave_prio(wave < 4);
-            compute(ntb_c, 1);
+            compute(ntb_c, 1, wB, hB);
+            load_w(wB, hB, min(st + 3, nst - 1));
             __syncthreads();
-            store_stage(rxA, rwA, rhA, rsA, 1);
+            store_x(rxA, rsA, 1);
         }
     };
     if (ntb == 1) run(std::integral_constant<int, 1>{});
