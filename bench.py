@@ -82,8 +82,8 @@ PMC_STEPS = 16
 # in profiles/ffn_fused8_kernel_a3b_decode_b1_traffic.md.  The figure belongs
 # to the kernel sources it was measured on; when they change it is reported
 # as null until the counters are taken again.
-TRAFFIC_BYTES_PER_LAUNCH = 26_826_780
-TRAFFIC_SOURCES_SHA256 = "c5819fc59c8cd4606edb28627b36c304264949e754d447ee3feb2a21e5da87dc"
+TRAFFIC_BYTES_PER_LAUNCH = 26_815_863
+TRAFFIC_SOURCES_SHA256 = "6e57e8c71b4a7d6659cd9222509a6706d7d6db7d3d3857962cb91eef9c06eba5"
 TRAFFIC_SOURCES = ("sparse_moe_decode_q3moe_amd/csrc/ffn_decode.hip",
                    "sparse_moe_decode_q3moe_amd/csrc/route_common.h",
                    "sparse_moe_decode_q3moe_amd/csrc/device_common.h")

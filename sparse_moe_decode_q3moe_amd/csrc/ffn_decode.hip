@@ -722,6 +722,8 @@ static_assert((kSyncExitTop + 1) * 4 <= (int)kFfnRouteSyncOffset, "sync header t
 constexpr int kSyncPresence = 6144 / 8;
 constexpr int kMaxPresence = 256;
 static_assert((kSyncPresence + kMaxPresence) * 8 <= (int)kFfnSyncBytes, "presence words outside the header");
+static_assert(kFfnRouteSyncOffset + kRouteCounterBytes <= (size_t)kSyncPresence * 8,
+              "the route kernel's counters overlap the presence words");
 
 __device__ __forceinline__ int stripe_members(int stripe, int grid) {
     return grid / kStripes + (stripe < grid % kStripes ? 1 : 0);

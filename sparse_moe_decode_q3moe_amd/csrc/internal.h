@@ -61,6 +61,9 @@ hipError_t launch_prefill_ffn(const float* hidden, int64_t T, int64_t H, int64_t
 // a caller that embeds the route in a larger workspace can keep the counter
 // at an offset that does not depend on the call's sizes.
 constexpr size_t kRouteSyncBytes = 4096;
+// The counters use the first kRouteCounterBytes of that (a top counter and
+// 8 stripe counters, 128 bytes apart).
+constexpr size_t kRouteCounterBytes = 9 * 128;
 size_t route_workspace_bytes(int64_t T, int32_t E);
 hipError_t launch_route(const float* hidden, int64_t T, int64_t H, const float* router,
                         int32_t E, int32_t k, int32_t* idx, float* w, int32_t* sync,
