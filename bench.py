@@ -104,7 +104,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "multi-GPU sharding of this block is a design, not part of this build",
+              "sharding this block across GPUs is described in the design notes, not implemented",
               file=sys.stderr)
         sys.exit(2)
     if args.steps < 1 or args.warmup < 0:

@@ -455,8 +455,8 @@ int orc_output_head(const float *x, int64_t T, const uint8_t *W, int qtype, int6
     return 0;
 }
 
-/* Token -> expert grouping of the routed (token, slot) pairs (survey row
- * a3; the pages' plan groups tokens by expert for batched prefill, #3714
+/* Token -> expert grouping of the routed (token, slot) pairs (the pages'
+ * plan groups tokens by expert for batched prefill: aprender issue #3714,
  * gap list).  Pair p = t*k + slot with expert idx[p].  For every expert e in
  * order, the pairs routed to it in increasing p: counts[e] of them starting
  * at offsets[e]; offsets[E] is the number of grouped pairs.  A pair whose
