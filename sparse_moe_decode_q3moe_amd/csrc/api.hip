@@ -207,9 +207,9 @@ q3moe_status moe_ffn_impl(const float* hidden, int64_t T, int64_t H, int64_t F, 
         if (e != hipSuccess) return from_hip(e);
         x = ws_norm;
     }
-    // The route's arrival counter lives in the expert-FFN header at a fixed
+    // The route's arrival counters live in the expert-FFN header at a fixed
     // offset: ws_route moves with T, H, F and k, and a region that a larger
-    // call filled with data must never serve as a counter that has to be zero.
+    // call filled with data must never serve as counters that have to be zero.
     hipError_t e = q3moe::launch_route(x, T, H, router, E, top_k, topk_idx, topk_w,
                                        reinterpret_cast<int32_t*>(ws + q3moe::kFfnRouteSyncOffset),
                                        reinterpret_cast<double*>(ws_route + q3moe::kRouteSyncBytes), s);

@@ -75,10 +75,11 @@ bool decode_ffn_supported(int64_t H, int64_t F, int32_t k);
 // words (the status word, then line-spaced completion counters of the fused
 // kernel), then holds the intermediate h from that offset on.
 constexpr size_t kFfnSyncBytes = 8192;
-// Byte offset, inside that header, of the route kernel's arrival counter when
+// Byte offset, inside that header, of the route kernel's arrival counters when
 // the route runs as part of the MoE block (the header's first half holds the
-// expert FFN's own words).  Fixed, so the counter sits at one address for
-// calls of every size through one workspace.
+// expert FFN's own words; the counters take kRouteCounterBytes, below the
+// fused kernel's presence words).  Fixed, so the counters sit at one address
+// for calls of every size through one workspace.
 constexpr size_t kFfnRouteSyncOffset = 4096;
 hipError_t launch_decode_ffn(const float* hidden, int64_t T, int64_t H, int64_t F, int32_t E,
                              int32_t k, const int32_t* idx, const float* w,
